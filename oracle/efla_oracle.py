@@ -1,0 +1,310 @@
+"""Plain fp64 CPU oracle for Exact Flow Linear Attention (EFLA).
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg of
+the benchmark may import or run this module. The HIP library never calls it, and
+this module shares no code, table or helper with the HIP library.
+
+What is computed (Exact Flow Linear Attention summary page; the pages print no
+equation, so the steps below are the plain reading of their statements):
+
+* Memory dynamics (section 3.1): on token t the d_k x d_v state obeys
+  dS/dtau = -A_t S + b_t for tau in [0, beta_t], with A_t = k_t k_t^T (the
+  rank-1 dynamics matrix named in section 6) and input b_t = k_t v_t^T held
+  constant on the interval (zero-order hold).
+* Exact flow (sections 3.2 and 6, Appendix E): S_t = e^{-beta A} S_{t-1}
+  + int_0^beta e^{-(beta-tau) A} dtau b. Because A^2 = lambda A with
+  lambda = k^T k (Appendix D: A is a scaled projection), the exponential is
+  I - (1 - e^{-beta lambda})/lambda * k k^T and the integral applied to b is
+  (1 - e^{-beta lambda})/lambda * k v^T. The update therefore keeps the delta
+  rule's form with beta_t replaced by alpha_t = (1 - e^{-beta_t lambda_t}) / lambda_t
+  (section 3.2):  S_t = S_{t-1} + alpha_t k_t (v_t - S_{t-1}^T k_t)^T.
+* Read-out: o_t = scale * S_t^T q_t, taken after the update of token t
+  (the causal mask of section 2 keeps the diagonal).
+* Chunkwise form (section 3.3, UT transform): for a chunk with rows K, V, Q and
+  incoming state S, T = (I + strictly_lower(diag(alpha) K K^T))^{-1} diag(alpha),
+  W = T K, U = T V, U~ = U - W S, O = scale (Q S + tril(Q K^T) U~),
+  S' = S + K^T U~.  Used only to produce per-stage values for tests.
+* Backward: reverse-mode differentiation of the token recurrence, written out
+  by hand (below); pinned against central finite differences in the tests.
+
+The state starts at zero (or at a given initial state) for every sequence;
+packed batches restart the state at every cu_seqlens offset.
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.linalg
+
+CHUNK = 64
+
+# Below this |x| the functions phi and phi' are summed from their Taylor series;
+# 25 terms keep the truncation error under 1e-25 for |x| < 1.
+_SERIES_BELOW = 1.0
+_SERIES_TERMS = 25
+
+
+def phi(x):
+    """phi(x) = (1 - e^{-x}) / x, phi(0) = 1, so alpha = beta * phi(beta * lambda).
+
+    Taylor series sum_{n>=0} (-x)^n / (n+1)! near zero, -expm1(-x)/x elsewhere.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    small = np.abs(x) < _SERIES_BELOW
+    xs = x[small]
+    term = np.ones_like(xs)
+    acc = np.ones_like(xs)
+    for n in range(1, _SERIES_TERMS):
+        term = term * (-xs) / (n + 1)
+        acc = acc + term
+    out[small] = acc
+    xl = x[~small]
+    out[~small] = -np.expm1(-xl) / xl
+    return out
+
+
+def dphi(x):
+    """phi'(x) = (e^{-x} (1 + x) - 1) / x^2, phi'(0) = -1/2.
+
+    Taylor series sum_{n>=1} -n (-x)^{n-1} / (n+1)! near zero (the closed form
+    cancels catastrophically there), the closed form elsewhere.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    small = np.abs(x) < _SERIES_BELOW
+    xs = x[small]
+    s = np.full_like(xs, 0.5)          # (-x)^{n-1} / (n+1)! at n = 1
+    acc = -1.0 * s
+    for n in range(2, _SERIES_TERMS + 1):
+        s = s * (-xs) / (n + 1)
+        acc = acc - n * s
+    out[small] = acc
+    xl = x[~small]
+    out[~small] = (np.exp(-xl) * (1.0 + xl) - 1.0) / (xl * xl)
+    return out
+
+
+def alpha(beta, lam):
+    """Effective step of the exact flow: (1 - e^{-beta lambda}) / lambda; beta when lambda = 0."""
+    beta = np.asarray(beta, dtype=np.float64)
+    lam = np.asarray(lam, dtype=np.float64)
+    return beta * phi(beta * lam)
+
+
+def coefficients(k, beta):
+    """Per-token lambda = ||k||^2, alpha, d alpha / d beta = e^{-beta lambda} and
+    d alpha / d lambda = beta^2 phi'(beta lambda). k: [..., d_k]; beta: [...]."""
+    k = np.asarray(k, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    lam = np.sum(k * k, axis=-1)
+    x = beta * lam
+    return dict(lam=lam, alpha=beta * phi(x), dalpha_dbeta=np.exp(-x),
+                dalpha_dlam=beta * beta * dphi(x))
+
+
+# ---------------------------------------------------------------------------
+# Token-by-token recurrence over N independent streams of length L.
+# ---------------------------------------------------------------------------
+
+def _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=0):
+    """q, k: [N, L, dk]; v: [N, L, dv]; beta: [N, L]; S0: [N, dk, dv] or None.
+
+    Returns o [N, L, dv], final state [N, dk, dv] and, when checkpoint_every > 0,
+    the states entering each block of that many tokens.
+    """
+    N, L, dk = k.shape
+    dv = v.shape[-1]
+    S = np.zeros((N, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((N, L, dv))
+    checkpoints = []
+    a = alpha(beta, np.sum(k * k, axis=-1))            # [N, L]
+    for t in range(L):
+        if checkpoint_every and t % checkpoint_every == 0:
+            checkpoints.append(S.copy())
+        kt = k[:, t, :]
+        r = v[:, t, :] - np.einsum("nd,ndv->nv", kt, S)   # v_t - S_{t-1}^T k_t
+        S = S + a[:, t, None, None] * kt[:, :, None] * r[:, None, :]
+        o[:, t, :] = scale * np.einsum("nd,ndv->nv", q[:, t, :], S)
+    return o, S, checkpoints
+
+
+def _backward_streams(q, k, v, beta, do, scale, S0, dS_final):
+    """Reverse-mode gradients of sum(o * do) (+ <S_final, dS_final>) for _forward_streams.
+
+    The state is stored only at block boundaries of CHUNK tokens and rebuilt
+    inside each block during the reverse sweep.
+    """
+    N, L, dk = k.shape
+    dv = v.shape[-1]
+    co = coefficients(k, beta)
+    a = co["alpha"]
+    _, _, ckpt = _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=CHUNK)
+    dq = np.zeros_like(q)
+    dk_ = np.zeros_like(k)
+    dv_ = np.zeros_like(v)
+    dalpha = np.zeros((N, L))
+    dS = np.zeros((N, dk, dv)) if dS_final is None else np.array(dS_final, dtype=np.float64)
+    nblk = (L + CHUNK - 1) // CHUNK
+    for blk in range(nblk - 1, -1, -1):
+        t0, t1 = blk * CHUNK, min(L, (blk + 1) * CHUNK)
+        # Rebuild S_{t-1} (states[i]) and S_t (states[i+1]) for the tokens of this block.
+        states = [ckpt[blk]]
+        for t in range(t0, t1):
+            S = states[-1]
+            kt = k[:, t, :]
+            r = v[:, t, :] - np.einsum("nd,ndv->nv", kt, S)
+            states.append(S + a[:, t, None, None] * kt[:, :, None] * r[:, None, :])
+        for t in range(t1 - 1, t0 - 1, -1):
+            S_prev, S_t = states[t - t0], states[t - t0 + 1]
+            kt, qt = k[:, t, :], q[:, t, :]
+            # o_t = scale * S_t^T q_t
+            dS = dS + scale * qt[:, :, None] * do[:, t, None, :]
+            dq[:, t, :] = scale * np.einsum("ndv,nv->nd", S_t, do[:, t, :])
+            # S_t = S_{t-1} + alpha_t k_t r_t^T,  r_t = v_t - S_{t-1}^T k_t
+            r = v[:, t, :] - np.einsum("nd,ndv->nv", kt, S_prev)
+            dS_r = np.einsum("ndv,nv->nd", dS, r)               # dS r
+            dalpha[:, t] = np.einsum("nd,nd->n", kt, dS_r)
+            dr = a[:, t, None] * np.einsum("ndv,nd->nv", dS, kt)   # alpha dS^T k
+            dv_[:, t, :] = dr
+            dk_[:, t, :] = a[:, t, None] * dS_r - np.einsum("ndv,nv->nd", S_prev, dr)
+            dS = dS - kt[:, :, None] * dr[:, None, :]
+    # alpha_t = alpha(beta_t, lambda_t), lambda_t = ||k_t||^2
+    dbeta = dalpha * co["dalpha_dbeta"]
+    dk_ = dk_ + 2.0 * k * (dalpha * co["dalpha_dlam"])[:, :, None]
+    return dq, dk_, dv_, dbeta, dS
+
+
+# ---------------------------------------------------------------------------
+# [B, H, T, d] layout and packed batches.
+# ---------------------------------------------------------------------------
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def sequences(B, T, cu_seqlens):
+    """(batch index, start, end) of every sequence; packed batches have B == 1."""
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(c) for c in np.asarray(cu_seqlens)]
+    if B != 1 or cu[0] != 0 or cu[-1] != T or any(cu[i] > cu[i + 1] for i in range(len(cu) - 1)):
+        raise ValueError("cu_seqlens must start at 0, end at T, be non-decreasing, with B == 1")
+    return [(0, cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+
+
+def forward(q, k, v, beta, scale=1.0, cu_seqlens=None, initial_state=None):
+    """EFLA forward. q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T].
+
+    initial_state: None or [n_seq, H, dk, dv] (n_seq = B, or the number of packed
+    sequences). Returns (o [B,H,T,dv], final_state [n_seq, H, dk, dv]), fp64.
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    seqs = sequences(B, T, cu_seqlens)
+    final = np.zeros((len(seqs), H, dk, dv))
+    S0 = _f64(initial_state)
+    for i, (b, s, e) in enumerate(seqs):
+        o_i, S_i, _ = _forward_streams(q[b, :, s:e], k[b, :, s:e], v[b, :, s:e], beta[b, :, s:e],
+                                       scale, None if S0 is None else S0[i])
+        o[b, :, s:e] = o_i
+        final[i] = S_i
+    return o, final
+
+
+def backward(q, k, v, beta, do, scale=1.0, cu_seqlens=None, initial_state=None,
+             d_final_state=None):
+    """Gradients of sum(o * do) (+ <final_state, d_final_state>) for `forward`.
+
+    Returns dict(dq, dk, dv, dbeta, d_initial_state), fp64.
+    """
+    q, k, v, beta, do = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(do)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    seqs = sequences(B, T, cu_seqlens)
+    S0 = _f64(initial_state)
+    dSF = _f64(d_final_state)
+    g = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+             dbeta=np.zeros_like(beta), d_initial_state=np.zeros((len(seqs), H, dk, dv)))
+    for i, (b, s, e) in enumerate(seqs):
+        dq, dk_, dv_, dbeta, dS0 = _backward_streams(
+            q[b, :, s:e], k[b, :, s:e], v[b, :, s:e], beta[b, :, s:e], do[b, :, s:e], scale,
+            None if S0 is None else S0[i], None if dSF is None else dSF[i])
+        g["dq"][b, :, s:e] = dq
+        g["dk"][b, :, s:e] = dk_
+        g["dv"][b, :, s:e] = dv_
+        g["dbeta"][b, :, s:e] = dbeta
+        g["d_initial_state"][i] = dS0
+    return g
+
+
+# ---------------------------------------------------------------------------
+# Chunkwise (UT transform) form: per-stage values for tests of the GPU stages.
+# ---------------------------------------------------------------------------
+
+def chunk_ut(k, v, beta):
+    """UT transform of one chunk. k: [C, dk]; v: [C, dv]; beta: [C].
+
+    Returns dict(alpha, T, W, U) with T = (I + strictly_lower(diag(alpha) K K^T))^{-1} diag(alpha).
+    """
+    k, v, beta = _f64(k), _f64(v), _f64(beta)
+    C = k.shape[0]
+    a = alpha(beta, np.sum(k * k, axis=-1))
+    A = np.tril(a[:, None] * (k @ k.T), -1)
+    T = scipy.linalg.solve_triangular(np.eye(C) + A, np.diag(a), lower=True, unit_diagonal=True)
+    return dict(alpha=a, T=T, W=T @ k, U=T @ v)
+
+
+def chunk_forward(q, k, v, beta, scale=1.0, cu_seqlens=None, chunk=CHUNK):
+    """Chunkwise forward: returns o [B,H,T,dv], W [B,H,T,dk], U [B,H,T,dv],
+    U~ = U - W S [B,H,T,dv] and the list of per-chunk incoming states, one entry
+    per (sequence, chunk) in sequence order, each [H, dk, dv]."""
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    Wf = np.zeros((B, H, T, dk))
+    Uf = np.zeros((B, H, T, dv))
+    Ut = np.zeros((B, H, T, dv))
+    states = []
+    for (b, s, e) in sequences(B, T, cu_seqlens):
+        S = np.zeros((H, dk, dv))
+        for c0 in range(s, e, chunk):
+            c1 = min(e, c0 + chunk)
+            states.append(S.copy())
+            for h in range(H):
+                f = chunk_ut(k[b, h, c0:c1], v[b, h, c0:c1], beta[b, h, c0:c1])
+                Q, K = q[b, h, c0:c1], k[b, h, c0:c1]
+                U_t = f["U"] - f["W"] @ S[h]
+                o[b, h, c0:c1] = scale * (Q @ S[h] + np.tril(Q @ K.T) @ U_t)
+                Wf[b, h, c0:c1], Uf[b, h, c0:c1], Ut[b, h, c0:c1] = f["W"], f["U"], U_t
+                S[h] = S[h] + K.T @ U_t
+    return dict(o=o, W=Wf, U=Uf, Ut=Ut, states=states)
+
+
+def euler_forward(q, k, v, beta, scale=1.0, cu_seqlens=None):
+    """The Euler (DeltaNet) recurrence with the raw step beta_t, for comparisons."""
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    for (b, s, e) in sequences(B, T, cu_seqlens):
+        S = np.zeros((H, dk, dv))
+        for t in range(s, e):
+            kt = k[b, :, t]
+            r = v[b, :, t] - np.einsum("hd,hdv->hv", kt, S)
+            S = S + beta[b, :, t, None, None] * kt[:, :, None] * r[:, None, :]
+            o[b, :, t] = scale * np.einsum("hd,hdv->hv", q[b, :, t], S)
+    return o
+
+
+def rel_err(x, ref):
+    """Normwise relative error max|x - ref| / max|ref| (0 when both are all zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(x - ref)) if ref.size else 0.0
+    if den == 0.0:
+        return float(num)
+    return float(num / den)

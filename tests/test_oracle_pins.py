@@ -1,0 +1,436 @@
+"""Pins for the fp64 oracle: each test checks it against something other than itself.
+
+The pages (Exact Flow Linear Attention summary page) print no equation and no
+worked example, so the pins are the mathematics their statements fix:
+the zero-order-hold flow itself (section 3.1, Appendix E) computed by a dense
+matrix exponential plus quadrature and by the Van Loan block exponential; the
+rank-1 structure (Appendix D); the small-step Euler limit (section 3.4); the
+contraction along k and the untouched orthogonal complement (section 3.4);
+the exactness of the flow (semigroup property); the chunkwise form (section 3.3)
+against the token recurrence; textbook special cases; mpmath for the
+coefficient functions; and central finite differences for the backward.
+"""
+import json
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+
+from oracle import efla_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _one_seq(S0, ks, vs, betas, qs=None, scale=1.0):
+    """Run the oracle on one sequence (B=H=1) from state S0; returns (o [T,dv], S_final)."""
+    ks = np.atleast_2d(ks)
+    vs = np.atleast_2d(vs)
+    T, dk = ks.shape
+    if qs is None:
+        qs = np.zeros_like(ks)
+    o, SF = O.forward(qs[None, None], ks[None, None], vs[None, None],
+                      np.asarray(betas, dtype=np.float64).reshape(1, 1, T), scale=scale,
+                      initial_state=None if S0 is None else S0[None, None])
+    return o[0, 0], SF[0, 0]
+
+
+def _zoh_dense(S, k, v, beta):
+    """Exact ZOH flow by definition: e^{-beta A} S + int_0^beta e^{-(beta - tau) A} dtau (k v^T)."""
+    A = np.outer(k, k)
+    b = np.outer(k, v)
+    E = scipy.linalg.expm(-beta * A)
+    integral, _ = scipy.integrate.quad_vec(lambda tau: scipy.linalg.expm(-(beta - tau) * A) @ b,
+                                           0.0, beta, epsabs=1e-15, epsrel=1e-13)
+    return E @ S + integral
+
+
+def _zoh_van_loan(S, k, v, beta):
+    """Same flow via exp(beta [[-A, k v^T], [0, 0]]) = [[e^{-beta A}, int ...], [0, I]]."""
+    dk, dv = len(k), len(v)
+    M = np.zeros((dk + dv, dk + dv))
+    M[:dk, :dk] = -np.outer(k, k)
+    M[:dk, dk:] = np.outer(k, v)
+    E = scipy.linalg.expm(beta * M)
+    return E[:dk, :dk] @ S + E[:dk, dk:]
+
+
+# ---------------------------------------------------------------- coefficients
+
+def test_phi_and_dphi_against_mpmath():
+    """phi(x) = (1 - e^{-x})/x and phi'(x) at 60 digits over x in [1e-12, 1e4] and small negatives."""
+    mpmath.mp.dps = 60
+    xs = np.concatenate([np.logspace(-12, 4, 601), -np.logspace(-12, 0.5, 121), [0.0, 1.0, 0.999999]])
+    ph, dp = O.phi(xs), O.dphi(xs)
+    worst_p = worst_d = 0.0
+    for x, p, d in zip(xs, ph, dp):
+        X = mpmath.mpf(float(x))
+        if X == 0:
+            P, D = mpmath.mpf(1), mpmath.mpf(-0.5)
+        else:
+            P = -mpmath.expm1(-X) / X
+            D = (mpmath.exp(-X) * (1 + X) - 1) / X ** 2
+        worst_p = max(worst_p, abs(p - float(P)) / abs(float(P)))
+        worst_d = max(worst_d, abs(d - float(D)) / abs(float(D)))
+    assert worst_p < 1e-15
+    assert worst_d < 1e-13
+
+
+def test_alpha_limits():
+    """alpha -> beta as beta*lambda -> 0 (section 3.4), alpha -> 1/lambda when e^{-beta lambda} underflows."""
+    beta = np.array([0.3, 0.7, 2.0])
+    assert np.allclose(O.alpha(beta, np.zeros(3)), beta, rtol=0, atol=0)
+    lam = np.array([1e-9, 1e-9, 1e-9])
+    assert np.allclose(O.alpha(beta, lam), beta * (1 - beta * lam / 2), rtol=1e-15)
+    assert np.allclose(O.alpha(np.array([50.0]), np.array([100.0])), 1.0 / 100.0, rtol=1e-15)
+
+
+def test_coefficient_derivatives_by_finite_differences():
+    r = _rng(3)
+    beta = r.uniform(0.05, 1.5, 50)
+    lam = np.exp(r.uniform(np.log(1e-6), np.log(50.0), 50))
+    co = O.coefficients(np.sqrt(lam)[:, None] * np.eye(1)[0], beta)
+    h = 1e-6
+    fd_b = (O.alpha(beta + h, lam) - O.alpha(beta - h, lam)) / (2 * h)
+    hl = h * np.maximum(lam, 1.0)
+    fd_l = (O.alpha(beta, lam + hl) - O.alpha(beta, lam - hl)) / (2 * hl)
+    assert np.allclose(co["dalpha_dbeta"], fd_b, rtol=1e-7, atol=1e-9)
+    assert np.allclose(co["dalpha_dlam"], fd_l, rtol=1e-6, atol=1e-9)
+
+
+# ---------------------------------------------------------------- exact flow
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_token_update_equals_dense_zoh_flow(seed):
+    """One token of the oracle equals expm + quadrature of the ZOH integral (d_k=5, d_v=4)."""
+    r = _rng(seed)
+    S = r.standard_normal((5, 4))
+    k = r.standard_normal(5) * r.uniform(0.3, 2.0)
+    v = r.standard_normal(4)
+    beta = r.uniform(0.1, 1.5)
+    _, S1 = _one_seq(S, k[None], v[None], [beta])
+    ref = _zoh_dense(S, k, v, beta)
+    assert np.max(np.abs(S1 - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_sequence_equals_van_loan_flow(seed):
+    """Eight tokens, outputs and states, against the Van Loan block exponential, token by token."""
+    r = _rng(10 + seed)
+    dk, dv, T = 6, 3, 8
+    ks = r.standard_normal((T, dk)) * r.uniform(0.2, 3.0, (T, 1))
+    vs = r.standard_normal((T, dv))
+    qs = r.standard_normal((T, dk))
+    betas = r.uniform(0.0, 2.0, T)
+    o, SF = _one_seq(None, ks, vs, betas, qs, scale=0.7)
+    S = np.zeros((dk, dv))
+    for t in range(T):
+        S = _zoh_van_loan(S, ks[t], vs[t], betas[t])
+        assert np.allclose(o[t], 0.7 * S.T @ qs[t], rtol=1e-12, atol=1e-12)
+    assert np.allclose(SF, S, rtol=1e-12, atol=1e-12)
+
+
+def test_rank1_structure_of_dynamics_matrix():
+    """A = k k^T is a scaled projection: A^2 = lambda A, so e^{-beta A} = I - alpha k k^T (Appendix D)."""
+    r = _rng(5)
+    k = r.standard_normal(7)
+    A = np.outer(k, k)
+    lam = k @ k
+    assert np.allclose(A @ A, lam * A, rtol=1e-14, atol=1e-12)
+    beta = 0.9
+    a = O.alpha(np.array([beta]), np.array([lam]))[0]
+    assert np.allclose(scipy.linalg.expm(-beta * A), np.eye(7) - a * A, rtol=1e-13, atol=1e-13)
+
+
+def test_semigroup_exact_but_not_euler():
+    """Exactness: flowing beta1 then beta2 with the same (k, v) equals flowing beta1 + beta2.
+    The Euler step (DeltaNet) does not have this property."""
+    r = _rng(7)
+    S = r.standard_normal((4, 3))
+    k = r.standard_normal(4)
+    v = r.standard_normal(3)
+    _, S2 = _one_seq(S, np.stack([k, k]), np.stack([v, v]), [0.4, 0.9])
+    _, S1 = _one_seq(S, k[None], v[None], [1.3])
+    assert np.max(np.abs(S2 - S1)) < 1e-13
+
+    def euler(S, k, v, b):
+        return S + b * np.outer(k, v - S.T @ k)
+    gap = np.max(np.abs(euler(euler(S, k, v, 0.4), k, v, 0.9) - euler(S, k, v, 1.3)))
+    assert gap > 1e-3
+
+
+def test_fixed_point_when_value_is_recalled():
+    """If v = S^T k the memory already maps k to v and the update leaves S unchanged."""
+    r = _rng(8)
+    S = r.standard_normal((5, 6))
+    k = r.standard_normal(5) * 3.0
+    _, S1 = _one_seq(S, k[None], (S.T @ k)[None], [0.8])
+    assert np.max(np.abs(S1 - S)) < 1e-13
+
+
+def test_contraction_along_key_and_orthogonal_complement():
+    """Section 3.4: the flow scales the component along k by e^{-beta lambda} (pulling it towards v)
+    and leaves the orthogonal complement unchanged; with v = 0 it is non-expansive."""
+    r = _rng(9)
+    for _ in range(20):
+        S = r.standard_normal((6, 4))
+        k = r.standard_normal(6) * r.uniform(0.1, 5.0)
+        v = r.standard_normal(4)
+        beta = r.uniform(0.0, 3.0)
+        lam = k @ k
+        P = np.eye(6) - np.outer(k, k) / lam
+        _, S1 = _one_seq(S, k[None], v[None], [beta])
+        e = np.exp(-beta * lam)
+        assert np.allclose(k @ S1, e * (k @ S) + (1 - e) * v, rtol=1e-12, atol=1e-12)
+        assert np.allclose(P @ S1, P @ S, rtol=1e-12, atol=1e-12)
+        _, S0v = _one_seq(S, k[None], np.zeros((1, 4)), [beta])
+        assert np.linalg.norm(S0v) <= np.linalg.norm(S) * (1 + 1e-14)
+
+
+def test_overwrite_limit_for_large_step():
+    """When beta*lambda is large the memory is overwritten along k: k^T S_t = v_t^T."""
+    r = _rng(11)
+    S = r.standard_normal((4, 3))
+    k = r.standard_normal(4)
+    v = r.standard_normal(3)
+    _, S1 = _one_seq(S, k[None], v[None], [80.0 / (k @ k)])
+    assert np.allclose(k @ S1, v, rtol=1e-13, atol=1e-13)
+
+
+def test_euler_limit_is_third_order_in_key_scale():
+    """Section 3.4: for small beta*lambda EFLA equals the delta rule up to higher-order terms.
+    With k -> s k the one-step gap to the Euler update shrinks like s^3."""
+    r = _rng(12)
+    S = r.standard_normal((5, 4))
+    k = r.standard_normal(5)
+    v = r.standard_normal(4)
+    beta = 0.8
+
+    def gap(s):
+        ks = s * k
+        _, S1 = _one_seq(S, ks[None], v[None], [beta])
+        return np.max(np.abs(S1 - (S + beta * np.outer(ks, v - S.T @ ks))))
+    g1, g2, g3 = gap(1e-1), gap(1e-2), gap(1e-3)
+    assert 800 < g1 / g2 < 1200
+    assert 800 < g2 / g3 < 1200
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_single_token_output():
+    """From S_0 = 0 a single token gives o_1 = scale * alpha_1 (k_1 . q_1) v_1."""
+    r = _rng(13)
+    q, k, v = r.standard_normal(8), r.standard_normal(8), r.standard_normal(5)
+    beta = 0.6
+    o, _ = _one_seq(None, k[None], v[None], [beta], q[None], scale=1.3)
+    a = (1 - np.exp(-beta * (k @ k))) / (k @ k)
+    assert np.allclose(o[0], 1.3 * a * (k @ q) * v, rtol=1e-14, atol=1e-14)
+
+
+def test_orthogonal_keys_reduce_to_masked_linear_attention():
+    """Mutually orthogonal keys from S_0 = 0: o_t = sum_{i<=t} alpha_i (k_i . q_t) v_i,
+    i.e. causal linear attention with per-token weights alpha (a masked matmul)."""
+    r = _rng(14)
+    d, T = 16, 12
+    Qm, _ = np.linalg.qr(r.standard_normal((d, d)))
+    ks = Qm[:, :T].T * r.uniform(0.2, 3.0, (T, 1))
+    vs = r.standard_normal((T, 5))
+    qs = r.standard_normal((T, d))
+    betas = r.uniform(0.1, 1.0, T)
+    o, _ = _one_seq(None, ks, vs, betas, qs)
+    lam = np.sum(ks * ks, axis=1)
+    a = (1 - np.exp(-betas * lam)) / lam
+    ref = np.tril(qs @ ks.T) @ (a[:, None] * vs)
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_keys_are_no_ops():
+    r = _rng(15)
+    S = r.standard_normal((4, 3))
+    _, S1 = _one_seq(S, np.zeros((3, 4)), r.standard_normal((3, 3)), [0.5, 0.9, 0.1])
+    assert np.array_equal(S1, S)
+
+
+# ---------------------------------------------------------------- chunk form, layouts
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 200])
+def test_chunk_form_equals_token_recurrence(T):
+    r = _rng(100 + T)
+    B, H, dk, dv = 2, 2, 8, 6
+    q = r.standard_normal((B, H, T, dk))
+    k = r.standard_normal((B, H, T, dk)) * r.uniform(0.3, 3.0, (B, H, T, 1))
+    v = r.standard_normal((B, H, T, dv))
+    beta = r.uniform(0.0, 1.0, (B, H, T))
+    o, _ = O.forward(q, k, v, beta, scale=0.5)
+    c = O.chunk_forward(q, k, v, beta, scale=0.5)
+    assert O.rel_err(c["o"], o) < 1e-12
+    # per-chunk states match the token recurrence at chunk boundaries
+    for b in range(B):
+        for ci, c0 in enumerate(range(0, T, O.CHUNK)):
+            _, S = O.forward(q[b:b + 1, :, :c0], k[b:b + 1, :, :c0], v[b:b + 1, :, :c0],
+                             beta[b:b + 1, :, :c0])
+            nchunk = (T + O.CHUNK - 1) // O.CHUNK
+            assert np.allclose(c["states"][b * nchunk + ci], S[0], rtol=1e-11, atol=1e-11)
+
+
+def test_chunk_ut_solves_its_triangular_system():
+    """T (I + A) ... written as (I + A) T = diag(alpha) with A strictly lower; W = T K, U = T V."""
+    r = _rng(21)
+    k = r.standard_normal((64, 16)) * r.uniform(0.5, 2.0, (64, 1))
+    v = r.standard_normal((64, 8))
+    beta = r.uniform(0.0, 1.0, 64)
+    f = O.chunk_ut(k, v, beta)
+    lam = np.sum(k * k, axis=1)
+    a = (1 - np.exp(-beta * lam)) / lam
+    A = np.tril(a[:, None] * (k @ k.T), -1)
+    assert np.allclose((np.eye(64) + A) @ f["T"], np.diag(a), rtol=1e-10, atol=1e-10)
+    assert np.allclose(np.triu(f["T"], 1), 0.0)
+
+
+def test_packed_batch_equals_separate_sequences():
+    r = _rng(22)
+    H, dk, dv = 2, 6, 5
+    lens = [3, 70, 1, 64, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = r.standard_normal((1, H, T, dk))
+    k = r.standard_normal((1, H, T, dk))
+    v = r.standard_normal((1, H, T, dv))
+    beta = r.uniform(0.0, 1.0, (1, H, T))
+    do = r.standard_normal((1, H, T, dv))
+    o, SF = O.forward(q, k, v, beta, cu_seqlens=cu)
+    g = O.backward(q, k, v, beta, do, cu_seqlens=cu)
+    co = O.chunk_forward(q, k, v, beta, cu_seqlens=cu)
+    assert O.rel_err(co["o"], o) < 1e-12
+    for i in range(len(lens)):
+        s, e = cu[i], cu[i + 1]
+        oi, Si = O.forward(q[:, :, s:e], k[:, :, s:e], v[:, :, s:e], beta[:, :, s:e])
+        gi = O.backward(q[:, :, s:e], k[:, :, s:e], v[:, :, s:e], beta[:, :, s:e], do[:, :, s:e])
+        assert np.array_equal(o[:, :, s:e], oi)
+        assert np.array_equal(SF[i], Si[0])
+        for name in ("dq", "dk", "dv", "dbeta"):
+            assert np.array_equal(g[name][:, :, s:e], gi[name])
+
+
+def test_split_sequence_with_carried_state():
+    """Forward over [0, T) equals [0, T1) then [T1, T) with the state carried; the backward
+    of the two halves, chained through the state gradient, equals the full backward."""
+    r = _rng(23)
+    H, T, T1, dk, dv = 2, 150, 70, 5, 4
+    q, k = r.standard_normal((1, H, T, dk)), r.standard_normal((1, H, T, dk))
+    v, do = r.standard_normal((1, H, T, dv)), r.standard_normal((1, H, T, dv))
+    beta = r.uniform(0.0, 1.0, (1, H, T))
+    o, SF = O.forward(q, k, v, beta)
+    oa, Sa = O.forward(q[..., :T1, :], k[..., :T1, :], v[..., :T1, :], beta[..., :T1])
+    ob, Sb = O.forward(q[..., T1:, :], k[..., T1:, :], v[..., T1:, :], beta[..., T1:], initial_state=Sa)
+    assert np.allclose(np.concatenate([oa, ob], axis=2), o, rtol=1e-12, atol=1e-12)
+    assert np.allclose(Sb, SF, rtol=1e-12, atol=1e-12)
+    g = O.backward(q, k, v, beta, do)
+    gb = O.backward(q[..., T1:, :], k[..., T1:, :], v[..., T1:, :], beta[..., T1:], do[..., T1:, :],
+                    initial_state=Sa)
+    ga = O.backward(q[..., :T1, :], k[..., :T1, :], v[..., :T1, :], beta[..., :T1], do[..., :T1, :],
+                    d_final_state=gb["d_initial_state"])
+    for name in ("dq", "dk", "dv", "dbeta"):
+        assert np.allclose(np.concatenate([ga[name], gb[name]], axis=2), g[name], rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, beta, do, dSF, S0, scale, cu=None):
+    o, SF = O.forward(q, k, v, beta, scale=scale, cu_seqlens=cu, initial_state=S0)
+    return float(np.sum(o * do) + np.sum(SF * dSF))
+
+
+def test_backward_against_central_differences_every_coordinate():
+    r = _rng(31)
+    B, H, T, dk, dv = 1, 2, 12, 4, 3
+    q, k = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk)) * 1.5
+    v, do = r.standard_normal((B, H, T, dv)), r.standard_normal((B, H, T, dv))
+    beta = r.uniform(0.05, 1.0, (B, H, T))
+    S0 = r.standard_normal((B, H, dk, dv))
+    dSF = r.standard_normal((B, H, dk, dv))
+    scale = 0.8
+    g = O.backward(q, k, v, beta, do, scale=scale, initial_state=S0, d_final_state=dSF)
+    args = dict(q=q, k=k, v=v, beta=beta, S0=S0)
+    names = dict(q="dq", k="dk", v="dv", beta="dbeta", S0="d_initial_state")
+    eps = 1e-6
+    for name, x in args.items():
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap, am = dict(args, **{name: xp}), dict(args, **{name: xm})
+            fd[idx] = (_loss(ap["q"], ap["k"], ap["v"], ap["beta"], do, dSF, ap["S0"], scale)
+                       - _loss(am["q"], am["k"], am["v"], am["beta"], do, dSF, am["S0"], scale)) / (2 * eps)
+        assert np.max(np.abs(fd - g[names[name]])) < 1e-7 * max(1.0, np.max(np.abs(fd))), name
+
+
+def test_backward_directional_derivative_multi_chunk_packed():
+    """Several 64-token blocks and a packed batch: <grad, u> against a central difference along u."""
+    r = _rng(32)
+    H, dk, dv = 2, 6, 5
+    cu = np.array([0, 3, 140, 141, 230], dtype=np.int32)
+    T = int(cu[-1])
+    q, k = r.standard_normal((1, H, T, dk)), r.standard_normal((1, H, T, dk)) * 1.3
+    v, do = r.standard_normal((1, H, T, dv)), r.standard_normal((1, H, T, dv))
+    beta = r.uniform(0.0, 1.0, (1, H, T))
+    S0 = np.zeros((4, H, dk, dv))
+    dSF = np.zeros((4, H, dk, dv))
+    g = O.backward(q, k, v, beta, do, scale=1.0, cu_seqlens=cu)
+    for trial in range(3):
+        u = {n: r.standard_normal(x.shape) for n, x in dict(q=q, k=k, v=v, beta=beta).items()}
+        eps = 1e-6
+        lp = _loss(q + eps * u["q"], k + eps * u["k"], v + eps * u["v"], beta + eps * u["beta"],
+                   do, dSF, S0, 1.0, cu)
+        lm = _loss(q - eps * u["q"], k - eps * u["k"], v - eps * u["v"], beta - eps * u["beta"],
+                   do, dSF, S0, 1.0, cu)
+        fd = (lp - lm) / (2 * eps)
+        an = sum(np.sum(g["d" + n] * u[n]) for n in ("q", "k", "v", "beta"))
+        assert abs(fd - an) < 1e-6 * max(1.0, abs(an))
+
+
+def test_backward_at_stiff_and_degenerate_keys():
+    """Keys with ||k|| from 1e-3 to 100 and exact zeros (lambda -> 0, e^{-x} underflow)."""
+    r = _rng(33)
+    H, T, dk, dv = 1, 20, 4, 3
+    kdir = r.standard_normal((1, H, T, dk))
+    kdir /= np.linalg.norm(kdir, axis=-1, keepdims=True)
+    norms = np.exp(r.uniform(np.log(1e-3), np.log(100.0), (1, H, T, 1)))
+    k = kdir * norms
+    k[0, 0, 4] = 0.0
+    q, v, do = r.standard_normal((1, H, T, dk)), r.standard_normal((1, H, T, dv)), r.standard_normal((1, H, T, dv))
+    beta = r.uniform(0.0, 1.0, (1, H, T))
+    g = O.backward(q, k, v, beta, do)
+    zero = np.zeros((1, H, dk, dv))
+    for name, x in dict(q=q, k=k, v=v, beta=beta).items():
+        for idx in [tuple(r.integers(0, s) for s in x.shape) for _ in range(15)]:
+            h = 1e-7 * max(1.0, abs(x[idx]))
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = dict(q=q, k=k, v=v, beta=beta)
+            lp = _loss(**{**a, name: xp}, do=do, dSF=zero, S0=None, scale=1.0)
+            lm = _loss(**{**a, name: xm}, do=do, dSF=zero, S0=None, scale=1.0)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g["d" + name][idx]) < 2e-5 * max(1.0, abs(fd)), (name, idx)
+
+
+# ---------------------------------------------------------------- stored regression case
+
+def test_golden_tiny_case_unchanged():
+    """tests/golden/tiny_case.json was written by tests/golden/make_golden.py from the oracle."""
+    with open(os.path.join(HERE, "golden", "tiny_case.json")) as f:
+        gold = json.load(f)
+    inp = {n: np.array(gold["inputs"][n]) for n in ("q", "k", "v", "beta", "do")}
+    o, _ = O.forward(inp["q"], inp["k"], inp["v"], inp["beta"], scale=gold["scale"])
+    g = O.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["do"], scale=gold["scale"])
+    assert np.allclose(o, np.array(gold["o"]), rtol=1e-13, atol=1e-14)
+    for name in ("dq", "dk", "dv", "dbeta"):
+        assert np.allclose(g[name], np.array(gold[name]), rtol=1e-12, atol=1e-14)
