@@ -1,0 +1,98 @@
+"""ctypes view of libefla.so (the C ABI declared in include/efla.h).
+
+Loading fails loudly when the library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libefla.so")
+
+EFLA_F32 = 0
+EFLA_BF16 = 1
+
+STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_NULL", 2: "EFLA_ERR_SHAPE", 3: "EFLA_ERR_DTYPE",
+          4: "EFLA_ERR_UNSUPPORTED", 5: "EFLA_ERR_WORKSPACE", 6: "EFLA_ERR_HIP",
+          7: "EFLA_ERR_ALIGN"}
+
+# Every symbol include/efla.h declares.
+EXPORTS = ["efla_abi_version", "efla_status_str", "efla_check_problem", "efla_workspace_bytes",
+           "efla_saved_bytes", "efla_get_saved_layout", "efla_prep", "efla_chunk_ut",
+           "efla_fwd", "efla_bwd", "efla_profile_enable", "efla_profile_read",
+           "efla_profile_reset"]
+
+
+class EflaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32)]
+
+
+class EflaSavedLayout(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_size_t), ("ut", ctypes.c_size_t), ("states", ctypes.c_size_t),
+                ("table", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("n_chunk_slots", ctypes.c_int64)]
+
+
+class EflaError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (fn, STATUS.get(code, "?"), code))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if libefla.so is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libefla.so is not built (%s); run python -m delta_rule_sequence_amd.build"
+                          % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(EflaProblem)
+    vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    L.efla_abi_version.restype = ctypes.c_int
+    L.efla_abi_version.argtypes = []
+    L.efla_status_str.restype = ctypes.c_char_p
+    L.efla_status_str.argtypes = [st]
+    L.efla_check_problem.restype = st
+    L.efla_check_problem.argtypes = [P]
+    L.efla_workspace_bytes.restype = sz
+    L.efla_workspace_bytes.argtypes = [P, ctypes.c_int]
+    L.efla_saved_bytes.restype = sz
+    L.efla_saved_bytes.argtypes = [P]
+    L.efla_get_saved_layout.restype = st
+    L.efla_get_saved_layout.argtypes = [P, ctypes.POINTER(EflaSavedLayout)]
+    L.efla_prep.restype = st
+    L.efla_prep.argtypes = [P, vp, vp, fp, fp, fp, fp, vp]
+    L.efla_chunk_ut.restype = st
+    L.efla_chunk_ut.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.efla_fwd.restype = st
+    L.efla_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.efla_bwd.restype = st
+    L.efla_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
+    L.efla_profile_enable.restype = st
+    L.efla_profile_enable.argtypes = [ctypes.c_int]
+    L.efla_profile_read.restype = ctypes.c_int
+    L.efla_profile_read.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    L.efla_profile_reset.restype = None
+    L.efla_profile_reset.argtypes = []
+    _lib = L
+    return L
+
+
+def check(fn, code):
+    if code != 0:
+        raise EflaError(fn, code)
+
+
+def problem(B, H, T, dk, dv, dtype, scale=1.0, cu_seqlens_ptr=None, n_seqs=0, chunk=64):
+    return EflaProblem(B, H, T, dk, dv, dtype, chunk, scale, cu_seqlens_ptr, n_seqs)

@@ -1,0 +1,68 @@
+"""Build libefla.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+    python -m delta_rule_sequence_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libefla.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+
+SOURCES = ["efla_api.hip", "efla_prep.hip", "efla_ut.hip", "efla_scan_fwd.hip",
+           "efla_scan_bwd.hip", "efla_chunk_bwd.hip"]
+
+# -packed-fp32-ops: keep hipcc from emitting packed fp32 vector instructions.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Wno-unused-function", "-Wno-unused-command-line-argument",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I" + os.path.join(ROOT, "include")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the EFLA library needs ROCm's hipcc to build")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "packed-fp32-ops"
+    msg = "\n".join(l for l in r.stdout.splitlines() if noise not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError("command failed: %s\n%s" % (" ".join(cmd), msg))
+    return msg
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libefla.so; returns its path."""
+    cc = hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
+
+    def compile_one(i):
+        src = os.path.join(CSRC, SOURCES[i])
+        return _run([cc] + FLAGS + ["-c", src, "-o", objs[i]])
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        logs = list(ex.map(compile_one, range(len(SOURCES))))
+    tmp = OUT + ".tmp%d" % os.getpid()
+    logs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
+    os.replace(tmp, OUT)
+    if verbose:
+        for l in logs:
+            if l:
+                print(l)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

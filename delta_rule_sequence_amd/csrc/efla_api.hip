@@ -1,0 +1,342 @@
+// C ABI of the EFLA library: argument validation, workspace layout, launch sequencing.
+// See include/efla.h for the contract of every entry point.
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "efla.h"
+#include "efla_internal.hpp"
+
+namespace efla {
+
+// ---------------------------------------------------------------------------
+// Profiling: events bracket each launch while enabled.
+// ---------------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_prof_free;
+std::vector<ProfRec> g_prof_pending;
+hipEvent_t g_prof_open = nullptr;
+std::map<std::string, std::pair<int64_t, double>> g_prof_totals;
+
+hipEvent_t prof_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void prof_drain() {
+  for (auto& r : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      auto& t = g_prof_totals[r.name];
+      t.first += 1;
+      t.second += ms;
+    }
+    g_prof_free.push_back(r.a);
+    g_prof_free.push_back(r.b);
+  }
+  g_prof_pending.clear();
+}
+}  // namespace
+
+void prof_begin(hipStream_t st) {
+  if (!g_prof_on) return;
+  g_prof_open = prof_event();
+  if (g_prof_open && hipEventRecord(g_prof_open, st) != hipSuccess) g_prof_open = nullptr;
+}
+
+void prof_end(const char* name, hipStream_t st) {
+  if (!g_prof_on || !g_prof_open) return;
+  hipEvent_t b = prof_event();
+  if (!b) return;
+  if (hipEventRecord(b, st) != hipSuccess) {
+    g_prof_free.push_back(b);
+    g_prof_free.push_back(g_prof_open);
+    g_prof_open = nullptr;
+    return;
+  }
+  g_prof_pending.push_back(ProfRec{name, g_prof_open, b});
+  g_prof_open = nullptr;
+  if (g_prof_pending.size() > 4096) prof_drain();
+}
+
+// ---------------------------------------------------------------------------
+// Validation and sizes.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool head_size_ok(int d) { return d == 64 || d == 128; }
+
+efla_status to_shape(const efla_problem* p, Shape& s) {
+  if (!p) return EFLA_ERR_NULL;
+  if (p->dtype != EFLA_F32 && p->dtype != EFLA_BF16) return EFLA_ERR_DTYPE;
+  if (p->B < 1 || p->H < 1 || p->T < 0 || p->dk < 1 || p->dv < 1) return EFLA_ERR_SHAPE;
+  if (p->cu_seqlens) {
+    if (p->B != 1 || p->n_seqs < 1) return EFLA_ERR_SHAPE;
+  } else if (p->n_seqs != 0 && p->n_seqs != p->B) {
+    return EFLA_ERR_SHAPE;
+  }
+  if (p->chunk != kChunk) return EFLA_ERR_UNSUPPORTED;
+  if (!head_size_ok(p->dk) || !head_size_ok(p->dv)) return EFLA_ERR_UNSUPPORTED;
+  const Dt dt = p->dtype == EFLA_BF16 ? Dt::BF16 : Dt::F32;
+  if (lds_ut_fwd(dt, p->dk, p->dv) == 0 || lds_chunk_bwd(dt, p->dk, p->dv) == 0)
+    return EFLA_ERR_UNSUPPORTED;
+  const int64_t tokens = (int64_t)p->B * p->H * p->T;
+  const int64_t dmax = p->dk > p->dv ? p->dk : p->dv;
+  if (tokens * dmax >= ((int64_t)1 << 40)) return EFLA_ERR_UNSUPPORTED;
+  s.B = p->B;
+  s.H = p->H;
+  s.T = p->T;
+  s.dk = p->dk;
+  s.dv = p->dv;
+  s.dt = dt;
+  s.scale = p->scale;
+  s.cu = p->cu_seqlens;
+  s.n_seqs = p->cu_seqlens ? p->n_seqs : p->B;
+  s.ntc = (p->T + kChunk - 1) / kChunk;
+  s.slots = p->cu_seqlens ? (int64_t)(p->T / kChunk) + p->n_seqs : (int64_t)p->B * s.ntc;
+  if (s.slots * p->H >= ((int64_t)1 << 31)) return EFLA_ERR_UNSUPPORTED;
+  return EFLA_OK;
+}
+
+size_t esize(const Shape& s) { return s.dt == Dt::BF16 ? 2 : 4; }
+size_t bytes_k(const Shape& s) { return (size_t)s.B * s.H * s.T * s.dk * esize(s); }
+size_t bytes_v(const Shape& s) { return (size_t)s.B * s.H * s.T * s.dv * esize(s); }
+size_t bytes_states(const Shape& s) { return (size_t)s.slots * s.H * s.dk * s.dv * esize(s); }
+size_t bytes_table(const Shape& s) { return s.cu ? (size_t)(s.n_seqs + 1) * 4 : 0; }
+
+// Layout of the forward->backward buffer.
+struct Saved {
+  size_t w, ut, states, table, total;
+};
+Saved saved_layout(const Shape& s) {
+  Saved L;
+  size_t o = 0;
+  L.w = o;
+  o += align_up(bytes_k(s));
+  L.ut = o;
+  o += align_up(bytes_v(s));
+  L.states = o;
+  o += align_up(bytes_states(s));
+  L.table = o;
+  o += align_up(bytes_table(s));
+  L.total = o;
+  return L;
+}
+
+// Forward workspace: U, plus W and the chunk table when no saved buffer is given.
+size_t ws_fwd(const Shape& s) {
+  return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s));
+}
+// Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer and U
+// for the recompute path.
+size_t ws_bwd(const Shape& s) {
+  return align_up(bytes_v(s)) + align_up(bytes_states(s)) + saved_layout(s).total +
+         align_up(bytes_v(s));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+efla_status hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
+
+bool empty(const Shape& s) { return s.T == 0; }
+
+// Forward stages shared by efla_fwd and the recompute path of efla_bwd.
+efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
+                        const void* beta, void* o, unsigned char* w, unsigned char* ut,
+                        unsigned char* states, int* table, unsigned char* u, hipStream_t st) {
+  if (s.cu) {
+    if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
+  }
+  if (efla_status r = hip_status(launch_ut_fwd(s, table, k, v, beta, w, u, st))) return r;
+  return hip_status(launch_scan_fwd(s, table, q, k, w, u, o, ut, states, st));
+}
+
+}  // namespace
+}  // namespace efla
+
+using namespace efla;
+
+extern "C" {
+
+int efla_abi_version(void) { return EFLA_ABI_VERSION; }
+
+const char* efla_status_str(efla_status s) {
+  switch (s) {
+    case EFLA_OK: return "ok";
+    case EFLA_ERR_NULL: return "a required pointer is NULL";
+    case EFLA_ERR_SHAPE: return "inconsistent problem sizes";
+    case EFLA_ERR_DTYPE: return "unknown dtype";
+    case EFLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case EFLA_ERR_WORKSPACE: return "workspace or saved buffer too small";
+    case EFLA_ERR_HIP: return "HIP launch failed";
+    case EFLA_ERR_ALIGN: return "data pointer not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+efla_status efla_check_problem(const efla_problem* p) {
+  Shape s;
+  return to_shape(p, s);
+}
+
+size_t efla_workspace_bytes(const efla_problem* p, int for_backward) {
+  Shape s;
+  if (to_shape(p, s) != EFLA_OK) return 0;
+  return for_backward ? ws_bwd(s) : ws_fwd(s);
+}
+
+size_t efla_saved_bytes(const efla_problem* p) {
+  Shape s;
+  if (to_shape(p, s) != EFLA_OK) return 0;
+  return saved_layout(s).total;
+}
+
+efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (!out) return EFLA_ERR_NULL;
+  const Saved L = saved_layout(s);
+  out->w = L.w;
+  out->ut = L.ut;
+  out->states = L.states;
+  out->table = L.table;
+  out->total = L.total;
+  out->n_chunk_slots = s.slots;
+  return EFLA_OK;
+}
+
+efla_status efla_prep(const efla_problem* p, const void* k, const void* beta, float* lam,
+                      float* alpha, float* dalpha_dbeta, float* dalpha_dlam, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (empty(s)) return EFLA_OK;
+  if (!k || !beta || !alpha) return EFLA_ERR_NULL;
+  if (!aligned16(k)) return EFLA_ERR_ALIGN;
+  return hip_status(launch_prep(s, k, beta, lam, alpha, dalpha_dbeta, dalpha_dlam,
+                                (hipStream_t)stream));
+}
+
+efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, const void* beta,
+                          void* w, void* u, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (empty(s)) return EFLA_OK;
+  if (!k || !v || !beta || !w || !u) return EFLA_ERR_NULL;
+  if (s.cu && !ws) return EFLA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) || !aligned16(ws))
+    return EFLA_ERR_ALIGN;
+  if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int* table = (int*)ws;
+  if (s.cu) {
+    if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
+  }
+  return hip_status(launch_ut_fwd(s, table, k, v, beta, w, u, st));
+}
+
+efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
+                     const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
+                     size_t ws_bytes, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (empty(s)) return EFLA_OK;
+  if (!q || !k || !v || !beta || !o || !ws) return EFLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(ws) ||
+      !aligned16(saved))
+    return EFLA_ERR_ALIGN;
+  if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
+  const Saved L = saved_layout(s);
+  if (saved && saved_bytes < L.total) return EFLA_ERR_WORKSPACE;
+  unsigned char* wsb = (unsigned char*)ws;
+  unsigned char* u = wsb;
+  unsigned char* w_ws = wsb + align_up(bytes_v(s));
+  int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
+  unsigned char* sv = (unsigned char*)saved;
+  unsigned char* w = sv ? sv + L.w : w_ws;
+  unsigned char* ut = sv ? sv + L.ut : nullptr;
+  unsigned char* states = sv ? sv + L.states : nullptr;
+  int* table = sv ? (int*)(sv + L.table) : table_ws;
+  return run_forward(s, q, k, v, beta, o, w, ut, states, table, u, (hipStream_t)stream);
+}
+
+efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
+                     const void* beta, const void* d_o, const void* saved, size_t saved_bytes,
+                     void* dq, void* dk, void* dv, void* dbeta, void* ws, size_t ws_bytes,
+                     void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (empty(s)) return EFLA_OK;
+  if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta || !ws) return EFLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(ws) || !aligned16(saved))
+    return EFLA_ERR_ALIGN;
+  const Saved L = saved_layout(s);
+  const size_t need = saved ? align_up(bytes_v(s)) + align_up(bytes_states(s)) : ws_bwd(s);
+  if (ws_bytes < need) return EFLA_ERR_WORKSPACE;
+  if (saved && saved_bytes < L.total) return EFLA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* wsb = (unsigned char*)ws;
+  unsigned char* dut = wsb;
+  unsigned char* dstates = dut + align_up(bytes_v(s));
+  const unsigned char* sv = (const unsigned char*)saved;
+  if (!sv) {
+    unsigned char* rec = dstates + align_up(bytes_states(s));
+    unsigned char* u = rec + L.total;
+    if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
+                                    rec + L.states, (int*)(rec + L.table), u, st))
+      return r;
+    sv = rec;
+  }
+  const int* table = (const int*)(sv + L.table);
+  if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, d_o, dut, dstates, st)))
+    return r;
+  return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
+                                     dstates, dq, dk, dv, dbeta, st));
+}
+
+efla_status efla_profile_enable(int on) {
+  if (!on) prof_drain();
+  g_prof_on = on != 0;
+  return EFLA_OK;
+}
+
+int efla_profile_read(char* names, int name_stride, int64_t* counts, double* total_ms,
+                      int max_kernels) {
+  prof_drain();
+  int i = 0;
+  for (auto& kv : g_prof_totals) {
+    if (i >= max_kernels) break;
+    if (names && name_stride > 0) {
+      strncpy(names + (size_t)i * name_stride, kv.first.c_str(), (size_t)name_stride - 1);
+      names[(size_t)i * name_stride + name_stride - 1] = '\0';
+    }
+    if (counts) counts[i] = kv.second.first;
+    if (total_ms) total_ms[i] = kv.second.second;
+    ++i;
+  }
+  return i;
+}
+
+void efla_profile_reset(void) {
+  prof_drain();
+  g_prof_totals.clear();
+}
+
+}  // extern "C"

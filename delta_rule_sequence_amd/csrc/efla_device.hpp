@@ -1,0 +1,423 @@
+// Device-side building blocks shared by the EFLA kernels (gfx950 / CDNA4).
+//
+// Every kernel runs 256 threads = 4 wavefronts of 64 lanes. Dense contractions use
+// 16x16 MFMA tiles: v_mfma_f32_16x16x32_bf16 for bf16 problems and
+// v_mfma_f32_16x16x4_f32 for fp32 problems, always accumulating in fp32.
+//
+// Operand convention for a 16x16 output tile C = A * B:
+//   A is read as 16 rows of A (row-major, the contraction index contiguous),
+//   B is read as 16 rows of B^T (row-major, the contraction index contiguous).
+//   Lane l reads row (l & 15) and 16 contiguous bytes of the contraction range
+//   starting at (l >> 4) * KC/4 inside each KC-wide step. A and B use the same
+//   mapping, so each k-slot pairs the same contraction index in both operands.
+//   The accumulator element i of lane l is C[4 * (l >> 4) + i][l & 15].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace efla {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 64;
+constexpr int kThreads = 256;
+
+#define EFLA_DEV __device__ __forceinline__
+
+template <typename E> EFLA_DEV E to_e(float x);
+template <> EFLA_DEV float to_e<float>(float x) { return x; }
+template <> EFLA_DEV __bf16 to_e<__bf16>(float x) { return (__bf16)x; }
+EFLA_DEV float to_f(float x) { return x; }
+EFLA_DEV float to_f(__bf16 x) { return (float)x; }
+
+EFLA_DEV f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row pitch (in elements) of an LDS tile whose rows hold `cols` elements: 16 bytes of
+// padding per row spreads consecutive rows over different LDS banks.
+template <typename E> constexpr int pitch(int cols) { return cols + 16 / (int)sizeof(E); }
+constexpr int kPitchF = 68;  // fp32 64x64 work matrices
+
+// ---------------------------------------------------------------------------
+// MFMA step: one 16-byte operand load per lane covers KC contraction indices.
+// ---------------------------------------------------------------------------
+template <typename E> struct Mma;
+
+template <> struct Mma<float> {
+  static constexpr int KC = 16;  // 4 fp32 per lane x 4 lane groups
+  typedef f32x4 vec;
+  EFLA_DEV static f32x4 step(vec a, vec b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+  }
+};
+
+template <> struct Mma<__bf16> {
+  static constexpr int KC = 32;  // 8 bf16 per lane x 4 lane groups
+  typedef bf16x8 vec;
+  EFLA_DEV static f32x4 step(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename E> EFLA_DEV constexpr int round_down_kc(int k) { return k - k % Mma<E>::KC; }
+template <typename E> EFLA_DEV constexpr int round_up_kc(int k) {
+  return (k + Mma<E>::KC - 1) / Mma<E>::KC * Mma<E>::KC;
+}
+
+// acc += A[0:16, k0:k1] * B[k0:k1, 0:16]; `a` points at row 0 of A (pitch lda), `bt` at
+// row 0 of B^T (pitch ldb). k0 and k1 are multiples of Mma<E>::KC. Works on LDS and
+// global pointers alike.
+template <typename E>
+EFLA_DEV f32x4 mma16(const E* a, int lda, const E* bt, int ldb, int k0, int k1, f32x4 acc,
+                     int lane) {
+  typedef typename Mma<E>::vec V;
+  const int r = lane & 15;
+  const int kq = (lane >> 4) * (Mma<E>::KC / 4);
+  const E* pa = a + r * lda + kq;
+  const E* pb = bt + r * ldb + kq;
+  for (int k = k0; k < k1; k += Mma<E>::KC)
+    acc = Mma<E>::step(*(const V*)(pa + k), *(const V*)(pb + k), acc);
+  return acc;
+}
+
+// Same with B^T in global memory addressed with a 64-bit pitch.
+template <typename E>
+EFLA_DEV f32x4 mma16_gb(const E* a, int lda, const E* __restrict__ bt, int64_t ldb, int k0, int k1,
+                        f32x4 acc, int lane) {
+  typedef typename Mma<E>::vec V;
+  const int r = lane & 15;
+  const int kq = (lane >> 4) * (Mma<E>::KC / 4);
+  const E* pa = a + r * lda + kq;
+  const E* pb = bt + r * ldb + kq;
+  for (int k = k0; k < k1; k += Mma<E>::KC)
+    acc = Mma<E>::step(*(const V*)(pa + k), *(const V*)(pb + k), acc);
+  return acc;
+}
+
+// Store an accumulator tile transposed: s[n][m] = C[m][n] (s points at the tile origin of
+// C^T, pitch ld). Four consecutive m per lane become one 8- or 16-byte store.
+template <typename E> EFLA_DEV void st_frag_t(E* s, int ld, f32x4 c, int lane);
+template <> EFLA_DEV void st_frag_t<float>(float* s, int ld, f32x4 c, int lane) {
+  *(f32x4*)(s + (lane & 15) * ld + 4 * (lane >> 4)) = c;
+}
+template <> EFLA_DEV void st_frag_t<__bf16>(__bf16* s, int ld, f32x4 c, int lane) {
+  bf16x4 v = {(__bf16)c[0], (__bf16)c[1], (__bf16)c[2], (__bf16)c[3]};
+  *(bf16x4*)(s + (lane & 15) * ld + 4 * (lane >> 4)) = v;
+}
+
+// Store an accumulator tile row-major into LDS: s[m][n] = C[m][n]. The stores are
+// volatile so that the backend never pairs them into ds_write2_b32: the ROCm 7.2 LLVM
+// backend was seen to emit such a pair with a wrong offset for MFMA results
+// (offset0 scaled down by four), which silently corrupted the tile.
+template <typename E>
+EFLA_DEV void st_frag_lds(E* s, int ld, f32x4 c, int lane) {
+  volatile E* p = s + 4 * (lane >> 4) * ld + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i * ld] = to_e<E>(c[i]);
+}
+
+// Store an accumulator tile row-major to global memory: g[m][n] = C[m][n].
+template <typename E>
+EFLA_DEV void st_frag_glb(E* __restrict__ g, int64_t ld, f32x4 c, int lane) {
+  E* p = g + (int64_t)(4 * (lane >> 4)) * ld + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i * ld] = to_e<E>(c[i]);
+}
+
+// Row-major store to global memory keeping only rows < nvalid (relative to the tile origin).
+template <typename E>
+EFLA_DEV void st_frag_rows(E* __restrict__ g, int64_t ld, f32x4 c, int lane, int row0, int nvalid) {
+  const int rb = 4 * (lane >> 4);
+  E* p = g + (int64_t)rb * ld + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (row0 + rb + i < nvalid) p[i * ld] = to_e<E>(c[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS tile copies (64 rows, rows >= nvalid read as zero).
+// ---------------------------------------------------------------------------
+template <typename E, int COLS>
+EFLA_DEV void g2s(E* s, int ld, const E* __restrict__ g, int64_t gld, int nvalid, int tid) {
+  constexpr int V = 16 / sizeof(E);
+  constexpr int VPR = COLS / V;
+  constexpr int TOT = kChunk * VPR;
+#pragma unroll
+  for (int it = 0; it < (TOT + kThreads - 1) / kThreads; ++it) {
+    const int i = it * kThreads + tid;
+    if (TOT % kThreads == 0 || i < TOT) {
+      const int r = i / VPR, c = (i % VPR) * V;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nvalid) val = *(const uint4*)(g + (int64_t)r * gld + c);
+      *(uint4*)(s + r * ld + c) = val;
+    }
+  }
+}
+
+// Transposed copy: s[c][r] = g[r][c] for r < 64, c < COLS.
+template <typename E, int COLS>
+EFLA_DEV void g2s_t(E* s, int ld, const E* __restrict__ g, int64_t gld, int nvalid, int tid);
+
+template <int COLS>
+EFLA_DEV void g2s_t_impl_f32(float* s, int ld, const float* __restrict__ g, int64_t gld, int nvalid,
+                             int tid) {
+  constexpr int VPR = COLS / 4;
+  constexpr int TOT = kChunk * VPR;
+#pragma unroll
+  for (int it = 0; it < (TOT + kThreads - 1) / kThreads; ++it) {
+    const int i = it * kThreads + tid;
+    if (TOT % kThreads == 0 || i < TOT) {
+      const int r = i % kChunk, c = (i / kChunk) * 4;
+      f32x4 val = zero4();
+      if (r < nvalid) val = *(const f32x4*)(g + (int64_t)r * gld + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[(c + e) * ld + r] = val[e];
+    }
+  }
+}
+
+template <int COLS>
+EFLA_DEV void g2s_t_impl_bf16(__bf16* s, int ld, const __bf16* __restrict__ g, int64_t gld,
+                              int nvalid, int tid) {
+  // Each thread moves two rows x 8 columns and writes eight 4-byte row pairs.
+  constexpr int VPR = COLS / 8;
+  constexpr int TOT = (kChunk / 2) * VPR;
+#pragma unroll
+  for (int it = 0; it < (TOT + kThreads - 1) / kThreads; ++it) {
+    const int i = it * kThreads + tid;
+    if (TOT % kThreads == 0 || i < TOT) {
+      const int rp = i % (kChunk / 2), c = (i / (kChunk / 2)) * 8;
+      const int r = 2 * rp;
+      bf16x8 v0, v1;
+      for (int e = 0; e < 8; ++e) { v0[e] = (__bf16)0.f; v1[e] = (__bf16)0.f; }
+      if (r < nvalid) v0 = *(const bf16x8*)(g + (int64_t)r * gld + c);
+      if (r + 1 < nvalid) v1 = *(const bf16x8*)(g + (int64_t)(r + 1) * gld + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x2 pr = {v0[e], v1[e]};
+        *(bf16x2*)(s + (c + e) * ld + r) = pr;
+      }
+    }
+  }
+}
+
+template <typename E, int COLS>
+EFLA_DEV void g2s_t(E* s, int ld, const E* __restrict__ g, int64_t gld, int nvalid, int tid) {
+  if constexpr (sizeof(E) == 4)
+    g2s_t_impl_f32<COLS>((float*)s, ld, (const float*)g, gld, nvalid, tid);
+  else
+    g2s_t_impl_bf16<COLS>((__bf16*)s, ld, (const __bf16*)g, gld, nvalid, tid);
+}
+
+// Copy 64 rows of an LDS tile to global memory with 16-byte stores, rows < nvalid only.
+template <typename E, int COLS>
+EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid, int tid) {
+  constexpr int V = 16 / sizeof(E);
+  constexpr int VPR = COLS / V;
+  constexpr int TOT = kChunk * VPR;
+#pragma unroll
+  for (int it = 0; it < (TOT + kThreads - 1) / kThreads; ++it) {
+    const int i = it * kThreads + tid;
+    if (TOT % kThreads == 0 || i < TOT) {
+      const int r = i / VPR, c = (i % VPR) * V;
+      if (r < nvalid) *(uint4*)(g + (int64_t)r * gld + c) = *(const uint4*)(s + r * ld + c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token coefficients of the exact flow.
+//   x = beta * lambda, phi(x) = (1 - e^-x) / x,
+//   alpha = beta phi(x), d alpha / d beta = e^-x, d alpha / d lambda = beta^2 phi'(x).
+// For |x| < 1 phi and phi' are Taylor polynomials (degree 11; truncation < 2e-10
+// relative), which avoids the cancellation of the closed forms near zero; elsewhere
+// the closed forms with expm1 are used. Overflow for large negative x follows IEEE.
+// ---------------------------------------------------------------------------
+struct FlowCoef {
+  float alpha, ex, dlam;
+};
+
+EFLA_DEV FlowCoef flow_coef(float beta, float lam) {
+  const float x = beta * lam;
+  float ph, dph;
+  const float ex = expf(-x);
+  if (fabsf(x) < 1.0f) {
+    // phi(x)  = sum_{n>=0} (-1)^n x^n / (n+1)!
+    ph = -1.0f / 479001600.0f;
+    ph = fmaf(ph, x, 1.0f / 39916800.0f);
+    ph = fmaf(ph, x, -1.0f / 3628800.0f);
+    ph = fmaf(ph, x, 1.0f / 362880.0f);
+    ph = fmaf(ph, x, -1.0f / 40320.0f);
+    ph = fmaf(ph, x, 1.0f / 5040.0f);
+    ph = fmaf(ph, x, -1.0f / 720.0f);
+    ph = fmaf(ph, x, 1.0f / 120.0f);
+    ph = fmaf(ph, x, -1.0f / 24.0f);
+    ph = fmaf(ph, x, 1.0f / 6.0f);
+    ph = fmaf(ph, x, -0.5f);
+    ph = fmaf(ph, x, 1.0f);
+    // phi'(x) = sum_{n>=0} (n+1) (-1)^(n+1) x^n / (n+2)!
+    dph = 1.0f / 518918400.0f;
+    dph = fmaf(dph, x, -1.0f / 43545600.0f);
+    dph = fmaf(dph, x, 1.0f / 3991680.0f);
+    dph = fmaf(dph, x, -1.0f / 403200.0f);
+    dph = fmaf(dph, x, 1.0f / 45360.0f);
+    dph = fmaf(dph, x, -1.0f / 5760.0f);
+    dph = fmaf(dph, x, 1.0f / 840.0f);
+    dph = fmaf(dph, x, -1.0f / 144.0f);
+    dph = fmaf(dph, x, 1.0f / 30.0f);
+    dph = fmaf(dph, x, -1.0f / 8.0f);
+    dph = fmaf(dph, x, 1.0f / 3.0f);
+    dph = fmaf(dph, x, -0.5f);
+  } else {
+    ph = -expm1f(-x) / x;
+    dph = (ex * (1.0f + x) - 1.0f) / (x * x);
+  }
+  return FlowCoef{beta * ph, ex, beta * beta * dph};
+}
+
+// ---------------------------------------------------------------------------
+// Chunk geometry. A "sequence" is one batch row (dense) or one packed segment.
+// Chunk slots number the chunks of all sequences: slot = b * ntc + c (dense) or
+// table[s] + c (packed), with table[s] = sum of ceil(len/64) over earlier sequences.
+// ---------------------------------------------------------------------------
+struct Geom {
+  int B, H, T;
+  int n_seqs;          // B for dense batches
+  int ntc;             // ceil(T / 64) for dense batches
+  const int* cu;       // packed: cu_seqlens, else nullptr
+  const int* table;    // packed: chunk start table [n_seqs + 1], else nullptr
+  int max_slots;       // chunk slots the state buffers hold per head
+  float scale;
+};
+
+struct SeqInfo {
+  int b, bos, len, slot0;
+};
+
+// Offsets are clamped into [0, T] so that a malformed cu_seqlens cannot send a kernel
+// outside the tensors (the result is then meaningless but memory stays in bounds).
+EFLA_DEV int clamp_t(const Geom& g, int x) { return min(max(x, 0), g.T); }
+
+EFLA_DEV SeqInfo seq_info(const Geom& g, int s) {
+  if (g.cu) {
+    const int bos = clamp_t(g, g.cu[s]);
+    const int end = max(clamp_t(g, g.cu[s + 1]), bos);
+    return SeqInfo{0, bos, end - bos, g.table[s]};
+  }
+  return SeqInfo{s, 0, g.T, s * g.ntc};
+}
+
+// Number of chunks of a sequence that fit in the state buffers.
+EFLA_DEV int seq_chunks(const Geom& g, const SeqInfo& si) {
+  const int nc = (si.len + kChunk - 1) / kChunk;
+  return max(0, min(nc, g.max_slots - si.slot0));
+}
+
+struct ChunkInfo {
+  int b, t0, n;   // batch row, first token (absolute T index), valid rows
+};
+
+// Returns false when the slot is past the last chunk of a packed batch.
+EFLA_DEV bool chunk_info(const Geom& g, int slot, ChunkInfo& ci) {
+  if (!g.cu) {
+    const int c = slot % g.ntc;
+    ci.b = slot / g.ntc;
+    ci.t0 = c * kChunk;
+    ci.n = min(kChunk, g.T - ci.t0);
+    return true;
+  }
+  if (slot >= g.max_slots || slot >= g.table[g.n_seqs]) return false;
+  int lo = 0, hi = g.n_seqs - 1;  // largest s with table[s] <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.table[mid] <= slot) lo = mid; else hi = mid - 1;
+  }
+  const SeqInfo si = seq_info(g, lo);
+  const int c = slot - si.slot0;
+  ci.b = 0;
+  ci.t0 = si.bos + c * kChunk;
+  ci.n = min(kChunk, si.len - c * kChunk);
+  return ci.n > 0;
+}
+
+// Map a linear workgroup id to (sequence*H + head, d_v tile) so that the tiles of one
+// (sequence, head) land on the same XCD (workgroups are dealt to the 8 XCDs round-robin)
+// and share its L2 for the K, Q, W tiles they all read.
+EFLA_DEV void scan_block(int bid, int nsh, int ntile, int& sh, int& tile) {
+  if (nsh % 8 == 0) {
+    const int xcd = bid & 7, local = bid >> 3;
+    sh = (local / ntile) * 8 + xcd;
+    tile = local % ntile;
+  } else {
+    sh = bid / ntile;
+    tile = bid % ntile;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// X = (I + A)^{-1} for a strictly lower triangular 64x64 fp32 A (LDS, pitch kPitchF).
+// Blocked forward substitution: the four 16x16 diagonal blocks by column substitution
+// (one wave each), then the off-diagonal blocks by block distance,
+//   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
+// scr: 4 x 16 x 20 floats of wave-private scratch. All 256 threads must call it.
+// ---------------------------------------------------------------------------
+EFLA_DEV void invert_unit_lower64(const float* sA, float* sX, float* scr, int tid) {
+  constexpr int ld = kPitchF;
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < 64 * 64; i += kThreads) {
+    const int r = i >> 6, c = i & 63;
+    if ((c >> 4) > (r >> 4)) sX[r * ld + c] = 0.f;
+  }
+  if (lane < 16) {
+    const int o = wv * 16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s = fmaf(-sA[(o + r) * ld + o + m], x[m], s);
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sX[(o + r) * ld + o + lane] = x[r];
+  }
+  __syncthreads();
+  const int r = lane >> 2, c4 = (lane & 3) * 4;
+  float* my = scr + wv * 16 * 20;
+  for (int d = 1; d < 4; ++d) {
+    const bool act = wv < 4 - d;
+    const int bi = wv + d, bj = wv;
+    if (act) {
+      f32x4 p = zero4();
+      for (int kb = bj; kb < bi; ++kb) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const float a = sA[(16 * bi + r) * ld + 16 * kb + m];
+          const f32x4 xv = *(const f32x4*)(sX + (16 * kb + m) * ld + 16 * bj + c4);
+          p += a * xv;
+        }
+      }
+      *(f32x4*)(my + r * 20 + c4) = p;
+    }
+    __syncthreads();
+    if (act) {
+      f32x4 q = zero4();
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float xi = sX[(16 * bi + r) * ld + 16 * bi + m];
+        q += xi * *(const f32x4*)(my + m * 20 + c4);
+      }
+      *(f32x4*)(sX + (16 * bi + r) * ld + 16 * bj + c4) = -q;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace efla

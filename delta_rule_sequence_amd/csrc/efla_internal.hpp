@@ -1,0 +1,70 @@
+// Host-side declarations shared by the EFLA launch code (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "efla_device.hpp"
+
+namespace efla {
+
+enum class Dt { F32 = 0, BF16 = 1 };
+
+// Problem sizes as the launchers see them.
+struct Shape {
+  int B, H, T, dk, dv;
+  Dt dt;
+  float scale;
+  const int* cu;   // device cu_seqlens or nullptr (then B == 1)
+  int n_seqs;      // sequences (B for dense batches)
+  int ntc;         // ceil(T/64) (dense)
+  int64_t slots;   // chunk slots per head (upper bound for packed batches)
+};
+
+// Optional per-kernel timing (efla_profile_enable): events recorded on the launch stream
+// before and after each kernel. No-ops while profiling is off.
+void prof_begin(hipStream_t st);
+void prof_end(const char* name, hipStream_t st);
+
+// Launchers. Each returns the HIP status of the launch.
+hipError_t launch_chunk_table(const Shape& s, int* table, hipStream_t st);
+hipError_t launch_prep(const Shape& s, const void* k, const void* beta, float* lam, float* alpha,
+                       float* ex, float* dlam, hipStream_t st);
+hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* k, const void* v,
+                         const void* beta, void* w, void* u, hipStream_t st);
+hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
+                           const void* w, const void* u, void* o, void* ut, void* states,
+                           hipStream_t st);
+hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
+                           const void* w, const void* d_o, void* dut, void* dstates,
+                           hipStream_t st);
+hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, const void* k,
+                            const void* v, const void* beta, const void* d_o, const void* ut,
+                            const void* dut, const void* states, const void* dstates, void* dq,
+                            void* dk, void* dv, void* dbeta, hipStream_t st);
+
+// Dynamic LDS bytes of each kernel for a head-size pair (0 = combination not built).
+size_t lds_ut_fwd(Dt dt, int dk, int dv);
+size_t lds_scan_fwd(Dt dt, int dk, int dv);
+size_t lds_scan_bwd(Dt dt, int dk, int dv);
+size_t lds_chunk_bwd(Dt dt, int dk, int dv);
+
+inline Geom make_geom(const Shape& s, const int* table) {
+  Geom g;
+  g.B = s.B;
+  g.H = s.H;
+  g.T = s.T;
+  g.n_seqs = s.n_seqs;
+  g.ntc = s.ntc;
+  g.cu = s.cu;
+  g.table = s.cu ? table : nullptr;
+  g.max_slots = (int)s.slots;
+  g.scale = s.scale;
+  return g;
+}
+
+// Width of the d_v slice one scan workgroup owns.
+inline int scan_tile(int dv) { return dv / 4; }
+
+}  // namespace efla

@@ -1,0 +1,198 @@
+"""PyTorch binding of the EFLA C ABI: argument marshalling only.
+
+Tensors are only allocated here (outputs, workspaces) and handed to libefla.so
+as device pointers together with torch's current HIP stream; every step of the
+computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.EFLA_F32, torch.bfloat16: _lib.EFLA_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None):
+    """Build the efla_problem for tensors q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T]."""
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError("k and v must be [B, H, T, d]")
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    if k.dtype not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", None), (v, "v", (B, H, T, dv)),
+                      (beta, "beta", (B, H, T))):
+        _need(t, n, k.dtype, shp)
+    n_seqs, cu_ptr = 0, None
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        n_seqs = cu_seqlens.numel() - 1
+        cu_ptr = cu_seqlens.data_ptr()
+    return _lib.problem(B, H, T, dk, dv, _DT[k.dtype], float(scale), cu_ptr, n_seqs)
+
+
+def efla_workspace_bytes(p, for_backward: bool) -> int:
+    return int(_lib.lib().efla_workspace_bytes(ctypes.byref(p), 1 if for_backward else 0))
+
+
+def efla_saved_bytes(p) -> int:
+    return int(_lib.lib().efla_saved_bytes(ctypes.byref(p)))
+
+
+def efla_get_saved_layout(p) -> dict:
+    out = _lib.EflaSavedLayout()
+    _lib.check("efla_get_saved_layout", _lib.lib().efla_get_saved_layout(ctypes.byref(p), ctypes.byref(out)))
+    return dict(w=out.w, ut=out.ut, states=out.states, table=out.table, total=out.total,
+                n_chunk_slots=out.n_chunk_slots)
+
+
+def _bytes(n, device):
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def efla_prep(k, beta):
+    """Per-token coefficients: dict(lam, alpha, dalpha_dbeta, dalpha_dlam), fp32 [B,H,T]."""
+    if k.dim() != 4 or k.dtype not in _DT:
+        raise ValueError("k must be [B, H, T, dk] float32 or bfloat16")
+    B, H, T, dk = k.shape
+    _need(k, "k", k.dtype)
+    _need(beta, "beta", k.dtype, (B, H, T))
+    p = _lib.problem(B, H, T, dk, dk, _DT[k.dtype])
+    out = {n: torch.empty((B, H, T), dtype=torch.float32, device=k.device)
+           for n in ("lam", "alpha", "dalpha_dbeta", "dalpha_dlam")}
+
+    def fptr(t):
+        return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
+    _lib.check("efla_prep", _lib.lib().efla_prep(ctypes.byref(p), _ptr(k), _ptr(beta), fptr(out["lam"]),
+                                                fptr(out["alpha"]), fptr(out["dalpha_dbeta"]),
+                                                fptr(out["dalpha_dlam"]), _stream()))
+    return out
+
+
+def efla_chunk_ut(k, v, beta, cu_seqlens=None):
+    """UT transform of every chunk: (W [B,H,T,dk], U [B,H,T,dv]) in the input dtype."""
+    p = make_problem(k, k, v, beta, 1.0, cu_seqlens)
+    w = torch.empty_like(k)
+    u = torch.empty_like(v)
+    ws_n = efla_workspace_bytes(p, False)
+    ws = _bytes(ws_n, k.device)
+    _lib.check("efla_chunk_ut", _lib.lib().efla_chunk_ut(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(beta),
+                                                        _ptr(w), _ptr(u), _ptr(ws), ws_n, _stream()))
+    return w, u
+
+
+def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None):
+    """Forward. Returns (o, saved) where saved is the uint8 buffer for efla_bwd (or None)."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens)
+    o = torch.empty_like(v)
+    saved = _bytes(efla_saved_bytes(p), k.device) if save else None
+    ws_n = efla_workspace_bytes(p, False)
+    if ws is None or ws.numel() < ws_n:
+        ws = _bytes(ws_n, k.device)
+    _lib.check("efla_fwd", _lib.lib().efla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                              _ptr(o), _ptr(saved), 0 if saved is None else saved.numel(),
+                                              _ptr(ws), ws.numel(), _stream()))
+    return o, saved
+
+
+def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None):
+    """Backward of sum(o * d_o): (dq, dk, dv, dbeta) in the input dtype."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens)
+    _need(d_o, "d_o", v.dtype, v.shape)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    ws_n = efla_workspace_bytes(p, True)
+    if ws is None or ws.numel() < ws_n:
+        ws = _bytes(ws_n, k.device)
+    _lib.check("efla_bwd", _lib.lib().efla_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                              _ptr(d_o), _ptr(saved), 0 if saved is None else saved.numel(),
+                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(ws),
+                                              ws.numel(), _stream()))
+    return dq, dk, dv, dbeta
+
+
+def saved_views(saved, q, k, v, beta, scale=1.0, cu_seqlens=None):
+    """Tensor views of a saved buffer: W [B,H,T,dk], U~ [B,H,T,dv], states [slots,H,dk,dv]."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens)
+    L = efla_get_saved_layout(p)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    es = k.element_size()
+
+    def view(off, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        return saved[off:off + n * es].view(k.dtype).view(*shape)
+    return dict(w=view(L["w"], (B, H, T, dk)), ut=view(L["ut"], (B, H, T, dv)),
+                states=view(L["states"], (L["n_chunk_slots"], H, dk, dv)))
+
+
+class EflaFunction(torch.autograd.Function):
+    """o = EFLA(q, k, v, beta); the backward runs the library's backward kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, scale, cu_seqlens):
+        q, k, v, beta = (t.contiguous() for t in (q, k, v, beta))
+        o, saved = efla_fwd(q, k, v, beta, scale, cu_seqlens, save=True)
+        ctx.save_for_backward(q, k, v, beta, saved, cu_seqlens)
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, beta, saved, cu = ctx.saved_tensors
+        dq, dk, dv, dbeta = efla_bwd(q, k, v, beta, d_o.contiguous(), saved, ctx.scale, cu)
+        return dq, dk, dv, dbeta, None, None
+
+
+def efla(q, k, v, beta, scale: float = 1.0, cu_seqlens: Optional[torch.Tensor] = None):
+    """Exact Flow Linear Attention token mixer: o [B,H,T,dv], differentiable."""
+    return EflaFunction.apply(q, k, v, beta, scale, cu_seqlens)
+
+
+def profile_enable(on: bool):
+    _lib.check("efla_profile_enable", _lib.lib().efla_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _lib.lib().efla_profile_reset()
+
+
+def profile_read(max_kernels: int = 32) -> dict:
+    """{kernel name: (launches, total ms)} since the last reset."""
+    stride = 64
+    names = ctypes.create_string_buffer(stride * max_kernels)
+    counts = (ctypes.c_int64 * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    n = _lib.lib().efla_profile_read(names, stride, counts, ms, max_kernels)
+    out = {}
+    for i in range(n):
+        nm = names.raw[i * stride:(i + 1) * stride].split(b"\0", 1)[0].decode()
+        out[nm] = (int(counts[i]), float(ms[i]))
+    return out

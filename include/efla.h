@@ -1,0 +1,150 @@
+/*
+ * efla.h - C ABI of the Exact Flow Linear Attention (EFLA) library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (Exact Flow Linear Attention summary page, sections 3.1-3.3;
+ * the pages print no equation, this is the plain reading of what they state):
+ * for every sequence and head, with a d_k x d_v state S starting at zero,
+ *
+ *   lambda_t = k_t . k_t                                  (key energy, section 3.4)
+ *   alpha_t  = (1 - exp(-beta_t lambda_t)) / lambda_t      (alpha_t = beta_t if lambda_t = 0)
+ *   S_t      = S_{t-1} + alpha_t k_t (v_t - S_{t-1}^T k_t)^T   (exact ZOH flow of
+ *              dS/dtau = -k k^T S + k v^T over tau in [0, beta_t]; sections 3.1, 3.2)
+ *   o_t      = scale * S_t^T q_t                           (read after the update)
+ *
+ * computed chunkwise (64 tokens) with the UT transform of section 3.3:
+ *   T = (I + strictly_lower(diag(alpha) K K^T))^{-1} diag(alpha),  W = T K,  U = T V,
+ *   U~ = U - W S,  O = scale (Q S + tril(Q K^T) U~),  S <- S + K^T U~.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense, contiguous, head-first: q, k [B,H,T,dk]; v, o, do [B,H,T,dv];
+ *    beta [B,H,T]. They hold elements of the problem dtype (fp32 or bf16).
+ *    Accumulation is always fp32.
+ *  - Every data pointer is a DEVICE pointer, 16-byte aligned, owned by the caller.
+ *    The library never allocates or frees device memory and never synchronises;
+ *    it enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *  - All arguments are validated on the host before anything is enqueued. On an
+ *    error nothing is launched and no output is written. A failed launch returns
+ *    EFLA_ERR_HIP (outputs are then unspecified). No C++ exception crosses the ABI.
+ *  - Packed batches: when `cu_seqlens` (device int32 [n_seqs+1]) is set, B must be 1,
+ *    the T axis holds n_seqs sequences back to back, and the state restarts at every
+ *    offset. Its contents must satisfy 0 = cu[0] <= cu[1] <= ... <= cu[n_seqs] = T;
+ *    that is the caller's contract and is not checked (it lives on the device).
+ *  - Supported: chunk = 64; dk, dv in {64, 128}; bf16 with any of those, fp32 with
+ *    dk = dv = 64. Other sizes return EFLA_ERR_UNSUPPORTED.
+ *  - Calls on different streams that share a workspace or saved buffer race.
+ */
+#ifndef EFLA_H
+#define EFLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EFLA_ABI_VERSION 1
+
+typedef enum {
+  EFLA_OK = 0,
+  EFLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  EFLA_ERR_SHAPE = 2,       /* inconsistent sizes (negative, B != 1 with cu_seqlens, ...) */
+  EFLA_ERR_DTYPE = 3,       /* dtype is not EFLA_F32 / EFLA_BF16 */
+  EFLA_ERR_UNSUPPORTED = 4, /* valid but not implemented (chunk != 64, head size, ...) */
+  EFLA_ERR_WORKSPACE = 5,   /* workspace or saved buffer smaller than required */
+  EFLA_ERR_HIP = 6,         /* a HIP launch failed */
+  EFLA_ERR_ALIGN = 7        /* a data pointer is not 16-byte aligned */
+} efla_status;
+
+typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
+
+typedef struct {
+  int32_t B, H, T, dk, dv;      /* q,k: [B,H,T,dk]; v,o: [B,H,T,dv]; beta: [B,H,T] */
+  int32_t dtype;                /* efla_dtype of q, k, v, beta, o, do and every gradient */
+  int32_t chunk;                /* must be 64 */
+  float scale;                  /* multiplies the read-out: o_t = scale * S_t^T q_t */
+  const int32_t* cu_seqlens;    /* device pointer or NULL (see packed batches above) */
+  int32_t n_seqs;               /* number of packed sequences when cu_seqlens is set */
+} efla_problem;
+
+/* Byte offsets of the tensors inside the buffer that efla_fwd saves for efla_bwd.
+ *   w      : W = T K per chunk, [B,H,T,dk], problem dtype
+ *   ut     : U~ = U - W S per chunk, [B,H,T,dv], problem dtype
+ *   states : state entering each chunk, [n_chunk_slots][H][dk][dv], problem dtype;
+ *            slot = b * ceil(T/64) + c (dense batch) or chunk_start[s] + c (packed),
+ *            where chunk_start[s] = sum over earlier sequences of ceil(len/64)
+ *   table  : chunk_start, int32 [n_seqs+1] (packed batches only, else unused)
+ *   total  : size of the whole buffer = efla_saved_bytes()                               */
+typedef struct {
+  size_t w, ut, states, table, total;
+  int64_t n_chunk_slots;
+} efla_saved_layout;
+
+/* Library ABI version (EFLA_ABI_VERSION of the build). */
+int efla_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* efla_status_str(efla_status s);
+
+/* Validate a problem without launching anything. */
+efla_status efla_check_problem(const efla_problem* p);
+
+/* Device workspace that efla_fwd (for_backward = 0) or efla_bwd (for_backward = 1)
+ * needs, in bytes; 0 if the problem is invalid. For efla_bwd the figure assumes
+ * saved == NULL (recompute); with a saved buffer less is used, never more. */
+size_t efla_workspace_bytes(const efla_problem* p, int for_backward);
+
+/* Size of the forward->backward buffer (chunk factors and chunk states); 0 if invalid. */
+size_t efla_saved_bytes(const efla_problem* p);
+
+/* Offsets inside that buffer (see efla_saved_layout). */
+efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out);
+
+/* Per-token coefficients of the exact flow (section 3.2: beta_t replaced by alpha_t;
+ * section 3.4: lambda_t = ||k_t||^2 in the denominator). Reads k [B,H,T,dk] and
+ * beta [B,H,T]; writes fp32 [B,H,T] arrays:
+ *   lam = ||k||^2, alpha, dalpha_dbeta = exp(-beta lam), dalpha_dlam = beta^2 phi'(beta lam)
+ * with phi(x) = (1 - e^-x)/x. `alpha` is required, the other outputs may be NULL.
+ * cu_seqlens is ignored (the coefficients are per token). */
+efla_status efla_prep(const efla_problem* p, const void* k, const void* beta, float* lam,
+                      float* alpha, float* dalpha_dbeta, float* dalpha_dlam, void* stream);
+
+/* UT transform of every chunk (section 3.3): W = T K, U = T V with
+ * T = (I + strictly_lower(diag(alpha) K K^T))^{-1} diag(alpha), written in the problem
+ * dtype as w [B,H,T,dk], u [B,H,T,dv]. Chunks start at every sequence start.
+ * ws must hold efla_workspace_bytes(p, 0) bytes. */
+efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, const void* beta,
+                          void* w, void* u, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward: o [B,H,T,dv] (problem dtype). `saved` (NULL, or efla_saved_bytes(p) bytes)
+ * receives W, U~ and the chunk states for efla_bwd. ws: efla_workspace_bytes(p, 0). */
+efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
+                     const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Backward of sum(o * d_o): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T], all in
+ * the problem dtype (every output fully overwritten). `saved` is the buffer a forward
+ * call on the same inputs filled, or NULL to recompute it inside ws.
+ * ws: efla_workspace_bytes(p, 1). */
+efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
+                     const void* beta, const void* d_o, const void* saved, size_t saved_bytes,
+                     void* dq, void* dk, void* dv, void* dbeta, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Kernel timing for profiling. While enabled, every kernel that efla_* enqueues is
+ * bracketed by two HIP events recorded on the same stream. efla_profile_read waits for
+ * those events and reports, per kernel name, the launch count and summed milliseconds
+ * since the last reset; it returns the number of kernels written (at most max_kernels).
+ * names receives max_kernels NUL-terminated strings of name_stride bytes each.
+ * Not thread-safe; meant for benchmarks. */
+efla_status efla_profile_enable(int on);
+int efla_profile_read(char* names, int name_stride, int64_t* counts, double* total_ms,
+                      int max_kernels);
+void efla_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EFLA_H */

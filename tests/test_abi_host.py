@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/efla.h declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from delta_rule_sequence_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "efla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(efla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version(L):
+    assert L.efla_abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in range(8):
+        assert L.efla_status_str(code)
+    assert L.efla_status_str(5) == b"workspace or saved buffer too small"
+
+
+def _p(**kw):
+    base = dict(B=4, H=16, T=2048, dk=128, dv=128, dtype=_lib.EFLA_BF16)
+    base.update(kw)
+    return _lib.problem(base["B"], base["H"], base["T"], base["dk"], base["dv"], base["dtype"],
+                        base.get("scale", 1.0), base.get("cu", None), base.get("n_seqs", 0),
+                        base.get("chunk", 64))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(dtype=_lib.EFLA_F32, dk=64, dv=64), 0),
+    (dict(dk=64, dv=128), 0),
+    (dict(dk=128, dv=64), 0),
+    (dict(T=0), 0),
+    (dict(T=1), 0),
+    (dict(B=0), 2),
+    (dict(H=0), 2),
+    (dict(T=-1), 2),
+    (dict(dtype=7), 3),
+    (dict(chunk=32), 4),
+    (dict(dk=96), 4),
+    (dict(dv=256), 4),
+    (dict(dtype=_lib.EFLA_F32), 4),          # fp32 with d = 128 is not built
+    (dict(B=2, cu=0x1000, n_seqs=3), 2),     # packed batches need B == 1
+    (dict(B=1, cu=0x1000, n_seqs=0), 2),
+    (dict(B=4, n_seqs=3), 2),
+])
+def test_problem_validation(L, kw, code):
+    p = _p(**kw)
+    assert L.efla_check_problem(ctypes.byref(p)) == code
+
+
+def test_null_problem(L):
+    assert L.efla_check_problem(None) == 1
+    assert L.efla_workspace_bytes(None, 0) == 0
+    assert L.efla_saved_bytes(None) == 0
+
+
+def test_workspace_and_saved_sizes(L):
+    p = _p()
+    e = 2
+    tok = 4 * 16 * 2048
+    slots = 4 * 32
+    w = tok * 128 * e
+    states = slots * 16 * 128 * 128 * e
+    assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states
+    assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * w
+    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states) + w
+    lay = _lib.EflaSavedLayout()
+    assert L.efla_get_saved_layout(ctypes.byref(p), ctypes.byref(lay)) == 0
+    assert (lay.w, lay.ut, lay.states, lay.n_chunk_slots) == (0, w, 2 * w, slots)
+    # packed batch: chunk slots are bounded by T/64 + n_seqs
+    pp = _p(B=1, T=1000, cu=0x1000, n_seqs=7)
+    assert L.efla_get_saved_layout(ctypes.byref(pp), ctypes.byref(lay)) == 0
+    assert lay.n_chunk_slots == 1000 // 64 + 7
+
+
+def test_entry_points_reject_bad_arguments_without_launching(L):
+    p = _p()
+    vp = ctypes.c_void_p
+    fake = vp(0x10000)        # never dereferenced: validation fails first
+    odd = vp(0x10008)
+    ws_need = L.efla_workspace_bytes(ctypes.byref(p), 0)
+    # missing pointers
+    assert L.efla_fwd(ctypes.byref(p), None, fake, fake, fake, fake, None, 0, fake, ws_need, None) == 1
+    assert L.efla_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, None, 0, fake, fake, fake, None,
+                      fake, 1 << 40, None) == 1
+    assert L.efla_prep(ctypes.byref(p), fake, fake, None, None, None, None, None) == 1
+    # misaligned pointer
+    assert L.efla_fwd(ctypes.byref(p), odd, fake, fake, fake, fake, None, 0, fake, ws_need, None) == 7
+    # workspace too small
+    assert L.efla_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, None, 0, fake, ws_need - 1, None) == 5
+    sb = L.efla_saved_bytes(ctypes.byref(p))
+    assert L.efla_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, sb - 1, fake, ws_need, None) == 5
+    assert L.efla_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, None, 0, fake, fake, fake, fake,
+                      fake, 16, None) == 5
+    assert L.efla_chunk_ut(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 0, None) == 5
+    # invalid problem wins over everything else
+    bad = _p(dk=96)
+    assert L.efla_fwd(ctypes.byref(bad), fake, fake, fake, fake, fake, None, 0, fake, 1 << 40, None) == 4
+    # an empty problem is a successful no-op that touches nothing
+    empty = _p(T=0)
+    assert L.efla_fwd(ctypes.byref(empty), None, None, None, None, None, None, 0, None, 0, None) == 0
+    assert L.efla_bwd(ctypes.byref(empty), None, None, None, None, None, None, 0, None, None, None,
+                      None, None, 0, None) == 0
+
+
+def test_profile_api_without_launches(L):
+    assert L.efla_profile_enable(1) == 0
+    assert L.efla_profile_enable(0) == 0
+    L.efla_profile_reset()
+    names = ctypes.create_string_buffer(64 * 4)
+    counts = (ctypes.c_int64 * 4)()
+    ms = (ctypes.c_double * 4)()
+    assert L.efla_profile_read(names, 64, counts, ms, 4) == 0

@@ -1,0 +1,85 @@
+"""Parity at the full sizes of the five workloads, in the launch configuration the
+benchmark times (efla_fwd with a saved buffer, then efla_bwd reading it).
+
+The GPU computes every head; the fp64 oracle recomputes a sample of independent
+(sequence, head) streams, which is exact for them because streams do not interact.
+Tolerances as in test_gpu_parity (normwise, per tensor and per stream).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import efla_oracle as O
+from workloads import make_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def E():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import delta_rule_sequence_amd as mod
+    mod._lib.lib()
+    return mod
+
+
+def _dev(x, dt):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dt)
+
+
+def _samples(inp, n_streams, rng):
+    """(b, h, start, end) of sampled independent streams."""
+    B, H, T, _ = inp["k"].shape
+    cu = inp["cu_seqlens"]
+    out = []
+    if cu is None:
+        for _ in range(n_streams):
+            out.append((int(rng.integers(B)), int(rng.integers(H)), 0, T))
+    else:
+        ns = len(cu) - 1
+        # always include the longest sequence, then random ones
+        lens = np.diff(cu)
+        picks = [int(np.argmax(lens))] + [int(rng.integers(ns)) for _ in range(n_streams - 1)]
+        for s in picks:
+            out.append((0, int(rng.integers(H)), int(cu[s]), int(cu[s + 1])))
+    return out
+
+
+@pytest.mark.parametrize("idx,n_streams", [(1, 2), (2, 4), (3, 2), (4, 4), (5, 3)])
+def test_fullsize_sampled(E, idx, n_streams):
+    w = workload(idx)
+    print("workload %d: %s" % (idx, w.name), flush=True)
+    inp = make_inputs(w)
+    dt = TDT[w.dtype]
+    q, k, v, beta = (_dev(inp[n], dt) for n in ("q", "k", "v", "beta"))
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
+    o, saved = E.efla_fwd(q, k, v, beta, 1.0, cu, save=True)
+    grads = None
+    if w.backward:
+        do = _dev(inp["do"], dt)
+        grads = E.efla_bwd(q, k, v, beta, do, saved, 1.0, cu)
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    rng = np.random.default_rng(1234 + idx)
+    for (b, h, s, e) in _samples(inp, n_streams, rng):
+        sl = lambda x: x[b:b + 1, h:h + 1, s:e]
+        ref_o, _ = O.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]))
+        got = o[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
+        err = O.rel_err(got, ref_o)
+        print("  stream b=%d h=%d [%d,%d): o %.3e" % (b, h, s, e, err), flush=True)
+        assert np.all(np.isfinite(got)) and err <= tol
+        if grads is not None:
+            g = O.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["do"]))
+            for name, t in zip(("dq", "dk", "dv", "dbeta"), grads):
+                gg = t[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
+                err = O.rel_err(gg, g[name])
+                print("    %s %.3e" % (name, err), flush=True)
+                assert np.all(np.isfinite(gg)) and err <= tol, name
+    # every output element is finite (no stream left unwritten or blown up)
+    assert torch.isfinite(o.float()).all()
+    if grads is not None:
+        for t in grads:
+            assert torch.isfinite(t.float()).all()

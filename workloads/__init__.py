@@ -101,19 +101,20 @@ def seq_lengths(w: Workload, rng: Optional[np.random.Generator] = None) -> np.nd
     return rng.integers(lo, hi + 1, size=w.n_seqs).astype(np.int64)
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None, with_grad: Optional[bool] = None) -> dict:
+def make_inputs(w: Workload, seed: Optional[int] = None, with_grad: Optional[bool] = None,
+                lengths=None) -> dict:
     """Draw q, k, v, beta (and grad_out when the workload has a backward) for workload `w`.
 
     Returns float32 numpy arrays q, k [B,H,T,dk]; v, do [B,H,T,dv]; beta [B,H,T];
     and cu_seqlens (int32 [n_seqs+1]) or None. For a packed batch B is 1 and T is
-    the total length.
+    the total length; `lengths` replaces the drawn sequence lengths.
     """
     rng = np.random.default_rng(BASE_SEED + w.seed_index if seed is None else seed)
     cu = None
     B, T = w.B, w.T
-    if w.n_seqs > 0:
-        lens = seq_lengths(w, rng)
-        cu = np.zeros(w.n_seqs + 1, dtype=np.int32)
+    if w.n_seqs > 0 or lengths is not None:
+        lens = seq_lengths(w, rng) if lengths is None else np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(len(lens) + 1, dtype=np.int32)
         cu[1:] = np.cumsum(lens)
         B, T = 1, int(cu[-1])
     H, dk, dv = w.H, w.dk, w.dv
