@@ -106,11 +106,18 @@ def efla_chunk_ut(k, v, beta, cu_seqlens=None):
     return w, u
 
 
-def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None):
-    """Forward. Returns (o, saved) where saved is the uint8 buffer for efla_bwd (or None)."""
+def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=None, saved=None):
+    """Forward. Returns (o, saved) where saved is the uint8 buffer for efla_bwd (or None).
+    o, saved and ws may be passed in preallocated."""
     p = make_problem(q, k, v, beta, scale, cu_seqlens)
-    o = torch.empty_like(v)
-    saved = _bytes(efla_saved_bytes(p), k.device) if save else None
+    if o is None:
+        o = torch.empty_like(v)
+    else:
+        _need(o, "o", v.dtype, v.shape)
+    if save and saved is None:
+        saved = _bytes(efla_saved_bytes(p), k.device)
+    if not save:
+        saved = None
     ws_n = efla_workspace_bytes(p, False)
     if ws is None or ws.numel() < ws_n:
         ws = _bytes(ws_n, k.device)
@@ -120,12 +127,18 @@ def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None):
     return o, saved
 
 
-def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None):
-    """Backward of sum(o * d_o): (dq, dk, dv, dbeta) in the input dtype."""
+def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None, grads=None):
+    """Backward of sum(o * d_o): (dq, dk, dv, dbeta) in the input dtype.
+    grads may be a preallocated (dq, dk, dv, dbeta) tuple."""
     p = make_problem(q, k, v, beta, scale, cu_seqlens)
     _need(d_o, "d_o", v.dtype, v.shape)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dbeta = torch.empty_like(beta)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dbeta = torch.empty_like(beta)
+    else:
+        dq, dk, dv, dbeta = grads
+        for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (dbeta, beta, "dbeta")):
+            _need(t, n, ref.dtype, ref.shape)
     ws_n = efla_workspace_bytes(p, True)
     if ws is None or ws.numel() < ws_n:
         ws = _bytes(ws_n, k.device)
