@@ -1,6 +1,7 @@
 // C ABI of the EFLA library: argument validation, workspace layout, launch sequencing.
 // See include/efla.h for the contract of every entry point.
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <map>
@@ -51,6 +52,18 @@ void prof_drain() {
   g_prof_pending.clear();
 }
 }  // namespace
+
+int scan_tile(const Shape& s) {
+  if (s.dv != 128) return 16;
+  static int forced = -1;
+  if (forced < 0) {
+    const char* e = getenv("EFLA_SCAN_TV");
+    forced = (e && (atoi(e) == 16 || atoi(e) == 32)) ? atoi(e) : 0;
+  }
+  if (forced) return forced;
+  const int64_t wgs32 = (int64_t)s.n_seqs * s.H * (s.dv / 32);
+  return wgs32 < 256 ? 16 : 32;
+}
 
 void prof_begin(hipStream_t st) {
   if (!g_prof_on) return;
@@ -120,10 +133,11 @@ size_t bytes_k(const Shape& s) { return (size_t)s.B * s.H * s.T * s.dk * esize(s
 size_t bytes_v(const Shape& s) { return (size_t)s.B * s.H * s.T * s.dv * esize(s); }
 size_t bytes_states(const Shape& s) { return (size_t)s.slots * s.H * s.dk * s.dv * esize(s); }
 size_t bytes_table(const Shape& s) { return s.cu ? (size_t)(s.n_seqs + 1) * 4 : 0; }
+size_t bytes_m(const Shape& s) { return (size_t)s.slots * s.H * kChunk * kChunk * esize(s); }
 
 // Layout of the forward->backward buffer.
 struct Saved {
-  size_t w, ut, states, table, total;
+  size_t w, ut, states, table, m, total;
 };
 Saved saved_layout(const Shape& s) {
   Saved L;
@@ -136,13 +150,16 @@ Saved saved_layout(const Shape& s) {
   o += align_up(bytes_states(s));
   L.table = o;
   o += align_up(bytes_table(s));
+  L.m = o;
+  o += align_up(bytes_m(s));
   L.total = o;
   return L;
 }
 
-// Forward workspace: U, plus W and the chunk table when no saved buffer is given.
+// Forward workspace: U, plus W, M and the chunk table when no saved buffer is given.
 size_t ws_fwd(const Shape& s) {
-  return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s));
+  return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s)) +
+         align_up(bytes_m(s));
 }
 // Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer and U
 // for the recompute path.
@@ -160,12 +177,13 @@ bool empty(const Shape& s) { return s.T == 0; }
 // Forward stages shared by efla_fwd and the recompute path of efla_bwd.
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                         const void* beta, void* o, unsigned char* w, unsigned char* ut,
-                        unsigned char* states, int* table, unsigned char* u, hipStream_t st) {
+                        unsigned char* states, int* table, unsigned char* m, unsigned char* u,
+                        hipStream_t st) {
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  if (efla_status r = hip_status(launch_ut_fwd(s, table, k, v, beta, w, u, st))) return r;
-  return hip_status(launch_scan_fwd(s, table, q, k, w, u, o, ut, states, st));
+  if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, w, u, m, st))) return r;
+  return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, st));
 }
 
 }  // namespace
@@ -217,6 +235,7 @@ efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out)
   out->ut = L.ut;
   out->states = L.states;
   out->table = L.table;
+  out->m = L.m;
   out->total = L.total;
   out->n_chunk_slots = s.slots;
   return EFLA_OK;
@@ -248,7 +267,7 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  return hip_status(launch_ut_fwd(s, table, k, v, beta, w, u, st));
+  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, w, u, nullptr, st));
 }
 
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -268,12 +287,14 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
   unsigned char* u = wsb;
   unsigned char* w_ws = wsb + align_up(bytes_v(s));
   int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
+  unsigned char* m_ws = (unsigned char*)table_ws + align_up(bytes_table(s));
   unsigned char* sv = (unsigned char*)saved;
   unsigned char* w = sv ? sv + L.w : w_ws;
   unsigned char* ut = sv ? sv + L.ut : nullptr;
   unsigned char* states = sv ? sv + L.states : nullptr;
   int* table = sv ? (int*)(sv + L.table) : table_ws;
-  return run_forward(s, q, k, v, beta, o, w, ut, states, table, u, (hipStream_t)stream);
+  unsigned char* m = sv ? sv + L.m : m_ws;
+  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, u, (hipStream_t)stream);
 }
 
 efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -300,12 +321,12 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
     unsigned char* rec = dstates + align_up(bytes_states(s));
     unsigned char* u = rec + L.total;
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
-                                    rec + L.states, (int*)(rec + L.table), u, st))
+                                    rec + L.states, (int*)(rec + L.table), rec + L.m, u, st))
       return r;
     sv = rec;
   }
   const int* table = (const int*)(sv + L.table);
-  if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, d_o, dut, dstates, st)))
+  if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o, dut, dstates, st)))
     return r;
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
                                      dstates, dq, dk, dv, dbeta, st));

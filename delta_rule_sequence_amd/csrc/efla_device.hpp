@@ -101,6 +101,61 @@ EFLA_DEV f32x4 mma16_gb(const E* a, int lda, const E* __restrict__ bt, int64_t l
   return acc;
 }
 
+// ---------------------------------------------------------------------------
+// Fragment loads. The operand X[m][k] of a 16-row tile is either stored "row-major"
+// (k contiguous: row m at src + m * ld) or "k-major" (m contiguous: row k at src + k * ld).
+// frag_rm: src points at X[m0][k0]; frag_km: src points at storage row k0, column m0.
+// Lane l receives X[m0 + (l & 15)][k0 + (l >> 4) * KC/4 + t] for t < KC/4.
+// bf16 k-major fragments use the gfx950 LDS transpose read ds_read_b64_tr_b16: within each
+// 16-lane group, output lane j, slot s holds element j % 4 of the 8-byte row addressed by
+// lane 4 s + j / 4; addressing rows k0 + 8 g + i / 4 (+4) at column m0 + 4 (i % 4) from lane
+// i of group g therefore yields the standard operand layout. k-major loads must come from LDS.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <typename E>
+EFLA_DEV typename Mma<E>::vec frag_rm(const E* src, int ld, int lane) {
+  return *(const typename Mma<E>::vec*)(src + (lane & 15) * ld + (lane >> 4) * (Mma<E>::KC / 4));
+}
+
+template <typename E> EFLA_DEV typename Mma<E>::vec frag_km(const E* src, int ld, int lane);
+
+template <> EFLA_DEV f32x4 frag_km<float>(const float* src, int ld, int lane) {
+  const float* p = src + (lane >> 4) * 4 * ld + (lane & 15);
+  return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+
+template <> EFLA_DEV bf16x8 frag_km<__bf16>(const __bf16* src, int ld, int lane) {
+  const int gq = lane >> 4, i = lane & 15;
+  const __bf16* p = src + (8 * gq + (i >> 2)) * ld + 4 * (i & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * ld));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// acc += A[0:16, k0:k1] * B[k0:k1, 0:16]. A is stored row-major (AK = false; a points at
+// row m0) or k-major (AK = true; a points at column m0 of storage row 0). B is given as B^T
+// row-major (BK = false; b points at row n0 of B^T) or as B itself, k-major for this
+// product (BK = true; b points at column n0 of storage row 0).
+template <typename E, bool AK, bool BK>
+EFLA_DEV f32x4 mma(const E* a, int lda, const E* b, int ldb, int k0, int k1, f32x4 acc,
+                   int lane) {
+  for (int k = k0; k < k1; k += Mma<E>::KC) {
+    typename Mma<E>::vec av, bv;
+    if constexpr (AK) av = frag_km<E>(a + k * lda, lda, lane); else av = frag_rm<E>(a + k, lda, lane);
+    if constexpr (BK) bv = frag_km<E>(b + k * ldb, ldb, lane); else bv = frag_rm<E>(b + k, ldb, lane);
+    acc = Mma<E>::step(av, bv, acc);
+  }
+  return acc;
+}
+
+template <typename E> EFLA_DEV typename Mma<E>::vec zero_vec() {
+  typename Mma<E>::vec v;
+#pragma unroll
+  for (int i = 0; i < 16 / (int)sizeof(E); ++i) v[i] = to_e<E>(0.f);
+  return v;
+}
+
 // Store an accumulator tile transposed: s[n][m] = C[m][n] (s points at the tile origin of
 // C^T, pitch ld). Four consecutive m per lane become one 8- or 16-byte store.
 template <typename E> EFLA_DEV void st_frag_t(E* s, int ld, f32x4 c, int lane);
@@ -112,15 +167,19 @@ template <> EFLA_DEV void st_frag_t<__bf16>(__bf16* s, int ld, f32x4 c, int lane
   *(bf16x4*)(s + (lane & 15) * ld + 4 * (lane >> 4)) = v;
 }
 
-// Store an accumulator tile row-major into LDS: s[m][n] = C[m][n]. The stores are
-// volatile so that the backend never pairs them into ds_write2_b32: the ROCm 7.2 LLVM
-// backend was seen to emit such a pair with a wrong offset for MFMA results
-// (offset0 scaled down by four), which silently corrupted the tile.
+// Store an accumulator tile row-major into LDS: s[m][n] = C[m][n]. The ROCm 7.2 LLVM
+// backend was seen to pair two such fp32 stores of MFMA results into a ds_write2_b32 with a
+// wrong first offset (scaled down by four), silently corrupting the tile. bf16 stores cannot
+// be paired (there is no 16-bit ds_write2); between fp32 stores an empty asm statement with a
+// memory clobber keeps the backend from pairing them. It costs no instruction.
 template <typename E>
 EFLA_DEV void st_frag_lds(E* s, int ld, f32x4 c, int lane) {
-  volatile E* p = s + 4 * (lane >> 4) * ld + (lane & 15);
+  E* p = s + 4 * (lane >> 4) * ld + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i * ld] = to_e<E>(c[i]);
+  for (int i = 0; i < 4; ++i) {
+    p[i * ld] = to_e<E>(c[i]);
+    if constexpr (sizeof(E) == 4) asm volatile("" ::: "memory");
+  }
 }
 
 // Store an accumulator tile row-major to global memory: g[m][n] = C[m][n].

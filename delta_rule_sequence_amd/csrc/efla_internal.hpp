@@ -31,14 +31,15 @@ void prof_end(const char* name, hipStream_t st);
 hipError_t launch_chunk_table(const Shape& s, int* table, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const void* k, const void* beta, float* lam, float* alpha,
                        float* ex, float* dlam, hipStream_t st);
-hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* k, const void* v,
-                         const void* beta, void* w, void* u, hipStream_t st);
+hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
+                         const void* v, const void* beta, void* w, void* u, void* m,
+                         hipStream_t st);
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                           const void* w, const void* u, void* o, void* ut, void* states,
-                           hipStream_t st);
+                           const void* w, const void* u, const void* m, void* o, void* ut,
+                           void* states, hipStream_t st);
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
-                           const void* w, const void* d_o, void* dut, void* dstates,
-                           hipStream_t st);
+                           const void* w, const void* m, const void* d_o, void* dut,
+                           void* dstates, hipStream_t st);
 hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, const void* k,
                             const void* v, const void* beta, const void* d_o, const void* ut,
                             const void* dut, const void* states, const void* dstates, void* dq,
@@ -64,7 +65,9 @@ inline Geom make_geom(const Shape& s, const int* table) {
   return g;
 }
 
-// Width of the d_v slice one scan workgroup owns.
-inline int scan_tile(int dv) { return dv / 4; }
+// Width of the d_v slice one scan workgroup owns: 16 when d_v = 64; for d_v = 128, 16 when
+// width 32 would leave compute units idle (fewer than 256 workgroups), else 32.
+// EFLA_SCAN_TV=16|32 overrides the choice for d_v = 128 (tuning).
+int scan_tile(const Shape& s);
 
 }  // namespace efla

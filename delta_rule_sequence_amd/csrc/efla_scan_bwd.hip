@@ -2,47 +2,59 @@
 //
 // Reverse-mode differentiation of the chunk recurrence of section 3.3 (Exact Flow Linear
 // Attention summary page): with G the gradient of the state leaving chunk c,
-//   dU~_c = scale tril(Q K^T)^T dO_c + K_c G,
-//   G    <- G + scale Q_c^T dO_c - W_c^T dU~_c      (gradient of the state entering c).
+//   dU~_c = scale M_c^T dO_c + K_c G,          M_c = tril(Q_c K_c^T) from the UT kernel,
+//   G    <- G + scale Q_c^T dO_c - W_c^T dU~_c (gradient of the state entering c).
 // One workgroup walks the chunks of one (sequence, head) backwards and owns a d_k x TV
-// slice of G in fp32 accumulators. It writes dU~ and, per chunk, the G that entered the
-// step (the gradient of the chunk's outgoing state) for the chunk-parallel gradient kernel.
+// slice of G, kept transposed (G^T, TV x d_k) in fp32 MFMA accumulators. It writes dU~ and,
+// per chunk, the G that entered the step (the gradient of the chunk's outgoing state) for
+// the chunk-parallel gradient kernel.
+//
+// Latency hiding as in the forward scan: the K rows of each wave are register A fragments;
+// the previous chunk's K rows and Q, W, M, dO tiles are loaded into registers while the
+// current chunk computes, and the LDS tiles are double-buffered. Products over the token
+// or d_k index read LDS tiles k-major with the LDS transpose read (bf16). dU~ and G leave
+// through LDS staging as 16-byte stores.
 #include "efla_internal.hpp"
 
 namespace efla {
 
 template <typename E, int DK, int DV, int TV>
 struct ScanBwdLds {
-  static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64);
-  static constexpr size_t oQ = 0;                               // Q      [64][LK]
-  static constexpr size_t oQt = oQ + 64 * LK * sizeof(E);       // Q^T    [DK][LT]
-  static constexpr size_t oK = oQt + DK * LT * sizeof(E);       // K      [64][LK]
-  static constexpr size_t oWt = oK + 64 * LK * sizeof(E);       // W^T    [DK][LT]
-  static constexpr size_t oOt = oWt + DK * LT * sizeof(E);      // dO^T   [TV][LT]
-  static constexpr size_t oGt = oOt + TV * LT * sizeof(E);      // G^T    [TV][LK]
-  static constexpr size_t oMt = oGt + TV * LK * sizeof(E);      // tril(QK^T)^T [64][LT]
-  static constexpr size_t oDt = oMt + 64 * LT * sizeof(E);      // dU~^T  [TV][LT]
-  static constexpr size_t bytes = oDt + TV * LT * sizeof(E);
+  static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64), LS = pitch<E>(TV);
+  // one stage: Q [64][LK], W [64][LK], M [64][LT], dO [64][LS]
+  static constexpr size_t oQ = 0;
+  static constexpr size_t oW = oQ + 64 * LK * sizeof(E);
+  static constexpr size_t oM = oW + 64 * LK * sizeof(E);
+  static constexpr size_t oO = oM + 64 * LT * sizeof(E);
+  static constexpr size_t stage = oO + 64 * LS * sizeof(E);
+  static constexpr size_t oG = 2 * stage;                       // G slice [DK][LS]
+  static constexpr size_t oDt = oG + DK * LS * sizeof(E);       // dU~^T  [TV][LT]
+  static constexpr size_t oDu = oDt + TV * LT * sizeof(E);      // dU~ staging [64][LS]
+  static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
 };
 
 template <typename E, int DK, int DV, int TV>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
-    const E* __restrict__ d_o, E* __restrict__ dut, E* __restrict__ dstates) {
+    const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
+    E* __restrict__ dstates) {
   typedef ScanBwdLds<E, DK, DV, TV> L;
+  typedef typename Mma<E>::vec V;
+  constexpr int KC = Mma<E>::KC, KS = DK / KC, KT = kChunk / KC;
   constexpr int NTILE = DV / TV;
   constexpr int NB = TV / 16;
   constexpr int TPW = (DK / 16) * NB / 4;
+  constexpr int VE = 16 / (int)sizeof(E);
+  constexpr int VQ = 64 * DK / VE / kThreads;      // Q (and W) vectors per thread
+  constexpr int VM = 64 * 64 / VE / kThreads;      // M vectors per thread
+  constexpr int OPR = TV / VE;                     // dO vectors per row
+  constexpr int VO = (64 * OPR + kThreads - 1) / kThreads;
   static_assert(TPW >= 1 && ((DK / 16) * NB) % 4 == 0, "state tiles must split over 4 waves");
+  static_assert(VQ >= 1 && VM >= 1 && (64 * DK / VE) % kThreads == 0, "tile split");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  E* sQ = (E*)(smem + L::oQ);
-  E* sQt = (E*)(smem + L::oQt);
-  E* sK = (E*)(smem + L::oK);
-  E* sWt = (E*)(smem + L::oWt);
-  E* sOt = (E*)(smem + L::oOt);
-  E* sGt = (E*)(smem + L::oGt);
-  E* sMt = (E*)(smem + L::oMt);
+  E* sG = (E*)(smem + L::oG);
   E* sDt = (E*)(smem + L::oDt);
+  E* sDu = (E*)(smem + L::oDu);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int sh, tile;
@@ -51,76 +63,134 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
   const SeqInfo si = seq_info(g, s);
   const int nchunks = seq_chunks(g, si);
   const int v0 = tile * TV;
-  const int k0M = round_down_kc<E>(16 * wv);  // row block wv of tril(.)^T needs cols >= 16 wv
+  const int rA = 16 * wv;
+  const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
 
-  f32x4 G[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) G[i] = zero4();
+  V kA[KS], kN[KS];
+  uint4 qR[VQ], wR[VQ], mR[VM], oR[VO];
 
-  for (int c = nchunks - 1; c >= 0; --c) {
+  auto load_chunk = [&](int c) {
     const int n = min(kChunk, si.len - c * kChunk);
-    const int64_t row0 = (int64_t)(si.b * g.H + h) * g.T + si.bos + c * kChunk;
-    g2s<E, DK>(sQ, L::LK, q + row0 * DK, DK, n, tid);
-    g2s_t<E, DK>(sQt, L::LT, q + row0 * DK, DK, n, tid);
-    g2s<E, DK>(sK, L::LK, k + row0 * DK, DK, n, tid);
-    g2s_t<E, DK>(sWt, L::LT, w + row0 * DK, DK, n, tid);
-    g2s_t<E, TV>(sOt, L::LT, d_o + row0 * DV + v0, DV, n, tid);
-    E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV;
+    const int64_t r0 = base + (int64_t)c * kChunk;
+    const int ra = min(rA + (lane & 15), n - 1) - (lane & 15);
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wv + 4 * i, mb = t / NB, nb = t % NB;
-      st_frag_t<E>(sGt + 16 * nb * L::LK + 16 * mb, L::LK, G[i], lane);
-      st_frag_glb<E>(gG + (int64_t)16 * mb * DV + v0 + 16 * nb, DV, G[i], lane);
+    for (int ks = 0; ks < KS; ++ks) kN[ks] = frag_rm<E>(k + (r0 + ra) * DK + ks * KC, DK, lane);
+#pragma unroll
+    for (int it = 0; it < VQ; ++it) {
+      const int i = it * kThreads + tid;
+      const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
+      qR[it] = *(const uint4*)(q + (r0 + r) * DK + cc);
+      wR[it] = *(const uint4*)(w + (r0 + r) * DK + cc);
     }
-    __syncthreads();
-
-    // tril(Q K^T)^T [j][i] = k_j . q_i for i >= j; row block wv (j).
+    const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      if (16 * nb >= k0M) {
-        f32x4 acc = zero4();
-        if (nb >= wv) {
-          acc = mma16<E>(sK + 16 * wv * L::LK, L::LK, sQ + 16 * nb * L::LK, L::LK, 0, DK, acc, lane);
-          if (nb == wv) {
+    for (int it = 0; it < VM; ++it) mR[it] = *(const uint4*)(mc + (it * kThreads + tid) * VE);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if ((lane & 15) < 4 * (lane >> 4) + i) acc[i] = 0.f;
-          }
-        }
-        st_frag_lds<E>(sMt + 16 * wv * L::LT + 16 * nb, L::LT, acc, lane);
+    for (int it = 0; it < VO; ++it) {
+      const int i = it * kThreads + tid;
+      if (i < 64 * OPR) {
+        const int r = min(i / OPR, n - 1), cc = (i % OPR) * VE;
+        oR[it] = *(const uint4*)(d_o + (r0 + r) * DV + v0 + cc);
       }
     }
-    f32x4 dU[NB];
+  };
+  auto commit_chunk = [&](int c, unsigned char* st) {
+    const int n = min(kChunk, si.len - c * kChunk);
+    E* sQ = (E*)(st + L::oQ);
+    E* sW = (E*)(st + L::oW);
+    E* sM = (E*)(st + L::oM);
+    E* sO = (E*)(st + L::oO);
+    const bool rowok = rA + (lane & 15) < n;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      dU[nb] = mma16<E>(sK + 16 * wv * L::LK, L::LK, sGt + 16 * nb * L::LK, L::LK, 0, DK, zero4(), lane);
-    __syncthreads();
-
+    for (int ks = 0; ks < KS; ++ks) kA[ks] = rowok ? kN[ks] : zero_vec<E>();
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const f32x4 m = mma16<E>(sMt + 16 * wv * L::LT, L::LT, sOt + 16 * nb * L::LT, L::LT, k0M, kChunk, zero4(), lane);
-      dU[nb] += g.scale * m;
-      st_frag_t<E>(sDt + 16 * nb * L::LT + 16 * wv, L::LT, dU[nb], lane);
-      st_frag_rows<E>(dut + (row0 + 16 * wv) * DV + v0 + 16 * nb, DV, dU[nb], lane, 16 * wv, n);
+    for (int it = 0; it < VQ; ++it) {
+      const int i = it * kThreads + tid;
+      const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
+      *(uint4*)(sQ + r * L::LK + cc) = r < n ? qR[it] : z;
+      *(uint4*)(sW + r * L::LK + cc) = r < n ? wR[it] : z;
     }
-    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < VM; ++it) {
+      const int i = (it * kThreads + tid) * VE;
+      *(uint4*)(sM + (i / 64) * L::LT + i % 64) = mR[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VO; ++it) {
+      const int i = it * kThreads + tid;
+      if (i < 64 * OPR) {
+        const int r = i / OPR, cc = (i % OPR) * VE;
+        *(uint4*)(sO + r * L::LS + cc) = r < n ? oR[it] : z;
+      }
+    }
+  };
 
+  f32x4 Gt[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) Gt[i] = zero4();
+  if (nchunks > 0) {
+    load_chunk(nchunks - 1);
+    commit_chunk(nchunks - 1, smem + ((nchunks - 1) & 1) * L::stage);
+  }
+
+  for (int c = nchunks - 1; c >= 0; --c) {
+    unsigned char* stc = smem + (c & 1) * L::stage;
+    const E* sQ = (const E*)(stc + L::oQ);
+    const E* sW = (const E*)(stc + L::oW);
+    const E* sM = (const E*)(stc + L::oM);
+    const E* sO = (const E*)(stc + L::oO);
+    const int n = min(kChunk, si.len - c * kChunk);
+    const int64_t r0 = base + (int64_t)c * kChunk;
+    // Stage G (gradient of the state leaving chunk c): G^T tiles written transposed.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int t = wv + 4 * i, mb = t / NB, nb = t % NB;
-      const f32x4 a = mma16<E>(sQt + 16 * mb * L::LT, L::LT, sOt + 16 * nb * L::LT, L::LT, 0, kChunk, zero4(), lane);
-      const f32x4 b = mma16<E>(sWt + 16 * mb * L::LT, L::LT, sDt + 16 * nb * L::LT, L::LT, 0, kChunk, zero4(), lane);
-      G[i] += g.scale * a - b;
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+      st_frag_t<E>(sG + 16 * db * L::LS + 16 * vb, L::LS, Gt[i], lane);
+    }
+    const bool more = c > 0;
+    load_chunk(more ? c - 1 : c);
+    __syncthreads();
+
+    {  // G of this slot -> dstates [d][v0 : v0 + TV]
+      E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
+      constexpr int VPR = TV / VE;
+      for (int i = tid; i < DK * VPR; i += kThreads) {
+        const int d = i / VPR, cc = (i % VPR) * VE;
+        *(uint4*)(gG + (int64_t)d * DV + cc) = *(const uint4*)(sG + d * L::LS + cc);
+      }
+    }
+    // dU~ = scale M^T dO + K G for this wave's rows (tokens j).
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 kg = zero4(), md = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * L::LS + 16 * nb, L::LS, lane), kg);
+      md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
+      f32x4 du = kg + g.scale * md;
+      st_frag_t<E>(sDt + 16 * nb * L::LT + rA, L::LT, du, lane);
+      st_frag_lds<E>(sDu + rA * L::LS + 16 * nb, L::LS, du, lane);
     }
     __syncthreads();
+
+    s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, L::LS, n, tid);
+    // G^T += scale dO^T Q - dU~^T W
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+      const f32x4 a = mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
+      const f32x4 b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
+      Gt[i] += g.scale * a - b;
+    }
+    if (more) commit_chunk(c - 1, smem + ((c - 1) & 1) * L::stage);
   }
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int TV>
 static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
-                              const void* w, const void* d_o, void* dut, void* dstates,
-                              hipStream_t st) {
-  constexpr int TV = DV / 4;
+                              const void* w, const void* m, const void* d_o, void* dut,
+                              void* dstates, hipStream_t st) {
   typedef ScanBwdLds<E, DK, DV, TV> L;
   static bool attr = false;
   if (!attr) {
@@ -134,7 +204,7 @@ static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, c
   prof_begin(st);
   hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV>), dim3((unsigned)blocks), dim3(kThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)d_o, (E*)dut, (E*)dstates);
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates);
   hipError_t e = hipGetLastError();
   prof_end("scan_bwd", st);
   return e;
@@ -153,15 +223,22 @@ size_t lds_scan_bwd(Dt dt, int dk, int dv) {
 }
 
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
-                           const void* w, const void* d_o, void* dut, void* dstates,
-                           hipStream_t st) {
+                           const void* w, const void* m, const void* d_o, void* dut,
+                           void* dstates, hipStream_t st) {
+#define EFLA_SB(E_, DK_, DV_, TV_) \
+  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, st)
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) return scan_bwd_go<__bf16, 64, 64>(s, table, q, k, w, d_o, dut, dstates, st);
-    if (s.dk == 64 && s.dv == 128) return scan_bwd_go<__bf16, 64, 128>(s, table, q, k, w, d_o, dut, dstates, st);
-    if (s.dk == 128 && s.dv == 64) return scan_bwd_go<__bf16, 128, 64>(s, table, q, k, w, d_o, dut, dstates, st);
-    return scan_bwd_go<__bf16, 128, 128>(s, table, q, k, w, d_o, dut, dstates, st);
+    if (s.dk == 64 && s.dv == 64) EFLA_SB(__bf16, 64, 64, 16);
+    if (s.dk == 128 && s.dv == 64) EFLA_SB(__bf16, 128, 64, 16);
+    if (scan_tile(s) == 16) {
+      if (s.dk == 64) EFLA_SB(__bf16, 64, 128, 16);
+      EFLA_SB(__bf16, 128, 128, 16);
+    }
+    if (s.dk == 64) EFLA_SB(__bf16, 64, 128, 32);
+    EFLA_SB(__bf16, 128, 128, 32);
   }
-  return scan_bwd_go<float, 64, 64>(s, table, q, k, w, d_o, dut, dstates, st);
+  EFLA_SB(float, 64, 64, 16);
+#undef EFLA_SB
 }
 
 }  // namespace efla

@@ -1,12 +1,13 @@
-// UT transform of one 64-token chunk per workgroup.
+// UT transform of one 64-token chunk per workgroup, plus the chunk's causal score block.
 //
 // Exact Flow Linear Attention summary page, section 3.3 (chunkwise form with the UT
 // transform; the WY/UT representation is the DeltaNet prior art of the fifth page):
 //   alpha_i = exact-flow step of token i,  A = strictly_lower(diag(alpha) K K^T),
-//   T = (I + A)^{-1} diag(alpha),  W = T K,  U = T V.
-// K K^T, T K and T V are MFMA contractions; the unit lower triangular inverse is a
-// blocked forward substitution in fp32 in LDS. Padded rows of a tail chunk read as zero
-// (their beta is zero, so alpha = 0 and they do not touch the valid rows).
+//   T = (I + A)^{-1} diag(alpha),  W = T K,  U = T V,   M = tril(Q K^T).
+// K K^T, Q K^T, T K and T V are MFMA contractions (products over the token index read the
+// row-major K and V tiles k-major); the unit lower triangular inverse is a blocked forward
+// substitution in fp32 in LDS. Padded rows of a tail chunk read as zero (their beta is zero,
+// so alpha = 0 and they do not touch the valid rows). M is optional (q may be null).
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -15,81 +16,117 @@ template <typename E, int DK, int DV>
 struct UtFwdLds {
   static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64), LV = pitch<E>(DV), LF = kPitchF;
   static constexpr size_t oK = 0;                                   // K        [64][LK]
-  static constexpr size_t oKt = oK + 64 * LK * sizeof(E);           // K^T      [DK][LT]
-  static constexpr size_t oVt = oKt + DK * LT * sizeof(E);          // V^T      [DV][LT]
-  static constexpr size_t oT = oVt + DV * LT * sizeof(E);           // T        [64][LT]
-  static constexpr size_t oA = oT + 64 * LT * sizeof(E);            // A (fp32) [64][LF]
-  static constexpr size_t oX = oA + 64 * LF * 4;                    // X (fp32) [64][LF]
+  static constexpr size_t oV = oK + 64 * LK * sizeof(E);            // V        [64][LV]
+  static constexpr size_t oA = oV + 64 * LV * sizeof(E);            // A (fp32) [64][LF]; later T
+  static constexpr size_t oX = oA + 64 * LF * 4;                    // X (fp32) [64][LF]; M staging first
   static constexpr size_t oAl = oX + 64 * LF * 4;                   // alpha    [64]
   static constexpr size_t oScr = oAl + 64 * 4;                      // inverse scratch
   static constexpr size_t bytes = oScr + 4 * 16 * 20 * 4;
-  static_assert(64 * LV * sizeof(E) <= 64 * LF * 4, "U staging must fit in the A buffer");
+  static_assert(64 * LT * sizeof(E) <= 64 * LF * 4, "T and M must fit in an fp32 work matrix");
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void ut_fwd_kernel(Geom g, const E* __restrict__ k,
-                                                          const E* __restrict__ v,
-                                                          const E* __restrict__ beta,
-                                                          E* __restrict__ w, E* __restrict__ u) {
+__global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
+    Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const E* __restrict__ beta, E* __restrict__ w, E* __restrict__ u, E* __restrict__ mout) {
   typedef UtFwdLds<E, DK, DV> L;
+  typedef typename Mma<E>::vec Vv;
+  constexpr int KC = Mma<E>::KC, KS = DK / KC;
+  constexpr int VE = 16 / (int)sizeof(E);
+  constexpr int VPR = DK / VE;                  // 16-byte vectors per K row
+  constexpr int KIT = 64 * VPR / kThreads;      // K vectors per thread
+  static_assert(VPR <= 64 && (64 % VPR) == 0 && KIT >= 1, "K row split");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   E* sK = (E*)(smem + L::oK);
-  E* sKt = (E*)(smem + L::oKt);
-  E* sVt = (E*)(smem + L::oVt);
-  E* sT = (E*)(smem + L::oT);
+  E* sV = (E*)(smem + L::oV);
   float* sA = (float*)(smem + L::oA);
+  E* sT = (E*)(smem + L::oA);
   float* sX = (float*)(smem + L::oX);
+  E* sM = (E*)(smem + L::oX);
   float* sAl = (float*)(smem + L::oAl);
   float* sScr = (float*)(smem + L::oScr);
-  E* sU = (E*)(smem + L::oA);  // U staging after the inverse is done
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int slot = blockIdx.x / g.H, h = blockIdx.x % g.H;
   ChunkInfo ci;
   if (!chunk_info(g, slot, ci)) return;
   const int n = ci.n;
+  const int rA = 16 * wv;
   const int64_t row0 = (int64_t)(ci.b * g.H + h) * g.T + ci.t0;
-  const E* gk = k + row0 * DK;
-  const E* gv = v + row0 * DV;
 
-  g2s<E, DK>(sK, L::LK, gk, DK, n, tid);
-  g2s_t<E, DK>(sKt, L::LT, gk, DK, n, tid);
-  g2s_t<E, DV>(sVt, L::LT, gv, DV, n, tid);
-  __syncthreads();
-
-  {  // alpha per row: 4 threads per row
-    const int r = tid >> 2, q4 = tid & 3;
+  // Q rows of this wave as A fragments (for M), straight from global memory.
+  Vv qA[KS];
+  if (mout) {
+    const int ra = min(rA + (lane & 15), n - 1) - (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qA[ks] = frag_rm<E>(q + (row0 + ra) * DK + ks * KC, DK, lane);
+    if (rA + (lane & 15) >= n)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qA[ks] = zero_vec<E>();
+  }
+  // K: stage in LDS and reduce ||k||^2 from the loaded vectors (VPR consecutive threads per row).
+  float lam[KIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int i = it * kThreads + tid;
+    const int r = i / VPR, c = (i % VPR) * VE;
+    typename Mma<E>::vec x = zero_vec<E>();
+    if (r < n) x = *(const Vv*)(k + (row0 + r) * DK + c);
+    *(Vv*)(sK + r * L::LK + c) = x;
     float acc = 0.f;
-#pragma unroll 8
-    for (int c = q4 * (DK / 4); c < (q4 + 1) * (DK / 4); ++c) {
-      const float x = to_f(sK[r * L::LK + c]);
-      acc = fmaf(x, x, acc);
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    if (q4 == 0) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
+#pragma unroll
+    for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    lam[it] = acc;
+  }
+  g2s<E, DV>(sV, L::LV, v + row0 * DV, DV, n, tid);
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int i = it * kThreads + tid;
+    if (i % VPR == 0) {
+      const int r = i / VPR;
       const float bt = r < n ? to_f(beta[row0 + r]) : 0.f;
-      sAl[r] = flow_coef(bt, acc).alpha;
+      sAl[r] = flow_coef(bt, lam[it]).alpha;
     }
   }
   __syncthreads();
 
-  // A = strictly_lower(diag(alpha) K K^T); wave wv owns row block wv.
+  // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T); wave wv owns row block wv.
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     f32x4 acc = zero4();
-    if (nb <= wv) acc = mma16<E>(sK + 16 * wv * L::LK, L::LK, sK + 16 * nb * L::LK, L::LK, 0, DK, acc, lane);
+    if (nb <= wv) acc = mma<E, false, false>(sK + rA * L::LK, L::LK, sK + 16 * nb * L::LK, L::LK, 0, DK, acc, lane);
     const int col = 16 * nb + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wv + 4 * (lane >> 4) + i;
+      const int row = rA + 4 * (lane >> 4) + i;
       sA[row * L::LF + col] = row > col ? sAl[row] * acc[i] : 0.f;
+    }
+    if (mout) {
+      f32x4 m = zero4();
+      if (nb <= wv) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          m = Mma<E>::step(qA[ks], frag_rm<E>(sK + 16 * nb * L::LK + ks * KC, L::LK, lane), m);
+        if (nb == wv) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((lane & 15) > 4 * (lane >> 4) + i) m[i] = 0.f;
+        }
+      }
+      st_frag_lds<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
     }
   }
   __syncthreads();
+  if (mout) {  // M [64][64] of this (chunk, head), 16-byte stores
+    E* gm = mout + ((int64_t)slot * g.H + h) * 64 * 64;
+    s2g<E, 64>(gm, 64, sM, L::LT, kChunk, tid);
+    __syncthreads();
+  }
   invert_unit_lower64(sA, sX, sScr, tid);
 
-  // T = X diag(alpha)
+  // T = X diag(alpha), written over A (A is no longer needed).
   for (int i = tid; i < 64 * 64; i += kThreads) {
     const int r = i >> 6, c = i & 63;
     sT[r * L::LT + c] = to_e<E>(sX[r * L::LF + c] * sAl[c]);
@@ -98,24 +135,27 @@ __global__ __launch_bounds__(kThreads) void ut_fwd_kernel(Geom g, const E* __res
 
   // W = T K, U = T V; T is lower triangular, so row block wv needs columns < 16 (wv + 1).
   const int k1 = round_up_kc<E>(16 * (wv + 1));
+  f32x4 Wf[DK / 16], Uf[DV / 16];
 #pragma unroll
-  for (int nb = 0; nb < DK / 16; ++nb) {
-    f32x4 acc = mma16<E>(sT + 16 * wv * L::LT, L::LT, sKt + 16 * nb * L::LT, L::LT, 0, k1, zero4(), lane);
-    st_frag_lds<E>(sK + 16 * wv * L::LK + 16 * nb, L::LK, acc, lane);
-  }
+  for (int nb = 0; nb < DK / 16; ++nb)
+    Wf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sK + 16 * nb, L::LK, 0, k1, zero4(), lane);
 #pragma unroll
-  for (int nb = 0; nb < DV / 16; ++nb) {
-    f32x4 acc = mma16<E>(sT + 16 * wv * L::LT, L::LT, sVt + 16 * nb * L::LT, L::LT, 0, k1, zero4(), lane);
-    st_frag_lds<E>(sU + 16 * wv * L::LV + 16 * nb, L::LV, acc, lane);
-  }
+  for (int nb = 0; nb < DV / 16; ++nb)
+    Uf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sV + 16 * nb, L::LV, 0, k1, zero4(), lane);
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < DK / 16; ++nb) st_frag_lds<E>(sK + rA * L::LK + 16 * nb, L::LK, Wf[nb], lane);
+#pragma unroll
+  for (int nb = 0; nb < DV / 16; ++nb) st_frag_lds<E>(sV + rA * L::LV + 16 * nb, L::LV, Uf[nb], lane);
   __syncthreads();
   s2g<E, DK>(w + row0 * DK, DK, sK, L::LK, n, tid);
-  s2g<E, DV>(u + row0 * DV, DV, sU, L::LV, n, tid);
+  s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
 }
 
 template <typename E, int DK, int DV>
-static hipError_t ut_go(const Shape& s, const int* table, const void* k, const void* v,
-                        const void* beta, void* w, void* u, hipStream_t st) {
+static hipError_t ut_go(const Shape& s, const int* table, const void* q, const void* k,
+                        const void* v, const void* beta, void* w, void* u, void* m,
+                        hipStream_t st) {
   typedef UtFwdLds<E, DK, DV> L;
   static bool attr = false;
   if (!attr) {
@@ -128,8 +168,8 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* k, const v
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
   hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
-                     st, make_geom(s, table), (const E*)k, (const E*)v, (const E*)beta, (E*)w,
-                     (E*)u);
+                     st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
+                     (const E*)beta, (E*)w, (E*)u, (E*)m);
   hipError_t e = hipGetLastError();
   prof_end("ut_fwd", st);
   return e;
@@ -147,15 +187,16 @@ size_t lds_ut_fwd(Dt dt, int dk, int dv) {
   return 0;
 }
 
-hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* k, const void* v,
-                         const void* beta, void* w, void* u, hipStream_t st) {
+hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
+                         const void* v, const void* beta, void* w, void* u, void* m,
+                         hipStream_t st) {
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) return ut_go<__bf16, 64, 64>(s, table, k, v, beta, w, u, st);
-    if (s.dk == 64 && s.dv == 128) return ut_go<__bf16, 64, 128>(s, table, k, v, beta, w, u, st);
-    if (s.dk == 128 && s.dv == 64) return ut_go<__bf16, 128, 64>(s, table, k, v, beta, w, u, st);
-    return ut_go<__bf16, 128, 128>(s, table, k, v, beta, w, u, st);
+    if (s.dk == 64 && s.dv == 64) return ut_go<__bf16, 64, 64>(s, table, q, k, v, beta, w, u, m, st);
+    if (s.dk == 64 && s.dv == 128) return ut_go<__bf16, 64, 128>(s, table, q, k, v, beta, w, u, m, st);
+    if (s.dk == 128 && s.dv == 64) return ut_go<__bf16, 128, 64>(s, table, q, k, v, beta, w, u, m, st);
+    return ut_go<__bf16, 128, 128>(s, table, q, k, v, beta, w, u, m, st);
   }
-  return ut_go<float, 64, 64>(s, table, k, v, beta, w, u, st);
+  return ut_go<float, 64, 64>(s, table, q, k, v, beta, w, u, m, st);
 }
 
 }  // namespace efla

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 1
+#define EFLA_ABI_VERSION 2
 
 typedef enum {
   EFLA_OK = 0,
@@ -75,9 +75,10 @@ typedef struct {
  *            slot = b * ceil(T/64) + c (dense batch) or chunk_start[s] + c (packed),
  *            where chunk_start[s] = sum over earlier sequences of ceil(len/64)
  *   table  : chunk_start, int32 [n_seqs+1] (packed batches only, else unused)
+ *   m      : tril(Q K^T) of each chunk, [n_chunk_slots][H][64][64], problem dtype
  *   total  : size of the whole buffer = efla_saved_bytes()                               */
 typedef struct {
-  size_t w, ut, states, table, total;
+  size_t w, ut, states, table, m, total;
   int64_t n_chunk_slots;
 } efla_saved_layout;
 
