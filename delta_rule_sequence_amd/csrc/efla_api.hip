@@ -134,10 +134,11 @@ size_t bytes_v(const Shape& s) { return (size_t)s.B * s.H * s.T * s.dv * esize(s
 size_t bytes_states(const Shape& s) { return (size_t)s.slots * s.H * s.dk * s.dv * esize(s); }
 size_t bytes_table(const Shape& s) { return s.cu ? (size_t)(s.n_seqs + 1) * 4 : 0; }
 size_t bytes_m(const Shape& s) { return (size_t)s.slots * s.H * kChunk * kChunk * esize(s); }
+size_t bytes_x(const Shape& s) { return bytes_m(s); }
 
 // Layout of the forward->backward buffer.
 struct Saved {
-  size_t w, ut, states, table, m, total;
+  size_t w, ut, states, table, m, x, total;
 };
 Saved saved_layout(const Shape& s) {
   Saved L;
@@ -152,6 +153,8 @@ Saved saved_layout(const Shape& s) {
   o += align_up(bytes_table(s));
   L.m = o;
   o += align_up(bytes_m(s));
+  L.x = o;
+  o += align_up(bytes_x(s));
   L.total = o;
   return L;
 }
@@ -177,12 +180,12 @@ bool empty(const Shape& s) { return s.T == 0; }
 // Forward stages shared by efla_fwd and the recompute path of efla_bwd.
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                         const void* beta, void* o, unsigned char* w, unsigned char* ut,
-                        unsigned char* states, int* table, unsigned char* m, unsigned char* u,
-                        hipStream_t st) {
+                        unsigned char* states, int* table, unsigned char* m, unsigned char* x,
+                        unsigned char* u, hipStream_t st) {
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, w, u, m, st))) return r;
+  if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, w, u, m, x, st))) return r;
   return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, st));
 }
 
@@ -236,6 +239,7 @@ efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out)
   out->states = L.states;
   out->table = L.table;
   out->m = L.m;
+  out->x = L.x;
   out->total = L.total;
   out->n_chunk_slots = s.slots;
   return EFLA_OK;
@@ -267,7 +271,7 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, w, u, nullptr, st));
+  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, w, u, nullptr, nullptr, st));
 }
 
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -294,7 +298,8 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
   unsigned char* states = sv ? sv + L.states : nullptr;
   int* table = sv ? (int*)(sv + L.table) : table_ws;
   unsigned char* m = sv ? sv + L.m : m_ws;
-  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, u, (hipStream_t)stream);
+  unsigned char* x = sv ? sv + L.x : nullptr;
+  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, (hipStream_t)stream);
 }
 
 efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -321,7 +326,8 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
     unsigned char* rec = dstates + align_up(bytes_states(s));
     unsigned char* u = rec + L.total;
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
-                                    rec + L.states, (int*)(rec + L.table), rec + L.m, u, st))
+                                    rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
+                                    u, st))
       return r;
     sv = rec;
   }
@@ -329,7 +335,7 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
   if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o, dut, dstates, st)))
     return r;
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
-                                     dstates, dq, dk, dv, dbeta, st));
+                                     dstates, sv + L.x, dq, dk, dv, dbeta, st));
 }
 
 efla_status efla_profile_enable(int on) {

@@ -22,6 +22,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes in registers
 
 constexpr int kChunk = 64;
 constexpr int kThreads = 256;
@@ -201,6 +202,18 @@ EFLA_DEV void st_frag_rows(E* __restrict__ g, int64_t ld, f32x4 c, int lane, int
 }
 
 // ---------------------------------------------------------------------------
+// A 16-byte vector, or zero unless `keep`. Written as a bitwise mask: a conditional
+// expression over register arrays can otherwise become a select between two private-memory
+// addresses (the arrays then live in scratch).
+EFLA_DEV u32x4 keep_if(u32x4 x, bool keep) {
+  const unsigned m = keep ? ~0u : 0u;
+  return x & m;
+}
+template <typename Vt> EFLA_DEV Vt keep_if_vec(Vt x, bool keep) {
+  static_assert(sizeof(Vt) == 16, "16-byte vectors only");
+  return __builtin_bit_cast(Vt, keep_if(__builtin_bit_cast(u32x4, x), keep));
+}
+
 // Global -> LDS tile copies (64 rows, rows >= nvalid read as zero).
 // ---------------------------------------------------------------------------
 template <typename E, int COLS>
@@ -213,9 +226,9 @@ EFLA_DEV void g2s(E* s, int ld, const E* __restrict__ g, int64_t gld, int nvalid
     const int i = it * kThreads + tid;
     if (TOT % kThreads == 0 || i < TOT) {
       const int r = i / VPR, c = (i % VPR) * V;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nvalid) val = *(const uint4*)(g + (int64_t)r * gld + c);
-      *(uint4*)(s + r * ld + c) = val;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if (r < nvalid) val = *(const u32x4*)(g + (int64_t)r * gld + c);
+      *(u32x4*)(s + r * ld + c) = val;
     }
   }
 }
@@ -275,18 +288,19 @@ EFLA_DEV void g2s_t(E* s, int ld, const E* __restrict__ g, int64_t gld, int nval
     g2s_t_impl_bf16<COLS>((__bf16*)s, ld, (const __bf16*)g, gld, nvalid, tid);
 }
 
-// Copy 64 rows of an LDS tile to global memory with 16-byte stores, rows < nvalid only.
-template <typename E, int COLS>
+// Copy 64 rows of an LDS tile to global memory with 16-byte stores, rows < nvalid only
+// (NT threads cooperate).
+template <typename E, int COLS, int NT = kThreads>
 EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid, int tid) {
   constexpr int V = 16 / sizeof(E);
   constexpr int VPR = COLS / V;
   constexpr int TOT = kChunk * VPR;
 #pragma unroll
-  for (int it = 0; it < (TOT + kThreads - 1) / kThreads; ++it) {
-    const int i = it * kThreads + tid;
-    if (TOT % kThreads == 0 || i < TOT) {
+  for (int it = 0; it < (TOT + NT - 1) / NT; ++it) {
+    const int i = it * NT + tid;
+    if (TOT % NT == 0 || i < TOT) {
       const int r = i / VPR, c = (i % VPR) * V;
-      if (r < nvalid) *(uint4*)(g + (int64_t)r * gld + c) = *(const uint4*)(s + r * ld + c);
+      if (r < nvalid) *(u32x4*)(g + (int64_t)r * gld + c) = *(const u32x4*)(s + r * ld + c);
     }
   }
 }

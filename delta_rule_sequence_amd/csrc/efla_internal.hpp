@@ -32,7 +32,7 @@ hipError_t launch_chunk_table(const Shape& s, int* table, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const void* k, const void* beta, float* lam, float* alpha,
                        float* ex, float* dlam, hipStream_t st);
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                         const void* v, const void* beta, void* w, void* u, void* m,
+                         const void* v, const void* beta, void* w, void* u, void* m, void* x,
                          hipStream_t st);
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
@@ -42,8 +42,9 @@ hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, cons
                            void* dstates, hipStream_t st);
 hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, const void* k,
                             const void* v, const void* beta, const void* d_o, const void* ut,
-                            const void* dut, const void* states, const void* dstates, void* dq,
-                            void* dk, void* dv, void* dbeta, hipStream_t st);
+                            const void* dut, const void* states, const void* dstates,
+                            const void* x, void* dq, void* dk, void* dv, void* dbeta,
+                            hipStream_t st);
 
 // Dynamic LDS bytes of each kernel for a head-size pair (0 = combination not built).
 size_t lds_ut_fwd(Dt dt, int dk, int dv);

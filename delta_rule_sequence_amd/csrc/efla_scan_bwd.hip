@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
   const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
 
   V kA[KS], kN[KS];
-  uint4 qR[VQ], wR[VQ], mR[VM], oR[VO];
+  u32x4 qR[VQ], wR[VQ], mR[VM], oR[VO];
 
   auto load_chunk = [&](int c) {
     const int n = min(kChunk, si.len - c * kChunk);
@@ -79,19 +79,17 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
-      qR[it] = *(const uint4*)(q + (r0 + r) * DK + cc);
-      wR[it] = *(const uint4*)(w + (r0 + r) * DK + cc);
+      qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
+      wR[it] = *(const u32x4*)(w + (r0 + r) * DK + cc);
     }
     const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
 #pragma unroll
-    for (int it = 0; it < VM; ++it) mR[it] = *(const uint4*)(mc + (it * kThreads + tid) * VE);
+    for (int it = 0; it < VM; ++it) mR[it] = *(const u32x4*)(mc + (it * kThreads + tid) * VE);
 #pragma unroll
-    for (int it = 0; it < VO; ++it) {
-      const int i = it * kThreads + tid;
-      if (i < 64 * OPR) {
-        const int r = min(i / OPR, n - 1), cc = (i % OPR) * VE;
-        oR[it] = *(const uint4*)(d_o + (r0 + r) * DV + v0 + cc);
-      }
+    for (int it = 0; it < VO; ++it) {  // unconditional (clamped) so no load sits in a branch
+      const int i = min(it * kThreads + tid, 64 * OPR - 1);
+      const int r = min(i / OPR, n - 1), cc = (i % OPR) * VE;
+      oR[it] = *(const u32x4*)(d_o + (r0 + r) * DV + v0 + cc);
     }
   };
   auto commit_chunk = [&](int c, unsigned char* st) {
@@ -102,26 +100,25 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     E* sO = (E*)(st + L::oO);
     const bool rowok = rA + (lane & 15) < n;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kA[ks] = rowok ? kN[ks] : zero_vec<E>();
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < KS; ++ks) kA[ks] = keep_if_vec(kN[ks], rowok);
 #pragma unroll
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
-      *(uint4*)(sQ + r * L::LK + cc) = r < n ? qR[it] : z;
-      *(uint4*)(sW + r * L::LK + cc) = r < n ? wR[it] : z;
+      *(u32x4*)(sQ + r * L::LK + cc) = keep_if(qR[it], r < n);
+      *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
     }
 #pragma unroll
     for (int it = 0; it < VM; ++it) {
       const int i = (it * kThreads + tid) * VE;
-      *(uint4*)(sM + (i / 64) * L::LT + i % 64) = mR[it];
+      *(u32x4*)(sM + (i / 64) * L::LT + i % 64) = mR[it];
     }
 #pragma unroll
     for (int it = 0; it < VO; ++it) {
       const int i = it * kThreads + tid;
       if (i < 64 * OPR) {
         const int r = i / OPR, cc = (i % OPR) * VE;
-        *(uint4*)(sO + r * L::LS + cc) = r < n ? oR[it] : z;
+        *(u32x4*)(sO + r * L::LS + cc) = keep_if(oR[it], r < n);
       }
     }
   };
@@ -157,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
       constexpr int VPR = TV / VE;
       for (int i = tid; i < DK * VPR; i += kThreads) {
         const int d = i / VPR, cc = (i % VPR) * VE;
-        *(uint4*)(gG + (int64_t)d * DV + cc) = *(const uint4*)(sG + d * L::LS + cc);
+        *(u32x4*)(gG + (int64_t)d * DV + cc) = *(const u32x4*)(sG + d * L::LS + cc);
       }
     }
     // dU~ = scale M^T dO + K G for this wave's rows (tokens j).

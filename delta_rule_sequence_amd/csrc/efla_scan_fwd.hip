@@ -36,7 +36,7 @@ struct ScanFwdStage {
   static constexpr int KV = 64 * DK * (int)sizeof(E) / 16 / kThreads;
   V w[KS], q[KS], m[KM];
   E u[NB][4];
-  uint4 k[KV];
+  u32x4 k[KV];
 };
 
 template <typename E, int DK, int DV, int TV>
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_fwd_kernel(
     for (int it = 0; it < KV; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
-      P.k[it] = *(const uint4*)(k + (r0 + r) * DK + cc);
+      P.k[it] = *(const u32x4*)(k + (r0 + r) * DK + cc);
     }
   };
   // Move stage P (chunk c) into the working registers and the LDS buffer sk.
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_fwd_kernel(
     const bool rowok = rA + (lane & 15) < n;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      wA[ks] = rowok ? P.w[ks] : zero_vec<E>();
-      qA[ks] = rowok ? P.q[ks] : zero_vec<E>();
+      wA[ks] = keep_if_vec(P.w[ks], rowok);
+      qA[ks] = keep_if_vec(P.q[ks], rowok);
     }
 #pragma unroll
     for (int ks = 0; ks < KM; ++ks) mA[ks] = P.m[ks];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_fwd_kernel(
     for (int it = 0; it < KV; ++it) {
       const int i = it * kThreads + tid;
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
-      *(uint4*)(sk + r * L::LK + cc) = r < n ? P.k[it] : make_uint4(0u, 0u, 0u, 0u);
+      *(u32x4*)(sk + r * L::LK + cc) = keep_if(P.k[it], r < n);
     }
   };
 
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_fwd_kernel(
       constexpr int VPR = TV / VE;
       for (int i = tid; i < DK * VPR; i += kThreads) {
         const int d = i / VPR, cc = (i % VPR) * VE;
-        *(uint4*)(gS + (int64_t)d * DV + cc) = *(const uint4*)(sS + d * L::LS + cc);
+        *(u32x4*)(gS + (int64_t)d * DV + cc) = *(const u32x4*)(sS + d * L::LS + cc);
       }
     }
     // U~ = U - W S and P = Q S for this wave's rows.

@@ -3,11 +3,12 @@
 // Exact Flow Linear Attention summary page, section 3.3 (chunkwise form with the UT
 // transform; the WY/UT representation is the DeltaNet prior art of the fifth page):
 //   alpha_i = exact-flow step of token i,  A = strictly_lower(diag(alpha) K K^T),
-//   T = (I + A)^{-1} diag(alpha),  W = T K,  U = T V,   M = tril(Q K^T).
+//   X = (I + A)^{-1},  T = X diag(alpha),  W = T K,  U = T V,   M = tril(Q K^T).
 // K K^T, Q K^T, T K and T V are MFMA contractions (products over the token index read the
 // row-major K and V tiles k-major); the unit lower triangular inverse is a blocked forward
 // substitution in fp32 in LDS. Padded rows of a tail chunk read as zero (their beta is zero,
-// so alpha = 0 and they do not touch the valid rows). M is optional (q may be null).
+// so alpha = 0 and they do not touch the valid rows). M (q may be null) and X (kept for the
+// backward pass, which then needs no inverse of its own) are optional outputs.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -28,7 +29,8 @@ struct UtFwdLds {
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const E* __restrict__ beta, E* __restrict__ w, E* __restrict__ u, E* __restrict__ mout) {
+    const E* __restrict__ beta, E* __restrict__ w, E* __restrict__ u, E* __restrict__ mout,
+    E* __restrict__ xout) {
   typedef UtFwdLds<E, DK, DV> L;
   typedef typename Mma<E>::vec Vv;
   constexpr int KC = Mma<E>::KC, KS = DK / KC;
@@ -126,10 +128,36 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   }
   invert_unit_lower64(sA, sX, sScr, tid);
 
-  // T = X diag(alpha), written over A (A is no longer needed).
-  for (int i = tid; i < 64 * 64; i += kThreads) {
-    const int r = i >> 6, c = i & 63;
-    sT[r * L::LT + c] = to_e<E>(sX[r * L::LF + c] * sAl[c]);
+  // T = X diag(alpha), written over A (A is no longer needed); X to global memory.
+  {
+    E* gx = xout ? xout + ((int64_t)slot * g.H + h) * 64 * 64 : nullptr;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // 8 consecutive elements of one row per thread
+      const int i = it * kThreads + tid;
+      const int r = i >> 3, c = (i & 7) * 8;
+      const f32x4 x0 = *(const f32x4*)(sX + r * L::LF + c);
+      const f32x4 x1 = *(const f32x4*)(sX + r * L::LF + c + 4);
+      const f32x4 a0 = *(const f32x4*)(sAl + c), a1 = *(const f32x4*)(sAl + c + 4);
+      if constexpr (sizeof(E) == 2) {
+        bf16x8 xe, te;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xe[e] = (__bf16)x0[e];
+          xe[e + 4] = (__bf16)x1[e];
+          te[e] = (__bf16)(x0[e] * a0[e]);
+          te[e + 4] = (__bf16)(x1[e] * a1[e]);
+        }
+        *(bf16x8*)(sT + r * L::LT + c) = te;
+        if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
+      } else {
+        *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
+        *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
+        if (gx) {
+          *(f32x4*)(gx + r * 64 + c) = x0;
+          *(f32x4*)(gx + r * 64 + c + 4) = x1;
+        }
+      }
+    }
   }
   __syncthreads();
 
@@ -154,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
 
 template <typename E, int DK, int DV>
 static hipError_t ut_go(const Shape& s, const int* table, const void* q, const void* k,
-                        const void* v, const void* beta, void* w, void* u, void* m,
+                        const void* v, const void* beta, void* w, void* u, void* m, void* x,
                         hipStream_t st) {
   typedef UtFwdLds<E, DK, DV> L;
   static bool attr = false;
@@ -169,7 +197,7 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
   prof_begin(st);
   hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
                      st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)beta, (E*)w, (E*)u, (E*)m);
+                     (const E*)beta, (E*)w, (E*)u, (E*)m, (E*)x);
   hipError_t e = hipGetLastError();
   prof_end("ut_fwd", st);
   return e;
@@ -188,15 +216,15 @@ size_t lds_ut_fwd(Dt dt, int dk, int dv) {
 }
 
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                         const void* v, const void* beta, void* w, void* u, void* m,
+                         const void* v, const void* beta, void* w, void* u, void* m, void* x,
                          hipStream_t st) {
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) return ut_go<__bf16, 64, 64>(s, table, q, k, v, beta, w, u, m, st);
-    if (s.dk == 64 && s.dv == 128) return ut_go<__bf16, 64, 128>(s, table, q, k, v, beta, w, u, m, st);
-    if (s.dk == 128 && s.dv == 64) return ut_go<__bf16, 128, 64>(s, table, q, k, v, beta, w, u, m, st);
-    return ut_go<__bf16, 128, 128>(s, table, q, k, v, beta, w, u, m, st);
+    if (s.dk == 64 && s.dv == 64) return ut_go<__bf16, 64, 64>(s, table, q, k, v, beta, w, u, m, x, st);
+    if (s.dk == 64 && s.dv == 128) return ut_go<__bf16, 64, 128>(s, table, q, k, v, beta, w, u, m, x, st);
+    if (s.dk == 128 && s.dv == 64) return ut_go<__bf16, 128, 64>(s, table, q, k, v, beta, w, u, m, x, st);
+    return ut_go<__bf16, 128, 128>(s, table, q, k, v, beta, w, u, m, x, st);
   }
-  return ut_go<float, 64, 64>(s, table, q, k, v, beta, w, u, m, st);
+  return ut_go<float, 64, 64>(s, table, q, k, v, beta, w, u, m, x, st);
 }
 
 }  // namespace efla

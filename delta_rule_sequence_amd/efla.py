@@ -67,8 +67,8 @@ def efla_saved_bytes(p) -> int:
 def efla_get_saved_layout(p) -> dict:
     out = _lib.EflaSavedLayout()
     _lib.check("efla_get_saved_layout", _lib.lib().efla_get_saved_layout(ctypes.byref(p), ctypes.byref(out)))
-    return dict(w=out.w, ut=out.ut, states=out.states, table=out.table, m=out.m, total=out.total,
-                n_chunk_slots=out.n_chunk_slots)
+    return dict(w=out.w, ut=out.ut, states=out.states, table=out.table, m=out.m, x=out.x,
+                total=out.total, n_chunk_slots=out.n_chunk_slots)
 
 
 def _bytes(n, device):
@@ -151,7 +151,7 @@ def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None
 
 def saved_views(saved, q, k, v, beta, scale=1.0, cu_seqlens=None):
     """Tensor views of a saved buffer: W [B,H,T,dk], U~ [B,H,T,dv], states [slots,H,dk,dv],
-    M = tril(Q K^T) per chunk [slots,H,64,64]."""
+    M = tril(Q K^T) and X = (I + A)^{-1} per chunk [slots,H,64,64]."""
     p = make_problem(q, k, v, beta, scale, cu_seqlens)
     L = efla_get_saved_layout(p)
     B, H, T, dk = k.shape
@@ -165,7 +165,8 @@ def saved_views(saved, q, k, v, beta, scale=1.0, cu_seqlens=None):
         return saved[off:off + n * es].view(k.dtype).view(*shape)
     return dict(w=view(L["w"], (B, H, T, dk)), ut=view(L["ut"], (B, H, T, dv)),
                 states=view(L["states"], (L["n_chunk_slots"], H, dk, dv)),
-                m=view(L["m"], (L["n_chunk_slots"], H, 64, 64)))
+                m=view(L["m"], (L["n_chunk_slots"], H, 64, 64)),
+                x=view(L["x"], (L["n_chunk_slots"], H, 64, 64)))
 
 
 class EflaFunction(torch.autograd.Function):

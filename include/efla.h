@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 2
+#define EFLA_ABI_VERSION 3
 
 typedef enum {
   EFLA_OK = 0,
@@ -76,9 +76,11 @@ typedef struct {
  *            where chunk_start[s] = sum over earlier sequences of ceil(len/64)
  *   table  : chunk_start, int32 [n_seqs+1] (packed batches only, else unused)
  *   m      : tril(Q K^T) of each chunk, [n_chunk_slots][H][64][64], problem dtype
+ *   x      : X = (I + strictly_lower(diag(alpha) K K^T))^{-1} of each chunk (so that
+ *            T = X diag(alpha)), [n_chunk_slots][H][64][64], problem dtype
  *   total  : size of the whole buffer = efla_saved_bytes()                               */
 typedef struct {
-  size_t w, ut, states, table, m, total;
+  size_t w, ut, states, table, m, x, total;
   int64_t n_chunk_slots;
 } efla_saved_layout;
 
@@ -119,7 +121,7 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
                           void* w, void* u, void* ws, size_t ws_bytes, void* stream);
 
 /* Forward: o [B,H,T,dv] (problem dtype). `saved` (NULL, or efla_saved_bytes(p) bytes)
- * receives W, U~ and the chunk states for efla_bwd. ws: efla_workspace_bytes(p, 0). */
+ * receives W, U~, the chunk states, M and X for efla_bwd. ws: efla_workspace_bytes(p, 0). */
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
                      const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
                      size_t ws_bytes, void* stream);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 2
+    assert L.efla_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -88,12 +88,13 @@ def test_workspace_and_saved_sizes(L):
     w = tok * 128 * e
     states = slots * 16 * 128 * 128 * e
     m = slots * 16 * 64 * 64 * e
-    assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states + m
+    assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states + 2 * m
     assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * w + m
-    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states + m) + w
+    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states + 2 * m) + w
     lay = _lib.EflaSavedLayout()
     assert L.efla_get_saved_layout(ctypes.byref(p), ctypes.byref(lay)) == 0
-    assert (lay.w, lay.ut, lay.states, lay.m, lay.n_chunk_slots) == (0, w, 2 * w, 2 * w + states, slots)
+    assert (lay.w, lay.ut, lay.states, lay.m, lay.x, lay.n_chunk_slots) == \
+        (0, w, 2 * w, 2 * w + states, 2 * w + states + m, slots)
     # packed batch: chunk slots are bounded by T/64 + n_seqs
     pp = _p(B=1, T=1000, cu=0x1000, n_seqs=7)
     assert L.efla_get_saved_layout(ctypes.byref(pp), ctypes.byref(lay)) == 0
