@@ -38,19 +38,20 @@ def kernel_model(name, dk, dv, e, C=CHUNK):
     """Algorithmic HBM bytes and flops of one kernel per (chunk, head) unit.
 
     Bytes are the tensors the kernel must read and write at its interface (each once);
-    flops count the dense tile contractions (2 per multiply-add)."""
-    if name == "ut_fwd":      # K, V, beta -> W, U
-        b = e * (C * dk + C * dv + C) + e * (C * dk + C * dv)
-        f = 2 * C * C * dk + C ** 3 / 3 + 2 * C * C * (dk + dv)
-    elif name == "scan_fwd":  # Q, K, W, U -> O, U~, S_c
-        b = e * (3 * C * dk + C * dv) + e * (2 * C * dv + dk * dv)
-        f = 2 * C * C * (dk + dv) + 6 * C * dk * dv
-    elif name == "scan_bwd":  # Q, K, W, dO -> dU~, dS
-        b = e * (3 * C * dk + C * dv) + e * (C * dv + dk * dv)
-        f = 2 * C * C * (dk + dv) + 6 * C * dk * dv
-    elif name == "chunk_bwd":  # Q, K, V, dO, U~, dU~, beta, S_c, dS -> dQ, dK, dV, dbeta
-        b = e * (2 * C * dk + 4 * C * dv + C + 2 * dk * dv) + e * (2 * C * dk + C * dv + C)
-        f = 6 * C * dk * dv + 12 * C * C * dk + 6 * C * C * dv + 4 * C ** 3
+    flops count the tile contractions the method needs, triangular factors at half size
+    (2 per multiply-add)."""
+    if name == "ut_fwd":      # Q, K, V, beta -> W, U, M = tril(QK^T), X = (I + A)^-1
+        b = e * (2 * C * dk + C * dv + C) + e * (C * dk + C * dv + 2 * C * C)
+        f = 3 * C * C * dk + C * C * dv + C ** 3 / 3
+    elif name == "scan_fwd":  # Q, K, W, U, M -> O, U~, S_c
+        b = e * (3 * C * dk + C * dv + C * C) + e * (2 * C * dv + dk * dv)
+        f = 6 * C * dk * dv + C * C * dv
+    elif name == "scan_bwd":  # Q, K, W, M, dO -> dU~, dS_c
+        b = e * (3 * C * dk + C * C + C * dv) + e * (C * dv + dk * dv)
+        f = 6 * C * dk * dv + C * C * dv
+    elif name == "chunk_bwd":  # Q, K, V, dO, U~, dU~, beta, S_c, dS_c, X -> dQ, dK, dV, dbeta
+        b = e * (2 * C * dk + 4 * C * dv + C + 2 * dk * dv + C * C) + e * (2 * C * dk + C * dv + C)
+        f = 6 * C * dk * dv + 7 * C * C * dk + 3 * C * C * dv + 2 * C ** 3 / 3
     else:
         return 0.0, 0.0
     return float(b), float(f)

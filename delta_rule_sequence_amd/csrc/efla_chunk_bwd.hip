@@ -18,6 +18,8 @@
 // LDS), so the workgroup pays the memory latency once. S and G are only ever read as
 // row-major MFMA operands and go straight from global memory into registers. Products over
 // the token index read their row-major LDS tiles k-major (LDS transpose reads for bf16).
+// Each wave computes 2x2 (or 2x1) blocks of 16x16 so that every operand fragment it reads
+// from LDS feeds two MFMAs: LDS bandwidth, not the matrix cores, bounds the arithmetic.
 // Seven barrier-separated steps:
 //   1 loads land; 2 dW, scale dO S^T, U~ G^T, dM, coefficients;
 //   3 dT (-> dalpha, dX), T^T dU, T^T dW, dM K, dM^T Q;
@@ -75,21 +77,34 @@ struct TileRegs {
   }
 };
 
-// Split of a [64][D] output over the eight waves: column block cb, row blocks rb0..rb0+NRB.
-template <int D>
-struct Part {
-  static constexpr int NCB = D / 16, WPC = kBwdWaves / NCB, NRB = 4 / WPC;
-  static_assert(NCB * WPC == kBwdWaves && NRB * WPC == 4, "wave split");
+// Zero a 16x16 block above the diagonal (nb > rb) and, on the diagonal (nb == rb), the
+// entries above it (keep_diag) or on and above it.
+EFLA_DEV f32x4 tri_mask(f32x4 c, int rb, int nb, bool keep_diag, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * rb + 4 * (lane >> 4) + i, col = 16 * nb + (lane & 15);
+    if (keep_diag ? r < col : r <= col) c[i] = 0.f;
+  }
+  return c;
+}
+
+// One (chunk, head) work unit: valid rows, first row of the chunk in the [B,H,T,*] tensors,
+// index of its [slot][H] state / X block.
+struct BwdUnit {
+  int n;
+  int64_t row0, sh;
 };
 
-// The 16 blocks of a 64x64 matrix, two per wave: the ten lower blocks (diagonal included)
-// first, then the six strictly upper ones.
-// Entry idx is the nibble 4 rb + nb at bit 4 idx (a register constant, no table in memory).
-EFLA_DEV void block_of(int idx, int& rb, int& nb) {
-  constexpr uint64_t tab = 0xB76321FEDCA98540ull;
-  const int e = (int)(tab >> (4 * idx)) & 15;
-  rb = e >> 2;
-  nb = e & 3;
+// Unit u = slot * H + h (u below the number of used slots times H).
+EFLA_DEV BwdUnit bwd_unit(const Geom& g, int u) {
+  const int slot = u / g.H, h = u % g.H;
+  ChunkInfo ci;
+  chunk_info(g, slot, ci);
+  BwdUnit r;
+  r.n = max(ci.n, 1);
+  r.row0 = (int64_t)(ci.b * g.H + h) * g.T + ci.t0;
+  r.sh = (int64_t)slot * g.H + h;
+  return r;
 }
 
 template <typename E, int DK, int DV>
@@ -101,10 +116,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     E* __restrict__ dbeta) {
   typedef ChunkBwdLds<E, DK, DV> L;
   typedef typename Mma<E>::vec Vv;
-  typedef Part<DK> PK;
-  typedef Part<DV> PV;
   constexpr int LK = L::LK, LV = L::LV, LT = L::LT;
   constexpr int KC = Mma<E>::KC, KSV = DV / KC;
+  constexpr int CK = DK / 64, CV = DV / 64;  // column blocks per wave of [64][d] outputs
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   E* sK = (E*)(smem + L::oK);
   E* sQ = (E*)(smem + L::oQ);
@@ -125,42 +139,69 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   float* pCol = (float*)(smem + L::oP);  // [4][64]: column sums of dT . X per row block
   float* pRow = pCol + 4 * 64;           // [4][64]: row sums of dA . KK^T per column block
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int slot = blockIdx.x / g.H, h = blockIdx.x % g.H;
-  ChunkInfo ci;
-  if (!chunk_info(g, slot, ci)) return;
-  const int n = ci.n;
-  const int64_t row0 = (int64_t)(ci.b * g.H + h) * g.T + ci.t0;
-  const int64_t sh = (int64_t)slot * g.H + h;
-  const int cbK = wv % PK::NCB, rbK = (wv / PK::NCB) * PK::NRB;
-  const int cbV = wv % PV::NCB, rbV = (wv / PV::NCB) * PV::NRB;
+  int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Chunks of all heads are numbered u = slot * H + h; packed batches use a prefix of them.
+  const int nslots = g.cu ? min(g.table[g.n_seqs], g.max_slots) : g.max_slots;
+  const int nu = nslots * g.H;
+  int u = blockIdx.x;
+  if (u >= nu) return;
+  // [64][d] outputs: wave wv owns row blocks rb0, rb0 + 1 and column blocks cK.. (cV..).
+  const int rb0 = 2 * (wv >> 2), cK = CK * (wv & 3), cV = CV * (wv & 3);
+  // 64x64 work matrices: wave wv owns blocks (pr, pn) and (pr, pn + 1).
+  const int pr = wv >> 1, pn = 2 * (wv & 1);
+  const bool plow = pn <= pr;  // at least one of the two blocks is on or below the diagonal
 
-  // ---- 1: request everything, in order of first use
-  TileRegs<E, DK> tK;
+  TileRegs<E, DK> tK, tQ;
   TileRegs<E, DV> tDU, tDO, tU, tV;
   TileRegs<E, 64> tX;
-  TileRegs<E, DK> tQ;
-  Vv fS[KSV], fG[KSV];  // rows 16 cbK.. of S and of G (B^T operands, contraction over d_v)
-  tK.load(k + row0 * DK, n, tid);
-  const float bt = to_f(beta[row0 + min(tid & 63, n - 1)]);
-  tDU.load(dut + row0 * DV, n, tid);
-  {
-    const E* Sg = states + sh * DK * DV + (int64_t)16 * cbK * DV;
+  Vv fS[CK][KSV], fG[CK][KSV];  // rows of S and G for this wave's d_k columns (B^T operands)
+  float bt;
+  // Requests for a chunk's inputs, issued for the next chunk in small groups spread over
+  // the steps of the current one: a large burst would stall the issuing waves until the
+  // memory system had taken all of it.
+  auto issue_k = [&](const BwdUnit& c) {
+    tK.load(k + c.row0 * DK, c.n, tid);
+    bt = to_f(beta[c.row0 + min(lane, c.n - 1)]);
+  };
+  auto issue_du_do = [&](const BwdUnit& c) {
+    tDU.load(dut + c.row0 * DV, c.n, tid);
+    tDO.load(d_o + c.row0 * DV, c.n, tid);
+  };
+  auto issue_u = [&](const BwdUnit& c) { tU.load(ut + c.row0 * DV, c.n, tid); };
+  auto issue_v_x = [&](const BwdUnit& c) {
+    tV.load(v + c.row0 * DV, c.n, tid);
+    tX.load(xsav + c.sh * 64 * 64, 64, tid);
+  };
+  auto issue_q = [&](const BwdUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
+  auto issue_sg = [&](const BwdUnit& c) {
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) fS[ks] = frag_rm<E>(Sg + ks * KC, DV, lane);
-  }
-  tDO.load(d_o + row0 * DV, n, tid);
-  tU.load(ut + row0 * DV, n, tid);
-  {
-    const E* Gg = dstates + sh * DK * DV + (int64_t)16 * cbK * DV;
+    for (int j = 0; j < CK; ++j)
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) fG[ks] = frag_rm<E>(Gg + ks * KC, DV, lane);
-  }
-  tV.load(v + row0 * DV, n, tid);
-  tX.load(xsav + sh * 64 * 64, 64, tid);
-  tQ.load(q + row0 * DK, n, tid);
+      for (int ks = 0; ks < KSV; ++ks) {
+        const int64_t o = c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC;
+        fS[j][ks] = frag_rm<E>(states + o, DV, lane);
+        fG[j][ks] = frag_rm<E>(dstates + o, DV, lane);
+      }
+  };
 
-  // K lands first; ||k||^2 is reduced from the loaded vectors (VPR consecutive threads/row).
+  BwdUnit cur = bwd_unit(g, u);
+  issue_k(cur);
+  issue_du_do(cur);
+  issue_sg(cur);
+  issue_u(cur);
+  issue_v_x(cur);
+  issue_q(cur);
+  for (;;) {
+  // Every per-lane address below derives from tid; making it opaque here keeps the compiler
+  // from hoisting dozens of loop-invariant LDS addresses out of the loop (they would hold
+  // registers through the whole chunk and spill). Recomputing them costs a few ALU ops.
+  asm volatile("" : "+v"(tid));
+  lane = tid & 63;
+  const int n = cur.n;
+  const int64_t row0 = cur.row0;
+  // ---- 1: this chunk's tiles land in LDS; ||k||^2 is reduced from the loaded K vectors
+  // (VPR consecutive threads per row). Then the next chunk's tiles are requested.
   tK.store(sK, LK, n, tid);
   {
     typedef TileRegs<E, DK> TKr;
@@ -176,6 +217,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       if (i % TKr::VPR == 0) cLam[i / TKr::VPR] = i / TKr::VPR < n ? acc : 0.f;
     }
   }
+  const float bt_cur = bt;
   tDU.store(sDU, LV, n, tid);
   tDO.store(sDO, LV, n, tid);
   tU.store(sU, LV, n, tid);
@@ -183,163 +225,216 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   tX.store(sX, LT, 64, tid);
   tQ.store(sQ, LK, n, tid);
   __syncthreads();
+  const int un = u + (int)gridDim.x;
+  const bool more = un < nu;
+  const BwdUnit nxt = bwd_unit(g, more ? un : u);
+  issue_k(nxt);
 
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);
   //         dM = scale tril(dO U~^T); per-token coefficients
-  f32x4 aQ[PK::NRB], aK[PK::NRB];
+  f32x4 aQ[2][CK], aK[2][CK];
+  {
+    f32x4 aW[2][CK];
 #pragma unroll
-  for (int j = 0; j < PK::NRB; ++j) {
-    const int rb = rbK + j;
-    f32x4 w = zero4(), qq = zero4(), kk = zero4();
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < CK; ++j) aW[i][j] = aQ[i][j] = aK[i][j] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KSV; ++ks) {
-      w = Mma<E>::step(frag_rm<E>(sDU + 16 * rb * LV + ks * KC, LV, lane), fS[ks], w);
-      qq = Mma<E>::step(frag_rm<E>(sDO + 16 * rb * LV + ks * KC, LV, lane), fS[ks], qq);
-      kk = Mma<E>::step(frag_rm<E>(sU + 16 * rb * LV + ks * KC, LV, lane), fG[ks], kk);
-    }
-    st_frag_lds<E>(sW + 16 * rb * LK + 16 * cbK, LK, -w, lane);
-    aQ[j] = qq * g.scale;
-    aK[j] = kk;
-  }
+      Vv fu[2], fo[2], fv[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int rb, nb;
-    block_of(wv + kBwdWaves * t, rb, nb);
-    f32x4 acc = zero4();
-    if (nb <= rb) {
-      acc = mma<E, false, false>(sDO + 16 * rb * LV, LV, sU + 16 * nb * LV, LV, 0, DV, acc, lane);
-      if (nb == rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((lane & 15) > 4 * (lane >> 4) + i) acc[i] = 0.f;
+      for (int i = 0; i < 2; ++i) {
+        fu[i] = frag_rm<E>(sDU + 16 * (rb0 + i) * LV + ks * KC, LV, lane);
+        fo[i] = frag_rm<E>(sDO + 16 * (rb0 + i) * LV + ks * KC, LV, lane);
+        fv[i] = frag_rm<E>(sU + 16 * (rb0 + i) * LV + ks * KC, LV, lane);
       }
-      acc *= g.scale;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < CK; ++j) {
+          aW[i][j] = Mma<E>::step(fu[i], fS[j][ks], aW[i][j]);
+          aQ[i][j] = Mma<E>::step(fo[i], fS[j][ks], aQ[i][j]);
+          aK[i][j] = Mma<E>::step(fv[i], fG[j][ks], aK[i][j]);
+        }
     }
-    st_frag_lds<E>(sM + 16 * rb * LT + 16 * nb, LT, acc, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < CK; ++j) {
+        st_frag_lds<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, -aW[i][j], lane);
+        aQ[i][j] *= g.scale;
+      }
+  }
+  {
+    f32x4 m[1][2] = {{zero4(), zero4()}};
+    if (plow) mma_blk<E, false, false, 1, 2, DV>(sDO + 16 * pr * LV, LV, sU + 16 * pn * LV, LV, 0, DV, m, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      st_frag_lds<E>(sM + 16 * pr * LT + 16 * (pn + j), LT,
+                     tri_mask(m[0][j], pr, pn + j, true, lane) * g.scale, lane);
   }
   if (tid < 64) {
-    const FlowCoef cf = flow_coef(tid < n ? bt : 0.f, cLam[tid]);
+    const FlowCoef cf = flow_coef(tid < n ? bt_cur : 0.f, cLam[tid]);
     cAl[tid] = cf.alpha;
     cEx[tid] = cf.ex;
     cDl[tid] = cf.dlam;
   }
   __syncthreads();
+  issue_du_do(nxt);
 
   // ---- 3: dT = dW K^T + dU V^T -> dalpha (columns) and dX = dT diag(alpha) (strictly lower);
   //         dV = T^T dU, dK += T^T dW (T^T = diag(alpha) X^T); dQ += dM K; dK += dM^T Q
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int rb, nb;
-    block_of(wv + kBwdWaves * t, rb, nb);
-    f32x4 acc = zero4();
-    if (nb <= rb) {
-      acc = mma<E, false, false>(sW + 16 * rb * LK, LK, sK + 16 * nb * LK, LK, 0, DK, acc, lane);
-      acc = mma<E, false, false>(sDU + 16 * rb * LV, LV, sV + 16 * nb * LV, LV, 0, DV, acc, lane);
-    }
-    const int col = 16 * nb + (lane & 15);
-    const float al = cAl[col];
-    float cs = 0.f;
-    f32x4 dx;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rb + 4 * (lane >> 4) + i;
-      cs = fmaf(acc[i], to_f(sX[row * LT + col]), cs);  // X is zero above the diagonal
-      dx[i] = row > col ? acc[i] * al : 0.f;
-    }
-    cs += __shfl_xor(cs, 16);
-    cs += __shfl_xor(cs, 32);
-    if (lane < 16) pCol[rb * 64 + col] = cs;
-    st_frag_lds<E>(sDX + 16 * rb * LT + 16 * nb, LT, dx, lane);
-  }
-  f32x4 aV[PV::NRB];
-#pragma unroll
-  for (int j = 0; j < PV::NRB; ++j) {
-    const int rb = rbV + j;
-    f32x4 acc = mma<E, true, true>(sX + 16 * rb, LT, sDU + 16 * cbV, LV, round_down_kc<E>(16 * rb),
-                                   kChunk, zero4(), lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= cAl[16 * rb + 4 * (lane >> 4) + i];
-    aV[j] = acc;
-  }
-#pragma unroll
-  for (int j = 0; j < PK::NRB; ++j) {
-    const int rb = rbK + j;
-    f32x4 tw = mma<E, true, true>(sX + 16 * rb, LT, sW + 16 * cbK, LK, round_down_kc<E>(16 * rb),
-                                  kChunk, zero4(), lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aK[j][i] = fmaf(cAl[16 * rb + 4 * (lane >> 4) + i], tw[i], aK[j][i]);
-    aQ[j] = mma<E, false, true>(sM + 16 * rb * LT, LT, sK + 16 * cbK, LK, 0,
-                                round_up_kc<E>(16 * (rb + 1)), aQ[j], lane);
-    aK[j] = mma<E, true, true>(sM + 16 * rb, LT, sQ + 16 * cbK, LK, round_down_kc<E>(16 * rb),
-                               kChunk, aK[j], lane);
-  }
-  __syncthreads();
-
-  // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s); stage dQ and dV
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int rb, nb;
-    block_of(wv + kBwdWaves * t, rb, nb);
-    f32x4 acc = zero4();
-    if (nb <= rb)
-      acc = mma<E, false, false>(sDX + 16 * rb * LT, LT, sX + 16 * nb * LT, LT, 0,
-                                 round_up_kc<E>(16 * (nb + 1)), acc, lane);
-    st_frag_lds<E>(sY + 16 * rb * LT + 16 * nb, LT, acc, lane);
-  }
-#pragma unroll
-  for (int j = 0; j < PK::NRB; ++j) st_frag_lds<E>(sQ + 16 * (rbK + j) * LK + 16 * cbK, LK, aQ[j], lane);
-#pragma unroll
-  for (int j = 0; j < PV::NRB; ++j) st_frag_lds<E>(sDU + 16 * (rbV + j) * LV + 16 * cbV, LV, aV[j], lane);
-  __syncthreads();
-
-  // ---- 5: dA = -X^T Y (strictly lower) -> dalpha (rows) and H = dG + dG^T; write dQ, dV
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int rb, nb;
-    block_of(wv + kBwdWaves * t, rb, nb);
-    if (nb > rb) {
-      if (lane < 16) pRow[nb * 64 + 16 * rb + lane] = 0.f;
-      continue;
-    }
-    const f32x4 da = mma<E, true, true>(sX + 16 * rb, LT, sY + 16 * nb, LT,
-                                        round_down_kc<E>(16 * rb), kChunk, zero4(), lane);
-    const f32x4 kk = mma<E, false, false>(sK + 16 * rb * LK, LK, sK + 16 * nb * LK, LK, 0, DK,
-                                          zero4(), lane);
-    const int col = 16 * nb + (lane & 15);
-    float rs[4];
-    f32x4 dg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rb + 4 * (lane >> 4) + i;
-      const float a = row > col ? -da[i] : 0.f;
-      rs[i] = a * kk[i];
-      dg[i] = a * cAl[row];
+  {
+    f32x4 t[1][2] = {{zero4(), zero4()}};
+    if (plow) {
+      mma_blk<E, false, false, 1, 2, DK>(sW + 16 * pr * LK, LK, sK + 16 * pn * LK, LK, 0, DK, t, lane);
+      mma_blk<E, false, false, 1, 2, DV>(sDU + 16 * pr * LV, LV, sV + 16 * pn * LV, LV, 0, DV, t, lane);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = rs[i];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
-      rs[i] = x;
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pRow[nb * 64 + 16 * rb + 4 * (lane >> 4) + i] = rs[i];
-    }
-    if (nb < rb) {
-      st_frag_lds<E>(sH + 16 * rb * LT + 16 * nb, LT, dg, lane);
-      st_frag_t<E>(sH + 16 * nb * LT + 16 * rb, LT, dg, lane);
-    } else {
+    for (int j = 0; j < 2; ++j) {
+      if (pn + j > pr) t[0][j] = zero4();
+      const int col = 16 * (pn + j) + (lane & 15);
+      const float al = cAl[col];
+      float cs = 0.f;
+      f32x4 dx;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * rb + 4 * (lane >> 4) + i;
-        if (row > col) {
-          sH[row * LT + col] = to_e<E>(dg[i]);
-          sH[col * LT + row] = to_e<E>(dg[i]);
-        } else if (row == col) {
-          sH[row * LT + col] = to_e<E>(0.f);
+        const int row = 16 * pr + 4 * (lane >> 4) + i;
+        cs = fmaf(t[0][j][i], to_f(sX[row * LT + col]), cs);  // X is zero above the diagonal
+        dx[i] = row > col ? t[0][j][i] * al : 0.f;
+      }
+      cs += __shfl_xor(cs, 16);
+      cs += __shfl_xor(cs, 32);
+      if (lane < 16) pCol[pr * 64 + col] = cs;
+      st_frag_lds<E>(sDX + 16 * pr * LT + 16 * (pn + j), LT, dx, lane);
+    }
+  }
+  f32x4 aV[2][CV];
+  {
+    f32x4 tw[2][CK];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < CV; ++j) aV[i][j] = zero4();
+#pragma unroll
+      for (int j = 0; j < CK; ++j) tw[i][j] = zero4();
+    }
+    // T^T = diag(alpha) X^T is upper triangular: rows of block rb need k >= 16 rb.
+    const int k0 = round_down_kc<E>(16 * rb0);
+#pragma unroll
+    for (int kk = 0; kk < kChunk; kk += KC) {
+      if (kk < k0) continue;
+      Vv xa[2], bu[CV], bw[CK];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) xa[i] = frag_km<E>(sX + 16 * (rb0 + i) + kk * LT, LT, lane);
+#pragma unroll
+      for (int j = 0; j < CV; ++j) bu[j] = frag_km<E>(sDU + 16 * (cV + j) + kk * LV, LV, lane);
+#pragma unroll
+      for (int j = 0; j < CK; ++j) bw[j] = frag_km<E>(sW + 16 * (cK + j) + kk * LK, LK, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < CV; ++j) aV[i][j] = Mma<E>::step(xa[i], bu[j], aV[i][j]);
+#pragma unroll
+        for (int j = 0; j < CK; ++j) tw[i][j] = Mma<E>::step(xa[i], bw[j], tw[i][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float al = cAl[16 * (rb0 + i) + 4 * (lane >> 4) + e];
+#pragma unroll
+        for (int j = 0; j < CV; ++j) aV[i][j][e] *= al;
+#pragma unroll
+        for (int j = 0; j < CK; ++j) aK[i][j][e] = fmaf(al, tw[i][j][e], aK[i][j][e]);
+      }
+  }
+  // dM is lower triangular: dM K for rows of block rb needs k < 16 (rb + 1); dM^T Q needs
+  // k >= 16 rb.
+  mma_blk<E, false, true, 2, CK, kChunk>(sM + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0,
+                                         round_up_kc<E>(16 * (rb0 + 2)), aQ, lane);
+  mma_blk<E, true, true, 2, CK, kChunk>(sM + 16 * rb0, LT, sQ + 16 * cK, LK,
+                                        round_down_kc<E>(16 * rb0), kChunk, aK, lane);
+  __syncthreads();
+  issue_sg(nxt);  // S and G registers are free again
+
+  // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s); stage dQ and dV
+  {
+    f32x4 y[1][2] = {{zero4(), zero4()}};
+    if (plow)
+      mma_blk<E, false, false, 1, 2, kChunk>(sDX + 16 * pr * LT, LT, sX + 16 * pn * LT, LT, 0,
+                                             round_up_kc<E>(16 * (pn + 2)), y, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 yy = pn + j <= pr ? y[0][j] : zero4();
+      st_frag_lds<E>(sY + 16 * pr * LT + 16 * (pn + j), LT, yy, lane);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < CK; ++j)
+      st_frag_lds<E>(sQ + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aQ[i][j], lane);
+#pragma unroll
+    for (int j = 0; j < CV; ++j)
+      st_frag_lds<E>(sDU + 16 * (rb0 + i) * LV + 16 * (cV + j), LV, aV[i][j], lane);
+  }
+  __syncthreads();
+  issue_u(nxt);
+  issue_v_x(nxt);
+
+  // ---- 5: dA = -X^T Y (strictly lower) -> dalpha (rows) and H = dG + dG^T; write dQ, dV
+  {
+    f32x4 da[1][2] = {{zero4(), zero4()}}, kk[1][2] = {{zero4(), zero4()}};
+    if (plow) {
+      mma_blk<E, true, true, 1, 2, kChunk>(sX + 16 * pr, LT, sY + 16 * pn, LT,
+                                           round_down_kc<E>(16 * pr), kChunk, da, lane);
+      mma_blk<E, false, false, 1, 2, DK>(sK + 16 * pr * LK, LK, sK + 16 * pn * LK, LK, 0, DK, kk, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int nb = pn + j;
+      if (nb > pr) {
+        if (lane < 16) pRow[nb * 64 + 16 * pr + lane] = 0.f;
+        continue;
+      }
+      const int col = 16 * nb + (lane & 15);
+      float rs[4];
+      f32x4 dg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * pr + 4 * (lane >> 4) + i;
+        const float a = row > col ? -da[0][j][i] : 0.f;
+        rs[i] = a * kk[0][j][i];
+        dg[i] = a * cAl[row];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = rs[i];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        rs[i] = x;
+      }
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pRow[nb * 64 + 16 * pr + 4 * (lane >> 4) + i] = rs[i];
+      }
+      if (nb < pr) {
+        st_frag_lds<E>(sH + 16 * pr * LT + 16 * nb, LT, dg, lane);
+        st_frag_t<E>(sH + 16 * nb * LT + 16 * pr, LT, dg, lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * pr + 4 * (lane >> 4) + i;
+          if (row > col) {
+            sH[row * LT + col] = to_e<E>(dg[i]);
+            sH[col * LT + row] = to_e<E>(dg[i]);
+          } else if (row == col) {
+            sH[row * LT + col] = to_e<E>(0.f);
+          }
         }
       }
     }
@@ -347,21 +442,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   s2g<E, DK, kBwdThreads>(dq + row0 * DK, DK, sQ, LK, n, tid);
   s2g<E, DV, kBwdThreads>(dv + row0 * DV, DV, sDU, LV, n, tid);
   __syncthreads();
+  issue_q(nxt);
 
   // ---- 6: dK += H K; dk += 2 k dalpha dalpha/dlam; dbeta = dalpha e^-x
+  mma_blk<E, false, true, 2, CK, kChunk>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0, kChunk, aK, lane);
 #pragma unroll
-  for (int j = 0; j < PK::NRB; ++j) {
-    const int rb = rbK + j;
-    f32x4 acc = mma<E, false, true>(sH + 16 * rb * LT, LT, sK + 16 * cbK, LK, 0, kChunk, aK[j], lane);
-    const int col = 16 * cbK + (lane & 15);
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rb + 4 * (lane >> 4) + i;
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * (rb0 + i) + 4 * (lane >> 4) + e;
       const float da = pCol[row] + pCol[64 + row] + pCol[128 + row] + pCol[192 + row] +
                        pRow[row] + pRow[64 + row] + pRow[128 + row] + pRow[192 + row];
-      acc[i] = fmaf(2.f * to_f(sK[row * LK + col]), da * cDl[row], acc[i]);
+      const float f = 2.f * da * cDl[row];
+#pragma unroll
+      for (int j = 0; j < CK; ++j)
+        aK[i][j][e] = fmaf(f, to_f(sK[row * LK + 16 * (cK + j) + (lane & 15)]), aK[i][j][e]);
     }
-    st_frag_lds<E>(sW + 16 * rb * LK + 16 * cbK, LK, acc, lane);
+#pragma unroll
+    for (int j = 0; j < CK; ++j)
+      st_frag_lds<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aK[i][j], lane);
   }
   if (tid < n) {
     const float da = pCol[tid] + pCol[64 + tid] + pCol[128 + tid] + pCol[192 + tid] + pRow[tid] +
@@ -370,6 +469,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   }
   __syncthreads();
   s2g<E, DK, kBwdThreads>(dk + row0 * DK, DK, sW, LK, n, tid);
+  if (!more) break;
+  __syncthreads();  // every LDS read of this chunk is done before the next one lands
+  u = un;
+  cur = nxt;
+  }
 }
 
 template <typename E, int DK, int DV>
@@ -386,8 +490,10 @@ static hipError_t chunk_bwd_go(const Shape& s, const int* table, const void* q, 
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int64_t blocks = s.slots * s.H;
-  if (blocks < 1) return hipSuccess;
+  // Persistent: one workgroup per compute unit walks the chunks, prefetching the next.
+  const int64_t units = s.slots * s.H;
+  if (units < 1) return hipSuccess;
+  const int64_t blocks = units < cu_count() ? units : cu_count();
   prof_begin(st);
   hipLaunchKernelGGL((chunk_bwd_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kBwdThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,

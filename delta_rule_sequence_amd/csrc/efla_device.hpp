@@ -150,6 +150,36 @@ EFLA_DEV f32x4 mma(const E* a, int lda, const E* b, int ldb, int k0, int k1, f32
   return acc;
 }
 
+// Register-blocked product: acc[i][j] += A_i B_j for NA row blocks and NB column blocks,
+// contraction index k in [k0, k1) (multiples of KC inside [0, K)). Row block i of A starts
+// 16 i rows (AK = false) or 16 i columns (AK = true, k-major) after a; column block j of B
+// likewise after b (BK = false: rows of B^T; BK = true: columns of k-major B). Every operand
+// fragment is read from memory once per k step and feeds NB (or NA) products.
+template <typename E, bool AK, bool BK, int NA, int NB, int K>
+EFLA_DEV void mma_blk(const E* a, int lda, const E* b, int ldb, int k0, int k1,
+                      f32x4 (&acc)[NA][NB], int lane) {
+  constexpr int KC = Mma<E>::KC;
+#pragma unroll
+  for (int k = 0; k < K; k += KC) {
+    if (k < k0 || k >= k1) continue;
+    typename Mma<E>::vec av[NA], bv[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if constexpr (AK) av[i] = frag_km<E>(a + 16 * i + k * lda, lda, lane);
+      else av[i] = frag_rm<E>(a + 16 * i * lda + k, lda, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (BK) bv[j] = frag_km<E>(b + 16 * j + k * ldb, ldb, lane);
+      else bv[j] = frag_rm<E>(b + 16 * j * ldb + k, ldb, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = Mma<E>::step(av[i], bv[j], acc[i][j]);
+  }
+}
+
 template <typename E> EFLA_DEV typename Mma<E>::vec zero_vec() {
   typename Mma<E>::vec v;
 #pragma unroll

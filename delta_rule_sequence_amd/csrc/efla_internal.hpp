@@ -66,6 +66,9 @@ inline Geom make_geom(const Shape& s, const int* table) {
   return g;
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int cu_count();
+
 // Width of the d_v slice one scan workgroup owns: 16 when d_v = 64; for d_v = 128, 16 when
 // width 32 would leave compute units idle (fewer than 256 workgroups), else 32.
 // EFLA_SCAN_TV=16|32 overrides the choice for d_v = 128 (tuning).

@@ -256,6 +256,20 @@ def chunk_ut(k, v, beta):
     return dict(alpha=a, T=T, W=T @ k, U=T @ v)
 
 
+def chunk_factors(q, k, beta):
+    """Per-chunk factors the forward keeps for the backward pass (section 3.3).
+
+    q, k: [C, dk]; beta: [C]. Returns dict(X, M): X = (I + strictly_lower(diag(alpha) K K^T))^{-1},
+    the inverse whose product with diag(alpha) is the UT factor T, and M = tril(Q K^T), the
+    causal score block (diagonal kept) of the intra-chunk read-out."""
+    q, k, beta = _f64(q), _f64(k), _f64(beta)
+    C = k.shape[0]
+    a = alpha(beta, np.sum(k * k, axis=-1))
+    A = np.tril(a[:, None] * (k @ k.T), -1)
+    X = scipy.linalg.solve_triangular(np.eye(C) + A, np.eye(C), lower=True, unit_diagonal=True)
+    return dict(X=X, M=np.tril(q @ k.T))
+
+
 def chunk_forward(q, k, v, beta, scale=1.0, cu_seqlens=None, chunk=CHUNK):
     """Chunkwise forward: returns o [B,H,T,dv], W [B,H,T,dk], U [B,H,T,dv],
     U~ = U - W S [B,H,T,dv] and the list of per-chunk incoming states, one entry

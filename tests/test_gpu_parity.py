@@ -124,6 +124,33 @@ def test_stage_values_match_chunk_oracle(E):
     _check("S_c", gpu["states"][: len(states)], states, tol, per_head=False)
 
 
+@pytest.mark.parametrize("widx,over", [(2, dict(B=2, H=2, T=150)), (5, dict(H=2))])
+def test_saved_chunk_factors_match_oracle(E, widx, over):
+    """M = tril(Q K^T) and X = (I + A)^{-1} that the forward saves for the backward, per
+    (chunk slot, head), on a ragged dense batch and on a packed batch. Rows past the end of
+    a sequence are padding and are not compared."""
+    w = workload(widx, **over)
+    inp = make_inputs(w, with_grad=False)
+    dt = TDT[w.dtype]
+    q, k, v, beta = (_dev(inp[n], dt) for n in ("q", "k", "v", "beta"))
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
+    _, saved = E.efla_fwd(q, k, v, beta, 1.0, cu, save=True)
+    views = E.saved_views(saved, q, k, v, beta, 1.0, cu)
+    gm, gx = _np(views["m"]), _np(views["x"])
+    tol = TOL[w.dtype]
+    slot = 0
+    B, H, T = inp["q"].shape[:3]
+    for (b, s0, e0) in O.sequences(B, T, inp["cu_seqlens"]):
+        for c0 in range(s0, e0, O.CHUNK):
+            n = min(e0, c0 + O.CHUNK) - c0
+            for h in range(H):
+                ref = O.chunk_factors(inp["q"][b, h, c0:c0 + n], inp["k"][b, h, c0:c0 + n],
+                                      inp["beta"][b, h, c0:c0 + n])
+                assert O.rel_err(gm[slot, h, :n, :n], ref["M"]) <= tol, ("M", slot, h)
+                assert O.rel_err(gx[slot, h, :n, :n], ref["X"]) <= tol, ("X", slot, h)
+            slot += 1
+
+
 def test_chunk_ut_entry_point(E):
     w = workload(4, B=1, H=2, T=170)
     inp = make_inputs(w, with_grad=False)

@@ -293,6 +293,30 @@ def test_chunk_ut_solves_its_triangular_system():
     assert np.allclose(np.triu(f["T"], 1), 0.0)
 
 
+def test_chunk_factors_against_ut_and_recurrence():
+    """X is the unit lower triangular inverse with X diag(alpha) = T of the UT transform;
+    M = tril(Q K^T) keeps the diagonal: from a zero state one chunk reads out
+    o = scale M X diag(alpha) V and leaves the state K^T X diag(alpha) V, as the token
+    recurrence does."""
+    r = _rng(23)
+    C, dk, dv = 40, 12, 7
+    q = r.standard_normal((C, dk))
+    k = r.standard_normal((C, dk)) * r.uniform(0.5, 2.0, (C, 1))
+    v = r.standard_normal((C, dv))
+    beta = r.uniform(0.05, 1.0, C)
+    f = O.chunk_factors(q, k, beta)
+    X, M = f["X"], f["M"]
+    a = O.alpha(beta, np.sum(k * k, axis=1))
+    assert np.allclose(np.triu(X, 1), 0.0) and np.allclose(np.diag(X), 1.0)
+    assert np.allclose(X * a[None, :], O.chunk_ut(k, v, beta)["T"], rtol=1e-11, atol=1e-12)
+    o, S = O.forward(q[None, None], k[None, None], v[None, None], beta[None, None], scale=0.7)
+    U = (X * a[None, :]) @ v
+    assert O.rel_err(0.7 * M @ U, o[0, 0]) < 1e-11
+    assert O.rel_err(k.T @ U, S[0, 0]) < 1e-11
+    # dropping the diagonal of M (a strict causal mask) would not reproduce the read-out
+    assert O.rel_err(0.7 * np.tril(q @ k.T, -1) @ U, o[0, 0]) > 1e-3
+
+
 def test_packed_batch_equals_separate_sequences():
     r = _rng(22)
     H, dk, dv = 2, 6, 5
