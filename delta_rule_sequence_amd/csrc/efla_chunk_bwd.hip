@@ -88,25 +88,6 @@ EFLA_DEV f32x4 tri_mask(f32x4 c, int rb, int nb, bool keep_diag, int lane) {
   return c;
 }
 
-// One (chunk, head) work unit: valid rows, first row of the chunk in the [B,H,T,*] tensors,
-// index of its [slot][H] state / X block.
-struct BwdUnit {
-  int n;
-  int64_t row0, sh;
-};
-
-// Unit u = slot * H + h (u below the number of used slots times H).
-EFLA_DEV BwdUnit bwd_unit(const Geom& g, int u) {
-  const int slot = u / g.H, h = u % g.H;
-  ChunkInfo ci;
-  chunk_info(g, slot, ci);
-  BwdUnit r;
-  r.n = max(ci.n, 1);
-  r.row0 = (int64_t)(ci.b * g.H + h) * g.T + ci.t0;
-  r.sh = (int64_t)slot * g.H + h;
-  return r;
-}
-
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
@@ -142,8 +123,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Chunks of all heads are numbered u = slot * H + h; packed batches use a prefix of them.
-  const int nslots = g.cu ? min(g.table[g.n_seqs], g.max_slots) : g.max_slots;
-  const int nu = nslots * g.H;
+  const int nu = used_slots(g) * g.H;
   int u = blockIdx.x;
   if (u >= nu) return;
   // [64][d] outputs: wave wv owns row blocks rb0, rb0 + 1 and column blocks cK.. (cV..).
@@ -160,21 +140,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // Requests for a chunk's inputs, issued for the next chunk in small groups spread over
   // the steps of the current one: a large burst would stall the issuing waves until the
   // memory system had taken all of it.
-  auto issue_k = [&](const BwdUnit& c) {
+  auto issue_k = [&](const ChunkUnit& c) {
     tK.load(k + c.row0 * DK, c.n, tid);
     bt = to_f(beta[c.row0 + min(lane, c.n - 1)]);
   };
-  auto issue_du_do = [&](const BwdUnit& c) {
+  auto issue_du_do = [&](const ChunkUnit& c) {
     tDU.load(dut + c.row0 * DV, c.n, tid);
     tDO.load(d_o + c.row0 * DV, c.n, tid);
   };
-  auto issue_u = [&](const BwdUnit& c) { tU.load(ut + c.row0 * DV, c.n, tid); };
-  auto issue_v_x = [&](const BwdUnit& c) {
+  auto issue_u = [&](const ChunkUnit& c) { tU.load(ut + c.row0 * DV, c.n, tid); };
+  auto issue_v_x = [&](const ChunkUnit& c) {
     tV.load(v + c.row0 * DV, c.n, tid);
     tX.load(xsav + c.sh * 64 * 64, 64, tid);
   };
-  auto issue_q = [&](const BwdUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
-  auto issue_sg = [&](const BwdUnit& c) {
+  auto issue_q = [&](const ChunkUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
+  auto issue_sg = [&](const ChunkUnit& c) {
 #pragma unroll
     for (int j = 0; j < CK; ++j)
 #pragma unroll
@@ -185,7 +165,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       }
   };
 
-  BwdUnit cur = bwd_unit(g, u);
+  ChunkUnit cur = chunk_unit(g, u);
   issue_k(cur);
   issue_du_do(cur);
   issue_sg(cur);
@@ -227,7 +207,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   __syncthreads();
   const int un = u + (int)gridDim.x;
   const bool more = un < nu;
-  const BwdUnit nxt = bwd_unit(g, more ? un : u);
+  const ChunkUnit nxt = chunk_unit(g, more ? un : u);
   issue_k(nxt);
 
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);

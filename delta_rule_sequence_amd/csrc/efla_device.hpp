@@ -450,6 +450,30 @@ EFLA_DEV bool chunk_info(const Geom& g, int slot, ChunkInfo& ci) {
   return ci.n > 0;
 }
 
+// Work unit u = slot * H + h of the chunk-parallel kernels: valid rows of the chunk, its
+// first row in the [B,H,T,*] tensors and the index of its [slot][H] blocks.
+struct ChunkUnit {
+  int n;
+  int64_t row0, sh;
+};
+
+// Chunk slots in use: a packed batch may leave the tail of the slot range empty, and the
+// used units u < used_slots * H are then exactly the valid ones.
+EFLA_DEV int used_slots(const Geom& g) {
+  return g.cu ? min(g.table[g.n_seqs], g.max_slots) : g.max_slots;
+}
+
+EFLA_DEV ChunkUnit chunk_unit(const Geom& g, int u) {
+  const int slot = u / g.H, h = u % g.H;
+  ChunkInfo ci;
+  chunk_info(g, slot, ci);
+  ChunkUnit r;
+  r.n = max(ci.n, 1);
+  r.row0 = (int64_t)(ci.b * g.H + h) * g.T + ci.t0;
+  r.sh = (int64_t)slot * g.H + h;
+  return r;
+}
+
 // Map a linear workgroup id to (sequence*H + head, d_v tile) so that the tiles of one
 // (sequence, head) land on the same XCD (workgroups are dealt to the 8 XCDs round-robin)
 // and share its L2 for the K, Q, W tiles they all read.
@@ -466,14 +490,17 @@ EFLA_DEV void scan_block(int bid, int nsh, int ntile, int& sh, int& tile) {
 
 // ---------------------------------------------------------------------------
 // X = (I + A)^{-1} for a strictly lower triangular 64x64 fp32 A (LDS, pitch kPitchF).
-// Blocked forward substitution: the four 16x16 diagonal blocks by column substitution
-// (one wave each), then the off-diagonal blocks by block distance,
-//   X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
-// scr: 4 x 16 x 20 floats of wave-private scratch. All 256 threads must call it.
+// Blocked forward substitution over 16x16 blocks:
+//   diagonal blocks X_ii = (I + A_ii)^{-1} by column substitution (16 lanes of wave i),
+//   then wave j fills block column j downwards, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
+//   with fp32 MFMA: an accumulator tile has exactly the layout of a B operand, so the
+//   X_kj already computed stay in registers and feed the next products.
+// All 256 threads must call it; X is complete in LDS (upper blocks zero) on return.
 // ---------------------------------------------------------------------------
-EFLA_DEV void invert_unit_lower64(const float* sA, float* sX, float* scr, int tid) {
+EFLA_DEV void invert_unit_lower64(const float* sA, float* sX, int tid) {
   constexpr int ld = kPitchF;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < 64 * 64; i += kThreads) {
     const int r = i >> 6, c = i & 63;
     if ((c >> 4) > (r >> 4)) sX[r * ld + c] = 0.f;
@@ -492,35 +519,25 @@ EFLA_DEV void invert_unit_lower64(const float* sA, float* sX, float* scr, int ti
     for (int r = 0; r < 16; ++r) sX[(o + r) * ld + o + lane] = x[r];
   }
   __syncthreads();
-  const int r = lane >> 2, c4 = (lane & 3) * 4;
-  float* my = scr + wv * 16 * 20;
-  for (int d = 1; d < 4; ++d) {
-    const bool act = wv < 4 - d;
-    const int bi = wv + d, bj = wv;
-    if (act) {
-      f32x4 p = zero4();
-      for (int kb = bj; kb < bi; ++kb) {
+  const int j = wv;
+  if (j < 3) {
+    f32x4 xc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const float a = sA[(16 * bi + r) * ld + 16 * kb + m];
-          const f32x4 xv = *(const f32x4*)(sX + (16 * kb + m) * ld + 16 * bj + c4);
-          p += a * xv;
-        }
-      }
-      *(f32x4*)(my + r * 20 + c4) = p;
-    }
-    __syncthreads();
-    if (act) {
-      f32x4 q = zero4();
+    for (int kb = 0; kb < 3; ++kb)
+      if (kb == j) xc[kb] = frag_km<float>(sX + 16 * j * ld + 16 * j, ld, lane);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float xi = sX[(16 * bi + r) * ld + 16 * bi + m];
-        q += xi * *(const f32x4*)(my + m * 20 + c4);
-      }
-      *(f32x4*)(sX + (16 * bi + r) * ld + 16 * bj + c4) = -q;
+    for (int i = 1; i < 4; ++i) {
+      if (i <= j) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb)
+        if (kb >= j && kb < i)
+          acc = Mma<float>::step(frag_rm<float>(sA + 16 * i * ld + 16 * kb, ld, lane), xc[kb], acc);
+      xc[i] = -Mma<float>::step(frag_rm<float>(sX + 16 * i * ld + 16 * i, ld, lane), acc, zero4());
+      st_frag_lds<float>(sX + 16 * i * ld + 16 * j, ld, xc[i], lane);
     }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
 }  // namespace efla

@@ -21,11 +21,12 @@ struct UtFwdLds {
   static constexpr size_t oA = oV + 64 * LV * sizeof(E);            // A (fp32) [64][LF]; later T
   static constexpr size_t oX = oA + 64 * LF * 4;                    // X (fp32) [64][LF]; M staging first
   static constexpr size_t oAl = oX + 64 * LF * 4;                   // alpha    [64]
-  static constexpr size_t oScr = oAl + 64 * 4;                      // inverse scratch
-  static constexpr size_t bytes = oScr + 4 * 16 * 20 * 4;
+  static constexpr size_t bytes = oAl + 64 * 4;
   static_assert(64 * LT * sizeof(E) <= 64 * LF * 4, "T and M must fit in an fp32 work matrix");
 };
 
+// Persistent: the workgroup walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...; the
+// next unit's K, V and Q rows are requested into registers while the current one computes.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
@@ -37,7 +38,8 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   constexpr int VE = 16 / (int)sizeof(E);
   constexpr int VPR = DK / VE;                  // 16-byte vectors per K row
   constexpr int KIT = 64 * VPR / kThreads;      // K vectors per thread
-  static_assert(VPR <= 64 && (64 % VPR) == 0 && KIT >= 1, "K row split");
+  constexpr int VIT = 64 * DV / VE / kThreads;  // V vectors per thread
+  static_assert(VPR <= 64 && (64 % VPR) == 0 && KIT >= 1 && VIT >= 1, "row split");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   E* sK = (E*)(smem + L::oK);
   E* sV = (E*)(smem + L::oV);
@@ -46,138 +48,176 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   float* sX = (float*)(smem + L::oX);
   E* sM = (E*)(smem + L::oX);
   float* sAl = (float*)(smem + L::oAl);
-  float* sScr = (float*)(smem + L::oScr);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int slot = blockIdx.x / g.H, h = blockIdx.x % g.H;
-  ChunkInfo ci;
-  if (!chunk_info(g, slot, ci)) return;
-  const int n = ci.n;
+  int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rA = 16 * wv;
-  const int64_t row0 = (int64_t)(ci.b * g.H + h) * g.T + ci.t0;
+  const int nu = used_slots(g) * g.H;
+  int un = blockIdx.x;
+  if (un >= nu) return;
 
-  // Q rows of this wave as A fragments (for M), straight from global memory.
-  Vv qA[KS];
-  if (mout) {
-    const int ra = min(rA + (lane & 15), n - 1) - (lane & 15);
+  u32x4 kR[KIT], vR[VIT];
+  float bR[KIT];
+  Vv qN[KS], qA[KS];
+  auto issue_k = [&](const ChunkUnit& c) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qA[ks] = frag_rm<E>(q + (row0 + ra) * DK + ks * KC, DK, lane);
-    if (rA + (lane & 15) >= n)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qA[ks] = zero_vec<E>();
-  }
-  // K: stage in LDS and reduce ||k||^2 from the loaded vectors (VPR consecutive threads per row).
-  float lam[KIT];
-#pragma unroll
-  for (int it = 0; it < KIT; ++it) {
-    const int i = it * kThreads + tid;
-    const int r = i / VPR, c = (i % VPR) * VE;
-    typename Mma<E>::vec x = zero_vec<E>();
-    if (r < n) x = *(const Vv*)(k + (row0 + r) * DK + c);
-    *(Vv*)(sK + r * L::LK + c) = x;
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
-#pragma unroll
-    for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    lam[it] = acc;
-  }
-  g2s<E, DV>(sV, L::LV, v + row0 * DV, DV, n, tid);
-#pragma unroll
-  for (int it = 0; it < KIT; ++it) {
-    const int i = it * kThreads + tid;
-    if (i % VPR == 0) {
-      const int r = i / VPR;
-      const float bt = r < n ? to_f(beta[row0 + r]) : 0.f;
-      sAl[r] = flow_coef(bt, lam[it]).alpha;
+    for (int it = 0; it < KIT; ++it) {
+      const int i = it * kThreads + tid;
+      const int r = min(i / VPR, c.n - 1), cc = (i % VPR) * VE;
+      kR[it] = *(const u32x4*)(k + (c.row0 + r) * DK + cc);
+      bR[it] = to_f(beta[c.row0 + r]);
     }
-  }
-  __syncthreads();
+  };
+  auto issue_v = [&](const ChunkUnit& c) {
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int i = it * kThreads + tid;
+      const int r = min(i / (DV / VE), c.n - 1), cc = (i % (DV / VE)) * VE;
+      vR[it] = *(const u32x4*)(v + (c.row0 + r) * DV + cc);
+    }
+  };
+  auto issue_q = [&](const ChunkUnit& c) {  // this wave's Q rows as A fragments (for M)
+    if (!mout) return;
+    const int ra = min(rA + (lane & 15), c.n - 1) - (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qN[ks] = frag_rm<E>(q + (c.row0 + ra) * DK + ks * KC, DK, lane);
+  };
 
-  // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T); wave wv owns row block wv.
+  ChunkUnit cur = chunk_unit(g, un);
+  issue_k(cur);
+  issue_v(cur);
+  issue_q(cur);
+  for (;;) {
+    // Per-lane addresses derive from tid: opaque once per unit so that they are not all
+    // hoisted out of the loop (they would hold registers through every step).
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    const int n = cur.n;
+    const int64_t row0 = cur.row0;
+
+    // K and V land in LDS; ||k||^2 is reduced from the K vectors (VPR consecutive threads
+    // per row), giving alpha.
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    f32x4 acc = zero4();
-    if (nb <= wv) acc = mma<E, false, false>(sK + rA * L::LK, L::LK, sK + 16 * nb * L::LK, L::LK, 0, DK, acc, lane);
-    const int col = 16 * nb + (lane & 15);
+    for (int it = 0; it < KIT; ++it) {
+      const int i = it * kThreads + tid;
+      const int r = i / VPR, c = (i % VPR) * VE;
+      const u32x4 xr = keep_if(kR[it], r < n);
+      *(u32x4*)(sK + r * L::LK + c) = xr;
+      const Vv x = __builtin_bit_cast(Vv, xr);
+      float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rA + 4 * (lane >> 4) + i;
-      sA[row * L::LF + col] = row > col ? sAl[row] * acc[i] : 0.f;
+      for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
+#pragma unroll
+      for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      if (i % VPR == 0) sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc).alpha;
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int i = it * kThreads + tid;
+      const int r = i / (DV / VE), c = (i % (DV / VE)) * VE;
+      *(u32x4*)(sV + r * L::LV + c) = keep_if(vR[it], r < n);
     }
     if (mout) {
-      f32x4 m = zero4();
-      if (nb <= wv) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          m = Mma<E>::step(qA[ks], frag_rm<E>(sK + 16 * nb * L::LK + ks * KC, L::LK, lane), m);
-        if (nb == wv) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((lane & 15) > 4 * (lane >> 4) + i) m[i] = 0.f;
-        }
-      }
-      st_frag_lds<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
+      for (int ks = 0; ks < KS; ++ks) qA[ks] = keep_if_vec(qN[ks], rA + (lane & 15) < n);
     }
-  }
-  __syncthreads();
-  if (mout) {  // M [64][64] of this (chunk, head), 16-byte stores
-    E* gm = mout + ((int64_t)slot * g.H + h) * 64 * 64;
-    s2g<E, 64>(gm, 64, sM, L::LT, kChunk, tid);
     __syncthreads();
-  }
-  invert_unit_lower64(sA, sX, sScr, tid);
+    const int unx = un + (int)gridDim.x;
+    const bool more = unx < nu;
+    const ChunkUnit nxt = chunk_unit(g, more ? unx : un);
+    issue_k(nxt);
 
-  // T = X diag(alpha), written over A (A is no longer needed); X to global memory.
-  {
-    E* gx = xout ? xout + ((int64_t)slot * g.H + h) * 64 * 64 : nullptr;
+    // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T); wave wv owns row block wv.
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {  // 8 consecutive elements of one row per thread
-      const int i = it * kThreads + tid;
-      const int r = i >> 3, c = (i & 7) * 8;
-      const f32x4 x0 = *(const f32x4*)(sX + r * L::LF + c);
-      const f32x4 x1 = *(const f32x4*)(sX + r * L::LF + c + 4);
-      const f32x4 a0 = *(const f32x4*)(sAl + c), a1 = *(const f32x4*)(sAl + c + 4);
-      if constexpr (sizeof(E) == 2) {
-        bf16x8 xe, te;
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x4 acc = zero4();
+      if (nb <= wv) acc = mma<E, false, false>(sK + rA * L::LK, L::LK, sK + 16 * nb * L::LK, L::LK, 0, DK, acc, lane);
+      const int col = 16 * nb + (lane & 15);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xe[e] = (__bf16)x0[e];
-          xe[e + 4] = (__bf16)x1[e];
-          te[e] = (__bf16)(x0[e] * a0[e]);
-          te[e + 4] = (__bf16)(x1[e] * a1[e]);
+      for (int i = 0; i < 4; ++i) {
+        const int row = rA + 4 * (lane >> 4) + i;
+        sA[row * L::LF + col] = row > col ? sAl[row] * acc[i] : 0.f;
+      }
+      if (mout) {
+        f32x4 m = zero4();
+        if (nb <= wv) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            m = Mma<E>::step(qA[ks], frag_rm<E>(sK + 16 * nb * L::LK + ks * KC, L::LK, lane), m);
+          if (nb == wv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if ((lane & 15) > 4 * (lane >> 4) + i) m[i] = 0.f;
+          }
         }
-        *(bf16x8*)(sT + r * L::LT + c) = te;
-        if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
-      } else {
-        *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
-        *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
-        if (gx) {
-          *(f32x4*)(gx + r * 64 + c) = x0;
-          *(f32x4*)(gx + r * 64 + c + 4) = x1;
+        st_frag_lds<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
+      }
+    }
+    __syncthreads();
+    if (mout) {  // M [64][64] of this (chunk, head), 16-byte stores
+      E* gm = mout + cur.sh * 64 * 64;
+      s2g<E, 64>(gm, 64, sM, L::LT, kChunk, tid);
+    }
+    issue_v(nxt);
+    __syncthreads();
+    invert_unit_lower64(sA, sX, tid);
+    issue_q(nxt);
+
+    // T = X diag(alpha), written over A (A is no longer needed); X to global memory.
+    {
+      E* gx = xout ? xout + cur.sh * 64 * 64 : nullptr;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {  // 8 consecutive elements of one row per thread
+        const int i = it * kThreads + tid;
+        const int r = i >> 3, c = (i & 7) * 8;
+        const f32x4 x0 = *(const f32x4*)(sX + r * L::LF + c);
+        const f32x4 x1 = *(const f32x4*)(sX + r * L::LF + c + 4);
+        const f32x4 a0 = *(const f32x4*)(sAl + c), a1 = *(const f32x4*)(sAl + c + 4);
+        if constexpr (sizeof(E) == 2) {
+          bf16x8 xe, te;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xe[e] = (__bf16)x0[e];
+            xe[e + 4] = (__bf16)x1[e];
+            te[e] = (__bf16)(x0[e] * a0[e]);
+            te[e + 4] = (__bf16)(x1[e] * a1[e]);
+          }
+          *(bf16x8*)(sT + r * L::LT + c) = te;
+          if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
+        } else {
+          *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
+          *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
+          if (gx) {
+            *(f32x4*)(gx + r * 64 + c) = x0;
+            *(f32x4*)(gx + r * 64 + c + 4) = x1;
+          }
         }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // W = T K, U = T V; T is lower triangular, so row block wv needs columns < 16 (wv + 1).
-  const int k1 = round_up_kc<E>(16 * (wv + 1));
-  f32x4 Wf[DK / 16], Uf[DV / 16];
+    // W = T K, U = T V; T is lower triangular, so row block wv needs columns < 16 (wv + 1).
+    const int k1 = round_up_kc<E>(16 * (wv + 1));
+    f32x4 Wf[DK / 16], Uf[DV / 16];
 #pragma unroll
-  for (int nb = 0; nb < DK / 16; ++nb)
-    Wf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sK + 16 * nb, L::LK, 0, k1, zero4(), lane);
+    for (int nb = 0; nb < DK / 16; ++nb)
+      Wf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sK + 16 * nb, L::LK, 0, k1, zero4(), lane);
 #pragma unroll
-  for (int nb = 0; nb < DV / 16; ++nb)
-    Uf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sV + 16 * nb, L::LV, 0, k1, zero4(), lane);
-  __syncthreads();
+    for (int nb = 0; nb < DV / 16; ++nb)
+      Uf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sV + 16 * nb, L::LV, 0, k1, zero4(), lane);
+    __syncthreads();
 #pragma unroll
-  for (int nb = 0; nb < DK / 16; ++nb) st_frag_lds<E>(sK + rA * L::LK + 16 * nb, L::LK, Wf[nb], lane);
+    for (int nb = 0; nb < DK / 16; ++nb) st_frag_lds<E>(sK + rA * L::LK + 16 * nb, L::LK, Wf[nb], lane);
 #pragma unroll
-  for (int nb = 0; nb < DV / 16; ++nb) st_frag_lds<E>(sV + rA * L::LV + 16 * nb, L::LV, Uf[nb], lane);
-  __syncthreads();
-  s2g<E, DK>(w + row0 * DK, DK, sK, L::LK, n, tid);
-  s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
+    for (int nb = 0; nb < DV / 16; ++nb) st_frag_lds<E>(sV + rA * L::LV + 16 * nb, L::LV, Uf[nb], lane);
+    __syncthreads();
+    s2g<E, DK>(w + row0 * DK, DK, sK, L::LK, n, tid);
+    s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
+    if (!more) break;
+    __syncthreads();  // the copies out of sK and sV are done before the next chunk lands
+    un = unx;
+    cur = nxt;
+  }
 }
 
 template <typename E, int DK, int DV>
@@ -192,8 +232,10 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int64_t blocks = s.slots * s.H;
-  if (blocks < 1) return hipSuccess;
+  // Persistent: two workgroups per compute unit walk the chunks.
+  const int64_t units = s.slots * s.H;
+  if (units < 1) return hipSuccess;
+  const int64_t blocks = units < 2 * cu_count() ? units : 2 * cu_count();
   prof_begin(st);
   hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
                      st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
