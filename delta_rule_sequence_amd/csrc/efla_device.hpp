@@ -336,6 +336,98 @@ EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid
 }
 
 // ---------------------------------------------------------------------------
+// Swizzled [64][COLS] LDS tiles filled by LDS DMA (global_load_lds_dwordx4). One DMA
+// instruction writes 1 KiB of LDS contiguously (16 bytes per lane), so the rows carry no
+// padding; instead 16-byte chunk c of row r sits at chunk c ^ (r mod NCH), NCH = chunks per
+// row, which spreads the 16 rows of one MFMA operand fetch over the LDS banks.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename E, int COLS, int SH = 0>
+struct Swz {
+  static constexpr int RB = COLS * (int)sizeof(E);  // bytes per row
+  static constexpr int NCH = RB / 16;
+  static constexpr int BYTES = 64 * RB;
+  static_assert((NCH & (NCH - 1)) == 0 && BYTES % 1024 == 0, "swizzled tile shape");
+  // byte offset of element (r, c); the chunk index is XORed with bits SH.. of the row
+  // (SH = 2 for tiles read in accumulator layout, whose lanes hold rows 4 (lane >> 4) + i)
+  EFLA_DEV static int off(int r, int c) {
+    const int b = c * (int)sizeof(E);
+    return r * RB + (((b >> 4) ^ ((r >> SH) & (NCH - 1))) << 4) + (b & 15);
+  }
+};
+
+// Request rows [0, 64) of a [64][COLS] tile (row r at g + r * gld; rows >= n repeat row n - 1,
+// so every address stays inside the chunk) into the swizzled LDS tile at dst. The NW waves
+// that call it share the instructions: wave wi issues numbers wi, wi + NW, ...
+template <typename E, int COLS, int NW, int SH = 0>
+EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld, int n, int wi,
+                       int lane) {
+  typedef Swz<E, COLS, SH> S;
+  constexpr int NI = S::BYTES / 1024;
+  static_assert(NI % NW == 0, "DMA split");
+#pragma unroll
+  for (int jj = 0; jj < NI / NW; ++jj) {
+    const int j = jj * NW + wi;
+    const int byte = j * 1024 + lane * 16;
+    const int r = byte / S::RB, pc = (byte % S::RB) >> 4;
+    const int lc = pc ^ ((r >> SH) & (S::NCH - 1));
+    const E* src = g + (int64_t)min(r, n - 1) * gld + lc * (16 / (int)sizeof(E));
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+  }
+}
+
+// Wait until this wave's outstanding vector memory operations (loads, stores, LDS DMA) are
+// done: s_waitcnt vmcnt(0).
+EFLA_DEV void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// MFMA operands in the accumulator-compatible contraction order. A 16x16 accumulator tile
+// holds rows 4 (lane >> 4) + i of column lane & 15, so for a product whose contraction index
+// runs over accumulator rows the k slots of one step are taken as
+//   bf16 (KC = 32): k = 32 ks + 16 h + 4 (lane >> 4) + i   (h = 0, 1; i < 4)
+//   fp32 (KC = 16): k = 16 ks + 4 (lane >> 4) + i
+// bop_acc builds the B operand straight from accumulator tiles c[] (tile b = rows 16 b..);
+// aop_rm / aop_km read the matching A operand from a swizzled LDS tile stored with the
+// contraction index along columns (aop_rm: A[m][k] at (m, k)) or along rows (aop_km:
+// A[m][k] at (k, m), LDS transpose reads for bf16).
+template <typename E> EFLA_DEV typename Mma<E>::vec bop_acc(const f32x4* c, int ks);
+template <> EFLA_DEV f32x4 bop_acc<float>(const f32x4* c, int ks) { return c[ks]; }
+template <> EFLA_DEV bf16x8 bop_acc<__bf16>(const f32x4* c, int ks) {
+  const f32x4 a = c[2 * ks], b = c[2 * ks + 1];
+  return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+}
+
+template <typename E, int COLS>
+EFLA_DEV typename Mma<E>::vec aop_rm(const unsigned char* t, int m0, int ks, int lane) {
+  typedef Swz<E, COLS> S;
+  const int r = m0 + (lane & 15), g4 = 4 * (lane >> 4);
+  if constexpr (sizeof(E) == 2) {
+    const bf16x4 lo = *(const bf16x4*)(t + S::off(r, 32 * ks + g4));
+    const bf16x4 hi = *(const bf16x4*)(t + S::off(r, 32 * ks + 16 + g4));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    return *(const f32x4*)(t + S::off(r, 16 * ks + g4));
+  }
+}
+
+template <typename E, int COLS>
+EFLA_DEV typename Mma<E>::vec aop_km(const unsigned char* t, int m0, int ks, int lane) {
+  typedef Swz<E, COLS> S;
+  const int i = lane & 15, g = lane >> 4;
+  if constexpr (sizeof(E) == 2) {
+    const int r = 32 * ks + 4 * g + (i >> 2), c = m0 + 4 * (i & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + S::off(r, c)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + S::off(r + 16, c)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const int r = 16 * ks + 4 * g, c = m0 + i;
+    return f32x4{*(const float*)(t + S::off(r, c)), *(const float*)(t + S::off(r + 1, c)),
+                 *(const float*)(t + S::off(r + 2, c)), *(const float*)(t + S::off(r + 3, c))};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Per-token coefficients of the exact flow.
 //   x = beta * lambda, phi(x) = (1 - e^-x) / x,
 //   alpha = beta phi(x), d alpha / d beta = e^-x, d alpha / d lambda = beta^2 phi'(x).
