@@ -39,7 +39,9 @@ struct ScanFwdLds {
   static constexpr size_t bytes = oStg + 2 * sstage;
 };
 
-template <typename E, int DK, int DV, int NWC>
+// WO: write O (also needs Q and M); WSV: write U~ and the chunk states (saved for the
+// backward pass). Compile-time, so the inner loops carry no branches on them.
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV>
 __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
     dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
     dma_tile<E, DK, NWL>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
-    if (o) {
+    if constexpr (WO) {
       dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
       dma_tile<E, 64, NWL>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                            kChunk, kChunk, wl, lane);
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     const int n = rows_of(c);
     const int64_t r0 = base + (int64_t)c * kChunk;
     constexpr int CPR = SU::NCH;  // 16-byte chunks per row
-    if (o) {
+    if constexpr (WO) {
 #pragma unroll
       for (int it = 0; it < (64 * CPR + NTL - 1) / NTL; ++it) {
         const int i = it * NTL + tl, r = i / CPR, lc = i % CPR;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
           *(u32x4*)(o + (r0 + r) * DV + v0 + lc * VE) = *(const u32x4*)(stg + L::gO + SU::off(r, lc * VE));
       }
     }
-    if (ut) {
+    if constexpr (WSV) {
 #pragma unroll
       for (int it = 0; it < (64 * CPR + NTL - 1) / NTL; ++it) {
         const int i = it * NTL + tl, r = i / CPR, lc = i % CPR;
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
           *(u32x4*)(ut + (r0 + r) * DV + v0 + lc * VE) = *(const u32x4*)(stg + L::gUt + SU::off(r, lc * VE));
       }
     }
-    if (states) {
+    if constexpr (WSV) {
       E* gS = states + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
 #pragma unroll
       for (int it = 0; it < (DK * CPR + NTL - 1) / NTL; ++it) {
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
         aw[rb][ks] = aop_rm<E, DK>(st + L::oW, 16 * rb, ks, lane);
-        if (o) aq[rb][ks] = aop_rm<E, DK>(st + L::oQ, 16 * rb, ks, lane);
+        if constexpr (WO) aq[rb][ks] = aop_rm<E, DK>(st + L::oQ, 16 * rb, ks, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) uv[rb][i] = *(const E*)(st + L::oU + SU::off(16 * rb + g4 + i, cw + cl));
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     V sb[KSK];
 #pragma unroll
     for (int ks = 0; ks < KSK; ++ks) sb[ks] = bop_acc<E>(Sacc, ks);
-    if (states) {  // S_c, the state entering chunk c
+    if constexpr (WSV) {  // S_c, the state entering chunk c
 #pragma unroll
       for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
         ws[rb] = Mma<E>::step(aw[rb][ks], sb[ks], ws[rb]);
-        if (o) oa[rb] = Mma<E>::step(aq[rb][ks], sb[ks], oa[rb]);
+        if constexpr (WO) oa[rb] = Mma<E>::step(aq[rb][ks], sb[ks], oa[rb]);
       }
     }
     V ak[NBK][KST], am[4][KST];
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
       for (int ks = 0; ks < KST; ++ks) ak[b][ks] = aop_km<E, DK>(st + L::oK, 16 * b, ks, lane);
-    if (o) {
+    if constexpr (WO) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
       for (int ks = 0; ks < KST; ++ks) Sacc[b] = Mma<E>::step(ak[b][ks], ub[ks], Sacc[b]);
-    if (o) {  // O = scale (P + M U~); M is lower triangular
+    if constexpr (WO) {  // O = scale (P + M U~); M is lower triangular
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
           *(E*)(stg + L::gO + SU::off(16 * rb + g4 + i, cw + cl)) = to_e<E>(g.scale * oa[rb][i]);
       }
     }
-    if (ut) {
+    if constexpr (WSV) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -227,14 +229,14 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   if (loader) copy_out(nchunks - 1);
 }
 
-template <typename E, int DK, int DV, int NWC>
-static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
-                              const void* w, const void* u, const void* m, void* o, void* ut,
-                              void* states, hipStream_t st) {
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV>
+static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
+                               const void* w, const void* u, const void* m, void* o, void* ut,
+                               void* states, hipStream_t st) {
   typedef ScanFwdLds<E, DK, DV, NWC> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC, WO, WSV>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -242,12 +244,24 @@ static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, c
   const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / L::TV);
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
-  hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC>), dim3((unsigned)blocks), dim3(128 * NWC),
-                     L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states);
+  hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV>), dim3((unsigned)blocks),
+                     dim3(128 * NWC), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
+                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states);
   hipError_t e = hipGetLastError();
   prof_end("scan_fwd", st);
   return e;
+}
+
+// Outputs: O alone, O with U~ and the chunk states, or U~ and the states alone (recompute).
+template <typename E, int DK, int DV, int NWC>
+static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
+                              const void* w, const void* u, const void* m, void* o, void* ut,
+                              void* states, hipStream_t st) {
+  const bool wsv = ut && states;
+  if (o && wsv) return scan_fwd_run<E, DK, DV, NWC, true, true>(s, table, q, k, w, u, m, o, ut, states, st);
+  if (o) return scan_fwd_run<E, DK, DV, NWC, true, false>(s, table, q, k, w, u, m, o, ut, states, st);
+  if (wsv) return scan_fwd_run<E, DK, DV, NWC, false, true>(s, table, q, k, w, u, m, o, ut, states, st);
+  return hipSuccess;
 }
 
 // bf16: two compute waves (32 state columns) and two loader waves per workgroup; fp32: one
