@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   const int un = u + (int)gridDim.x;
   const bool more = un < nu;
   const ChunkUnit nxt = chunk_unit(g, more ? un : u);
-  issue_k(nxt);
+  if (more) issue_k(nxt);
 
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);
   //         dM = scale tril(dO U~^T); per-token coefficients
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     cDl[tid] = cf.dlam;
   }
   __syncthreads();
-  issue_du_do(nxt);
+  if (more) issue_du_do(nxt);
 
   // ---- 3: dT = dW K^T + dU V^T -> dalpha (columns) and dX = dT diag(alpha) (strictly lower);
   //         dV = T^T dU, dK += T^T dW (T^T = diag(alpha) X^T); dQ += dM K; dK += dM^T Q
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   mma_blk<E, true, true, 2, CK, kChunk>(sM + 16 * rb0, LT, sQ + 16 * cK, LK,
                                         round_down_kc<E>(16 * rb0), kChunk, aK, lane);
   __syncthreads();
-  issue_sg(nxt);  // S and G registers are free again
+  if (more) issue_sg(nxt);  // S and G registers are free again
 
   // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s); stage dQ and dV
   {
@@ -361,8 +361,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       st_frag_lds<E>(sDU + 16 * (rb0 + i) * LV + 16 * (cV + j), LV, aV[i][j], lane);
   }
   __syncthreads();
-  issue_u(nxt);
-  issue_v_x(nxt);
+  if (more) {
+    issue_u(nxt);
+    issue_v_x(nxt);
+  }
 
   // ---- 5: dA = -X^T Y (strictly lower) -> dalpha (rows) and H = dG + dG^T; write dQ, dV
   {
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   s2g<E, DK, kBwdThreads>(dq + row0 * DK, DK, sQ, LK, n, tid);
   s2g<E, DV, kBwdThreads>(dv + row0 * DV, DV, sDU, LV, n, tid);
   __syncthreads();
-  issue_q(nxt);
+  if (more) issue_q(nxt);
 
   // ---- 6: dK += H K; dk += 2 k dalpha dalpha/dlam; dbeta = dalpha e^-x
   mma_blk<E, false, true, 2, CK, kChunk>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0, kChunk, aK, lane);

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     const int unx = un + (int)gridDim.x;
     const bool more = unx < nu;
     const ChunkUnit nxt = chunk_unit(g, more ? unx : un);
-    issue_k(nxt);
+    if (more) issue_k(nxt);
 
     // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T); wave wv owns row block wv.
 #pragma unroll
@@ -158,10 +158,10 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       E* gm = mout + cur.sh * 64 * 64;
       s2g<E, 64>(gm, 64, sM, L::LT, kChunk, tid);
     }
-    issue_v(nxt);
+    if (more) issue_v(nxt);
     __syncthreads();
     invert_unit_lower64(sA, sX, tid);
-    issue_q(nxt);
+    if (more) issue_q(nxt);
 
     // T = X diag(alpha), written over A (A is no longer needed); X to global memory.
     {
