@@ -212,6 +212,34 @@ def main():
     prof = E.profile_read()
     E.profile_enable(False)
 
+    # The pages' only efficiency claim: training throughput on par with the delta rule. Same
+    # tensors and kernels with alpha = beta (Euler mode), timed the same way.
+    def step_euler():
+        E.efla_fwd(q, k, v, beta, 1.0, None, True, ws, o=o, saved=saved, mode="euler")
+        E.efla_bwd(q, k, v, beta, do, saved, 1.0, None, ws, grads=grads, mode="euler")
+
+    for _ in range(args.warmup):
+        step_euler()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_euler()
+    torch.cuda.synchronize()
+    euler_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # Recurrent decoding: one token for every (batch row, head), state in fp32.
+    state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=dev)
+    q1, k1, v1, b1 = (t[:, :, :1].contiguous() for t in (q, k, v, beta))
+    o1 = torch.empty_like(v1)
+    for _ in range(args.warmup):
+        E.efla_decode(q1, k1, v1, b1, state, 1.0, o=o1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        E.efla_decode(q1, k1, v1, b1, state, 1.0, o=o1)
+    torch.cuda.synchronize()
+    decode_us = (time.perf_counter() - t0) * 1e6 / args.steps
+
     units = B * H * (T // CHUNK)
     kernels = {}
     for name, (count, total_ms) in prof.items():
@@ -251,6 +279,10 @@ def main():
         "step_mfma_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "roofline": roofline,
+        "euler_mode": {"ms_per_step": round(euler_ms, 4),
+                       "exact_over_euler_time": round(ms_per_step / euler_ms, 4)},
+        "decode": {"us_per_call": round(decode_us, 2), "tokens_per_call": B,
+                   "state_MB": round(B * H * dk * dv * 4 / 1e6, 2)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

@@ -12,6 +12,9 @@ LIB_PATH = os.path.join(_PKG, "libefla.so")
 
 EFLA_F32 = 0
 EFLA_BF16 = 1
+EFLA_EXACT = 0
+EFLA_EULER = 1
+MODES = {"exact": EFLA_EXACT, "euler": EFLA_EULER}
 
 STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_NULL", 2: "EFLA_ERR_SHAPE", 3: "EFLA_ERR_DTYPE",
           4: "EFLA_ERR_UNSUPPORTED", 5: "EFLA_ERR_WORKSPACE", 6: "EFLA_ERR_HIP",
@@ -20,15 +23,15 @@ STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_NULL", 2: "EFLA_ERR_SHAPE", 3: "EFLA_ERR_DT
 # Every symbol include/efla.h declares.
 EXPORTS = ["efla_abi_version", "efla_status_str", "efla_check_problem", "efla_workspace_bytes",
            "efla_saved_bytes", "efla_get_saved_layout", "efla_prep", "efla_chunk_ut",
-           "efla_fwd", "efla_bwd", "efla_profile_enable", "efla_profile_read",
-           "efla_profile_reset"]
+           "efla_fwd", "efla_fwd_state", "efla_bwd", "efla_bwd_state", "efla_decode",
+           "efla_profile_enable", "efla_profile_read", "efla_profile_reset"]
 
 
 class EflaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32)]
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
 
 class EflaSavedLayout(ctypes.Structure):
@@ -79,6 +82,13 @@ def lib():
     L.efla_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     L.efla_bwd.restype = st
     L.efla_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
+    L.efla_fwd_state.restype = st
+    L.efla_fwd_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.efla_bwd_state.restype = st
+    L.efla_bwd_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
+                                 sz, vp]
+    L.efla_decode.restype = st
+    L.efla_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.efla_profile_enable.restype = st
     L.efla_profile_enable.argtypes = [ctypes.c_int]
     L.efla_profile_read.restype = ctypes.c_int
@@ -95,5 +105,6 @@ def check(fn, code):
         raise EflaError(fn, code)
 
 
-def problem(B, H, T, dk, dv, dtype, scale=1.0, cu_seqlens_ptr=None, n_seqs=0, chunk=64):
-    return EflaProblem(B, H, T, dk, dv, dtype, chunk, scale, cu_seqlens_ptr, n_seqs)
+def problem(B, H, T, dk, dv, dtype, scale=1.0, cu_seqlens_ptr=None, n_seqs=0, chunk=64,
+            mode=EFLA_EXACT):
+    return EflaProblem(B, H, T, dk, dv, dtype, chunk, scale, cu_seqlens_ptr, n_seqs, mode)

@@ -119,6 +119,7 @@ efla_status to_shape(const efla_problem* p, Shape& s) {
     return EFLA_ERR_SHAPE;
   }
   if (p->chunk != kChunk) return EFLA_ERR_UNSUPPORTED;
+  if (p->mode != EFLA_EXACT && p->mode != EFLA_EULER) return EFLA_ERR_UNSUPPORTED;
   if (!head_size_ok(p->dk) || !head_size_ok(p->dv)) return EFLA_ERR_UNSUPPORTED;
   const Dt dt = p->dtype == EFLA_BF16 ? Dt::BF16 : Dt::F32;
   if (lds_ut_fwd(dt, p->dk, p->dv) == 0 || lds_chunk_bwd(dt, p->dk, p->dv) == 0)
@@ -137,6 +138,7 @@ efla_status to_shape(const efla_problem* p, Shape& s) {
   s.n_seqs = p->cu_seqlens ? p->n_seqs : p->B;
   s.ntc = (p->T + kChunk - 1) / kChunk;
   s.slots = p->cu_seqlens ? (int64_t)(p->T / kChunk) + p->n_seqs : (int64_t)p->B * s.ntc;
+  s.euler = p->mode == EFLA_EULER;
   if (s.slots * p->H >= ((int64_t)1 << 31)) return EFLA_ERR_UNSUPPORTED;
   return EFLA_OK;
 }
@@ -194,12 +196,12 @@ bool empty(const Shape& s) { return s.T == 0; }
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                         const void* beta, void* o, unsigned char* w, unsigned char* ut,
                         unsigned char* states, int* table, unsigned char* m, unsigned char* x,
-                        unsigned char* u, hipStream_t st) {
+                        unsigned char* u, const float* h0, float* ht, hipStream_t st) {
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
   if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, w, u, m, x, st))) return r;
-  return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, st));
+  return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, h0, ht, st));
 }
 
 }  // namespace
@@ -287,15 +289,15 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
   return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, w, u, nullptr, nullptr, st));
 }
 
-efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
-                     const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
-                     size_t ws_bytes, void* stream) {
+efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const float* h0, void* o, float* ht, void* saved,
+                           size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   if (efla_status r = to_shape(p, s)) return r;
   if (empty(s)) return EFLA_OK;
   if (!q || !k || !v || !beta || !o || !ws) return EFLA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(ws) ||
-      !aligned16(saved))
+      !aligned16(saved) || !aligned16(h0) || !aligned16(ht))
     return EFLA_ERR_ALIGN;
   if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
   const Saved L = saved_layout(s);
@@ -312,19 +314,28 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
   int* table = sv ? (int*)(sv + L.table) : table_ws;
   unsigned char* m = sv ? sv + L.m : m_ws;
   unsigned char* x = sv ? sv + L.x : nullptr;
-  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, (hipStream_t)stream);
+  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, h0, ht,
+                     (hipStream_t)stream);
 }
 
-efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
-                     const void* beta, const void* d_o, const void* saved, size_t saved_bytes,
-                     void* dq, void* dk, void* dv, void* dbeta, void* ws, size_t ws_bytes,
-                     void* stream) {
+efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
+                     const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return efla_fwd_state(p, q, k, v, beta, nullptr, o, nullptr, saved, saved_bytes, ws, ws_bytes,
+                        stream);
+}
+
+efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const float* h0, const void* d_o, const float* dht,
+                           const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
+                           void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   if (efla_status r = to_shape(p, s)) return r;
   if (empty(s)) return EFLA_OK;
   if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta || !ws) return EFLA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(ws) || !aligned16(saved))
+      !aligned16(dk) || !aligned16(dv) || !aligned16(ws) || !aligned16(saved) || !aligned16(h0) ||
+      !aligned16(dht) || !aligned16(dh0))
     return EFLA_ERR_ALIGN;
   const Saved L = saved_layout(s);
   const size_t need = saved ? align_up(bytes_v(s)) + align_up(bytes_states(s)) : ws_bwd(s);
@@ -340,15 +351,36 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
     unsigned char* u = rec + L.total;
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
                                     rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
-                                    u, st))
+                                    u, h0, nullptr, st))
       return r;
     sv = rec;
   }
   const int* table = (const int*)(sv + L.table);
-  if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o, dut, dstates, st)))
+  if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o, dut,
+                                                 dstates, dht, dh0, st)))
     return r;
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
                                      dstates, sv + L.x, dq, dk, dv, dbeta, st));
+}
+
+efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
+                     const void* beta, const void* d_o, const void* saved, size_t saved_bytes,
+                     void* dq, void* dk, void* dv, void* dbeta, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return efla_bwd_state(p, q, k, v, beta, nullptr, d_o, nullptr, saved, saved_bytes, dq, dk, dv,
+                        dbeta, nullptr, ws, ws_bytes, stream);
+}
+
+efla_status efla_decode(const efla_problem* p, const void* q, const void* k, const void* v,
+                        const void* beta, float* state, void* o, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (s.cu) return EFLA_ERR_UNSUPPORTED;
+  if (empty(s)) return EFLA_OK;
+  if (!q || !k || !v || !beta || !state || !o) return EFLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
+    return EFLA_ERR_ALIGN;
+  return hip_status(launch_decode(s, q, k, v, beta, state, o, (hipStream_t)stream));
 }
 
 efla_status efla_profile_enable(int on) {

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
                      tri_mask(m[0][j], pr, pn + j, true, lane) * g.scale, lane);
   }
   if (tid < 64) {
-    const FlowCoef cf = flow_coef(tid < n ? bt_cur : 0.f, cLam[tid]);
+    const FlowCoef cf = flow_coef(tid < n ? bt_cur : 0.f, cLam[tid], g.euler);
     cAl[tid] = cf.alpha;
     cEx[tid] = cf.ex;
     cDl[tid] = cf.dlam;

@@ -431,6 +431,8 @@ EFLA_DEV typename Mma<E>::vec aop_km(const unsigned char* t, int m0, int ks, int
 // Per-token coefficients of the exact flow.
 //   x = beta * lambda, phi(x) = (1 - e^-x) / x,
 //   alpha = beta phi(x), d alpha / d beta = e^-x, d alpha / d lambda = beta^2 phi'(x).
+// With euler set the step is the delta rule's own: alpha = beta, d alpha / d beta = 1,
+// d alpha / d lambda = 0.
 // For |x| < 1 phi and phi' are Taylor polynomials (degree 11; truncation < 2e-10
 // relative), which avoids the cancellation of the closed forms near zero; elsewhere
 // the closed forms with expm1 are used. Overflow for large negative x follows IEEE.
@@ -439,7 +441,8 @@ struct FlowCoef {
   float alpha, ex, dlam;
 };
 
-EFLA_DEV FlowCoef flow_coef(float beta, float lam) {
+EFLA_DEV FlowCoef flow_coef(float beta, float lam, bool euler = false) {
+  if (euler) return FlowCoef{beta, 1.0f, 0.0f};  // delta rule: alpha = beta
   const float x = beta * lam;
   float ph, dph;
   const float ex = expf(-x);
@@ -490,6 +493,7 @@ struct Geom {
   const int* table;    // packed: chunk start table [n_seqs + 1], else nullptr
   int max_slots;       // chunk slots the state buffers hold per head
   float scale;
+  int euler;           // step rule: 0 exact flow, 1 delta rule (alpha = beta)
 };
 
 struct SeqInfo {

@@ -20,6 +20,7 @@ struct Shape {
   int n_seqs;      // sequences (B for dense batches)
   int ntc;         // ceil(T/64) (dense)
   int64_t slots;   // chunk slots per head (upper bound for packed batches)
+  bool euler;      // step rule: delta rule (alpha = beta) instead of the exact flow
 };
 
 // Optional per-kernel timing (efla_profile_enable): events recorded on the launch stream
@@ -34,12 +35,16 @@ hipError_t launch_prep(const Shape& s, const void* k, const void* beta, float* l
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
                          const void* v, const void* beta, void* w, void* u, void* m, void* x,
                          hipStream_t st);
+// h0 / ht (scan_fwd) and dht / dh0 (scan_bwd): fp32 [n_seqs][H][dk][dv] per-sequence
+// states entering / leaving the sequence, or null (zero in, not written out).
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
-                           void* states, hipStream_t st);
+                           void* states, const float* h0, float* ht, hipStream_t st);
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
-                           void* dstates, hipStream_t st);
+                           void* dstates, const float* dht, float* dh0, hipStream_t st);
+hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
+                         const void* beta, float* state, void* o, hipStream_t st);
 hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, const void* k,
                             const void* v, const void* beta, const void* d_o, const void* ut,
                             const void* dut, const void* states, const void* dstates,
@@ -63,6 +68,7 @@ inline Geom make_geom(const Shape& s, const int* table) {
   g.table = s.cu ? table : nullptr;
   g.max_slots = (int)s.slots;
   g.scale = s.scale;
+  g.euler = s.euler ? 1 : 0;
   return g;
 }
 

@@ -10,7 +10,7 @@
 namespace efla {
 
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads) void prep_kernel(int64_t ntok, const E* __restrict__ k,
+__global__ __launch_bounds__(kThreads) void prep_kernel(int64_t ntok, int euler, const E* __restrict__ k,
                                                         const E* __restrict__ beta,
                                                         float* __restrict__ lam,
                                                         float* __restrict__ alpha,
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int64_t ntok, const E* _
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (sub == 0) {
-      const FlowCoef c = flow_coef(to_f(beta[row]), acc);
+      const FlowCoef c = flow_coef(to_f(beta[row]), acc, euler != 0);
       if (lam) lam[row] = acc;
       alpha[row] = c.alpha;
       if (ex) ex[row] = c.ex;
@@ -102,7 +102,7 @@ static hipError_t prep_go(const Shape& s, const void* k, const void* beta, float
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
   hipLaunchKernelGGL((prep_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, st, ntok,
-                     (const E*)k, (const E*)beta, lam, alpha, ex, dlam);
+                     s.euler ? 1 : 0, (const E*)k, (const E*)beta, lam, alpha, ex, dlam);
   hipError_t e = hipGetLastError();
   prof_end("prep", st);
   return e;

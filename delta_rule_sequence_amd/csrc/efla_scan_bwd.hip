@@ -37,7 +37,7 @@ template <typename E, int DK, int DV, int TV>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
-    E* __restrict__ dstates) {
+    E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0) {
   typedef ScanBwdLds<E, DK, DV, TV> L;
   typedef typename Mma<E>::vec V;
   constexpr int KC = Mma<E>::KC, KS = DK / KC, KT = kChunk / KC;
@@ -123,9 +123,22 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     }
   };
 
+  // G^T tile t = wv + 4 i holds G[16 db + (lane & 15)][v0 + 16 vb + 4 (lane >> 4) + e];
+  // dht / dh0: fp32 [n_seqs][H][DK][DV] gradients at the state leaving / entering the sequence
   f32x4 Gt[TPW];
+  auto goff = [&](int i, int e) {
+    const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+    return ((int64_t)s * g.H + h) * DK * DV + (int64_t)(16 * db + (lane & 15)) * DV + v0 + 16 * vb +
+           4 * (lane >> 4) + e;
+  };
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) Gt[i] = zero4();
+  for (int i = 0; i < TPW; ++i) {
+    Gt[i] = zero4();
+    if (dht) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
+    }
+  }
   if (nchunks > 0) {
     load_chunk(nchunks - 1);
     commit_chunk(nchunks - 1, smem + ((nchunks - 1) & 1) * L::stage);
@@ -182,12 +195,18 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     }
     if (more) commit_chunk(c - 1, smem + ((c - 1) & 1) * L::stage);
   }
+  if (dh0) {  // gradient at the state entering the sequence
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh0[goff(i, e)] = Gt[i][e];
+  }
 }
 
 template <typename E, int DK, int DV, int TV>
 static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* m, const void* d_o, void* dut,
-                              void* dstates, hipStream_t st) {
+                              void* dstates, const float* dht, float* dh0, hipStream_t st) {
   typedef ScanBwdLds<E, DK, DV, TV> L;
   static bool attr = false;
   if (!attr) {
@@ -201,7 +220,7 @@ static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, c
   prof_begin(st);
   hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV>), dim3((unsigned)blocks), dim3(kThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates);
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0);
   hipError_t e = hipGetLastError();
   prof_end("scan_bwd", st);
   return e;
@@ -221,9 +240,9 @@ size_t lds_scan_bwd(Dt dt, int dk, int dv) {
 
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
-                           void* dstates, hipStream_t st) {
+                           void* dstates, const float* dht, float* dh0, hipStream_t st) {
 #define EFLA_SB(E_, DK_, DV_, TV_) \
-  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, st)
+  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SB(__bf16, 64, 64, 16);
     if (s.dk == 128 && s.dv == 64) EFLA_SB(__bf16, 128, 64, 16);

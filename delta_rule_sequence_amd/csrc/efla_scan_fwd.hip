@@ -45,7 +45,7 @@ template <typename E, int DK, int DV, int NWC, bool WO, bool WSV>
 __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
-    E* __restrict__ states) {
+    E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht) {
   typedef ScanFwdLds<E, DK, DV, NWC> L;
   typedef typename L::SU SU;
   typedef typename Mma<E>::vec V;
@@ -65,10 +65,23 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   const int s = sh / g.H, h = sh % g.H;
   const SeqInfo si = seq_info(g, s);
   const int nchunks = seq_chunks(g, si);
-  if (nchunks <= 0) return;
   const int v0 = tile * TV;          // first column of this workgroup
   const int cw = 16 * wi;            // first column of this (compute) wave inside the tile
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
+  // h0 / ht: fp32 [n_seqs][H][DK][DV]; this wave's columns
+  const int64_t hoff = ((int64_t)s * g.H + h) * DK * DV + v0 + cw + cl;
+  if (nchunks <= 0) {  // empty sequence: the state passes through
+    if (ht && !loader) {
+#pragma unroll
+      for (int b = 0; b < NBK; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t o_ = hoff + (int64_t)(16 * b + g4 + i) * DV;
+          ht[o_] = h0 ? h0[o_] : 0.f;
+        }
+    }
+    return;
+  }
   const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
   auto rows_of = [&](int c) { return min(kChunk, si.len - c * kChunk); };
 
@@ -123,6 +136,12 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   f32x4 Sacc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) Sacc[b] = zero4();
+  if (h0 && !loader) {  // state entering the sequence
+#pragma unroll
+    for (int b = 0; b < NBK; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sacc[b][i] = h0[hoff + (int64_t)(16 * b + g4 + i) * DV];
+  }
   auto compute = [&](int c) {
     const unsigned char* st = smem + (c & 1) * L::stage;
     unsigned char* stg = smem + L::oStg + (c & 1) * L::sstage;
@@ -227,12 +246,18 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   }
   __syncthreads();
   if (loader) copy_out(nchunks - 1);
+  if (ht && !loader) {  // state after the last token
+#pragma unroll
+    for (int b = 0; b < NBK; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ht[hoff + (int64_t)(16 * b + g4 + i) * DV] = Sacc[b][i];
+  }
 }
 
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV>
 static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* u, const void* m, void* o, void* ut,
-                               void* states, hipStream_t st) {
+                               void* states, const float* h0, float* ht, hipStream_t st) {
   typedef ScanFwdLds<E, DK, DV, NWC> L;
   static bool attr = false;
   if (!attr) {
@@ -246,7 +271,7 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
   prof_begin(st);
   hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV>), dim3((unsigned)blocks),
                      dim3(128 * NWC), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
-                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states);
+                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht);
   hipError_t e = hipGetLastError();
   prof_end("scan_fwd", st);
   return e;
@@ -256,11 +281,13 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
 template <typename E, int DK, int DV, int NWC>
 static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* u, const void* m, void* o, void* ut,
-                              void* states, hipStream_t st) {
+                              void* states, const float* h0, float* ht, hipStream_t st) {
   const bool wsv = ut && states;
-  if (o && wsv) return scan_fwd_run<E, DK, DV, NWC, true, true>(s, table, q, k, w, u, m, o, ut, states, st);
-  if (o) return scan_fwd_run<E, DK, DV, NWC, true, false>(s, table, q, k, w, u, m, o, ut, states, st);
-  if (wsv) return scan_fwd_run<E, DK, DV, NWC, false, true>(s, table, q, k, w, u, m, o, ut, states, st);
+  if (o && wsv)
+    return scan_fwd_run<E, DK, DV, NWC, true, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
+  if (o) return scan_fwd_run<E, DK, DV, NWC, true, false>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
+  if (wsv)
+    return scan_fwd_run<E, DK, DV, NWC, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
   return hipSuccess;
 }
 
@@ -280,9 +307,9 @@ size_t lds_scan_fwd(Dt dt, int dk, int dv) {
 
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
-                           void* states, hipStream_t st) {
+                           void* states, const float* h0, float* ht, hipStream_t st) {
 #define EFLA_SF(E_, DK_, DV_, NWC_) \
-  return scan_fwd_go<E_, DK_, DV_, NWC_>(s, table, q, k, w, u, m, o, ut, states, st)
+  return scan_fwd_go<E_, DK_, DV_, NWC_>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SF(__bf16, 64, 64, 2);
     if (s.dk == 64 && s.dv == 128) EFLA_SF(__bf16, 64, 128, 2);

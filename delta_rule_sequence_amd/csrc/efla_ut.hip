@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
 #pragma unroll
       for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-      if (i % VPR == 0) sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc).alpha;
+      if (i % VPR == 0) sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc, g.euler).alpha;
     }
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {

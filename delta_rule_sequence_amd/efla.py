@@ -37,8 +37,15 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
-def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None):
-    """Build the efla_problem for tensors q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T]."""
+def _mode(mode):
+    if mode not in _lib.MODES:
+        raise ValueError("mode must be one of %s" % sorted(_lib.MODES))
+    return _lib.MODES[mode]
+
+
+def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None, mode="exact"):
+    """Build the efla_problem for tensors q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T].
+    mode "exact" (the exact flow) or "euler" (the delta rule, alpha = beta)."""
     if k.dim() != 4 or v.dim() != 4:
         raise ValueError("k and v must be [B, H, T, d]")
     B, H, T, dk = k.shape
@@ -53,7 +60,8 @@ def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None):
         _need(cu_seqlens, "cu_seqlens", torch.int32)
         n_seqs = cu_seqlens.numel() - 1
         cu_ptr = cu_seqlens.data_ptr()
-    return _lib.problem(B, H, T, dk, dv, _DT[k.dtype], float(scale), cu_ptr, n_seqs)
+    return _lib.problem(B, H, T, dk, dv, _DT[k.dtype], float(scale), cu_ptr, n_seqs,
+                        mode=_mode(mode))
 
 
 def efla_workspace_bytes(p, for_backward: bool) -> int:
@@ -75,14 +83,14 @@ def _bytes(n, device):
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
-def efla_prep(k, beta):
+def efla_prep(k, beta, mode="exact"):
     """Per-token coefficients: dict(lam, alpha, dalpha_dbeta, dalpha_dlam), fp32 [B,H,T]."""
     if k.dim() != 4 or k.dtype not in _DT:
         raise ValueError("k must be [B, H, T, dk] float32 or bfloat16")
     B, H, T, dk = k.shape
     _need(k, "k", k.dtype)
     _need(beta, "beta", k.dtype, (B, H, T))
-    p = _lib.problem(B, H, T, dk, dk, _DT[k.dtype])
+    p = _lib.problem(B, H, T, dk, dk, _DT[k.dtype], mode=_mode(mode))
     out = {n: torch.empty((B, H, T), dtype=torch.float32, device=k.device)
            for n in ("lam", "alpha", "dalpha_dbeta", "dalpha_dlam")}
 
@@ -94,9 +102,9 @@ def efla_prep(k, beta):
     return out
 
 
-def efla_chunk_ut(k, v, beta, cu_seqlens=None):
+def efla_chunk_ut(k, v, beta, cu_seqlens=None, mode="exact"):
     """UT transform of every chunk: (W [B,H,T,dk], U [B,H,T,dv]) in the input dtype."""
-    p = make_problem(k, k, v, beta, 1.0, cu_seqlens)
+    p = make_problem(k, k, v, beta, 1.0, cu_seqlens, mode)
     w = torch.empty_like(k)
     u = torch.empty_like(v)
     ws_n = efla_workspace_bytes(p, False)
@@ -106,10 +114,25 @@ def efla_chunk_ut(k, v, beta, cu_seqlens=None):
     return w, u
 
 
-def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=None, saved=None):
+def _n_state(p):
+    return p.n_seqs if p.cu_seqlens else p.B
+
+
+def _state_tensor(t, name, p, device):
+    shape = (_n_state(p), p.H, p.dk, p.dv)
+    if t is None:
+        return None
+    _need(t, name, torch.float32, shape)
+    return t
+
+
+def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=None, saved=None,
+             mode="exact", initial_state=None, final_state=None):
     """Forward. Returns (o, saved) where saved is the uint8 buffer for efla_bwd (or None).
-    o, saved and ws may be passed in preallocated."""
-    p = make_problem(q, k, v, beta, scale, cu_seqlens)
+    o, saved and ws may be passed in preallocated. initial_state: fp32 [n_state, H, dk, dv] or
+    None (zero). final_state: True (allocate) or a preallocated fp32 tensor of that shape to
+    receive the state after each sequence; then (o, saved, final_state) is returned."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode)
     if o is None:
         o = torch.empty_like(v)
     else:
@@ -118,19 +141,28 @@ def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=No
         saved = _bytes(efla_saved_bytes(p), k.device)
     if not save:
         saved = None
+    h0 = _state_tensor(initial_state, "initial_state", p, k.device)
+    ht = None
+    if final_state is True:
+        ht = torch.empty((_n_state(p), p.H, p.dk, p.dv), dtype=torch.float32, device=k.device)
+    elif final_state is not None and final_state is not False:
+        ht = _state_tensor(final_state, "final_state", p, k.device)
     ws_n = efla_workspace_bytes(p, False)
     if ws is None or ws.numel() < ws_n:
         ws = _bytes(ws_n, k.device)
-    _lib.check("efla_fwd", _lib.lib().efla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                              _ptr(o), _ptr(saved), 0 if saved is None else saved.numel(),
-                                              _ptr(ws), ws.numel(), _stream()))
-    return o, saved
+    _lib.check("efla_fwd_state", _lib.lib().efla_fwd_state(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+        _ptr(saved), 0 if saved is None else saved.numel(), _ptr(ws), ws.numel(), _stream()))
+    return (o, saved) if ht is None else (o, saved, ht)
 
 
-def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None, grads=None):
-    """Backward of sum(o * d_o): (dq, dk, dv, dbeta) in the input dtype.
-    grads may be a preallocated (dq, dk, dv, dbeta) tuple."""
-    p = make_problem(q, k, v, beta, scale, cu_seqlens)
+def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None, grads=None,
+             mode="exact", initial_state=None, d_final_state=None, d_initial_state=False):
+    """Backward of sum(o * d_o) (+ <final_state, d_final_state>): (dq, dk, dv, dbeta) in the
+    input dtype. grads may be a preallocated (dq, dk, dv, dbeta) tuple. initial_state is the
+    one the forward used (read only when saved is None). With d_initial_state True (or a
+    preallocated fp32 tensor) the gradient at the initial states is returned as a fifth item."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode)
     _need(d_o, "d_o", v.dtype, v.shape)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -139,14 +171,35 @@ def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None
         dq, dk, dv, dbeta = grads
         for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (dbeta, beta, "dbeta")):
             _need(t, n, ref.dtype, ref.shape)
+    h0 = _state_tensor(initial_state, "initial_state", p, k.device)
+    dht = _state_tensor(d_final_state, "d_final_state", p, k.device)
+    dh0 = None
+    if d_initial_state is True:
+        dh0 = torch.empty((_n_state(p), p.H, p.dk, p.dv), dtype=torch.float32, device=k.device)
+    elif d_initial_state is not None and d_initial_state is not False:
+        dh0 = _state_tensor(d_initial_state, "d_initial_state", p, k.device)
     ws_n = efla_workspace_bytes(p, True)
     if ws is None or ws.numel() < ws_n:
         ws = _bytes(ws_n, k.device)
-    _lib.check("efla_bwd", _lib.lib().efla_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                              _ptr(d_o), _ptr(saved), 0 if saved is None else saved.numel(),
-                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(ws),
-                                              ws.numel(), _stream()))
-    return dq, dk, dv, dbeta
+    _lib.check("efla_bwd_state", _lib.lib().efla_bwd_state(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(h0), _ptr(d_o), _ptr(dht),
+        _ptr(saved), 0 if saved is None else saved.numel(), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream()))
+    return (dq, dk, dv, dbeta) if dh0 is None else (dq, dk, dv, dbeta, dh0)
+
+
+def efla_decode(q, k, v, beta, state, scale=1.0, mode="exact", o=None):
+    """Recurrent inference over the T tokens of q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T]
+    (dense batch). state: fp32 [B, H, dk, dv], updated in place. Returns o [B,H,T,dv]."""
+    p = make_problem(q, k, v, beta, scale, None, mode)
+    _need(state, "state", torch.float32, (p.B, p.H, p.dk, p.dv))
+    if o is None:
+        o = torch.empty_like(v)
+    else:
+        _need(o, "o", v.dtype, v.shape)
+    _lib.check("efla_decode", _lib.lib().efla_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                                    _ptr(beta), _ptr(state), _ptr(o), _stream()))
+    return o
 
 
 def saved_views(saved, q, k, v, beta, scale=1.0, cu_seqlens=None):
@@ -173,23 +226,27 @@ class EflaFunction(torch.autograd.Function):
     """o = EFLA(q, k, v, beta); the backward runs the library's backward kernels."""
 
     @staticmethod
-    def forward(ctx, q, k, v, beta, scale, cu_seqlens):
+    def forward(ctx, q, k, v, beta, scale, cu_seqlens, mode):
         q, k, v, beta = (t.contiguous() for t in (q, k, v, beta))
-        o, saved = efla_fwd(q, k, v, beta, scale, cu_seqlens, save=True)
+        o, saved = efla_fwd(q, k, v, beta, scale, cu_seqlens, save=True, mode=mode)
         ctx.save_for_backward(q, k, v, beta, saved, cu_seqlens)
         ctx.scale = scale
+        ctx.mode = mode
         return o
 
     @staticmethod
     def backward(ctx, d_o):
         q, k, v, beta, saved, cu = ctx.saved_tensors
-        dq, dk, dv, dbeta = efla_bwd(q, k, v, beta, d_o.contiguous(), saved, ctx.scale, cu)
-        return dq, dk, dv, dbeta, None, None
+        dq, dk, dv, dbeta = efla_bwd(q, k, v, beta, d_o.contiguous(), saved, ctx.scale, cu,
+                                     mode=ctx.mode)
+        return dq, dk, dv, dbeta, None, None, None
 
 
-def efla(q, k, v, beta, scale: float = 1.0, cu_seqlens: Optional[torch.Tensor] = None):
-    """Exact Flow Linear Attention token mixer: o [B,H,T,dv], differentiable."""
-    return EflaFunction.apply(q, k, v, beta, scale, cu_seqlens)
+def efla(q, k, v, beta, scale: float = 1.0, cu_seqlens: Optional[torch.Tensor] = None,
+         mode: str = "exact"):
+    """Exact Flow Linear Attention token mixer: o [B,H,T,dv], differentiable.
+    mode "euler" runs the delta rule (alpha = beta) through the same kernels."""
+    return EflaFunction.apply(q, k, v, beta, scale, cu_seqlens, mode)
 
 
 def profile_enable(on: bool):

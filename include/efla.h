@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 3
+#define EFLA_ABI_VERSION 4
 
 typedef enum {
   EFLA_OK = 0,
@@ -59,6 +59,12 @@ typedef enum {
 
 typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
 
+/* Step rule. EFLA_EXACT: alpha_t = (1 - exp(-beta_t lambda_t)) / lambda_t, the exact flow
+ * (summary page, section 3.2). EFLA_EULER: alpha_t = beta_t, the delta rule, which is the
+ * explicit Euler step of the same dynamics (summary page, section 2; DeltaNet page); it runs
+ * through the same kernels and exists for comparisons. */
+typedef enum { EFLA_EXACT = 0, EFLA_EULER = 1 } efla_mode;
+
 typedef struct {
   int32_t B, H, T, dk, dv;      /* q,k: [B,H,T,dk]; v,o: [B,H,T,dv]; beta: [B,H,T] */
   int32_t dtype;                /* efla_dtype of q, k, v, beta, o, do and every gradient */
@@ -66,6 +72,7 @@ typedef struct {
   float scale;                  /* multiplies the read-out: o_t = scale * S_t^T q_t */
   const int32_t* cu_seqlens;    /* device pointer or NULL (see packed batches above) */
   int32_t n_seqs;               /* number of packed sequences when cu_seqlens is set */
+  int32_t mode;                 /* efla_mode; other values return EFLA_ERR_UNSUPPORTED */
 } efla_problem;
 
 /* Byte offsets of the tensors inside the buffer that efla_fwd saves for efla_bwd.
@@ -126,6 +133,15 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
                      const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* Forward with recurrent state I/O. States are fp32 [n_state][H][dk][dv] with n_state = B
+ * (dense) or n_seqs (packed), one per sequence: h0 (NULL = zero) is the state entering each
+ * sequence, ht (NULL = not written) receives the state after its last token, so a long stream
+ * can be processed in pieces (summary page, section 3.3: the chunk-level recurrence carries the
+ * state from chunk to chunk). efla_fwd(...) is efla_fwd_state(..., NULL, o, NULL, ...). */
+efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const float* h0, void* o, float* ht, void* saved,
+                           size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of sum(o * d_o): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T], all in
  * the problem dtype (every output fully overwritten). `saved` is the buffer a forward
  * call on the same inputs filled, or NULL to recompute it inside ws.
@@ -134,6 +150,24 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
                      const void* beta, const void* d_o, const void* saved, size_t saved_bytes,
                      void* dq, void* dk, void* dv, void* dbeta, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Backward with recurrent state I/O: the gradient of sum(o * d_o) + <ht, dht> with respect to
+ * q, k, v, beta and h0. h0 must be what the forward used (only read when saved == NULL; NULL =
+ * zero); dht (NULL = zero) is the gradient arriving at the final states; dh0 (NULL = not
+ * written) receives the gradient at the initial states. fp32 [n_state][H][dk][dv] each. */
+efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const float* h0, const void* d_o, const float* dht,
+                           const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
+                           void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream);
+
+/* Recurrent inference: the token recurrence itself (summary page, section 3.2), one token
+ * after the other, for dense batches (cu_seqlens must be NULL). Reads q, k [B,H,T,dk],
+ * v [B,H,T,dv], beta [B,H,T] (problem dtype) and state, fp32 [B][H][dk][dv] in place: on
+ * entry the state before the first token, on return the state after the last one. Writes
+ * o [B,H,T,dv]. Meant for short T (decoding one or a few tokens per call); the chunked
+ * efla_fwd_state is the fast path for long T. Needs no workspace. */
+efla_status efla_decode(const efla_problem* p, const void* q, const void* k, const void* v,
+                        const void* beta, float* state, void* o, void* stream);
 
 /* Kernel timing for profiling. While enabled, every kernel that efla_* enqueues is
  * bracketed by two HIP events recorded on the same stream. efla_profile_read waits for

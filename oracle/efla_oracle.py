@@ -84,19 +84,33 @@ def dphi(x):
     return out
 
 
-def alpha(beta, lam):
-    """Effective step of the exact flow: (1 - e^{-beta lambda}) / lambda; beta when lambda = 0."""
+MODES = ("exact", "euler")
+
+
+def alpha(beta, lam, mode="exact"):
+    """Effective step of the exact flow: (1 - e^{-beta lambda}) / lambda; beta when lambda = 0.
+
+    mode "euler" is the delta rule's own step, alpha = beta: the explicit Euler step of the
+    same dynamics (summary page, section 2), kept as the comparison mode."""
     beta = np.asarray(beta, dtype=np.float64)
     lam = np.asarray(lam, dtype=np.float64)
+    if mode == "euler":
+        return beta + 0.0 * lam
+    assert mode == "exact", mode
     return beta * phi(beta * lam)
 
 
-def coefficients(k, beta):
+def coefficients(k, beta, mode="exact"):
     """Per-token lambda = ||k||^2, alpha, d alpha / d beta = e^{-beta lambda} and
-    d alpha / d lambda = beta^2 phi'(beta lambda). k: [..., d_k]; beta: [...]."""
+    d alpha / d lambda = beta^2 phi'(beta lambda) (1 and 0 in mode "euler").
+    k: [..., d_k]; beta: [...]."""
     k = np.asarray(k, dtype=np.float64)
     beta = np.asarray(beta, dtype=np.float64)
     lam = np.sum(k * k, axis=-1)
+    if mode == "euler":
+        return dict(lam=lam, alpha=beta.copy(), dalpha_dbeta=np.ones_like(beta),
+                    dalpha_dlam=np.zeros_like(beta))
+    assert mode == "exact", mode
     x = beta * lam
     return dict(lam=lam, alpha=beta * phi(x), dalpha_dbeta=np.exp(-x),
                 dalpha_dlam=beta * beta * dphi(x))
@@ -106,7 +120,7 @@ def coefficients(k, beta):
 # Token-by-token recurrence over N independent streams of length L.
 # ---------------------------------------------------------------------------
 
-def _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=0):
+def _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=0, mode="exact"):
     """q, k: [N, L, dk]; v: [N, L, dv]; beta: [N, L]; S0: [N, dk, dv] or None.
 
     Returns o [N, L, dv], final state [N, dk, dv] and, when checkpoint_every > 0,
@@ -117,7 +131,7 @@ def _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=0):
     S = np.zeros((N, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
     o = np.zeros((N, L, dv))
     checkpoints = []
-    a = alpha(beta, np.sum(k * k, axis=-1))            # [N, L]
+    a = alpha(beta, np.sum(k * k, axis=-1), mode)      # [N, L]
     for t in range(L):
         if checkpoint_every and t % checkpoint_every == 0:
             checkpoints.append(S.copy())
@@ -128,7 +142,7 @@ def _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=0):
     return o, S, checkpoints
 
 
-def _backward_streams(q, k, v, beta, do, scale, S0, dS_final):
+def _backward_streams(q, k, v, beta, do, scale, S0, dS_final, mode="exact"):
     """Reverse-mode gradients of sum(o * do) (+ <S_final, dS_final>) for _forward_streams.
 
     The state is stored only at block boundaries of CHUNK tokens and rebuilt
@@ -136,9 +150,9 @@ def _backward_streams(q, k, v, beta, do, scale, S0, dS_final):
     """
     N, L, dk = k.shape
     dv = v.shape[-1]
-    co = coefficients(k, beta)
+    co = coefficients(k, beta, mode)
     a = co["alpha"]
-    _, _, ckpt = _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=CHUNK)
+    _, _, ckpt = _forward_streams(q, k, v, beta, scale, S0, checkpoint_every=CHUNK, mode=mode)
     dq = np.zeros_like(q)
     dk_ = np.zeros_like(k)
     dv_ = np.zeros_like(v)
@@ -192,8 +206,8 @@ def sequences(B, T, cu_seqlens):
     return [(0, cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
 
 
-def forward(q, k, v, beta, scale=1.0, cu_seqlens=None, initial_state=None):
-    """EFLA forward. q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T].
+def forward(q, k, v, beta, scale=1.0, cu_seqlens=None, initial_state=None, mode="exact"):
+    """EFLA forward (mode "euler": the delta rule). q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T].
 
     initial_state: None or [n_seq, H, dk, dv] (n_seq = B, or the number of packed
     sequences). Returns (o [B,H,T,dv], final_state [n_seq, H, dk, dv]), fp64.
@@ -207,14 +221,14 @@ def forward(q, k, v, beta, scale=1.0, cu_seqlens=None, initial_state=None):
     S0 = _f64(initial_state)
     for i, (b, s, e) in enumerate(seqs):
         o_i, S_i, _ = _forward_streams(q[b, :, s:e], k[b, :, s:e], v[b, :, s:e], beta[b, :, s:e],
-                                       scale, None if S0 is None else S0[i])
+                                       scale, None if S0 is None else S0[i], mode=mode)
         o[b, :, s:e] = o_i
         final[i] = S_i
     return o, final
 
 
 def backward(q, k, v, beta, do, scale=1.0, cu_seqlens=None, initial_state=None,
-             d_final_state=None):
+             d_final_state=None, mode="exact"):
     """Gradients of sum(o * do) (+ <final_state, d_final_state>) for `forward`.
 
     Returns dict(dq, dk, dv, dbeta, d_initial_state), fp64.
@@ -230,7 +244,7 @@ def backward(q, k, v, beta, do, scale=1.0, cu_seqlens=None, initial_state=None,
     for i, (b, s, e) in enumerate(seqs):
         dq, dk_, dv_, dbeta, dS0 = _backward_streams(
             q[b, :, s:e], k[b, :, s:e], v[b, :, s:e], beta[b, :, s:e], do[b, :, s:e], scale,
-            None if S0 is None else S0[i], None if dSF is None else dSF[i])
+            None if S0 is None else S0[i], None if dSF is None else dSF[i], mode=mode)
         g["dq"][b, :, s:e] = dq
         g["dk"][b, :, s:e] = dk_
         g["dv"][b, :, s:e] = dv_
@@ -243,20 +257,20 @@ def backward(q, k, v, beta, do, scale=1.0, cu_seqlens=None, initial_state=None,
 # Chunkwise (UT transform) form: per-stage values for tests of the GPU stages.
 # ---------------------------------------------------------------------------
 
-def chunk_ut(k, v, beta):
+def chunk_ut(k, v, beta, mode="exact"):
     """UT transform of one chunk. k: [C, dk]; v: [C, dv]; beta: [C].
 
     Returns dict(alpha, T, W, U) with T = (I + strictly_lower(diag(alpha) K K^T))^{-1} diag(alpha).
     """
     k, v, beta = _f64(k), _f64(v), _f64(beta)
     C = k.shape[0]
-    a = alpha(beta, np.sum(k * k, axis=-1))
+    a = alpha(beta, np.sum(k * k, axis=-1), mode)
     A = np.tril(a[:, None] * (k @ k.T), -1)
     T = scipy.linalg.solve_triangular(np.eye(C) + A, np.diag(a), lower=True, unit_diagonal=True)
     return dict(alpha=a, T=T, W=T @ k, U=T @ v)
 
 
-def chunk_factors(q, k, beta):
+def chunk_factors(q, k, beta, mode="exact"):
     """Per-chunk factors the forward keeps for the backward pass (section 3.3).
 
     q, k: [C, dk]; beta: [C]. Returns dict(X, M): X = (I + strictly_lower(diag(alpha) K K^T))^{-1},
@@ -264,7 +278,7 @@ def chunk_factors(q, k, beta):
     causal score block (diagonal kept) of the intra-chunk read-out."""
     q, k, beta = _f64(q), _f64(k), _f64(beta)
     C = k.shape[0]
-    a = alpha(beta, np.sum(k * k, axis=-1))
+    a = alpha(beta, np.sum(k * k, axis=-1), mode)
     A = np.tril(a[:, None] * (k @ k.T), -1)
     X = scipy.linalg.solve_triangular(np.eye(C) + A, np.eye(C), lower=True, unit_diagonal=True)
     return dict(X=X, M=np.tril(q @ k.T))

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 3
+    assert L.efla_abi_version() == 4
 
 
 def test_status_strings(L):
@@ -47,7 +47,7 @@ def _p(**kw):
     base.update(kw)
     return _lib.problem(base["B"], base["H"], base["T"], base["dk"], base["dv"], base["dtype"],
                         base.get("scale", 1.0), base.get("cu", None), base.get("n_seqs", 0),
-                        base.get("chunk", 64))
+                        base.get("chunk", 64), base.get("mode", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,6 +68,9 @@ def _p(**kw):
     (dict(B=2, cu=0x1000, n_seqs=3), 2),     # packed batches need B == 1
     (dict(B=1, cu=0x1000, n_seqs=0), 2),
     (dict(B=4, n_seqs=3), 2),
+    (dict(mode=1), 0),
+    (dict(mode=2), 4),
+    (dict(mode=-1), 4),
 ])
 def test_problem_validation(L, kw, code):
     p = _p(**kw)
@@ -124,6 +127,21 @@ def test_entry_points_reject_bad_arguments_without_launching(L):
     # invalid problem wins over everything else
     bad = _p(dk=96)
     assert L.efla_fwd(ctypes.byref(bad), fake, fake, fake, fake, fake, None, 0, fake, 1 << 40, None) == 4
+    # state I/O entry points: the same checks, plus the alignment of the state pointers
+    assert L.efla_fwd_state(ctypes.byref(p), fake, fake, fake, fake, odd, fake, None, None, 0, fake,
+                            ws_need, None) == 7
+    assert L.efla_fwd_state(ctypes.byref(p), fake, fake, fake, fake, None, fake, odd, None, 0, fake,
+                            ws_need, None) == 7
+    assert L.efla_bwd_state(ctypes.byref(p), fake, fake, fake, fake, None, fake, None, None, 0, fake,
+                            fake, fake, fake, odd, fake, 1 << 40, None) == 7
+    assert L.efla_bwd_state(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None, 0, fake,
+                            fake, fake, fake, None, fake, 1 << 40, None) == 1
+    # decode: dense batches only; every pointer required
+    assert L.efla_decode(ctypes.byref(p), fake, fake, fake, fake, None, fake, None) == 1
+    assert L.efla_decode(ctypes.byref(p), fake, fake, fake, fake, odd, fake, None) == 7
+    packed = _p(B=1, T=100, cu=0x1000, n_seqs=2)
+    assert L.efla_decode(ctypes.byref(packed), fake, fake, fake, fake, fake, fake, None) == 4
+    assert L.efla_decode(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None) == 4
     # an empty problem is a successful no-op that touches nothing
     empty = _p(T=0)
     assert L.efla_fwd(ctypes.byref(empty), None, None, None, None, None, None, 0, None, 0, None) == 0

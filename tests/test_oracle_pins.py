@@ -203,6 +203,24 @@ def test_overwrite_limit_for_large_step():
     assert np.allclose(k @ S1, v, rtol=1e-13, atol=1e-13)
 
 
+def test_euler_mode_is_the_delta_rule():
+    """mode "euler" of the forward equals the separately written delta-rule loop, on a packed
+    batch; the chunked form in that mode agrees as well."""
+    r = _rng(15)
+    H, dk, dv = 2, 5, 4
+    cu = np.array([0, 7, 70, 71, 140], dtype=np.int32)
+    T = int(cu[-1])
+    q, k = r.standard_normal((1, H, T, dk)), r.standard_normal((1, H, T, dk))
+    v, beta = r.standard_normal((1, H, T, dv)), r.uniform(0.0, 1.0, (1, H, T))
+    o, _ = O.forward(q, k, v, beta, scale=0.6, cu_seqlens=cu, mode="euler")
+    assert O.rel_err(o, O.euler_forward(q, k, v, beta, scale=0.6, cu_seqlens=cu)) < 1e-13
+    o_exact, _ = O.forward(q, k, v, beta, scale=0.6, cu_seqlens=cu)
+    assert O.rel_err(o, o_exact) > 1e-2   # the two modes do differ at these key norms
+    c = O.coefficients(k, beta, mode="euler")
+    assert np.array_equal(c["alpha"], beta) and np.all(c["dalpha_dbeta"] == 1.0)
+    assert np.all(c["dalpha_dlam"] == 0.0)
+
+
 def test_euler_limit_is_third_order_in_key_scale():
     """Section 3.4: for small beta*lambda EFLA equals the delta rule up to higher-order terms.
     With k -> s k the one-step gap to the Euler update shrinks like s^3."""
@@ -366,12 +384,13 @@ def test_split_sequence_with_carried_state():
 
 # ---------------------------------------------------------------- backward
 
-def _loss(q, k, v, beta, do, dSF, S0, scale, cu=None):
-    o, SF = O.forward(q, k, v, beta, scale=scale, cu_seqlens=cu, initial_state=S0)
+def _loss(q, k, v, beta, do, dSF, S0, scale, cu=None, mode="exact"):
+    o, SF = O.forward(q, k, v, beta, scale=scale, cu_seqlens=cu, initial_state=S0, mode=mode)
     return float(np.sum(o * do) + np.sum(SF * dSF))
 
 
-def test_backward_against_central_differences_every_coordinate():
+@pytest.mark.parametrize("mode", ["exact", "euler"])
+def test_backward_against_central_differences_every_coordinate(mode):
     r = _rng(31)
     B, H, T, dk, dv = 1, 2, 12, 4, 3
     q, k = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk)) * 1.5
@@ -380,7 +399,7 @@ def test_backward_against_central_differences_every_coordinate():
     S0 = r.standard_normal((B, H, dk, dv))
     dSF = r.standard_normal((B, H, dk, dv))
     scale = 0.8
-    g = O.backward(q, k, v, beta, do, scale=scale, initial_state=S0, d_final_state=dSF)
+    g = O.backward(q, k, v, beta, do, scale=scale, initial_state=S0, d_final_state=dSF, mode=mode)
     args = dict(q=q, k=k, v=v, beta=beta, S0=S0)
     names = dict(q="dq", k="dk", v="dv", beta="dbeta", S0="d_initial_state")
     eps = 1e-6
@@ -391,8 +410,9 @@ def test_backward_against_central_differences_every_coordinate():
             xp[idx] += eps
             xm[idx] -= eps
             ap, am = dict(args, **{name: xp}), dict(args, **{name: xm})
-            fd[idx] = (_loss(ap["q"], ap["k"], ap["v"], ap["beta"], do, dSF, ap["S0"], scale)
-                       - _loss(am["q"], am["k"], am["v"], am["beta"], do, dSF, am["S0"], scale)) / (2 * eps)
+            fd[idx] = (_loss(ap["q"], ap["k"], ap["v"], ap["beta"], do, dSF, ap["S0"], scale, mode=mode)
+                       - _loss(am["q"], am["k"], am["v"], am["beta"], do, dSF, am["S0"], scale,
+                               mode=mode)) / (2 * eps)
         assert np.max(np.abs(fd - g[names[name]])) < 1e-7 * max(1.0, np.max(np.abs(fd))), name
 
 
