@@ -154,16 +154,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     tX.load(xsav + c.sh * 64 * 64, 64, tid);
   };
   auto issue_q = [&](const ChunkUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
-  auto issue_sg = [&](const ChunkUnit& c) {
+  auto issue_s = [&](const ChunkUnit& c) {
 #pragma unroll
     for (int j = 0; j < CK; ++j)
 #pragma unroll
-      for (int ks = 0; ks < KSV; ++ks) {
-        const int64_t o = c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC;
-        fS[j][ks] = frag_rm<E>(states + o, DV, lane);
-        fG[j][ks] = frag_rm<E>(dstates + o, DV, lane);
-      }
+      for (int ks = 0; ks < KSV; ++ks)
+        fS[j][ks] = frag_rm<E>(states + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
   };
+  auto issue_g = [&](const ChunkUnit& c) {
+#pragma unroll
+    for (int j = 0; j < CK; ++j)
+#pragma unroll
+      for (int ks = 0; ks < KSV; ++ks)
+        fG[j][ks] = frag_rm<E>(dstates + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
+  };
+  auto issue_sg = [&](const ChunkUnit& c) { issue_s(c); issue_g(c); };
 
   ChunkUnit cur = chunk_unit(g, u);
   issue_k(cur);
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   mma_blk<E, true, true, 2, CK, kChunk>(sM + 16 * rb0, LT, sQ + 16 * cK, LK,
                                         round_down_kc<E>(16 * rb0), kChunk, aK, lane);
   __syncthreads();
-  if (more) issue_sg(nxt);  // S and G registers are free again
+  if (more) issue_s(nxt);  // S registers are free again; G follows two steps later
 
   // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s); stage dQ and dV
   {
@@ -424,7 +429,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   s2g<E, DK, kBwdThreads>(dq + row0 * DK, DK, sQ, LK, n, tid);
   s2g<E, DV, kBwdThreads>(dv + row0 * DV, DV, sDU, LV, n, tid);
   __syncthreads();
-  if (more) issue_q(nxt);
+  if (more) { issue_q(nxt); issue_g(nxt); }
 
   // ---- 6: dK += H K; dk += 2 k dalpha dalpha/dlam; dbeta = dalpha e^-x
   mma_blk<E, false, true, 2, CK, kChunk>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0, kChunk, aK, lane);
