@@ -20,6 +20,8 @@
 // the token index read their row-major LDS tiles k-major (LDS transpose reads for bf16).
 // Each wave computes 2x2 (or 2x1) blocks of 16x16 so that every operand fragment it reads
 // from LDS feeds two MFMAs: LDS bandwidth, not the matrix cores, bounds the arithmetic.
+// Products that end up in LDS row-major are formed transposed (operands swapped), so each
+// lane holds four consecutive columns of one row and stores them with one vector write.
 // Seven barrier-separated steps:
 //   1 loads land; 2 dW, scale dO S^T, U~ G^T, dM, coefficients;
 //   3 dT (-> dalpha, dX), T^T dU, T^T dW, dM K, dM^T Q;
@@ -46,7 +48,7 @@ struct ChunkBwdLds {
   static constexpr size_t oX = oV + TV;          // X   [64][LT]
   static constexpr size_t oM = oX + TT;          // dM  [64][LT]
   static constexpr size_t oC = oM + TT;          // lambda, alpha, e^-x, dalpha/dlam [64]
-  static constexpr size_t oP = oC + 4 * 64 * 4;  // dalpha partials [8][64]
+  static constexpr size_t oP = oC + 4 * 64 * 4;  // dalpha partials [64][8]
   static constexpr size_t bytes = oP + 8 * 64 * 4;
   static_assert(TT <= TV, "64x64 work tiles reuse d_v-wide regions");
 };
@@ -64,7 +66,7 @@ struct TileRegs {
     for (int it = 0; it < IT; ++it) {
       const int i = it * kBwdThreads + tid;
       const int r = min(i / VPR, n - 1), c = (i % VPR) * VE;
-      v[it] = *(const u32x4*)(g + (int64_t)r * COLS + c);
+      v[it] = *at_byte<u32x4>(g, (unsigned)(r * COLS + c) * (unsigned)sizeof(E));
     }
   }
   EFLA_DEV void store(E* s, int ld, int n, int tid) const {
@@ -83,6 +85,16 @@ EFLA_DEV f32x4 tri_mask(f32x4 c, int rb, int nb, bool keep_diag, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * rb + 4 * (lane >> 4) + i, col = 16 * nb + (lane & 15);
+    if (keep_diag ? r < col : r <= col) c[i] = 0.f;
+  }
+  return c;
+}
+
+// The same for a block held in row layout (lane owns row lane & 15, columns 4 (lane >> 4)..).
+EFLA_DEV f32x4 tri_mask_row(f32x4 c, int rb, int nb, bool keep_diag, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * rb + (lane & 15), col = 16 * nb + 4 * (lane >> 4) + i;
     if (keep_diag ? r < col : r <= col) c[i] = 0.f;
   }
   return c;
@@ -117,20 +129,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   float* cAl = cLam + 64;
   float* cEx = cLam + 128;
   float* cDl = cLam + 192;
-  float* pCol = (float*)(smem + L::oP);  // [4][64]: column sums of dT . X per row block
-  float* pRow = pCol + 4 * 64;           // [4][64]: row sums of dA . KK^T per column block
+  // dalpha partials [64][8]: slots 0-3 column sums of dT . X per row block, slots 4-7 row
+  // sums of dA . KK^T per column block (one token's eight partials are one 32-byte row).
+  float* pDa = (float*)(smem + L::oP);
 
   int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv0 = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Chunks of all heads are numbered u = slot * H + h; packed batches use a prefix of them.
   const int nu = used_slots(g) * g.H;
   int u = blockIdx.x;
   if (u >= nu) return;
-  // [64][d] outputs: wave wv owns row blocks rb0, rb0 + 1 and column blocks cK.. (cV..).
-  const int rb0 = 2 * (wv >> 2), cK = CK * (wv & 3), cV = CV * (wv & 3);
-  // 64x64 work matrices: wave wv owns blocks (pr, pn) and (pr, pn + 1).
-  const int pr = wv >> 1, pn = 2 * (wv & 1);
-  const bool plow = pn <= pr;  // at least one of the two blocks is on or below the diagonal
 
   TileRegs<E, DK> tK, tQ;
   TileRegs<E, DV> tDU, tDO, tU, tV;
@@ -154,26 +162,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     tX.load(xsav + c.sh * 64 * 64, 64, tid);
   };
   auto issue_q = [&](const ChunkUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
-  auto issue_s = [&](const ChunkUnit& c) {
+  auto issue_s = [&](const ChunkUnit& c, int cK) {
 #pragma unroll
     for (int j = 0; j < CK; ++j)
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks)
-        fS[j][ks] = frag_rm<E>(states + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
+        fS[j][ks] = frag_rm_g<E>(states + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
   };
-  auto issue_g = [&](const ChunkUnit& c) {
+  auto issue_g = [&](const ChunkUnit& c, int cK) {
 #pragma unroll
     for (int j = 0; j < CK; ++j)
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks)
-        fG[j][ks] = frag_rm<E>(dstates + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
+        fG[j][ks] = frag_rm_g<E>(dstates + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
   };
-  auto issue_sg = [&](const ChunkUnit& c) { issue_s(c); issue_g(c); };
 
   ChunkUnit cur = chunk_unit(g, u);
   issue_k(cur);
   issue_du_do(cur);
-  issue_sg(cur);
+  issue_s(cur, CK * (wv0 & 3));
+  issue_g(cur, CK * (wv0 & 3));
   issue_u(cur);
   issue_v_x(cur);
   issue_q(cur);
@@ -183,6 +191,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // registers through the whole chunk and spill). Recomputing them costs a few ALU ops.
   asm volatile("" : "+v"(tid));
   lane = tid & 63;
+  // The same for the wave index: wave-dependent LDS offsets are formed again in scalar
+  // registers where they are used instead of being held (and spilled) across the loop.
+  int wv = wv0;
+  asm volatile("" : "+s"(wv));
+  // [64][d] outputs: wave wv owns row blocks rb0, rb0 + 1 and column blocks cK.. (cV..).
+  const int rb0 = 2 * (wv >> 2), cK = CK * (wv & 3), cV = CV * (wv & 3);
+  // 64x64 work matrices: wave wv owns blocks (pr, pn) and (pr, pn + 1).
+  const int pr = wv >> 1, pn = 2 * (wv & 1);
+  const bool plow = pn <= pr;  // at least one of the two blocks is on or below the diagonal
   const int n = cur.n;
   const int64_t row0 = cur.row0;
   // ---- 1: this chunk's tiles land in LDS; ||k||^2 is reduced from the loaded K vectors
@@ -197,8 +214,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < TKr::VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
-#pragma unroll
-      for (int off = TKr::VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      acc = group_sum<TKr::VPR>(acc);
       if (i % TKr::VPR == 0) cLam[i / TKr::VPR] = i / TKr::VPR < n ? acc : 0.f;
     }
   }
@@ -237,26 +253,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < CK; ++j) {
-          aW[i][j] = Mma<E>::step(fu[i], fS[j][ks], aW[i][j]);
-          aQ[i][j] = Mma<E>::step(fo[i], fS[j][ks], aQ[i][j]);
-          aK[i][j] = Mma<E>::step(fv[i], fG[j][ks], aK[i][j]);
+          aW[i][j] = Mma<E>::step(fS[j][ks], fu[i], aW[i][j]);
+          aQ[i][j] = Mma<E>::step(fS[j][ks], fo[i], aQ[i][j]);
+          aK[i][j] = Mma<E>::step(fG[j][ks], fv[i], aK[i][j]);
         }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < CK; ++j) {
-        st_frag_lds<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, -aW[i][j], lane);
+        st_frag_t<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, -aW[i][j], lane);
         aQ[i][j] *= g.scale;
       }
   }
   {
     f32x4 m[1][2] = {{zero4(), zero4()}};
-    if (plow) mma_blk<E, false, false, 1, 2, DV>(sDO + 16 * pr * LV, LV, sU + 16 * pn * LV, LV, 0, DV, m, lane);
+    if (plow) mma_blk<E, false, false, 1, 2, DV, true>(sDO + 16 * pr * LV, LV, sU + 16 * pn * LV, LV, 0, DV, m, lane);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      st_frag_lds<E>(sM + 16 * pr * LT + 16 * (pn + j), LT,
-                     tri_mask(m[0][j], pr, pn + j, true, lane) * g.scale, lane);
+      st_frag_t<E>(sM + 16 * pr * LT + 16 * (pn + j), LT,
+                   tri_mask_row(m[0][j], pr, pn + j, true, lane) * g.scale, lane);
   }
   if (tid < 64) {
     const FlowCoef cf = flow_coef(tid < n ? bt_cur : 0.f, cLam[tid], g.euler);
@@ -290,7 +306,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       }
       cs += __shfl_xor(cs, 16);
       cs += __shfl_xor(cs, 32);
-      if (lane < 16) pCol[pr * 64 + col] = cs;
+      if (lane < 16) pDa[col * 8 + pr] = cs;
       st_frag_lds<E>(sDX + 16 * pr * LT + 16 * (pn + j), LT, dx, lane);
     }
   }
@@ -319,32 +335,34 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < CV; ++j) aV[i][j] = Mma<E>::step(xa[i], bu[j], aV[i][j]);
+        for (int j = 0; j < CV; ++j) aV[i][j] = Mma<E>::step(bu[j], xa[i], aV[i][j]);
 #pragma unroll
-        for (int j = 0; j < CK; ++j) tw[i][j] = Mma<E>::step(xa[i], bw[j], tw[i][j]);
+        for (int j = 0; j < CK; ++j) tw[i][j] = Mma<E>::step(bw[j], xa[i], tw[i][j]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const float al = cAl[16 * (rb0 + i) + (lane & 15)];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float al = cAl[16 * (rb0 + i) + 4 * (lane >> 4) + e];
 #pragma unroll
         for (int j = 0; j < CV; ++j) aV[i][j][e] *= al;
 #pragma unroll
         for (int j = 0; j < CK; ++j) aK[i][j][e] = fmaf(al, tw[i][j][e], aK[i][j][e]);
       }
+    }
   }
   // dM is lower triangular: dM K for rows of block rb needs k < 16 (rb + 1); dM^T Q needs
   // k >= 16 rb.
-  mma_blk<E, false, true, 2, CK, kChunk>(sM + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0,
-                                         round_up_kc<E>(16 * (rb0 + 2)), aQ, lane);
-  mma_blk<E, true, true, 2, CK, kChunk>(sM + 16 * rb0, LT, sQ + 16 * cK, LK,
-                                        round_down_kc<E>(16 * rb0), kChunk, aK, lane);
+  mma_blk<E, false, true, 2, CK, kChunk, true>(sM + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0,
+                                               round_up_kc<E>(16 * (rb0 + 2)), aQ, lane);
+  mma_blk<E, true, true, 2, CK, kChunk, true>(sM + 16 * rb0, LT, sQ + 16 * cK, LK,
+                                              round_down_kc<E>(16 * rb0), kChunk, aK, lane);
   __syncthreads();
-  if (more) issue_s(nxt);  // S registers are free again; G follows two steps later
+  if (more) issue_s(nxt, cK);  // S registers are free again; G follows two steps later
 
-  // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s); stage dQ and dV
+  // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s), kept transposed
+  //         (sY[s][t] = Y[t][s]); stage dQ and dV
   {
     f32x4 y[1][2] = {{zero4(), zero4()}};
     if (plow)
@@ -353,17 +371,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const f32x4 yy = pn + j <= pr ? y[0][j] : zero4();
-      st_frag_lds<E>(sY + 16 * pr * LT + 16 * (pn + j), LT, yy, lane);
+      st_frag_t<E>(sY + 16 * (pn + j) * LT + 16 * pr, LT, yy, lane);
     }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int j = 0; j < CK; ++j)
-      st_frag_lds<E>(sQ + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aQ[i][j], lane);
+      st_frag_t<E>(sQ + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aQ[i][j], lane);
 #pragma unroll
     for (int j = 0; j < CV; ++j)
-      st_frag_lds<E>(sDU + 16 * (rb0 + i) * LV + 16 * (cV + j), LV, aV[i][j], lane);
+      st_frag_t<E>(sDU + 16 * (rb0 + i) * LV + 16 * (cV + j), LV, aV[i][j], lane);
   }
   __syncthreads();
   if (more) {
@@ -375,15 +393,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   {
     f32x4 da[1][2] = {{zero4(), zero4()}}, kk[1][2] = {{zero4(), zero4()}};
     if (plow) {
-      mma_blk<E, true, true, 1, 2, kChunk>(sX + 16 * pr, LT, sY + 16 * pn, LT,
-                                           round_down_kc<E>(16 * pr), kChunk, da, lane);
+      mma_blk<E, true, false, 1, 2, kChunk>(sX + 16 * pr, LT, sY + 16 * pn * LT, LT,
+                                            round_down_kc<E>(16 * pr), kChunk, da, lane);
       mma_blk<E, false, false, 1, 2, DK>(sK + 16 * pr * LK, LK, sK + 16 * pn * LK, LK, 0, DK, kk, lane);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int nb = pn + j;
       if (nb > pr) {
-        if (lane < 16) pRow[nb * 64 + 16 * pr + lane] = 0.f;
+        if (lane < 16) pDa[(16 * pr + lane) * 8 + 4 + nb] = 0.f;
         continue;
       }
       const int col = 16 * nb + (lane & 15);
@@ -397,17 +415,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
         dg[i] = a * cAl[row];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = rs[i];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        rs[i] = x;
-      }
+      for (int i = 0; i < 4; ++i) rs[i] = group_sum<16>(rs[i]);
       if ((lane & 15) == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pRow[nb * 64 + 16 * pr + 4 * (lane >> 4) + i] = rs[i];
+        for (int i = 0; i < 4; ++i) pDa[(16 * pr + 4 * (lane >> 4) + i) * 8 + 4 + nb] = rs[i];
       }
       if (nb < pr) {
         st_frag_lds<E>(sH + 16 * pr * LT + 16 * nb, LT, dg, lane);
@@ -429,31 +440,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   s2g<E, DK, kBwdThreads>(dq + row0 * DK, DK, sQ, LK, n, tid);
   s2g<E, DV, kBwdThreads>(dv + row0 * DV, DV, sDU, LV, n, tid);
   __syncthreads();
-  if (more) { issue_q(nxt); issue_g(nxt); }
+  if (more) { issue_q(nxt); issue_g(nxt, cK); }
 
   // ---- 6: dK += H K; dk += 2 k dalpha dalpha/dlam; dbeta = dalpha e^-x
-  mma_blk<E, false, true, 2, CK, kChunk>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0, kChunk, aK, lane);
+  mma_blk<E, false, true, 2, CK, kChunk, true>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0,
+                                               kChunk, aK, lane);
+  auto dalpha = [&](int t) {
+    const f32x4 a = *(const f32x4*)(pDa + 8 * t), b = *(const f32x4*)(pDa + 8 * t + 4);
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (rb0 + i) + (lane & 15);
+    const float f = 2.f * dalpha(row) * cDl[row];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * (rb0 + i) + 4 * (lane >> 4) + e;
-      const float da = pCol[row] + pCol[64 + row] + pCol[128 + row] + pCol[192 + row] +
-                       pRow[row] + pRow[64 + row] + pRow[128 + row] + pRow[192 + row];
-      const float f = 2.f * da * cDl[row];
+    for (int j = 0; j < CK; ++j) {
+      const f32x4 kv = ld4f<E>(sK + row * LK + 16 * (cK + j) + 4 * (lane >> 4));
 #pragma unroll
-      for (int j = 0; j < CK; ++j)
-        aK[i][j][e] = fmaf(f, to_f(sK[row * LK + 16 * (cK + j) + (lane & 15)]), aK[i][j][e]);
+      for (int e = 0; e < 4; ++e) aK[i][j][e] = fmaf(f, kv[e], aK[i][j][e]);
+      st_frag_t<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aK[i][j], lane);
     }
-#pragma unroll
-    for (int j = 0; j < CK; ++j)
-      st_frag_lds<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aK[i][j], lane);
   }
-  if (tid < n) {
-    const float da = pCol[tid] + pCol[64 + tid] + pCol[128 + tid] + pCol[192 + tid] + pRow[tid] +
-                     pRow[64 + tid] + pRow[128 + tid] + pRow[192 + tid];
-    dbeta[row0 + tid] = to_e<E>(da * cEx[tid]);
-  }
+  if (tid < n) dbeta[row0 + tid] = to_e<E>(dalpha(tid) * cEx[tid]);
   __syncthreads();
   s2g<E, DK, kBwdThreads>(dk + row0 * DK, DK, sW, LK, n, tid);
   if (!more) break;

@@ -121,6 +121,23 @@ EFLA_DEV typename Mma<E>::vec frag_rm(const E* src, int ld, int lane) {
 
 template <typename E> EFLA_DEV typename Mma<E>::vec frag_km(const E* src, int ld, int lane);
 
+// Global memory addressed as a wave-uniform base plus a 32-bit unsigned byte offset per lane:
+// the access can then use the scalar-base form (no 64-bit address arithmetic per lane).
+template <typename T, typename E> EFLA_DEV T* at_byte(E* base, unsigned byte_off) {
+  return (T*)((char*)base + byte_off);
+}
+template <typename T, typename E> EFLA_DEV const T* at_byte(const E* base, unsigned byte_off) {
+  return (const T*)((const char*)base + byte_off);
+}
+
+// frag_rm from global memory, src uniform across the wave.
+template <typename E>
+EFLA_DEV typename Mma<E>::vec frag_rm_g(const E* __restrict__ src, int ld, int lane) {
+  const unsigned off = ((unsigned)(lane & 15) * (unsigned)ld + (unsigned)(lane >> 4) * (Mma<E>::KC / 4)) *
+                       (unsigned)sizeof(E);
+  return *at_byte<typename Mma<E>::vec>(src, off);
+}
+
 template <> EFLA_DEV f32x4 frag_km<float>(const float* src, int ld, int lane) {
   const float* p = src + (lane >> 4) * 4 * ld + (lane & 15);
   return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
@@ -155,7 +172,10 @@ EFLA_DEV f32x4 mma(const E* a, int lda, const E* b, int ldb, int k0, int k1, f32
 // 16 i rows (AK = false) or 16 i columns (AK = true, k-major) after a; column block j of B
 // likewise after b (BK = false: rows of B^T; BK = true: columns of k-major B). Every operand
 // fragment is read from memory once per k step and feeds NB (or NA) products.
-template <typename E, bool AK, bool BK, int NA, int NB, int K>
+// TR = true hands the two operands to the matrix core the other way round, which yields the
+// transposed product: the accumulator then holds each block in row layout (lane l owns row
+// l & 15, columns 4 (l >> 4) .. + 3), ready for one vector store per lane (st_frag_t).
+template <typename E, bool AK, bool BK, int NA, int NB, int K, bool TR = false>
 EFLA_DEV void mma_blk(const E* a, int lda, const E* b, int ldb, int k0, int k1,
                       f32x4 (&acc)[NA][NB], int lane) {
   constexpr int KC = Mma<E>::KC;
@@ -176,7 +196,8 @@ EFLA_DEV void mma_blk(const E* a, int lda, const E* b, int ldb, int k0, int k1,
 #pragma unroll
     for (int i = 0; i < NA; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = Mma<E>::step(av[i], bv[j], acc[i][j]);
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = TR ? Mma<E>::step(bv[j], av[i], acc[i][j]) : Mma<E>::step(av[i], bv[j], acc[i][j]);
   }
 }
 
@@ -196,6 +217,31 @@ template <> EFLA_DEV void st_frag_t<float>(float* s, int ld, f32x4 c, int lane) 
 template <> EFLA_DEV void st_frag_t<__bf16>(__bf16* s, int ld, f32x4 c, int lane) {
   bf16x4 v = {(__bf16)c[0], (__bf16)c[1], (__bf16)c[2], (__bf16)c[3]};
   *(bf16x4*)(s + (lane & 15) * ld + 4 * (lane >> 4)) = v;
+}
+
+// Cross-lane sums inside a 16-lane row with DPP moves folded into the adds (VALU only, no
+// LDS-pipe permutes): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+template <int CTRL> EFLA_DEV float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+// Sum over each aligned group of N consecutive lanes (N = 1, 2, 4, 8 or 16); every lane of
+// the group receives the sum.
+template <int N> EFLA_DEV float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+
+// Four consecutive elements as fp32 (8- or 16-byte aligned LDS or global address).
+template <typename E> EFLA_DEV f32x4 ld4f(const E* p);
+template <> EFLA_DEV f32x4 ld4f<float>(const float* p) { return *(const f32x4*)p; }
+template <> EFLA_DEV f32x4 ld4f<__bf16>(const __bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
 // Store an accumulator tile row-major into LDS: s[m][n] = C[m][n]. The ROCm 7.2 LLVM
@@ -330,7 +376,10 @@ EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid
     const int i = it * NT + tid;
     if (TOT % NT == 0 || i < TOT) {
       const int r = i / VPR, c = (i % VPR) * V;
-      if (r < nvalid) *(u32x4*)(g + (int64_t)r * gld + c) = *(const u32x4*)(s + r * ld + c);
+      // 32-bit unsigned element offset from the (uniform) tile base: the store can use the
+      // scalar-base addressing form instead of a 64-bit address per lane.
+      const unsigned off = ((unsigned)r * (unsigned)gld + (unsigned)c) * (unsigned)sizeof(E);
+      if (r < nvalid) *at_byte<u32x4>(g, off) = *(const u32x4*)(s + r * ld + c);
     }
   }
 }

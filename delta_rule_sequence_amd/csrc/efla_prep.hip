@@ -36,8 +36,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int64_t ntok, int euler,
         acc = fmaf(f, f, acc);
       }
     }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    acc = group_sum<LPR>(acc);
     if (sub == 0) {
       const FlowCoef c = flow_coef(to_f(beta[row]), acc, euler != 0);
       if (lam) lam[row] = acc;

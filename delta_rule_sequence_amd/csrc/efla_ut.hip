@@ -107,8 +107,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
-#pragma unroll
-      for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      acc = group_sum<VPR>(acc);
       if (i % VPR == 0) sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc, g.euler).alpha;
     }
 #pragma unroll
