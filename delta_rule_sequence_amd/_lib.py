@@ -31,7 +31,8 @@ class EflaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("mode", ctypes.c_int32)]
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("segments", ctypes.c_int32)]
 
 
 class EflaSavedLayout(ctypes.Structure):
@@ -106,5 +107,5 @@ def check(fn, code):
 
 
 def problem(B, H, T, dk, dv, dtype, scale=1.0, cu_seqlens_ptr=None, n_seqs=0, chunk=64,
-            mode=EFLA_EXACT):
-    return EflaProblem(B, H, T, dk, dv, dtype, chunk, scale, cu_seqlens_ptr, n_seqs, mode)
+            mode=EFLA_EXACT, segments=0):
+    return EflaProblem(B, H, T, dk, dv, dtype, chunk, scale, cu_seqlens_ptr, n_seqs, mode, segments)

@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libefla.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["efla_api.hip", "efla_prep.hip", "efla_ut.hip", "efla_scan_fwd.hip",
-           "efla_scan_bwd.hip", "efla_chunk_bwd.hip", "efla_decode.hip"]
+           "efla_scan_seg.hip", "efla_scan_bwd.hip", "efla_chunk_bwd.hip", "efla_decode.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 vector instructions.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -140,6 +140,26 @@ efla_status to_shape(const efla_problem* p, Shape& s) {
   s.slots = p->cu_seqlens ? (int64_t)(p->T / kChunk) + p->n_seqs : (int64_t)p->B * s.ntc;
   s.euler = p->mode == EFLA_EULER;
   if (s.slots * p->H >= ((int64_t)1 << 31)) return EFLA_ERR_UNSUPPORTED;
+  // Segment plan of the forward scan (dense batches): G segments of nc chunks each.
+  if (p->segments < 0) return EFLA_ERR_SHAPE;
+  s.seg = 1;
+  s.seg_nc = 0;
+  s.seg_plan = 1;
+  s.seg_plan_nc = 0;
+  if (!p->cu_seqlens && s.ntc > 1) {
+    int want = p->segments;
+    if (want == 0) {  // split only when whole-sequence scans would leave compute units idle
+      const int64_t wgs = (int64_t)p->B * p->H * (p->dv / 32 > 0 ? p->dv / 32 : 1);
+      want = (wgs < 128 && s.ntc >= 32) ? (int)(512 / wgs) : 1;
+      if (want > s.ntc / 16) want = s.ntc / 16;
+    }
+    if (want > s.ntc) want = s.ntc;
+    if (want > 1) {
+      const int nc = (s.ntc + want - 1) / want;
+      s.seg_plan = (s.ntc + nc - 1) / nc;  // no empty segment
+      s.seg_plan_nc = nc;
+    }
+  }
   return EFLA_OK;
 }
 
@@ -150,6 +170,16 @@ size_t bytes_states(const Shape& s) { return (size_t)s.slots * s.H * s.dk * s.dv
 size_t bytes_table(const Shape& s) { return s.cu ? (size_t)(s.n_seqs + 1) * 4 : 0; }
 size_t bytes_m(const Shape& s) { return (size_t)s.slots * s.H * kChunk * kChunk * esize(s); }
 size_t bytes_x(const Shape& s) { return bytes_m(s); }
+// Segment-parallel scan: R and S_in, fp32 [B * G][H][dk][dv], and P, fp32 [B * G][H][dk][dk].
+size_t bytes_seg_state(const Shape& s) {
+  return s.seg_plan > 1 ? (size_t)s.B * s.seg_plan * s.H * s.dk * s.dv * 4 : 0;
+}
+size_t bytes_seg_p(const Shape& s) {
+  return s.seg_plan > 1 ? (size_t)s.B * s.seg_plan * s.H * s.dk * s.dk * 4 : 0;
+}
+size_t bytes_seg(const Shape& s) {
+  return 2 * align_up(bytes_seg_state(s)) + align_up(bytes_seg_p(s));
+}
 
 // Layout of the forward->backward buffer.
 struct Saved {
@@ -174,16 +204,17 @@ Saved saved_layout(const Shape& s) {
   return L;
 }
 
-// Forward workspace: U, plus W, M and the chunk table when no saved buffer is given.
+// Forward workspace: U, plus W, M and the chunk table when no saved buffer is given, plus
+// the segment-parallel scan's buffers.
 size_t ws_fwd(const Shape& s) {
   return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s)) +
-         align_up(bytes_m(s));
+         align_up(bytes_m(s)) + bytes_seg(s);
 }
-// Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer and U
-// for the recompute path.
+// Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer, U and
+// the segment buffers for the recompute path.
 size_t ws_bwd(const Shape& s) {
   return align_up(bytes_v(s)) + align_up(bytes_states(s)) + saved_layout(s).total +
-         align_up(bytes_v(s));
+         align_up(bytes_v(s)) + bytes_seg(s);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -192,16 +223,31 @@ efla_status hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_E
 
 bool empty(const Shape& s) { return s.T == 0; }
 
-// Forward stages shared by efla_fwd and the recompute path of efla_bwd.
+// Forward stages shared by efla_fwd and the recompute path of efla_bwd. seg: bytes_seg(s)
+// of workspace for the segment-parallel scan (unused when the plan has one segment).
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                         const void* beta, void* o, unsigned char* w, unsigned char* ut,
                         unsigned char* states, int* table, unsigned char* m, unsigned char* x,
-                        unsigned char* u, const float* h0, float* ht, hipStream_t st) {
+                        unsigned char* u, const float* h0, float* ht, unsigned char* seg,
+                        hipStream_t st) {
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
   if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, w, u, m, x, st))) return r;
-  return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, h0, ht, st));
+  if (s.seg_plan <= 1)
+    return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, h0, ht, st));
+  // Segment-parallel: zero-start states R and transitions P of all segments, the sequential
+  // chain S_in, then the output scan over all segments from S_in.
+  const Shape sv = segment_view(s);
+  float* R = (float*)seg;
+  float* S_in = (float*)(seg + align_up(bytes_seg_state(s)));
+  float* P = (float*)(seg + 2 * align_up(bytes_seg_state(s)));
+  if (efla_status r = hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, nullptr, nullptr,
+                                                 nullptr, nullptr, R, st)))
+    return r;
+  if (efla_status r = hip_status(launch_scan_fwd_transition(sv, k, w, P, st))) return r;
+  if (efla_status r = hip_status(launch_seg_combine(s, P, R, h0, S_in, ht, st))) return r;
+  return hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, o, ut, states, S_in, nullptr, st));
 }
 
 }  // namespace
@@ -307,6 +353,7 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
   unsigned char* w_ws = wsb + align_up(bytes_v(s));
   int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
   unsigned char* m_ws = (unsigned char*)table_ws + align_up(bytes_table(s));
+  unsigned char* seg_ws = m_ws + align_up(bytes_m(s));
   unsigned char* sv = (unsigned char*)saved;
   unsigned char* w = sv ? sv + L.w : w_ws;
   unsigned char* ut = sv ? sv + L.ut : nullptr;
@@ -314,7 +361,7 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
   int* table = sv ? (int*)(sv + L.table) : table_ws;
   unsigned char* m = sv ? sv + L.m : m_ws;
   unsigned char* x = sv ? sv + L.x : nullptr;
-  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, h0, ht,
+  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, h0, ht, seg_ws,
                      (hipStream_t)stream);
 }
 
@@ -349,9 +396,10 @@ efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, 
   if (!sv) {
     unsigned char* rec = dstates + align_up(bytes_states(s));
     unsigned char* u = rec + L.total;
+    unsigned char* seg = u + align_up(bytes_v(s));
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
                                     rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
-                                    u, h0, nullptr, st))
+                                    u, h0, nullptr, seg, st))
       return r;
     sv = rec;
   }

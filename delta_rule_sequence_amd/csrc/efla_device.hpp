@@ -543,6 +543,8 @@ struct Geom {
   int max_slots;       // chunk slots the state buffers hold per head
   float scale;
   int euler;           // step rule: 0 exact flow, 1 delta rule (alpha = beta)
+  int seg;             // dense batches only: > 1 splits every sequence into seg segments of
+  int seg_nc;          // seg_nc chunks (the last one shorter); sequence index = b * seg + j
 };
 
 struct SeqInfo {
@@ -558,6 +560,11 @@ EFLA_DEV SeqInfo seq_info(const Geom& g, int s) {
     const int bos = clamp_t(g, g.cu[s]);
     const int end = max(clamp_t(g, g.cu[s + 1]), bos);
     return SeqInfo{0, bos, end - bos, g.table[s]};
+  }
+  if (g.seg > 1) {
+    const int b = s / g.seg, j = s - b * g.seg;
+    const int bos = min(j * g.seg_nc * kChunk, g.T);
+    return SeqInfo{b, bos, min(g.seg_nc * kChunk, g.T - bos), b * g.ntc + j * g.seg_nc};
   }
   return SeqInfo{s, 0, g.T, s * g.ntc};
 }

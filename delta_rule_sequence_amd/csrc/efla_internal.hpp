@@ -21,6 +21,10 @@ struct Shape {
   int ntc;         // ceil(T/64) (dense)
   int64_t slots;   // chunk slots per head (upper bound for packed batches)
   bool euler;      // step rule: delta rule (alpha = beta) instead of the exact flow
+  int seg_plan;    // dense batches: segments per sequence of the forward scan (1 = none)
+  int seg_plan_nc; // chunks per segment when seg_plan > 1
+  int seg;         // segment view handed to a scan launch (1 = whole sequences): n_seqs is
+  int seg_nc;      // then B * seg and sequence s is segment s % seg of batch row s / seg
 };
 
 // Optional per-kernel timing (efla_profile_enable): events recorded on the launch stream
@@ -40,6 +44,15 @@ hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const 
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
                            void* states, const float* h0, float* ht, hipStream_t st);
+// Transition of each sequence of a segment view: P = prod over its chunks of
+// (I - K^T W), as fp32 [n_seqs][H][dk][dk] (the scan with U = 0 from S = I).
+hipError_t launch_scan_fwd_transition(const Shape& s, const void* k, const void* w, float* p,
+                                      hipStream_t st);
+// Chain the segments of every sequence: S_0 = h0 (zero if null), S_{j+1} = P_j S_j + R_j;
+// writes S_j of every segment to sin ([B * seg_plan][H][dk][dv]) and the final state to ht
+// (if not null). P, R as produced by the transition and state-only scans of segment_view(s).
+hipError_t launch_seg_combine(const Shape& s, const float* p, const float* r, const float* h0,
+                              float* sin, float* ht, hipStream_t st);
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
                            void* dstates, const float* dht, float* dh0, hipStream_t st);
@@ -69,7 +82,18 @@ inline Geom make_geom(const Shape& s, const int* table) {
   g.max_slots = (int)s.slots;
   g.scale = s.scale;
   g.euler = s.euler ? 1 : 0;
+  g.seg = s.seg;
+  g.seg_nc = s.seg_nc;
   return g;
+}
+
+// The same problem seen by a scan launch as B * seg_plan independent segments.
+inline Shape segment_view(const Shape& s) {
+  Shape v = s;
+  v.seg = s.seg_plan;
+  v.seg_nc = s.seg_plan_nc;
+  v.n_seqs = s.B * s.seg_plan;
+  return v;
 }
 
 // Compute units of the current device (cached per device; 256 if the query fails).

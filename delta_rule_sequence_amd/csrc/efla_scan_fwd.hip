@@ -41,7 +41,10 @@ struct ScanFwdLds {
 
 // WO: write O (also needs Q and M); WSV: write U~ and the chunk states (saved for the
 // backward pass). Compile-time, so the inner loops carry no branches on them.
-template <typename E, int DK, int DV, int NWC, bool WO, bool WSV>
+// PM: transition mode for the segment-parallel scan. The chunk step is affine in the state,
+// S <- (I - K^T W) S + K^T U, so running it with U = 0 from S = I (DV = DK) leaves in ht the
+// product of the (I - K^T W) over the sequence; U is neither read nor needed.
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM>
 __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t o_ = hoff + (int64_t)(16 * b + g4 + i) * DV;
-          ht[o_] = h0 ? h0[o_] : 0.f;
+          if constexpr (PM) ht[o_] = 16 * b + g4 + i == v0 + cw + cl ? 1.f : 0.f;
+          else ht[o_] = h0 ? h0[o_] : 0.f;
         }
     }
     return;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     const int n = rows_of(c);
     const int64_t r0 = base + (int64_t)c * kChunk;
     dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
-    dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
+    if constexpr (!PM) dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
     dma_tile<E, DK, NWL>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
     if constexpr (WO) {
       dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
@@ -136,7 +140,12 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   f32x4 Sacc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) Sacc[b] = zero4();
-  if (h0 && !loader) {  // state entering the sequence
+  if constexpr (PM) {  // S = I (this wave's columns)
+#pragma unroll
+    for (int b = 0; b < NBK; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sacc[b][i] = 16 * b + g4 + i == v0 + cw + cl ? 1.f : 0.f;
+  } else if (h0 && !loader) {  // state entering the sequence
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -158,7 +167,8 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
         if constexpr (WO) aq[rb][ks] = aop_rm<E, DK>(st + L::oQ, 16 * rb, ks, lane);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) uv[rb][i] = *(const E*)(st + L::oU + SU::off(16 * rb + g4 + i, cw + cl));
+      for (int i = 0; i < 4; ++i)
+        uv[rb][i] = PM ? to_e<E>(0.f) : *(const E*)(st + L::oU + SU::off(16 * rb + g4 + i, cw + cl));
     }
     V sb[KSK];
 #pragma unroll
@@ -254,14 +264,14 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   }
 }
 
-template <typename E, int DK, int DV, int NWC, bool WO, bool WSV>
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM = false>
 static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* u, const void* m, void* o, void* ut,
                                void* states, const float* h0, float* ht, hipStream_t st) {
   typedef ScanFwdLds<E, DK, DV, NWC> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC, WO, WSV>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -269,15 +279,16 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
   const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / L::TV);
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
-  hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM>), dim3((unsigned)blocks),
                      dim3(128 * NWC), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
                      (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht);
   hipError_t e = hipGetLastError();
-  prof_end("scan_fwd", st);
+  prof_end(PM ? "scan_fwd_transition" : WO || WSV ? "scan_fwd" : "scan_fwd_state", st);
   return e;
 }
 
-// Outputs: O alone, O with U~ and the chunk states, or U~ and the states alone (recompute).
+// Outputs: O alone, O with U~ and the chunk states, U~ and the states alone (recompute), or
+// only the final states (first pass of the segment-parallel scan).
 template <typename E, int DK, int DV, int NWC>
 static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* u, const void* m, void* o, void* ut,
@@ -288,6 +299,8 @@ static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, c
   if (o) return scan_fwd_run<E, DK, DV, NWC, true, false>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
   if (wsv)
     return scan_fwd_run<E, DK, DV, NWC, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
+  if (ht)
+    return scan_fwd_run<E, DK, DV, NWC, false, false>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
   return hipSuccess;
 }
 
@@ -318,6 +331,20 @@ hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, cons
   }
   EFLA_SF(float, 64, 64, 1);
 #undef EFLA_SF
+}
+
+hipError_t launch_scan_fwd_transition(const Shape& s, const void* k, const void* w, float* p,
+                                      hipStream_t st) {
+#define EFLA_ST(E_, DK_, NWC_)                                                               \
+  return scan_fwd_run<E_, DK_, DK_, NWC_, false, false, true>(s, nullptr, nullptr, k, w, nullptr, \
+                                                             nullptr, nullptr, nullptr, nullptr, \
+                                                             nullptr, p, st)
+  if (s.dt == Dt::BF16) {
+    if (s.dk == 64) EFLA_ST(__bf16, 64, 2);
+    EFLA_ST(__bf16, 128, 2);
+  }
+  EFLA_ST(float, 64, 1);
+#undef EFLA_ST
 }
 
 }  // namespace efla

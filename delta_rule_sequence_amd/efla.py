@@ -43,9 +43,10 @@ def _mode(mode):
     return _lib.MODES[mode]
 
 
-def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None, mode="exact"):
+def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None, mode="exact", segments=0):
     """Build the efla_problem for tensors q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T].
-    mode "exact" (the exact flow) or "euler" (the delta rule, alpha = beta)."""
+    mode "exact" (the exact flow) or "euler" (the delta rule, alpha = beta). segments: forward
+    scan split of long sequences (0 = library's choice, 1 = none, n = at most n segments)."""
     if k.dim() != 4 or v.dim() != 4:
         raise ValueError("k and v must be [B, H, T, d]")
     B, H, T, dk = k.shape
@@ -60,8 +61,10 @@ def make_problem(q, k, v, beta, scale=1.0, cu_seqlens=None, mode="exact"):
         _need(cu_seqlens, "cu_seqlens", torch.int32)
         n_seqs = cu_seqlens.numel() - 1
         cu_ptr = cu_seqlens.data_ptr()
+    if int(segments) < 0:
+        raise ValueError("segments must be >= 0")
     return _lib.problem(B, H, T, dk, dv, _DT[k.dtype], float(scale), cu_ptr, n_seqs,
-                        mode=_mode(mode))
+                        mode=_mode(mode), segments=int(segments))
 
 
 def efla_workspace_bytes(p, for_backward: bool) -> int:
@@ -127,12 +130,13 @@ def _state_tensor(t, name, p, device):
 
 
 def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=None, saved=None,
-             mode="exact", initial_state=None, final_state=None):
+             mode="exact", initial_state=None, final_state=None, segments=0):
     """Forward. Returns (o, saved) where saved is the uint8 buffer for efla_bwd (or None).
     o, saved and ws may be passed in preallocated. initial_state: fp32 [n_state, H, dk, dv] or
     None (zero). final_state: True (allocate) or a preallocated fp32 tensor of that shape to
-    receive the state after each sequence; then (o, saved, final_state) is returned."""
-    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode)
+    receive the state after each sequence; then (o, saved, final_state) is returned.
+    segments: see make_problem."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode, segments)
     if o is None:
         o = torch.empty_like(v)
     else:
@@ -157,12 +161,14 @@ def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=No
 
 
 def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None, grads=None,
-             mode="exact", initial_state=None, d_final_state=None, d_initial_state=False):
+             mode="exact", initial_state=None, d_final_state=None, d_initial_state=False,
+             segments=0):
     """Backward of sum(o * d_o) (+ <final_state, d_final_state>): (dq, dk, dv, dbeta) in the
     input dtype. grads may be a preallocated (dq, dk, dv, dbeta) tuple. initial_state is the
     one the forward used (read only when saved is None). With d_initial_state True (or a
-    preallocated fp32 tensor) the gradient at the initial states is returned as a fifth item."""
-    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode)
+    preallocated fp32 tensor) the gradient at the initial states is returned as a fifth item.
+    segments applies to the forward recomputed when saved is None (see make_problem)."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode, segments)
     _need(d_o, "d_o", v.dtype, v.shape)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 4
+#define EFLA_ABI_VERSION 5
 
 typedef enum {
   EFLA_OK = 0,
@@ -73,6 +73,11 @@ typedef struct {
   const int32_t* cu_seqlens;    /* device pointer or NULL (see packed batches above) */
   int32_t n_seqs;               /* number of packed sequences when cu_seqlens is set */
   int32_t mode;                 /* efla_mode; other values return EFLA_ERR_UNSUPPORTED */
+  int32_t segments;             /* forward scan of long sequences, dense batches only (packed
+                                   batches always use 1): 0 = chosen by the library, 1 = one
+                                   sequential chain of chunks per sequence, n >= 2 = split each
+                                   sequence into at most n segments scanned in parallel
+                                   (segment-parallel scan, see efla_fwd); < 0 = EFLA_ERR_SHAPE */
 } efla_problem;
 
 /* Byte offsets of the tensors inside the buffer that efla_fwd saves for efla_bwd.
@@ -128,7 +133,16 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
                           void* w, void* u, void* ws, size_t ws_bytes, void* stream);
 
 /* Forward: o [B,H,T,dv] (problem dtype). `saved` (NULL, or efla_saved_bytes(p) bytes)
- * receives W, U~, the chunk states, M and X for efla_bwd. ws: efla_workspace_bytes(p, 0). */
+ * receives W, U~, the chunk states, M and X for efla_bwd. ws: efla_workspace_bytes(p, 0).
+ * Segment-parallel scan (summary page, section 3.3: from chunk to chunk the state follows an
+ * affine map, S <- (I - K^T W) S + K^T U, so the maps of consecutive chunks compose): when
+ * the plan splits sequences into G > 1 segments, every segment's composed transition P and
+ * zero-start state R are formed in parallel, a short sequential pass chains them
+ * (S_in of segment j+1 = P_j S_in_j + R_j, fp32), and the output scan runs over all segments
+ * at once from those states. Same results up to rounding; the workspace grows by
+ * 4 B G H dk (2 dv + dk) bytes.
+ * The library's choice (segments = 0) splits only when B * H * dv / 32 < 128 and a
+ * sequence has at least 32 chunks, aiming at about 512 scan workgroups. */
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
                      const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
                      size_t ws_bytes, void* stream);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 4
+    assert L.efla_abi_version() == 5
 
 
 def test_status_strings(L):
@@ -47,7 +47,7 @@ def _p(**kw):
     base.update(kw)
     return _lib.problem(base["B"], base["H"], base["T"], base["dk"], base["dv"], base["dtype"],
                         base.get("scale", 1.0), base.get("cu", None), base.get("n_seqs", 0),
-                        base.get("chunk", 64), base.get("mode", 0))
+                        base.get("chunk", 64), base.get("mode", 0), base.get("segments", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -71,6 +71,10 @@ def _p(**kw):
     (dict(mode=1), 0),
     (dict(mode=2), 4),
     (dict(mode=-1), 4),
+    (dict(segments=1), 0),
+    (dict(segments=64), 0),
+    (dict(segments=-1), 2),
+    (dict(B=1, cu=0x1000, n_seqs=3, segments=4), 0),   # packed: accepted, scan not split
 ])
 def test_problem_validation(L, kw, code):
     p = _p(**kw)
@@ -157,3 +161,27 @@ def test_profile_api_without_launches(L):
     counts = (ctypes.c_int64 * 4)()
     ms = (ctypes.c_double * 4)()
     assert L.efla_profile_read(names, 64, counts, ms, 4) == 0
+
+
+def test_segment_plan_workspace(L):
+    """The segment-parallel forward needs R and S_in (fp32 [B*G][H][dk][dv]) and P (fp32
+    [B*G][H][dk][dk]) on top of the sequential-scan workspace; G follows the plan."""
+    def extra(**kw):
+        return (L.efla_workspace_bytes(ctypes.byref(_p(**kw)), 0) -
+                L.efla_workspace_bytes(ctypes.byref(_p(**dict(kw, segments=1))), 0))
+    per_seg = 16 * 128 * (2 * 128 + 128) * 4       # H * dk * (2 dv + dk) * 4 bytes
+    # long context, 16 heads: 512 chunks -> the library picks 8 segments
+    assert extra(B=1, T=32768) == 8 * per_seg
+    # a full chip of whole-sequence scans already: no split
+    assert extra() == 0
+    # explicit requests: at most one segment per chunk, no empty segment
+    assert extra(B=1, T=32768, segments=3) == 3 * per_seg
+    assert extra(B=1, T=64 * 10, segments=4) == 4 * per_seg      # 10 chunks -> 3,3,3,1
+    assert extra(B=1, T=64 * 10, segments=7) == 5 * per_seg      # 10 chunks -> 2 each
+    assert extra(B=1, T=64 * 3, segments=50) == 3 * per_seg
+    assert extra(B=1, T=64, segments=8) == 0                     # one chunk: nothing to split
+    assert extra(B=2, T=64 * 40, segments=4) == 2 * 4 * per_seg
+    # the backward's recompute path runs the same forward
+    p, p1 = _p(B=1, T=32768), _p(B=1, T=32768, segments=1)
+    assert (L.efla_workspace_bytes(ctypes.byref(p), 1) -
+            L.efla_workspace_bytes(ctypes.byref(p1), 1)) == 8 * per_seg
