@@ -460,6 +460,53 @@ EFLA_DEV typename Mma<E>::vec aop_rm(const unsigned char* t, int m0, int ks, int
   }
 }
 
+// Contiguous-contraction order. bop_acc hands lane group g of a bf16 B operand the rows
+// 4 g + i of accumulator tiles 2 ks and 2 ks + 1, so its A operand needs columns
+// 32 ks + 4 g.. and 32 ks + 16 + 4 g.. (two 8-byte LDS reads, which the compiler pairs into
+// the slow ds_read2 forms). Numbering the accumulator rows instead so that tile b, MFMA row
+// r stands for row prow(b, r) of the matrix (tiles 2j and 2j + 1 of each 32-row block
+// interleave in runs of four) gives every lane group 8 consecutive rows, 32 ks + 8 g.., and
+// the matching A operand is one 16-byte read. The numbering is chosen by the rows the
+// producing product's A operand is fed in (aop_rc / aop_kc below), so it costs nothing; only
+// the code that moves accumulator entries to or from memory must use prow. fp32 operands
+// (KC = 16) are contiguous already.
+template <typename E> EFLA_DEV constexpr int prow(int b, int r) {
+  if constexpr (sizeof(E) == 2) return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3);
+  else return 16 * b + r;
+}
+
+// A operand, row-major in a swizzled tile, for a product whose B operand is bop_acc of
+// prow-ordered accumulators and whose result is prow-ordered: output tile rb takes rows
+// prow(rb, lane & 15), contraction slots ks.
+template <typename E, int COLS>
+EFLA_DEV typename Mma<E>::vec aop_rc(const unsigned char* t, int rb, int ks, int lane) {
+  typedef Swz<E, COLS> S;
+  const int r = prow<E>(rb, lane & 15), g = lane >> 4;
+  if constexpr (sizeof(E) == 2) return *(const bf16x8*)(t + S::off(r, 32 * ks + 8 * g));
+  else return *(const f32x4*)(t + S::off(r, 16 * ks + 4 * g));
+}
+
+// The same with the contraction index along the tile's rows (k-major, LDS transpose reads
+// for bf16): output tile b takes columns prow(b, lane & 15).
+template <typename E, int COLS>
+EFLA_DEV typename Mma<E>::vec aop_kc(const unsigned char* t, int b, int ks, int lane) {
+  typedef Swz<E, COLS> S;
+  const int i = lane & 15, g = lane >> 4;
+  if constexpr (sizeof(E) == 2) {
+    // transpose read: output lane j, slot s gets element j % 4 of the 8-byte row that lane
+    // 4 s + j / 4 addresses; lane i addresses row 32 ks + 8 g + i / 4 (then + 4) at column
+    // prow(b, 4 (i & 3)), so lane j receives column prow(b, j) of rows 32 ks + 8 g + s.
+    const int r = 32 * ks + 8 * g + (i >> 2), c = prow<E>(b, 4 * (i & 3));
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + S::off(r, c)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + S::off(r + 4, c)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const int r = 16 * ks + 4 * g, c = 16 * b + i;
+    return f32x4{*(const float*)(t + S::off(r, c)), *(const float*)(t + S::off(r + 1, c)),
+                 *(const float*)(t + S::off(r + 2, c)), *(const float*)(t + S::off(r + 3, c))};
+  }
+}
+
 template <typename E, int COLS>
 EFLA_DEV typename Mma<E>::vec aop_km(const unsigned char* t, int m0, int ks, int lane) {
   typedef Swz<E, COLS> S;

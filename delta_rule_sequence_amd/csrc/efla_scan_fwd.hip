@@ -9,9 +9,10 @@
 //
 // Each compute wave owns 16 columns of S for the whole sequence and keeps them in fp32 MFMA
 // accumulators. Products whose contraction runs over the rows of an accumulator take that
-// accumulator directly as their B operand (the contraction slots are ordered to match its
-// layout), so the recurrence S -> W S -> U~ -> K^T U~ -> S runs inside one wave's registers
-// with no LDS round trip. Separate loader waves move the data: they fill swizzled LDS tiles
+// accumulator directly as their B operand, so the recurrence S -> W S -> U~ -> K^T U~ -> S
+// runs inside one wave's registers with no LDS round trip. Accumulator rows (of S, and the
+// token rows of U~ and O) are numbered in the contiguous-contraction order (prow), so every
+// A operand from LDS is a single 16-byte read. Separate loader waves move the data: they fill swizzled LDS tiles
 // of W, Q, K, M and U one chunk ahead by LDS DMA (double-buffered) and copy the staged O,
 // U~ and chunk states out as 16-byte rows, so the compute waves never stall on memory
 // issue. One barrier per chunk hands the buffers over.
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
       for (int b = 0; b < NBK; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t o_ = hoff + (int64_t)(16 * b + g4 + i) * DV;
-          if constexpr (PM) ht[o_] = 16 * b + g4 + i == v0 + cw + cl ? 1.f : 0.f;
+          const int64_t o_ = hoff + (int64_t)prow<E>(b, g4 + i) * DV;
+          if constexpr (PM) ht[o_] = prow<E>(b, g4 + i) == v0 + cw + cl ? 1.f : 0.f;
           else ht[o_] = h0 ? h0[o_] : 0.f;
         }
     }
@@ -144,12 +145,12 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sacc[b][i] = 16 * b + g4 + i == v0 + cw + cl ? 1.f : 0.f;
+      for (int i = 0; i < 4; ++i) Sacc[b][i] = prow<E>(b, g4 + i) == v0 + cw + cl ? 1.f : 0.f;
   } else if (h0 && !loader) {  // state entering the sequence
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sacc[b][i] = h0[hoff + (int64_t)(16 * b + g4 + i) * DV];
+      for (int i = 0; i < 4; ++i) Sacc[b][i] = h0[hoff + (int64_t)prow<E>(b, g4 + i) * DV];
   }
   auto compute = [&](int c) {
     const unsigned char* st = smem + (c & 1) * L::stage;
@@ -163,12 +164,12 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
-        aw[rb][ks] = aop_rm<E, DK>(st + L::oW, 16 * rb, ks, lane);
-        if constexpr (WO) aq[rb][ks] = aop_rm<E, DK>(st + L::oQ, 16 * rb, ks, lane);
+        aw[rb][ks] = aop_rc<E, DK>(st + L::oW, rb, ks, lane);
+        if constexpr (WO) aq[rb][ks] = aop_rc<E, DK>(st + L::oQ, rb, ks, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        uv[rb][i] = PM ? to_e<E>(0.f) : *(const E*)(st + L::oU + SU::off(16 * rb + g4 + i, cw + cl));
+        uv[rb][i] = PM ? to_e<E>(0.f) : *(const E*)(st + L::oU + SU::off(prow<E>(rb, g4 + i), cw + cl));
     }
     V sb[KSK];
 #pragma unroll
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
       for (int b = 0; b < NBK; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *(E*)(stg + L::gS + SU::off(16 * b + g4 + i, cw + cl)) = to_e<E>(Sacc[b][i]);
+          *(E*)(stg + L::gS + SU::off(prow<E>(b, g4 + i), cw + cl)) = to_e<E>(Sacc[b][i]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -198,13 +199,13 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) ak[b][ks] = aop_km<E, DK>(st + L::oK, 16 * b, ks, lane);
+      for (int ks = 0; ks < KST; ++ks) ak[b][ks] = aop_kc<E, DK>(st + L::oK, b, ks, lane);
     if constexpr (WO) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int ks = 0; ks < KST; ++ks)
-          if (KC * ks <= 16 * rb + 15) am[rb][ks] = aop_rm<E, 64>(st + L::oM, 16 * rb, ks, lane);
+          if (KC * ks <= 16 * rb + 15) am[rb][ks] = aop_rc<E, 64>(st + L::oM, rb, ks, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        uta[rb][i] = 16 * rb + g4 + i < n ? to_f(uv[rb][i]) - ws[rb][i] : 0.f;
+        uta[rb][i] = prow<E>(rb, g4 + i) < n ? to_f(uv[rb][i]) - ws[rb][i] : 0.f;
     V ub[KST];
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) ub[ks] = bop_acc<E>(uta, ks);
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
           if (KC * ks <= 16 * rb + 15) oa[rb] = Mma<E>::step(am[rb][ks], ub[ks], oa[rb]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *(E*)(stg + L::gO + SU::off(16 * rb + g4 + i, cw + cl)) = to_e<E>(g.scale * oa[rb][i]);
+          *(E*)(stg + L::gO + SU::off(prow<E>(rb, g4 + i), cw + cl)) = to_e<E>(g.scale * oa[rb][i]);
       }
     }
     if constexpr (WSV) {
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *(E*)(stg + L::gUt + SU::off(16 * rb + g4 + i, cw + cl)) = to_e<E>(uta[rb][i]);
+          *(E*)(stg + L::gUt + SU::off(prow<E>(rb, g4 + i), cw + cl)) = to_e<E>(uta[rb][i]);
     }
   };
 
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ht[hoff + (int64_t)(16 * b + g4 + i) * DV] = Sacc[b][i];
+      for (int i = 0; i < 4; ++i) ht[hoff + (int64_t)prow<E>(b, g4 + i) * DV] = Sacc[b][i];
   }
 }
 

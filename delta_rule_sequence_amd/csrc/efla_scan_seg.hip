@@ -41,9 +41,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int col = 16 * wi + (lane & 15), g4 = 4 * (lane >> 4);
-  // this lane's entries of a state slice: rows 16 bb + g4 + i, column col
+  // this lane's entries of a state slice: rows prow(bb, g4 + i), column col
   auto at = [&](const float* base, int64_t seq, int bb, int i) {
-    return base + ((seq * H + h) * DK + 16 * bb + g4 + i) * (int64_t)DV + col;
+    return base + ((seq * H + h) * DK + prow<E>(bb, g4 + i)) * (int64_t)DV + col;
   };
   auto stage = [&](int j) {  // P_j (fp32) -> LDS buffer j & 1 in the problem dtype
     unsigned char* dst = smem + (j & 1) * L::TILE;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
 #pragma unroll
     for (int rb = 0; rb < NBK; ++rb)
 #pragma unroll
-      for (int ks = 0; ks < KSK; ++ks) acc[rb] = Mma<E>::step(aop_rm<E, DK>(pt, 16 * rb, ks, lane), sb[ks], acc[rb]);
+      for (int ks = 0; ks < KSK; ++ks) acc[rb] = Mma<E>::step(aop_rc<E, DK>(pt, rb, ks, lane), sb[ks], acc[rb]);
 #pragma unroll
     for (int bb = 0; bb < NBK; ++bb) S[bb] = acc[bb];
     __syncthreads();  // P_{j+1} staged for every wave; buffer j & 1 free for P_{j+2}
