@@ -690,30 +690,28 @@ EFLA_DEV void scan_block(int bid, int nsh, int ntile, int& sh, int& tile) {
 // ---------------------------------------------------------------------------
 // X = (I + A)^{-1} for a strictly lower triangular 64x64 fp32 A (LDS, pitch kPitchF).
 // Blocked forward substitution over 16x16 blocks:
-//   diagonal blocks X_ii = (I + A_ii)^{-1} by column substitution (16 lanes of wave i),
+//   diagonal blocks X_ii = (I + A_ii)^{-1} by column substitution (16 lanes of wave i; each
+//   solved row at once updates every later row, so the FMAs form short independent chains),
 //   then wave j fills block column j downwards, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
 //   with fp32 MFMA: an accumulator tile has exactly the layout of a B operand, so the
 //   X_kj already computed stay in registers and feed the next products.
-// All 256 threads must call it; X is complete in LDS (upper blocks zero) on return.
+// All 256 threads must call it. On return the diagonal and lower 16x16 blocks of X are in
+// LDS; the blocks above the diagonal are NOT written (they are zero by definition and the
+// caller masks them when it reads whole rows).
 // ---------------------------------------------------------------------------
 EFLA_DEV void invert_unit_lower64(const float* sA, float* sX, int tid) {
   constexpr int ld = kPitchF;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = tid; i < 64 * 64; i += kThreads) {
-    const int r = i >> 6, c = i & 63;
-    if ((c >> 4) > (r >> 4)) sX[r * ld + c] = 0.f;
-  }
   if (lane < 16) {
     const int o = wv * 16;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = (r == lane) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s = fmaf(-sA[(o + r) * ld + o + m], x[m], s);
-      x[r] = s;
-    }
+    for (int m = 0; m < 15; ++m)
+#pragma unroll
+      for (int r = m + 1; r < 16; ++r) x[r] = fmaf(-sA[(o + r) * ld + o + m], x[m], x[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sX[(o + r) * ld + o + lane] = x[r];
   }

@@ -169,8 +169,11 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       for (int it = 0; it < 2; ++it) {  // 8 consecutive elements of one row per thread
         const int i = it * kThreads + tid;
         const int r = i >> 3, c = (i & 7) * 8;
-        const f32x4 x0 = *(const f32x4*)(sX + r * L::LF + c);
-        const f32x4 x1 = *(const f32x4*)(sX + r * L::LF + c + 4);
+        // blocks above the diagonal are zero (the inverse leaves them unwritten)
+        const bool up = (c >> 4) > (r >> 4);
+        f32x4 x0 = *(const f32x4*)(sX + r * L::LF + c);
+        f32x4 x1 = *(const f32x4*)(sX + r * L::LF + c + 4);
+        if (up) x0 = x1 = zero4();
         const f32x4 a0 = *(const f32x4*)(sAl + c), a1 = *(const f32x4*)(sAl + c + 4);
         if constexpr (sizeof(E) == 2) {
           bf16x8 xe, te;
