@@ -126,30 +126,38 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     const ChunkUnit nxt = chunk_unit(g, more ? unx : un);
     if (more) issue_k(nxt);
 
-    // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T); wave wv owns row block wv.
+    // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T), lower blocks only (the
+    // inverse never reads A above the diagonal). Wave wv takes A's row block 3 - wv and M's
+    // row block wv: five block products each. Both are formed transposed (operands swapped),
+    // so a lane holds four consecutive columns of one row and stores them at once.
+    {
+      const int ra = 3 - wv, rowa = 16 * ra + (lane & 15), c4 = 4 * (lane >> 4);
+      const float ala = sAl[rowa];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      f32x4 acc = zero4();
-      if (nb <= wv) acc = mma<E, false, false>(sK + rA * L::LK, L::LK, sK + 16 * nb * L::LK, L::LK, 0, DK, acc, lane);
-      const int col = 16 * nb + (lane & 15);
+      for (int nb = 0; nb < 4; ++nb) {
+        if (nb > ra) continue;
+        f32x4 acc = mma<E, false, false>(sK + 16 * nb * L::LK, L::LK, sK + 16 * ra * L::LK, L::LK, 0, DK, zero4(), lane);
+        f32x4 av;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rA + 4 * (lane >> 4) + i;
-        sA[row * L::LF + col] = row > col ? sAl[row] * acc[i] : 0.f;
+        for (int i = 0; i < 4; ++i) av[i] = rowa > 16 * nb + c4 + i ? ala * acc[i] : 0.f;
+        *(f32x4*)(sA + rowa * L::LF + 16 * nb + c4) = av;
       }
-      if (mout) {
+    }
+    if (mout) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
         f32x4 m = zero4();
         if (nb <= wv) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            m = Mma<E>::step(qA[ks], frag_rm<E>(sK + 16 * nb * L::LK + ks * KC, L::LK, lane), m);
-          if (nb == wv) {
+            m = Mma<E>::step(frag_rm<E>(sK + 16 * nb * L::LK + ks * KC, L::LK, lane), qA[ks], m);
+          if (nb == wv) {  // keep columns <= row
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if ((lane & 15) > 4 * (lane >> 4) + i) m[i] = 0.f;
+              if (4 * (lane >> 4) + i > (lane & 15)) m[i] = 0.f;
           }
         }
-        st_frag_lds<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
+        st_frag_t<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
       }
     }
     __syncthreads();
@@ -198,20 +206,37 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     }
     __syncthreads();
 
-    // W = T K, U = T V; T is lower triangular, so row block wv needs columns < 16 (wv + 1).
-    const int k1 = round_up_kc<E>(16 * (wv + 1));
-    f32x4 Wf[DK / 16], Uf[DV / 16];
+    // W = T K, U = T V. Wave wv owns a quarter of the columns of each over all four row
+    // blocks (equal work per wave); T is lower triangular, so row blocks 0-1 need columns
+    // < 32 and row blocks 2-3 all 64. Formed transposed for row-layout stores.
+    constexpr int CW = DK / 64, CU = DV / 64;  // 16-column tiles per wave
+    f32x4 Wf[4][CW], Uf[4][CU];
+    {
+      f32x4 (&w01)[2][CW] = *reinterpret_cast<f32x4(*)[2][CW]>(&Wf[0]);
+      f32x4 (&w23)[2][CW] = *reinterpret_cast<f32x4(*)[2][CW]>(&Wf[2]);
+      f32x4 (&u01)[2][CU] = *reinterpret_cast<f32x4(*)[2][CU]>(&Uf[0]);
+      f32x4 (&u23)[2][CU] = *reinterpret_cast<f32x4(*)[2][CU]>(&Uf[2]);
 #pragma unroll
-    for (int nb = 0; nb < DK / 16; ++nb)
-      Wf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sK + 16 * nb, L::LK, 0, k1, zero4(), lane);
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int nb = 0; nb < DV / 16; ++nb)
-      Uf[nb] = mma<E, false, true>(sT + rA * L::LT, L::LT, sV + 16 * nb, L::LV, 0, k1, zero4(), lane);
+        for (int j = 0; j < CW; ++j) Wf[i][j] = zero4();
+#pragma unroll
+        for (int j = 0; j < CU; ++j) Uf[i][j] = zero4();
+      }
+      const int k01 = round_up_kc<E>(32);
+      mma_blk<E, false, true, 2, CW, kChunk, true>(sT, L::LT, sK + 16 * CW * wv, L::LK, 0, k01, w01, lane);
+      mma_blk<E, false, true, 2, CW, kChunk, true>(sT + 32 * L::LT, L::LT, sK + 16 * CW * wv, L::LK, 0, kChunk, w23, lane);
+      mma_blk<E, false, true, 2, CU, kChunk, true>(sT, L::LT, sV + 16 * CU * wv, L::LV, 0, k01, u01, lane);
+      mma_blk<E, false, true, 2, CU, kChunk, true>(sT + 32 * L::LT, L::LT, sV + 16 * CU * wv, L::LV, 0, kChunk, u23, lane);
+    }
     __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < DK / 16; ++nb) st_frag_lds<E>(sK + rA * L::LK + 16 * nb, L::LK, Wf[nb], lane);
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int nb = 0; nb < DV / 16; ++nb) st_frag_lds<E>(sV + rA * L::LV + 16 * nb, L::LV, Uf[nb], lane);
+      for (int j = 0; j < CW; ++j) st_frag_t<E>(sK + 16 * i * L::LK + 16 * (CW * wv + j), L::LK, Wf[i][j], lane);
+#pragma unroll
+      for (int j = 0; j < CU; ++j) st_frag_t<E>(sV + 16 * i * L::LV + 16 * (CU * wv + j), L::LV, Uf[i][j], lane);
+    }
     __syncthreads();
     s2g<E, DK>(w + row0 * DK, DK, sK, L::LK, n, tid);
     s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
