@@ -134,12 +134,48 @@ def cpu_baseline():
                       "4096 tokens), fp64 numpy token recurrence fwd+bwd, %.1f s wall" % wall}
 
 
+def long_context(E, make_inputs, workload, warmup, iters):
+    """Forward of the B=1, H=16, T=32768, d=128 bf16 workload: segment-parallel scan (segments
+    chosen by the library) and a single sequential chain per sequence, same buffers."""
+    import torch
+    w = workload(3)
+    inp = make_inputs(w, with_grad=False)
+    q, k, v, beta = (torch.from_numpy(inp[n]).to("cuda", torch.bfloat16)
+                     for n in ("q", "k", "v", "beta"))
+    o = torch.empty_like(v)
+    res = {"workload": "efla_fwd_B1_H16_T32768_d128_bf16"}
+    lay = None
+    for segs, key in ((0, "segmented"), (1, "sequential")):
+        p = E.make_problem(q, k, v, beta, segments=segs)
+        ws = torch.empty(E.efla_workspace_bytes(p, False), dtype=torch.uint8, device="cuda")
+        f = lambda: E.efla_fwd(q, k, v, beta, 1.0, None, False, ws, o=o, segments=segs)
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            f()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / iters
+        res[key] = {"ms_fwd": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1)}
+        if segs == 0:
+            lay = E.efla_workspace_bytes(p, False) - E.efla_workspace_bytes(
+                E.make_problem(q, k, v, beta, segments=1), False)
+    # segments the library chose: extra workspace / (4 H dk (2 dv + dk)) bytes per segment
+    res["segments"] = int(lay // (4 * w.H * w.dk * (2 * w.dv + w.dk)))
+    res["speedup"] = round(res["sequential"]["ms_fwd"] / res["segmented"]["ms_fwd"], 3)
+    del q, k, v, beta, o
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the B=1, T=32768 forward (e.g. for per-kernel counter runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -240,6 +276,11 @@ def main():
     torch.cuda.synchronize()
     decode_us = (time.perf_counter() - t0) * 1e6 / args.steps
 
+    # Long context (the pages' long-sequence setting, forward only): B=1, H=16, T=32768. The
+    # segment-parallel scan (library's choice of segments) against one sequential chain.
+    long_ctx = None if args.no_long_context else long_context(E, make_inputs, workload, args.warmup,
+                                                                max(5, args.steps // 5))
+
     units = B * H * (T // CHUNK)
     kernels = {}
     for name, (count, total_ms) in prof.items():
@@ -283,6 +324,7 @@ def main():
                        "exact_over_euler_time": round(ms_per_step / euler_ms, 4)},
         "decode": {"us_per_call": round(decode_us, 2), "tokens_per_call": B,
                    "state_MB": round(B * H * dk * dv * 4 / 1e6, 2)},
+        "long_context": long_ctx,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
