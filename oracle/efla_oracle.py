@@ -29,6 +29,15 @@ equation, so the steps below are the plain reading of their statements):
 
 The state starts at zero (or at a given initial state) for every sequence;
 packed batches restart the state at every cu_seqlens offset.
+
+Gated EFLA (section 3.4 names it; Appendix E/F apply the exact flow to Gated DeltaNet with an
+integrating factor; no formula is printed). Reading taken: a per-token log-decay a_t <= 0
+enters the dynamics matrix as a multiple of the identity over the step interval,
+dS/dtau = -(gamma_t I + k_t k_t^T) S + k_t v_t^T, tau in [0, beta_t], gamma_t beta_t = -a_t.
+The identity part commutes with the rank-1 part, so the exact flow is
+  S_t = g_t (I - alpha_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,
+  g_t = e^{a_t},  alpha_t = beta_t phi(beta_t lambda_t),  b_t = beta_t phi(beta_t lambda_t - a_t)
+(the input integral int_0^beta e^{-(gamma + lambda) s} ds k v^T). a = 0 is EFLA.
 """
 from __future__ import annotations
 
@@ -325,6 +334,82 @@ def euler_forward(q, k, v, beta, scale=1.0, cu_seqlens=None):
             S = S + beta[b, :, t, None, None] * kt[:, :, None] * r[:, None, :]
             o[b, :, t] = scale * np.einsum("hd,hdv->hv", q[b, :, t], S)
     return o
+
+
+# ---------------------------------------------------------------------------
+# Gated EFLA (reading in the module docstring).
+# ---------------------------------------------------------------------------
+
+def gated_coefficients(k, beta, gate):
+    """lambda, alpha = beta phi(beta lambda), g = e^a, b = beta phi(beta lambda - a) per token.
+    k: [..., d_k]; beta, gate (log-decay a): [...]."""
+    k, beta, gate = _f64(k), _f64(beta), _f64(gate)
+    lam = np.sum(k * k, axis=-1)
+    x = beta * lam
+    return dict(lam=lam, alpha=beta * phi(x), g=np.exp(gate), b=beta * phi(x - gate))
+
+
+def gated_forward(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, initial_state=None):
+    """Gated EFLA forward, token by token. gate: log-decay a_t [B,H,T] (a_t <= 0 is a decay).
+
+    Returns (o [B,H,T,dv], final_state [n_seq,H,dk,dv]), fp64."""
+    q, k, v, beta, gate = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(gate)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    c = gated_coefficients(k, beta, gate)
+    o = np.zeros((B, H, T, dv))
+    seqs = sequences(B, T, cu_seqlens)
+    final = np.zeros((len(seqs), H, dk, dv))
+    S0 = _f64(initial_state)
+    for i, (b, s, e) in enumerate(seqs):
+        S = np.zeros((H, dk, dv)) if S0 is None else S0[i].copy()
+        for t in range(s, e):
+            kt = k[b, :, t]
+            kS = np.einsum("hd,hdv->hv", kt, S)                        # k_t^T S_{t-1}
+            S = c["g"][b, :, t, None, None] * (S - c["alpha"][b, :, t, None, None] * kt[:, :, None] * kS[:, None, :]) \
+                + c["b"][b, :, t, None, None] * kt[:, :, None] * v[b, :, t][:, None, :]
+            o[b, :, t] = scale * np.einsum("hd,hdv->hv", q[b, :, t], S)
+        final[i] = S
+    return o, final
+
+
+def gated_chunk_forward(q, k, v, beta, gate, scale=1.0, chunk=CHUNK, initial_state=None):
+    """Chunkwise gated form (dense batches), for tests of the chunk algebra the kernels use.
+
+    Within a chunk with incoming state S, c_t = sum of a over the chunk's tokens up to t,
+    Gamma_t = e^{c_t}; A_ts = alpha_t e^{c_t - c_s} k_t . k_s (s < t); X = (I + A)^{-1};
+    W = X diag(alpha Gamma) K; U = X diag(b) V; U~ = U - W S;
+    O = scale (diag(Gamma) Q S + (tril(Q K^T) * e^{c_t - c_s}) U~);
+    S' = Gamma_C S + K^T diag(e^{c_C - c_t}) U~.
+    Returns dict(o, final, W, U, Ut, cum) with cum the per-token c (restarting at each chunk)."""
+    q, k, v, beta, gate = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(gate)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    co = gated_coefficients(k, beta, gate)
+    o = np.zeros((B, H, T, dv))
+    Wf, Uf, Ut = np.zeros((B, H, T, dk)), np.zeros((B, H, T, dv)), np.zeros((B, H, T, dv))
+    cum = np.zeros((B, H, T))
+    final = np.zeros((B, H, dk, dv))
+    S0 = _f64(initial_state)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else S0[b, h].copy()
+            for c0 in range(0, T, chunk):
+                c1 = min(T, c0 + chunk)
+                K, V, Q = k[b, h, c0:c1], v[b, h, c0:c1], q[b, h, c0:c1]
+                al, bb = co["alpha"][b, h, c0:c1], co["b"][b, h, c0:c1]
+                cc = np.cumsum(gate[b, h, c0:c1])
+                D = np.exp(np.tril(cc[:, None] - cc[None, :]))          # e^{c_t - c_s}, s <= t
+                A = np.tril(al[:, None] * D * (K @ K.T), -1)
+                X = np.linalg.inv(np.eye(c1 - c0) + A)
+                W = X @ ((al * np.exp(cc))[:, None] * K)
+                U = X @ (bb[:, None] * V)
+                U_t = U - W @ S
+                o[b, h, c0:c1] = scale * (np.exp(cc)[:, None] * (Q @ S) + (np.tril(Q @ K.T) * D) @ U_t)
+                S = np.exp(cc[-1]) * S + K.T @ (np.exp(cc[-1] - cc)[:, None] * U_t)
+                Wf[b, h, c0:c1], Uf[b, h, c0:c1], Ut[b, h, c0:c1], cum[b, h, c0:c1] = W, U, U_t, cc
+            final[b, h] = S
+    return dict(o=o, final=final, W=Wf, U=Uf, Ut=Ut, cum=cum)
 
 
 def rel_err(x, ref):

@@ -478,3 +478,101 @@ def test_golden_tiny_case_unchanged():
     assert np.allclose(o, np.array(gold["o"]), rtol=1e-13, atol=1e-14)
     for name in ("dq", "dk", "dv", "dbeta"):
         assert np.allclose(g[name], np.array(gold[name]), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- gated EFLA
+# Reading (oracle docstring): the log-decay a_t adds gamma_t I to the dynamics matrix over the
+# step interval [0, beta_t], gamma_t beta_t = -a_t. The pins integrate that ODE directly.
+
+def _gated_dense(S, k, v, beta, a):
+    """By definition: e^{-beta M} S + int_0^beta e^{-(beta - tau) M} dtau (k v^T), M = gamma I + k k^T."""
+    gamma = -a / beta
+    M = gamma * np.eye(len(k)) + np.outer(k, k)
+    E = scipy.linalg.expm(-beta * M)
+    integral, _ = scipy.integrate.quad_vec(lambda tau: scipy.linalg.expm(-(beta - tau) * M) @ np.outer(k, v),
+                                           0.0, beta, epsabs=1e-15, epsrel=1e-13)
+    return E @ S + integral
+
+
+def _gated_van_loan(S, k, v, beta, a):
+    dk, dv = len(k), len(v)
+    Mb = np.zeros((dk + dv, dk + dv))
+    Mb[:dk, :dk] = -((-a / beta) * np.eye(dk) + np.outer(k, k))
+    Mb[:dk, dk:] = np.outer(k, v)
+    E = scipy.linalg.expm(beta * Mb)
+    return E[:dk, :dk] @ S + E[:dk, dk:]
+
+
+def _gated_one_seq(S0, ks, vs, betas, gates, qs=None, scale=1.0):
+    ks, vs = np.atleast_2d(ks), np.atleast_2d(vs)
+    T = ks.shape[0]
+    qs = np.zeros_like(ks) if qs is None else qs
+    o, SF = O.gated_forward(qs[None, None], ks[None, None], vs[None, None],
+                            np.asarray(betas, dtype=np.float64).reshape(1, 1, T),
+                            np.asarray(gates, dtype=np.float64).reshape(1, 1, T), scale=scale,
+                            initial_state=None if S0 is None else S0[None, None])
+    return o[0, 0], SF[0, 0]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gated_token_update_equals_dense_flow(seed):
+    """One gated token equals expm + quadrature of the decayed ZOH integral (d_k=5, d_v=4)."""
+    r = _rng(100 + seed)
+    S = r.standard_normal((5, 4))
+    k = r.standard_normal(5) * r.uniform(0.3, 2.0)
+    v = r.standard_normal(4)
+    beta, a = r.uniform(0.1, 1.5), -r.uniform(0.01, 2.0)
+    _, S1 = _gated_one_seq(S, k, v, [beta], [a])
+    ref = _gated_dense(S, k, v, beta, a)
+    assert np.max(np.abs(S1 - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_gated_sequence_equals_van_loan_flow():
+    """Ten gated tokens, outputs and states, against the Van Loan block exponential."""
+    r = _rng(120)
+    dk, dv, T = 6, 3, 10
+    ks = r.standard_normal((T, dk)) * r.uniform(0.2, 3.0, (T, 1))
+    vs, qs = r.standard_normal((T, dv)), r.standard_normal((T, dk))
+    betas, gates = r.uniform(0.05, 2.0, T), -r.uniform(0.0, 3.0, T)
+    S0 = r.standard_normal((dk, dv))
+    o, SF = _gated_one_seq(S0, ks, vs, betas, gates, qs, scale=0.6)
+    S = S0
+    for t in range(T):
+        S = _gated_van_loan(S, ks[t], vs[t], betas[t], gates[t])
+        assert np.allclose(o[t], 0.6 * S.T @ qs[t], rtol=1e-12, atol=1e-12)
+    assert np.allclose(SF, S, rtol=1e-12, atol=1e-12)
+
+
+def test_gated_special_cases():
+    """a = 0 is EFLA; k = 0 is pure decay S_t = e^{a_t} S_{t-1}; lambda -> 0 gives the decayed
+    Euler-like input b = beta (1 - e^{a}) / (-a)."""
+    r = _rng(130)
+    B, H, T, dk, dv = 1, 2, 70, 6, 5
+    q, k, v = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dv))
+    beta, a = r.uniform(0, 1, (B, H, T)), -r.uniform(0, 1, (B, H, T))
+    S0 = r.standard_normal((B, H, dk, dv))
+    o_g, f_g = O.gated_forward(q, k, v, beta, np.zeros_like(a), initial_state=S0)
+    o_e, f_e = O.forward(q, k, v, beta, initial_state=S0)
+    assert O.rel_err(o_g, o_e) < 1e-14 and O.rel_err(f_g, f_e) < 1e-14
+    o_z, f_z = O.gated_forward(q, np.zeros_like(k), v, beta, a, initial_state=S0)
+    cum = np.cumsum(a, axis=-1)
+    ref = np.exp(cum)[..., None] * np.einsum("bhtd,bhdv->bhtv", q, S0)
+    assert O.rel_err(o_z, ref) < 1e-13
+    co = O.gated_coefficients(np.full((3, 4), 1e-9), np.array([0.5, 1.0, 2.0]), np.array([-0.3, -1.0, -2.5]))
+    assert np.allclose(co["b"], np.array([0.5, 1.0, 2.0]) * (1 - np.exp([-0.3, -1.0, -2.5])) / np.array([0.3, 1.0, 2.5]), rtol=1e-12)
+
+
+def test_gated_chunk_form_equals_token_recurrence():
+    """The decayed chunk algebra the kernels use (cumulative log-decays inside each chunk) equals
+    the token recurrence, with a ragged tail, a carried initial state and strong decay."""
+    r = _rng(140)
+    B, H, T, dk, dv = 2, 2, 64 * 3 + 17, 8, 6
+    q, k, v = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk)) * 0.6, r.standard_normal((B, H, T, dv))
+    beta, a = r.uniform(0, 1, (B, H, T)), -r.uniform(0, 2.0, (B, H, T))
+    S0 = r.standard_normal((B, H, dk, dv))
+    o, f = O.gated_forward(q, k, v, beta, a, scale=0.9, initial_state=S0)
+    c = O.gated_chunk_forward(q, k, v, beta, a, scale=0.9, initial_state=S0)
+    assert O.rel_err(c["o"], o) < 1e-12 and O.rel_err(c["final"], f) < 1e-12
+    # a wrong decay on the output's state term (Gamma_{t-1} instead of Gamma_t) is caught
+    ob = O.gated_chunk_forward(q, k, v, beta, np.roll(a, 1, axis=-1), scale=0.9, initial_state=S0)
+    assert O.rel_err(ob["o"], o) > 1e-3
