@@ -23,7 +23,8 @@ STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_NULL", 2: "EFLA_ERR_SHAPE", 3: "EFLA_ERR_DT
 # Every symbol include/efla.h declares.
 EXPORTS = ["efla_abi_version", "efla_status_str", "efla_check_problem", "efla_workspace_bytes",
            "efla_saved_bytes", "efla_get_saved_layout", "efla_prep", "efla_chunk_ut",
-           "efla_fwd", "efla_fwd_state", "efla_bwd", "efla_bwd_state", "efla_decode",
+           "efla_fwd", "efla_fwd_state", "efla_fwd_gated", "efla_bwd", "efla_bwd_state",
+           "efla_decode", "efla_decode_gated",
            "efla_profile_enable", "efla_profile_read", "efla_profile_reset"]
 
 
@@ -90,6 +91,10 @@ def lib():
                                  sz, vp]
     L.efla_decode.restype = st
     L.efla_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    L.efla_fwd_gated.restype = st
+    L.efla_fwd_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.efla_decode_gated.restype = st
+    L.efla_decode_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.efla_profile_enable.restype = st
     L.efla_profile_enable.argtypes = [ctypes.c_int]
     L.efla_profile_read.restype = ctypes.c_int

@@ -180,6 +180,8 @@ size_t bytes_seg_p(const Shape& s) {
 size_t bytes_seg(const Shape& s) {
   return 2 * align_up(bytes_seg_state(s)) + align_up(bytes_seg_p(s));
 }
+// Gated forward: running log-decay sums per chunk, fp32 [slots][H][64].
+size_t bytes_cum(const Shape& s) { return (size_t)s.slots * s.H * kChunk * 4; }
 
 // Layout of the forward->backward buffer.
 struct Saved {
@@ -208,7 +210,7 @@ Saved saved_layout(const Shape& s) {
 // the segment-parallel scan's buffers.
 size_t ws_fwd(const Shape& s) {
   return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s)) +
-         align_up(bytes_m(s)) + bytes_seg(s);
+         align_up(bytes_m(s)) + bytes_seg(s) + align_up(bytes_cum(s));
 }
 // Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer, U and
 // the segment buffers for the recompute path.
@@ -225,17 +227,21 @@ bool empty(const Shape& s) { return s.T == 0; }
 
 // Forward stages shared by efla_fwd and the recompute path of efla_bwd. seg: bytes_seg(s)
 // of workspace for the segment-parallel scan (unused when the plan has one segment).
+// gate (null, or log-decays) selects gated EFLA, which then needs cum (bytes_cum(s)).
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                         const void* beta, void* o, unsigned char* w, unsigned char* ut,
                         unsigned char* states, int* table, unsigned char* m, unsigned char* x,
                         unsigned char* u, const float* h0, float* ht, unsigned char* seg,
-                        hipStream_t st) {
+                        hipStream_t st, const void* gate = nullptr, float* cum = nullptr) {
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, w, u, m, x, st))) return r;
+  if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, gate, w, u, m, x,
+                                               gate ? cum : nullptr, st)))
+    return r;
+  const float* cm = gate ? cum : nullptr;
   if (s.seg_plan <= 1)
-    return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, h0, ht, st));
+    return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cm));
   // Segment-parallel: zero-start states R and transitions P of all segments, the sequential
   // chain S_in, then the output scan over all segments from S_in.
   const Shape sv = segment_view(s);
@@ -243,11 +249,11 @@ efla_status run_forward(const Shape& s, const void* q, const void* k, const void
   float* S_in = (float*)(seg + align_up(bytes_seg_state(s)));
   float* P = (float*)(seg + 2 * align_up(bytes_seg_state(s)));
   if (efla_status r = hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, nullptr, nullptr,
-                                                 nullptr, nullptr, R, st)))
+                                                 nullptr, nullptr, R, st, cm)))
     return r;
-  if (efla_status r = hip_status(launch_scan_fwd_transition(sv, k, w, P, st))) return r;
+  if (efla_status r = hip_status(launch_scan_fwd_transition(sv, k, w, P, st, cm))) return r;
   if (efla_status r = hip_status(launch_seg_combine(s, P, R, h0, S_in, ht, st))) return r;
-  return hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, o, ut, states, S_in, nullptr, st));
+  return hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, o, ut, states, S_in, nullptr, st, cm));
 }
 
 }  // namespace
@@ -332,7 +338,7 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, w, u, nullptr, nullptr, st));
+  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, nullptr, w, u, nullptr, nullptr, nullptr, st));
 }
 
 efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -370,6 +376,29 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
                      size_t ws_bytes, void* stream) {
   return efla_fwd_state(p, q, k, v, beta, nullptr, o, nullptr, saved, saved_bytes, ws, ws_bytes,
                         stream);
+}
+
+efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const void* gate, const float* h0, void* o,
+                           float* ht, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (s.dt != Dt::BF16) return EFLA_ERR_UNSUPPORTED;
+  if (empty(s)) return EFLA_OK;
+  if (!q || !k || !v || !beta || !gate || !o || !ws) return EFLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(ws) ||
+      !aligned16(h0) || !aligned16(ht))
+    return EFLA_ERR_ALIGN;
+  if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
+  unsigned char* wsb = (unsigned char*)ws;
+  unsigned char* u = wsb;
+  unsigned char* w_ws = wsb + align_up(bytes_v(s));
+  int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
+  unsigned char* m_ws = (unsigned char*)table_ws + align_up(bytes_table(s));
+  unsigned char* seg_ws = m_ws + align_up(bytes_m(s));
+  float* cum = (float*)(seg_ws + bytes_seg(s));
+  return run_forward(s, q, k, v, beta, o, w_ws, nullptr, nullptr, table_ws, m_ws, nullptr, u, h0,
+                     ht, seg_ws, (hipStream_t)stream, gate, cum);
 }
 
 efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -429,6 +458,19 @@ efla_status efla_decode(const efla_problem* p, const void* q, const void* k, con
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
     return EFLA_ERR_ALIGN;
   return hip_status(launch_decode(s, q, k, v, beta, state, o, (hipStream_t)stream));
+}
+
+efla_status efla_decode_gated(const efla_problem* p, const void* q, const void* k,
+                              const void* v, const void* beta, const void* gate, float* state,
+                              void* o, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (s.cu) return EFLA_ERR_UNSUPPORTED;
+  if (empty(s)) return EFLA_OK;
+  if (!q || !k || !v || !beta || !gate || !state || !o) return EFLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
+    return EFLA_ERR_ALIGN;
+  return hip_status(launch_decode(s, q, k, v, beta, state, o, (hipStream_t)stream, gate));
 }
 
 efla_status efla_profile_enable(int on) {

@@ -7,6 +7,8 @@
 // One workgroup per (batch row, head); thread j keeps column j of the fp32 d_k x d_v state in
 // registers for all T tokens, so the state is read and written once per call. k_t and q_t are
 // shared through LDS; every thread forms ||k_t||^2 itself (d_k FMAs, cheaper than a reduction).
+// With log-decays (gated EFLA): S <- e^{a} (S - alpha k k^T S) + b k v^T, b the gated input
+// coefficient, i.e. column j: S_j <- e^{a} S_j + k (b v_j - e^{a} alpha (S^T k)_j).
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -16,6 +18,7 @@ __global__ __launch_bounds__(DV) void decode_kernel(Geom g, const E* __restrict_
                                                     const E* __restrict__ k,
                                                     const E* __restrict__ v,
                                                     const E* __restrict__ beta,
+                                                    const E* __restrict__ gate,
                                                     float* __restrict__ state,
                                                     E* __restrict__ o) {
   __shared__ float sk[DK], sq[DK];
@@ -41,13 +44,24 @@ __global__ __launch_bounds__(DV) void decode_kernel(Geom g, const E* __restrict_
       lam = fmaf(kd, kd, lam);
       skj = fmaf(col[d], kd, skj);  // (S^T k)_j
     }
-    const float a = flow_coef(to_f(beta[r]), lam, g.euler != 0).alpha;
-    const float rj = a * (to_f(v[r * DV + j]) - skj);
+    const float bt = to_f(beta[r]);
+    const float a = flow_coef(bt, lam, g.euler != 0).alpha;
     float oj = 0.f;
+    if (gate) {
+      const float lg = to_f(gate[r]), gd = expf(lg);
+      const float rj = gated_input_coef(bt, lam, lg, g.euler != 0) * to_f(v[r * DV + j]) - gd * a * skj;
 #pragma unroll
-    for (int d = 0; d < DK; ++d) {
-      col[d] = fmaf(sk[d], rj, col[d]);
-      oj = fmaf(col[d], sq[d], oj);
+      for (int d = 0; d < DK; ++d) {
+        col[d] = fmaf(sk[d], rj, gd * col[d]);
+        oj = fmaf(col[d], sq[d], oj);
+      }
+    } else {
+      const float rj = a * (to_f(v[r * DV + j]) - skj);
+#pragma unroll
+      for (int d = 0; d < DK; ++d) {
+        col[d] = fmaf(sk[d], rj, col[d]);
+        oj = fmaf(col[d], sq[d], oj);
+      }
     }
     o[r * DV + j] = to_e<E>(g.scale * oj);
   }
@@ -57,21 +71,23 @@ __global__ __launch_bounds__(DV) void decode_kernel(Geom g, const E* __restrict_
 
 template <typename E, int DK, int DV>
 static hipError_t decode_go(const Shape& s, const void* q, const void* k, const void* v,
-                            const void* beta, float* state, void* o, hipStream_t st) {
+                            const void* beta, const void* gate, float* state, void* o,
+                            hipStream_t st) {
   const int64_t blocks = (int64_t)s.B * s.H;
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
   hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(DV), 0, st,
                      make_geom(s, nullptr), (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)beta, state, (E*)o);
+                     (const E*)beta, (const E*)gate, state, (E*)o);
   hipError_t e = hipGetLastError();
   prof_end("decode", st);
   return e;
 }
 
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
-                         const void* beta, float* state, void* o, hipStream_t st) {
-#define EFLA_DC(E_, DK_, DV_) return decode_go<E_, DK_, DV_>(s, q, k, v, beta, state, o, st)
+                         const void* beta, float* state, void* o, hipStream_t st,
+                         const void* gate) {
+#define EFLA_DC(E_, DK_, DV_) return decode_go<E_, DK_, DV_>(s, q, k, v, beta, gate, state, o, st)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_DC(__bf16, 64, 64);
     if (s.dk == 64 && s.dv == 128) EFLA_DC(__bf16, 64, 128);

@@ -537,14 +537,12 @@ struct FlowCoef {
   float alpha, ex, dlam;
 };
 
-EFLA_DEV FlowCoef flow_coef(float beta, float lam, bool euler = false) {
-  if (euler) return FlowCoef{beta, 1.0f, 0.0f};  // delta rule: alpha = beta
-  const float x = beta * lam;
-  float ph, dph;
-  const float ex = expf(-x);
+// phi(x) = (1 - e^{-x}) / x (phi(0) = 1): Taylor polynomial for |x| < 1 (degree 11), else the
+// closed form with expm1.
+EFLA_DEV float phi_f(float x) {
   if (fabsf(x) < 1.0f) {
     // phi(x)  = sum_{n>=0} (-1)^n x^n / (n+1)!
-    ph = -1.0f / 479001600.0f;
+    float ph = -1.0f / 479001600.0f;
     ph = fmaf(ph, x, 1.0f / 39916800.0f);
     ph = fmaf(ph, x, -1.0f / 3628800.0f);
     ph = fmaf(ph, x, 1.0f / 362880.0f);
@@ -555,7 +553,26 @@ EFLA_DEV FlowCoef flow_coef(float beta, float lam, bool euler = false) {
     ph = fmaf(ph, x, -1.0f / 24.0f);
     ph = fmaf(ph, x, 1.0f / 6.0f);
     ph = fmaf(ph, x, -0.5f);
-    ph = fmaf(ph, x, 1.0f);
+    return fmaf(ph, x, 1.0f);
+  }
+  return -expm1f(-x) / x;
+}
+
+// Input coefficient of gated EFLA: with the log-decay a added to the dynamics as -a / beta
+// times the identity over the step interval, the exact flow's input term is
+// int_0^beta e^{-(gamma + lambda) s} ds = beta phi(beta lambda - a) (beta in the delta-rule mode,
+// the gated delta rule's own input step).
+EFLA_DEV float gated_input_coef(float beta, float lam, float a, bool euler) {
+  return euler ? beta : beta * phi_f(beta * lam - a);
+}
+
+EFLA_DEV FlowCoef flow_coef(float beta, float lam, bool euler = false) {
+  if (euler) return FlowCoef{beta, 1.0f, 0.0f};  // delta rule: alpha = beta
+  const float x = beta * lam;
+  float ph, dph;
+  const float ex = expf(-x);
+  if (fabsf(x) < 1.0f) {
+    ph = phi_f(x);
     // phi'(x) = sum_{n>=0} (n+1) (-1)^(n+1) x^n / (n+2)!
     dph = 1.0f / 518918400.0f;
     dph = fmaf(dph, x, -1.0f / 43545600.0f);

@@ -36,18 +36,22 @@ void prof_end(const char* name, hipStream_t st);
 hipError_t launch_chunk_table(const Shape& s, int* table, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const void* k, const void* beta, float* lam, float* alpha,
                        float* ex, float* dlam, hipStream_t st);
+// gate (log-decays, problem dtype, or null) selects gated EFLA; cum then receives the running
+// sums of the log-decays inside each chunk, fp32 [slots][H][64].
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                         const void* v, const void* beta, void* w, void* u, void* m, void* x,
-                         hipStream_t st);
+                         const void* v, const void* beta, const void* gate, void* w, void* u,
+                         void* m, void* x, float* cum, hipStream_t st);
 // h0 / ht (scan_fwd) and dht / dh0 (scan_bwd): fp32 [n_seqs][H][dk][dv] per-sequence
 // states entering / leaving the sequence, or null (zero in, not written out).
+// cum (null, or the running log-decay sums of launch_ut_fwd) selects gated EFLA.
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
-                           void* states, const float* h0, float* ht, hipStream_t st);
+                           void* states, const float* h0, float* ht, hipStream_t st,
+                           const float* cum = nullptr);
 // Transition of each sequence of a segment view: P = prod over its chunks of
 // (I - K^T W), as fp32 [n_seqs][H][dk][dk] (the scan with U = 0 from S = I).
 hipError_t launch_scan_fwd_transition(const Shape& s, const void* k, const void* w, float* p,
-                                      hipStream_t st);
+                                      hipStream_t st, const float* cum = nullptr);
 // Chain the segments of every sequence: S_0 = h0 (zero if null), S_{j+1} = P_j S_j + R_j;
 // writes S_j of every segment to sin ([B * seg_plan][H][dk][dv]) and the final state to ht
 // (if not null). P, R as produced by the transition and state-only scans of segment_view(s).
@@ -57,7 +61,8 @@ hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, cons
                            const void* w, const void* m, const void* d_o, void* dut,
                            void* dstates, const float* dht, float* dh0, hipStream_t st);
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
-                         const void* beta, float* state, void* o, hipStream_t st);
+                         const void* beta, float* state, void* o, hipStream_t st,
+                         const void* gate = nullptr);
 hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, const void* k,
                             const void* v, const void* beta, const void* d_o, const void* ut,
                             const void* dut, const void* states, const void* dstates,

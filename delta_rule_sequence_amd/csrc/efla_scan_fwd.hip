@@ -20,7 +20,7 @@
 
 namespace efla {
 
-template <typename E, int DK, int DV, int NWC>
+template <typename E, int DK, int DV, int NWC, bool GT = false>
 struct ScanFwdLds {
   static constexpr int TV = 16 * NWC;
   static constexpr int NWL = NWC;  // loader waves
@@ -32,7 +32,8 @@ struct ScanFwdLds {
   static constexpr size_t oK = oQ + SK::BYTES;          // K  [64][DK]
   static constexpr size_t oM = oK + SK::BYTES;          // M  [64][64]
   static constexpr size_t oU = oM + SM::BYTES;          // U  [64][TV] (this tile's columns)
-  static constexpr size_t stage = oU + SU::BYTES;
+  static constexpr size_t oC = oU + SU::BYTES;         // running log-decay sums [64] (gated)
+  static constexpr size_t stage = oC + (GT ? 64 * 4 : 0);
   // output staging (layout SU): O [64][TV], U~ [64][TV], S [DK][TV]; two buffers
   static constexpr size_t gO = 0, gUt = SU::BYTES, gS = 2 * SU::BYTES;
   static constexpr size_t sstage = gS + (size_t)DK * SU::RB;
@@ -42,15 +43,19 @@ struct ScanFwdLds {
 
 // WO: write O (also needs Q and M); WSV: write U~ and the chunk states (saved for the
 // backward pass). Compile-time, so the inner loops carry no branches on them.
+// GT: gated EFLA. With c_t the running log-decay sum inside the chunk (from the UT kernel),
+// O = scale (diag(e^{c}) Q S + M U~) (M carries the decay ratios), and
+// S <- e^{c_last} S + K^T diag(e^{c_last - c}) U~; the decays are applied to accumulators.
 // PM: transition mode for the segment-parallel scan. The chunk step is affine in the state,
 // S <- (I - K^T W) S + K^T U, so running it with U = 0 from S = I (DV = DK) leaves in ht the
 // product of the (I - K^T W) over the sequence; U is neither read nor needed.
-template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM>
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
 __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
-    E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht) {
-  typedef ScanFwdLds<E, DK, DV, NWC> L;
+    E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
+    const float* __restrict__ cum) {
+  typedef ScanFwdLds<E, DK, DV, NWC, GT> L;
   typedef typename L::SU SU;
   typedef typename Mma<E>::vec V;
   constexpr int TV = L::TV, NWL = L::NWL, NTILE = DV / TV, KC = Mma<E>::KC;
@@ -103,6 +108,9 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
       dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
       dma_tile<E, 64, NWL>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                            kChunk, kChunk, wl, lane);
+    }
+    if constexpr (GT) {  // 64 floats: one plain load per lane of the first loader wave
+      if (wl == 0) ((float*)(st + L::oC))[lane] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
     }
   };
   auto copy_out = [&](int c) {  // staged outputs of chunk c -> global memory, 16-byte rows
@@ -174,6 +182,21 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     V sb[KSK];
 #pragma unroll
     for (int ks = 0; ks < KSK; ++ks) sb[ks] = bop_acc<E>(Sacc, ks);
+    // gated: e^{c_t} for the output's state term, e^{c_last - c_t} for the state update
+    float gam[4][4], dec[4][4], gC = 1.f;
+    if constexpr (GT) {
+      const float* cv = (const float*)(st + L::oC);
+      const float cl = cv[n - 1];
+      gC = expf(cl);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float cr = cv[prow<E>(rb, g4 + i)];
+          gam[rb][i] = expf(cr);
+          dec[rb][i] = expf(fminf(cl - cr, 0.f));
+        }
+    }
     if constexpr (WSV) {  // S_c, the state entering chunk c
 #pragma unroll
       for (int b = 0; b < NBK; ++b)
@@ -194,6 +217,12 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
         ws[rb] = Mma<E>::step(aw[rb][ks], sb[ks], ws[rb]);
         if constexpr (WO) oa[rb] = Mma<E>::step(aq[rb][ks], sb[ks], oa[rb]);
       }
+    }
+    if constexpr (GT && WO) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oa[rb][i] *= gam[rb][i];
     }
     V ak[NBK][KST], am[4][KST];
 #pragma unroll
@@ -216,14 +245,28 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         uta[rb][i] = prow<E>(rb, g4 + i) < n ? to_f(uv[rb][i]) - ws[rb][i] : 0.f;
-    V ub[KST];
+    V ub[KST], ubd[KST];
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) ub[ks] = bop_acc<E>(uta, ks);
+    if constexpr (GT) {  // S <- e^{c_last} S + K^T diag(e^{c_last - c}) U~
+      f32x4 utd[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) utd[rb][i] = uta[rb][i] * dec[rb][i];
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) ubd[ks] = bop_acc<E>(utd, ks);
+#pragma unroll
+      for (int b = 0; b < NBK; ++b) Sacc[b] *= gC;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) ubd[ks] = ub[ks];
+    }
     // S += K^T U~
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) Sacc[b] = Mma<E>::step(ak[b][ks], ub[ks], Sacc[b]);
+      for (int ks = 0; ks < KST; ++ks) Sacc[b] = Mma<E>::step(ak[b][ks], ubd[ks], Sacc[b]);
     if constexpr (WO) {  // O = scale (P + M U~); M is lower triangular
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
@@ -265,14 +308,15 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   }
 }
 
-template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM = false>
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM = false, bool GT = false>
 static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* u, const void* m, void* o, void* ut,
-                               void* states, const float* h0, float* ht, hipStream_t st) {
-  typedef ScanFwdLds<E, DK, DV, NWC> L;
+                               void* states, const float* h0, float* ht, hipStream_t st,
+                               const float* cum = nullptr) {
+  typedef ScanFwdLds<E, DK, DV, NWC, GT> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM, GT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -280,11 +324,13 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
   const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / L::TV);
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
-  hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM, GT>), dim3((unsigned)blocks),
                      dim3(128 * NWC), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
-                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht);
+                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht, cum);
   hipError_t e = hipGetLastError();
-  prof_end(PM ? "scan_fwd_transition" : WO || WSV ? "scan_fwd" : "scan_fwd_state", st);
+  prof_end(PM ? (GT ? "scan_fwd_transition_gated" : "scan_fwd_transition")
+             : WO || WSV ? (GT ? "scan_fwd_gated" : "scan_fwd") : (GT ? "scan_fwd_state_gated" : "scan_fwd_state"),
+           st);
   return e;
 }
 
@@ -293,8 +339,21 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
 template <typename E, int DK, int DV, int NWC>
 static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* u, const void* m, void* o, void* ut,
-                              void* states, const float* h0, float* ht, hipStream_t st) {
+                              void* states, const float* h0, float* ht, hipStream_t st,
+                              const float* cum) {
   const bool wsv = ut && states;
+  if (cum) {  // gated: outputs O (and final states), or final states alone; no saving
+    if constexpr (sizeof(E) == 2) {
+      if (wsv) return hipErrorInvalidValue;
+      if (o)
+        return scan_fwd_run<E, DK, DV, NWC, true, false, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
+      if (ht)
+        return scan_fwd_run<E, DK, DV, NWC, false, false, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
+      return hipSuccess;
+    } else {
+      return hipErrorInvalidValue;  // the fp32 tiles leave no LDS room for the decays
+    }
+  }
   if (o && wsv)
     return scan_fwd_run<E, DK, DV, NWC, true, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
   if (o) return scan_fwd_run<E, DK, DV, NWC, true, false>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
@@ -321,9 +380,10 @@ size_t lds_scan_fwd(Dt dt, int dk, int dv) {
 
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
-                           void* states, const float* h0, float* ht, hipStream_t st) {
+                           void* states, const float* h0, float* ht, hipStream_t st,
+                           const float* cum) {
 #define EFLA_SF(E_, DK_, DV_, NWC_) \
-  return scan_fwd_go<E_, DK_, DV_, NWC_>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st)
+  return scan_fwd_go<E_, DK_, DV_, NWC_>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SF(__bf16, 64, 64, 2);
     if (s.dk == 64 && s.dv == 128) EFLA_SF(__bf16, 64, 128, 2);
@@ -335,11 +395,19 @@ hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, cons
 }
 
 hipError_t launch_scan_fwd_transition(const Shape& s, const void* k, const void* w, float* p,
-                                      hipStream_t st) {
+                                      hipStream_t st, const float* cum) {
 #define EFLA_ST(E_, DK_, NWC_)                                                               \
   return scan_fwd_run<E_, DK_, DK_, NWC_, false, false, true>(s, nullptr, nullptr, k, w, nullptr, \
                                                              nullptr, nullptr, nullptr, nullptr, \
                                                              nullptr, p, st)
+  if (cum) {
+    if (s.dt != Dt::BF16) return hipErrorInvalidValue;
+    if (s.dk == 64)
+      return scan_fwd_run<__bf16, 64, 64, 2, false, false, true, true>(s, nullptr, nullptr, k, w, nullptr, nullptr,
+                                                                      nullptr, nullptr, nullptr, nullptr, p, st, cum);
+    return scan_fwd_run<__bf16, 128, 128, 2, false, false, true, true>(s, nullptr, nullptr, k, w, nullptr, nullptr,
+                                                                      nullptr, nullptr, nullptr, nullptr, p, st, cum);
+  }
   if (s.dt == Dt::BF16) {
     if (s.dk == 64) EFLA_ST(__bf16, 64, 2);
     EFLA_ST(__bf16, 128, 2);

@@ -9,11 +9,16 @@
 // substitution in fp32 in LDS. Padded rows of a tail chunk read as zero (their beta is zero,
 // so alpha = 0 and they do not touch the valid rows). M (q may be null) and X (kept for the
 // backward pass, which then needs no inverse of its own) are optional outputs.
+//
+// Gated EFLA (GT): with c_t the running sum of the log-decays inside the chunk,
+//   A_ts = alpha_t e^{c_t - c_s} k_t . k_s (s < t),  X = (I + A)^{-1},
+//   W = X diag(alpha e^{c}) K,  U = X diag(b) V,  M_ts = e^{c_t - c_s} q_t . k_s (s <= t),
+// b the gated input coefficient; the c_t are written out for the scan.
 #include "efla_internal.hpp"
 
 namespace efla {
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool GT = false>
 struct UtFwdLds {
   static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64), LV = pitch<E>(DV), LF = kPitchF;
   static constexpr size_t oK = 0;                                   // K        [64][LK]
@@ -21,18 +26,21 @@ struct UtFwdLds {
   static constexpr size_t oA = oV + 64 * LV * sizeof(E);            // A (fp32) [64][LF]; later T
   static constexpr size_t oX = oA + 64 * LF * 4;                    // X (fp32) [64][LF]; M staging first
   static constexpr size_t oAl = oX + 64 * LF * 4;                   // alpha    [64]
-  static constexpr size_t bytes = oAl + 64 * 4;
+  static constexpr size_t oBl = oAl + 64 * 4;                       // b, c     [64] each (GT)
+  static constexpr size_t oCm = oBl + 64 * 4;
+  static constexpr size_t oT2 = oCm + 64 * 4;                       // X diag(b) [64][LT] (GT)
+  static constexpr size_t bytes = GT ? oT2 + 64 * LT * sizeof(E) : oAl + 64 * 4;
   static_assert(64 * LT * sizeof(E) <= 64 * LF * 4, "T and M must fit in an fp32 work matrix");
 };
 
 // Persistent: the workgroup walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...; the
 // next unit's K, V and Q rows are requested into registers while the current one computes.
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool GT>
 __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const E* __restrict__ beta, E* __restrict__ w, E* __restrict__ u, E* __restrict__ mout,
-    E* __restrict__ xout) {
-  typedef UtFwdLds<E, DK, DV> L;
+    const E* __restrict__ beta, const E* __restrict__ gate, E* __restrict__ w, E* __restrict__ u,
+    E* __restrict__ mout, E* __restrict__ xout, float* __restrict__ cum) {
+  typedef UtFwdLds<E, DK, DV, GT> L;
   typedef typename Mma<E>::vec Vv;
   constexpr int KC = Mma<E>::KC, KS = DK / KC;
   constexpr int VE = 16 / (int)sizeof(E);
@@ -48,6 +56,9 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   float* sX = (float*)(smem + L::oX);
   E* sM = (E*)(smem + L::oX);
   float* sAl = (float*)(smem + L::oAl);
+  float* sBl = (float*)(smem + L::oBl);
+  float* sCm = (float*)(smem + L::oCm);
+  E* sT2 = (E*)(smem + L::oT2);
 
   int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -57,7 +68,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   if (un >= nu) return;
 
   u32x4 kR[KIT], vR[VIT];
-  float bR[KIT];
+  float bR[KIT], aR[KIT], aN = 0.f;
   Vv qN[KS], qA[KS];
   auto issue_k = [&](const ChunkUnit& c) {
 #pragma unroll
@@ -66,7 +77,9 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       const int r = min(i / VPR, c.n - 1), cc = (i % VPR) * VE;
       kR[it] = *(const u32x4*)(k + (c.row0 + r) * DK + cc);
       bR[it] = to_f(beta[c.row0 + r]);
+      if constexpr (GT) aR[it] = to_f(gate[c.row0 + r]);
     }
+    if constexpr (GT) aN = lane < c.n ? to_f(gate[c.row0 + lane]) : 0.f;  // token = lane
   };
   auto issue_v = [&](const ChunkUnit& c) {
 #pragma unroll
@@ -108,7 +121,10 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
       acc = group_sum<VPR>(acc);
-      if (i % VPR == 0) sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc, g.euler).alpha;
+      if (i % VPR == 0) {
+        sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc, g.euler).alpha;
+        if constexpr (GT) sBl[r] = r < n ? gated_input_coef(bR[it], acc, aR[it], g.euler) : 0.f;
+      }
     }
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
@@ -119,6 +135,18 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     if (mout) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qA[ks] = keep_if_vec(qN[ks], rA + (lane & 15) < n);
+    }
+    if constexpr (GT) {  // c_t: inclusive running sum of the log-decays (padded rows add 0)
+      if (wv == 0) {
+        float cs = aN;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float t = __shfl_up(cs, off);
+          if (lane >= off) cs += t;
+        }
+        sCm[lane] = cs;
+        if (cum) cum[cur.sh * 64 + lane] = cs;
+      }
     }
     __syncthreads();
     const int unx = un + (int)gridDim.x;
@@ -133,13 +161,18 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     {
       const int ra = 3 - wv, rowa = 16 * ra + (lane & 15), c4 = 4 * (lane >> 4);
       const float ala = sAl[rowa];
+      const float cra = GT ? sCm[rowa] : 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         if (nb > ra) continue;
         f32x4 acc = mma<E, false, false>(sK + 16 * nb * L::LK, L::LK, sK + 16 * ra * L::LK, L::LK, 0, DK, zero4(), lane);
         f32x4 av;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = rowa > 16 * nb + c4 + i ? ala * acc[i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int col = 16 * nb + c4 + i;
+          const float dec = GT ? expf(fminf(cra - sCm[col], 0.f)) : 1.f;  // e^{c_t - c_s}
+          av[i] = rowa > col ? ala * dec * acc[i] : 0.f;
+        }
         *(f32x4*)(sA + rowa * L::LF + 16 * nb + c4) = av;
       }
     }
@@ -155,6 +188,11 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (4 * (lane >> 4) + i > (lane & 15)) m[i] = 0.f;
+          }
+          if constexpr (GT) {
+            const float cr = sCm[rA + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m[i] *= expf(fminf(cr - sCm[16 * nb + 4 * (lane >> 4) + i], 0.f));
           }
         }
         st_frag_t<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
@@ -182,21 +220,39 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
         f32x4 x0 = *(const f32x4*)(sX + r * L::LF + c);
         f32x4 x1 = *(const f32x4*)(sX + r * L::LF + c + 4);
         if (up) x0 = x1 = zero4();
-        const f32x4 a0 = *(const f32x4*)(sAl + c), a1 = *(const f32x4*)(sAl + c + 4);
+        f32x4 a0 = *(const f32x4*)(sAl + c), a1 = *(const f32x4*)(sAl + c + 4);
+        f32x4 b0 = a0, b1 = a1;  // column scales of the U factor
+        if constexpr (GT) {      // W factor X diag(alpha e^{c}), U factor X diag(b)
+          const f32x4 c0 = *(const f32x4*)(sCm + c), c1 = *(const f32x4*)(sCm + c + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a0[e] *= expf(c0[e]);
+            a1[e] *= expf(c1[e]);
+          }
+          b0 = *(const f32x4*)(sBl + c);
+          b1 = *(const f32x4*)(sBl + c + 4);
+        }
         if constexpr (sizeof(E) == 2) {
-          bf16x8 xe, te;
+          bf16x8 xe, te, tu;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             xe[e] = (__bf16)x0[e];
             xe[e + 4] = (__bf16)x1[e];
             te[e] = (__bf16)(x0[e] * a0[e]);
             te[e + 4] = (__bf16)(x1[e] * a1[e]);
+            tu[e] = (__bf16)(x0[e] * b0[e]);
+            tu[e + 4] = (__bf16)(x1[e] * b1[e]);
           }
           *(bf16x8*)(sT + r * L::LT + c) = te;
+          if constexpr (GT) *(bf16x8*)(sT2 + r * L::LT + c) = tu;
           if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
         } else {
           *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
           *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
+          if constexpr (GT) {
+            *(f32x4*)(sT2 + r * L::LT + c) = x0 * b0;
+            *(f32x4*)(sT2 + r * L::LT + c + 4) = x1 * b1;
+          }
           if (gx) {
             *(f32x4*)(gx + r * 64 + c) = x0;
             *(f32x4*)(gx + r * 64 + c + 4) = x1;
@@ -226,8 +282,9 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       const int k01 = round_up_kc<E>(32);
       mma_blk<E, false, true, 2, CW, kChunk, true>(sT, L::LT, sK + 16 * CW * wv, L::LK, 0, k01, w01, lane);
       mma_blk<E, false, true, 2, CW, kChunk, true>(sT + 32 * L::LT, L::LT, sK + 16 * CW * wv, L::LK, 0, kChunk, w23, lane);
-      mma_blk<E, false, true, 2, CU, kChunk, true>(sT, L::LT, sV + 16 * CU * wv, L::LV, 0, k01, u01, lane);
-      mma_blk<E, false, true, 2, CU, kChunk, true>(sT + 32 * L::LT, L::LT, sV + 16 * CU * wv, L::LV, 0, kChunk, u23, lane);
+      const E* tU = GT ? sT2 : sT;
+      mma_blk<E, false, true, 2, CU, kChunk, true>(tU, L::LT, sV + 16 * CU * wv, L::LV, 0, k01, u01, lane);
+      mma_blk<E, false, true, 2, CU, kChunk, true>(tU + 32 * L::LT, L::LT, sV + 16 * CU * wv, L::LV, 0, kChunk, u23, lane);
     }
     __syncthreads();
 #pragma unroll
@@ -247,14 +304,14 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   }
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool GT>
 static hipError_t ut_go(const Shape& s, const int* table, const void* q, const void* k,
-                        const void* v, const void* beta, void* w, void* u, void* m, void* x,
-                        hipStream_t st) {
-  typedef UtFwdLds<E, DK, DV> L;
+                        const void* v, const void* beta, const void* gate, void* w, void* u,
+                        void* m, void* x, float* cum, hipStream_t st) {
+  typedef UtFwdLds<E, DK, DV, GT> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)ut_fwd_kernel<E, DK, DV>,
+    hipError_t e = hipFuncSetAttribute((const void*)ut_fwd_kernel<E, DK, DV, GT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -264,12 +321,20 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
   if (units < 1) return hipSuccess;
   const int64_t blocks = units < 2 * cu_count() ? units : 2 * cu_count();
   prof_begin(st);
-  hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
+  hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV, GT>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
                      st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)beta, (E*)w, (E*)u, (E*)m, (E*)x);
+                     (const E*)beta, (const E*)gate, (E*)w, (E*)u, (E*)m, (E*)x, cum);
   hipError_t e = hipGetLastError();
-  prof_end("ut_fwd", st);
+  prof_end(GT ? "ut_fwd_gated" : "ut_fwd", st);
   return e;
+}
+
+template <typename E, int DK, int DV>
+static hipError_t ut_dispatch(const Shape& s, const int* table, const void* q, const void* k,
+                              const void* v, const void* beta, const void* gate, void* w,
+                              void* u, void* m, void* x, float* cum, hipStream_t st) {
+  if (gate) return ut_go<E, DK, DV, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, st);
+  return ut_go<E, DK, DV, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, st);
 }
 
 size_t lds_ut_fwd(Dt dt, int dk, int dv) {
@@ -285,15 +350,17 @@ size_t lds_ut_fwd(Dt dt, int dk, int dv) {
 }
 
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                         const void* v, const void* beta, void* w, void* u, void* m, void* x,
-                         hipStream_t st) {
+                         const void* v, const void* beta, const void* gate, void* w, void* u,
+                         void* m, void* x, float* cum, hipStream_t st) {
+#define EFLA_UT(E_, DK_, DV_) return ut_dispatch<E_, DK_, DV_>(s, table, q, k, v, beta, gate, w, u, m, x, cum, st)
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) return ut_go<__bf16, 64, 64>(s, table, q, k, v, beta, w, u, m, x, st);
-    if (s.dk == 64 && s.dv == 128) return ut_go<__bf16, 64, 128>(s, table, q, k, v, beta, w, u, m, x, st);
-    if (s.dk == 128 && s.dv == 64) return ut_go<__bf16, 128, 64>(s, table, q, k, v, beta, w, u, m, x, st);
-    return ut_go<__bf16, 128, 128>(s, table, q, k, v, beta, w, u, m, x, st);
+    if (s.dk == 64 && s.dv == 64) EFLA_UT(__bf16, 64, 64);
+    if (s.dk == 64 && s.dv == 128) EFLA_UT(__bf16, 64, 128);
+    if (s.dk == 128 && s.dv == 64) EFLA_UT(__bf16, 128, 64);
+    EFLA_UT(__bf16, 128, 128);
   }
-  return ut_go<float, 64, 64>(s, table, q, k, v, beta, w, u, m, x, st);
+  EFLA_UT(float, 64, 64);
+#undef EFLA_UT
 }
 
 }  // namespace efla

@@ -160,6 +160,32 @@ def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=No
     return (o, saved) if ht is None else (o, saved, ht)
 
 
+def efla_fwd_gated(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, ws=None, o=None,
+                   mode="exact", initial_state=None, final_state=None, segments=0):
+    """Gated EFLA forward (efla_fwd_gated in include/efla.h): gate is the per-token log-decay
+    [B,H,T] in the input dtype (bf16 only). Returns o, or (o, final_state) when final_state is
+    True or a preallocated fp32 [n_state, H, dk, dv] tensor."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode, segments)
+    _need(gate, "gate", k.dtype, tuple(beta.shape))
+    if o is None:
+        o = torch.empty_like(v)
+    else:
+        _need(o, "o", v.dtype, v.shape)
+    h0 = _state_tensor(initial_state, "initial_state", p, k.device)
+    ht = None
+    if final_state is True:
+        ht = torch.empty((_n_state(p), p.H, p.dk, p.dv), dtype=torch.float32, device=k.device)
+    elif final_state is not None and final_state is not False:
+        ht = _state_tensor(final_state, "final_state", p, k.device)
+    ws_n = efla_workspace_bytes(p, False)
+    if ws is None or ws.numel() < ws_n:
+        ws = _bytes(ws_n, k.device)
+    _lib.check("efla_fwd_gated", _lib.lib().efla_fwd_gated(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(h0), _ptr(o),
+        _ptr(ht), _ptr(ws), ws.numel(), _stream()))
+    return o if ht is None else (o, ht)
+
+
 def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None, grads=None,
              mode="exact", initial_state=None, d_final_state=None, d_initial_state=False,
              segments=0):
@@ -205,6 +231,22 @@ def efla_decode(q, k, v, beta, state, scale=1.0, mode="exact", o=None):
         _need(o, "o", v.dtype, v.shape)
     _lib.check("efla_decode", _lib.lib().efla_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                                     _ptr(beta), _ptr(state), _ptr(o), _stream()))
+    return o
+
+
+def efla_decode_gated(q, k, v, beta, gate, state, scale=1.0, mode="exact", o=None):
+    """Gated recurrent inference (efla_decode_gated): as efla_decode with the per-token
+    log-decay gate [B,H,T] in the input dtype. state is updated in place. Returns o."""
+    p = make_problem(q, k, v, beta, scale, None, mode)
+    _need(gate, "gate", k.dtype, tuple(beta.shape))
+    _need(state, "state", torch.float32, (p.B, p.H, p.dk, p.dv))
+    if o is None:
+        o = torch.empty_like(v)
+    else:
+        _need(o, "o", v.dtype, v.shape)
+    _lib.check("efla_decode_gated", _lib.lib().efla_decode_gated(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(state), _ptr(o),
+        _stream()))
     return o
 
 

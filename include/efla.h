@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 5
+#define EFLA_ABI_VERSION 6
 
 typedef enum {
   EFLA_OK = 0,
@@ -156,6 +156,23 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
                            const void* beta, const float* h0, void* o, float* ht, void* saved,
                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
 
+/* Gated EFLA forward (summary page, section 3.4 names it; the appendix applies the exact flow
+ * to Gated DeltaNet; the pages print no formula, this is the reading taken): a per-token
+ * log-decay a_t (gate, [B,H,T], problem dtype; a_t <= 0 decays) adds -a_t / beta_t times the
+ * identity to the dynamics matrix over the step interval, and the exact flow is
+ *   S_t = e^{a_t} (I - alpha_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,
+ *   alpha_t = beta_t phi(beta_t lambda_t),  b_t = beta_t phi(beta_t lambda_t - a_t),
+ * phi(x) = (1 - e^{-x}) / x (mode EFLA_EULER: alpha_t = b_t = beta_t, the gated delta rule).
+ * a = 0 gives efla_fwd_state. Computed chunkwise with the running log-decay sums c of each
+ * chunk: A_ts = alpha_t e^{c_t - c_s} k_t . k_s, W = X diag(alpha e^c) K, U = X diag(b) V,
+ * O = scale (diag(e^c) Q S + (tril(Q K^T) * e^{c_t - c_s}) U~),
+ * S <- e^{c_last} S + K^T diag(e^{c_last - c}) U~. h0 / ht as in efla_fwd_state; segments as in
+ * efla_fwd. Inference forward: no saved buffer (no gated backward is provided). bf16 problems
+ * only (EFLA_ERR_UNSUPPORTED otherwise). ws: efla_workspace_bytes(p, 0). */
+efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const void* gate, const float* h0, void* o,
+                           float* ht, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of sum(o * d_o): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T], all in
  * the problem dtype (every output fully overwritten). `saved` is the buffer a forward
  * call on the same inputs filled, or NULL to recompute it inside ws.
@@ -182,6 +199,12 @@ efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, 
  * efla_fwd_state is the fast path for long T. Needs no workspace. */
 efla_status efla_decode(const efla_problem* p, const void* q, const void* k, const void* v,
                         const void* beta, float* state, void* o, void* stream);
+
+/* Recurrent inference of gated EFLA (the recurrence of efla_fwd_gated, token by token), with
+ * gate [B,H,T] in the problem dtype; otherwise as efla_decode. */
+efla_status efla_decode_gated(const efla_problem* p, const void* q, const void* k,
+                              const void* v, const void* beta, const void* gate, float* state,
+                              void* o, void* stream);
 
 /* Kernel timing for profiling. While enabled, every kernel that efla_* enqueues is
  * bracketed by two HIP events recorded on the same stream. efla_profile_read waits for

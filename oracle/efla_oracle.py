@@ -340,23 +340,27 @@ def euler_forward(q, k, v, beta, scale=1.0, cu_seqlens=None):
 # Gated EFLA (reading in the module docstring).
 # ---------------------------------------------------------------------------
 
-def gated_coefficients(k, beta, gate):
+def gated_coefficients(k, beta, gate, mode="exact"):
     """lambda, alpha = beta phi(beta lambda), g = e^a, b = beta phi(beta lambda - a) per token.
-    k: [..., d_k]; beta, gate (log-decay a): [...]."""
+    k: [..., d_k]; beta, gate (log-decay a): [...]. mode "euler": alpha = b = beta, the gated
+    delta rule's own steps (its explicit-Euler counterpart)."""
     k, beta, gate = _f64(k), _f64(beta), _f64(gate)
     lam = np.sum(k * k, axis=-1)
+    if mode == "euler":
+        return dict(lam=lam, alpha=beta.copy(), g=np.exp(gate), b=beta.copy())
+    assert mode == "exact", mode
     x = beta * lam
     return dict(lam=lam, alpha=beta * phi(x), g=np.exp(gate), b=beta * phi(x - gate))
 
 
-def gated_forward(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, initial_state=None):
+def gated_forward(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, initial_state=None, mode="exact"):
     """Gated EFLA forward, token by token. gate: log-decay a_t [B,H,T] (a_t <= 0 is a decay).
 
     Returns (o [B,H,T,dv], final_state [n_seq,H,dk,dv]), fp64."""
     q, k, v, beta, gate = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(gate)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
-    c = gated_coefficients(k, beta, gate)
+    c = gated_coefficients(k, beta, gate, mode)
     o = np.zeros((B, H, T, dv))
     seqs = sequences(B, T, cu_seqlens)
     final = np.zeros((len(seqs), H, dk, dv))

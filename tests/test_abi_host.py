@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 5
+    assert L.efla_abi_version() == 6
 
 
 def test_status_strings(L):
@@ -96,7 +96,8 @@ def test_workspace_and_saved_sizes(L):
     states = slots * 16 * 128 * 128 * e
     m = slots * 16 * 64 * 64 * e
     assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states + 2 * m
-    assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * w + m
+    cum = slots * 16 * 64 * 4  # running log-decay sums of the gated forward
+    assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * w + m + cum
     assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states + 2 * m) + w
     lay = _lib.EflaSavedLayout()
     assert L.efla_get_saved_layout(ctypes.byref(p), ctypes.byref(lay)) == 0
@@ -185,3 +186,20 @@ def test_segment_plan_workspace(L):
     p, p1 = _p(B=1, T=32768), _p(B=1, T=32768, segments=1)
     assert (L.efla_workspace_bytes(ctypes.byref(p), 1) -
             L.efla_workspace_bytes(ctypes.byref(p1), 1)) == 8 * per_seg
+
+
+def test_gated_entry_points_reject_bad_arguments(L):
+    """Gated forward and decode: bf16 only, gate required, same validation as the others."""
+    fake = ctypes.c_void_p(0x100000)
+    p = _p(B=1, H=2, T=128)
+    ws = L.efla_workspace_bytes(ctypes.byref(p), 0)
+    # fp32 problems: not provided
+    pf = _p(B=1, H=2, T=128, dtype=_lib.EFLA_F32, dk=64, dv=64)
+    assert L.efla_fwd_gated(ctypes.byref(pf), fake, fake, fake, fake, fake, None, fake, None, fake, 1 << 40, None) == 4
+    # missing gate / missing workspace / short workspace
+    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, None, fake, ws, None) == 1
+    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, None, None, ws, None) == 1
+    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, None, fake, ws - 1, None) == 5
+    assert L.efla_decode_gated(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None) == 1
+    packed = _p(B=1, T=128, cu=0x1000, n_seqs=2)
+    assert L.efla_decode_gated(ctypes.byref(packed), fake, fake, fake, fake, fake, fake, fake, None) == 4
