@@ -263,6 +263,24 @@ def main():
     torch.cuda.synchronize()
     euler_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    # Gated EFLA forward on the same tensors (log-decays log sigmoid(N(3, 1)), bf16) against the
+    # ungated forward without a saved buffer (the gated forward is an inference forward).
+    gate = torch.from_numpy(-np.logaddexp(0.0, -(np.random.default_rng(5).standard_normal((B, H, T)) + 3.0))
+                            .astype(np.float32)).to(dev, torch.bfloat16)
+    gated = {}
+    for key, f in (("gated", lambda: E.efla_fwd_gated(q, k, v, beta, gate, 1.0, None, ws, o=o)),
+                   ("ungated", lambda: E.efla_fwd(q, k, v, beta, 1.0, None, False, ws, o=o))):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            f()
+        torch.cuda.synchronize()
+        gated[key + "_fwd_ms"] = round((time.perf_counter() - t0) * 1e3 / args.steps, 4)
+    gated["gated_over_ungated_time"] = round(gated["gated_fwd_ms"] / gated["ungated_fwd_ms"], 4)
+    gated["gated_fwd_tokens_per_s"] = round(B * T / (gated["gated_fwd_ms"] * 1e-3), 1)
+
     # Recurrent decoding: one token for every (batch row, head), state in fp32.
     state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=dev)
     q1, k1, v1, b1 = (t[:, :, :1].contiguous() for t in (q, k, v, beta))
@@ -324,6 +342,7 @@ def main():
                        "exact_over_euler_time": round(ms_per_step / euler_ms, 4)},
         "decode": {"us_per_call": round(decode_us, 2), "tokens_per_call": B,
                    "state_MB": round(B * H * dk * dv * 4 / 1e6, 2)},
+        "gated_forward": gated,
         "long_context": long_ctx,
     }
     if not args.no_cpu_baseline:

@@ -377,7 +377,73 @@ def gated_forward(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, initial_state
     return o, final
 
 
-def gated_chunk_forward(q, k, v, beta, gate, scale=1.0, chunk=CHUNK, initial_state=None):
+def gated_coefficient_derivatives(k, beta, gate, mode="exact"):
+    """Partial derivatives of alpha = beta phi(x) and b = beta phi(x - a), x = beta lambda:
+    da/dbeta = e^{-x}, da/dlam = beta^2 phi'(x), db/dbeta = phi(x - a) + x phi'(x - a),
+    db/dlam = beta^2 phi'(x - a), db/da = -beta phi'(x - a) (mode "euler": 1, 0, 1, 0, 0)."""
+    k, beta, gate = _f64(k), _f64(beta), _f64(gate)
+    lam = np.sum(k * k, axis=-1)
+    if mode == "euler":
+        one, zero = np.ones_like(beta), np.zeros_like(beta)
+        return dict(da_dbeta=one, da_dlam=zero, db_dbeta=one, db_dlam=zero, db_da=zero)
+    x = beta * lam
+    dpg = dphi(x - gate)
+    return dict(da_dbeta=np.exp(-x), da_dlam=beta * beta * dphi(x), db_dbeta=phi(x - gate) + x * dpg,
+                db_dlam=beta * beta * dpg, db_da=-beta * dpg)
+
+
+def gated_backward(q, k, v, beta, gate, do, scale=1.0, initial_state=None, d_final_state=None,
+                   mode="exact"):
+    """Reverse-mode gradients of sum(o * do) (+ <final_state, d_final_state>) for gated_forward
+    (dense batches), written out by hand per token:
+      S_t = g (S_{t-1} - alpha k y^T) + b k v^T,  y = S_{t-1}^T k,  o_t = scale S_t^T q_t;
+      dq = scale S_t do;  dv = b dS^T k;  db = k^T dS v;  dg = <dS, S_{t-1}> - alpha k^T dS y;
+      dalpha = -g k^T dS y;  dk = -g alpha (dS y + S_{t-1} dS^T k) + b dS v + 2 k dlambda;
+      dS_{t-1} = g (dS - alpha k k^T dS);  da = g dg + db db/da.
+    Returns dict(dq, dk, dv, dbeta, dgate, d_initial_state), fp64."""
+    q, k, v, beta, gate, do = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(gate), _f64(do)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    co = gated_coefficients(k, beta, gate, mode)
+    de = gated_coefficient_derivatives(k, beta, gate, mode)
+    S0 = _f64(initial_state)
+    dSF = _f64(d_final_state)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), dbeta=np.zeros_like(beta),
+               dgate=np.zeros_like(gate), d_initial_state=np.zeros((B, H, dk, dv)))
+    for b_ in range(B):
+        for h in range(H):
+            al, bb, gg = co["alpha"][b_, h], co["b"][b_, h], co["g"][b_, h]
+            K, V, Q, dO = k[b_, h], v[b_, h], q[b_, h], do[b_, h]
+            states = [np.zeros((dk, dv)) if S0 is None else S0[b_, h].copy()]
+            for t in range(T):  # all states (tests use short sequences)
+                S = states[-1]
+                y = S.T @ K[t]
+                states.append(gg[t] * (S - al[t] * np.outer(K[t], y)) + bb[t] * np.outer(K[t], V[t]))
+            dS = np.zeros((dk, dv)) if dSF is None else dSF[b_, h].copy()
+            dalpha, dbc, dlg = np.zeros(T), np.zeros(T), np.zeros(T)
+            for t in range(T - 1, -1, -1):
+                Sp, St = states[t], states[t + 1]
+                kt = K[t]
+                dS = dS + scale * np.outer(Q[t], dO[t])
+                out["dq"][b_, h, t] = scale * St @ dO[t]
+                y = Sp.T @ kt
+                dStk = dS.T @ kt
+                out["dv"][b_, h, t] = bb[t] * dStk
+                dbc[t] = kt @ dS @ V[t]
+                dg = np.sum(dS * Sp) - al[t] * (kt @ dS @ y)
+                dalpha[t] = -gg[t] * (kt @ dS @ y)
+                out["dk"][b_, h, t] = -gg[t] * al[t] * (dS @ y + Sp @ dStk) + bb[t] * (dS @ V[t])
+                dlg[t] = gg[t] * dg
+                dS = gg[t] * (dS - al[t] * np.outer(kt, dStk))
+            out["d_initial_state"][b_, h] = dS
+            out["dbeta"][b_, h] = dalpha * de["da_dbeta"][b_, h] + dbc * de["db_dbeta"][b_, h]
+            dlam = dalpha * de["da_dlam"][b_, h] + dbc * de["db_dlam"][b_, h]
+            out["dk"][b_, h] += 2.0 * K * dlam[:, None]
+            out["dgate"][b_, h] = dlg + dbc * de["db_da"][b_, h]
+    return out
+
+
+def gated_chunk_forward(q, k, v, beta, gate, scale=1.0, chunk=CHUNK, initial_state=None, mode="exact"):
     """Chunkwise gated form (dense batches), for tests of the chunk algebra the kernels use.
 
     Within a chunk with incoming state S, c_t = sum of a over the chunk's tokens up to t,
@@ -389,7 +455,7 @@ def gated_chunk_forward(q, k, v, beta, gate, scale=1.0, chunk=CHUNK, initial_sta
     q, k, v, beta, gate = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(gate)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
-    co = gated_coefficients(k, beta, gate)
+    co = gated_coefficients(k, beta, gate, mode)
     o = np.zeros((B, H, T, dv))
     Wf, Uf, Ut = np.zeros((B, H, T, dk)), np.zeros((B, H, T, dv)), np.zeros((B, H, T, dv))
     cum = np.zeros((B, H, T))
@@ -414,6 +480,103 @@ def gated_chunk_forward(q, k, v, beta, gate, scale=1.0, chunk=CHUNK, initial_sta
                 Wf[b, h, c0:c1], Uf[b, h, c0:c1], Ut[b, h, c0:c1], cum[b, h, c0:c1] = W, U, U_t, cc
             final[b, h] = S
     return dict(o=o, final=final, W=Wf, U=Uf, Ut=Ut, cum=cum)
+
+
+def gated_chunk_backward(q, k, v, beta, gate, do, scale=1.0, chunk=CHUNK, initial_state=None,
+                         d_final_state=None, mode="exact"):
+    """Chunkwise gated backward (dense batches): the reverse-mode form of gated_chunk_forward,
+    chunk by chunk, for tests of the algebra the kernels would use. Per chunk (c, Gamma = e^c,
+    G_C = e^{c_last}, D_ts = e^{c_t - c_s}, r = e^{c_last - c}, P = tril(Q K^T) * D) and the
+    gradient G of the outgoing state:
+      dU~ = scale P^T dO + diag(r) K G;   G_in = G_C G + scale Q^T diag(Gamma) dO - W^T dU~;
+      dP = scale tril(dO U~^T);  dQ = scale diag(Gamma) dO S^T + (dP * D) K;
+      dK = (dP * D)^T Q + diag(r) U~ G^T + T_w^T dW + (H + H^T) K + 2 K dlambda;
+      W = T_w K, T_w = X diag(alpha Gamma);  U = T_u V, T_u = X diag(b);
+      dT_w = -dU~ S^T K^T,  dT_u = dU~ V^T,  dX = dT_w diag(alpha Gamma) + dT_u diag(b),
+      dA = -X^T dX X^T (strictly lower),  H = (diag(alpha) dA) * D;
+    the log-decay gradient collects every e^{c} factor into dc and sums it backwards over the
+    chunk (c_t = sum_{s <= t} a_s). Returns the same dict as gated_backward."""
+    q, k, v, beta, gate, do = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(gate), _f64(do)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    co = gated_coefficients(k, beta, gate, mode)
+    de = gated_coefficient_derivatives(k, beta, gate, mode)
+    fw = gated_chunk_forward(q, k, v, beta, gate, scale, chunk, initial_state, mode)
+    S0 = _f64(initial_state)
+    dSF = _f64(d_final_state)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), dbeta=np.zeros_like(beta),
+               dgate=np.zeros_like(gate), d_initial_state=np.zeros((B, H, dk, dv)))
+    for b_ in range(B):
+        for h in range(H):
+            # incoming states of the chunks, recomputed from the forward's factors
+            starts = list(range(0, T, chunk))
+            S_in, S = [], (np.zeros((dk, dv)) if S0 is None else S0[b_, h].copy())
+            for c0 in starts:
+                c1 = min(T, c0 + chunk)
+                S_in.append(S)
+                cc = fw["cum"][b_, h, c0:c1]
+                S = np.exp(cc[-1]) * S + k[b_, h, c0:c1].T @ (np.exp(cc[-1] - cc)[:, None] * fw["Ut"][b_, h, c0:c1])
+            G = np.zeros((dk, dv)) if dSF is None else dSF[b_, h].copy()
+            for ci in range(len(starts) - 1, -1, -1):
+                c0 = starts[ci]
+                c1 = min(T, c0 + chunk)
+                n = c1 - c0
+                K, V, Q, dO = k[b_, h, c0:c1], v[b_, h, c0:c1], q[b_, h, c0:c1], do[b_, h, c0:c1]
+                al, bb = co["alpha"][b_, h, c0:c1], co["b"][b_, h, c0:c1]
+                Sc = S_in[ci]
+                cc = np.cumsum(gate[b_, h, c0:c1])
+                Gm = np.exp(cc)
+                GC = np.exp(cc[-1])
+                D = np.exp(np.tril(cc[:, None] - cc[None, :])) * np.tril(np.ones((n, n)))
+                r = np.exp(cc[-1] - cc)
+                A = np.tril(al[:, None] * D * (K @ K.T), -1)
+                X = np.linalg.inv(np.eye(n) + A)
+                Tw = X * (al * Gm)[None, :]
+                Tu = X * bb[None, :]
+                W = Tw @ K
+                Ut = Tu @ V - W @ Sc
+                P = np.tril(Q @ K.T) * D
+                dUt = scale * P.T @ dO + r[:, None] * (K @ G)
+                G_in = GC * G + scale * Q.T @ (Gm[:, None] * dO) - W.T @ dUt
+                dP = scale * np.tril(dO @ Ut.T)
+                dQs = scale * Gm[:, None] * (dO @ Sc.T)
+                dQ = dQs + (dP * D) @ K
+                dK = (dP * D).T @ Q + r[:, None] * (Ut @ G.T)
+                dc = np.zeros(n)
+                dc += np.sum(dQs * Q, axis=1)
+                E = dP * P
+                dc += E.sum(axis=1)
+                dc -= E.sum(axis=0)
+                dr = np.sum((K @ G) * Ut, axis=1)
+                dc -= r * dr
+                dc[-1] += np.sum(r * dr) + GC * np.sum(G * Sc)
+                dW = -dUt @ Sc.T
+                dTw = dW @ K.T
+                dK += Tw.T @ dW
+                dTu = dUt @ V.T
+                dV = Tu.T @ dUt
+                daG = np.sum(dTw * X, axis=0)           # d(alpha Gamma)_j
+                db = np.sum(dTu * X, axis=0)
+                dX = dTw * (al * Gm)[None, :] + dTu * bb[None, :]
+                dA = np.tril(-X.T @ dX @ X.T, -1)
+                dal = daG * Gm
+                dc += daG * al * Gm
+                dal += np.sum(dA * (K @ K.T) * D, axis=1)
+                Hm = (al[:, None] * dA) * D
+                dK += (Hm + Hm.T) @ K
+                F = dA * A
+                dc += F.sum(axis=1)
+                dc -= F.sum(axis=0)
+                dg = np.cumsum(dc[::-1])[::-1]           # c_t = sum_{s<=t} a_s
+                out["dq"][b_, h, c0:c1] = dQ
+                dlam = dal * de["da_dlam"][b_, h, c0:c1] + db * de["db_dlam"][b_, h, c0:c1]
+                out["dk"][b_, h, c0:c1] = dK + 2.0 * K * dlam[:, None]
+                out["dv"][b_, h, c0:c1] = dV
+                out["dbeta"][b_, h, c0:c1] = dal * de["da_dbeta"][b_, h, c0:c1] + db * de["db_dbeta"][b_, h, c0:c1]
+                out["dgate"][b_, h, c0:c1] = dg + db * de["db_da"][b_, h, c0:c1]
+                G = G_in
+            out["d_initial_state"][b_, h] = G
+    return out
 
 
 def rel_err(x, ref):

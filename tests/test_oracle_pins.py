@@ -576,3 +576,48 @@ def test_gated_chunk_form_equals_token_recurrence():
     # a wrong decay on the output's state term (Gamma_{t-1} instead of Gamma_t) is caught
     ob = O.gated_chunk_forward(q, k, v, beta, np.roll(a, 1, axis=-1), scale=0.9, initial_state=S0)
     assert O.rel_err(ob["o"], o) > 1e-3
+
+
+@pytest.mark.parametrize("mode", ["exact", "euler"])
+def test_gated_backward_against_central_differences(mode):
+    """Every coordinate of every input of gated EFLA (q, k, v, beta, gate, initial state) by
+    central differences of sum(o * do) + <final state, d_final>, T = 11 (d_k = 4, d_v = 3)."""
+    r = _rng(150)
+    B, H, T, dk, dv = 1, 1, 11, 4, 3
+    q, k, v = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk)) * 0.8, r.standard_normal((B, H, T, dv))
+    beta, gate = r.uniform(0.1, 1.0, (B, H, T)), -r.uniform(0.05, 1.5, (B, H, T))
+    S0, do, dF = r.standard_normal((B, H, dk, dv)), r.standard_normal((B, H, T, dv)), r.standard_normal((B, H, dk, dv))
+
+    def loss(q_, k_, v_, b_, g_, s_):
+        o, f = O.gated_forward(q_, k_, v_, b_, g_, scale=0.7, initial_state=s_, mode=mode)
+        return np.sum(o * do) + np.sum(f * dF)
+
+    g = O.gated_backward(q, k, v, beta, gate, do, scale=0.7, initial_state=S0, d_final_state=dF, mode=mode)
+    args = [q, k, v, beta, gate, S0]
+    names = ["dq", "dk", "dv", "dbeta", "dgate", "d_initial_state"]
+    eps = 1e-6
+    for i, (x, nm) in enumerate(zip(args, names)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = [a.copy() for a in args], [a.copy() for a in args]
+            xp[i][idx] += eps
+            xm[i][idx] -= eps
+            num[idx] = (loss(*xp) - loss(*xm)) / (2 * eps)
+        assert np.max(np.abs(num - g[nm])) < 1e-7 * max(1.0, np.max(np.abs(num))), (nm, np.max(np.abs(num - g[nm])))
+
+
+@pytest.mark.parametrize("mode", ["exact", "euler"])
+def test_gated_chunk_backward_equals_token_backward(mode):
+    """The chunkwise gated backward (decayed UT factors, running log-decay sums) equals the
+    hand-written token backward (itself pinned by central differences), ragged tail included."""
+    r = _rng(160)
+    B, H, T, dk, dv = 1, 2, 64 * 2 + 21, 6, 5
+    q, k, v = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk)) * 0.6, r.standard_normal((B, H, T, dv))
+    beta, a = r.uniform(0, 1, (B, H, T)), -r.uniform(0, 1.5, (B, H, T))
+    do, S0, dF = r.standard_normal((B, H, T, dv)), r.standard_normal((B, H, dk, dv)), r.standard_normal((B, H, dk, dv))
+    g1 = O.gated_backward(q, k, v, beta, a, do, 0.8, S0, dF, mode=mode)
+    g2 = O.gated_chunk_backward(q, k, v, beta, a, do, 0.8, initial_state=S0, d_final_state=dF, mode=mode)
+    for n in g1:
+        assert O.rel_err(g2[n], g1[n]) < 1e-12, n
