@@ -268,7 +268,7 @@ def main():
     gate = torch.from_numpy(-np.logaddexp(0.0, -(np.random.default_rng(5).standard_normal((B, H, T)) + 3.0))
                             .astype(np.float32)).to(dev, torch.bfloat16)
     gated = {}
-    for key, f in (("gated", lambda: E.efla_fwd_gated(q, k, v, beta, gate, 1.0, None, ws, o=o)),
+    for key, f in (("gated", lambda: E.efla_fwd_gated(q, k, v, beta, gate, 1.0, None, False, ws, o=o)),
                    ("ungated", lambda: E.efla_fwd(q, k, v, beta, 1.0, None, False, ws, o=o))):
         for _ in range(args.warmup):
             f()

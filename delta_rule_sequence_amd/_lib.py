@@ -24,6 +24,7 @@ STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_NULL", 2: "EFLA_ERR_SHAPE", 3: "EFLA_ERR_DT
 EXPORTS = ["efla_abi_version", "efla_status_str", "efla_check_problem", "efla_workspace_bytes",
            "efla_saved_bytes", "efla_get_saved_layout", "efla_prep", "efla_chunk_ut",
            "efla_fwd", "efla_fwd_state", "efla_fwd_gated", "efla_bwd", "efla_bwd_state",
+           "efla_bwd_gated",
            "efla_decode", "efla_decode_gated",
            "efla_profile_enable", "efla_profile_read", "efla_profile_reset"]
 
@@ -39,7 +40,7 @@ class EflaProblem(ctypes.Structure):
 class EflaSavedLayout(ctypes.Structure):
     _fields_ = [("w", ctypes.c_size_t), ("ut", ctypes.c_size_t), ("states", ctypes.c_size_t),
                 ("table", ctypes.c_size_t), ("m", ctypes.c_size_t), ("x", ctypes.c_size_t),
-                ("total", ctypes.c_size_t),
+                ("cum", ctypes.c_size_t), ("total", ctypes.c_size_t),
                 ("n_chunk_slots", ctypes.c_int64)]
 
 
@@ -92,7 +93,10 @@ def lib():
     L.efla_decode.restype = st
     L.efla_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.efla_fwd_gated.restype = st
-    L.efla_fwd_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.efla_fwd_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.efla_bwd_gated.restype = st
+    L.efla_bwd_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
+                                 vp, sz, vp]
     L.efla_decode_gated.restype = st
     L.efla_decode_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.efla_profile_enable.restype = st

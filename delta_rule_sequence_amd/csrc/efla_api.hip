@@ -185,7 +185,7 @@ size_t bytes_cum(const Shape& s) { return (size_t)s.slots * s.H * kChunk * 4; }
 
 // Layout of the forward->backward buffer.
 struct Saved {
-  size_t w, ut, states, table, m, x, total;
+  size_t w, ut, states, table, m, x, cum, total;
 };
 Saved saved_layout(const Shape& s) {
   Saved L;
@@ -202,6 +202,8 @@ Saved saved_layout(const Shape& s) {
   o += align_up(bytes_m(s));
   L.x = o;
   o += align_up(bytes_x(s));
+  L.cum = o;
+  o += align_up(bytes_cum(s));
   L.total = o;
   return L;
 }
@@ -307,6 +309,7 @@ efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out)
   out->table = L.table;
   out->m = L.m;
   out->x = L.x;
+  out->cum = L.cum;
   out->total = L.total;
   out->n_chunk_slots = s.slots;
   return EFLA_OK;
@@ -380,35 +383,49 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
 
 efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,
                            const void* beta, const void* gate, const float* h0, void* o,
-                           float* ht, void* ws, size_t ws_bytes, void* stream) {
+                           float* ht, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                           void* stream) {
   Shape s;
   if (efla_status r = to_shape(p, s)) return r;
   if (s.dt != Dt::BF16) return EFLA_ERR_UNSUPPORTED;
   if (empty(s)) return EFLA_OK;
   if (!q || !k || !v || !beta || !gate || !o || !ws) return EFLA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(ws) ||
-      !aligned16(h0) || !aligned16(ht))
+      !aligned16(saved) || !aligned16(h0) || !aligned16(ht))
     return EFLA_ERR_ALIGN;
   if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
+  const Saved L = saved_layout(s);
+  if (saved && saved_bytes < L.total) return EFLA_ERR_WORKSPACE;
   unsigned char* wsb = (unsigned char*)ws;
   unsigned char* u = wsb;
   unsigned char* w_ws = wsb + align_up(bytes_v(s));
   int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
   unsigned char* m_ws = (unsigned char*)table_ws + align_up(bytes_table(s));
   unsigned char* seg_ws = m_ws + align_up(bytes_m(s));
-  float* cum = (float*)(seg_ws + bytes_seg(s));
-  return run_forward(s, q, k, v, beta, o, w_ws, nullptr, nullptr, table_ws, m_ws, nullptr, u, h0,
-                     ht, seg_ws, (hipStream_t)stream, gate, cum);
+  float* cum_ws = (float*)(seg_ws + bytes_seg(s));
+  unsigned char* sv = (unsigned char*)saved;
+  return run_forward(s, q, k, v, beta, o, sv ? sv + L.w : w_ws, sv ? sv + L.ut : nullptr,
+                     sv ? sv + L.states : nullptr, sv ? (int*)(sv + L.table) : table_ws,
+                     sv ? sv + L.m : m_ws, sv ? sv + L.x : nullptr, u, h0, ht, seg_ws,
+                     (hipStream_t)stream, gate, sv ? (float*)(sv + L.cum) : cum_ws);
 }
 
-efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
-                           const void* beta, const float* h0, const void* d_o, const float* dht,
-                           const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
-                           void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace efla {
+namespace {
+// Backward shared by efla_bwd_state and efla_bwd_gated (gate != NULL: gated EFLA, then dgate).
+efla_status run_backward(const efla_problem* p, const void* q, const void* k, const void* v,
+                         const void* beta, const void* gate, const float* h0, const void* d_o,
+                         const float* dht, const void* saved, size_t saved_bytes, void* dq,
+                         void* dk, void* dv, void* dbeta, void* dgate, float* dh0, void* ws,
+                         size_t ws_bytes, void* stream) {
   Shape s;
   if (efla_status r = to_shape(p, s)) return r;
+  if (gate && s.dt != Dt::BF16) return EFLA_ERR_UNSUPPORTED;
   if (empty(s)) return EFLA_OK;
   if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta || !ws) return EFLA_ERR_NULL;
+  if (gate && !dgate) return EFLA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned16(ws) || !aligned16(saved) || !aligned16(h0) ||
       !aligned16(dht) || !aligned16(dh0))
@@ -428,16 +445,40 @@ efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, 
     unsigned char* seg = u + align_up(bytes_v(s));
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
                                     rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
-                                    u, h0, nullptr, seg, st))
+                                    u, h0, nullptr, seg, st, gate, (float*)(rec + L.cum)))
       return r;
     sv = rec;
   }
   const int* table = (const int*)(sv + L.table);
+  const float* cum = gate ? (const float*)(sv + L.cum) : nullptr;
   if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o, dut,
-                                                 dstates, dht, dh0, st)))
+                                                 dstates, dht, dh0, st, cum)))
     return r;
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
-                                     dstates, sv + L.x, dq, dk, dv, dbeta, st));
+                                     dstates, sv + L.x, dq, dk, dv, dbeta, st, gate, cum,
+                                     gate ? sv + L.m : nullptr, dgate));
+}
+}  // namespace
+}  // namespace efla
+
+extern "C" {
+
+efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const float* h0, const void* d_o, const float* dht,
+                           const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
+                           void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+  return run_backward(p, q, k, v, beta, nullptr, h0, d_o, dht, saved, saved_bytes, dq, dk, dv,
+                      dbeta, nullptr, dh0, ws, ws_bytes, stream);
+}
+
+efla_status efla_bwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const void* gate, const float* h0, const void* d_o,
+                           const float* dht, const void* saved, size_t saved_bytes, void* dq,
+                           void* dk, void* dv, void* dbeta, void* dgate, float* dh0, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!gate) return EFLA_ERR_NULL;
+  return run_backward(p, q, k, v, beta, gate, h0, d_o, dht, saved, saved_bytes, dq, dk, dv, dbeta,
+                      dgate, dh0, ws, ws_bytes, stream);
 }
 
 efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,

@@ -26,6 +26,14 @@
 //   1 loads land; 2 dW, scale dO S^T, U~ G^T, dM, coefficients;
 //   3 dT (-> dalpha, dX), T^T dU, T^T dW, dM K, dM^T Q;
 //   4 Y = dX X^T;  5 dA = -X^T Y (-> dalpha, H);  6 H K and the outputs.
+//
+// Gated EFLA (GT): with c the running log-decay sums of the chunk (saved by the forward),
+// Gamma = e^c, r = e^{c_last - c}, D_ts = e^{c_t - c_s} and P = tril(Q K^T) * D (saved in place
+// of M): dQ's state part is scale diag(Gamma) dO S^T, dK's is diag(r) U~ G^T, dM becomes
+// dP * D, the UT factors are T_w = X diag(alpha Gamma) and T_u = X diag(b) (dT split into
+// dW K^T and dU V^T), A carries D. Every e^c factor also adds to the log-decay gradient dc
+// (accumulated per token in LDS), which a reverse running sum over the chunk turns into the
+// gate gradient, plus db db/da.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -33,7 +41,7 @@ namespace efla {
 constexpr int kBwdThreads = 512;
 constexpr int kBwdWaves = kBwdThreads / 64;
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool GT = false>
 struct ChunkBwdLds {
   static constexpr int LK = pitch<E>(DK), LV = pitch<E>(DV), LT = pitch<E>(64);
   static constexpr size_t TK = 64 * LK * sizeof(E), TV = 64 * LV * sizeof(E),
@@ -49,7 +57,13 @@ struct ChunkBwdLds {
   static constexpr size_t oM = oX + TT;          // dM  [64][LT]
   static constexpr size_t oC = oM + TT;          // lambda, alpha, e^-x, dalpha/dlam [64]
   static constexpr size_t oP = oC + 4 * 64 * 4;  // dalpha partials [64][8]
-  static constexpr size_t bytes = oP + 8 * 64 * 4;
+  // gated only: P [64][LT]; c, b, db/dbeta, db/dlam, db/da [64]; dc [64] + two scalars;
+  // db column-sum partials [64][4]
+  static constexpr size_t oPg = oP + 8 * 64 * 4;
+  static constexpr size_t oGc = oPg + TT;
+  static constexpr size_t oDc = oGc + 5 * 64 * 4;
+  static constexpr size_t oDb = oDc + 80 * 4;
+  static constexpr size_t bytes = GT ? oDb + 4 * 64 * 4 : oP + 8 * 64 * 4;
   static_assert(TT <= TV, "64x64 work tiles reuse d_v-wide regions");
 };
 
@@ -100,14 +114,15 @@ EFLA_DEV f32x4 tri_mask_row(f32x4 c, int rb, int nb, bool keep_diag, int lane) {
   return c;
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool GT>
 __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ beta, const E* __restrict__ d_o, const E* __restrict__ ut,
     const E* __restrict__ dut, const E* __restrict__ states, const E* __restrict__ dstates,
     const E* __restrict__ xsav, E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
-    E* __restrict__ dbeta) {
-  typedef ChunkBwdLds<E, DK, DV> L;
+    E* __restrict__ dbeta, const E* __restrict__ gate, const float* __restrict__ cum,
+    const E* __restrict__ psav, E* __restrict__ dgate) {
+  typedef ChunkBwdLds<E, DK, DV, GT> L;
   typedef typename Mma<E>::vec Vv;
   constexpr int LK = L::LK, LV = L::LV, LT = L::LT;
   constexpr int KC = Mma<E>::KC, KSV = DV / KC;
@@ -132,6 +147,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // dalpha partials [64][8]: slots 0-3 column sums of dT . X per row block, slots 4-7 row
   // sums of dA . KK^T per column block (one token's eight partials are one 32-byte row).
   float* pDa = (float*)(smem + L::oP);
+  E* sPg = (E*)(smem + L::oPg);            // gated: P
+  float* cC = (float*)(smem + L::oGc);     // gated: c, b, db/dbeta, db/dlam, db/da
+  float* cB = cC + 64;
+  float* cBb = cC + 128;
+  float* cBl = cC + 192;
+  float* cBa = cC + 256;
+  float* sDc = (float*)(smem + L::oDc);    // gated: dc per token; [64] c_last term; [65] <G, S>
+  float* pDb = (float*)(smem + L::oDb);    // gated: db partials [64][4]
 
   int tid = threadIdx.x, lane = tid & 63;
   const int wv0 = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -142,15 +165,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
 
   TileRegs<E, DK> tK, tQ;
   TileRegs<E, DV> tDU, tDO, tU, tV;
-  TileRegs<E, 64> tX;
+  TileRegs<E, 64> tX, tP;
   Vv fS[CK][KSV], fG[CK][KSV];  // rows of S and G for this wave's d_k columns (B^T operands)
-  float bt;
+  float bt, cR = 0.f, aR = 0.f;  // beta, and (gated) c and log-decay of token lane
   // Requests for a chunk's inputs, issued for the next chunk in small groups spread over
   // the steps of the current one: a large burst would stall the issuing waves until the
   // memory system had taken all of it.
   auto issue_k = [&](const ChunkUnit& c) {
     tK.load(k + c.row0 * DK, c.n, tid);
     bt = to_f(beta[c.row0 + min(lane, c.n - 1)]);
+    if constexpr (GT) {
+      cR = cum[c.sh * kChunk + lane];
+      aR = to_f(gate[c.row0 + min(lane, c.n - 1)]);
+    }
   };
   auto issue_du_do = [&](const ChunkUnit& c) {
     tDU.load(dut + c.row0 * DV, c.n, tid);
@@ -160,6 +187,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   auto issue_v_x = [&](const ChunkUnit& c) {
     tV.load(v + c.row0 * DV, c.n, tid);
     tX.load(xsav + c.sh * 64 * 64, 64, tid);
+    if constexpr (GT) tP.load(psav + c.sh * 64 * 64, 64, tid);
   };
   auto issue_q = [&](const ChunkUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
   auto issue_s = [&](const ChunkUnit& c, int cK) {
@@ -218,7 +246,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       if (i % TKr::VPR == 0) cLam[i / TKr::VPR] = i / TKr::VPR < n ? acc : 0.f;
     }
   }
-  const float bt_cur = bt;
+  const float bt_cur = bt, a_cur = aR;
+  if constexpr (GT) {
+    tP.store(sPg, LT, 64, tid);
+    if (tid < 64) {
+      cC[tid] = cR;
+      sDc[tid] = 0.f;
+    }
+    if (tid == 0) sDc[64] = sDc[65] = 0.f;
+  }
   tDU.store(sDU, LV, n, tid);
   tDO.store(sDO, LV, n, tid);
   tU.store(sU, LV, n, tid);
@@ -266,47 +302,134 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
         aQ[i][j] *= g.scale;
       }
   }
+  if constexpr (GT) {
+    // dQ's state part scale diag(Gamma) dO S^T adds its row dot with Q to dc; dK's state part
+    // diag(r) U~ G^T: with dr_t = k_t . (U~ G^T)_t, dc_t -= r_t dr_t and dc_last += r_t dr_t.
+    const float cl = cC[n - 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * (rb0 + i) + (lane & 15);
+      const float ct = cC[t], gm = expf(ct), rr = expf(fminf(cl - ct, 0.f));
+      float p1 = 0.f, p2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < CK; ++j) {
+        const int col = 16 * (cK + j) + 4 * (lane >> 4);
+        const f32x4 qv = ld4f<E>(sQ + t * LK + col), kv = ld4f<E>(sK + t * LK + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          aQ[i][j][e] *= gm;
+          p1 = fmaf(aQ[i][j][e], qv[e], p1);
+          p2 = fmaf(aK[i][j][e], kv[e], p2);
+          aK[i][j][e] *= rr;
+        }
+      }
+      p1 += __shfl_xor(p1, 16);
+      p1 += __shfl_xor(p1, 32);
+      p2 += __shfl_xor(p2, 16);
+      p2 += __shfl_xor(p2, 32);
+      if (lane < 16) {
+        atomicAdd(&sDc[t], p1 - rr * p2);
+        atomicAdd(&sDc[64], rr * p2);
+      }
+    }
+    // dc_last += e^{c_last} <G, S>: waves 0-3 hold every row of S and G once
+    if (wv < 4) {
+      float gs = 0.f;
+#pragma unroll
+      for (int j = 0; j < CK; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks)
+#pragma unroll
+          for (int e = 0; e < 16 / (int)sizeof(E); ++e) gs = fmaf(to_f(fS[j][ks][e]), to_f(fG[j][ks][e]), gs);
+      gs = group_sum<16>(gs);
+      gs += __shfl_xor(gs, 16);
+      gs += __shfl_xor(gs, 32);
+      if (lane == 0) atomicAdd(&sDc[65], gs);
+    }
+  }
   {
     f32x4 m[1][2] = {{zero4(), zero4()}};
     if (plow) mma_blk<E, false, false, 1, 2, DV, true>(sDO + 16 * pr * LV, LV, sU + 16 * pn * LV, LV, 0, DV, m, lane);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      st_frag_t<E>(sM + 16 * pr * LT + 16 * (pn + j), LT,
-                   tri_mask_row(m[0][j], pr, pn + j, true, lane) * g.scale, lane);
+    for (int j = 0; j < 2; ++j) {
+      f32x4 mm = tri_mask_row(m[0][j], pr, pn + j, true, lane) * g.scale;
+      if constexpr (GT) {  // dP * P adds to dc (rows +, columns -); then dM = dP * D
+        const int t = 16 * pr + (lane & 15), s0 = 16 * (pn + j) + 4 * (lane >> 4);
+        const f32x4 pv = ld4f<E>(sPg + t * LT + s0);
+        const float ct = cC[t];
+        float rsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ev = mm[e] * pv[e];
+          rsum += ev;
+          const float csum = group_sum<16>(ev);
+          if ((lane & 15) == 0) atomicAdd(&sDc[s0 + e], -csum);
+          mm[e] *= expf(fminf(ct - cC[s0 + e], 0.f));
+        }
+        rsum += __shfl_xor(rsum, 16);
+        rsum += __shfl_xor(rsum, 32);
+        if (lane < 16) atomicAdd(&sDc[t], rsum);
+      }
+      st_frag_t<E>(sM + 16 * pr * LT + 16 * (pn + j), LT, mm, lane);
+    }
   }
   if (tid < 64) {
     const FlowCoef cf = flow_coef(tid < n ? bt_cur : 0.f, cLam[tid], g.euler);
     cAl[tid] = cf.alpha;
     cEx[tid] = cf.ex;
     cDl[tid] = cf.dlam;
+    if constexpr (GT) {
+      const GatedCoef gc = gated_coef(tid < n ? bt_cur : 0.f, cLam[tid], a_cur, g.euler);
+      cB[tid] = tid < n ? gc.b : 0.f;
+      cBb[tid] = gc.db_dbeta;
+      cBl[tid] = gc.db_dlam;
+      cBa[tid] = gc.db_da;
+    }
   }
   __syncthreads();
   if (more) issue_du_do(nxt);
 
   // ---- 3: dT = dW K^T + dU V^T -> dalpha (columns) and dX = dT diag(alpha) (strictly lower);
   //         dV = T^T dU, dK += T^T dW (T^T = diag(alpha) X^T); dQ += dM K; dK += dM^T Q
+  //         (gated: dT_w = dW K^T and dT_u = dU V^T apart; dX = dT_w diag(alpha Gamma) +
+  //         dT_u diag(b); column sums of dT_w . X give d(alpha Gamma), of dT_u . X give db)
   {
-    f32x4 t[1][2] = {{zero4(), zero4()}};
+    f32x4 t[1][2] = {{zero4(), zero4()}}, tu[1][2] = {{zero4(), zero4()}};
     if (plow) {
       mma_blk<E, false, false, 1, 2, DK>(sW + 16 * pr * LK, LK, sK + 16 * pn * LK, LK, 0, DK, t, lane);
-      mma_blk<E, false, false, 1, 2, DV>(sDU + 16 * pr * LV, LV, sV + 16 * pn * LV, LV, 0, DV, t, lane);
+      if constexpr (GT)
+        mma_blk<E, false, false, 1, 2, DV>(sDU + 16 * pr * LV, LV, sV + 16 * pn * LV, LV, 0, DV, tu, lane);
+      else
+        mma_blk<E, false, false, 1, 2, DV>(sDU + 16 * pr * LV, LV, sV + 16 * pn * LV, LV, 0, DV, t, lane);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if (pn + j > pr) t[0][j] = zero4();
+      if (pn + j > pr) t[0][j] = tu[0][j] = zero4();
       const int col = 16 * (pn + j) + (lane & 15);
       const float al = cAl[col];
-      float cs = 0.f;
+      const float gmc = GT ? expf(cC[col]) : 1.f, bc = GT ? cB[col] : 0.f;
+      float cs = 0.f, cb = 0.f;
       f32x4 dx;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * pr + 4 * (lane >> 4) + i;
-        cs = fmaf(t[0][j][i], to_f(sX[row * LT + col]), cs);  // X is zero above the diagonal
-        dx[i] = row > col ? t[0][j][i] * al : 0.f;
+        const float xv = to_f(sX[row * LT + col]);  // X is zero above the diagonal
+        cs = fmaf(t[0][j][i], xv, cs);
+        if constexpr (GT) {
+          cb = fmaf(tu[0][j][i], xv, cb);
+          dx[i] = row > col ? t[0][j][i] * (al * gmc) + tu[0][j][i] * bc : 0.f;
+        } else {
+          dx[i] = row > col ? t[0][j][i] * al : 0.f;
+        }
       }
       cs += __shfl_xor(cs, 16);
       cs += __shfl_xor(cs, 32);
-      if (lane < 16) pDa[col * 8 + pr] = cs;
+      if (lane < 16) pDa[col * 8 + pr] = cs * gmc;  // dalpha part: d(alpha Gamma) Gamma
+      if constexpr (GT) {
+        cb += __shfl_xor(cb, 16);
+        cb += __shfl_xor(cb, 32);
+        if (lane < 16) pDb[col * 4 + pr] = cb;
+      }
       st_frag_lds<E>(sDX + 16 * pr * LT + 16 * (pn + j), LT, dx, lane);
     }
   }
@@ -342,13 +465,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float al = cAl[16 * (rb0 + i) + (lane & 15)];
+      const int row = 16 * (rb0 + i) + (lane & 15);
+      const float al = cAl[row];
+      // gated: T_u^T = diag(b) X^T, T_w^T = diag(alpha Gamma) X^T
+      const float fu = GT ? cB[row] : al, fw = GT ? al * expf(cC[row]) : al;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
-        for (int j = 0; j < CV; ++j) aV[i][j][e] *= al;
+        for (int j = 0; j < CV; ++j) aV[i][j][e] *= fu;
 #pragma unroll
-        for (int j = 0; j < CK; ++j) aK[i][j][e] = fmaf(al, tw[i][j][e], aK[i][j][e]);
+        for (int j = 0; j < CK; ++j) aK[i][j][e] = fmaf(fw, tw[i][j][e], aK[i][j][e]);
       }
     }
   }
@@ -405,14 +531,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
         continue;
       }
       const int col = 16 * nb + (lane & 15);
-      float rs[4];
+      float rs[4], fc = 0.f;
       f32x4 dg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * pr + 4 * (lane >> 4) + i;
-        const float a = row > col ? -da[0][j][i] : 0.f;
+        float a = row > col ? -da[0][j][i] : 0.f;
+        if constexpr (GT) a *= expf(fminf(cC[row] - cC[col], 0.f));  // A carries D
         rs[i] = a * kk[0][j][i];
         dg[i] = a * cAl[row];
+        if constexpr (GT) fc = fmaf(cAl[row], rs[i], fc);  // dA . A, column part
+      }
+      if constexpr (GT) {  // dc_s -= sum_t dA_ts A_ts (the row part enters as alpha dalpha)
+        fc += __shfl_xor(fc, 16);
+        fc += __shfl_xor(fc, 32);
+        if (lane < 16) atomicAdd(&sDc[col], -fc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[i] = group_sum<16>(rs[i]);
@@ -449,10 +582,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     const f32x4 a = *(const f32x4*)(pDa + 8 * t), b = *(const f32x4*)(pDa + 8 * t + 4);
     return ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
   };
+  auto dbsum = [&](int t) {
+    const f32x4 a = *(const f32x4*)(pDb + 4 * t);
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * (rb0 + i) + (lane & 15);
-    const float f = 2.f * dalpha(row) * cDl[row];
+    float f = 2.f * dalpha(row) * cDl[row];
+    if constexpr (GT) f = fmaf(2.f * dbsum(row), cBl[row], f);
 #pragma unroll
     for (int j = 0; j < CK; ++j) {
       const f32x4 kv = ld4f<E>(sK + row * LK + 16 * (cK + j) + 4 * (lane >> 4));
@@ -461,7 +599,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       st_frag_t<E>(sW + 16 * (rb0 + i) * LK + 16 * (cK + j), LK, aK[i][j], lane);
     }
   }
-  if (tid < n) dbeta[row0 + tid] = to_e<E>(dalpha(tid) * cEx[tid]);
+  if constexpr (GT) {
+    if (tid < 64) {
+      // dbeta and the gate gradient: dc_t gains alpha_t dalpha_t (the e^{c} in T_w and the row
+      // part of dA . A); the last token carries the chunk-end factors; then
+      // dgate_t = sum_{s >= t} dc_s + db_t db_t/da_t.
+      const float da_t = dalpha(tid), db_t = dbsum(tid);
+      if (tid < n) dbeta[row0 + tid] = to_e<E>(da_t * cEx[tid] + db_t * cBb[tid]);
+      float dc = tid < n ? fmaf(cAl[tid], da_t, sDc[tid]) : 0.f;
+      if (tid == n - 1) dc += sDc[64] + expf(cC[tid]) * sDc[65];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_down(dc, o);
+        if (tid + o < 64) dc += y;
+      }
+      if (tid < n) dgate[row0 + tid] = to_e<E>(fmaf(db_t, cBa[tid], dc));
+    }
+  } else {
+    if (tid < n) dbeta[row0 + tid] = to_e<E>(dalpha(tid) * cEx[tid]);
+  }
   __syncthreads();
   s2g<E, DK, kBwdThreads>(dk + row0 * DK, DK, sW, LK, n, tid);
   if (!more) break;
@@ -471,16 +627,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   }
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool GT>
 static hipError_t chunk_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
                                const void* v, const void* beta, const void* d_o, const void* ut,
                                const void* dut, const void* states, const void* dstates,
                                const void* x, void* dq, void* dk, void* dv, void* dbeta,
+                               const void* gate, const float* cum, const void* m, void* dgate,
                                hipStream_t st) {
-  typedef ChunkBwdLds<E, DK, DV> L;
+  typedef ChunkBwdLds<E, DK, DV, GT> L;
+  static_assert(L::bytes <= 160 * 1024, "LDS budget");
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_bwd_kernel<E, DK, DV>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_bwd_kernel<E, DK, DV, GT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -490,13 +648,13 @@ static hipError_t chunk_bwd_go(const Shape& s, const int* table, const void* q, 
   if (units < 1) return hipSuccess;
   const int64_t blocks = units < cu_count() ? units : cu_count();
   prof_begin(st);
-  hipLaunchKernelGGL((chunk_bwd_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(kBwdThreads),
+  hipLaunchKernelGGL((chunk_bwd_kernel<E, DK, DV, GT>), dim3((unsigned)blocks), dim3(kBwdThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
                      (const E*)beta, (const E*)d_o, (const E*)ut, (const E*)dut,
                      (const E*)states, (const E*)dstates, (const E*)x, (E*)dq, (E*)dk, (E*)dv,
-                     (E*)dbeta);
+                     (E*)dbeta, (const E*)gate, cum, (const E*)m, (E*)dgate);
   hipError_t e = hipGetLastError();
-  prof_end("chunk_bwd", st);
+  prof_end(GT ? "chunk_bwd_gated" : "chunk_bwd", st);
   return e;
 }
 
@@ -516,17 +674,25 @@ hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, con
                             const void* v, const void* beta, const void* d_o, const void* ut,
                             const void* dut, const void* states, const void* dstates,
                             const void* x, void* dq, void* dk, void* dv, void* dbeta,
-                            hipStream_t st) {
-#define EFLA_CB(E_, DK_, DV_)                                                                   \
-  return chunk_bwd_go<E_, DK_, DV_>(s, table, q, k, v, beta, d_o, ut, dut, states, dstates, x, \
-                                    dq, dk, dv, dbeta, st)
+                            hipStream_t st, const void* gate, const float* cum, const void* m,
+                            void* dgate) {
+#define EFLA_CB(E_, DK_, DV_, GT_)                                                              \
+  return chunk_bwd_go<E_, DK_, DV_, GT_>(s, table, q, k, v, beta, d_o, ut, dut, states, dstates, \
+                                         x, dq, dk, dv, dbeta, gate, cum, m, dgate, st)
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) EFLA_CB(__bf16, 64, 64);
-    if (s.dk == 64 && s.dv == 128) EFLA_CB(__bf16, 64, 128);
-    if (s.dk == 128 && s.dv == 64) EFLA_CB(__bf16, 128, 64);
-    EFLA_CB(__bf16, 128, 128);
+    if (gate) {
+      if (s.dk == 64 && s.dv == 64) EFLA_CB(__bf16, 64, 64, true);
+      if (s.dk == 64 && s.dv == 128) EFLA_CB(__bf16, 64, 128, true);
+      if (s.dk == 128 && s.dv == 64) EFLA_CB(__bf16, 128, 64, true);
+      EFLA_CB(__bf16, 128, 128, true);
+    }
+    if (s.dk == 64 && s.dv == 64) EFLA_CB(__bf16, 64, 64, false);
+    if (s.dk == 64 && s.dv == 128) EFLA_CB(__bf16, 64, 128, false);
+    if (s.dk == 128 && s.dv == 64) EFLA_CB(__bf16, 128, 64, false);
+    EFLA_CB(__bf16, 128, 128, false);
   }
-  EFLA_CB(float, 64, 64);
+  if (gate) return hipErrorInvalidValue;  // gated EFLA is built for bf16 only
+  EFLA_CB(float, 64, 64, false);
 #undef EFLA_CB
 }
 

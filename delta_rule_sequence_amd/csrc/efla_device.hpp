@@ -558,12 +558,45 @@ EFLA_DEV float phi_f(float x) {
   return -expm1f(-x) / x;
 }
 
+// phi'(x) = (e^{-x} (1 + x) - 1) / x^2 (phi'(0) = -1/2): Taylor polynomial for |x| < 1
+// (the closed form cancels there), else the closed form.
+EFLA_DEV float dphi_f(float x) {
+  if (fabsf(x) < 1.0f) {
+    // phi'(x) = sum_{n>=0} (n+1) (-1)^(n+1) x^n / (n+2)!
+    float d = 1.0f / 518918400.0f;
+    d = fmaf(d, x, -1.0f / 43545600.0f);
+    d = fmaf(d, x, 1.0f / 3991680.0f);
+    d = fmaf(d, x, -1.0f / 403200.0f);
+    d = fmaf(d, x, 1.0f / 45360.0f);
+    d = fmaf(d, x, -1.0f / 5760.0f);
+    d = fmaf(d, x, 1.0f / 840.0f);
+    d = fmaf(d, x, -1.0f / 144.0f);
+    d = fmaf(d, x, 1.0f / 30.0f);
+    d = fmaf(d, x, -1.0f / 8.0f);
+    d = fmaf(d, x, 1.0f / 3.0f);
+    return fmaf(d, x, -0.5f);
+  }
+  return (expf(-x) * (1.0f + x) - 1.0f) / (x * x);
+}
+
 // Input coefficient of gated EFLA: with the log-decay a added to the dynamics as -a / beta
 // times the identity over the step interval, the exact flow's input term is
 // int_0^beta e^{-(gamma + lambda) s} ds = beta phi(beta lambda - a) (beta in the delta-rule mode,
 // the gated delta rule's own input step).
 EFLA_DEV float gated_input_coef(float beta, float lam, float a, bool euler) {
   return euler ? beta : beta * phi_f(beta * lam - a);
+}
+
+// b = beta phi(beta lambda - a) and its partial derivatives: db/dbeta = phi(y) + beta lambda
+// phi'(y), db/dlambda = beta^2 phi'(y), db/da = -beta phi'(y), y = beta lambda - a
+// (delta-rule mode: b = beta, 1, 0, 0).
+struct GatedCoef {
+  float b, db_dbeta, db_dlam, db_da;
+};
+EFLA_DEV GatedCoef gated_coef(float beta, float lam, float a, bool euler) {
+  if (euler) return GatedCoef{beta, 1.0f, 0.0f, 0.0f};
+  const float y = beta * lam - a, ph = phi_f(y), dph = dphi_f(y);
+  return GatedCoef{beta * ph, ph + beta * lam * dph, beta * beta * dph, -beta * dph};
 }
 
 EFLA_DEV FlowCoef flow_coef(float beta, float lam, bool euler = false) {

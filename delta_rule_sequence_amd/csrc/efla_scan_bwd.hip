@@ -14,11 +14,16 @@
 // current chunk computes, and the LDS tiles are double-buffered. Products over the token
 // or d_k index read LDS tiles k-major with the LDS transpose read (bf16). dU~ and G leave
 // through LDS staging as 16-byte stores.
+//
+// Gated EFLA (GT), with c the running log-decay sums of the chunk, Gamma = e^c,
+// r = e^{c_last - c}: dU~ = scale P^T dO + diag(r) K G (P = tril(Q K^T) * e^{c_t - c_s}, saved
+// by the forward in place of M) and G <- e^{c_last} G + scale Q^T diag(Gamma) dO - W^T dU~.
+// Q rows are scaled by Gamma when they land in LDS; the rest acts on accumulators.
 #include "efla_internal.hpp"
 
 namespace efla {
 
-template <typename E, int DK, int DV, int TV>
+template <typename E, int DK, int DV, int TV, bool GT = false>
 struct ScanBwdLds {
   static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64), LS = pitch<E>(TV);
   // one stage: Q [64][LK], W [64][LK], M [64][LT], dO [64][LS]
@@ -26,19 +31,21 @@ struct ScanBwdLds {
   static constexpr size_t oW = oQ + 64 * LK * sizeof(E);
   static constexpr size_t oM = oW + 64 * LK * sizeof(E);
   static constexpr size_t oO = oM + 64 * LT * sizeof(E);
-  static constexpr size_t stage = oO + 64 * LS * sizeof(E);
+  static constexpr size_t oCs = oO + 64 * LS * sizeof(E);     // running log-decay sums [64] (GT)
+  static constexpr size_t stage = oCs + (GT ? 64 * 4 : 0);
   static constexpr size_t oG = 2 * stage;                       // G slice [DK][LS]
   static constexpr size_t oDt = oG + DK * LS * sizeof(E);       // dU~^T  [TV][LT]
   static constexpr size_t oDu = oDt + TV * LT * sizeof(E);      // dU~ staging [64][LS]
   static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
 };
 
-template <typename E, int DK, int DV, int TV>
+template <typename E, int DK, int DV, int TV, bool GT>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
-    E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0) {
-  typedef ScanBwdLds<E, DK, DV, TV> L;
+    E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0,
+    const float* __restrict__ cum) {
+  typedef ScanBwdLds<E, DK, DV, TV, GT> L;
   typedef typename Mma<E>::vec V;
   constexpr int KC = Mma<E>::KC, KS = DK / KC, KT = kChunk / KC;
   constexpr int NTILE = DV / TV;
@@ -68,6 +75,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
 
   V kA[KS], kN[KS];
   u32x4 qR[VQ], wR[VQ], mR[VM], oR[VO];
+  float cQ[VQ], cR = 0.f;  // gated: running log-decay sums of the Q rows / of token lane
 
   auto load_chunk = [&](int c) {
     const int n = min(kChunk, si.len - c * kChunk);
@@ -81,7 +89,9 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
       const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
       qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
       wR[it] = *(const u32x4*)(w + (r0 + r) * DK + cc);
+      if constexpr (GT) cQ[it] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + r];
     }
+    if constexpr (GT) cR = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
     const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
 #pragma unroll
     for (int it = 0; it < VM; ++it) mR[it] = *(const u32x4*)(mc + (it * kThreads + tid) * VE);
@@ -105,8 +115,19 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
-      *(u32x4*)(sQ + r * L::LK + cc) = keep_if(qR[it], r < n);
+      u32x4 qv = qR[it];
+      if constexpr (GT) {  // Q rows scaled by Gamma = e^c
+        const float gm = expf(cQ[it]);
+        V x = __builtin_bit_cast(V, qv);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) x[e] = to_e<E>(to_f(x[e]) * gm);
+        qv = __builtin_bit_cast(u32x4, x);
+      }
+      *(u32x4*)(sQ + r * L::LK + cc) = keep_if(qv, r < n);
       *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
+    }
+    if constexpr (GT) {
+      if (tid < 64) ((float*)(st + L::oCs))[tid] = cR;
     }
 #pragma unroll
     for (int it = 0; it < VM; ++it) {
@@ -150,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     const E* sW = (const E*)(stc + L::oW);
     const E* sM = (const E*)(stc + L::oM);
     const E* sO = (const E*)(stc + L::oO);
+    const float* sCs = (const float*)(stc + L::oCs);
     const int n = min(kChunk, si.len - c * kChunk);
     const int64_t r0 = base + (int64_t)c * kChunk;
     // Stage G (gradient of the state leaving chunk c): G^T tiles written transposed.
@@ -178,6 +200,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
       for (int ks = 0; ks < KS; ++ks)
         kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * L::LS + 16 * nb, L::LS, lane), kg);
       md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
+      if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
+        const float cl = sCs[n - 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kg[i] *= expf(fminf(cl - sCs[rA + 4 * (lane >> 4) + i], 0.f));
+      }
       f32x4 du = kg + g.scale * md;
       st_frag_t<E>(sDt + 16 * nb * L::LT + rA, L::LT, du, lane);
       st_frag_lds<E>(sDu + rA * L::LS + 16 * nb, L::LS, du, lane);
@@ -185,13 +212,14 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     __syncthreads();
 
     s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, L::LS, n, tid);
-    // G^T += scale dO^T Q - dU~^T W
+    // G^T += scale dO^T Q - dU~^T W (gated: G^T <- e^{c_last} G^T + ..., Q pre-scaled)
+    const float gC = GT ? expf(sCs[n - 1]) : 1.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
       const f32x4 a = mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
       const f32x4 b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
-      Gt[i] += g.scale * a - b;
+      Gt[i] = gC * Gt[i] + (g.scale * a - b);
     }
     if (more) commit_chunk(c - 1, smem + ((c - 1) & 1) * L::stage);
   }
@@ -203,14 +231,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
   }
 }
 
-template <typename E, int DK, int DV, int TV>
-static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
-                              const void* w, const void* m, const void* d_o, void* dut,
-                              void* dstates, const float* dht, float* dh0, hipStream_t st) {
-  typedef ScanBwdLds<E, DK, DV, TV> L;
+template <typename E, int DK, int DV, int TV, bool GT>
+static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, const void* k,
+                               const void* w, const void* m, const void* d_o, void* dut,
+                               void* dstates, const float* dht, float* dh0, hipStream_t st,
+                               const float* cum) {
+  typedef ScanBwdLds<E, DK, DV, TV, GT> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_kernel<E, DK, DV, TV>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_kernel<E, DK, DV, TV, GT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -218,12 +247,26 @@ static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, c
   const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / TV);
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
-  hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV, GT>), dim3((unsigned)blocks), dim3(kThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0);
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
   hipError_t e = hipGetLastError();
-  prof_end("scan_bwd", st);
+  prof_end(GT ? "scan_bwd_gated" : "scan_bwd", st);
   return e;
+}
+
+template <typename E, int DK, int DV, int TV>
+static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
+                              const void* w, const void* m, const void* d_o, void* dut,
+                              void* dstates, const float* dht, float* dh0, hipStream_t st,
+                              const float* cum) {
+  if (cum) {
+    if constexpr (sizeof(E) == 2)
+      return scan_bwd_run<E, DK, DV, TV, true>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+    else
+      return hipErrorInvalidValue;
+  }
+  return scan_bwd_run<E, DK, DV, TV, false>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
 }
 
 size_t lds_scan_bwd(Dt dt, int dk, int dv) {
@@ -240,9 +283,10 @@ size_t lds_scan_bwd(Dt dt, int dk, int dv) {
 
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
-                           void* dstates, const float* dht, float* dh0, hipStream_t st) {
+                           void* dstates, const float* dht, float* dh0, hipStream_t st,
+                           const float* cum) {
 #define EFLA_SB(E_, DK_, DV_, TV_) \
-  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st)
+  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SB(__bf16, 64, 64, 16);
     if (s.dk == 128 && s.dv == 64) EFLA_SB(__bf16, 128, 64, 16);

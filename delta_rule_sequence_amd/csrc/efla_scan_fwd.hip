@@ -342,9 +342,12 @@ static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, c
                               void* states, const float* h0, float* ht, hipStream_t st,
                               const float* cum) {
   const bool wsv = ut && states;
-  if (cum) {  // gated: outputs O (and final states), or final states alone; no saving
+  if (cum) {  // gated
     if constexpr (sizeof(E) == 2) {
-      if (wsv) return hipErrorInvalidValue;
+      if (o && wsv)
+        return scan_fwd_run<E, DK, DV, NWC, true, true, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
+      if (wsv)
+        return scan_fwd_run<E, DK, DV, NWC, false, true, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
       if (o)
         return scan_fwd_run<E, DK, DV, NWC, true, false, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
       if (ht)

@@ -160,17 +160,21 @@ def efla_fwd(q, k, v, beta, scale=1.0, cu_seqlens=None, save=True, ws=None, o=No
     return (o, saved) if ht is None else (o, saved, ht)
 
 
-def efla_fwd_gated(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, ws=None, o=None,
-                   mode="exact", initial_state=None, final_state=None, segments=0):
+def efla_fwd_gated(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, save=False, ws=None, o=None,
+                   saved=None, mode="exact", initial_state=None, final_state=None, segments=0):
     """Gated EFLA forward (efla_fwd_gated in include/efla.h): gate is the per-token log-decay
-    [B,H,T] in the input dtype (bf16 only). Returns o, or (o, final_state) when final_state is
-    True or a preallocated fp32 [n_state, H, dk, dv] tensor."""
+    [B,H,T] in the input dtype (bf16 only). Returns (o, saved) where saved is the buffer for
+    efla_bwd_gated (None unless save), plus final_state as in efla_fwd."""
     p = make_problem(q, k, v, beta, scale, cu_seqlens, mode, segments)
     _need(gate, "gate", k.dtype, tuple(beta.shape))
     if o is None:
         o = torch.empty_like(v)
     else:
         _need(o, "o", v.dtype, v.shape)
+    if save and saved is None:
+        saved = _bytes(efla_saved_bytes(p), k.device)
+    if not save:
+        saved = None
     h0 = _state_tensor(initial_state, "initial_state", p, k.device)
     ht = None
     if final_state is True:
@@ -182,8 +186,8 @@ def efla_fwd_gated(q, k, v, beta, gate, scale=1.0, cu_seqlens=None, ws=None, o=N
         ws = _bytes(ws_n, k.device)
     _lib.check("efla_fwd_gated", _lib.lib().efla_fwd_gated(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(h0), _ptr(o),
-        _ptr(ht), _ptr(ws), ws.numel(), _stream()))
-    return o if ht is None else (o, ht)
+        _ptr(ht), _ptr(saved), 0 if saved is None else saved.numel(), _ptr(ws), ws.numel(), _stream()))
+    return (o, saved) if ht is None else (o, saved, ht)
 
 
 def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None, grads=None,
@@ -218,6 +222,42 @@ def efla_bwd(q, k, v, beta, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None
         _ptr(saved), 0 if saved is None else saved.numel(), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream()))
     return (dq, dk, dv, dbeta) if dh0 is None else (dq, dk, dv, dbeta, dh0)
+
+
+def efla_bwd_gated(q, k, v, beta, gate, d_o, saved=None, scale=1.0, cu_seqlens=None, ws=None,
+                   grads=None, mode="exact", initial_state=None, d_final_state=None,
+                   d_initial_state=False, segments=0):
+    """Gated EFLA backward (efla_bwd_gated in include/efla.h): (dq, dk, dv, dbeta, dgate) in the
+    input dtype, plus the initial-state gradient as in efla_bwd. saved is the buffer
+    efla_fwd_gated(save=True) returned, or None to recompute it. grads may be a preallocated
+    (dq, dk, dv, dbeta, dgate) tuple."""
+    p = make_problem(q, k, v, beta, scale, cu_seqlens, mode, segments)
+    _need(gate, "gate", k.dtype, tuple(beta.shape))
+    _need(d_o, "d_o", v.dtype, v.shape)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dbeta, dgate = torch.empty_like(beta), torch.empty_like(gate)
+    else:
+        dq, dk, dv, dbeta, dgate = grads
+        for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (dbeta, beta, "dbeta"),
+                          (dgate, gate, "dgate")):
+            _need(t, n, ref.dtype, ref.shape)
+    h0 = _state_tensor(initial_state, "initial_state", p, k.device)
+    dht = _state_tensor(d_final_state, "d_final_state", p, k.device)
+    dh0 = None
+    if d_initial_state is True:
+        dh0 = torch.empty((_n_state(p), p.H, p.dk, p.dv), dtype=torch.float32, device=k.device)
+    elif d_initial_state is not None and d_initial_state is not False:
+        dh0 = _state_tensor(d_initial_state, "d_initial_state", p, k.device)
+    ws_n = efla_workspace_bytes(p, True)
+    if ws is None or ws.numel() < ws_n:
+        ws = _bytes(ws_n, k.device)
+    _lib.check("efla_bwd_gated", _lib.lib().efla_bwd_gated(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(h0), _ptr(d_o),
+        _ptr(dht), _ptr(saved), 0 if saved is None else saved.numel(), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dbeta), _ptr(dgate), _ptr(dh0), _ptr(ws), ws.numel(), _stream()))
+    out = (dq, dk, dv, dbeta, dgate)
+    return out if dh0 is None else out + (dh0,)
 
 
 def efla_decode(q, k, v, beta, state, scale=1.0, mode="exact", o=None):
@@ -288,6 +328,32 @@ class EflaFunction(torch.autograd.Function):
         dq, dk, dv, dbeta = efla_bwd(q, k, v, beta, d_o.contiguous(), saved, ctx.scale, cu,
                                      mode=ctx.mode)
         return dq, dk, dv, dbeta, None, None, None
+
+
+class EflaGatedFunction(torch.autograd.Function):
+    """o = gated EFLA(q, k, v, beta, gate); the backward runs the library's gated kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, gate, scale, cu_seqlens, mode):
+        q, k, v, beta, gate = (t.contiguous() for t in (q, k, v, beta, gate))
+        o, saved = efla_fwd_gated(q, k, v, beta, gate, scale, cu_seqlens, save=True, mode=mode)
+        ctx.save_for_backward(q, k, v, beta, gate, saved, cu_seqlens)
+        ctx.scale = scale
+        ctx.mode = mode
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, beta, gate, saved, cu = ctx.saved_tensors
+        g = efla_bwd_gated(q, k, v, beta, gate, d_o.contiguous(), saved, ctx.scale, cu, mode=ctx.mode)
+        return g + (None, None, None)
+
+
+def efla_gated(q, k, v, beta, gate, scale: float = 1.0, cu_seqlens: Optional[torch.Tensor] = None,
+               mode: str = "exact"):
+    """Gated EFLA token mixer (per-token log-decays gate [B,H,T], bf16): o [B,H,T,dv],
+    differentiable in q, k, v, beta and gate."""
+    return EflaGatedFunction.apply(q, k, v, beta, gate, scale, cu_seqlens, mode)
 
 
 def efla(q, k, v, beta, scale: float = 1.0, cu_seqlens: Optional[torch.Tensor] = None,

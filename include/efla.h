@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 6
+#define EFLA_ABI_VERSION 7
 
 typedef enum {
   EFLA_OK = 0,
@@ -90,9 +90,12 @@ typedef struct {
  *   m      : tril(Q K^T) of each chunk, [n_chunk_slots][H][64][64], problem dtype
  *   x      : X = (I + strictly_lower(diag(alpha) K K^T))^{-1} of each chunk (so that
  *            T = X diag(alpha)), [n_chunk_slots][H][64][64], problem dtype
+ *   cum    : gated forward only: running sums of the log-decays inside each chunk,
+ *            fp32 [n_chunk_slots][H][64] (then w, m and x hold the decayed factors of
+ *            efla_fwd_gated)
  *   total  : size of the whole buffer = efla_saved_bytes()                               */
 typedef struct {
-  size_t w, ut, states, table, m, x, total;
+  size_t w, ut, states, table, m, x, cum, total;
   int64_t n_chunk_slots;
 } efla_saved_layout;
 
@@ -167,11 +170,13 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
  * chunk: A_ts = alpha_t e^{c_t - c_s} k_t . k_s, W = X diag(alpha e^c) K, U = X diag(b) V,
  * O = scale (diag(e^c) Q S + (tril(Q K^T) * e^{c_t - c_s}) U~),
  * S <- e^{c_last} S + K^T diag(e^{c_last - c}) U~. h0 / ht as in efla_fwd_state; segments as in
- * efla_fwd. Inference forward: no saved buffer (no gated backward is provided). bf16 problems
- * only (EFLA_ERR_UNSUPPORTED otherwise). ws: efla_workspace_bytes(p, 0). */
+ * efla_fwd. `saved` (NULL, or efla_saved_bytes(p) bytes) receives the decayed factors, U~,
+ * the chunk states and the running log-decay sums for efla_bwd_gated. bf16 problems only
+ * (EFLA_ERR_UNSUPPORTED otherwise). ws: efla_workspace_bytes(p, 0). */
 efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,
                            const void* beta, const void* gate, const float* h0, void* o,
-                           float* ht, void* ws, size_t ws_bytes, void* stream);
+                           float* ht, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Backward of sum(o * d_o): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T], all in
  * the problem dtype (every output fully overwritten). `saved` is the buffer a forward
@@ -190,6 +195,22 @@ efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, 
                            const void* beta, const float* h0, const void* d_o, const float* dht,
                            const void* saved, size_t saved_bytes, void* dq, void* dk, void* dv,
                            void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of gated EFLA: the gradient of sum(o * d_o) + <ht, dht> with respect to q, k, v,
+ * beta, the log-decays (dgate [B,H,T], problem dtype) and h0, for the forward of
+ * efla_fwd_gated. Reverse mode of the chunk form given there: per chunk, with c its running
+ * log-decay sums, Gamma = e^c, r = e^{c_last - c}, D_ts = e^{c_t - c_s}, P = tril(Q K^T) * D and
+ * G the gradient of the state leaving the chunk,
+ *   dU~ = scale P^T dO + diag(r) K G,  G_in = e^{c_last} G + scale Q^T diag(Gamma) dO - W^T dU~;
+ * every factor e^{c} also contributes to dc, and dgate_t = sum over s >= t in the chunk of dc_s
+ * plus db_t db_t/da_t. `saved` is the buffer efla_fwd_gated filled on the same inputs, or NULL to
+ * recompute it inside ws (then h0 must be the forward's). Other arguments as efla_bwd_state.
+ * bf16 problems only. ws: efla_workspace_bytes(p, 1). */
+efla_status efla_bwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const void* gate, const float* h0, const void* d_o,
+                           const float* dht, const void* saved, size_t saved_bytes, void* dq,
+                           void* dk, void* dv, void* dbeta, void* dgate, float* dh0, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* Recurrent inference: the token recurrence itself (summary page, section 3.2), one token
  * after the other, for dense batches (cu_seqlens must be NULL). Reads q, k [B,H,T,dk],

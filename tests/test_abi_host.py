@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 6
+    assert L.efla_abi_version() == 7
 
 
 def test_status_strings(L):
@@ -95,10 +95,10 @@ def test_workspace_and_saved_sizes(L):
     w = tok * 128 * e
     states = slots * 16 * 128 * 128 * e
     m = slots * 16 * 64 * 64 * e
-    assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states + 2 * m
     cum = slots * 16 * 64 * 4  # running log-decay sums of the gated forward
+    assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states + 2 * m + cum
     assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * w + m + cum
-    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states + 2 * m) + w
+    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states + 2 * m + cum) + w
     lay = _lib.EflaSavedLayout()
     assert L.efla_get_saved_layout(ctypes.byref(p), ctypes.byref(lay)) == 0
     assert (lay.w, lay.ut, lay.states, lay.m, lay.x, lay.n_chunk_slots) == \
@@ -189,17 +189,31 @@ def test_segment_plan_workspace(L):
 
 
 def test_gated_entry_points_reject_bad_arguments(L):
-    """Gated forward and decode: bf16 only, gate required, same validation as the others."""
+    """Gated forward, backward and decode: bf16 only, gate required, same validation as the others."""
     fake = ctypes.c_void_p(0x100000)
     p = _p(B=1, H=2, T=128)
     ws = L.efla_workspace_bytes(ctypes.byref(p), 0)
     # fp32 problems: not provided
     pf = _p(B=1, H=2, T=128, dtype=_lib.EFLA_F32, dk=64, dv=64)
-    assert L.efla_fwd_gated(ctypes.byref(pf), fake, fake, fake, fake, fake, None, fake, None, fake, 1 << 40, None) == 4
+    assert L.efla_fwd_gated(ctypes.byref(pf), fake, fake, fake, fake, fake, None, fake, None, None, 0, fake, 1 << 40, None) == 4
     # missing gate / missing workspace / short workspace
-    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, None, fake, ws, None) == 1
-    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, None, None, ws, None) == 1
-    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, None, fake, ws - 1, None) == 5
+    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, None, None, 0, fake, ws, None) == 1
+    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, None, None, 0, None, ws, None) == 1
+    assert L.efla_fwd_gated(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, None, None, 0, fake, ws - 1, None) == 5
     assert L.efla_decode_gated(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None) == 1
     packed = _p(B=1, T=128, cu=0x1000, n_seqs=2)
     assert L.efla_decode_gated(ctypes.byref(packed), fake, fake, fake, fake, fake, fake, fake, None) == 4
+    # gated backward: q k v beta gate h0 d_o dht saved saved_bytes dq dk dv dbeta dgate dh0 ws ws_bytes
+    wb = L.efla_workspace_bytes(ctypes.byref(p), 1)
+    sb = L.efla_saved_bytes(ctypes.byref(p))
+
+    def bwd(prob, gate=fake, saved=None, saved_bytes=0, dgate=fake, ws_=fake, ws_bytes=wb):
+        return L.efla_bwd_gated(ctypes.byref(prob), fake, fake, fake, fake, gate, None, fake, None,
+                                saved, saved_bytes, fake, fake, fake, fake, dgate, None, ws_,
+                                ws_bytes, None)
+    assert bwd(pf, ws_bytes=1 << 40) == 4
+    assert bwd(p, gate=None) == 1
+    assert bwd(p, dgate=None) == 1
+    assert bwd(p, ws_=None) == 1
+    assert bwd(p, ws_bytes=wb - 1) == 5
+    assert bwd(p, saved=fake, saved_bytes=sb - 1) == 5

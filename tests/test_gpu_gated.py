@@ -1,6 +1,7 @@
-"""GPU parity of gated EFLA (efla_fwd_gated, efla_decode_gated) through the C ABI against the
-fp64 oracle (oracle.gated_forward, pinned in test_oracle_pins against the dense decayed ZOH
-flow). bf16 problems, normwise tolerance 2e-2 per tensor as in the other parity tests.
+"""GPU parity of gated EFLA (efla_fwd_gated, efla_bwd_gated, efla_decode_gated) through the C ABI
+against the fp64 oracle (oracle.gated_forward, pinned in test_oracle_pins against the dense
+decayed ZOH flow; oracle.gated_backward, pinned there by central differences). bf16 problems,
+normwise tolerance 2e-2 per tensor as in the other parity tests.
 
 Gate recipe: log-decays a = log sigmoid(x) per (batch, head, token), x ~ N(mu, 1) with mu = 3
 (mild decay, e^a about 0.95), 0 (strong decay, e^a about 0.5: e^{-30} and below across a
@@ -72,8 +73,8 @@ def test_gated_forward(E, name, wl, mu, segments, mode):
     print("%s: B=%d H=%d T=%d dk=%d dv=%d segments=%d mode=%s" % (name, B, H, T, dk, dv, segments, mode),
           flush=True)
     q, k, v, beta, g = (_dev(x) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a))
-    o, ht = E.efla_fwd_gated(q, k, v, beta, g, 0.8, mode=mode, initial_state=_dev(h0, torch.float32),
-                             final_state=True, segments=segments)
+    o, _, ht = E.efla_fwd_gated(q, k, v, beta, g, 0.8, mode=mode, initial_state=_dev(h0, torch.float32),
+                                final_state=True, segments=segments)
     torch.cuda.synchronize()
     ref_o, ref_ht = O.gated_forward(inp["q"], inp["k"], inp["v"], inp["beta"], a, scale=0.8,
                                     initial_state=h0, mode=mode)
@@ -90,7 +91,7 @@ def test_zero_gate_is_efla(E):
     w = workload(2, B=2, H=2, T=64 * 3 + 11)
     inp = make_inputs(w, with_grad=False)
     q, k, v, beta = (_dev(inp[n]) for n in ("q", "k", "v", "beta"))
-    o_g = E.efla_fwd_gated(q, k, v, beta, torch.zeros_like(beta), 1.0)
+    o_g, _ = E.efla_fwd_gated(q, k, v, beta, torch.zeros_like(beta), 1.0)
     o_p, _ = E.efla_fwd(q, k, v, beta, 1.0, None, save=False)
     torch.cuda.synchronize()
     assert O.rel_err(_np(o_g), _np(o_p)) < 1e-2
@@ -115,7 +116,85 @@ def test_gated_decode(E, dk, dv, mu):
     ref_o, ref_s = O.gated_forward(inp["q"], inp["k"], inp["v"], inp["beta"], a, scale=0.7, initial_state=h0)
     _check("o", np.concatenate([_np(o1), _np(o2)], axis=2), ref_o)
     _check("state", _np(state), ref_s)
-    o3, ht = E.efla_fwd_gated(q, k, v, beta, g, 0.7, initial_state=_dev(h0, torch.float32), final_state=True)
+    o3, _, ht = E.efla_fwd_gated(q, k, v, beta, g, 0.7, initial_state=_dev(h0, torch.float32), final_state=True)
     torch.cuda.synchronize()
     _check("fwd.o", _np(o3), ref_o)
     _check("fwd.ht", _np(ht), ref_s)
+
+
+GRAD_NAMES = ("dq", "dk", "dv", "dbeta", "dgate", "d_initial_state")
+
+
+@pytest.mark.parametrize("name,wl,mu,segments,mode", CASES, ids=[c[0] for c in CASES])
+def test_gated_backward(E, name, wl, mu, segments, mode):
+    """Gradients in q, k, v, beta, the log-decays and the initial state, from the buffer the
+    gated forward saved (with the same segment plan), with a gradient arriving at the final
+    state."""
+    w = workload(2, **wl)
+    inp = make_inputs(w, with_grad=True)
+    if mode == "euler":
+        kk = inp["k"] / np.maximum(np.linalg.norm(inp["k"], axis=-1, keepdims=True), 1e-30)
+        inp["k"] = round_to_bf16(kk.astype(np.float32))
+    B, H, T, dk = inp["k"].shape
+    dv = inp["v"].shape[-1]
+    a = _gates((B, H, T), mu, 19)
+    r = np.random.default_rng(7)
+    h0 = (r.standard_normal((B, H, dk, dv)) * 0.3).astype(np.float32)
+    dht = (r.standard_normal((B, H, dk, dv)) * 0.1).astype(np.float32)
+    print("%s: B=%d H=%d T=%d dk=%d dv=%d segments=%d mode=%s" % (name, B, H, T, dk, dv, segments, mode),
+          flush=True)
+    q, k, v, beta, g, do = (_dev(x) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"]))
+    h0_d, dht_d = _dev(h0, torch.float32), _dev(dht, torch.float32)
+    _, saved = E.efla_fwd_gated(q, k, v, beta, g, 0.8, save=True, mode=mode, initial_state=h0_d,
+                                segments=segments)
+    grads = E.efla_bwd_gated(q, k, v, beta, g, do, saved, 0.8, mode=mode, initial_state=h0_d,
+                             d_final_state=dht_d, d_initial_state=True, segments=segments)
+    torch.cuda.synchronize()
+    ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"], scale=0.8,
+                           initial_state=h0, d_final_state=dht, mode=mode)
+    for nm, t in zip(GRAD_NAMES, grads):
+        _check(nm, _np(t), ref[nm])
+
+
+def test_gated_recompute_backward(E):
+    """Without a saved buffer the gated forward is recomputed inside the workspace."""
+    w = workload(2, B=2, H=2, T=64 * 4 + 21)
+    inp = make_inputs(w, with_grad=True)
+    a = _gates((2, 2, w.T), 1.0, 23)
+    q, k, v, beta, g, do = (_dev(x) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"]))
+    grads = E.efla_bwd_gated(q, k, v, beta, g, do, None, 1.0)
+    torch.cuda.synchronize()
+    ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"])
+    for nm, t in zip(GRAD_NAMES, grads):
+        _check(nm, _np(t), ref[nm])
+
+
+def test_zero_gate_backward_is_efla(E):
+    """a = 0: the gated backward gives the ungated gradients, and the log-decay gradient the
+    oracle's (it does not vanish at a = 0)."""
+    w = workload(2, B=1, H=3, T=64 * 3 + 40)
+    inp = make_inputs(w, with_grad=True)
+    q, k, v, beta, do = (_dev(inp[n]) for n in ("q", "k", "v", "beta", "do"))
+    z = torch.zeros_like(beta)
+    gg = E.efla_bwd_gated(q, k, v, beta, z, do, None, 1.0)
+    gp = E.efla_bwd(q, k, v, beta, do, None, 1.0, None)
+    torch.cuda.synchronize()
+    for nm, a_, b_ in zip(("dq", "dk", "dv", "dbeta"), gg, gp):
+        assert O.rel_err(_np(a_), _np(b_)) < 1e-2, nm
+    ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], np.zeros_like(inp["beta"]), inp["do"])
+    assert np.max(np.abs(ref["dgate"])) > 0
+    _check("dgate", _np(gg[4]), ref["dgate"])
+
+
+def test_gated_autograd(E):
+    """efla_gated under torch autograd runs the library's gated backward."""
+    w = workload(2, B=1, H=2, T=100)
+    inp = make_inputs(w, with_grad=True)
+    a = _gates((1, 2, 100), 2.0, 31)
+    ts = [_dev(x).requires_grad_(True) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a)]
+    o = E.efla_gated(*ts, scale=0.9)
+    o.backward(_dev(inp["do"]))
+    torch.cuda.synchronize()
+    ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"], scale=0.9)
+    for nm, t in zip(GRAD_NAMES, ts):
+        _check(nm, _np(t.grad), ref[nm])
