@@ -455,8 +455,7 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
                                                  dstates, dht, dh0, st, cum)))
     return r;
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
-                                     dstates, sv + L.x, dq, dk, dv, dbeta, st, gate, cum,
-                                     gate ? sv + L.m : nullptr, dgate));
+                                     dstates, sv + L.x, dq, dk, dv, dbeta, st, gate, cum, dgate));
 }
 }  // namespace
 }  // namespace efla

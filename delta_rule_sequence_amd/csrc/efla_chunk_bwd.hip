@@ -28,8 +28,8 @@
 //   4 Y = dX X^T;  5 dA = -X^T Y (-> dalpha, H);  6 H K and the outputs.
 //
 // Gated EFLA (GT): with c the running log-decay sums of the chunk (saved by the forward),
-// Gamma = e^c, r = e^{c_last - c}, D_ts = e^{c_t - c_s} and P = tril(Q K^T) * D (saved in place
-// of M): dQ's state part is scale diag(Gamma) dO S^T, dK's is diag(r) U~ G^T, dM becomes
+// Gamma = e^c, r = e^{c_last - c}, D_ts = e^{c_t - c_s} and P = tril(Q K^T) * D (formed again
+// from the Q and K tiles in LDS, beside dM): dQ's state part is scale diag(Gamma) dO S^T, dK's is diag(r) U~ G^T, dM becomes
 // dP * D, the UT factors are T_w = X diag(alpha Gamma) and T_u = X diag(b) (dT split into
 // dW K^T and dU V^T), A carries D. Every e^c factor also adds to the log-decay gradient dc
 // (accumulated per token in LDS), which a reverse running sum over the chunk turns into the
@@ -57,10 +57,9 @@ struct ChunkBwdLds {
   static constexpr size_t oM = oX + TT;          // dM  [64][LT]
   static constexpr size_t oC = oM + TT;          // lambda, alpha, e^-x, dalpha/dlam [64]
   static constexpr size_t oP = oC + 4 * 64 * 4;  // dalpha partials [64][8]
-  // gated only: P [64][LT]; c, b, db/dbeta, db/dlam, db/da [64]; dc [64] + two scalars;
-  // db column-sum partials [64][4]
-  static constexpr size_t oPg = oP + 8 * 64 * 4;
-  static constexpr size_t oGc = oPg + TT;
+  // gated only: c, b, db/dbeta, db/dlam, db/da [64]; dc [64] + two scalars; db column-sum
+  // partials [64][4]
+  static constexpr size_t oGc = oP + 8 * 64 * 4;
   static constexpr size_t oDc = oGc + 5 * 64 * 4;
   static constexpr size_t oDb = oDc + 80 * 4;
   static constexpr size_t bytes = GT ? oDb + 4 * 64 * 4 : oP + 8 * 64 * 4;
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     const E* __restrict__ dut, const E* __restrict__ states, const E* __restrict__ dstates,
     const E* __restrict__ xsav, E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
     E* __restrict__ dbeta, const E* __restrict__ gate, const float* __restrict__ cum,
-    const E* __restrict__ psav, E* __restrict__ dgate) {
+    E* __restrict__ dgate) {
   typedef ChunkBwdLds<E, DK, DV, GT> L;
   typedef typename Mma<E>::vec Vv;
   constexpr int LK = L::LK, LV = L::LV, LT = L::LT;
@@ -147,7 +146,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // dalpha partials [64][8]: slots 0-3 column sums of dT . X per row block, slots 4-7 row
   // sums of dA . KK^T per column block (one token's eight partials are one 32-byte row).
   float* pDa = (float*)(smem + L::oP);
-  E* sPg = (E*)(smem + L::oPg);            // gated: P
   float* cC = (float*)(smem + L::oGc);     // gated: c, b, db/dbeta, db/dlam, db/da
   float* cB = cC + 64;
   float* cBb = cC + 128;
@@ -165,7 +163,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
 
   TileRegs<E, DK> tK, tQ;
   TileRegs<E, DV> tDU, tDO, tU, tV;
-  TileRegs<E, 64> tX, tP;
+  TileRegs<E, 64> tX;
   Vv fS[CK][KSV], fG[CK][KSV];  // rows of S and G for this wave's d_k columns (B^T operands)
   float bt, cR = 0.f, aR = 0.f;  // beta, and (gated) c and log-decay of token lane
   // Requests for a chunk's inputs, issued for the next chunk in small groups spread over
@@ -187,7 +185,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   auto issue_v_x = [&](const ChunkUnit& c) {
     tV.load(v + c.row0 * DV, c.n, tid);
     tX.load(xsav + c.sh * 64 * 64, 64, tid);
-    if constexpr (GT) tP.load(psav + c.sh * 64 * 64, 64, tid);
   };
   auto issue_q = [&](const ChunkUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
   auto issue_s = [&](const ChunkUnit& c, int cK) {
@@ -248,7 +245,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   }
   const float bt_cur = bt, a_cur = aR;
   if constexpr (GT) {
-    tP.store(sPg, LT, 64, tid);
     if (tid < 64) {
       cC[tid] = cR;
       sDc[tid] = 0.f;
@@ -270,6 +266,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);
   //         dM = scale tril(dO U~^T); per-token coefficients
   f32x4 aQ[2][CK], aK[2][CK];
+  if constexpr (GT) {
+    // dc_last += e^{c_last} <G, S>: waves 0-3 hold every row of S and G once
+    if (wv < 4) {
+      float gs = 0.f;
+#pragma unroll
+      for (int j = 0; j < CK; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks)
+#pragma unroll
+          for (int e = 0; e < 16 / (int)sizeof(E); ++e) gs = fmaf(to_f(fS[j][ks][e]), to_f(fG[j][ks][e]), gs);
+      gs = group_sum<16>(gs);
+      gs += __shfl_xor(gs, 16);
+      gs += __shfl_xor(gs, 32);
+      if (lane == 0) atomicAdd(&sDc[65], gs);
+    }
+  }
   {
     f32x4 aW[2][CK];
 #pragma unroll
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t = 16 * (rb0 + i) + (lane & 15);
-      const float ct = cC[t], gm = expf(ct), rr = expf(fminf(cl - ct, 0.f));
+      const float ct = cC[t], gm = exp_decay(ct), rr = exp_decay(fminf(cl - ct, 0.f));
       float p1 = 0.f, p2 = 0.f;
 #pragma unroll
       for (int j = 0; j < CK; ++j) {
@@ -332,39 +344,29 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
         atomicAdd(&sDc[64], rr * p2);
       }
     }
-    // dc_last += e^{c_last} <G, S>: waves 0-3 hold every row of S and G once
-    if (wv < 4) {
-      float gs = 0.f;
-#pragma unroll
-      for (int j = 0; j < CK; ++j)
-#pragma unroll
-        for (int ks = 0; ks < KSV; ++ks)
-#pragma unroll
-          for (int e = 0; e < 16 / (int)sizeof(E); ++e) gs = fmaf(to_f(fS[j][ks][e]), to_f(fG[j][ks][e]), gs);
-      gs = group_sum<16>(gs);
-      gs += __shfl_xor(gs, 16);
-      gs += __shfl_xor(gs, 32);
-      if (lane == 0) atomicAdd(&sDc[65], gs);
-    }
   }
   {
-    f32x4 m[1][2] = {{zero4(), zero4()}};
-    if (plow) mma_blk<E, false, false, 1, 2, DV, true>(sDO + 16 * pr * LV, LV, sU + 16 * pn * LV, LV, 0, DV, m, lane);
+    f32x4 m[1][2] = {{zero4(), zero4()}}, qk[1][2] = {{zero4(), zero4()}};
+    if (plow) {
+      mma_blk<E, false, false, 1, 2, DV, true>(sDO + 16 * pr * LV, LV, sU + 16 * pn * LV, LV, 0, DV, m, lane);
+      if constexpr (GT)
+        mma_blk<E, false, false, 1, 2, DK, true>(sQ + 16 * pr * LK, LK, sK + 16 * pn * LK, LK, 0, DK, qk, lane);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       f32x4 mm = tri_mask_row(m[0][j], pr, pn + j, true, lane) * g.scale;
       if constexpr (GT) {  // dP * P adds to dc (rows +, columns -); then dM = dP * D
         const int t = 16 * pr + (lane & 15), s0 = 16 * (pn + j) + 4 * (lane >> 4);
-        const f32x4 pv = ld4f<E>(sPg + t * LT + s0);
         const float ct = cC[t];
         float rsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float ev = mm[e] * pv[e];
+          const float d = exp_decay(fminf(ct - cC[s0 + e], 0.f));
+          const float ev = mm[e] * (qk[0][j][e] * d);  // dP * P (mm is zero above the diagonal)
           rsum += ev;
           const float csum = group_sum<16>(ev);
           if ((lane & 15) == 0) atomicAdd(&sDc[s0 + e], -csum);
-          mm[e] *= expf(fminf(ct - cC[s0 + e], 0.f));
+          mm[e] *= d;
         }
         rsum += __shfl_xor(rsum, 16);
         rsum += __shfl_xor(rsum, 32);
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       if (pn + j > pr) t[0][j] = tu[0][j] = zero4();
       const int col = 16 * (pn + j) + (lane & 15);
       const float al = cAl[col];
-      const float gmc = GT ? expf(cC[col]) : 1.f, bc = GT ? cB[col] : 0.f;
+      const float gmc = GT ? exp_decay(cC[col]) : 1.f, bc = GT ? cB[col] : 0.f;
       float cs = 0.f, cb = 0.f;
       f32x4 dx;
 #pragma unroll
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       const int row = 16 * (rb0 + i) + (lane & 15);
       const float al = cAl[row];
       // gated: T_u^T = diag(b) X^T, T_w^T = diag(alpha Gamma) X^T
-      const float fu = GT ? cB[row] : al, fw = GT ? al * expf(cC[row]) : al;
+      const float fu = GT ? cB[row] : al, fw = GT ? al * exp_decay(cC[row]) : al;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
@@ -485,7 +487,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   mma_blk<E, true, true, 2, CK, kChunk, true>(sM + 16 * rb0, LT, sQ + 16 * cK, LK,
                                               round_down_kc<E>(16 * rb0), kChunk, aK, lane);
   __syncthreads();
-  if (more) issue_s(nxt, cK);  // S registers are free again; G follows two steps later
+  // S registers are free again; G follows two steps later. The gated kernel, which holds more
+  // per-token state, requests S with G so that S is not held through the dA step.
+  if constexpr (!GT) {
+    if (more) issue_s(nxt, cK);
+  }
 
   // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s), kept transposed
   //         (sY[s][t] = Y[t][s]); stage dQ and dV
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * pr + 4 * (lane >> 4) + i;
         float a = row > col ? -da[0][j][i] : 0.f;
-        if constexpr (GT) a *= expf(fminf(cC[row] - cC[col], 0.f));  // A carries D
+        if constexpr (GT) a *= exp_decay(fminf(cC[row] - cC[col], 0.f));  // A carries D
         rs[i] = a * kk[0][j][i];
         dg[i] = a * cAl[row];
         if constexpr (GT) fc = fmaf(cAl[row], rs[i], fc);  // dA . A, column part
@@ -573,7 +579,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   s2g<E, DK, kBwdThreads>(dq + row0 * DK, DK, sQ, LK, n, tid);
   s2g<E, DV, kBwdThreads>(dv + row0 * DV, DV, sDU, LV, n, tid);
   __syncthreads();
-  if (more) { issue_q(nxt); issue_g(nxt, cK); }
+  if (more) {
+    issue_q(nxt);
+    if constexpr (GT) issue_s(nxt, cK);
+    issue_g(nxt, cK);
+  }
 
   // ---- 6: dK += H K; dk += 2 k dalpha dalpha/dlam; dbeta = dalpha e^-x
   mma_blk<E, false, true, 2, CK, kChunk, true>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0,
@@ -607,7 +617,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       const float da_t = dalpha(tid), db_t = dbsum(tid);
       if (tid < n) dbeta[row0 + tid] = to_e<E>(da_t * cEx[tid] + db_t * cBb[tid]);
       float dc = tid < n ? fmaf(cAl[tid], da_t, sDc[tid]) : 0.f;
-      if (tid == n - 1) dc += sDc[64] + expf(cC[tid]) * sDc[65];
+      if (tid == n - 1) dc += sDc[64] + exp_decay(cC[tid]) * sDc[65];
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_down(dc, o);
@@ -632,8 +642,7 @@ static hipError_t chunk_bwd_go(const Shape& s, const int* table, const void* q, 
                                const void* v, const void* beta, const void* d_o, const void* ut,
                                const void* dut, const void* states, const void* dstates,
                                const void* x, void* dq, void* dk, void* dv, void* dbeta,
-                               const void* gate, const float* cum, const void* m, void* dgate,
-                               hipStream_t st) {
+                               const void* gate, const float* cum, void* dgate, hipStream_t st) {
   typedef ChunkBwdLds<E, DK, DV, GT> L;
   static_assert(L::bytes <= 160 * 1024, "LDS budget");
   static bool attr = false;
@@ -652,7 +661,7 @@ static hipError_t chunk_bwd_go(const Shape& s, const int* table, const void* q, 
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
                      (const E*)beta, (const E*)d_o, (const E*)ut, (const E*)dut,
                      (const E*)states, (const E*)dstates, (const E*)x, (E*)dq, (E*)dk, (E*)dv,
-                     (E*)dbeta, (const E*)gate, cum, (const E*)m, (E*)dgate);
+                     (E*)dbeta, (const E*)gate, cum, (E*)dgate);
   hipError_t e = hipGetLastError();
   prof_end(GT ? "chunk_bwd_gated" : "chunk_bwd", st);
   return e;
@@ -674,11 +683,10 @@ hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, con
                             const void* v, const void* beta, const void* d_o, const void* ut,
                             const void* dut, const void* states, const void* dstates,
                             const void* x, void* dq, void* dk, void* dv, void* dbeta,
-                            hipStream_t st, const void* gate, const float* cum, const void* m,
-                            void* dgate) {
+                            hipStream_t st, const void* gate, const float* cum, void* dgate) {
 #define EFLA_CB(E_, DK_, DV_, GT_)                                                              \
   return chunk_bwd_go<E_, DK_, DV_, GT_>(s, table, q, k, v, beta, d_o, ut, dut, states, dstates, \
-                                         x, dq, dk, dv, dbeta, gate, cum, m, dgate, st)
+                                         x, dq, dk, dv, dbeta, gate, cum, dgate, st)
   if (s.dt == Dt::BF16) {
     if (gate) {
       if (s.dk == 64 && s.dv == 64) EFLA_CB(__bf16, 64, 64, true);

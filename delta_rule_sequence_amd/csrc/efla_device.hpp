@@ -537,6 +537,12 @@ struct FlowCoef {
   float alpha, ex, dlam;
 };
 
+// Decay factors of gated EFLA (e^{c} for running log-decay sums c): the hardware base-2
+// exponential after one multiply by log2(e), two instructions instead of the libm sequence.
+// The product's rounding gives a relative error of about |x| 2^-24 on top of the instruction's
+// ~1 ulp, far below the resolution of bf16 data; results below the normal range may flush to 0.
+EFLA_DEV float exp_decay(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
 // phi(x) = (1 - e^{-x}) / x (phi(0) = 1): Taylor polynomial for |x| < 1 (degree 11), else the
 // closed form with expm1.
 EFLA_DEV float phi_f(float x) {

@@ -65,14 +65,14 @@ hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, cons
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
                          const void* beta, float* state, void* o, hipStream_t st,
                          const void* gate = nullptr);
-// gate (null, or log-decays) selects gated EFLA: then cum (saved running log-decay sums),
-// m (the saved decayed scores P) and dgate (the log-decay gradient) are used.
+// gate (null, or log-decays) selects gated EFLA: then cum (saved running log-decay sums) and
+// dgate (the log-decay gradient) are used.
 hipError_t launch_chunk_bwd(const Shape& s, const int* table, const void* q, const void* k,
                             const void* v, const void* beta, const void* d_o, const void* ut,
                             const void* dut, const void* states, const void* dstates,
                             const void* x, void* dq, void* dk, void* dv, void* dbeta,
                             hipStream_t st, const void* gate = nullptr, const float* cum = nullptr,
-                            const void* m = nullptr, void* dgate = nullptr);
+                            void* dgate = nullptr);
 
 // Dynamic LDS bytes of each kernel for a head-size pair (0 = combination not built).
 size_t lds_ut_fwd(Dt dt, int dk, int dv);

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
       u32x4 qv = qR[it];
       if constexpr (GT) {  // Q rows scaled by Gamma = e^c
-        const float gm = expf(cQ[it]);
+        const float gm = exp_decay(cQ[it]);
         V x = __builtin_bit_cast(V, qv);
 #pragma unroll
         for (int e = 0; e < VE; ++e) x[e] = to_e<E>(to_f(x[e]) * gm);
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
       if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
         const float cl = sCs[n - 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kg[i] *= expf(fminf(cl - sCs[rA + 4 * (lane >> 4) + i], 0.f));
+        for (int i = 0; i < 4; ++i) kg[i] *= exp_decay(fminf(cl - sCs[rA + 4 * (lane >> 4) + i], 0.f));
       }
       f32x4 du = kg + g.scale * md;
       st_frag_t<E>(sDt + 16 * nb * L::LT + rA, L::LT, du, lane);
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
 
     s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, L::LS, n, tid);
     // G^T += scale dO^T Q - dU~^T W (gated: G^T <- e^{c_last} G^T + ..., Q pre-scaled)
-    const float gC = GT ? expf(sCs[n - 1]) : 1.f;
+    const float gC = GT ? exp_decay(sCs[n - 1]) : 1.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;

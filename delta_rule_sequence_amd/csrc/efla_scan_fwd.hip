@@ -187,14 +187,14 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     if constexpr (GT) {
       const float* cv = (const float*)(st + L::oC);
       const float cl = cv[n - 1];
-      gC = expf(cl);
+      gC = exp_decay(cl);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float cr = cv[prow<E>(rb, g4 + i)];
-          gam[rb][i] = expf(cr);
-          dec[rb][i] = expf(fminf(cl - cr, 0.f));
+          gam[rb][i] = exp_decay(cr);
+          dec[rb][i] = exp_decay(fminf(cl - cr, 0.f));
         }
     }
     if constexpr (WSV) {  // S_c, the state entering chunk c

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = 16 * nb + c4 + i;
-          const float dec = GT ? expf(fminf(cra - sCm[col], 0.f)) : 1.f;  // e^{c_t - c_s}
+          const float dec = GT ? exp_decay(fminf(cra - sCm[col], 0.f)) : 1.f;  // e^{c_t - c_s}
           av[i] = rowa > col ? ala * dec * acc[i] : 0.f;
         }
         *(f32x4*)(sA + rowa * L::LF + 16 * nb + c4) = av;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
           if constexpr (GT) {
             const float cr = sCm[rA + (lane & 15)];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m[i] *= expf(fminf(cr - sCm[16 * nb + 4 * (lane >> 4) + i], 0.f));
+            for (int i = 0; i < 4; ++i) m[i] *= exp_decay(fminf(cr - sCm[16 * nb + 4 * (lane >> 4) + i], 0.f));
           }
         }
         st_frag_t<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);
@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
           const f32x4 c0 = *(const f32x4*)(sCm + c), c1 = *(const f32x4*)(sCm + c + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            a0[e] *= expf(c0[e]);
-            a1[e] *= expf(c1[e]);
+            a0[e] *= exp_decay(c0[e]);
+            a1[e] *= exp_decay(c1[e]);
           }
           b0 = *(const f32x4*)(sBl + c);
           b1 = *(const f32x4*)(sBl + c + 4);

@@ -198,3 +198,47 @@ def test_gated_autograd(E):
     ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"], scale=0.9)
     for nm, t in zip(GRAD_NAMES, ts):
         _check(nm, _np(t.grad), ref[nm])
+
+
+def test_gated_packed_sequences(E):
+    """Packed batch (cu_seqlens): the state, and the running log-decay sums, restart at every
+    sequence; each sequence against the oracle on its own, forward and backward, with initial
+    and final states per sequence."""
+    lens = [70, 200, 1, 64, 133]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    w = workload(2, B=1, H=2, T=T)
+    inp = make_inputs(w, with_grad=True)
+    a = _gates((1, 2, T), 1.0, 37)
+    r = np.random.default_rng(13)
+    h0 = (r.standard_normal((len(lens), 2, 128, 128)) * 0.3).astype(np.float32)
+    dht = (r.standard_normal((len(lens), 2, 128, 128)) * 0.1).astype(np.float32)
+    q, k, v, beta, g, do = (_dev(x) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"]))
+    cu_d = torch.from_numpy(cu).cuda()
+    h0_d, dht_d = _dev(h0, torch.float32), _dev(dht, torch.float32)
+    o, saved, ht = E.efla_fwd_gated(q, k, v, beta, g, 0.8, cu_d, save=True, initial_state=h0_d,
+                                    final_state=True)
+    grads = E.efla_bwd_gated(q, k, v, beta, g, do, saved, 0.8, cu_d, initial_state=h0_d,
+                             d_final_state=dht_d, d_initial_state=True)
+    torch.cuda.synchronize()
+    ref_o, ref_ht = np.zeros(inp["v"].shape), np.zeros(h0.shape)
+    ref = {nm: np.zeros(inp[src].shape) for nm, src in (("dq", "q"), ("dk", "k"), ("dv", "v"),
+                                                         ("dbeta", "beta"), ("dgate", "beta"))}
+    ref["d_initial_state"] = np.zeros(h0.shape)
+    for i in range(len(lens)):
+        s0, s1 = cu[i], cu[i + 1]
+        sl = lambda x: x[:, :, s0:s1]
+        oo, hh = O.gated_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
+                                 scale=0.8, initial_state=h0[i:i + 1])
+        ref_o[:, :, s0:s1] = oo
+        ref_ht[i] = hh[0]
+        gr = O.gated_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
+                              sl(inp["do"]), scale=0.8, initial_state=h0[i:i + 1],
+                              d_final_state=dht[i:i + 1])
+        for nm in ("dq", "dk", "dv", "dbeta", "dgate"):
+            ref[nm][:, :, s0:s1] = gr[nm]
+        ref["d_initial_state"][i] = gr["d_initial_state"][0]
+    _check("o", _np(o), ref_o)
+    _check("ht", _np(ht), ref_ht)
+    for nm, t in zip(GRAD_NAMES, grads):
+        _check(nm, _np(t), ref[nm])
