@@ -83,3 +83,41 @@ def test_fullsize_sampled(E, idx, n_streams):
     if grads is not None:
         for t in grads:
             assert torch.isfinite(t.float()).all()
+
+
+@pytest.mark.parametrize("idx,n_streams", [(2, 2), (3, 2)])
+def test_fullsize_gated_sampled(E, idx, n_streams):
+    """Gated EFLA at full size: the benchmark workload forward (saving) + backward, and the
+    long-context workload's forward (segment-parallel scan). Log-decays log sigmoid(x),
+    x ~ N(3, 1) per (batch, head, token), in bf16, as in the benchmark's gated step."""
+    w = workload(idx)
+    print("workload %d (gated): %s" % (idx, w.name), flush=True)
+    inp = make_inputs(w)
+    B, H, T, _ = inp["k"].shape
+    x = np.random.default_rng(77 + idx).standard_normal((B, H, T)) + 3.0
+    a = (-np.logaddexp(0.0, -x)).astype(np.float32)
+    a = torch.from_numpy(a).to(torch.bfloat16).float().numpy()  # the values the GPU sees
+    dt = TDT[w.dtype]
+    q, k, v, beta, g = (_dev(t, dt) for t in (inp["q"], inp["k"], inp["v"], inp["beta"], a))
+    o, saved = E.efla_fwd_gated(q, k, v, beta, g, 1.0, save=w.backward)
+    grads = None
+    if w.backward:
+        grads = E.efla_bwd_gated(q, k, v, beta, g, _dev(inp["do"], dt), saved, 1.0)
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    rng = np.random.default_rng(4321 + idx)
+    for (b, h, s, e) in _samples(inp, n_streams, rng):
+        sl = lambda t: t[b:b + 1, h:h + 1, s:e]
+        ref_o, _ = O.gated_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a))
+        got = o[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
+        err = O.rel_err(got, ref_o)
+        print("  stream b=%d h=%d [%d,%d): o %.3e" % (b, h, s, e, err), flush=True)
+        assert np.all(np.isfinite(got)) and err <= tol
+        if grads is not None:
+            ref = O.gated_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
+                                   sl(inp["do"]))
+            for name, t in zip(("dq", "dk", "dv", "dbeta", "dgate"), grads):
+                gg = t[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
+                err = O.rel_err(gg, ref[name])
+                print("    %s %.3e" % (name, err), flush=True)
+                assert np.all(np.isfinite(gg)) and err <= tol, name
