@@ -243,6 +243,27 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # The same step captured once into a HIP graph and replayed (every kernel still runs; only
+    # the host launches are gone), timed the same way.
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graph
+
     # Per-kernel durations: HIP events recorded by the library around each launch, on the
     # stream the kernel runs on, over a second timed region of the same length.
     E.profile_reset()
@@ -389,6 +410,8 @@ def main():
         "step_mfma_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "roofline": roofline,
+        "hip_graph": {"ms_per_step": round(graph_ms, 4),
+                      "tokens_per_s": round(B * T / (graph_ms * 1e-3), 1)},
         "cold_cache": {"median_ms_per_step": round(cold_ms[len(cold_ms) // 2], 4),
                        "tokens_per_s": round(B * T / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),
                        "steps": len(cold_ms)},

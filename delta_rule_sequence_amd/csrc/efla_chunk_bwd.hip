@@ -33,7 +33,8 @@
 // dP * D, the UT factors are T_w = X diag(alpha Gamma) and T_u = X diag(b) (dT split into
 // dW K^T and dU V^T), A carries D. Every e^c factor also adds to the log-decay gradient dc
 // (accumulated per token in LDS), which a reverse running sum over the chunk turns into the
-// gate gradient, plus db db/da.
+// gate gradient, plus db db/da. Each contribution to dc has its own LDS slot (no atomics), and
+// the slots are summed in a fixed order, so the gate gradient is deterministic.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -57,11 +58,12 @@ struct ChunkBwdLds {
   static constexpr size_t oM = oX + TT;          // dM  [64][LT]
   static constexpr size_t oC = oM + TT;          // lambda, alpha, e^-x, dalpha/dlam [64]
   static constexpr size_t oP = oC + 4 * 64 * 4;  // dalpha partials [64][8]
-  // gated only: c, b, db/dbeta, db/dlam, db/da [64]; dc [64] + two scalars; db column-sum
-  // partials [64][4]
+  // gated only: c, b, db/dbeta, db/dlam, db/da [64]; dc partials [64][kDcSlots] + <G, S>
+  // partials [4]; db column-sum partials [64][4]
+  static constexpr int kDcSlots = 20;
   static constexpr size_t oGc = oP + 8 * 64 * 4;
   static constexpr size_t oDc = oGc + 5 * 64 * 4;
-  static constexpr size_t oDb = oDc + 80 * 4;
+  static constexpr size_t oDb = oDc + (64 * kDcSlots + 4) * 4;
   static constexpr size_t bytes = GT ? oDb + 4 * 64 * 4 : oP + 8 * 64 * 4;
   static_assert(TT <= TV, "64x64 work tiles reuse d_v-wide regions");
 };
@@ -151,7 +153,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   float* cBb = cC + 128;
   float* cBl = cC + 192;
   float* cBa = cC + 256;
-  float* sDc = (float*)(smem + L::oDc);    // gated: dc per token; [64] c_last term; [65] <G, S>
+  // gated: dc partials per token, slots 0-3 state part of dQ . Q (column group), 4-7
+  // r dr (column group), 8-11 dP * P row sums (pair parity, block), 12-15 dP * P column sums
+  // (row block), 16-19 dA * A column sums (row block); then <G, S> per column group
+  constexpr int NS = L::kDcSlots;
+  float* pDc = (float*)(smem + L::oDc);
+  float* pGS = pDc + 64 * NS;
   float* pDb = (float*)(smem + L::oDb);    // gated: db partials [64][4]
 
   int tid = threadIdx.x, lane = tid & 63;
@@ -245,11 +252,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   }
   const float bt_cur = bt, a_cur = aR;
   if constexpr (GT) {
-    if (tid < 64) {
-      cC[tid] = cR;
-      sDc[tid] = 0.f;
-    }
-    if (tid == 0) sDc[64] = sDc[65] = 0.f;
+    if (tid < 64) cC[tid] = cR;
+    for (int i = tid; i < 64 * NS; i += kBwdThreads) pDc[i] = 0.f;
   }
   tDU.store(sDU, LV, n, tid);
   tDO.store(sDO, LV, n, tid);
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       gs = group_sum<16>(gs);
       gs += __shfl_xor(gs, 16);
       gs += __shfl_xor(gs, 32);
-      if (lane == 0) atomicAdd(&sDc[65], gs);
+      if (lane == 0) pGS[wv] = gs;
     }
   }
   {
@@ -340,8 +344,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       p2 += __shfl_xor(p2, 16);
       p2 += __shfl_xor(p2, 32);
       if (lane < 16) {
-        atomicAdd(&sDc[t], p1 - rr * p2);
-        atomicAdd(&sDc[64], rr * p2);
+        pDc[t * NS + (wv & 3)] = p1;
+        pDc[t * NS + 4 + (wv & 3)] = rr * p2;
       }
     }
   }
@@ -365,12 +369,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
           const float ev = mm[e] * (qk[0][j][e] * d);  // dP * P (mm is zero above the diagonal)
           rsum += ev;
           const float csum = group_sum<16>(ev);
-          if ((lane & 15) == 0) atomicAdd(&sDc[s0 + e], -csum);
+          if ((lane & 15) == 0) pDc[(s0 + e) * NS + 12 + pr] = -csum;
           mm[e] *= d;
         }
         rsum += __shfl_xor(rsum, 16);
         rsum += __shfl_xor(rsum, 32);
-        if (lane < 16) atomicAdd(&sDc[t], rsum);
+        if (lane < 16) pDc[t * NS + 8 + 2 * (wv & 1) + j] = rsum;
       }
       st_frag_t<E>(sM + 16 * pr * LT + 16 * (pn + j), LT, mm, lane);
     }
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       if constexpr (GT) {  // dc_s -= sum_t dA_ts A_ts (the row part enters as alpha dalpha)
         fc += __shfl_xor(fc, 16);
         fc += __shfl_xor(fc, 32);
-        if (lane < 16) atomicAdd(&sDc[col], -fc);
+        if (lane < 16) pDc[col * NS + 16 + pr] = -fc;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[i] = group_sum<16>(rs[i]);
@@ -616,8 +620,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       // dgate_t = sum_{s >= t} dc_s + db_t db_t/da_t.
       const float da_t = dalpha(tid), db_t = dbsum(tid);
       if (tid < n) dbeta[row0 + tid] = to_e<E>(da_t * cEx[tid] + db_t * cBb[tid]);
-      float dc = tid < n ? fmaf(cAl[tid], da_t, sDc[tid]) : 0.f;
-      if (tid == n - 1) dc += sDc[64] + exp_decay(cC[tid]) * sDc[65];
+      const float* pt = pDc + tid * NS;
+      float sq = 0.f, rdr = 0.f, se = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sq += pt[j];
+        rdr += pt[4 + j];
+      }
+#pragma unroll
+      for (int j = 8; j < NS; ++j) se += pt[j];
+      float dc = tid < n ? fmaf(cAl[tid], da_t, (sq - rdr) + se) : 0.f;
+      float rsum = group_sum<16>(rdr);  // rows >= n hold zeros
+      rsum += __shfl_xor(rsum, 16);
+      rsum += __shfl_xor(rsum, 32);
+      if (tid == n - 1) dc += rsum + exp_decay(cC[tid]) * ((pGS[0] + pGS[1]) + (pGS[2] + pGS[3]));
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_down(dc, o);
