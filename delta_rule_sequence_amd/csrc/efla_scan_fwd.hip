@@ -12,10 +12,12 @@
 // accumulator directly as their B operand, so the recurrence S -> W S -> U~ -> K^T U~ -> S
 // runs inside one wave's registers with no LDS round trip. Accumulator rows (of S, and the
 // token rows of U~ and O) are numbered in the contiguous-contraction order (prow), so every
-// A operand from LDS is a single 16-byte read. Separate loader waves move the data: they fill swizzled LDS tiles
-// of W, Q, K, M and U one chunk ahead by LDS DMA (double-buffered) and copy the staged O,
-// U~ and chunk states out as 16-byte rows, so the compute waves never stall on memory
-// issue. One barrier per chunk hands the buffers over.
+// A operand from LDS is a single 16-byte read. Two further waves move the data, each in a loop
+// of its own with the same barrier sequence: the loader wave fills swizzled LDS tiles of W, Q,
+// K, M and U one chunk ahead by LDS DMA (double-buffered); the storer wave copies the staged O,
+// U~ and chunk states out as 16-byte rows. An LDS DMA in flight makes the compiler drain every
+// outstanding memory operation of its wave at the next barrier; kept apart from the DMA, the
+// output stores are never waited for. One barrier per chunk hands the buffers over.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -23,7 +25,7 @@ namespace efla {
 template <typename E, int DK, int DV, int NWC, bool GT = false>
 struct ScanFwdLds {
   static constexpr int TV = 16 * NWC;
-  static constexpr int NWL = NWC;  // loader waves
+  static constexpr int NWL = 1;  // loader waves (one; a second wave stores the outputs)
   typedef Swz<E, DK> SK;
   typedef Swz<E, 64> SM;
   typedef Swz<E, TV, 2> SU;  // read in accumulator layout
@@ -50,7 +52,7 @@ struct ScanFwdLds {
 // S <- (I - K^T W) S + K^T U, so running it with U = 0 from S = I (DV = DK) leaves in ht the
 // product of the (I - K^T W) over the sequence; U is neither read nor needed.
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
-__global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
+__global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
     E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
@@ -61,14 +63,14 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   constexpr int TV = L::TV, NWL = L::NWL, NTILE = DV / TV, KC = Mma<E>::KC;
   constexpr int NBK = DK / 16;                 // accumulator tiles of the state slice
   constexpr int KSK = DK / KC, KST = kChunk / KC;
-  constexpr int NTL = 64 * NWL;                // loader threads
+  constexpr int NTL = 64;                      // storer threads (one wave)
   constexpr int VE = 16 / (int)sizeof(E);
   static_assert(DV % TV == 0, "column tiles");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool loader = wi >= NWC;
+  const bool loader = wi == NWC, storer = wi == NWC + 1;
   int sh, tile;
   scan_block(blockIdx.x, g.n_seqs * g.H, NTILE, sh, tile);
   const int s = sh / g.H, h = sh % g.H;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   // h0 / ht: fp32 [n_seqs][H][DK][DV]; this wave's columns
   const int64_t hoff = ((int64_t)s * g.H + h) * DK * DV + v0 + cw + cl;
   if (nchunks <= 0) {  // empty sequence: the state passes through
-    if (ht && !loader) {
+    if (ht && !loader && !storer) {
 #pragma unroll
       for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -95,8 +97,8 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
   const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
   auto rows_of = [&](int c) { return min(kChunk, si.len - c * kChunk); };
 
-  // ---- loader waves
-  const int wl = wi - NWC, tl = tid - 64 * NWC;
+  // ---- loader wave (wl: its index among the loader waves) and storer wave (tl: its lane)
+  const int wl = 0, tl = tid - 64 * (NWC + 1);
   auto issue = [&](int c) {
     unsigned char* st = smem + (c & 1) * L::stage;
     const int n = rows_of(c);
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
       dma_tile<E, 64, NWL>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                            kChunk, kChunk, wl, lane);
     }
-    if constexpr (GT) {  // 64 floats: one plain load per lane of the first loader wave
+    if constexpr (GT) {  // 64 floats: one plain load per lane of the loader wave
       if (wl == 0) ((float*)(st + L::oC))[lane] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
     }
   };
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sacc[b][i] = prow<E>(b, g4 + i) == v0 + cw + cl ? 1.f : 0.f;
-  } else if (h0 && !loader) {  // state entering the sequence
+  } else if (h0 && !loader && !storer) {  // state entering the sequence
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -287,20 +289,32 @@ __global__ __launch_bounds__(128 * NWC, 1) void scan_fwd_kernel(
     }
   };
 
-  if (loader) issue(0);
-  for (int c = 0; c < nchunks; ++c) {
-    if (loader) wait_vm_all();  // chunk c has landed (and older stores are done)
-    __syncthreads();            // chunk c is in LDS; staging of c - 1 is complete
-    if (loader) {
-      if (c > 0) copy_out(c - 1);
+  // Three loops, nchunks + 1 barriers each.
+  if (loader) {
+    issue(0);
+    for (int c = 0; c < nchunks; ++c) {
+      wait_vm_all();    // chunk c has landed
+      __syncthreads();  // chunk c is in LDS; every wave is done with chunk c - 1's stage
       if (c + 1 < nchunks) issue(c + 1);
-    } else {
-      compute(c);
     }
+    __syncthreads();
+    return;
+  }
+  if (storer) {
+    for (int c = 0; c < nchunks; ++c) {
+      __syncthreads();  // staging of chunk c - 1 is complete
+      if (c > 0) copy_out(c - 1);
+    }
+    __syncthreads();
+    copy_out(nchunks - 1);
+    return;
+  }
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();
+    compute(c);
   }
   __syncthreads();
-  if (loader) copy_out(nchunks - 1);
-  if (ht && !loader) {  // state after the last token
+  if (ht) {  // state after the last token
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -325,7 +339,7 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
   hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM, GT>), dim3((unsigned)blocks),
-                     dim3(128 * NWC), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
+                     dim3(64 * NWC + 128), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
                      (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht, cum);
   hipError_t e = hipGetLastError();
   prof_end(PM ? (GT ? "scan_fwd_transition_gated" : "scan_fwd_transition")
@@ -367,8 +381,8 @@ static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, c
   return hipSuccess;
 }
 
-// bf16: two compute waves (32 state columns) and two loader waves per workgroup; fp32: one
-// of each (the double-buffered fp32 tiles leave LDS room for 16 columns of staging only).
+// bf16: two compute waves (32 state columns), a loader and a storer wave per workgroup; fp32:
+// one compute wave (the double-buffered fp32 tiles leave LDS room for 16 columns of staging).
 size_t lds_scan_fwd(Dt dt, int dk, int dv) {
   if (dt == Dt::BF16) {
     if (dk == 64 && dv == 64) return ScanFwdLds<__bf16, 64, 64, 2>::bytes;
