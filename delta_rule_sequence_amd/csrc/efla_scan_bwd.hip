@@ -33,14 +33,16 @@ struct ScanBwdLds {
   static constexpr size_t oO = oM + 64 * LT * sizeof(E);
   static constexpr size_t oCs = oO + 64 * LS * sizeof(E);     // running log-decay sums [64] (GT)
   static constexpr size_t stage = oCs + (GT ? 64 * 4 : 0);
-  static constexpr size_t oG = 2 * stage;                       // G slice [DK][LS]
+  // bf16 with 16-column tiles: one stage, so that two workgroups share a compute unit
+  static constexpr int NSTG = (sizeof(E) == 2 && TV == 16) ? 1 : 2;
+  static constexpr size_t oG = NSTG * stage;                    // G slice [DK][LS]
   static constexpr size_t oDt = oG + DK * LS * sizeof(E);       // dU~^T  [TV][LT]
   static constexpr size_t oDu = oDt + TV * LT * sizeof(E);      // dU~ staging [64][LS]
   static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
 };
 
 template <typename E, int DK, int DV, int TV, bool GT>
-__global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
+__global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) void scan_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
     E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0,
@@ -162,11 +164,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
   }
   if (nchunks > 0) {
     load_chunk(nchunks - 1);
-    commit_chunk(nchunks - 1, smem + ((nchunks - 1) & 1) * L::stage);
+    commit_chunk(nchunks - 1, smem + (L::NSTG == 2 ? ((nchunks - 1) & 1) : 0) * L::stage);
   }
 
   for (int c = nchunks - 1; c >= 0; --c) {
-    unsigned char* stc = smem + (c & 1) * L::stage;
+    unsigned char* stc = smem + (L::NSTG == 2 ? (c & 1) : 0) * L::stage;
     const E* sQ = (const E*)(stc + L::oQ);
     const E* sW = (const E*)(stc + L::oW);
     const E* sM = (const E*)(stc + L::oM);
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
       const f32x4 b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
       Gt[i] = gC * Gt[i] + (g.scale * a - b);
     }
-    if (more) commit_chunk(c - 1, smem + ((c - 1) & 1) * L::stage);
+    if constexpr (L::NSTG == 1) __syncthreads();  // every wave is done with the stage
+    if (more) commit_chunk(c - 1, smem + (L::NSTG == 2 ? ((c - 1) & 1) : 0) * L::stage);
   }
   if (dh0) {  // gradient at the state entering the sequence
 #pragma unroll
