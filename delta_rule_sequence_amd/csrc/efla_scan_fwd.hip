@@ -328,6 +328,7 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
                                void* states, const float* h0, float* ht, hipStream_t st,
                                const float* cum = nullptr) {
   typedef ScanFwdLds<E, DK, DV, NWC, GT> L;
+  static_assert(L::bytes <= 160 * 1024, "LDS budget");
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM, GT>,
