@@ -140,20 +140,20 @@ def cpu_baseline():
 
 
 def long_context(E, make_inputs, workload, warmup, iters):
-    """Forward of the B=1, H=16, T=32768, d=128 bf16 workload: segment-parallel scan (segments
-    chosen by the library) and a single sequential chain per sequence, same buffers."""
+    """B=1, H=16, T=32768, d=128 bf16 (few sequence-head pairs, long sequences): the forward
+    alone (inference), and forward + backward (training step), each with the segment-parallel
+    scans (segments chosen by the library) and with a single sequential chain per sequence."""
     import torch
     w = workload(3)
-    inp = make_inputs(w, with_grad=False)
-    q, k, v, beta = (torch.from_numpy(inp[n]).to("cuda", torch.bfloat16)
-                     for n in ("q", "k", "v", "beta"))
+    inp = make_inputs(w, with_grad=True)
+    q, k, v, beta, do = (torch.from_numpy(inp[n]).to("cuda", torch.bfloat16)
+                         for n in ("q", "k", "v", "beta", "do"))
     o = torch.empty_like(v)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(beta))
     res = {"workload": "efla_fwd_B1_H16_T32768_d128_bf16"}
     lay = None
-    for segs, key in ((0, "segmented"), (1, "sequential")):
-        p = E.make_problem(q, k, v, beta, segments=segs)
-        ws = torch.empty(E.efla_workspace_bytes(p, False), dtype=torch.uint8, device="cuda")
-        f = lambda: E.efla_fwd(q, k, v, beta, 1.0, None, False, ws, o=o, segments=segs)
+
+    def timed(f):
         for _ in range(warmup):
             f()
         torch.cuda.synchronize()
@@ -161,15 +161,32 @@ def long_context(E, make_inputs, workload, warmup, iters):
         for _ in range(iters):
             f()
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / iters
-        res[key] = {"ms_fwd": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1)}
+        return (time.perf_counter() - t0) * 1e3 / iters
+
+    for segs, key in ((0, "segmented"), (1, "sequential")):
+        p = E.make_problem(q, k, v, beta, segments=segs)
+        ws = torch.empty(max(E.efla_workspace_bytes(p, False), E.efla_workspace_bytes(p, True)),
+                         dtype=torch.uint8, device="cuda")
+        saved = torch.empty(E.efla_saved_bytes(p), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: E.efla_fwd(q, k, v, beta, 1.0, None, False, ws, o=o, segments=segs))
+
+        def step():
+            E.efla_fwd(q, k, v, beta, 1.0, None, True, ws, o=o, saved=saved, segments=segs)
+            E.efla_bwd(q, k, v, beta, do, saved, 1.0, None, ws, grads=grads, segments=segs)
+
+        ms_step = timed(step)
+        res[key] = {"ms_fwd": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+                    "ms_fwd_bwd": round(ms_step, 4),
+                    "fwd_bwd_tokens_per_s": round(w.B * w.T / (ms_step * 1e-3), 1)}
         if segs == 0:
             lay = E.efla_workspace_bytes(p, False) - E.efla_workspace_bytes(
                 E.make_problem(q, k, v, beta, segments=1), False)
+        del ws, saved
     # segments the library chose: extra workspace / (4 H dk (2 dv + dk)) bytes per segment
     res["segments"] = int(lay // (4 * w.H * w.dk * (2 * w.dv + w.dk)))
     res["speedup"] = round(res["sequential"]["ms_fwd"] / res["segmented"]["ms_fwd"], 3)
-    del q, k, v, beta, o
+    res["fwd_bwd_speedup"] = round(res["sequential"]["ms_fwd_bwd"] / res["segmented"]["ms_fwd_bwd"], 3)
+    del q, k, v, beta, o, do, grads
     return res
 
 

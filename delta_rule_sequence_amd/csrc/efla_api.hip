@@ -431,18 +431,22 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
       !aligned16(dht) || !aligned16(dh0))
     return EFLA_ERR_ALIGN;
   const Saved L = saved_layout(s);
-  const size_t need = saved ? align_up(bytes_v(s)) + align_up(bytes_states(s)) : ws_bwd(s);
+  const size_t seg_bytes = s.seg_plan > 1 ? bytes_seg(s) : 0;
+  const size_t need =
+      saved ? align_up(bytes_v(s)) + align_up(bytes_states(s)) + seg_bytes : ws_bwd(s);
   if (ws_bytes < need) return EFLA_ERR_WORKSPACE;
   if (saved && saved_bytes < L.total) return EFLA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   unsigned char* wsb = (unsigned char*)ws;
   unsigned char* dut = wsb;
   unsigned char* dstates = dut + align_up(bytes_v(s));
+  // segment buffers: after the gradients with a saved buffer, else after the recomputed one
+  unsigned char* seg = dstates + align_up(bytes_states(s));
   const unsigned char* sv = (const unsigned char*)saved;
   if (!sv) {
     unsigned char* rec = dstates + align_up(bytes_states(s));
     unsigned char* u = rec + L.total;
-    unsigned char* seg = u + align_up(bytes_v(s));
+    seg = u + align_up(bytes_v(s));
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
                                     rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
                                     u, h0, nullptr, seg, st, gate, (float*)(rec + L.cum)))
@@ -451,9 +455,27 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
   }
   const int* table = (const int*)(sv + L.table);
   const float* cum = gate ? (const float*)(sv + L.cum) : nullptr;
-  if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o, dut,
-                                                 dstates, dht, dh0, st, cum)))
+  if (s.seg_plan > 1) {
+    // Segment-parallel reverse scan: zero-start gradients R and transitions A of all segments,
+    // the chain over segments from the last (dht) to the first (dh0), then the full scan over
+    // all segments from the gradient entering each from its end.
+    const Shape svw = segment_view(s);
+    float* R = (float*)seg;
+    float* G_in = (float*)(seg + align_up(bytes_seg_state(s)));
+    float* A = (float*)(seg + 2 * align_up(bytes_seg_state(s)));
+    if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, sv + L.w, sv + L.m, d_o,
+                                                   nullptr, nullptr, nullptr, R, st, cum, true)))
+      return r;
+    if (efla_status r = hip_status(launch_scan_bwd_transition(svw, table, k, sv + L.w, A, st, cum)))
+      return r;
+    if (efla_status r = hip_status(launch_seg_combine(s, A, R, dht, G_in, dh0, st, true))) return r;
+    if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, sv + L.w, sv + L.m, d_o, dut,
+                                                   dstates, G_in, nullptr, st, cum)))
+      return r;
+  } else if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o,
+                                                        dut, dstates, dht, dh0, st, cum))) {
     return r;
+  }
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,
                                      dstates, sv + L.x, dq, dk, dv, dbeta, st, gate, cum, dgate));
 }

@@ -19,6 +19,13 @@
 // r = e^{c_last - c}: dU~ = scale P^T dO + diag(r) K G (P = tril(Q K^T) * e^{c_t - c_s}, saved
 // by the forward in place of M) and G <- e^{c_last} G + scale Q^T diag(Gamma) dO - W^T dU~.
 // Q rows are scaled by Gamma when they land in LDS; the rest acts on accumulators.
+//
+// Segment-parallel backward (long sequences, few sequence-head pairs). The chunk step is affine
+// in the state gradient, G <- (I - W^T K) G + scale (Q - M W)^T dO (gated: with the decays), so
+// a segment of chunks maps the gradient leaving it to the one entering it as A G + R. MODE 1
+// (state only) runs from zero and keeps only the result, R; MODE 2 (transition) runs with dO
+// taken as zero from G = I (d_v = d_k), giving A. MODE 0 is the full scan that writes dU~ and
+// the per-chunk gradients.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -41,7 +48,7 @@ struct ScanBwdLds {
   static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
 };
 
-template <typename E, int DK, int DV, int TV, bool GT>
+template <typename E, int DK, int DV, int TV, bool GT, int MODE>
 __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) void scan_bwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
@@ -75,6 +82,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   const int rA = 16 * wv;
   const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
 
+  constexpr bool OUT = MODE == 0, TR = MODE == 2;  // write dU~ and dS_c; transition
   V kA[KS], kN[KS];
   u32x4 qR[VQ], wR[VQ], mR[VM], oR[VO];
   float cQ[VQ], cR = 0.f;  // gated: running log-decay sums of the Q rows / of token lane
@@ -89,19 +97,21 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
-      qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
+      if constexpr (!TR) qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
       wR[it] = *(const u32x4*)(w + (r0 + r) * DK + cc);
-      if constexpr (GT) cQ[it] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + r];
+      if constexpr (GT && !TR) cQ[it] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + r];
     }
     if constexpr (GT) cR = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
-    const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
+    if constexpr (!TR) {  // M and dO only enter through the dO term
+      const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
 #pragma unroll
-    for (int it = 0; it < VM; ++it) mR[it] = *(const u32x4*)(mc + (it * kThreads + tid) * VE);
+      for (int it = 0; it < VM; ++it) mR[it] = *(const u32x4*)(mc + (it * kThreads + tid) * VE);
 #pragma unroll
-    for (int it = 0; it < VO; ++it) {  // unconditional (clamped) so no load sits in a branch
-      const int i = min(it * kThreads + tid, 64 * OPR - 1);
-      const int r = min(i / OPR, n - 1), cc = (i % OPR) * VE;
-      oR[it] = *(const u32x4*)(d_o + (r0 + r) * DV + v0 + cc);
+      for (int it = 0; it < VO; ++it) {  // unconditional (clamped) so no load sits in a branch
+        const int i = min(it * kThreads + tid, 64 * OPR - 1);
+        const int r = min(i / OPR, n - 1), cc = (i % OPR) * VE;
+        oR[it] = *(const u32x4*)(d_o + (r0 + r) * DV + v0 + cc);
+      }
     }
   };
   auto commit_chunk = [&](int c, unsigned char* st) {
@@ -117,6 +127,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
+      *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
+      if constexpr (TR) continue;
       u32x4 qv = qR[it];
       if constexpr (GT) {  // Q rows scaled by Gamma = e^c
         const float gm = exp_decay(cQ[it]);
@@ -126,22 +138,23 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
         qv = __builtin_bit_cast(u32x4, x);
       }
       *(u32x4*)(sQ + r * L::LK + cc) = keep_if(qv, r < n);
-      *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
     }
     if constexpr (GT) {
       if (tid < 64) ((float*)(st + L::oCs))[tid] = cR;
     }
+    if constexpr (!TR) {
 #pragma unroll
-    for (int it = 0; it < VM; ++it) {
-      const int i = (it * kThreads + tid) * VE;
-      *(u32x4*)(sM + (i / 64) * L::LT + i % 64) = mR[it];
-    }
+      for (int it = 0; it < VM; ++it) {
+        const int i = (it * kThreads + tid) * VE;
+        *(u32x4*)(sM + (i / 64) * L::LT + i % 64) = mR[it];
+      }
 #pragma unroll
-    for (int it = 0; it < VO; ++it) {
-      const int i = it * kThreads + tid;
-      if (i < 64 * OPR) {
-        const int r = i / OPR, cc = (i % OPR) * VE;
-        *(u32x4*)(sO + r * L::LS + cc) = keep_if(oR[it], r < n);
+      for (int it = 0; it < VO; ++it) {
+        const int i = it * kThreads + tid;
+        if (i < 64 * OPR) {
+          const int r = i / OPR, cc = (i % OPR) * VE;
+          *(u32x4*)(sO + r * L::LS + cc) = keep_if(oR[it], r < n);
+        }
       }
     }
   };
@@ -157,7 +170,12 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     Gt[i] = zero4();
-    if (dht) {
+    if constexpr (TR) {  // G = I (d_v = d_k): this slice's columns
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Gt[i][e] = 16 * db + (lane & 15) == v0 + 16 * vb + 4 * (lane >> 4) + e ? 1.f : 0.f;
+    } else if (dht) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
     }
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     load_chunk(more ? c - 1 : c);
     __syncthreads();
 
-    {  // G of this slot -> dstates [d][v0 : v0 + TV]
+    if constexpr (OUT) {  // G of this slot -> dstates [d][v0 : v0 + TV]
       E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
       constexpr int VPR = TV / VE;
       for (int i = tid; i < DK * VPR; i += kThreads) {
@@ -201,7 +219,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * L::LS + 16 * nb, L::LS, lane), kg);
-      md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
+      if constexpr (!TR)
+        md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
       if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
         const float cl = sCs[n - 1];
 #pragma unroll
@@ -209,17 +228,18 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
       }
       f32x4 du = kg + g.scale * md;
       st_frag_t<E>(sDt + 16 * nb * L::LT + rA, L::LT, du, lane);
-      st_frag_lds<E>(sDu + rA * L::LS + 16 * nb, L::LS, du, lane);
+      if constexpr (OUT) st_frag_lds<E>(sDu + rA * L::LS + 16 * nb, L::LS, du, lane);
     }
     __syncthreads();
 
-    s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, L::LS, n, tid);
+    if constexpr (OUT) s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, L::LS, n, tid);
     // G^T += scale dO^T Q - dU~^T W (gated: G^T <- e^{c_last} G^T + ..., Q pre-scaled)
     const float gC = GT ? exp_decay(sCs[n - 1]) : 1.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
-      const f32x4 a = mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
+      const f32x4 a =
+          TR ? zero4() : mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
       const f32x4 b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
       Gt[i] = gC * Gt[i] + (g.scale * a - b);
     }
@@ -234,7 +254,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   }
 }
 
-template <typename E, int DK, int DV, int TV, bool GT>
+template <typename E, int DK, int DV, int TV, bool GT, int MODE>
 static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* m, const void* d_o, void* dut,
                                void* dstates, const float* dht, float* dh0, hipStream_t st,
@@ -242,7 +262,7 @@ static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, 
   typedef ScanBwdLds<E, DK, DV, TV, GT> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_kernel<E, DK, DV, TV, GT>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_kernel<E, DK, DV, TV, GT, MODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -250,26 +270,38 @@ static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, 
   const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / TV);
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
-  hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV, GT>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV, GT, MODE>), dim3((unsigned)blocks), dim3(kThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
                      (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
   hipError_t e = hipGetLastError();
-  prof_end(GT ? "scan_bwd_gated" : "scan_bwd", st);
+  static const char* const names[2][3] = {{"scan_bwd", "scan_bwd_state", "scan_bwd_transition"},
+                                           {"scan_bwd_gated", "scan_bwd_state_gated", "scan_bwd_transition_gated"}};
+  prof_end(names[GT][MODE], st);
   return e;
+}
+
+template <typename E, int DK, int DV, int TV, int MODE>
+static hipError_t scan_bwd_mode(const Shape& s, const int* table, const void* q, const void* k,
+                                const void* w, const void* m, const void* d_o, void* dut,
+                                void* dstates, const float* dht, float* dh0, hipStream_t st,
+                                const float* cum) {
+  if (cum) {
+    if constexpr (sizeof(E) == 2)
+      return scan_bwd_run<E, DK, DV, TV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+    else
+      return hipErrorInvalidValue;
+  }
+  return scan_bwd_run<E, DK, DV, TV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
 }
 
 template <typename E, int DK, int DV, int TV>
 static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* m, const void* d_o, void* dut,
                               void* dstates, const float* dht, float* dh0, hipStream_t st,
-                              const float* cum) {
-  if (cum) {
-    if constexpr (sizeof(E) == 2)
-      return scan_bwd_run<E, DK, DV, TV, true>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
-    else
-      return hipErrorInvalidValue;
-  }
-  return scan_bwd_run<E, DK, DV, TV, false>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+                              const float* cum, int mode) {
+  if (mode == 1)
+    return scan_bwd_mode<E, DK, DV, TV, 1>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+  return scan_bwd_mode<E, DK, DV, TV, 0>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
 }
 
 size_t lds_scan_bwd(Dt dt, int dk, int dv) {
@@ -287,9 +319,10 @@ size_t lds_scan_bwd(Dt dt, int dk, int dv) {
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
                            void* dstates, const float* dht, float* dh0, hipStream_t st,
-                           const float* cum) {
+                           const float* cum, bool state_only) {
+  const int mode = state_only ? 1 : 0;
 #define EFLA_SB(E_, DK_, DV_, TV_) \
-  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum)
+  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, mode)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SB(__bf16, 64, 64, 16);
     if (s.dk == 128 && s.dv == 64) EFLA_SB(__bf16, 128, 64, 16);
@@ -302,6 +335,26 @@ hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, cons
   }
   EFLA_SB(float, 64, 64, 16);
 #undef EFLA_SB
+}
+
+}  // namespace efla
+
+namespace efla {
+
+hipError_t launch_scan_bwd_transition(const Shape& s, const int* table, const void* k,
+                                      const void* w, float* p, hipStream_t st, const float* cum) {
+  Shape t = s;
+  t.dv = s.dk;  // the map acts on d_k x d_k
+#define EFLA_ST(E_, DK_, TV_)                                                                    \
+  return scan_bwd_mode<E_, DK_, DK_, TV_, 2>(t, table, nullptr, k, w, nullptr, nullptr, nullptr, \
+                                             nullptr, nullptr, p, st, cum)
+  if (s.dt == Dt::BF16) {
+    if (s.dk == 64) EFLA_ST(__bf16, 64, 16);
+    if (scan_tile(t) == 16) EFLA_ST(__bf16, 128, 16);
+    EFLA_ST(__bf16, 128, 32);
+  }
+  EFLA_ST(float, 64, 16);
+#undef EFLA_ST
 }
 
 }  // namespace efla

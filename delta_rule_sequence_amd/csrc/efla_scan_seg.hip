@@ -8,7 +8,8 @@
 // this kernel then walks the segments of each sequence in order,
 //   S_0 = h0 (or 0),  S_{j+1} = P_j S_j + R_j,
 // writing the state entering every segment (the initial state of the second, output-writing
-// scan over the segments) and the state after the last one. States, P and R are held in
+// scan over the segments) and the state after the last one. The backward pass chains its state
+// gradients the same way with the segments taken from the last to the first. States, P and R are held in
 // fp32; P_j and S enter the products in the problem dtype, as W and S do in the scan.
 //
 // One workgroup per (batch row, head). Each wave owns 16 state columns and keeps them in
@@ -29,7 +30,7 @@ struct SegLds {
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
-    int H, int G, const float* __restrict__ P, const float* __restrict__ R,
+    int H, int G, int rev, const float* __restrict__ P, const float* __restrict__ R,
     const float* __restrict__ h0, float* __restrict__ sin, float* __restrict__ ht) {
   typedef SegLds<E, DK> L;
   typedef typename L::SP SP;
@@ -45,9 +46,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
   auto at = [&](const float* base, int64_t seq, int bb, int i) {
     return base + ((seq * H + h) * DK + prow<E>(bb, g4 + i)) * (int64_t)DV + col;
   };
-  auto stage = [&](int j) {  // P_j (fp32) -> LDS buffer j & 1 in the problem dtype
+  // processing step j handles segment seg(j): j itself, or G - 1 - j when walking backwards
+  auto seg = [&](int j) { return rev ? G - 1 - j : j; };
+  auto stage = [&](int j) {  // P of step j (fp32) -> LDS buffer j & 1 in the problem dtype
     unsigned char* dst = smem + (j & 1) * L::TILE;
-    const float* Pj = P + (((int64_t)b * G + j) * H + h) * DK * DK;
+    const float* Pj = P + (((int64_t)b * G + seg(j)) * H + h) * DK * DK;
     for (int i = tid; i < DK * DK / VE; i += NT) {
       const int r = i / (DK / VE), c = (i % (DK / VE)) * VE;
       if constexpr (sizeof(E) == 2) {
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
 #pragma unroll
     for (int bb = 0; bb < NBK; ++bb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Rn[bb][i] = *at(R, (int64_t)b * G + j, bb, i);
+      for (int i = 0; i < 4; ++i) Rn[bb][i] = *at(R, (int64_t)b * G + seg(j), bb, i);
   };
 #pragma unroll
   for (int bb = 0; bb < NBK; ++bb)
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
   }
   __syncthreads();
   for (int j = 0; j < G; ++j) {
-    const int64_t sj = (int64_t)b * G + j;
+    const int64_t sj = (int64_t)b * G + seg(j);
 #pragma unroll
     for (int bb = 0; bb < NBK; ++bb)
 #pragma unroll
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
 
 template <typename E, int DK, int DV>
 static hipError_t seg_combine_go(const Shape& s, const float* p, const float* r, const float* h0,
-                                 float* sin, float* ht, hipStream_t st) {
+                                 float* sin, float* ht, hipStream_t st, bool rev) {
   typedef SegLds<E, DK> L;
   static bool attr = false;
   if (!attr) {
@@ -128,21 +131,21 @@ static hipError_t seg_combine_go(const Shape& s, const float* p, const float* r,
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
   hipLaunchKernelGGL((seg_combine_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(64 * (DV / 16)),
-                     L::bytes, st, s.H, s.seg_plan, p, r, h0, sin, ht);
+                     L::bytes, st, s.H, s.seg_plan, rev ? 1 : 0, p, r, h0, sin, ht);
   hipError_t e = hipGetLastError();
   prof_end("seg_combine", st);
   return e;
 }
 
 hipError_t launch_seg_combine(const Shape& s, const float* p, const float* r, const float* h0,
-                              float* sin, float* ht, hipStream_t st) {
+                              float* sin, float* ht, hipStream_t st, bool rev) {
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) return seg_combine_go<__bf16, 64, 64>(s, p, r, h0, sin, ht, st);
-    if (s.dk == 64 && s.dv == 128) return seg_combine_go<__bf16, 64, 128>(s, p, r, h0, sin, ht, st);
-    if (s.dk == 128 && s.dv == 64) return seg_combine_go<__bf16, 128, 64>(s, p, r, h0, sin, ht, st);
-    return seg_combine_go<__bf16, 128, 128>(s, p, r, h0, sin, ht, st);
+    if (s.dk == 64 && s.dv == 64) return seg_combine_go<__bf16, 64, 64>(s, p, r, h0, sin, ht, st, rev);
+    if (s.dk == 64 && s.dv == 128) return seg_combine_go<__bf16, 64, 128>(s, p, r, h0, sin, ht, st, rev);
+    if (s.dk == 128 && s.dv == 64) return seg_combine_go<__bf16, 128, 64>(s, p, r, h0, sin, ht, st, rev);
+    return seg_combine_go<__bf16, 128, 128>(s, p, r, h0, sin, ht, st, rev);
   }
-  return seg_combine_go<float, 64, 64>(s, p, r, h0, sin, ht, st);
+  return seg_combine_go<float, 64, 64>(s, p, r, h0, sin, ht, st, rev);
 }
 
 }  // namespace efla

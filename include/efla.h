@@ -73,11 +73,12 @@ typedef struct {
   const int32_t* cu_seqlens;    /* device pointer or NULL (see packed batches above) */
   int32_t n_seqs;               /* number of packed sequences when cu_seqlens is set */
   int32_t mode;                 /* efla_mode; other values return EFLA_ERR_UNSUPPORTED */
-  int32_t segments;             /* forward scan of long sequences, dense batches only (packed
-                                   batches always use 1): 0 = chosen by the library, 1 = one
-                                   sequential chain of chunks per sequence, n >= 2 = split each
-                                   sequence into at most n segments scanned in parallel
-                                   (segment-parallel scan, see efla_fwd); < 0 = EFLA_ERR_SHAPE */
+  int32_t segments;             /* state scans of long sequences (forward and backward),
+                                   dense batches only (packed batches always use 1): 0 = chosen
+                                   by the library, 1 = one sequential chain of chunks per
+                                   sequence, n >= 2 = split each sequence into at most n
+                                   segments scanned in parallel (segment-parallel scan, see
+                                   efla_fwd and efla_bwd_state); < 0 = EFLA_ERR_SHAPE */
 } efla_problem;
 
 /* Byte offsets of the tensors inside the buffer that efla_fwd saves for efla_bwd.
@@ -188,7 +189,13 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
                      void* stream);
 
 /* Backward with recurrent state I/O: the gradient of sum(o * d_o) + <ht, dht> with respect to
- * q, k, v, beta and h0. h0 must be what the forward used (only read when saved == NULL; NULL =
+ * q, k, v, beta and h0. With a segment plan (efla_problem.segments) the reverse state-gradient
+ * scan is segment-parallel like the forward's: going backwards a chunk maps the gradient
+ * affinely, G <- (I - W^T K) G + scale (Q - M W)^T dO, so each segment's composed map A and
+ * zero-start gradient R are formed in parallel, chained from the last segment to the first,
+ * and the full scan then runs over all segments from their incoming gradients; with a saved
+ * buffer the workspace then needs 4 B G H dk (2 dv + dk) more bytes (never more than
+ * efla_workspace_bytes(p, 1)). h0 must be what the forward used (only read when saved == NULL; NULL =
  * zero); dht (NULL = zero) is the gradient arriving at the final states; dh0 (NULL = not
  * written) receives the gradient at the initial states. fp32 [n_state][H][dk][dv] each. */
 efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,

@@ -107,3 +107,54 @@ def test_segmented_euler_mode(E):
     torch.cuda.synchronize()
     ref_o, _ = O.forward(inp["q"], inp["k"], inp["v"], inp["beta"], mode="euler")
     _check("o", _np(o), ref_o, TOL["bf16"])
+
+
+BWD_CASES = [  # name, workload overrides, segments, mode
+    ("bf16_seg2", dict(idx=2, B=1, H=2, T=64 * 33 + 7), 2, "exact"),
+    ("bf16_seg5", dict(idx=2, B=2, H=1, T=64 * 37 + 5), 5, "exact"),
+    ("bf16_seg_per_chunk", dict(idx=2, B=1, H=1, T=64 * 9 + 30), 64, "exact"),
+    ("f32_seg3", dict(idx=4, B=1, H=2, T=64 * 20 + 3), 3, "exact"),
+    ("bf16_dk64_dv128", dict(idx=2, B=1, H=2, T=64 * 12 + 40, dk=64, dv=128), 3, "exact"),
+    ("bf16_dk128_dv64", dict(idx=2, B=1, H=2, T=64 * 12 + 40, dk=128, dv=64), 3, "exact"),
+    ("bf16_delta_rule", dict(idx=2, B=1, H=2, T=64 * 16), 4, "euler"),
+]
+
+
+@pytest.mark.parametrize("name,wl,segments,mode", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_segmented_backward_with_state_gradients(E, name, wl, segments, mode):
+    """Segment-parallel reverse scan (zero-start gradients and transitions of all segments, the
+    chain from the last segment to the first, then the full scan from each segment's incoming
+    gradient): every gradient, including the one arriving at the final state and the one
+    leaving the initial state, against the oracle and against the unsegmented backward. The
+    segment chain applies each segment's transition to the incoming gradient as one bf16 product
+    (one extra rounding per segment), so the two bf16 scans agree to the parity tolerance, not
+    to rounding (fp32 agrees to 5e-5)."""
+    wl = dict(wl)
+    w = workload(wl.pop("idx"), **wl)
+    inp = make_inputs(w, with_grad=True)
+    if mode == "euler":
+        from workloads import round_to_bf16
+        kk = inp["k"] / np.maximum(np.linalg.norm(inp["k"], axis=-1, keepdims=True), 1e-30)
+        inp["k"] = round_to_bf16(kk.astype(np.float32))
+    dt, tol = TDT[w.dtype], TOL[w.dtype]
+    B, H, T, dk = inp["k"].shape
+    dv = inp["v"].shape[-1]
+    r = np.random.default_rng(8)
+    h0 = (r.standard_normal((B, H, dk, dv)) * 0.3).astype(np.float32)
+    dht = (r.standard_normal((B, H, dk, dv)) * 0.2).astype(np.float32)
+    q, k, v, beta, do = (_dev(inp[n], dt) for n in ("q", "k", "v", "beta", "do"))
+    h0_d, dht_d = _dev(h0, torch.float32), _dev(dht, torch.float32)
+    print("%s: B=%d H=%d T=%d dk=%d dv=%d segments=%d mode=%s" % (name, B, H, T, dk, dv, segments, mode),
+          flush=True)
+    _, saved = E.efla_fwd(q, k, v, beta, 0.8, None, save=True, initial_state=h0_d, mode=mode, segments=1)
+    g = E.efla_bwd(q, k, v, beta, do, saved, 0.8, None, mode=mode, initial_state=h0_d,
+                   d_final_state=dht_d, d_initial_state=True, segments=segments)
+    g1 = E.efla_bwd(q, k, v, beta, do, saved, 0.8, None, mode=mode, initial_state=h0_d,
+                    d_final_state=dht_d, d_initial_state=True, segments=1)
+    torch.cuda.synchronize()
+    ref = O.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["do"], scale=0.8, initial_state=h0,
+                     d_final_state=dht, mode=mode)
+    for nm, t, t1 in zip(("dq", "dk", "dv", "dbeta", "d_initial_state"), g, g1):
+        _check(nm, _np(t), ref[nm], tol)
+        assert O.rel_err(_np(t), _np(t1)) <= (tol if w.dtype == "bf16" else tol / 2), \
+            nm + " differs from the unsegmented scan"
