@@ -75,6 +75,13 @@ def _p(**kw):
     (dict(segments=64), 0),
     (dict(segments=-1), 2),
     (dict(B=1, cu=0x1000, n_seqs=3, segments=4), 0),   # packed: accepted, scan not split
+    # index limits: B*H*T*max(dk, dv) below 2^40, state slots * H below 2^31
+    (dict(B=64, H=64, T=2**21 - 1), 0),
+    (dict(B=64, H=64, T=2**21), 4),
+    (dict(B=64, H=64, T=2**21, dk=64, dv=64), 0),
+    (dict(B=64, H=64, T=2**21, dk=64, dv=128), 4),
+    (dict(B=1, H=4, T=1024, cu=0x1000, n_seqs=2**29 - 17), 0),
+    (dict(B=1, H=4, T=1024, cu=0x1000, n_seqs=2**29 - 16), 4),
 ])
 def test_problem_validation(L, kw, code):
     p = _p(**kw)
