@@ -364,8 +364,11 @@ EFLA_DEV void g2s_t(E* s, int ld, const E* __restrict__ g, int64_t gld, int nval
     g2s_t_impl_bf16<COLS>((__bf16*)s, ld, (const __bf16*)g, gld, nvalid, tid);
 }
 
-// Copy 64 rows of an LDS tile to global memory with 16-byte stores, rows < nvalid only
-// (NT threads cooperate).
+// Copy rows [0, nvalid) of a 64-row LDS tile to global memory with 16-byte stores (NT threads
+// cooperate, 1 <= nvalid <= 64). Every thread stores on every step: work past the end is
+// clamped onto the last row and chunk, so those lanes write the same bytes again. With no store
+// inside a branch the compiler knows how many stores follow an earlier load and waits for that
+// load alone, not for the stores.
 template <typename E, int COLS, int NT = kThreads>
 EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid, int tid) {
   constexpr int V = 16 / sizeof(E);
@@ -373,14 +376,12 @@ EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid
   constexpr int TOT = kChunk * VPR;
 #pragma unroll
   for (int it = 0; it < (TOT + NT - 1) / NT; ++it) {
-    const int i = it * NT + tid;
-    if (TOT % NT == 0 || i < TOT) {
-      const int r = i / VPR, c = (i % VPR) * V;
-      // 32-bit unsigned element offset from the (uniform) tile base: the store can use the
-      // scalar-base addressing form instead of a 64-bit address per lane.
-      const unsigned off = ((unsigned)r * (unsigned)gld + (unsigned)c) * (unsigned)sizeof(E);
-      if (r < nvalid) *at_byte<u32x4>(g, off) = *(const u32x4*)(s + r * ld + c);
-    }
+    const int i = TOT % NT == 0 ? it * NT + tid : min(it * NT + tid, TOT - 1);
+    const int r = min(i / VPR, nvalid - 1), c = (i % VPR) * V;
+    // 32-bit unsigned element offset from the (uniform) tile base: the store can use the
+    // scalar-base addressing form instead of a 64-bit address per lane.
+    const unsigned off = ((unsigned)r * (unsigned)gld + (unsigned)c) * (unsigned)sizeof(E);
+    *at_byte<u32x4>(g, off) = *(const u32x4*)(s + r * ld + c);
   }
 }
 
@@ -429,6 +430,28 @@ EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld,
 // Wait until this wave's outstanding vector memory operations (loads, stores, LDS DMA) are
 // done: s_waitcnt vmcnt(0).
 EFLA_DEV void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// L2 warm-up for a later read of bytes [0, nbytes) at p (nbytes > 0). Part `part` of `nparts`
+// (the workgroups that will all read the range) is shared by NT threads; thread `lane` of them
+// takes the 128-byte lines part + nparts (lane + NT i), i < N, and loads one word of each into
+// w. A line index past the end is clamped to the last line, so every address stays inside the
+// range. The caller leaves w alone until l2_sink, so no wait for these loads is placed before
+// that point.
+template <int N, int NT = 64>
+EFLA_DEV void l2_touch(int* w, const void* p, int nbytes, int part, int nparts, int lane) {
+  const int last = (nbytes - 1) >> 7;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int j = min(part + nparts * (lane + NT * i), last);
+    w[i] = *(const int*)((const char*)p + (j << 7));
+  }
+}
+// Consumes the words of l2_touch: the compiler waits for those loads here and nowhere earlier.
+template <int N>
+EFLA_DEV void l2_sink(const int* w) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(w[i]));
+}
 
 // MFMA operands in the accumulator-compatible contraction order. A 16x16 accumulator tile
 // holds rows 4 (lane >> 4) + i of column lane & 15, so for a product whose contraction index

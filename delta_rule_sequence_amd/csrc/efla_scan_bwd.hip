@@ -180,8 +180,33 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
       for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
     }
   }
+  // L2 warm-up two chunks ahead of the compute (one word per 128-byte line; the workgroups of
+  // the (sequence, head) split the shared tiles): the register loads of chunk c - 1, issued a
+  // step later, then hit L2, and HBM keeps a request stream across the barriers. Each warm-up is
+  // consumed right after the next step's register loads are issued, so it is waited for there,
+  // a step after it was issued, and never together with a load still in flight.
+  constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * kThreads - 1) /
+                     (NTILE * kThreads);
+  int pw[5 * NL];
+#pragma unroll
+  for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
+  auto warm = [&](int c) {
+    const int n = min(kChunk, si.len - c * kChunk);
+    const int64_t r0 = base + (int64_t)c * kChunk;
+    const int bk = n * DK * (int)sizeof(E);
+    l2_touch<NL, kThreads>(pw, w + r0 * DK, bk, tile, NTILE, tid);
+    l2_touch<NL, kThreads>(pw + NL, k + r0 * DK, bk, tile, NTILE, tid);
+    if constexpr (!TR) {
+      l2_touch<NL, kThreads>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, tid);
+      l2_touch<NL, kThreads>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                             kChunk * kChunk * (int)sizeof(E), tile, NTILE, tid);
+      l2_touch<NL, kThreads>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, tid);
+    }
+  };
   if (nchunks > 0) {
     load_chunk(nchunks - 1);
+    warm(max(nchunks - 2, 0));  // unconditional, like every warm-up: a load in a branch would
+                                // make the compiler's wait counts assume the worst path
     commit_chunk(nchunks - 1, smem + (L::NSTG == 2 ? ((nchunks - 1) & 1) : 0) * L::stage);
   }
 
@@ -202,13 +227,17 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     }
     const bool more = c > 0;
     load_chunk(more ? c - 1 : c);
+    l2_sink<5 * NL>(pw);
+    warm(max(c - 2, 0));
     __syncthreads();
 
     if constexpr (OUT) {  // G of this slot -> dstates [d][v0 : v0 + TV]
       E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
       constexpr int VPR = TV / VE;
-      for (int i = tid; i < DK * VPR; i += kThreads) {
-        const int d = i / VPR, cc = (i % VPR) * VE;
+      // no store in a branch (see s2g): work past the end repeats the last vector
+#pragma unroll
+      for (int it = 0; it < (DK * VPR + kThreads - 1) / kThreads; ++it) {
+        const int i = min(it * kThreads + tid, DK * VPR - 1), d = i / VPR, cc = (i % VPR) * VE;
         *(u32x4*)(gG + (int64_t)d * DV + cc) = *(const u32x4*)(sG + d * L::LS + cc);
       }
     }

@@ -301,9 +301,32 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
     return;
   }
   if (storer) {
+    // Besides the stores, this wave warms L2 two chunks ahead of the compute waves, so the
+    // loader's DMA of chunk c + 1 reads lines requested a step earlier and HBM keeps a request
+    // stream across the barriers. The workgroups of one (sequence, head) split the shared tiles
+    // line by line; nothing waits for these loads until the next step.
+    constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + 64 * NTILE - 1) / (64 * NTILE);
+    int pw[5 * NL];
+#pragma unroll
+    for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
+    auto warm = [&](int c) {
+      const int n = rows_of(c);
+      const int64_t r0 = base + (int64_t)c * kChunk;
+      l2_touch<NL>(pw, w + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, tl);
+      l2_touch<NL>(pw + NL, k + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, tl);
+      if constexpr (WO) {
+        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, tl);
+        l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, tl);
+      }
+      if constexpr (!PM) l2_touch<NL>(pw + 4 * NL, u + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, tl);
+    };
+    warm(min(1, nchunks - 1));
     for (int c = 0; c < nchunks; ++c) {
       __syncthreads();  // staging of chunk c - 1 is complete
+      l2_sink<5 * NL>(pw);  // the warm-up of the previous step, before any store of this one
       if (c > 0) copy_out(c - 1);
+      warm(min(c + 2, nchunks - 1));  // unconditional: no load inside a branch
     }
     __syncthreads();
     copy_out(nchunks - 1);
