@@ -175,7 +175,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   float bt, cR = 0.f, aR = 0.f;  // beta, and (gated) c and log-decay of token lane
   // Requests for a chunk's inputs, issued for the next chunk in small groups spread over
   // the steps of the current one: a large burst would stall the issuing waves until the
-  // memory system had taken all of it.
+  // memory system had taken all of it. The last group goes through opaque copies of its
+  // base pointers (fresh each iteration), which keeps the compiler from sinking its loads past
+  // the chunk's final stores towards their use in the next iteration.
+  const E* qL = q;
+  const E* gL = dstates;
   auto issue_k = [&](const ChunkUnit& c) {
     tK.load(k + c.row0 * DK, c.n, tid);
     bt = to_f(beta[c.row0 + min(lane, c.n - 1)]);
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     tV.load(v + c.row0 * DV, c.n, tid);
     tX.load(xsav + c.sh * 64 * 64, 64, tid);
   };
-  auto issue_q = [&](const ChunkUnit& c) { tQ.load(q + c.row0 * DK, c.n, tid); };
+  auto issue_q = [&](const ChunkUnit& c) { tQ.load(qL + c.row0 * DK, c.n, tid); };
   auto issue_s = [&](const ChunkUnit& c, int cK) {
 #pragma unroll
     for (int j = 0; j < CK; ++j)
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     for (int j = 0; j < CK; ++j)
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks)
-        fG[j][ks] = frag_rm_g<E>(dstates + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
+        fG[j][ks] = frag_rm_g<E>(gL + c.sh * DK * DV + (int64_t)16 * (cK + j) * DV + ks * KC, DV, lane);
   };
 
   ChunkUnit cur = chunk_unit(g, u);
@@ -217,6 +221,42 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   issue_u(cur);
   issue_v_x(cur);
   issue_q(cur);
+  // ---- 1: a chunk's tiles land in LDS; ||k||^2 is reduced from the loaded K vectors (VPR
+  // consecutive threads per row). Done before the loop for the first chunk and at the end of
+  // each iteration for the next one, after that iteration's stores: every load and store in the
+  // loop is unconditional (the last chunk requests itself again), so the compiler knows how many
+  // stores follow the loads and waits for the loads alone.
+  float bt_cur = 0.f, a_cur = 0.f;
+  auto land = [&](const ChunkUnit& c) {
+    const int n = c.n;
+    tK.store(sK, LK, n, tid);
+    {
+      typedef TileRegs<E, DK> TKr;
+#pragma unroll
+      for (int it = 0; it < TKr::IT; ++it) {
+        const int i = it * kBwdThreads + tid;
+        const Vv x = __builtin_bit_cast(Vv, tK.v[it]);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < TKr::VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
+        acc = group_sum<TKr::VPR>(acc);
+        if (i % TKr::VPR == 0) cLam[i / TKr::VPR] = i / TKr::VPR < n ? acc : 0.f;
+      }
+    }
+    bt_cur = bt;
+    a_cur = aR;
+    if constexpr (GT) {
+      if (tid < 64) cC[tid] = cR;
+      for (int i = tid; i < 64 * NS; i += kBwdThreads) pDc[i] = 0.f;
+    }
+    tDU.store(sDU, LV, n, tid);
+    tDO.store(sDO, LV, n, tid);
+    tU.store(sU, LV, n, tid);
+    tV.store(sV, LV, n, tid);
+    tX.store(sX, LT, 64, tid);
+    tQ.store(sQ, LK, n, tid);
+  };
+  land(cur);
   for (;;) {
   // Every per-lane address below derives from tid; making it opaque here keeps the compiler
   // from hoisting dozens of loop-invariant LDS addresses out of the loop (they would hold
@@ -227,6 +267,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // registers where they are used instead of being held (and spilled) across the loop.
   int wv = wv0;
   asm volatile("" : "+s"(wv));
+  qL = opaque_global(q);
+  gL = opaque_global(dstates);
   // [64][d] outputs: wave wv owns row blocks rb0, rb0 + 1 and column blocks cK.. (cV..).
   const int rb0 = 2 * (wv >> 2), cK = CK * (wv & 3), cV = CV * (wv & 3);
   // 64x64 work matrices: wave wv owns blocks (pr, pn) and (pr, pn + 1).
@@ -234,38 +276,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   const bool plow = pn <= pr;  // at least one of the two blocks is on or below the diagonal
   const int n = cur.n;
   const int64_t row0 = cur.row0;
-  // ---- 1: this chunk's tiles land in LDS; ||k||^2 is reduced from the loaded K vectors
-  // (VPR consecutive threads per row). Then the next chunk's tiles are requested.
-  tK.store(sK, LK, n, tid);
-  {
-    typedef TileRegs<E, DK> TKr;
-#pragma unroll
-    for (int it = 0; it < TKr::IT; ++it) {
-      const int i = it * kBwdThreads + tid;
-      const Vv x = __builtin_bit_cast(Vv, tK.v[it]);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < TKr::VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
-      acc = group_sum<TKr::VPR>(acc);
-      if (i % TKr::VPR == 0) cLam[i / TKr::VPR] = i / TKr::VPR < n ? acc : 0.f;
-    }
-  }
-  const float bt_cur = bt, a_cur = aR;
-  if constexpr (GT) {
-    if (tid < 64) cC[tid] = cR;
-    for (int i = tid; i < 64 * NS; i += kBwdThreads) pDc[i] = 0.f;
-  }
-  tDU.store(sDU, LV, n, tid);
-  tDO.store(sDO, LV, n, tid);
-  tU.store(sU, LV, n, tid);
-  tV.store(sV, LV, n, tid);
-  tX.store(sX, LT, 64, tid);
-  tQ.store(sQ, LK, n, tid);
-  __syncthreads();
+  __syncthreads();  // this chunk's tiles are in LDS; the next chunk's are requested from here on
   const int un = u + (int)gridDim.x;
   const bool more = un < nu;
   const ChunkUnit nxt = chunk_unit(g, more ? un : u);
-  if (more) issue_k(nxt);
+  issue_k(nxt);
 
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);
   //         dM = scale tril(dO U~^T); per-token coefficients
@@ -393,7 +408,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
     }
   }
   __syncthreads();
-  if (more) issue_du_do(nxt);
+  issue_du_do(nxt);
 
   // ---- 3: dT = dW K^T + dU V^T -> dalpha (columns) and dX = dT diag(alpha) (strictly lower);
   //         dV = T^T dU, dK += T^T dW (T^T = diag(alpha) X^T); dQ += dM K; dK += dM^T Q
@@ -493,9 +508,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   __syncthreads();
   // S registers are free again; G follows two steps later. The gated kernel, which holds more
   // per-token state, requests S with G so that S is not held through the dA step.
-  if constexpr (!GT) {
-    if (more) issue_s(nxt, cK);
-  }
+  if constexpr (!GT) issue_s(nxt, cK);
 
   // ---- 4: Y = dX X^T (only the lower blocks are used: rows t > s), kept transposed
   //         (sY[s][t] = Y[t][s]); stage dQ and dV
@@ -520,10 +533,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       st_frag_t<E>(sDU + 16 * (rb0 + i) * LV + 16 * (cV + j), LV, aV[i][j], lane);
   }
   __syncthreads();
-  if (more) {
-    issue_u(nxt);
-    issue_v_x(nxt);
-  }
+  issue_u(nxt);
+  issue_v_x(nxt);
 
   // ---- 5: dA = -X^T Y (strictly lower) -> dalpha (rows) and H = dG + dG^T; write dQ, dV
   {
@@ -583,11 +594,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   s2g<E, DK, kBwdThreads>(dq + row0 * DK, DK, sQ, LK, n, tid);
   s2g<E, DV, kBwdThreads>(dv + row0 * DV, DV, sDU, LV, n, tid);
   __syncthreads();
-  if (more) {
-    issue_q(nxt);
-    if constexpr (GT) issue_s(nxt, cK);
-    issue_g(nxt, cK);
-  }
+  issue_q(nxt);
+  if constexpr (GT) issue_s(nxt, cK);
+  issue_g(nxt, cK);
 
   // ---- 6: dK += H K; dk += 2 k dalpha dalpha/dlam; dbeta = dalpha e^-x
   mma_blk<E, false, true, 2, CK, kChunk, true>(sH + 16 * rb0 * LT, LT, sK + 16 * cK, LK, 0,
@@ -619,8 +628,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       // part of dA . A); the last token carries the chunk-end factors; then
       // dgate_t = sum_{s >= t} dc_s + db_t db_t/da_t.
       const float da_t = dalpha(tid), db_t = dbsum(tid);
-      if (tid < n) dbeta[row0 + tid] = to_e<E>(da_t * cEx[tid] + db_t * cBb[tid]);
-      const float* pt = pDc + tid * NS;
+      float* pt = pDc + tid * NS;
       float sq = 0.f, rdr = 0.f, se = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -639,15 +647,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
         const float y = __shfl_down(dc, o);
         if (tid + o < 64) dc += y;
       }
-      if (tid < n) dgate[row0 + tid] = to_e<E>(fmaf(db_t, cBa[tid], dc));
+      pt[0] = da_t * cEx[tid] + db_t * cBb[tid];  // dbeta and dgate, stored below by all waves
+      pt[1] = fmaf(db_t, cBa[tid], dc);
     }
-  } else {
-    if (tid < n) dbeta[row0 + tid] = to_e<E>(dalpha(tid) * cEx[tid]);
   }
   __syncthreads();
+  {  // every thread stores (see s2g): lanes past the last token repeat it
+    const int t = min(tid & 63, n - 1);
+    if constexpr (GT) {
+      dbeta[row0 + t] = to_e<E>(pDc[t * NS]);
+      dgate[row0 + t] = to_e<E>(pDc[t * NS + 1]);
+    } else {
+      dbeta[row0 + t] = to_e<E>(dalpha(t) * cEx[t]);
+    }
+  }
   s2g<E, DK, kBwdThreads>(dk + row0 * DK, DK, sW, LK, n, tid);
   if (!more) break;
   __syncthreads();  // every LDS read of this chunk is done before the next one lands
+  land(nxt);
   u = un;
   cur = nxt;
   }

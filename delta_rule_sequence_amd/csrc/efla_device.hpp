@@ -130,6 +130,16 @@ template <typename T, typename E> EFLA_DEV const T* at_byte(const E* base, unsig
   return (const T*)((const char*)base + byte_off);
 }
 
+// A copy of a global pointer that the compiler cannot trace back to its kernel argument. Loads
+// through it are ordinary loads, ordered with the stores around them; loads through a read-only
+// kernel argument may be moved anywhere, e.g. sunk from a loop body to just before the back edge.
+template <typename E> EFLA_DEV const E* opaque_global(const E* p) {
+  typedef const E __attribute__((address_space(1)))* G;
+  G g = (G)p;
+  asm volatile("" : "+s"(g));
+  return (const E*)g;
+}
+
 // frag_rm from global memory, src uniform across the wave.
 template <typename E>
 EFLA_DEV typename Mma<E>::vec frag_rm_g(const E* __restrict__ src, int ld, int lane) {

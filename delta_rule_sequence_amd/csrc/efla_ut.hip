@@ -70,46 +70,43 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   u32x4 kR[KIT], vR[VIT];
   float bR[KIT], aR[KIT], aN = 0.f;
   Vv qN[KS], qA[KS];
+  // Requests for the next chunk's inputs, spread over the current one. Every request is
+  // unconditional (row indices are clamped; the last chunk requests itself again), and inside
+  // the loop the base pointers are opaque copies made each iteration: loads through a read-only
+  // kernel argument may be sunk by the compiler to just before the back edge.
+  const E *kL = k, *vL = v, *qL = q, *bL = beta, *aL = gate;
   auto issue_k = [&](const ChunkUnit& c) {
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / VPR, c.n - 1), cc = (i % VPR) * VE;
-      kR[it] = *(const u32x4*)(k + (c.row0 + r) * DK + cc);
-      bR[it] = to_f(beta[c.row0 + r]);
-      if constexpr (GT) aR[it] = to_f(gate[c.row0 + r]);
+      kR[it] = *(const u32x4*)(kL + (c.row0 + r) * DK + cc);
+      bR[it] = to_f(bL[c.row0 + r]);
+      if constexpr (GT) aR[it] = to_f(aL[c.row0 + r]);
     }
-    if constexpr (GT) aN = lane < c.n ? to_f(gate[c.row0 + lane]) : 0.f;  // token = lane
+    if constexpr (GT) aN = to_f(aL[c.row0 + min(lane, c.n - 1)]);  // token = lane
   };
   auto issue_v = [&](const ChunkUnit& c) {
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / (DV / VE), c.n - 1), cc = (i % (DV / VE)) * VE;
-      vR[it] = *(const u32x4*)(v + (c.row0 + r) * DV + cc);
+      vR[it] = *(const u32x4*)(vL + (c.row0 + r) * DV + cc);
     }
   };
   auto issue_q = [&](const ChunkUnit& c) {  // this wave's Q rows as A fragments (for M)
     if (!mout) return;
     const int ra = min(rA + (lane & 15), c.n - 1) - (lane & 15);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qN[ks] = frag_rm<E>(q + (c.row0 + ra) * DK + ks * KC, DK, lane);
+    for (int ks = 0; ks < KS; ++ks) qN[ks] = frag_rm<E>(qL + (c.row0 + ra) * DK + ks * KC, DK, lane);
   };
 
-  ChunkUnit cur = chunk_unit(g, un);
-  issue_k(cur);
-  issue_v(cur);
-  issue_q(cur);
-  for (;;) {
-    // Per-lane addresses derive from tid: opaque once per unit so that they are not all
-    // hoisted out of the loop (they would hold registers through every step).
-    asm volatile("" : "+v"(tid));
-    lane = tid & 63;
-    const int n = cur.n;
-    const int64_t row0 = cur.row0;
-
-    // K and V land in LDS; ||k||^2 is reduced from the K vectors (VPR consecutive threads
-    // per row), giving alpha.
+  // K and V land in LDS; ||k||^2 is reduced from the K vectors (VPR consecutive threads per
+  // row), giving alpha. Done before the loop for the first chunk and at the end of each
+  // iteration for the next one, after that iteration's stores, so the compiler waits for the
+  // loads alone there.
+  auto land = [&](const ChunkUnit& cu) {
+    const int n = cu.n;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int i = it * kThreads + tid;
@@ -138,21 +135,40 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     }
     if constexpr (GT) {  // c_t: inclusive running sum of the log-decays (padded rows add 0)
       if (wv == 0) {
-        float cs = aN;
+        float cs = lane < n ? aN : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float t = __shfl_up(cs, off);
           if (lane >= off) cs += t;
         }
         sCm[lane] = cs;
-        if (cum) cum[cur.sh * 64 + lane] = cs;
+        if (cum) cum[cu.sh * 64 + lane] = cs;
       }
     }
+  };
+
+  ChunkUnit cur = chunk_unit(g, un);
+  issue_k(cur);
+  issue_v(cur);
+  issue_q(cur);
+  land(cur);
+  for (;;) {
+    // Per-lane addresses derive from tid: opaque once per unit so that they are not all
+    // hoisted out of the loop (they would hold registers through every step).
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    kL = opaque_global(k);
+    vL = opaque_global(v);
+    qL = opaque_global(q);
+    bL = opaque_global(beta);
+    if constexpr (GT) aL = opaque_global(gate);
+    const int n = cur.n;
+    const int64_t row0 = cur.row0;
     __syncthreads();
     const int unx = un + (int)gridDim.x;
     const bool more = unx < nu;
     const ChunkUnit nxt = chunk_unit(g, more ? unx : un);
-    if (more) issue_k(nxt);
+    issue_k(nxt);
 
     // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T), lower blocks only (the
     // inverse never reads A above the diagonal). Wave wv takes A's row block 3 - wv and M's
@@ -203,10 +219,10 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
       E* gm = mout + cur.sh * 64 * 64;
       s2g<E, 64>(gm, 64, sM, L::LT, kChunk, tid);
     }
-    if (more) issue_v(nxt);
+    issue_v(nxt);
     __syncthreads();
     invert_unit_lower64(sA, sX, tid);
-    if (more) issue_q(nxt);
+    issue_q(nxt);
 
     // T = X diag(alpha), written over A (A is no longer needed); X to global memory.
     {
@@ -299,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
     if (!more) break;
     __syncthreads();  // the copies out of sK and sV are done before the next chunk lands
+    land(nxt);
     un = unx;
     cur = nxt;
   }
