@@ -25,6 +25,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
 
+# Per-file flags. The two state scans keep their MFMA accumulators in VGPRs rather than the
+# compiler's default AGPR placement: their accumulators feed VALU work (bf16 conversion, the
+# next product's operands) every chunk, and copying them out of AGPRs cost about a third of
+# the forward scan's VALU instructions (measured: 2-4% faster scans, identical results).
+FILE_FLAGS = {
+    "efla_scan_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "efla_scan_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -50,7 +59,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(i):
         src = os.path.join(CSRC, SOURCES[i])
-        return _run([cc] + FLAGS + ["-c", src, "-o", objs[i]])
+        return _run([cc] + FLAGS + FILE_FLAGS.get(SOURCES[i], []) + ["-c", src, "-o", objs[i]])
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         logs = list(ex.map(compile_one, range(len(SOURCES))))

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   // ---- 1: a chunk's tiles land in LDS; ||k||^2 is reduced from the loaded K vectors (VPR
   // consecutive threads per row). Done before the loop for the first chunk and at the end of
   // each iteration for the next one, after that iteration's stores: every load and store in the
-  // loop is unconditional (the last chunk requests itself again), so the compiler knows how many
+  // loop is unconditional (after the last chunk, one row of the first), so the compiler knows how many
   // stores follow the loads and waits for the loads alone.
   float bt_cur = 0.f, a_cur = 0.f;
   auto land = [&](const ChunkUnit& c) {
@@ -279,7 +279,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   __syncthreads();  // this chunk's tiles are in LDS; the next chunk's are requested from here on
   const int un = u + (int)gridDim.x;
   const bool more = un < nu;
-  const ChunkUnit nxt = chunk_unit(g, more ? un : u);
+  // After the last chunk the requests still go out (every load is unconditional), to one row
+  // of the first chunk, which all workgroups then share in L2.
+  ChunkUnit nxt = chunk_unit(g, more ? un : 0);
+  if (!more) nxt.n = 1;
   issue_k(nxt);
 
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);

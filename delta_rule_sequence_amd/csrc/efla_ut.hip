@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   float bR[KIT], aR[KIT], aN = 0.f;
   Vv qN[KS], qA[KS];
   // Requests for the next chunk's inputs, spread over the current one. Every request is
-  // unconditional (row indices are clamped; the last chunk requests itself again), and inside
+  // unconditional (row indices are clamped; after the last chunk, one row of the first), and inside
   // the loop the base pointers are opaque copies made each iteration: loads through a read-only
   // kernel argument may be sunk by the compiler to just before the back edge.
   const E *kL = k, *vL = v, *qL = q, *bL = beta, *aL = gate;
@@ -167,7 +167,10 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     __syncthreads();
     const int unx = un + (int)gridDim.x;
     const bool more = unx < nu;
-    const ChunkUnit nxt = chunk_unit(g, more ? unx : un);
+    // After the last chunk the requests still go out (every load is unconditional), to one
+    // row of the first chunk, which all workgroups then share in L2.
+    ChunkUnit nxt = chunk_unit(g, more ? unx : 0);
+    if (!more) nxt.n = 1;
     issue_k(nxt);
 
     // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T), lower blocks only (the
