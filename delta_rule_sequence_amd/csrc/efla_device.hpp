@@ -540,6 +540,30 @@ EFLA_DEV typename Mma<E>::vec aop_kc(const unsigned char* t, int b, int ks, int 
   }
 }
 
+// Standard-order fragments (as frag_rm / frag_km: lane group g takes k0 + KC/4 g..) from a
+// swizzled LDS tile: frag_rm_sw reads A[m0 + (lane & 15)][k0..] with A[m][k] at (m, k);
+// frag_km_sw reads X[k0..][m0 + (lane & 15)] with X stored at (k, m), by transpose reads.
+template <typename E, int COLS>
+EFLA_DEV typename Mma<E>::vec frag_rm_sw(const unsigned char* t, int m0, int k0, int lane) {
+  typedef Swz<E, COLS> S;
+  return *(const typename Mma<E>::vec*)(t + S::off(m0 + (lane & 15), k0 + (lane >> 4) * (Mma<E>::KC / 4)));
+}
+template <typename E, int COLS>
+EFLA_DEV typename Mma<E>::vec frag_km_sw(const unsigned char* t, int k0, int m0, int lane) {
+  typedef Swz<E, COLS> S;
+  const int gq = lane >> 4, i = lane & 15;
+  if constexpr (sizeof(E) == 2) {
+    const int r = k0 + 8 * gq + (i >> 2), c = m0 + 4 * (i & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + S::off(r, c)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + S::off(r + 4, c)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const int r = k0 + 4 * gq, c = m0 + i;
+    return f32x4{*(const float*)(t + S::off(r, c)), *(const float*)(t + S::off(r + 1, c)),
+                 *(const float*)(t + S::off(r + 2, c)), *(const float*)(t + S::off(r + 3, c))};
+  }
+}
+
 template <typename E, int COLS>
 EFLA_DEV typename Mma<E>::vec aop_km(const unsigned char* t, int m0, int ks, int lane) {
   typedef Swz<E, COLS> S;

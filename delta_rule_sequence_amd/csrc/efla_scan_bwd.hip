@@ -283,6 +283,242 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   }
 }
 
+// DMA-fed variant for bf16 problems with 32-column tiles (ungated): a fifth wave fills
+// swizzled LDS tiles of K, Q, W, M and dO one chunk ahead by LDS DMA, as in the forward scan,
+// so the compute waves neither load nor commit tiles and never wait for memory except for
+// their own stores. The loader waits for its DMA only before the barrier that publishes the
+// chunk; the other barrier of the step is a bare s_barrier for it, which waits for nothing.
+// Rows past the end of a partial chunk, which the DMA fills with copies of the last row, are
+// cleared by the loader (the products over tokens need zeros there).
+template <typename E, int DK, int DV>
+struct ScanBwdDmaLds {
+  static constexpr int TV = 32;
+  typedef Swz<E, DK> SK;  // K, Q, W [64][DK]
+  typedef Swz<E, 64> SM;  // M [64][64]
+  typedef Swz<E, TV> SO;  // dO [64][TV] (this tile's columns)
+  static constexpr int LS = pitch<E>(TV), LT = pitch<E>(64);
+  static constexpr size_t oK = 0, oQ = oK + SK::BYTES, oW = oQ + SK::BYTES, oM = oW + SK::BYTES;
+  static constexpr size_t oO = oM + SM::BYTES;
+  static constexpr size_t stage = oO + SO::BYTES;
+  static constexpr size_t oG = 2 * stage;                   // G slice [DK][LS]
+  static constexpr size_t oDt = oG + DK * LS * sizeof(E);   // dU~^T [TV][LT]
+  static constexpr size_t oDu = oDt + TV * LT * sizeof(E);  // dU~ staging [64][LS]
+  static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
+};
+
+constexpr int kScanBwdDmaThreads = 5 * 64;  // four compute waves and the loader
+
+template <typename E, int DK, int DV, int MODE>
+__global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
+    Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
+    const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
+    E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0) {
+  typedef ScanBwdDmaLds<E, DK, DV> L;
+  typedef typename Mma<E>::vec V;
+  constexpr int TV = L::TV, LS = L::LS, LT = L::LT;
+  constexpr int KC = Mma<E>::KC, KS = DK / KC;
+  constexpr int NTILE = DV / TV;
+  constexpr int NB = TV / 16;
+  constexpr int TPW = (DK / 16) * NB / 4;
+  constexpr int VE = 16 / (int)sizeof(E);
+  constexpr int NT = 256;  // compute threads
+  constexpr bool OUT = MODE == 0, TR = MODE == 2;  // write dU~ and dS_c; transition
+  static_assert(TPW >= 1 && ((DK / 16) * NB) % 4 == 0, "state tiles must split over 4 waves");
+  static_assert(L::bytes <= 160 * 1024, "LDS budget");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  E* sG = (E*)(smem + L::oG);
+  E* sDt = (E*)(smem + L::oDt);
+  E* sDu = (E*)(smem + L::oDu);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int sh, tile;
+  scan_block(blockIdx.x, g.n_seqs * g.H, NTILE, sh, tile);
+  const int s = sh / g.H, h = sh % g.H;
+  const SeqInfo si = seq_info(g, s);
+  const int nchunks = seq_chunks(g, si);
+  const int v0 = tile * TV;
+  const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
+  auto rows_of = [&](int c) { return min(kChunk, si.len - c * kChunk); };
+  auto tiles = [&](int c) { return smem + (c & 1) * L::stage; };
+
+  if (wv == 4) {  // ---- loader wave
+    auto issue = [&](int c) {
+      unsigned char* st = tiles(c);
+      const int n = rows_of(c);
+      const int64_t r0 = base + (int64_t)c * kChunk;
+      dma_tile<E, DK, 1>(st + L::oK, k + r0 * DK, DK, n, 0, lane);
+      dma_tile<E, DK, 1>(st + L::oW, w + r0 * DK, DK, n, 0, lane);
+      if constexpr (!TR) {  // Q, M and dO only enter through the dO term
+        dma_tile<E, DK, 1>(st + L::oQ, q + r0 * DK, DK, n, 0, lane);
+        dma_tile<E, 64, 1>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                           kChunk, kChunk, 0, lane);
+        dma_tile<E, TV, 1>(st + L::oO, d_o + r0 * DV + v0, DV, n, 0, lane);
+      }
+    };
+    auto clear_tail = [&](int c) {  // rows >= n (whole rows: the swizzle stays inside a row)
+      const int n = rows_of(c);
+      if (n >= kChunk) return;
+      unsigned char* st = tiles(c);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int b = n * L::SK::RB + 16 * lane; b < kChunk * L::SK::RB; b += 16 * 64) {
+        *(u32x4*)(st + L::oK + b) = z;
+        *(u32x4*)(st + L::oW + b) = z;
+        if constexpr (!TR) *(u32x4*)(st + L::oQ + b) = z;
+      }
+      if constexpr (!TR)
+        for (int b = n * L::SO::RB + 16 * lane; b < kChunk * L::SO::RB; b += 16 * 64)
+          *(u32x4*)(st + L::oO + b) = z;
+    };
+    if (nchunks > 0) {
+      issue(nchunks - 1);
+      wait_vm_all();
+      clear_tail(nchunks - 1);
+    }
+    for (int c = nchunks - 1; c >= 0; --c) {
+      __syncthreads();  // chunk c is in LDS; every wave is done with chunk c + 1's stage
+      if (c > 0) issue(c - 1);
+      __builtin_amdgcn_s_barrier();  // the step's second barrier
+      wait_vm_all();
+      if (c > 0) clear_tail(c - 1);
+    }
+    return;
+  }
+
+  // ---- compute waves: G^T tile t = wv + 4 i holds G[16 db + (lane & 15)][v0 + 16 vb + 4 (lane >> 4) + e]
+  const int rA = 16 * wv;
+  f32x4 Gt[TPW];
+  auto goff = [&](int i, int e) {
+    const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+    return ((int64_t)s * g.H + h) * DK * DV + (int64_t)(16 * db + (lane & 15)) * DV + v0 + 16 * vb +
+           4 * (lane >> 4) + e;
+  };
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    Gt[i] = zero4();
+    if constexpr (TR) {  // G = I (d_v = d_k): this slice's columns
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Gt[i][e] = 16 * db + (lane & 15) == v0 + 16 * vb + 4 * (lane >> 4) + e ? 1.f : 0.f;
+    } else if (dht) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
+    }
+  }
+  // L2 warm-up two chunks ahead (see the register-fed kernel above)
+  constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * NT - 1) / (NTILE * NT);
+  int pw[5 * NL];
+#pragma unroll
+  for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
+  auto warm = [&](int c) {
+    const int n = rows_of(c);
+    const int64_t r0 = base + (int64_t)c * kChunk;
+    const int bk = n * DK * (int)sizeof(E);
+    l2_touch<NL, NT>(pw, w + r0 * DK, bk, tile, NTILE, tid);
+    l2_touch<NL, NT>(pw + NL, k + r0 * DK, bk, tile, NTILE, tid);
+    if constexpr (!TR) {
+      l2_touch<NL, NT>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, tid);
+      l2_touch<NL, NT>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                       kChunk * kChunk * (int)sizeof(E), tile, NTILE, tid);
+      l2_touch<NL, NT>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, tid);
+    }
+  };
+  if (nchunks > 0) warm(max(nchunks - 2, 0));
+
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const unsigned char* st = tiles(c);
+    const int n = rows_of(c);
+    const int64_t r0 = base + (int64_t)c * kChunk;
+    // Stage G (gradient of the state leaving chunk c): G^T tiles written transposed.
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+      st_frag_t<E>(sG + 16 * db * LS + 16 * vb, LS, Gt[i], lane);
+    }
+    l2_sink<5 * NL>(pw);
+    warm(max(c - 2, 0));
+    __syncthreads();
+
+    V kA[KS];  // this wave's K rows (A operand of K G)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kA[ks] = frag_rm_sw<E, DK>(st + L::oK, rA, ks * KC, lane);
+    if constexpr (OUT) {  // G of this slot -> dstates [d][v0 : v0 + TV]
+      E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
+      constexpr int VPR = TV / VE;
+#pragma unroll
+      for (int it = 0; it < (DK * VPR + NT - 1) / NT; ++it) {
+        const int i = min(it * NT + tid, DK * VPR - 1), d = i / VPR, cc = (i % VPR) * VE;
+        *(u32x4*)(gG + (int64_t)d * DV + cc) = *(const u32x4*)(sG + d * LS + cc);
+      }
+    }
+    // dU~ = scale M^T dO + K G for this wave's rows (tokens).
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 kg = zero4(), md = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * LS + 16 * nb, LS, lane), kg);
+      if constexpr (!TR) {  // M^T[t][s] = M[s][t]: k-major from M's rows s >= t
+        for (int k0 = round_down_kc<E>(rA); k0 < kChunk; k0 += KC)
+          md = Mma<E>::step(frag_km_sw<E, 64>(st + L::oM, k0, rA, lane),
+                            frag_km_sw<E, TV>(st + L::oO, k0, 16 * nb, lane), md);
+      }
+      f32x4 du = kg + g.scale * md;
+      st_frag_t<E>(sDt + 16 * nb * LT + rA, LT, du, lane);
+      if constexpr (OUT) st_frag_lds<E>(sDu + rA * LS + 16 * nb, LS, du, lane);
+    }
+    __syncthreads();
+
+    if constexpr (OUT) s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, LS, n, tid);
+    // G^T += scale dO^T Q - dU~^T W
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+      f32x4 a = zero4(), b = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < kChunk; k0 += KC) {
+        if constexpr (!TR)
+          a = Mma<E>::step(frag_km_sw<E, TV>(st + L::oO, k0, 16 * vb, lane),
+                           frag_km_sw<E, DK>(st + L::oQ, k0, 16 * db, lane), a);
+        b = Mma<E>::step(frag_rm<E>(sDt + 16 * vb * LT + k0, LT, lane),
+                         frag_km_sw<E, DK>(st + L::oW, k0, 16 * db, lane), b);
+      }
+      Gt[i] = Gt[i] + (g.scale * a - b);
+    }
+  }
+  if (dh0) {  // gradient at the state entering the sequence
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh0[goff(i, e)] = Gt[i][e];
+  }
+}
+
+template <typename E, int DK, int DV, int MODE>
+static hipError_t scan_bwd_dma_run(const Shape& s, const int* table, const void* q, const void* k,
+                                   const void* w, const void* m, const void* d_o, void* dut,
+                                   void* dstates, const float* dht, float* dh0, hipStream_t st) {
+  typedef ScanBwdDmaLds<E, DK, DV> L;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_dma_kernel<E, DK, DV, MODE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / L::TV);
+  if (blocks < 1) return hipSuccess;
+  prof_begin(st);
+  hipLaunchKernelGGL((scan_bwd_dma_kernel<E, DK, DV, MODE>), dim3((unsigned)blocks), dim3(kScanBwdDmaThreads),
+                     L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0);
+  hipError_t e = hipGetLastError();
+  static const char* const names[3] = {"scan_bwd", "scan_bwd_state", "scan_bwd_transition"};
+  prof_end(names[MODE], st);
+  return e;
+}
+
 template <typename E, int DK, int DV, int TV, bool GT, int MODE>
 static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* m, const void* d_o, void* dut,
@@ -320,7 +556,10 @@ static hipError_t scan_bwd_mode(const Shape& s, const int* table, const void* q,
     else
       return hipErrorInvalidValue;
   }
-  return scan_bwd_run<E, DK, DV, TV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+  if constexpr (sizeof(E) == 2 && TV == 32)
+    return scan_bwd_dma_run<E, DK, DV, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st);
+  else
+    return scan_bwd_run<E, DK, DV, TV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
 }
 
 template <typename E, int DK, int DV, int TV>
