@@ -283,13 +283,15 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   }
 }
 
-// DMA-fed variant for bf16 problems with 32-column tiles (ungated): a fifth wave fills
-// swizzled LDS tiles of K, Q, W, M and dO one chunk ahead by LDS DMA, as in the forward scan,
-// so the compute waves neither load nor commit tiles and never wait for memory except for
-// their own stores. The loader waits for its DMA only before the barrier that publishes the
-// chunk; the other barrier of the step is a bare s_barrier for it, which waits for nothing.
-// Rows past the end of a partial chunk, which the DMA fills with copies of the last row, are
-// cleared by the loader (the products over tokens need zeros there).
+// DMA-fed variant for bf16 problems with 32-column tiles (ungated), organised like the forward
+// scan: a loader wave fills swizzled LDS tiles of K, Q, W, M and dO one chunk ahead by LDS DMA,
+// and a storer wave copies the staged G and dU~ out and warms L2 two chunks ahead, so the four
+// compute waves issue no global memory operation in the loop. The loader waits for its DMA
+// only before the barrier that publishes the chunk; the step's other barrier is a bare
+// s_barrier for it, which waits for nothing. Rows past the end of a partial chunk, which the
+// DMA fills with copies of the last row, are cleared by the loader (the products over tokens
+// need zeros there). The storer reads the G staging between the step's two barriers and dU~
+// after the second, before the compute waves write either again.
 template <typename E, int DK, int DV>
 struct ScanBwdDmaLds {
   static constexpr int TV = 32;
@@ -306,7 +308,7 @@ struct ScanBwdDmaLds {
   static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
 };
 
-constexpr int kScanBwdDmaThreads = 5 * 64;  // four compute waves and the loader
+constexpr int kScanBwdDmaThreads = 6 * 64;  // four compute waves, the loader and the storer
 
 template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
@@ -321,7 +323,6 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   constexpr int NB = TV / 16;
   constexpr int TPW = (DK / 16) * NB / 4;
   constexpr int VE = 16 / (int)sizeof(E);
-  constexpr int NT = 256;  // compute threads
   constexpr bool OUT = MODE == 0, TR = MODE == 2;  // write dU~ and dS_c; transition
   static_assert(TPW >= 1 && ((DK / 16) * NB) % 4 == 0, "state tiles must split over 4 waves");
   static_assert(L::bytes <= 160 * 1024, "LDS budget");
@@ -385,6 +386,44 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
     return;
   }
 
+  if (wv == 5) {  // ---- storer wave (lane: its thread index)
+    constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * 64 - 1) / (NTILE * 64);
+    int pw[5 * NL];
+#pragma unroll
+    for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
+    auto warm = [&](int c) {  // one word per 128-byte line; the head's workgroups split the lines
+      const int n = rows_of(c);
+      const int64_t r0 = base + (int64_t)c * kChunk;
+      const int bk = n * DK * (int)sizeof(E);
+      l2_touch<NL>(pw, w + r0 * DK, bk, tile, NTILE, lane);
+      l2_touch<NL>(pw + NL, k + r0 * DK, bk, tile, NTILE, lane);
+      if constexpr (!TR) {
+        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, lane);
+        l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+        l2_touch<NL>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
+      }
+    };
+    if (nchunks > 0) warm(max(nchunks - 2, 0));
+    for (int c = nchunks - 1; c >= 0; --c) {
+      __syncthreads();  // G of chunk c is staged
+      l2_sink<5 * NL>(pw);  // the warm-up of the previous step, before this step's stores
+      if constexpr (OUT) {  // G of this slot -> dstates [d][v0 : v0 + TV] (no store in a branch)
+        E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
+        constexpr int VPR = TV / VE;
+#pragma unroll
+        for (int it = 0; it < (DK * VPR + 63) / 64; ++it) {
+          const int i = min(it * 64 + lane, DK * VPR - 1), d = i / VPR, cc = (i % VPR) * VE;
+          *(u32x4*)(gG + (int64_t)d * DV + cc) = *(const u32x4*)(sG + d * LS + cc);
+        }
+      }
+      warm(max(c - 2, 0));
+      __syncthreads();  // dU~ of chunk c is staged
+      if constexpr (OUT) s2g<E, TV, 64>(dut + (base + (int64_t)c * kChunk) * DV + v0, DV, sDu, LS, rows_of(c), lane);
+    }
+    return;
+  }
+
   // ---- compute waves: G^T tile t = wv + 4 i holds G[16 db + (lane & 15)][v0 + 16 vb + 4 (lane >> 4) + e]
   const int rA = 16 * wv;
   f32x4 Gt[TPW];
@@ -406,52 +445,19 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
     }
   }
-  // L2 warm-up two chunks ahead (see the register-fed kernel above)
-  constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * NT - 1) / (NTILE * NT);
-  int pw[5 * NL];
-#pragma unroll
-  for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
-  auto warm = [&](int c) {
-    const int n = rows_of(c);
-    const int64_t r0 = base + (int64_t)c * kChunk;
-    const int bk = n * DK * (int)sizeof(E);
-    l2_touch<NL, NT>(pw, w + r0 * DK, bk, tile, NTILE, tid);
-    l2_touch<NL, NT>(pw + NL, k + r0 * DK, bk, tile, NTILE, tid);
-    if constexpr (!TR) {
-      l2_touch<NL, NT>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, tid);
-      l2_touch<NL, NT>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                       kChunk * kChunk * (int)sizeof(E), tile, NTILE, tid);
-      l2_touch<NL, NT>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, tid);
-    }
-  };
-  if (nchunks > 0) warm(max(nchunks - 2, 0));
-
   for (int c = nchunks - 1; c >= 0; --c) {
     const unsigned char* st = tiles(c);
-    const int n = rows_of(c);
-    const int64_t r0 = base + (int64_t)c * kChunk;
     // Stage G (gradient of the state leaving chunk c): G^T tiles written transposed.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
       st_frag_t<E>(sG + 16 * db * LS + 16 * vb, LS, Gt[i], lane);
     }
-    l2_sink<5 * NL>(pw);
-    warm(max(c - 2, 0));
     __syncthreads();
 
     V kA[KS];  // this wave's K rows (A operand of K G)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kA[ks] = frag_rm_sw<E, DK>(st + L::oK, rA, ks * KC, lane);
-    if constexpr (OUT) {  // G of this slot -> dstates [d][v0 : v0 + TV]
-      E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
-      constexpr int VPR = TV / VE;
-#pragma unroll
-      for (int it = 0; it < (DK * VPR + NT - 1) / NT; ++it) {
-        const int i = min(it * NT + tid, DK * VPR - 1), d = i / VPR, cc = (i % VPR) * VE;
-        *(u32x4*)(gG + (int64_t)d * DV + cc) = *(const u32x4*)(sG + d * LS + cc);
-      }
-    }
     // dU~ = scale M^T dO + K G for this wave's rows (tokens).
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -470,7 +476,6 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
     }
     __syncthreads();
 
-    if constexpr (OUT) s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, LS, n, tid);
     // G^T += scale dO^T Q - dU~^T W
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
