@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   }
 }
 
-// DMA-fed variant for bf16 problems with 32-column tiles (ungated), organised like the forward
+// DMA-fed variant for bf16 problems with 32-column tiles, organised like the forward
 // scan: a loader wave fills swizzled LDS tiles of K, Q, W, M and dO one chunk ahead by LDS DMA,
 // and a storer wave copies the staged G and dU~ out and warms L2 two chunks ahead, so the four
 // compute waves issue no global memory operation in the loop. The loader waits for its DMA
@@ -291,8 +291,11 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 // s_barrier for it, which waits for nothing. Rows past the end of a partial chunk, which the
 // DMA fills with copies of the last row, are cleared by the loader (the products over tokens
 // need zeros there). The storer reads the G staging between the step's two barriers and dU~
-// after the second, before the compute waves write either again.
-template <typename E, int DK, int DV>
+// after the second, before the compute waves write either again. Gated EFLA (GT) as in the
+// register-fed kernel: the loader also stages the chunk's running log-decay sums and Gamma, Q
+// elements are scaled by Gamma as they are read (rounded as the register-fed kernel rounds them
+// when they land), and the decays of K G and of G act on registers.
+template <typename E, int DK, int DV, bool GT = false>
 struct ScanBwdDmaLds {
   static constexpr int TV = 32;
   typedef Swz<E, DK> SK;  // K, Q, W [64][DK]
@@ -301,7 +304,9 @@ struct ScanBwdDmaLds {
   static constexpr int LS = pitch<E>(TV), LT = pitch<E>(64);
   static constexpr size_t oK = 0, oQ = oK + SK::BYTES, oW = oQ + SK::BYTES, oM = oW + SK::BYTES;
   static constexpr size_t oO = oM + SM::BYTES;
-  static constexpr size_t stage = oO + SO::BYTES;
+  static constexpr size_t oCs = oO + SO::BYTES;  // running log-decay sums c [64] (GT)
+  static constexpr size_t oGm = oCs + 64 * 4;     // Gamma = e^c [64] (GT)
+  static constexpr size_t stage = oCs + (GT ? 2 * 64 * 4 : 0);
   static constexpr size_t oG = 2 * stage;                   // G slice [DK][LS]
   static constexpr size_t oDt = oG + DK * LS * sizeof(E);   // dU~^T [TV][LT]
   static constexpr size_t oDu = oDt + TV * LT * sizeof(E);  // dU~ staging [64][LS]
@@ -310,12 +315,13 @@ struct ScanBwdDmaLds {
 
 constexpr int kScanBwdDmaThreads = 6 * 64;  // four compute waves, the loader and the storer
 
-template <typename E, int DK, int DV, int MODE>
+template <typename E, int DK, int DV, bool GT, int MODE>
 __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
-    E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0) {
-  typedef ScanBwdDmaLds<E, DK, DV> L;
+    E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0,
+    const float* __restrict__ cum) {
+  typedef ScanBwdDmaLds<E, DK, DV, GT> L;
   typedef typename Mma<E>::vec V;
   constexpr int TV = L::TV, LS = L::LS, LT = L::LT;
   constexpr int KC = Mma<E>::KC, KS = DK / KC;
@@ -344,6 +350,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   auto tiles = [&](int c) { return smem + (c & 1) * L::stage; };
 
   if (wv == 4) {  // ---- loader wave
+    float cumv = 0.f;  // gated: the chunk's running log-decay sum of token lane, on its way to LDS
     auto issue = [&](int c) {
       unsigned char* st = tiles(c);
       const int n = rows_of(c);
@@ -356,11 +363,18 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
                            kChunk, kChunk, 0, lane);
         dma_tile<E, TV, 1>(st + L::oO, d_o + r0 * DV + v0, DV, n, 0, lane);
       }
+      // 64 floats, one plain load per lane; stored to LDS only after the wait for the DMA, since
+      // using the value earlier would wait for every DMA issued before it
+      if constexpr (GT) cumv = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
     };
-    auto clear_tail = [&](int c) {  // rows >= n (whole rows: the swizzle stays inside a row)
-      const int n = rows_of(c);
-      if (n >= kChunk) return;
+    auto finish = [&](int c) {  // after the wait: the decay sums, and rows >= n cleared
       unsigned char* st = tiles(c);
+      if constexpr (GT) {
+        ((float*)(st + L::oCs))[lane] = cumv;
+        ((float*)(st + L::oGm))[lane] = exp_decay(cumv);
+      }
+      const int n = rows_of(c);
+      if (n >= kChunk) return;  // whole rows are cleared: the swizzle stays inside a row
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int b = n * L::SK::RB + 16 * lane; b < kChunk * L::SK::RB; b += 16 * 64) {
         *(u32x4*)(st + L::oK + b) = z;
@@ -374,14 +388,14 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
     if (nchunks > 0) {
       issue(nchunks - 1);
       wait_vm_all();
-      clear_tail(nchunks - 1);
+      finish(nchunks - 1);
     }
     for (int c = nchunks - 1; c >= 0; --c) {
       __syncthreads();  // chunk c is in LDS; every wave is done with chunk c + 1's stage
       if (c > 0) issue(c - 1);
       __builtin_amdgcn_s_barrier();  // the step's second barrier
       wait_vm_all();
-      if (c > 0) clear_tail(c - 1);
+      if (c > 0) finish(c - 1);
     }
     return;
   }
@@ -447,6 +461,9 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   }
   for (int c = nchunks - 1; c >= 0; --c) {
     const unsigned char* st = tiles(c);
+    const int n = rows_of(c);
+    const float* sCs = (const float*)(st + L::oCs);
+    const float* sGm = (const float*)(st + L::oGm);
     // Stage G (gradient of the state leaving chunk c): G^T tiles written transposed.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -470,26 +487,38 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
           md = Mma<E>::step(frag_km_sw<E, 64>(st + L::oM, k0, rA, lane),
                             frag_km_sw<E, TV>(st + L::oO, k0, 16 * nb, lane), md);
       }
+      if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
+        const float cl = sCs[n - 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kg[i] *= exp_decay(fminf(cl - sCs[rA + 4 * (lane >> 4) + i], 0.f));
+      }
       f32x4 du = kg + g.scale * md;
       st_frag_t<E>(sDt + 16 * nb * LT + rA, LT, du, lane);
       if constexpr (OUT) st_frag_lds<E>(sDu + rA * LS + 16 * nb, LS, du, lane);
     }
     __syncthreads();
 
-    // G^T += scale dO^T Q - dU~^T W
+    // G^T += scale dO^T Q - dU~^T W (gated: G^T <- e^{c_last} G^T + ..., Q scaled by Gamma)
+    const float gC = GT ? exp_decay(sCs[n - 1]) : 1.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
       f32x4 a = zero4(), b = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < kChunk; k0 += KC) {
-        if constexpr (!TR)
-          a = Mma<E>::step(frag_km_sw<E, TV>(st + L::oO, k0, 16 * vb, lane),
-                           frag_km_sw<E, DK>(st + L::oQ, k0, 16 * db, lane), a);
+        if constexpr (!TR) {
+          V qf = frag_km_sw<E, DK>(st + L::oQ, k0, 16 * db, lane);
+          if constexpr (GT) {  // element e is token k0 + KC/4 (lane >> 4) + e
+            const int t0 = k0 + (KC / 4) * (lane >> 4);
+#pragma unroll
+            for (int e = 0; e < KC / 4; ++e) qf[e] = to_e<E>(to_f(qf[e]) * sGm[t0 + e]);
+          }
+          a = Mma<E>::step(frag_km_sw<E, TV>(st + L::oO, k0, 16 * vb, lane), qf, a);
+        }
         b = Mma<E>::step(frag_rm<E>(sDt + 16 * vb * LT + k0, LT, lane),
                          frag_km_sw<E, DK>(st + L::oW, k0, 16 * db, lane), b);
       }
-      Gt[i] = Gt[i] + (g.scale * a - b);
+      Gt[i] = gC * Gt[i] + (g.scale * a - b);
     }
   }
   if (dh0) {  // gradient at the state entering the sequence
@@ -500,14 +529,15 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   }
 }
 
-template <typename E, int DK, int DV, int MODE>
+template <typename E, int DK, int DV, bool GT, int MODE>
 static hipError_t scan_bwd_dma_run(const Shape& s, const int* table, const void* q, const void* k,
                                    const void* w, const void* m, const void* d_o, void* dut,
-                                   void* dstates, const float* dht, float* dh0, hipStream_t st) {
-  typedef ScanBwdDmaLds<E, DK, DV> L;
+                                   void* dstates, const float* dht, float* dh0, hipStream_t st,
+                                   const float* cum) {
+  typedef ScanBwdDmaLds<E, DK, DV, GT> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_dma_kernel<E, DK, DV, MODE>,
+    hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_dma_kernel<E, DK, DV, GT, MODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -515,12 +545,13 @@ static hipError_t scan_bwd_dma_run(const Shape& s, const int* table, const void*
   const int64_t blocks = (int64_t)s.n_seqs * s.H * (DV / L::TV);
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
-  hipLaunchKernelGGL((scan_bwd_dma_kernel<E, DK, DV, MODE>), dim3((unsigned)blocks), dim3(kScanBwdDmaThreads),
+  hipLaunchKernelGGL((scan_bwd_dma_kernel<E, DK, DV, GT, MODE>), dim3((unsigned)blocks), dim3(kScanBwdDmaThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0);
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
   hipError_t e = hipGetLastError();
-  static const char* const names[3] = {"scan_bwd", "scan_bwd_state", "scan_bwd_transition"};
-  prof_end(names[MODE], st);
+  static const char* const names[2][3] = {{"scan_bwd", "scan_bwd_state", "scan_bwd_transition"},
+                                           {"scan_bwd_gated", "scan_bwd_state_gated", "scan_bwd_transition_gated"}};
+  prof_end(names[GT][MODE], st);
   return e;
 }
 
@@ -556,13 +587,15 @@ static hipError_t scan_bwd_mode(const Shape& s, const int* table, const void* q,
                                 void* dstates, const float* dht, float* dh0, hipStream_t st,
                                 const float* cum) {
   if (cum) {
-    if constexpr (sizeof(E) == 2)
+    if constexpr (sizeof(E) == 2 && TV == 32)
+      return scan_bwd_dma_run<E, DK, DV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+    else if constexpr (sizeof(E) == 2)
       return scan_bwd_run<E, DK, DV, TV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
     else
       return hipErrorInvalidValue;
   }
   if constexpr (sizeof(E) == 2 && TV == 32)
-    return scan_bwd_dma_run<E, DK, DV, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st);
+    return scan_bwd_dma_run<E, DK, DV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
   else
     return scan_bwd_run<E, DK, DV, TV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
 }
