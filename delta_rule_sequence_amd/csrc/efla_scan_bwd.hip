@@ -284,14 +284,15 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 }
 
 // DMA-fed variant for bf16 problems with 32-column tiles, organised like the forward
-// scan: a loader wave fills swizzled LDS tiles of K, Q, W, M and dO one chunk ahead by LDS DMA,
-// and a storer wave copies the staged G and dU~ out and warms L2 two chunks ahead, so the four
-// compute waves issue no global memory operation in the loop. The loader waits for its DMA
-// only before the barrier that publishes the chunk; the step's other barrier is a bare
-// s_barrier for it, which waits for nothing. Rows past the end of a partial chunk, which the
-// DMA fills with copies of the last row, are cleared by the loader (the products over tokens
-// need zeros there). The storer reads the G staging between the step's two barriers and dU~
-// after the second, before the compute waves write either again. Gated EFLA (GT) as in the
+// scan: a loader wave fills swizzled LDS tiles of K, Q, W, M and dO one chunk ahead by LDS DMA
+// and warms L2 for the chunk after, and a storer wave copies the staged G and dU~ out, so the
+// four compute waves issue no global memory operation in the loop. The loader's barriers are
+// bare s_barriers (a fence would wait for every load in flight); before the one that publishes
+// a chunk it waits for the DMA only, by a counted vmcnt that leaves the younger warm-up loads in
+// flight. Rows past the end of a partial chunk, which the DMA fills with copies of the last row,
+// are cleared by the loader (the products over tokens need zeros there). The storer reads the G
+// staging between the step's two barriers and dU~ after the second, before the compute waves
+// write either again. Gated EFLA (GT) as in the
 // register-fed kernel: the loader also stages the chunk's running log-decay sums and Gamma, Q
 // elements are scaled by Gamma as they are read (rounded as the register-fed kernel rounds them
 // when they land), and the decays of K G and of G act on registers.
@@ -349,8 +350,29 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   auto rows_of = [&](int c) { return min(kChunk, si.len - c * kChunk); };
   auto tiles = [&](int c) { return smem + (c & 1) * L::stage; };
 
+  constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * 64 - 1) / (NTILE * 64);
+  constexpr int NWARM = NL * (TR ? 2 : 5);  // warm-up loads issued after each DMA: W, K (, Q, M, dO)
+  static_assert(NWARM <= 15, "vmcnt field");
   if (wv == 4) {  // ---- loader wave
     float cumv = 0.f;  // gated: the chunk's running log-decay sum of token lane, on its way to LDS
+    int pw[5 * NL];
+#pragma unroll
+    for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
+    auto warm = [&](int c) {  // one word per 128-byte line; the head's workgroups split the lines
+      const int n = rows_of(c);
+      const int64_t r0 = base + (int64_t)c * kChunk;
+      const int bk = n * DK * (int)sizeof(E);
+      l2_touch<NL>(pw, w + r0 * DK, bk, tile, NTILE, lane);
+      l2_touch<NL>(pw + NL, k + r0 * DK, bk, tile, NTILE, lane);
+      if constexpr (!TR) {
+        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, lane);
+        l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+        l2_touch<NL>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
+      }
+    };
+    // the DMA has landed: vmcnt(NWARM) leaves only the younger warm-up loads in flight
+    auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | NWARM); };
     auto issue = [&](int c) {
       unsigned char* st = tiles(c);
       const int n = rows_of(c);
@@ -387,41 +409,29 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
     };
     if (nchunks > 0) {
       issue(nchunks - 1);
-      wait_vm_all();
+      warm(max(nchunks - 2, 0));
+      wait_dma();
       finish(nchunks - 1);
     }
     for (int c = nchunks - 1; c >= 0; --c) {
-      __syncthreads();  // chunk c is in LDS; every wave is done with chunk c + 1's stage
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): finish's LDS writes are done
+      __builtin_amdgcn_s_barrier();  // chunk c is in LDS; every wave is done with chunk c + 1's stage
       if (c > 0) issue(c - 1);
       __builtin_amdgcn_s_barrier();  // the step's second barrier
-      wait_vm_all();
-      if (c > 0) finish(c - 1);
+      l2_sink<5 * NL>(pw);           // the previous step's warm-up (and, at worst, this DMA)
+      warm(max(c - 2, 0));
+      if (c > 0) {
+        wait_dma();
+        finish(c - 1);
+      }
     }
+    wait_vm_all();
     return;
   }
 
   if (wv == 5) {  // ---- storer wave (lane: its thread index)
-    constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * 64 - 1) / (NTILE * 64);
-    int pw[5 * NL];
-#pragma unroll
-    for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
-    auto warm = [&](int c) {  // one word per 128-byte line; the head's workgroups split the lines
-      const int n = rows_of(c);
-      const int64_t r0 = base + (int64_t)c * kChunk;
-      const int bk = n * DK * (int)sizeof(E);
-      l2_touch<NL>(pw, w + r0 * DK, bk, tile, NTILE, lane);
-      l2_touch<NL>(pw + NL, k + r0 * DK, bk, tile, NTILE, lane);
-      if constexpr (!TR) {
-        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, lane);
-        l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
-        l2_touch<NL>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
-      }
-    };
-    if (nchunks > 0) warm(max(nchunks - 2, 0));
     for (int c = nchunks - 1; c >= 0; --c) {
       __syncthreads();  // G of chunk c is staged
-      l2_sink<5 * NL>(pw);  // the warm-up of the previous step, before this step's stores
       if constexpr (OUT) {  // G of this slot -> dstates [d][v0 : v0 + TV] (no store in a branch)
         E* gG = dstates + ((int64_t)(si.slot0 + c) * g.H + h) * DK * DV + v0;
         constexpr int VPR = TV / VE;
@@ -431,7 +441,6 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
           *(u32x4*)(gG + (int64_t)d * DV + cc) = *(const u32x4*)(sG + d * LS + cc);
         }
       }
-      warm(max(c - 2, 0));
       __syncthreads();  // dU~ of chunk c is staged
       if constexpr (OUT) s2g<E, TV, 64>(dut + (base + (int64_t)c * kChunk) * DV + v0, DV, sDu, LS, rows_of(c), lane);
     }

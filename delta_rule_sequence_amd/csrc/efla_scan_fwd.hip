@@ -14,10 +14,9 @@
 // token rows of U~ and O) are numbered in the contiguous-contraction order (prow), so every
 // A operand from LDS is a single 16-byte read. Two further waves move the data, each in a loop
 // of its own with the same barrier sequence: the loader wave fills swizzled LDS tiles of W, Q,
-// K, M and U one chunk ahead by LDS DMA (double-buffered); the storer wave copies the staged O,
-// U~ and chunk states out as 16-byte rows. An LDS DMA in flight makes the compiler drain every
-// outstanding memory operation of its wave at the next barrier; kept apart from the DMA, the
-// output stores are never waited for. One barrier per chunk hands the buffers over.
+// K, M and U one chunk ahead by LDS DMA (double-buffered) and warms L2 for the chunk after; the
+// storer wave copies the staged O, U~ and chunk states out as 16-byte rows. Kept apart from the
+// loads, the output stores are never waited for. One barrier per chunk hands the buffers over.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -290,21 +289,14 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
   };
 
   // Three loops, nchunks + 1 barriers each.
+  // The loader also warms L2 two chunks ahead (one word per 128-byte line; the workgroups of the
+  // (sequence, head) split the shared tiles), so its DMA of chunk c + 1 reads lines requested a
+  // step earlier and HBM keeps a request stream across the barriers. Before the barrier that
+  // publishes a chunk it waits for the DMA only (a counted vmcnt: the younger warm-up loads stay
+  // in flight) and the barrier is a bare s_barrier, whose fence would wait for everything; each
+  // warm-up is consumed a step later. Every request is unconditional (clamped chunk index), so
+  // the compiler's counts stay exact. The storer then never waits for anything but the barriers.
   if (loader) {
-    issue(0);
-    for (int c = 0; c < nchunks; ++c) {
-      wait_vm_all();    // chunk c has landed
-      __syncthreads();  // chunk c is in LDS; every wave is done with chunk c - 1's stage
-      if (c + 1 < nchunks) issue(c + 1);
-    }
-    __syncthreads();
-    return;
-  }
-  if (storer) {
-    // Besides the stores, this wave warms L2 two chunks ahead of the compute waves, so the
-    // loader's DMA of chunk c + 1 reads lines requested a step earlier and HBM keeps a request
-    // stream across the barriers. The workgroups of one (sequence, head) split the shared tiles
-    // line by line; nothing waits for these loads until the next step.
     constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + 64 * NTILE - 1) / (64 * NTILE);
     int pw[5 * NL];
 #pragma unroll
@@ -312,21 +304,37 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
     auto warm = [&](int c) {
       const int n = rows_of(c);
       const int64_t r0 = base + (int64_t)c * kChunk;
-      l2_touch<NL>(pw, w + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, tl);
-      l2_touch<NL>(pw + NL, k + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, tl);
+      l2_touch<NL>(pw, w + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
+      l2_touch<NL>(pw + NL, k + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
       if constexpr (WO) {
-        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, tl);
+        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
         l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, tl);
+                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
       }
-      if constexpr (!PM) l2_touch<NL>(pw + 4 * NL, u + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, tl);
+      if constexpr (!PM) l2_touch<NL>(pw + 4 * NL, u + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
     };
+    // warm-up loads issued after each DMA: W and K, Q and M with the output, U unless PM
+    constexpr int NWARM = NL * (2 + (WO ? 2 : 0) + (PM ? 0 : 1));
+    static_assert(NWARM <= 15, "vmcnt field");
+    issue(0);
     warm(min(1, nchunks - 1));
     for (int c = 0; c < nchunks; ++c) {
+      // vmcnt(NWARM), lgkmcnt(0): chunk c's DMA has landed (only the younger warm-up loads may
+      // still be in flight), and so has the gated loader's LDS store
+      __builtin_amdgcn_s_waitcnt(0x0070 | NWARM);
+      __builtin_amdgcn_s_barrier();
+      issue(min(c + 1, nchunks - 1));
+      l2_sink<5 * NL>(pw);
+      warm(min(c + 2, nchunks - 1));
+    }
+    wait_vm_all();
+    __syncthreads();
+    return;
+  }
+  if (storer) {
+    for (int c = 0; c < nchunks; ++c) {
       __syncthreads();  // staging of chunk c - 1 is complete
-      l2_sink<5 * NL>(pw);  // the warm-up of the previous step, before any store of this one
       if (c > 0) copy_out(c - 1);
-      warm(min(c + 2, nchunks - 1));  // unconditional: no load inside a branch
     }
     __syncthreads();
     copy_out(nchunks - 1);
