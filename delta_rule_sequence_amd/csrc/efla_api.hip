@@ -148,9 +148,10 @@ efla_status to_shape(const efla_problem* p, Shape& s) {
   s.seg_plan_nc = 0;
   if (!p->cu_seqlens && s.ntc > 1) {
     int want = p->segments;
-    if (want == 0) {  // split only when whole-sequence scans would leave compute units idle
+    if (want == 0) {  // split only when whole-sequence scans would leave compute units idle;
+                      // aim at one scan workgroup per compute unit (256)
       const int64_t wgs = (int64_t)p->B * p->H * (p->dv / 32 > 0 ? p->dv / 32 : 1);
-      want = (wgs < 128 && s.ntc >= 32) ? (int)(512 / wgs) : 1;
+      want = (wgs < 128 && s.ntc >= 32) ? (int)(256 / wgs) : 1;
       if (want > s.ntc / 16) want = s.ntc / 16;
     }
     if (want > s.ntc) want = s.ntc;

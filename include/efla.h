@@ -146,7 +146,8 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
  * at once from those states. Same results up to rounding; the workspace grows by
  * 4 B G H dk (2 dv + dk) bytes.
  * The library's choice (segments = 0) splits only when B * H * dv / 32 < 128 and a
- * sequence has at least 32 chunks, aiming at about 512 scan workgroups. */
+ * sequence has at least 32 chunks, aiming at about 256 scan workgroups (one per compute unit)
+ * and at least 16 chunks per segment. */
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
                      const void* beta, void* o, void* saved, size_t saved_bytes, void* ws,
                      size_t ws_bytes, void* stream);

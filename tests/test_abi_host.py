@@ -178,8 +178,11 @@ def test_segment_plan_workspace(L):
         return (L.efla_workspace_bytes(ctypes.byref(_p(**kw)), 0) -
                 L.efla_workspace_bytes(ctypes.byref(_p(**dict(kw, segments=1))), 0))
     per_seg = 16 * 128 * (2 * 128 + 128) * 4       # H * dk * (2 dv + dk) * 4 bytes
-    # long context, 16 heads: 512 chunks -> the library picks 8 segments
-    assert extra(B=1, T=32768) == 8 * per_seg
+    # long context, 16 heads: 512 chunks -> the library picks 4 segments (256 scan workgroups)
+    assert extra(B=1, T=32768) == 4 * per_seg
+    # 8 heads: 8 segments; 2 heads, 32 chunks: capped at 16 chunks per segment -> 2
+    assert extra(B=1, H=8, T=32768) == 8 * per_seg // 2
+    assert extra(B=1, H=2, T=64 * 32) == 2 * per_seg // 8
     # a full chip of whole-sequence scans already: no split
     assert extra() == 0
     # explicit requests: at most one segment per chunk, no empty segment
@@ -192,7 +195,7 @@ def test_segment_plan_workspace(L):
     # the backward's recompute path runs the same forward
     p, p1 = _p(B=1, T=32768), _p(B=1, T=32768, segments=1)
     assert (L.efla_workspace_bytes(ctypes.byref(p), 1) -
-            L.efla_workspace_bytes(ctypes.byref(p1), 1)) == 8 * per_seg
+            L.efla_workspace_bytes(ctypes.byref(p1), 1)) == 4 * per_seg
 
 
 def test_gated_entry_points_reject_bad_arguments(L):
