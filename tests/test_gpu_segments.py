@@ -117,6 +117,9 @@ BWD_CASES = [  # name, workload overrides, segments, mode
     ("bf16_dk64_dv128", dict(idx=2, B=1, H=2, T=64 * 12 + 40, dk=64, dv=128), 3, "exact"),
     ("bf16_dk128_dv64", dict(idx=2, B=1, H=2, T=64 * 12 + 40, dk=128, dv=64), 3, "exact"),
     ("bf16_delta_rule", dict(idx=2, B=1, H=2, T=64 * 16), 4, "euler"),
+    # 4 segments x 16 heads: wide enough for the 32-column tiling, whose state-only, transition
+    # and full reverse scans are DMA-fed (the unsegmented comparison runs the 16-column tiling)
+    ("bf16_wide_seg4", dict(idx=2, B=1, H=16, T=64 * 20 + 7), 4, "exact"),
 ]
 
 
