@@ -56,6 +56,8 @@ CASES = [  # name, workload overrides, gate mean, segments, mode
     ("mild_seg5", dict(B=1, H=2, T=64 * 37 + 5), 3.0, 5, "exact"),
     ("strong_seg3", dict(B=2, H=2, T=64 * 12 + 30), 0.0, 3, "exact"),
     ("mild_delta_rule", dict(B=1, H=2, T=150), 3.0, 1, "euler"),
+    # 4 segments x 16 heads: the 32-column tiling (DMA-fed gated reverse scans in every mode)
+    ("mild_wide_seg4", dict(B=1, H=16, T=64 * 20 + 7), 3.0, 4, "exact"),
 ]
 
 
