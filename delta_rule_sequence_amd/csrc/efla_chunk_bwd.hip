@@ -284,6 +284,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   ChunkUnit nxt = chunk_unit(g, more ? un : 0);
   if (!more) nxt.n = 1;
   issue_k(nxt);
+  __builtin_amdgcn_sched_barrier(0);  // these requests go out now, not after step 2's products
 
   // ---- 2: dW = -dU~ S^T, dQ = scale dO S^T, dK = U~ G^T (S and G from registers);
   //         dM = scale tril(dO U~^T); per-token coefficients
