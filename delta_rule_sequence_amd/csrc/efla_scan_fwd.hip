@@ -98,8 +98,8 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
 
   // ---- loader wave (wl: its index among the loader waves) and storer wave (tl: its lane)
   const int wl = 0, tl = tid - 64 * (NWC + 1);
-  auto issue = [&](int c) {
-    unsigned char* st = smem + (c & 1) * L::stage;
+  auto issue = [&](int c, int slot) {  // chunk c into LDS stage `slot`
+    unsigned char* st = smem + slot * L::stage;
     const int n = rows_of(c);
     const int64_t r0 = base + (int64_t)c * kChunk;
     dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
@@ -316,14 +316,16 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
     // warm-up loads issued after each DMA: W and K, Q and M with the output, U unless PM
     constexpr int NWARM = NL * (2 + (WO ? 2 : 0) + (PM ? 0 : 1));
     static_assert(NWARM <= 15, "vmcnt field");
-    issue(0);
+    issue(0, 0);
     warm(min(1, nchunks - 1));
     for (int c = 0; c < nchunks; ++c) {
       // vmcnt(NWARM), lgkmcnt(0): chunk c's DMA has landed (only the younger warm-up loads may
       // still be in flight), and so has the gated loader's LDS store
       __builtin_amdgcn_s_waitcnt(0x0070 | NWARM);
       __builtin_amdgcn_s_barrier();
-      issue(min(c + 1, nchunks - 1));
+      // after the last chunk the request repeats it into the stage that chunk c + 1 would use,
+      // which no wave reads any more (every request is unconditional)
+      issue(min(c + 1, nchunks - 1), (c + 1) & 1);
       l2_sink<5 * NL>(pw);
       warm(min(c + 2, nchunks - 1));
     }
