@@ -9,11 +9,13 @@
 // per chunk, the G that entered the step (the gradient of the chunk's outgoing state) for
 // the chunk-parallel gradient kernel.
 //
-// Latency hiding as in the forward scan: the K rows of each wave are register A fragments;
-// the previous chunk's K rows and Q, W, M, dO tiles are loaded into registers while the
-// current chunk computes, and the LDS tiles are double-buffered. Products over the token
-// or d_k index read LDS tiles k-major with the LDS transpose read (bf16). dU~ and G leave
-// through LDS staging as 16-byte stores.
+// Two kernels share this math. The register-fed one (16-column tiles, fp32): the K rows of
+// each wave are register A fragments, the previous chunk's K rows and Q, W, M, dO tiles are
+// loaded into registers while the current chunk computes, and the LDS tiles are double-
+// buffered. The DMA-fed one (bf16, 32-column tiles, further below) has a loader wave fill the
+// LDS tiles by DMA and a storer wave write the outputs, as the forward scan does. Products over
+// the token or d_k index read LDS tiles k-major with the LDS transpose read (bf16). dU~ and G
+// leave through LDS staging as 16-byte stores.
 //
 // Gated EFLA (GT), with c the running log-decay sums of the chunk, Gamma = e^c,
 // r = e^{c_last - c}: dU~ = scale P^T dO + diag(r) K G (P = tril(Q K^T) * e^{c_t - c_s}, saved
