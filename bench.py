@@ -99,7 +99,8 @@ def ingest_counters(fetch_csv, write_csv, probe_mib):
     fetch_scale, write_scale = copy_kib / cf[0], copy_kib / cw[0]
 
     def step_instance(d, name):  # the template instance the timed step launches most often
-        cand = [(v[1], v[0]) for k, v in d.items() if "efla" in k and name + "_kernel" in k]
+        cand = [(v[1], v[0]) for k, v in d.items()
+                if "efla" in k and (name + "_kernel" in k or name + "_dma_kernel" in k)]
         return [max(cand)[1]] if cand else []
 
     out = {}
