@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t = 16 * (rb0 + i) + (lane & 15);
-      const float ct = cC[t], gm = exp_decay(ct), rr = exp_decay(fminf(cl - ct, 0.f));
+      const float ct = cC[t], gm = exp_decay(ct), rr = exp_decay(cl - ct);
       float p1 = 0.f, p2 = 0.f;
 #pragma unroll
       for (int j = 0; j < CK; ++j) {
@@ -384,7 +384,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
         float rsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float d = exp_decay(fminf(ct - cC[s0 + e], 0.f));
+          // D_ts = e^{c_t - c_s} on and below the diagonal only: above it dP * P is zero, and the
+          // factor alone may overflow when the log-decays are negative
+          const float d = s0 + e <= t ? exp_decay(ct - cC[s0 + e]) : 0.f;
           const float ev = mm[e] * (qk[0][j][e] * d);  // dP * P (mm is zero above the diagonal)
           rsum += ev;
           const float csum = group_sum<16>(ev);
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * pr + 4 * (lane >> 4) + i;
         float a = row > col ? -da[0][j][i] : 0.f;
-        if constexpr (GT) a *= exp_decay(fminf(cC[row] - cC[col], 0.f));  // A carries D
+        if constexpr (GT) a = row > col ? a * exp_decay(cC[row] - cC[col]) : 0.f;  // A carries D
         rs[i] = a * kk[0][j][i];
         dg[i] = a * cAl[row];
         if constexpr (GT) fc = fmaf(cAl[row], rs[i], fc);  // dA . A, column part

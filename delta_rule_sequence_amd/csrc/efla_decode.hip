@@ -4,81 +4,117 @@
 // effective step alpha_t) and the recurrent, linear-time inference the pages credit the
 // delta-rule family with: per token
 //   S <- S + alpha_t k_t (v_t - S^T k_t)^T,   o_t = scale S^T q_t   (state after the update).
-// One workgroup per (batch row, head); thread j keeps column j of the fp32 d_k x d_v state in
-// registers for all T tokens, so the state is read and written once per call. k_t and q_t are
-// shared through LDS; every thread forms ||k_t||^2 itself (d_k FMAs, cheaper than a reduction).
 // With log-decays (gated EFLA): S <- e^{a} (S - alpha k k^T S) + b k v^T, b the gated input
-// coefficient, i.e. column j: S_j <- e^{a} S_j + k (b v_j - e^{a} alpha (S^T k)_j).
+// coefficient. Column j of the update is S_j <- g S_j + k r_j with g = e^{a} (1 without a gate)
+// and r_j = b v_j - g alpha (S^T k)_j, so the read-out after the update needs no second pass
+// over the state: o_j = g (S^T q)_j + r_j (k . q), from the state before the update.
+//
+// The state is [B][H][d_k][d_v] fp32; decoding is bound by reading and writing it once per
+// call, which for one token is a single round trip to memory and back. Each (batch row, head) is
+// split over d_v / 8 workgroups of one wave each (1,024 waves at 4 x 16 heads of width 128), so a
+// call fills the chip and every reduction stays inside a wave: no barrier, no LDS. Lane l holds
+// the 16-byte column group l & 1 of the rows l / 2 + 32 i (i < d_k / 32) in registers for all T
+// tokens and loads the k and q entries of its own rows itself. Per token the partial sums of
+// S^T k, S^T q, ||k||^2 and k . q over a lane's rows are reduced over the 32 lanes that share its
+// column group (five xor shuffles). The four workgroups that cover one 128-byte line of every
+// state row (32 columns) are placed on the same XCD (workgroups are dealt to the 8 XCDs round
+// robin), so each line is fetched into one L2 only.
 #include "efla_internal.hpp"
 
 namespace efla {
 
+constexpr int kDecCols = 8;    // state columns per workgroup (one wave)
+constexpr int kDecRows = 32;   // rows covered by one pass of the wave (two column groups)
+
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(DV) void decode_kernel(Geom g, const E* __restrict__ q,
+__global__ __launch_bounds__(64) void decode_kernel(Geom g, const E* __restrict__ q,
                                                     const E* __restrict__ k,
                                                     const E* __restrict__ v,
                                                     const E* __restrict__ beta,
                                                     const E* __restrict__ gate,
                                                     float* __restrict__ state,
-                                                    E* __restrict__ o) {
-  __shared__ float sk[DK], sq[DK];
-  const int j = threadIdx.x;
-  const int64_t bh = blockIdx.x;               // b * H + h
-  float* S = state + bh * DK * DV;
-  float col[DK];
+                                                    E* __restrict__ o, int xcd_map) {
+  constexpr int RPT = DK / kDecRows;            // rows per lane (4 or 2)
+  constexpr int NT = DV / kDecCols;             // workgroups per (batch row, head)
+  const int lane = threadIdx.x;
+  const int cg = lane & 1, rg = lane >> 1;      // column group, first row
+  int u = blockIdx.x;
+  if (xcd_map) {  // the 4 consecutive units of one 32-column group share blockIdx % 8
+    const int L = u >> 3, x = u & 7;
+    u = ((L >> 2) << 5) + (x << 2) + (L & 3);
+  }
+  const int64_t bh = u / NT;                    // b * H + h
+  const int c0 = (u % NT) * kDecCols + 4 * cg;  // this lane's first column
+  float* S = state + bh * DK * DV + c0;
+  f32x4 col[RPT];                               // S[rg + 32 i][c0 .. c0 + 3]
 #pragma unroll
-  for (int d = 0; d < DK; ++d) col[d] = S[(int64_t)d * DV + j];
+  for (int i = 0; i < RPT; ++i) col[i] = *(const f32x4*)(S + (int64_t)(rg + kDecRows * i) * DV);
   const int64_t row0 = bh * g.T;
   for (int t = 0; t < g.T; ++t) {
     const int64_t r = row0 + t;
-    __syncthreads();  // the previous token's reads of sk, sq are done
-    for (int d = j; d < DK; d += DV) {
-      sk[d] = to_f(k[r * DK + d]);
-      sq[d] = to_f(q[r * DK + d]);
-    }
-    __syncthreads();
-    float lam = 0.f, skj = 0.f;
+    float kd[RPT], qd[RPT];
 #pragma unroll
-    for (int d = 0; d < DK; ++d) {
-      const float kd = sk[d];
-      lam = fmaf(kd, kd, lam);
-      skj = fmaf(col[d], kd, skj);  // (S^T k)_j
+    for (int i = 0; i < RPT; ++i) {
+      kd[i] = to_f(k[r * DK + rg + kDecRows * i]);
+      qd[i] = to_f(q[r * DK + rg + kDecRows * i]);
     }
+    const f32x4 vv = ld4f<E>(v + r * DV + c0);
     const float bt = to_f(beta[r]);
-    const float a = flow_coef(bt, lam, g.euler != 0).alpha;
-    float oj = 0.f;
-    if (gate) {
-      const float lg = to_f(gate[r]), gd = expf(lg);
-      const float rj = gated_input_coef(bt, lam, lg, g.euler != 0) * to_f(v[r * DV + j]) - gd * a * skj;
+    const float lg = gate ? to_f(gate[r]) : 0.f;
+    f32x4 y = zero4(), z = zero4();
+    float lam = 0.f, kq = 0.f;
 #pragma unroll
-      for (int d = 0; d < DK; ++d) {
-        col[d] = fmaf(sk[d], rj, gd * col[d]);
-        oj = fmaf(col[d], sq[d], oj);
+    for (int i = 0; i < RPT; ++i) {
+      y += col[i] * kd[i];
+      z += col[i] * qd[i];
+      lam = fmaf(kd[i], kd[i], lam);
+      kq = fmaf(kd[i], qd[i], kq);
+    }
+    // sum over the 32 lanes of this column group (every lane ends with the full sums)
+#pragma unroll
+    for (int off = 2; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] += __shfl_xor(y[e], off);
+        z[e] += __shfl_xor(z[e], off);
       }
-    } else {
-      const float rj = a * (to_f(v[r * DV + j]) - skj);
+      lam += __shfl_xor(lam, off);
+      kq += __shfl_xor(kq, off);
+    }
+    const float alpha = flow_coef(bt, lam, g.euler != 0).alpha;
+    float gd = 1.f, bin = alpha;  // state decay and input coefficient (ungated: 1, alpha)
+    if (gate) {
+      gd = expf(lg);
+      bin = gated_input_coef(bt, lam, lg, g.euler != 0);
+    }
+    const f32x4 rr = bin * vv - (gd * alpha) * y;   // r_j (ungated: alpha (v_j - y_j))
 #pragma unroll
-      for (int d = 0; d < DK; ++d) {
-        col[d] = fmaf(sk[d], rj, col[d]);
-        oj = fmaf(col[d], sq[d], oj);
+    for (int i = 0; i < RPT; ++i) col[i] = gd * col[i] + kd[i] * rr;
+    if (rg == 0) {  // o_j = scale (g (S^T q)_j + r_j k . q): lanes 0 and 1
+      const f32x4 oj = g.scale * (gd * z + kq * rr);
+      if constexpr (sizeof(E) == 4) {
+        *(f32x4*)(o + r * DV + c0) = oj;
+      } else {
+        *(bf16x4*)(o + r * DV + c0) = bf16x4{(__bf16)oj[0], (__bf16)oj[1], (__bf16)oj[2], (__bf16)oj[3]};
       }
     }
-    o[r * DV + j] = to_e<E>(g.scale * oj);
   }
 #pragma unroll
-  for (int d = 0; d < DK; ++d) S[(int64_t)d * DV + j] = col[d];
+  for (int i = 0; i < RPT; ++i) *(f32x4*)(S + (int64_t)(rg + kDecRows * i) * DV) = col[i];
 }
 
 template <typename E, int DK, int DV>
 static hipError_t decode_go(const Shape& s, const void* q, const void* k, const void* v,
                             const void* beta, const void* gate, float* state, void* o,
                             hipStream_t st) {
-  const int64_t blocks = (int64_t)s.B * s.H;
+  static_assert(DK % kDecRows == 0 && DV % (4 * kDecCols) == 0, "decode tiling");
+  const int64_t blocks = (int64_t)s.B * s.H * (DV / kDecCols);
   if (blocks < 1) return hipSuccess;
+  const int xcd_map = blocks % 32 == 0 ? 1 : 0;  // the unit mapping is a bijection then
   prof_begin(st);
-  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(DV), 0, st,
+  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(64), 0, st,
                      make_geom(s, nullptr), (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)beta, (const E*)gate, state, (E*)o);
+                     (const E*)beta, (const E*)gate, state, (E*)o, xcd_map);
   hipError_t e = hipGetLastError();
   prof_end("decode", st);
   return e;

@@ -541,16 +541,17 @@ EFLA_DEV typename Mma<E>::vec aop_kc(const unsigned char* t, int b, int ks, int 
 }
 
 // Standard-order fragments (as frag_rm / frag_km: lane group g takes k0 + KC/4 g..) from a
-// swizzled LDS tile: frag_rm_sw reads A[m0 + (lane & 15)][k0..] with A[m][k] at (m, k);
-// frag_km_sw reads X[k0..][m0 + (lane & 15)] with X stored at (k, m), by transpose reads.
-template <typename E, int COLS>
+// swizzled LDS tile (swizzle keyed on row >> SH): frag_rm_sw reads A[m0 + (lane & 15)][k0..] with
+// A[m][k] at (m, k); frag_km_sw reads X[k0..][m0 + (lane & 15)] with X stored at (k, m), by
+// transpose reads.
+template <typename E, int COLS, int SH = 0>
 EFLA_DEV typename Mma<E>::vec frag_rm_sw(const unsigned char* t, int m0, int k0, int lane) {
-  typedef Swz<E, COLS> S;
+  typedef Swz<E, COLS, SH> S;
   return *(const typename Mma<E>::vec*)(t + S::off(m0 + (lane & 15), k0 + (lane >> 4) * (Mma<E>::KC / 4)));
 }
-template <typename E, int COLS>
+template <typename E, int COLS, int SH = 0>
 EFLA_DEV typename Mma<E>::vec frag_km_sw(const unsigned char* t, int k0, int m0, int lane) {
-  typedef Swz<E, COLS> S;
+  typedef Swz<E, COLS, SH> S;
   const int gq = lane >> 4, i = lane & 15;
   if constexpr (sizeof(E) == 2) {
     const int r = k0 + 8 * gq + (i >> 2), c = m0 + 4 * (i & 3);

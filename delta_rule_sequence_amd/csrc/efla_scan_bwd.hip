@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
       if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
         const float cl = sCs[n - 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kg[i] *= exp_decay(fminf(cl - sCs[rA + 4 * (lane >> 4) + i], 0.f));
+        for (int i = 0; i < 4; ++i) kg[i] *= exp_decay(cl - sCs[rA + 4 * (lane >> 4) + i]);
       }
       f32x4 du = kg + g.scale * md;
       st_frag_t<E>(sDt + 16 * nb * L::LT + rA, L::LT, du, lane);
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
         const float cl = sCs[n - 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kg[i] *= exp_decay(fminf(cl - sCs[rA + 4 * (lane >> 4) + i], 0.f));
+        for (int i = 0; i < 4; ++i) kg[i] *= exp_decay(cl - sCs[rA + 4 * (lane >> 4) + i]);
       }
       f32x4 du = kg + g.scale * md;
       st_frag_t<E>(sDt + 16 * nb * LT + rA, LT, du, lane);

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
         for (int i = 0; i < 4; ++i) {
           const float cr = cv[prow<E>(rb, g4 + i)];
           gam[rb][i] = exp_decay(cr);
-          dec[rb][i] = exp_decay(fminf(cl - cr, 0.f));
+          dec[rb][i] = exp_decay(cl - cr);
         }
     }
     if constexpr (WSV) {  // S_c, the state entering chunk c

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = 16 * nb + c4 + i;
-          const float dec = GT ? exp_decay(fminf(cra - sCm[col], 0.f)) : 1.f;  // e^{c_t - c_s}
+          const float dec = GT ? exp_decay(cra - sCm[col]) : 1.f;  // e^{c_t - c_s}, used for s < t
           av[i] = rowa > col ? ala * dec * acc[i] : 0.f;
         }
         *(f32x4*)(sA + rowa * L::LF + 16 * nb + c4) = av;
@@ -211,7 +211,10 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
           if constexpr (GT) {
             const float cr = sCm[rA + (lane & 15)];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m[i] *= exp_decay(fminf(cr - sCm[16 * nb + 4 * (lane >> 4) + i], 0.f));
+            for (int i = 0; i < 4; ++i) {  // e^{c_t - c_s} for s <= t (above, the factor may overflow)
+              const int col = 16 * nb + 4 * (lane >> 4) + i;
+              m[i] = col <= rA + (lane & 15) ? m[i] * exp_decay(cr - sCm[col]) : 0.f;
+            }
           }
         }
         st_frag_t<E>(sM + rA * L::LT + 16 * nb, L::LT, m, lane);

@@ -163,7 +163,8 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
 
 /* Gated EFLA forward (summary page, section 3.4 names it; the appendix applies the exact flow
  * to Gated DeltaNet; the pages print no formula, this is the reading taken): a per-token
- * log-decay a_t (gate, [B,H,T], problem dtype; a_t <= 0 decays) adds -a_t / beta_t times the
+ * log-decay a_t (gate, [B,H,T], problem dtype; a_t <= 0 decays; a_t > 0, growth, is computed
+ * by the same formulas, unclipped) adds -a_t / beta_t times the
  * identity to the dynamics matrix over the step interval, and the exact flow is
  *   S_t = e^{a_t} (I - alpha_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,
  *   alpha_t = beta_t phi(beta_t lambda_t),  b_t = beta_t phi(beta_t lambda_t - a_t),

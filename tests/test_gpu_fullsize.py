@@ -1,15 +1,24 @@
 """Parity at the full sizes of the five workloads, in the launch configuration the
 benchmark times (efla_fwd with a saved buffer, then efla_bwd reading it).
 
-The GPU computes every head; the fp64 oracle recomputes a sample of independent
-(sequence, head) streams, which is exact for them because streams do not interact.
-Tolerances as in test_gpu_parity (normwise, per tensor and per stream).
+The GPU computes the whole problem once; the fp64 oracle then recomputes EVERY independent
+(sequence, head) stream (tests/oracle_streams.py runs them in a thread pool), and each
+stream's outputs and gradients are compared with the GPU's: normwise relative error
+max|gpu - ref| / max|ref| per tensor and per stream, at most 1e-4 (fp32) or 2e-2 (bf16).
+Every GPU value must be finite.
+
+For the fp32 stiff workload the tokens are also checked one by one (reading R9 of the design
+notes): with key norms from 1e-3 to 100 and 5% of values scaled by 50, the largest rows of a
+stream set its normwise scale, so each token row t of o, dk and dbeta must also satisfy
+||gpu_t - ref_t|| <= tol * max(||ref_t||, f * max_s ||ref_s||), with the floors f of
+oracle_streams.TOKEN_FLOORS (1e-3 for o and dk, 3e-2 for dbeta), at tol for o and dk and 5 tol
+for dbeta (one token's cancellation, described there).
 """
 import numpy as np
 import pytest
 import torch
 
-from oracle import efla_oracle as O
+from oracle_streams import assert_streams, compare_streams
 from workloads import make_inputs, workload
 
 pytestmark = pytest.mark.gpu
@@ -30,26 +39,12 @@ def _dev(x, dt):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dt)
 
 
-def _samples(inp, n_streams, rng):
-    """(b, h, start, end) of sampled independent streams."""
-    B, H, T, _ = inp["k"].shape
-    cu = inp["cu_seqlens"]
-    out = []
-    if cu is None:
-        for _ in range(n_streams):
-            out.append((int(rng.integers(B)), int(rng.integers(H)), 0, T))
-    else:
-        ns = len(cu) - 1
-        # always include the longest sequence, then random ones
-        lens = np.diff(cu)
-        picks = [int(np.argmax(lens))] + [int(rng.integers(ns)) for _ in range(n_streams - 1)]
-        for s in picks:
-            out.append((0, int(rng.integers(H)), int(cu[s]), int(cu[s + 1])))
-    return out
+def _host(t):
+    return t.detach().float().cpu().numpy()
 
 
-@pytest.mark.parametrize("idx,n_streams", [(1, 2), (2, 4), (3, 2), (4, 4), (5, 3)])
-def test_fullsize_sampled(E, idx, n_streams):
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_fullsize_all_streams(E, idx):
     w = workload(idx)
     print("workload %d: %s" % (idx, w.name), flush=True)
     inp = make_inputs(w)
@@ -57,67 +52,43 @@ def test_fullsize_sampled(E, idx, n_streams):
     q, k, v, beta = (_dev(inp[n], dt) for n in ("q", "k", "v", "beta"))
     cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
     o, saved = E.efla_fwd(q, k, v, beta, 1.0, cu, save=True)
-    grads = None
+    gpu = {"o": o}
     if w.backward:
         do = _dev(inp["do"], dt)
-        grads = E.efla_bwd(q, k, v, beta, do, saved, 1.0, cu)
+        gpu.update(zip(("dq", "dk", "dv", "dbeta"), E.efla_bwd(q, k, v, beta, do, saved, 1.0, cu)))
     torch.cuda.synchronize()
-    tol = TOL[w.dtype]
-    rng = np.random.default_rng(1234 + idx)
-    for (b, h, s, e) in _samples(inp, n_streams, rng):
-        sl = lambda x: x[b:b + 1, h:h + 1, s:e]
-        ref_o, _ = O.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]))
-        got = o[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
-        err = O.rel_err(got, ref_o)
-        print("  stream b=%d h=%d [%d,%d): o %.3e" % (b, h, s, e, err), flush=True)
-        assert np.all(np.isfinite(got)) and err <= tol
-        if grads is not None:
-            g = O.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["do"]))
-            for name, t in zip(("dq", "dk", "dv", "dbeta"), grads):
-                gg = t[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
-                err = O.rel_err(gg, g[name])
-                print("    %s %.3e" % (name, err), flush=True)
-                assert np.all(np.isfinite(gg)) and err <= tol, name
-    # every output element is finite (no stream left unwritten or blown up)
-    assert torch.isfinite(o.float()).all()
-    if grads is not None:
-        for t in grads:
-            assert torch.isfinite(t.float()).all()
+    del q, k, v, beta, saved
+    gpu = {n: _host(t) for n, t in gpu.items()}
+    torch.cuda.empty_cache()
+    # the stiff fp32 workload is also checked token by token (o, dk, dbeta)
+    res = compare_streams(inp, gpu, w.backward, token_rows=("o", "dk", "dbeta") if idx == 4 else ())
+    assert_streams(res, TOL[w.dtype])
 
 
-@pytest.mark.parametrize("idx,n_streams", [(2, 2), (3, 2)])
-def test_fullsize_gated_sampled(E, idx, n_streams):
+def _gates(shape, seed):
+    """log sigmoid(x), x ~ N(3, 1) per (batch, head, token), as the values the GPU sees (bf16)."""
+    x = np.random.default_rng(seed).standard_normal(shape) + 3.0
+    a = (-np.logaddexp(0.0, -x)).astype(np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_fullsize_gated_all_streams(E, idx):
     """Gated EFLA at full size: the benchmark workload forward (saving) + backward, and the
-    long-context workload's forward (segment-parallel scan). Log-decays log sigmoid(x),
-    x ~ N(3, 1) per (batch, head, token), in bf16, as in the benchmark's gated step."""
+    long-context workload's forward (segment-parallel scan), every stream against the oracle."""
     w = workload(idx)
     print("workload %d (gated): %s" % (idx, w.name), flush=True)
     inp = make_inputs(w)
     B, H, T, _ = inp["k"].shape
-    x = np.random.default_rng(77 + idx).standard_normal((B, H, T)) + 3.0
-    a = (-np.logaddexp(0.0, -x)).astype(np.float32)
-    a = torch.from_numpy(a).to(torch.bfloat16).float().numpy()  # the values the GPU sees
+    a = _gates((B, H, T), 77 + idx)
     dt = TDT[w.dtype]
     q, k, v, beta, g = (_dev(t, dt) for t in (inp["q"], inp["k"], inp["v"], inp["beta"], a))
     o, saved = E.efla_fwd_gated(q, k, v, beta, g, 1.0, save=w.backward)
-    grads = None
+    gpu = {"o": o}
     if w.backward:
-        grads = E.efla_bwd_gated(q, k, v, beta, g, _dev(inp["do"], dt), saved, 1.0)
+        gpu.update(zip(("dq", "dk", "dv", "dbeta", "dgate"),
+                       E.efla_bwd_gated(q, k, v, beta, g, _dev(inp["do"], dt), saved, 1.0)))
     torch.cuda.synchronize()
-    tol = TOL[w.dtype]
-    rng = np.random.default_rng(4321 + idx)
-    for (b, h, s, e) in _samples(inp, n_streams, rng):
-        sl = lambda t: t[b:b + 1, h:h + 1, s:e]
-        ref_o, _ = O.gated_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a))
-        got = o[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
-        err = O.rel_err(got, ref_o)
-        print("  stream b=%d h=%d [%d,%d): o %.3e" % (b, h, s, e, err), flush=True)
-        assert np.all(np.isfinite(got)) and err <= tol
-        if grads is not None:
-            ref = O.gated_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
-                                   sl(inp["do"]))
-            for name, t in zip(("dq", "dk", "dv", "dbeta", "dgate"), grads):
-                gg = t[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
-                err = O.rel_err(gg, ref[name])
-                print("    %s %.3e" % (name, err), flush=True)
-                assert np.all(np.isfinite(gg)) and err <= tol, name
+    gpu = {n: _host(t) for n, t in gpu.items()}
+    res = compare_streams(inp, gpu, w.backward, gate=a)
+    assert_streams(res, TOL[w.dtype])

@@ -244,3 +244,28 @@ def test_gated_packed_sequences(E):
     _check("ht", _np(ht), ref_ht)
     for nm, t in zip(GRAD_NAMES, grads):
         _check(nm, _np(t), ref[nm])
+
+
+@pytest.mark.parametrize("segments", [1, 3])
+def test_positive_gate_follows_formula(E, segments):
+    """Log-decays of either sign, a ~ N(0.01, 0.03): a > 0 is growth, outside the decay reading,
+    but the kernels compute it with the same formulas (e^{c_t - c_s} and e^{c_last - c_t} taken
+    as they are, masked by index, never clipped at 1). Forward with final state and backward,
+    against the oracle; the positive part of the gate changes the result far beyond tolerance."""
+    w = workload(2, B=1, H=2, T=64 * 7 + 17)
+    inp = make_inputs(w, with_grad=True)
+    B, H, T, dk = inp["k"].shape
+    a = round_to_bf16((np.random.default_rng(41).standard_normal((B, H, T)) * 0.03 + 0.01).astype(np.float32))
+    assert np.mean(a > 0) > 0.5
+    q, k, v, beta, g, do = (_dev(x) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"]))
+    o, saved, ht = E.efla_fwd_gated(q, k, v, beta, g, 1.0, save=True, final_state=True, segments=segments)
+    grads = E.efla_bwd_gated(q, k, v, beta, g, do, saved, 1.0, segments=segments)
+    torch.cuda.synchronize()
+    ref_o, ref_ht = O.gated_forward(inp["q"], inp["k"], inp["v"], inp["beta"], a)
+    _check("o", _np(o), ref_o)
+    _check("ht", _np(ht), ref_ht)
+    ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"])
+    for nm, t in zip(GRAD_NAMES[:5], grads):
+        _check(nm, _np(t), ref[nm])
+    clipped, _ = O.gated_forward(inp["q"], inp["k"], inp["v"], inp["beta"], np.minimum(a, 0.0))
+    assert O.rel_err(clipped, ref_o) > 10 * TOL

@@ -2,16 +2,17 @@
 
 With d_v = 128 the scans use 32-column workgroups once sequences x heads reach 64; that tiling's
 backward scan is fed by LDS DMA and clears the rows past the end of a partial chunk itself, and
-the small parity problems never reach it. These cases do: a dense batch whose length is not a
-multiple of the chunk, and a packed batch with a one-token sequence and ragged tails, in plain
-and gated EFLA, forward (saving) and backward, against the fp64 oracle on sampled streams
-(streams are independent, so the oracle is exact for each of them).
+the small parity problems never reach it. These cases do, for d_k = 128 and d_k = 64: a dense
+batch whose length is not a multiple of the chunk, and a packed batch with a one-token sequence
+and ragged tails, in plain and gated EFLA, forward (saving) and backward, with every
+(sequence, head) stream compared against the fp64 oracle (streams are independent, so the
+oracle is exact for each of them).
 """
 import numpy as np
 import pytest
 import torch
 
-from oracle import efla_oracle as O
+from oracle_streams import assert_streams, compare_streams
 from workloads import make_inputs, workload
 
 pytestmark = pytest.mark.gpu
@@ -21,6 +22,8 @@ TOL = 2e-2  # bf16, normwise per tensor and stream, as in the other parity tests
 CASES = [
     ("dense_T150", 2, dict(B=4, H=16, T=150), None),
     ("packed", 5, dict(H=16), [150, 64, 1, 100, 300]),
+    ("dense_T150_dk64", 2, dict(B=4, H=16, T=150, dk=64), None),
+    ("packed_dk64", 5, dict(H=16, dk=64), [150, 64, 1, 100, 300]),
 ]
 
 
@@ -34,15 +37,6 @@ def E():
 
 def _dev(x, dt=torch.bfloat16):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dt)
-
-
-def _streams(inp, rng):
-    """(b, h, start, end): every sequence of a packed batch once, or four dense streams."""
-    B, H, T, _ = inp["k"].shape
-    cu = inp["cu_seqlens"]
-    if cu is None:
-        return [(int(rng.integers(B)), int(rng.integers(H)), 0, T) for _ in range(4)]
-    return [(0, int(rng.integers(H)), int(cu[s]), int(cu[s + 1])) for s in range(len(cu) - 1)]
 
 
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
@@ -69,24 +63,7 @@ def test_wide_ragged(E, name, idx, over, lengths, gated):
         grads = E.efla_bwd(q, k, v, beta, do, saved, 1.0, cu)
         names = ("dq", "dk", "dv", "dbeta")
     torch.cuda.synchronize()
-    for (b, h, s, e) in _streams(inp, np.random.default_rng(5 + idx)):
-        sl = lambda t: t[b:b + 1, h:h + 1, s:e]
-        if gated:
-            ref_o, _ = O.gated_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a))
-            ref = O.gated_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
-                                   sl(inp["do"]))
-        else:
-            ref_o, _ = O.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]))
-            ref = O.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["do"]))
-        got = o[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
-        err = O.rel_err(got, ref_o)
-        print("  stream b=%d h=%d [%d,%d): o %.3e" % (b, h, s, e, err), flush=True)
-        assert np.all(np.isfinite(got)) and err <= TOL
-        for nm, t in zip(names, grads):
-            gg = t[b:b + 1, h:h + 1, s:e].float().cpu().numpy()
-            err = O.rel_err(gg, ref[nm])
-            print("    %s %.3e" % (nm, err), flush=True)
-            assert np.all(np.isfinite(gg)) and err <= TOL, nm
-    assert torch.isfinite(o.float()).all()
-    for t in grads:
-        assert torch.isfinite(t.float()).all()
+    gpu = {"o": o.float().cpu().numpy()}
+    gpu.update({nm: t.float().cpu().numpy() for nm, t in zip(names, grads)})
+    res = compare_streams(inp, gpu, True, gate=a if gated else None)
+    assert_streams(res, TOL)
