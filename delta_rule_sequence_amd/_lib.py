@@ -20,10 +20,12 @@ STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_NULL", 2: "EFLA_ERR_SHAPE", 3: "EFLA_ERR_DT
           4: "EFLA_ERR_UNSUPPORTED", 5: "EFLA_ERR_WORKSPACE", 6: "EFLA_ERR_HIP",
           7: "EFLA_ERR_ALIGN"}
 
+NOALLOC_WS_BYTES = 64 << 20  # EFLA_NOALLOC_WS_BYTES: static workspace of efla_fwd_noalloc
+
 # Every symbol include/efla.h declares.
 EXPORTS = ["efla_abi_version", "efla_status_str", "efla_check_problem", "efla_workspace_bytes",
            "efla_saved_bytes", "efla_get_saved_layout", "efla_prep", "efla_chunk_ut",
-           "efla_fwd", "efla_fwd_state", "efla_fwd_gated", "efla_bwd", "efla_bwd_state",
+           "efla_fwd", "efla_fwd_state", "efla_fwd_noalloc", "efla_fwd_gated", "efla_bwd", "efla_bwd_state",
            "efla_bwd_gated",
            "efla_decode", "efla_decode_gated",
            "efla_profile_enable", "efla_profile_read", "efla_profile_reset"]
@@ -90,6 +92,8 @@ def lib():
     L.efla_bwd_state.restype = st
     L.efla_bwd_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
                                  sz, vp]
+    L.efla_fwd_noalloc.restype = st
+    L.efla_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     L.efla_decode.restype = st
     L.efla_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.efla_fwd_gated.restype = st

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -260,6 +261,34 @@ efla_status run_forward(const Shape& s, const void* q, const void* k, const void
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Workspace of efla_fwd_noalloc: a static device array, one copy per GPU, alive until the
+// process ends. In host code `scratch` names a host-side stand-in, not device memory: kernels
+// and copies get the device address that hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)EFLA_NOALLOC_WS_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up once per device, with that device
+// current); null if the device index is out of range or the lookup fails.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
 }  // namespace efla
 
 using namespace efla;
@@ -380,6 +409,30 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
                      size_t ws_bytes, void* stream) {
   return efla_fwd_state(p, q, k, v, beta, nullptr, o, nullptr, saved, saved_bytes, ws, ws_bytes,
                         stream);
+}
+
+efla_status efla_fwd_noalloc(const efla_problem* p, const void* q, const void* k, const void* v,
+                             const void* beta, const float* h0, void* o, float* ht, void* stream) {
+  Shape s;
+  if (efla_status r = to_shape(p, s)) return r;
+  if (empty(s)) return EFLA_OK;
+  if (!q || !k || !v || !beta || !o) return EFLA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(h0) ||
+      !aligned16(ht))
+    return EFLA_ERR_ALIGN;
+  if (ws_fwd(s) > kScratchBytes) return EFLA_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return EFLA_ERR_HIP;
+  // the workspace layout of efla_fwd_state without a saved buffer; nothing in it has to start
+  // at zero (every kernel writes what a later one reads)
+  unsigned char* wsb = (unsigned char*)ws;
+  unsigned char* u = wsb;
+  unsigned char* w = wsb + align_up(bytes_v(s));
+  int* table = (int*)(w + align_up(bytes_k(s)));
+  unsigned char* m = (unsigned char*)table + align_up(bytes_table(s));
+  unsigned char* seg = m + align_up(bytes_m(s));
+  return run_forward(s, q, k, v, beta, o, w, nullptr, nullptr, table, m, nullptr, u, h0, ht, seg,
+                     (hipStream_t)stream);
 }
 
 efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, const void* v,

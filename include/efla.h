@@ -44,7 +44,10 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 7
+#define EFLA_ABI_VERSION 8
+
+/* Size of the static device workspace of efla_fwd_noalloc (per GPU): 64 MiB. */
+#define EFLA_NOALLOC_WS_BYTES (64ull << 20)
 
 typedef enum {
   EFLA_OK = 0,
@@ -160,6 +163,20 @@ efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const 
 efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
                            const void* beta, const float* h0, void* o, float* ht, void* saved,
                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same results as efla_fwd_state(p, q, k, v,
+ * beta, h0, o, ht, NULL, 0, ws, ...) with no saved buffer, but it takes no workspace: it uses a
+ * static device array of EFLA_NOALLOC_WS_BYTES inside the library, one per GPU, which each GPU
+ * holds until the process ends. Problems whose efla_workspace_bytes(p, 0) exceeds that size
+ * return EFLA_ERR_WORKSPACE before anything is enqueued (64 MiB holds, for example, 16 heads of
+ * 4,096 bf16 tokens at d_k = d_v = 128, with the library's segment plan). It allocates nothing,
+ * ever. Every call on a GPU uses that GPU's array and leaves its contents behind: calls that
+ * overlap on one GPU (different streams or host threads) race; calls on one stream are ordered.
+ * No part of the array has to start at zero. On the first call on a device the array's address is looked up
+ * (hipGetSymbolAddress); EFLA_ERR_HIP if that fails. */
+efla_status efla_fwd_noalloc(const efla_problem* p, const void* q, const void* k, const void* v,
+                             const void* beta, const float* h0, void* o, float* ht, void* stream);
 
 /* Gated EFLA forward (summary page, section 3.4 names it; the appendix applies the exact flow
  * to Gated DeltaNet; the pages print no formula, this is the reading taken): a per-token

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 7
+    assert L.efla_abi_version() == 8
 
 
 def test_status_strings(L):
@@ -227,3 +227,24 @@ def test_gated_entry_points_reject_bad_arguments(L):
     assert bwd(p, ws_=None) == 1
     assert bwd(p, ws_bytes=wb - 1) == 5
     assert bwd(p, saved=fake, saved_bytes=sb - 1) == 5
+
+def test_noalloc_entry_point_rejects_without_touching_hip(L):
+    """efla_fwd_noalloc validates everything, including the size of its static workspace,
+    before it looks up the workspace or enqueues anything."""
+    fake, odd = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008)
+    cap = _lib.NOALLOC_WS_BYTES
+
+    def call(prob, q=fake, h0=None, o=fake, ht=None):
+        return L.efla_fwd_noalloc(ctypes.byref(prob), q, fake, fake, fake, h0, o, ht, None)
+    big = _p(B=1, H=16, T=8192)
+    assert L.efla_workspace_bytes(ctypes.byref(big), 0) > cap
+    assert call(big) == 5
+    fits = _p(B=1, H=16, T=4096)      # the header's example: 16 heads of 4,096 bf16 tokens
+    assert L.efla_workspace_bytes(ctypes.byref(fits), 0) <= cap
+    assert call(fits, q=None) == 1
+    assert call(fits, o=None) == 1
+    assert call(fits, q=odd) == 7
+    assert call(fits, h0=odd) == 7
+    assert call(fits, ht=odd) == 7
+    assert call(_p(B=1, H=16, T=4096, dk=96)) == 4
+    assert L.efla_fwd_noalloc(ctypes.byref(_p(T=0)), None, None, None, None, None, None, None, None) == 0
