@@ -187,7 +187,7 @@ size_t bytes_cum(const Shape& s) { return (size_t)s.slots * s.H * kChunk * 4; }
 
 // Layout of the forward->backward buffer.
 struct Saved {
-  size_t w, ut, states, table, m, x, cum, total;
+  size_t w, ut, states, table, m, x, cum, segp, total;
 };
 Saved saved_layout(const Shape& s) {
   Saved L;
@@ -206,6 +206,8 @@ Saved saved_layout(const Shape& s) {
   o += align_up(bytes_x(s));
   L.cum = o;
   o += align_up(bytes_cum(s));
+  L.segp = o;
+  o += align_up(bytes_seg_p(s));
   L.total = o;
   return L;
 }
@@ -216,11 +218,14 @@ size_t ws_fwd(const Shape& s) {
   return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s)) +
          align_up(bytes_m(s)) + bytes_seg(s) + align_up(bytes_cum(s));
 }
-// Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer, U and
-// the segment buffers for the recompute path.
+// Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer and U for
+// the recompute path, plus two segment state buffers (R and the states entering the segments of
+// the recomputed forward, then R and the gradients entering the segments of the backward; the
+// transitions live in the saved buffer).
+size_t bytes_seg_bwd(const Shape& s) { return 2 * align_up(bytes_seg_state(s)); }
 size_t ws_bwd(const Shape& s) {
   return align_up(bytes_v(s)) + align_up(bytes_states(s)) + saved_layout(s).total +
-         align_up(bytes_v(s)) + bytes_seg(s);
+         align_up(bytes_v(s)) + bytes_seg_bwd(s);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -232,11 +237,14 @@ bool empty(const Shape& s) { return s.T == 0; }
 // Forward stages shared by efla_fwd and the recompute path of efla_bwd. seg: bytes_seg(s)
 // of workspace for the segment-parallel scan (unused when the plan has one segment).
 // gate (null, or log-decays) selects gated EFLA, which then needs cum (bytes_cum(s)).
+// segp (null, or the saved buffer's region) receives the segments' transitions P for the
+// backward; without it they stay in the workspace.
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                         const void* beta, void* o, unsigned char* w, unsigned char* ut,
                         unsigned char* states, int* table, unsigned char* m, unsigned char* x,
                         unsigned char* u, const float* h0, float* ht, unsigned char* seg,
-                        hipStream_t st, const void* gate = nullptr, float* cum = nullptr) {
+                        hipStream_t st, const void* gate = nullptr, float* cum = nullptr,
+                        float* segp = nullptr) {
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
@@ -251,11 +259,8 @@ efla_status run_forward(const Shape& s, const void* q, const void* k, const void
   const Shape sv = segment_view(s);
   float* R = (float*)seg;
   float* S_in = (float*)(seg + align_up(bytes_seg_state(s)));
-  float* P = (float*)(seg + 2 * align_up(bytes_seg_state(s)));
-  if (efla_status r = hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, nullptr, nullptr,
-                                                 nullptr, nullptr, R, st, cm)))
-    return r;
-  if (efla_status r = hip_status(launch_scan_fwd_transition(sv, k, w, P, st, cm))) return r;
+  float* P = segp ? segp : (float*)(seg + 2 * align_up(bytes_seg_state(s)));
+  if (efla_status r = hip_status(launch_scan_fwd_pair(sv, k, w, u, R, P, st, cm))) return r;
   if (efla_status r = hip_status(launch_seg_combine(s, P, R, h0, S_in, ht, st))) return r;
   return hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, o, ut, states, S_in, nullptr, st, cm));
 }
@@ -340,6 +345,7 @@ efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out)
   out->m = L.m;
   out->x = L.x;
   out->cum = L.cum;
+  out->segp = L.segp;
   out->total = L.total;
   out->n_chunk_slots = s.slots;
   return EFLA_OK;
@@ -401,7 +407,7 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
   unsigned char* m = sv ? sv + L.m : m_ws;
   unsigned char* x = sv ? sv + L.x : nullptr;
   return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, h0, ht, seg_ws,
-                     (hipStream_t)stream);
+                     (hipStream_t)stream, nullptr, nullptr, sv ? (float*)(sv + L.segp) : nullptr);
 }
 
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -461,7 +467,8 @@ efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, 
   return run_forward(s, q, k, v, beta, o, sv ? sv + L.w : w_ws, sv ? sv + L.ut : nullptr,
                      sv ? sv + L.states : nullptr, sv ? (int*)(sv + L.table) : table_ws,
                      sv ? sv + L.m : m_ws, sv ? sv + L.x : nullptr, u, h0, ht, seg_ws,
-                     (hipStream_t)stream, gate, sv ? (float*)(sv + L.cum) : cum_ws);
+                     (hipStream_t)stream, gate, sv ? (float*)(sv + L.cum) : cum_ws,
+                     sv ? (float*)(sv + L.segp) : nullptr);
 }
 
 }  // extern "C"
@@ -485,7 +492,7 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
       !aligned16(dht) || !aligned16(dh0))
     return EFLA_ERR_ALIGN;
   const Saved L = saved_layout(s);
-  const size_t seg_bytes = s.seg_plan > 1 ? bytes_seg(s) : 0;
+  const size_t seg_bytes = s.seg_plan > 1 ? bytes_seg_bwd(s) : 0;
   const size_t need =
       saved ? align_up(bytes_v(s)) + align_up(bytes_states(s)) + seg_bytes : ws_bwd(s);
   if (ws_bytes < need) return EFLA_ERR_WORKSPACE;
@@ -503,26 +510,27 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
     seg = u + align_up(bytes_v(s));
     if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
                                     rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
-                                    u, h0, nullptr, seg, st, gate, (float*)(rec + L.cum)))
+                                    u, h0, nullptr, seg, st, gate, (float*)(rec + L.cum),
+                                    (float*)(rec + L.segp)))
       return r;
     sv = rec;
   }
   const int* table = (const int*)(sv + L.table);
   const float* cum = gate ? (const float*)(sv + L.cum) : nullptr;
   if (s.seg_plan > 1) {
-    // Segment-parallel reverse scan: zero-start gradients R and transitions A of all segments,
-    // the chain over segments from the last (dht) to the first (dh0), then the full scan over
-    // all segments from the gradient entering each from its end.
+    // Segment-parallel reverse scan: zero-start gradients R of all segments, the chain over
+    // segments from the last (dht) to the first (dh0) with the transposed forward transitions
+    // (a segment maps the state gradient by P^T), then the full scan over all segments from the
+    // gradient entering each from its end.
     const Shape svw = segment_view(s);
     float* R = (float*)seg;
     float* G_in = (float*)(seg + align_up(bytes_seg_state(s)));
-    float* A = (float*)(seg + 2 * align_up(bytes_seg_state(s)));
+    const float* A = (const float*)(sv + L.segp);
     if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, sv + L.w, sv + L.m, d_o,
                                                    nullptr, nullptr, nullptr, R, st, cum, true)))
       return r;
-    if (efla_status r = hip_status(launch_scan_bwd_transition(svw, table, k, sv + L.w, A, st, cum)))
+    if (efla_status r = hip_status(launch_seg_combine(s, A, R, dht, G_in, dh0, st, true, true)))
       return r;
-    if (efla_status r = hip_status(launch_seg_combine(s, A, R, dht, G_in, dh0, st, true))) return r;
     if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, sv + L.w, sv + L.m, d_o, dut,
                                                    dstates, G_in, nullptr, st, cum)))
       return r;

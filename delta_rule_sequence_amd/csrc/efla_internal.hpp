@@ -48,29 +48,27 @@ hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, cons
                            const void* w, const void* u, const void* m, void* o, void* ut,
                            void* states, const float* h0, float* ht, hipStream_t st,
                            const float* cum = nullptr);
-// Transition of each sequence of a segment view: P = prod over its chunks of
-// (I - K^T W), as fp32 [n_seqs][H][dk][dk] (the scan with U = 0 from S = I).
-hipError_t launch_scan_fwd_transition(const Shape& s, const void* k, const void* w, float* p,
-                                      hipStream_t st, const float* cum = nullptr);
+// For a segment view, in one launch: the zero-start state scan (final states into r, fp32
+// [n_seqs][H][dk][dv]) and the transition scan, the product over each sequence's chunks of
+// (I - K^T W) (gated: with the decays) into p, fp32 [n_seqs][H][dk][dk] (the scan with U = 0 from
+// S = I).
+hipError_t launch_scan_fwd_pair(const Shape& s, const void* k, const void* w, const void* u,
+                                float* r, float* p, hipStream_t st, const float* cum = nullptr);
 // Chain the segments of every sequence: S_0 = h0 (zero if null), S_{j+1} = P_j S_j + R_j;
 // writes S_j of every segment to sin ([B * seg_plan][H][dk][dv]) and the final state to ht
 // (if not null). P, R as produced by the transition and state-only scans of segment_view(s).
 // reverse walks the segments from the last to the first (backward: state gradients), so
-// sin[j] is the value entering segment j from its end.
+// sin[j] is the value entering segment j from its end; transpose applies P_j^T (the backward
+// chains the state gradients with the forward's transitions, transposed).
 hipError_t launch_seg_combine(const Shape& s, const float* p, const float* r, const float* h0,
-                              float* sin, float* ht, hipStream_t st, bool reverse = false);
+                              float* sin, float* ht, hipStream_t st, bool reverse = false,
+                              bool transpose = false);
 // cum (null, or the saved running log-decay sums) selects gated EFLA. state_only: neither dU~
 // nor the per-chunk gradients are written, only dh0 (first pass of the segment-parallel scan).
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
                            void* dstates, const float* dht, float* dh0, hipStream_t st,
                            const float* cum = nullptr, bool state_only = false);
-// Transition of each sequence of a segment view for the backward scan: the product over its
-// chunks of (I - W^T K) (gated: with the decays) as fp32 [n_seqs][H][dk][dk], the scan with
-// dO = 0 from G = I.
-hipError_t launch_scan_bwd_transition(const Shape& s, const int* table, const void* k,
-                                      const void* w, float* p, hipStream_t st,
-                                      const float* cum = nullptr);
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
                          const void* beta, float* state, void* o, hipStream_t st,
                          const void* gate = nullptr);

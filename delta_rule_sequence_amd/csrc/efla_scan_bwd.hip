@@ -24,10 +24,10 @@
 //
 // Segment-parallel backward (long sequences, few sequence-head pairs). The chunk step is affine
 // in the state gradient, G <- (I - W^T K) G + scale (Q - M W)^T dO (gated: with the decays), so
-// a segment of chunks maps the gradient leaving it to the one entering it as A G + R. MODE 1
-// (state only) runs from zero and keeps only the result, R; MODE 2 (transition) runs with dO
-// taken as zero from G = I (d_v = d_k), giving A. MODE 0 is the full scan that writes dU~ and
-// the per-chunk gradients.
+// a segment of chunks maps the gradient leaving it to the one entering it as A G + R, where A is
+// the transpose of the forward's segment transition (kept from the forward). MODE 1 (state only)
+// runs from zero and keeps only the result, R. MODE 0 is the full scan that writes dU~ and the
+// per-chunk gradients.
 #include "efla_internal.hpp"
 
 namespace efla {
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   const int rA = 16 * wv;
   const int64_t base = (int64_t)(si.b * g.H + h) * g.T + si.bos;
 
-  constexpr bool OUT = MODE == 0, TR = MODE == 2;  // write dU~ and dS_c; transition
+  constexpr bool OUT = MODE == 0;  // write dU~ and dS_c
   V kA[KS], kN[KS];
   u32x4 qR[VQ], wR[VQ], mR[VM], oR[VO];
   float cQ[VQ], cR = 0.f;  // gated: running log-decay sums of the Q rows / of token lane
@@ -99,12 +99,12 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
-      if constexpr (!TR) qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
+      qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
       wR[it] = *(const u32x4*)(w + (r0 + r) * DK + cc);
-      if constexpr (GT && !TR) cQ[it] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + r];
+      if constexpr (GT) cQ[it] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + r];
     }
     if constexpr (GT) cR = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
-    if constexpr (!TR) {  // M and dO only enter through the dO term
+    {  // M and dO (the dO term)
       const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
 #pragma unroll
       for (int it = 0; it < VM; ++it) mR[it] = *(const u32x4*)(mc + (it * kThreads + tid) * VE);
@@ -130,7 +130,6 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
       const int i = it * kThreads + tid;
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
       *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
-      if constexpr (TR) continue;
       u32x4 qv = qR[it];
       if constexpr (GT) {  // Q rows scaled by Gamma = e^c
         const float gm = exp_decay(cQ[it]);
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     if constexpr (GT) {
       if (tid < 64) ((float*)(st + L::oCs))[tid] = cR;
     }
-    if constexpr (!TR) {
+    {
 #pragma unroll
       for (int it = 0; it < VM; ++it) {
         const int i = (it * kThreads + tid) * VE;
@@ -172,12 +171,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     Gt[i] = zero4();
-    if constexpr (TR) {  // G = I (d_v = d_k): this slice's columns
-      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Gt[i][e] = 16 * db + (lane & 15) == v0 + 16 * vb + 4 * (lane >> 4) + e ? 1.f : 0.f;
-    } else if (dht) {
+    if (dht) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
     }
@@ -198,7 +192,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     const int bk = n * DK * (int)sizeof(E);
     l2_touch<NL, kThreads>(pw, w + r0 * DK, bk, tile, NTILE, tid);
     l2_touch<NL, kThreads>(pw + NL, k + r0 * DK, bk, tile, NTILE, tid);
-    if constexpr (!TR) {
+    {
       l2_touch<NL, kThreads>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, tid);
       l2_touch<NL, kThreads>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                              kChunk * kChunk * (int)sizeof(E), tile, NTILE, tid);
@@ -250,7 +244,6 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * L::LS + 16 * nb, L::LS, lane), kg);
-      if constexpr (!TR)
         md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
       if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
         const float cl = sCs[n - 1];
@@ -269,8 +262,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
-      const f32x4 a =
-          TR ? zero4() : mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
+      const f32x4 a = mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
       const f32x4 b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
       Gt[i] = gC * Gt[i] + (g.scale * a - b);
     }
@@ -332,7 +324,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   constexpr int NB = TV / 16;
   constexpr int TPW = (DK / 16) * NB / 4;
   constexpr int VE = 16 / (int)sizeof(E);
-  constexpr bool OUT = MODE == 0, TR = MODE == 2;  // write dU~ and dS_c; transition
+  constexpr bool OUT = MODE == 0;  // write dU~ and dS_c
   static_assert(TPW >= 1 && ((DK / 16) * NB) % 4 == 0, "state tiles must split over 4 waves");
   static_assert(L::bytes <= 160 * 1024, "LDS budget");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -353,7 +345,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   auto tiles = [&](int c) { return smem + (c & 1) * L::stage; };
 
   constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * 64 - 1) / (NTILE * 64);
-  constexpr int NWARM = NL * (TR ? 2 : 5);  // warm-up loads issued after each DMA: W, K (, Q, M, dO)
+  constexpr int NWARM = NL * 5;  // warm-up loads issued after each DMA: W, K, Q, M, dO
   static_assert(NWARM <= 15, "vmcnt field");
   if (wv == 4) {  // ---- loader wave
     float cumv = 0.f;  // gated: the chunk's running log-decay sum of token lane, on its way to LDS
@@ -366,7 +358,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       const int bk = n * DK * (int)sizeof(E);
       l2_touch<NL>(pw, w + r0 * DK, bk, tile, NTILE, lane);
       l2_touch<NL>(pw + NL, k + r0 * DK, bk, tile, NTILE, lane);
-      if constexpr (!TR) {
+      {
         l2_touch<NL>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, lane);
         l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                      kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
@@ -381,7 +373,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       const int64_t r0 = base + (int64_t)c * kChunk;
       dma_tile<E, DK, 1>(st + L::oK, k + r0 * DK, DK, n, 0, lane);
       dma_tile<E, DK, 1>(st + L::oW, w + r0 * DK, DK, n, 0, lane);
-      if constexpr (!TR) {  // Q, M and dO only enter through the dO term
+      {  // Q, M and dO (the dO term)
         dma_tile<E, DK, 1>(st + L::oQ, q + r0 * DK, DK, n, 0, lane);
         dma_tile<E, 64, 1>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                            kChunk, kChunk, 0, lane);
@@ -403,9 +395,8 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       for (int b = n * L::SK::RB + 16 * lane; b < kChunk * L::SK::RB; b += 16 * 64) {
         *(u32x4*)(st + L::oK + b) = z;
         *(u32x4*)(st + L::oW + b) = z;
-        if constexpr (!TR) *(u32x4*)(st + L::oQ + b) = z;
+        *(u32x4*)(st + L::oQ + b) = z;
       }
-      if constexpr (!TR)
         for (int b = n * L::SO::RB + 16 * lane; b < kChunk * L::SO::RB; b += 16 * 64)
           *(u32x4*)(st + L::oO + b) = z;
     };
@@ -460,12 +451,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     Gt[i] = zero4();
-    if constexpr (TR) {  // G = I (d_v = d_k): this slice's columns
-      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Gt[i][e] = 16 * db + (lane & 15) == v0 + 16 * vb + 4 * (lane >> 4) + e ? 1.f : 0.f;
-    } else if (dht) {
+    if (dht) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) Gt[i][e] = dht[goff(i, e)];
     }
@@ -493,7 +479,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * LS + 16 * nb, LS, lane), kg);
-      if constexpr (!TR) {  // M^T[t][s] = M[s][t]: k-major from M's rows s >= t
+      {  // M^T[t][s] = M[s][t]: k-major from M's rows s >= t
         for (int k0 = round_down_kc<E>(rA); k0 < kChunk; k0 += KC)
           md = Mma<E>::step(frag_km_sw<E, 64>(st + L::oM, k0, rA, lane),
                             frag_km_sw<E, TV>(st + L::oO, k0, 16 * nb, lane), md);
@@ -517,7 +503,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       f32x4 a = zero4(), b = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < kChunk; k0 += KC) {
-        if constexpr (!TR) {
+        {
           V qf = frag_km_sw<E, DK>(st + L::oQ, k0, 16 * db, lane);
           if constexpr (GT) {  // element e is token k0 + KC/4 (lane >> 4) + e
             const int t0 = k0 + (KC / 4) * (lane >> 4);
@@ -560,8 +546,8 @@ static hipError_t scan_bwd_dma_run(const Shape& s, const int* table, const void*
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
                      (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
   hipError_t e = hipGetLastError();
-  static const char* const names[2][3] = {{"scan_bwd", "scan_bwd_state", "scan_bwd_transition"},
-                                           {"scan_bwd_gated", "scan_bwd_state_gated", "scan_bwd_transition_gated"}};
+  static const char* const names[2][2] = {{"scan_bwd", "scan_bwd_state"},
+                                           {"scan_bwd_gated", "scan_bwd_state_gated"}};
   prof_end(names[GT][MODE], st);
   return e;
 }
@@ -586,8 +572,8 @@ static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, 
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
                      (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
   hipError_t e = hipGetLastError();
-  static const char* const names[2][3] = {{"scan_bwd", "scan_bwd_state", "scan_bwd_transition"},
-                                           {"scan_bwd_gated", "scan_bwd_state_gated", "scan_bwd_transition_gated"}};
+  static const char* const names[2][2] = {{"scan_bwd", "scan_bwd_state"},
+                                           {"scan_bwd_gated", "scan_bwd_state_gated"}};
   prof_end(names[GT][MODE], st);
   return e;
 }
@@ -656,22 +642,3 @@ hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, cons
 
 }  // namespace efla
 
-namespace efla {
-
-hipError_t launch_scan_bwd_transition(const Shape& s, const int* table, const void* k,
-                                      const void* w, float* p, hipStream_t st, const float* cum) {
-  Shape t = s;
-  t.dv = s.dk;  // the map acts on d_k x d_k
-#define EFLA_ST(E_, DK_, TV_)                                                                    \
-  return scan_bwd_mode<E_, DK_, DK_, TV_, 2>(t, table, nullptr, k, w, nullptr, nullptr, nullptr, \
-                                             nullptr, nullptr, p, st, cum)
-  if (s.dt == Dt::BF16) {
-    if (s.dk == 64) EFLA_ST(__bf16, 64, 16);
-    if (scan_tile(t) == 16) EFLA_ST(__bf16, 128, 16);
-    EFLA_ST(__bf16, 128, 32);
-  }
-  EFLA_ST(float, 64, 16);
-#undef EFLA_ST
-}
-
-}  // namespace efla

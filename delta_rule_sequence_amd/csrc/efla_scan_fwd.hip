@@ -21,23 +21,26 @@
 
 namespace efla {
 
-template <typename E, int DK, int DV, int NWC, bool GT = false>
+// WO: O is written (Q and M are staged); WSV: U~ and the chunk states are written. The
+// output-free modes (the zero-start and transition scans of the segment-parallel forward) stage
+// only W, K and U, so two of their workgroups fit on a compute unit.
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool GT = false>
 struct ScanFwdLds {
   static constexpr int TV = 16 * NWC;
   static constexpr int NWL = 1;  // loader waves (one; a second wave stores the outputs)
   typedef Swz<E, DK> SK;
   typedef Swz<E, 64> SM;
   typedef Swz<E, TV, 2> SU;  // read in accumulator layout
-  static constexpr size_t oW = 0;                       // W  [64][DK]
-  static constexpr size_t oQ = oW + SK::BYTES;          // Q  [64][DK]
-  static constexpr size_t oK = oQ + SK::BYTES;          // K  [64][DK]
-  static constexpr size_t oM = oK + SK::BYTES;          // M  [64][64]
-  static constexpr size_t oU = oM + SM::BYTES;          // U  [64][TV] (this tile's columns)
-  static constexpr size_t oC = oU + SU::BYTES;         // running log-decay sums [64] (gated)
+  static constexpr size_t oW = 0;                              // W  [64][DK]
+  static constexpr size_t oK = oW + SK::BYTES;                 // K  [64][DK]
+  static constexpr size_t oU = oK + SK::BYTES;                 // U  [64][TV] (this tile's columns)
+  static constexpr size_t oQ = oU + SU::BYTES;                 // Q  [64][DK] (WO)
+  static constexpr size_t oM = oQ + (WO ? SK::BYTES : 0);      // M  [64][64] (WO)
+  static constexpr size_t oC = oM + (WO ? SM::BYTES : 0);      // running log-decay sums [64] (gated)
   static constexpr size_t stage = oC + (GT ? 64 * 4 : 0);
-  // output staging (layout SU): O [64][TV], U~ [64][TV], S [DK][TV]; two buffers
-  static constexpr size_t gO = 0, gUt = SU::BYTES, gS = 2 * SU::BYTES;
-  static constexpr size_t sstage = gS + (size_t)DK * SU::RB;
+  // output staging (layout SU): O [64][TV] (WO), U~ [64][TV] and S [DK][TV] (WSV); two buffers
+  static constexpr size_t gO = 0, gUt = WO ? SU::BYTES : 0, gS = gUt + (WSV ? SU::BYTES : 0);
+  static constexpr size_t sstage = gS + (WSV ? (size_t)DK * SU::RB : 0);
   static constexpr size_t oStg = 2 * stage;
   static constexpr size_t bytes = oStg + 2 * sstage;
 };
@@ -50,13 +53,14 @@ struct ScanFwdLds {
 // PM: transition mode for the segment-parallel scan. The chunk step is affine in the state,
 // S <- (I - K^T W) S + K^T U, so running it with U = 0 from S = I (DV = DK) leaves in ht the
 // product of the (I - K^T W) over the sequence; U is neither read nor needed.
+// The scan of one workgroup; bid plays the role of the block index.
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
-__global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
-    Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
+__device__ __forceinline__ void scan_fwd_body(
+    int bid, Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
     E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
     const float* __restrict__ cum) {
-  typedef ScanFwdLds<E, DK, DV, NWC, GT> L;
+  typedef ScanFwdLds<E, DK, DV, NWC, WO, WSV, GT> L;
   typedef typename L::SU SU;
   typedef typename Mma<E>::vec V;
   constexpr int TV = L::TV, NWL = L::NWL, NTILE = DV / TV, KC = Mma<E>::KC;
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool loader = wi == NWC, storer = wi == NWC + 1;
   int sh, tile;
-  scan_block(blockIdx.x, g.n_seqs * g.H, NTILE, sh, tile);
+  scan_block(bid, g.n_seqs * g.H, NTILE, sh, tile);
   const int s = sh / g.H, h = sh % g.H;
   const SeqInfo si = seq_info(g, s);
   const int nchunks = seq_chunks(g, si);
@@ -355,12 +359,62 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
   }
 }
 
+template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
+__global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
+    Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
+    const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
+    E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
+    const float* __restrict__ cum) {
+  scan_fwd_body<E, DK, DV, NWC, WO, WSV, PM, GT>(blockIdx.x, g, q, k, w, u, m, o, ut, states, h0, ht, cum);
+}
+
+// The two independent first passes of the segment-parallel forward in one launch: blocks
+// [0, nr) run the zero-start state scan of every segment (R, d_k x d_v per segment), the rest
+// the transition scan (P, d_k x d_k). Both use the output-free LDS layout, so two workgroups
+// share a compute unit and the passes overlap instead of running one after the other.
+template <typename E, int DK, int DV, int NWC, bool GT>
+__global__ __launch_bounds__(64 * NWC + 128, 2) void scan_fwd_pair_kernel(
+    Geom g, int nr, const E* __restrict__ k, const E* __restrict__ w, const E* __restrict__ u,
+    float* __restrict__ R, float* __restrict__ P, const float* __restrict__ cum) {
+  if ((int)blockIdx.x < nr)
+    scan_fwd_body<E, DK, DV, NWC, false, false, false, GT>(blockIdx.x, g, nullptr, k, w, u, nullptr, nullptr,
+                                                          nullptr, nullptr, nullptr, R, cum);
+  else
+    scan_fwd_body<E, DK, DK, NWC, false, false, true, GT>(blockIdx.x - nr, g, nullptr, k, w, nullptr, nullptr,
+                                                         nullptr, nullptr, nullptr, nullptr, P, cum);
+}
+
+template <typename E, int DK, int DV, int NWC, bool GT>
+static hipError_t scan_fwd_pair_run(const Shape& s, const void* k, const void* w, const void* u,
+                                    float* R, float* P, hipStream_t st, const float* cum) {
+  typedef ScanFwdLds<E, DK, DV, NWC, false, false, GT> LR;
+  typedef ScanFwdLds<E, DK, DK, NWC, false, false, GT> LP;
+  constexpr size_t bytes = LR::bytes > LP::bytes ? LR::bytes : LP::bytes;
+  static_assert(2 * bytes <= 160 * 1024, "two workgroups per compute unit");
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_pair_kernel<E, DK, DV, NWC, GT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t nr = (int64_t)s.n_seqs * s.H * (DV / LR::TV), np = (int64_t)s.n_seqs * s.H * (DK / LP::TV);
+  if (nr + np < 1) return hipSuccess;
+  prof_begin(st);
+  hipLaunchKernelGGL((scan_fwd_pair_kernel<E, DK, DV, NWC, GT>), dim3((unsigned)(nr + np)),
+                     dim3(64 * NWC + 128), bytes, st, make_geom(s, nullptr), (int)nr, (const E*)k,
+                     (const E*)w, (const E*)u, R, P, cum);
+  hipError_t e = hipGetLastError();
+  prof_end(GT ? "scan_fwd_state_transition_gated" : "scan_fwd_state_transition", st);
+  return e;
+}
+
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM = false, bool GT = false>
 static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* u, const void* m, void* o, void* ut,
                                void* states, const float* h0, float* ht, hipStream_t st,
                                const float* cum = nullptr) {
-  typedef ScanFwdLds<E, DK, DV, NWC, GT> L;
+  typedef ScanFwdLds<E, DK, DV, NWC, WO, WSV, GT> L;
   static_assert(L::bytes <= 160 * 1024, "LDS budget");
   static bool attr = false;
   if (!attr) {
@@ -419,13 +473,13 @@ static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, c
 // one compute wave (the double-buffered fp32 tiles leave LDS room for 16 columns of staging).
 size_t lds_scan_fwd(Dt dt, int dk, int dv) {
   if (dt == Dt::BF16) {
-    if (dk == 64 && dv == 64) return ScanFwdLds<__bf16, 64, 64, 2>::bytes;
-    if (dk == 64 && dv == 128) return ScanFwdLds<__bf16, 64, 128, 2>::bytes;
-    if (dk == 128 && dv == 64) return ScanFwdLds<__bf16, 128, 64, 2>::bytes;
-    if (dk == 128 && dv == 128) return ScanFwdLds<__bf16, 128, 128, 2>::bytes;
+    if (dk == 64 && dv == 64) return ScanFwdLds<__bf16, 64, 64, 2, true, true>::bytes;
+    if (dk == 64 && dv == 128) return ScanFwdLds<__bf16, 64, 128, 2, true, true>::bytes;
+    if (dk == 128 && dv == 64) return ScanFwdLds<__bf16, 128, 64, 2, true, true>::bytes;
+    if (dk == 128 && dv == 128) return ScanFwdLds<__bf16, 128, 128, 2, true, true>::bytes;
     return 0;
   }
-  if (dk == 64 && dv == 64) return ScanFwdLds<float, 64, 64, 1>::bytes;
+  if (dk == 64 && dv == 64) return ScanFwdLds<float, 64, 64, 1, true, true>::bytes;
   return 0;
 }
 
@@ -445,26 +499,25 @@ hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, cons
 #undef EFLA_SF
 }
 
-hipError_t launch_scan_fwd_transition(const Shape& s, const void* k, const void* w, float* p,
-                                      hipStream_t st, const float* cum) {
-#define EFLA_ST(E_, DK_, NWC_)                                                               \
-  return scan_fwd_run<E_, DK_, DK_, NWC_, false, false, true>(s, nullptr, nullptr, k, w, nullptr, \
-                                                             nullptr, nullptr, nullptr, nullptr, \
-                                                             nullptr, p, st)
-  if (cum) {
-    if (s.dt != Dt::BF16) return hipErrorInvalidValue;
-    if (s.dk == 64)
-      return scan_fwd_run<__bf16, 64, 64, 2, false, false, true, true>(s, nullptr, nullptr, k, w, nullptr, nullptr,
-                                                                      nullptr, nullptr, nullptr, nullptr, p, st, cum);
-    return scan_fwd_run<__bf16, 128, 128, 2, false, false, true, true>(s, nullptr, nullptr, k, w, nullptr, nullptr,
-                                                                      nullptr, nullptr, nullptr, nullptr, p, st, cum);
-  }
+hipError_t launch_scan_fwd_pair(const Shape& s, const void* k, const void* w, const void* u,
+                                float* r, float* p, hipStream_t st, const float* cum) {
+#define EFLA_SP(E_, DK_, DV_, NWC_, GT_) \
+  return scan_fwd_pair_run<E_, DK_, DV_, NWC_, GT_>(s, k, w, u, r, p, st, cum)
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64) EFLA_ST(__bf16, 64, 2);
-    EFLA_ST(__bf16, 128, 2);
+    if (cum) {
+      if (s.dk == 64 && s.dv == 64) EFLA_SP(__bf16, 64, 64, 2, true);
+      if (s.dk == 64 && s.dv == 128) EFLA_SP(__bf16, 64, 128, 2, true);
+      if (s.dk == 128 && s.dv == 64) EFLA_SP(__bf16, 128, 64, 2, true);
+      EFLA_SP(__bf16, 128, 128, 2, true);
+    }
+    if (s.dk == 64 && s.dv == 64) EFLA_SP(__bf16, 64, 64, 2, false);
+    if (s.dk == 64 && s.dv == 128) EFLA_SP(__bf16, 64, 128, 2, false);
+    if (s.dk == 128 && s.dv == 64) EFLA_SP(__bf16, 128, 64, 2, false);
+    EFLA_SP(__bf16, 128, 128, 2, false);
   }
-  EFLA_ST(float, 64, 1);
-#undef EFLA_ST
+  if (cum) return hipErrorInvalidValue;  // gated EFLA is built for bf16 only
+  EFLA_SP(float, 64, 64, 1, false);
+#undef EFLA_SP
 }
 
 }  // namespace efla

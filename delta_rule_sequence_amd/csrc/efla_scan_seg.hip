@@ -28,9 +28,14 @@ struct SegLds {
   static constexpr size_t bytes = 2 * TILE;          // double-buffered
 };
 
+// rev: walk the segments from the last to the first (state gradients). tr: apply P_j^T instead of
+// P_j. Going backwards a segment maps the gradient by the product of the (I - W^T K) of its
+// chunks in forward order, which is the transpose of the forward transition (the product of the
+// (I - K^T W) in reverse order; with decays both carry e^{c_last} I in place of I), so the
+// backward chains with the forward's P.
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
-    int H, int G, int rev, const float* __restrict__ P, const float* __restrict__ R,
+    int H, int G, int rev, int tr, const float* __restrict__ P, const float* __restrict__ R,
     const float* __restrict__ h0, float* __restrict__ sin, float* __restrict__ ht) {
   typedef SegLds<E, DK> L;
   typedef typename L::SP SP;
@@ -51,6 +56,18 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
   auto stage = [&](int j) {  // P of step j (fp32) -> LDS buffer j & 1 in the problem dtype
     unsigned char* dst = smem + (j & 1) * L::TILE;
     const float* Pj = P + (((int64_t)b * G + seg(j)) * H + h) * DK * DK;
+    if (tr) {  // tile element (r, c) = P_j[c][r]: rows of P_j read whole, written as columns
+      for (int i = tid; i < DK * DK / VE; i += NT) {
+        const int rr = i / (DK / VE), cc = (i % (DK / VE)) * VE;
+        const f32x4 x0 = *(const f32x4*)(Pj + (int64_t)rr * DK + cc);
+        f32x4 x1 = zero4();
+        if constexpr (VE == 8) x1 = *(const f32x4*)(Pj + (int64_t)rr * DK + cc + 4);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          *(E*)(dst + SP::off(cc + e, rr)) = to_e<E>(e < 4 ? x0[e & 3] : x1[e & 3]);
+      }
+      return;
+    }
     for (int i = tid; i < DK * DK / VE; i += NT) {
       const int r = i / (DK / VE), c = (i % (DK / VE)) * VE;
       if constexpr (sizeof(E) == 2) {
@@ -118,7 +135,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
 
 template <typename E, int DK, int DV>
 static hipError_t seg_combine_go(const Shape& s, const float* p, const float* r, const float* h0,
-                                 float* sin, float* ht, hipStream_t st, bool rev) {
+                                 float* sin, float* ht, hipStream_t st, bool rev, bool tr) {
   typedef SegLds<E, DK> L;
   static bool attr = false;
   if (!attr) {
@@ -131,21 +148,21 @@ static hipError_t seg_combine_go(const Shape& s, const float* p, const float* r,
   if (blocks < 1) return hipSuccess;
   prof_begin(st);
   hipLaunchKernelGGL((seg_combine_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(64 * (DV / 16)),
-                     L::bytes, st, s.H, s.seg_plan, rev ? 1 : 0, p, r, h0, sin, ht);
+                     L::bytes, st, s.H, s.seg_plan, rev ? 1 : 0, tr ? 1 : 0, p, r, h0, sin, ht);
   hipError_t e = hipGetLastError();
   prof_end("seg_combine", st);
   return e;
 }
 
 hipError_t launch_seg_combine(const Shape& s, const float* p, const float* r, const float* h0,
-                              float* sin, float* ht, hipStream_t st, bool rev) {
+                              float* sin, float* ht, hipStream_t st, bool rev, bool tr) {
   if (s.dt == Dt::BF16) {
-    if (s.dk == 64 && s.dv == 64) return seg_combine_go<__bf16, 64, 64>(s, p, r, h0, sin, ht, st, rev);
-    if (s.dk == 64 && s.dv == 128) return seg_combine_go<__bf16, 64, 128>(s, p, r, h0, sin, ht, st, rev);
-    if (s.dk == 128 && s.dv == 64) return seg_combine_go<__bf16, 128, 64>(s, p, r, h0, sin, ht, st, rev);
-    return seg_combine_go<__bf16, 128, 128>(s, p, r, h0, sin, ht, st, rev);
+    if (s.dk == 64 && s.dv == 64) return seg_combine_go<__bf16, 64, 64>(s, p, r, h0, sin, ht, st, rev, tr);
+    if (s.dk == 64 && s.dv == 128) return seg_combine_go<__bf16, 64, 128>(s, p, r, h0, sin, ht, st, rev, tr);
+    if (s.dk == 128 && s.dv == 64) return seg_combine_go<__bf16, 128, 64>(s, p, r, h0, sin, ht, st, rev, tr);
+    return seg_combine_go<__bf16, 128, 128>(s, p, r, h0, sin, ht, st, rev, tr);
   }
-  return seg_combine_go<float, 64, 64>(s, p, r, h0, sin, ht, st, rev);
+  return seg_combine_go<float, 64, 64>(s, p, r, h0, sin, ht, st, rev, tr);
 }
 
 }  // namespace efla

@@ -79,7 +79,7 @@ def efla_get_saved_layout(p) -> dict:
     out = _lib.EflaSavedLayout()
     _lib.check("efla_get_saved_layout", _lib.lib().efla_get_saved_layout(ctypes.byref(p), ctypes.byref(out)))
     return dict(w=out.w, ut=out.ut, states=out.states, table=out.table, m=out.m, x=out.x,
-                total=out.total, n_chunk_slots=out.n_chunk_slots)
+                cum=out.cum, segp=out.segp, total=out.total, n_chunk_slots=out.n_chunk_slots)
 
 
 def _bytes(n, device):

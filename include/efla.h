@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 8
+#define EFLA_ABI_VERSION 9
 
 /* Size of the static device workspace of efla_fwd_noalloc (per GPU): 64 MiB. */
 #define EFLA_NOALLOC_WS_BYTES (64ull << 20)
@@ -97,9 +97,12 @@ typedef struct {
  *   cum    : gated forward only: running sums of the log-decays inside each chunk,
  *            fp32 [n_chunk_slots][H][64] (then w, m and x hold the decayed factors of
  *            efla_fwd_gated)
+ *   segp   : segment-parallel plans only (empty otherwise): each segment's transition, the
+ *            product of (I - K^T W) over its chunks (gated: with the decays), fp32
+ *            [B * G][H][dk][dk]; the backward chains the state gradients with its transpose
  *   total  : size of the whole buffer = efla_saved_bytes()                               */
 typedef struct {
-  size_t w, ut, states, table, m, x, cum, total;
+  size_t w, ut, states, table, m, x, cum, segp, total;
   int64_t n_chunk_slots;
 } efla_saved_layout;
 
@@ -144,10 +147,10 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
  * Segment-parallel scan (summary page, section 3.3: from chunk to chunk the state follows an
  * affine map, S <- (I - K^T W) S + K^T U, so the maps of consecutive chunks compose): when
  * the plan splits sequences into G > 1 segments, every segment's composed transition P and
- * zero-start state R are formed in parallel, a short sequential pass chains them
+ * zero-start state R are formed in parallel (one launch), a short sequential pass chains them
  * (S_in of segment j+1 = P_j S_in_j + R_j, fp32), and the output scan runs over all segments
  * at once from those states. Same results up to rounding; the workspace grows by
- * 4 B G H dk (2 dv + dk) bytes.
+ * 4 B G H dk (2 dv + dk) bytes, and a saved buffer keeps the P_j for the backward.
  * The library's choice (segments = 0) splits only when B * H * dv / 32 < 128 and a
  * sequence has at least 32 chunks, aiming at about 256 scan workgroups (one per compute unit)
  * and at least 16 chunks per segment. */
@@ -210,11 +213,13 @@ efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const 
 /* Backward with recurrent state I/O: the gradient of sum(o * d_o) + <ht, dht> with respect to
  * q, k, v, beta and h0. With a segment plan (efla_problem.segments) the reverse state-gradient
  * scan is segment-parallel like the forward's: going backwards a chunk maps the gradient
- * affinely, G <- (I - W^T K) G + scale (Q - M W)^T dO, so each segment's composed map A and
- * zero-start gradient R are formed in parallel, chained from the last segment to the first,
- * and the full scan then runs over all segments from their incoming gradients; with a saved
- * buffer the workspace then needs 4 B G H dk (2 dv + dk) more bytes (never more than
- * efla_workspace_bytes(p, 1)). h0 must be what the forward used (only read when saved == NULL; NULL =
+ * affinely, G <- (I - W^T K) G + scale (Q - M W)^T dO; over a segment these maps compose to the
+ * transpose of the forward's segment transition P_j (saved by the forward, or recomputed with
+ * it), so only each segment's zero-start gradient R is formed, in parallel; the segments are
+ * chained from the last to the first with P_j^T, and the full scan then runs over all segments
+ * from their incoming gradients. With a saved buffer the workspace then needs 8 B G H dk dv more
+ * bytes (never more than efla_workspace_bytes(p, 1)). The saved buffer must come from a forward
+ * call with the same problem, segment plan included. h0 must be what the forward used (only read when saved == NULL; NULL =
  * zero); dht (NULL = zero) is the gradient arriving at the final states; dh0 (NULL = not
  * written) receives the gradient at the initial states. fp32 [n_state][H][dk][dv] each. */
 efla_status efla_bwd_state(const efla_problem* p, const void* q, const void* k, const void* v,

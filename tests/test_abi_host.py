@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 8
+    assert L.efla_abi_version() == 9
 
 
 def test_status_strings(L):
@@ -192,6 +192,12 @@ def test_segment_plan_workspace(L):
     assert extra(B=1, T=64 * 3, segments=50) == 3 * per_seg
     assert extra(B=1, T=64, segments=8) == 0                     # one chunk: nothing to split
     assert extra(B=2, T=64 * 40, segments=4) == 2 * 4 * per_seg
+    # a saved buffer keeps each segment's transition, fp32 [B * G][H][dk][dk], for the backward
+    lay = _lib.EflaSavedLayout()
+    assert L.efla_get_saved_layout(ctypes.byref(_p(B=1, T=32768)), ctypes.byref(lay)) == 0
+    assert lay.total - lay.segp == 4 * 16 * 128 * 128 * 4
+    assert L.efla_get_saved_layout(ctypes.byref(_p(B=1, T=32768, segments=1)), ctypes.byref(lay)) == 0
+    assert lay.total == lay.segp
     # the backward's recompute path runs the same forward
     p, p1 = _p(B=1, T=32768), _p(B=1, T=32768, segments=1)
     assert (L.efla_workspace_bytes(ctypes.byref(p), 1) -
@@ -227,6 +233,7 @@ def test_gated_entry_points_reject_bad_arguments(L):
     assert bwd(p, ws_=None) == 1
     assert bwd(p, ws_bytes=wb - 1) == 5
     assert bwd(p, saved=fake, saved_bytes=sb - 1) == 5
+
 
 def test_noalloc_entry_point_rejects_without_touching_hip(L):
     """efla_fwd_noalloc validates everything, including the size of its static workspace,

@@ -65,7 +65,7 @@ def test_segmented_forward_and_saved_backward(E, name, wl, segments):
     print("%s: B=%d H=%d T=%d dk=%d dv=%d segments=%d" % (name, B, H, T, dk, dv, segments), flush=True)
     o, saved, ht = E.efla_fwd(q, k, v, beta, 0.8, None, save=True, initial_state=h0_d,
                               final_state=True, segments=segments)
-    g = E.efla_bwd(q, k, v, beta, do, saved, 0.8, None, initial_state=h0_d)
+    g = E.efla_bwd(q, k, v, beta, do, saved, 0.8, None, initial_state=h0_d, segments=segments)
     torch.cuda.synchronize()
     ref_o, ref_ht = O.forward(inp["q"], inp["k"], inp["v"], inp["beta"], scale=0.8,
                               initial_state=h0)
@@ -117,21 +117,23 @@ BWD_CASES = [  # name, workload overrides, segments, mode
     ("bf16_dk64_dv128", dict(idx=2, B=1, H=2, T=64 * 12 + 40, dk=64, dv=128), 3, "exact"),
     ("bf16_dk128_dv64", dict(idx=2, B=1, H=2, T=64 * 12 + 40, dk=128, dv=64), 3, "exact"),
     ("bf16_delta_rule", dict(idx=2, B=1, H=2, T=64 * 16), 4, "euler"),
-    # 4 segments x 16 heads: wide enough for the 32-column tiling, whose state-only, transition
-    # and full reverse scans are DMA-fed (the unsegmented comparison runs the 16-column tiling)
+    # 4 segments x 16 heads: wide enough for the 32-column tiling, whose state-only and full
+    # reverse scans are DMA-fed (the unsegmented comparison runs the 16-column tiling)
     ("bf16_wide_seg4", dict(idx=2, B=1, H=16, T=64 * 20 + 7), 4, "exact"),
 ]
 
 
 @pytest.mark.parametrize("name,wl,segments,mode", BWD_CASES, ids=[c[0] for c in BWD_CASES])
 def test_segmented_backward_with_state_gradients(E, name, wl, segments, mode):
-    """Segment-parallel reverse scan (zero-start gradients and transitions of all segments, the
-    chain from the last segment to the first, then the full scan from each segment's incoming
-    gradient): every gradient, including the one arriving at the final state and the one
-    leaving the initial state, against the oracle and against the unsegmented backward. The
-    segment chain applies each segment's transition to the incoming gradient as one bf16 product
-    (one extra rounding per segment), so the two bf16 scans agree to the parity tolerance, not
-    to rounding (fp32 agrees to 5e-5)."""
+    """Segment-parallel reverse scan (zero-start gradients of all segments, the chain from the
+    last segment to the first with the transposed transitions the segment-parallel forward
+    saved, then the full scan from each segment's incoming gradient): every gradient, including
+    the one arriving at the final state and the one leaving the initial state, against the
+    oracle and against the unsegmented forward and backward. The segment chain applies each
+    segment's transition to the incoming gradient as one bf16 product (one extra rounding per
+    segment), so the two bf16 paths agree to the parity tolerance, not to rounding (fp32 agrees
+    to 5e-5). A saved buffer belongs to its problem's segment plan: the unsegmented backward
+    reads the unsegmented forward's buffer."""
     wl = dict(wl)
     w = workload(wl.pop("idx"), **wl)
     inp = make_inputs(w, with_grad=True)
@@ -149,10 +151,12 @@ def test_segmented_backward_with_state_gradients(E, name, wl, segments, mode):
     h0_d, dht_d = _dev(h0, torch.float32), _dev(dht, torch.float32)
     print("%s: B=%d H=%d T=%d dk=%d dv=%d segments=%d mode=%s" % (name, B, H, T, dk, dv, segments, mode),
           flush=True)
-    _, saved = E.efla_fwd(q, k, v, beta, 0.8, None, save=True, initial_state=h0_d, mode=mode, segments=1)
+    _, saved = E.efla_fwd(q, k, v, beta, 0.8, None, save=True, initial_state=h0_d, mode=mode,
+                          segments=segments)
+    _, saved1 = E.efla_fwd(q, k, v, beta, 0.8, None, save=True, initial_state=h0_d, mode=mode, segments=1)
     g = E.efla_bwd(q, k, v, beta, do, saved, 0.8, None, mode=mode, initial_state=h0_d,
                    d_final_state=dht_d, d_initial_state=True, segments=segments)
-    g1 = E.efla_bwd(q, k, v, beta, do, saved, 0.8, None, mode=mode, initial_state=h0_d,
+    g1 = E.efla_bwd(q, k, v, beta, do, saved1, 0.8, None, mode=mode, initial_state=h0_d,
                     d_final_state=dht_d, d_initial_state=True, segments=1)
     torch.cuda.synchronize()
     ref = O.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["do"], scale=0.8, initial_state=h0,
