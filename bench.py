@@ -134,6 +134,46 @@ def ingest_counters(fetch_csv, write_csv, probe_mib):
     print(json.dumps(out, indent=1))
 
 
+def _kernel_label(mangled):
+    """efla kernel symbol -> 'name<args>' (bf16/f32, integers, T/F); other symbols unchanged."""
+    import re
+    m = re.match(r"_ZN4efla\d+(\w+?)_kernelI", mangled)
+    if not m:
+        return mangled[:60]
+    rest, args = mangled[m.end():], []
+    while rest and rest[0] != "E":
+        t = re.match(r"DF16b|f|Li(-?\d+)E|Lb([01])E", rest)
+        if not t:
+            break
+        tok = t.group(0)
+        args.append("bf16" if tok == "DF16b" else "f32" if tok == "f" else
+                    t.group(1) if t.group(1) is not None else "TF"[1 - int(t.group(2))])
+        rest = rest[t.end():]
+    return "%s<%s>" % (m.group(1), ",".join(args))
+
+
+def trace_summary(path):
+    """Markdown table of a rocprofv3 kernel trace (kernel_trace.csv, or .csv.gz): dispatches
+    grouped by kernel instance and grid size, with count and average / min / max duration."""
+    import csv
+    import gzip
+    import collections
+    opener = gzip.open if path.endswith(".gz") else open
+    groups = collections.OrderedDict()
+    with opener(path, "rt") as f:
+        for r in csv.DictReader(f):
+            wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            key = (_kernel_label(r["Kernel_Name"]), wgs, int(r["Workgroup_Size_X"]))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | workgroups x threads | calls | avg us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for (name, wgs, wgsz), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if len(d) < 2 and "efla" not in name and "<" not in name:
+            continue
+        print("| %s | %d x %d | %d | %.1f | %.1f | %.1f |" % (name, wgs, wgsz, len(d), sum(d) / len(d),
+                                                          min(d), max(d)))
+
+
 def host_info():
     """Host cores available to this process, CPU model and BLAS threads (the oracle's numpy)."""
     import numpy  # noqa: F401  (loads the BLAS library threadpoolctl reports)
@@ -201,15 +241,11 @@ def long_context(E, make_inputs, workload, warmup, iters):
     res = {"workload": "efla_fwd_B1_H16_T32768_d128_bf16"}
     lay = None
 
+    run = event_timer(torch, torch.cuda.current_stream())
+
     def timed(f):
-        for _ in range(warmup):
-            f()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(iters):
-            f()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / iters
+        prewarm(torch, f, 0.3)
+        return run(f, iters)
 
     for segs, key in ((0, "segmented"), (1, "sequential")):
         p = E.make_problem(q, k, v, beta, segments=segs)
@@ -225,7 +261,10 @@ def long_context(E, make_inputs, workload, warmup, iters):
         ms_step = timed(step)
         res[key] = {"ms_fwd": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
                     "ms_fwd_bwd": round(ms_step, 4),
-                    "fwd_bwd_tokens_per_s": round(w.B * w.T / (ms_step * 1e-3), 1)}
+                    "fwd_bwd_tokens_per_s": round(w.B * w.T / (ms_step * 1e-3), 1),
+                    "fwd_kernels_avg_ms": kernel_avgs(
+                        E, lambda: E.efla_fwd(q, k, v, beta, 1.0, None, False, ws, o=o, segments=segs), iters)[0],
+                    "fwd_bwd_kernels_avg_ms": kernel_avgs(E, step, iters)[0]}
         if segs == 0:
             lay = E.efla_workspace_bytes(p, False) - E.efla_workspace_bytes(
                 E.make_problem(q, k, v, beta, segments=1), False)
@@ -236,6 +275,16 @@ def long_context(E, make_inputs, workload, warmup, iters):
     res["fwd_bwd_speedup"] = round(res["sequential"]["ms_fwd_bwd"] / res["segmented"]["ms_fwd_bwd"], 3)
     del q, k, v, beta, o, do, grads
     return res
+
+
+def prewarm(torch, f, seconds=0.5):
+    """Runs f repeatedly for about `seconds` (untimed): after idle time the GPU needs some tens
+    of milliseconds of work before its step time settles (clock and power ramp)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
 
 
 def event_timer(torch, stream):
@@ -323,11 +372,9 @@ def all_configs(E, args):
             E.efla_bwd(q, k, v, beta, do, saved, 1.0, cu, ws, grads=grads)
         run = event_timer(torch, torch.cuda.current_stream())
         n = 20 if B * H * T <= 2 ** 21 else 8
-        for f in (fwd, step):
-            for _ in range(3):
-                f()
-        torch.cuda.synchronize()
+        prewarm(torch, fwd)
         ms_f = run(fwd, n)
+        prewarm(torch, step)
         ms_s = run(step, n)
         gpu = {"o": o.float().cpu().numpy()}
         if w.backward:
@@ -397,68 +444,13 @@ def all_configs(E, args):
             json.dump(out, f, indent=1)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the B=1, T=32768 forward (e.g. for per-kernel counter runs)")
-    ap.add_argument("--all-configs", action="store_true",
-                    help="instead of the benchmark line: every workload's GPU times, roofline "
-                         "fractions, fp64 oracle time and error vs the oracle (several minutes)")
-    ap.add_argument("--out", default=None, help="--all-configs: also write the table here")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="first run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="store per-kernel HBM traffic from two rocprofv3 --pmc csv files and exit")
-    args = ap.parse_args()
-    if args.ingest_counters:
-        ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.copy_probe_mib or 1024)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)"
-              % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import delta_rule_sequence_amd as E
-    from workloads import make_inputs, workload
-
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
-    E._lib.lib()
-    if args.all_configs:
-        all_configs(E, args)
-        return
-    if args.copy_probe_mib > 0:
-        # A plain copy of known size: reads and writes copy_probe_mib MiB once each.
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    w = workload(2)
-    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
-    inp = make_inputs(w)
-    dev = torch.device("cuda:0")
-    q, k, v, beta, do = (torch.from_numpy(inp[n]).to(dev, torch.bfloat16)
-                         for n in ("q", "k", "v", "beta", "do"))
-    p = E.make_problem(q, k, v, beta)
-    o = torch.empty_like(v)
-    saved = torch.empty(E.efla_saved_bytes(p), dtype=torch.uint8, device=dev)
-    ws = torch.empty(max(E.efla_workspace_bytes(p, False), E.efla_workspace_bytes(p, True)),
-                     dtype=torch.uint8, device=dev)
-    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(beta))
-
-    def step():
-        E.efla_fwd(q, k, v, beta, 1.0, None, True, ws, o=o, saved=saved)
-        E.efla_bwd(q, k, v, beta, do, saved, 1.0, None, ws, grads=grads)
-
+def aux_measurements(E, args, torch, np, make_inputs, workload, step, q, k, v, beta, do, o, saved,
+                     ws, grads):
+    """Everything in the bench line beside the headline: the step as a HIP graph, a cold-cache
+    step, the delta-rule A/B, gated EFLA, decode and the long-context workload."""
+    B, H, T = q.shape[0], q.shape[1], q.shape[2]
+    dk, dv = k.shape[-1], v.shape[-1]
+    dev = q.device
     stream = torch.cuda.current_stream()
     # The same step captured once into a HIP graph and replayed (every kernel still runs; only
     # the host launches are gone), timed the same way.
@@ -571,6 +563,91 @@ def main():
     long_ctx = None if args.no_long_context else long_context(E, make_inputs, workload, args.warmup,
                                                                 max(5, args.steps // 5))
 
+    return {"graph_ms": graph_ms, "cold_ms": cold_ms, "euler": euler, "gated": gated,
+            "decode_us": decode_us, "dec_k": dec_k, "dec_kernel_us": dec_kernel_us,
+            "state_bytes": state_bytes, "long_ctx": long_ctx}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the B=1, T=32768 forward (e.g. for per-kernel counter runs)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the benchmark step (no graph, cold-cache, delta-rule, gated, "
+                         "decode or long-context parts; for kernel traces and counter runs)")
+    ap.add_argument("--long-context-only", action="store_true",
+                    help="run only the B=1, T=32768 part and print its JSON (for its kernel trace)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the benchmark line: every workload's GPU times, roofline "
+                         "fractions, fp64 oracle time and error vs the oracle (several minutes)")
+    ap.add_argument("--out", default=None, help="--all-configs: also write the table here")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print a rocprofv3 kernel trace grouped by kernel instance and grid, then exit")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store per-kernel HBM traffic from two rocprofv3 --pmc csv files and exit")
+    args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.copy_probe_mib or 1024)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import delta_rule_sequence_amd as E
+    from workloads import make_inputs, workload
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    E._lib.lib()
+    if args.all_configs:
+        all_configs(E, args)
+        return
+    if args.long_context_only:
+        print(json.dumps(long_context(E, make_inputs, workload, args.warmup, max(5, args.steps // 5))),
+              flush=True)
+        return
+    if args.copy_probe_mib > 0:
+        # A plain copy of known size: reads and writes copy_probe_mib MiB once each.
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    w = workload(2)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, beta, do = (torch.from_numpy(inp[n]).to(dev, torch.bfloat16)
+                         for n in ("q", "k", "v", "beta", "do"))
+    p = E.make_problem(q, k, v, beta)
+    o = torch.empty_like(v)
+    saved = torch.empty(E.efla_saved_bytes(p), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(E.efla_workspace_bytes(p, False), E.efla_workspace_bytes(p, True)),
+                     dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(beta))
+
+    def step():
+        E.efla_fwd(q, k, v, beta, 1.0, None, True, ws, o=o, saved=saved)
+        E.efla_bwd(q, k, v, beta, do, saved, 1.0, None, ws, grads=grads)
+
+    stream = torch.cuda.current_stream()
+    prewarm(torch, step)  # untimed; the measurements below then see the GPU at its steady clocks
+    aux = aux_measurements(E, args, torch, np, make_inputs, workload, step, q, k, v, beta, do, o,
+                           saved, ws, grads) if not args.headline_only else {}
     # The headline: W untimed warmup steps, then exactly K steps between two synchronizations.
     # It runs after the measurements above, which keep the GPU busy: after a few seconds idle
     # (input generation, allocations) a step takes 0.30 ms and needs some 60-80 steps to settle
@@ -589,7 +666,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
-    gated["gated_over_ungated_fwd_bwd_time"] = round(gated["gated_fwd_bwd_ms"] / ms_per_step, 4)
+    if aux:
+        aux["gated"]["gated_over_ungated_fwd_bwd_time"] = round(aux["gated"]["gated_fwd_bwd_ms"] / ms_per_step, 4)
 
     # Per-kernel durations: HIP events recorded by the library around each launch, on the
     # stream the kernel runs on, over a second timed region of the same length.
@@ -651,19 +729,25 @@ def main():
         "step_mfma_frac": round(step_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "roofline": roofline,
-        "hip_graph": {"ms_per_step": round(graph_ms, 4),
-                      "tokens_per_s": round(B * T / (graph_ms * 1e-3), 1)},
-        "cold_cache": {"median_ms_per_step": round(cold_ms[len(cold_ms) // 2], 4),
-                       "tokens_per_s": round(B * T / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),
-                       "steps": len(cold_ms)},
-        "euler_mode": euler,
-        "decode": {"us_per_call": round(decode_us, 2), "kernel_us": round(dec_kernel_us, 2),
-                   "kernels_avg_ms": dec_k, "tokens_per_call": B, "token_heads_per_call": B * H,
-                   "hbm_bytes_per_call": state_bytes,
-                   "kernel_hbm_frac": round(state_bytes / (dec_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "gated": gated,
-        "long_context": long_ctx,
     }
+    if aux:
+        graph_ms, cold_ms = aux["graph_ms"], aux["cold_ms"]
+        out.update({
+            "hip_graph": {"ms_per_step": round(graph_ms, 4),
+                          "tokens_per_s": round(B * T / (graph_ms * 1e-3), 1)},
+            "cold_cache": {"median_ms_per_step": round(cold_ms[len(cold_ms) // 2], 4),
+                           "tokens_per_s": round(B * T / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),
+                           "steps": len(cold_ms)},
+            "euler_mode": aux["euler"],
+            "decode": {"us_per_call": round(aux["decode_us"], 2),
+                       "kernel_us": round(aux["dec_kernel_us"], 2),
+                       "kernels_avg_ms": aux["dec_k"], "tokens_per_call": B, "token_heads_per_call": B * H,
+                       "hbm_bytes_per_call": aux["state_bytes"],
+                       "kernel_hbm_frac": round(aux["state_bytes"] / (aux["dec_kernel_us"] * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4)},
+            "gated": aux["gated"],
+            "long_context": aux["long_ctx"],
+        })
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -8,7 +8,12 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libefla.so")
+# Debug builds of the same sources (python -m delta_rule_sequence_amd.build --sanitize or
+# --lds-poison) are loaded instead when EFLA_LIBRARY_VARIANT names them: "hostsan" (host code
+# under AddressSanitizer/UndefinedBehaviorSanitizer, for the host-side checks of the C ABI) or
+# "ldspoison" (kernels that fill their LDS with NaN before they start).
+_VARIANTS = {"": "libefla.so", "hostsan": "libefla_hostsan.so", "ldspoison": "libefla_ldspoison.so"}
+LIB_PATH = os.path.join(_PKG, _VARIANTS[os.environ.get("EFLA_LIBRARY_VARIANT", "")])
 
 EFLA_F32 = 0
 EFLA_BF16 = 1

@@ -1,6 +1,8 @@
 """Build libefla.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m delta_rule_sequence_amd.build
+    python -m delta_rule_sequence_amd.build              # libefla.so
+    python -m delta_rule_sequence_amd.build --sanitize   # libefla_hostsan.so (host code only)
+    python -m delta_rule_sequence_amd.build --lds-poison # libefla_ldspoison.so (debug)
 """
 from __future__ import annotations
 
@@ -51,27 +53,70 @@ def _run(cmd):
     return msg
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libefla.so; returns its path."""
+# The same sources with AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+# (argument checks, sizing, workspace carving), for exercising the host paths of the C ABI on a
+# machine without a GPU. Each -fsanitize= follows -Xarch_host, so device code is built as usual
+# and not instrumented.
+SAN_OUT = os.path.join(PKG, "libefla_hostsan.so")
+SAN_FLAGS = ["--offload-arch=gfx950", "-O3", "-Xarch_host", "-O1", "-Xarch_host", "-g",
+             "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-Wall",
+             "-Wno-unused-function", "-Wno-unused-command-line-argument",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all",
+             "-I" + os.path.join(ROOT, "include")]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (preloaded into the process that loads
+    libefla_hostsan.so; it also carries the UndefinedBehaviorSanitizer handlers)."""
+    r = subprocess.run([os.path.join(os.path.dirname(hipcc()), "..", "llvm", "bin", "clang"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found next to hipcc")
+    return path
+
+
+# Debug build with -DEFLA_LDS_POISON: every kernel fills its dynamic LDS with NaN bytes before it
+# starts, so a read of LDS that the kernel did not write first shows up as NaN in the results.
+POISON_OUT = os.path.join(PKG, "libefla_ldspoison.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False, lds_poison: bool = False) -> str:
+    """Compile every source and link libefla.so (sanitize: libefla_hostsan.so, host code
+    instrumented; lds_poison: libefla_ldspoison.so); returns its path."""
+    assert not (sanitize and lds_poison), "one variant at a time"
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
+    bdir = BUILD_DIR + ("_hostsan" if sanitize else "_ldspoison" if lds_poison else "")
+    out = SAN_OUT if sanitize else POISON_OUT if lds_poison else OUT
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, s.replace(".hip", ".o")) for s in SOURCES]
 
     def compile_one(i):
         src = os.path.join(CSRC, SOURCES[i])
-        return _run([cc] + FLAGS + FILE_FLAGS.get(SOURCES[i], []) + ["-c", src, "-o", objs[i]])
+        flags = SAN_FLAGS if sanitize else FLAGS + FILE_FLAGS.get(SOURCES[i], [])
+        if lds_poison:
+            flags = flags + ["-DEFLA_LDS_POISON"]
+        return _run([cc] + flags + ["-c", src, "-o", objs[i]])
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         logs = list(ex.map(compile_one, range(len(SOURCES))))
-    tmp = OUT + ".tmp%d" % os.getpid()
-    logs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
-    os.replace(tmp, OUT)
+    tmp = out + ".tmp%d" % os.getpid()
+    link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if sanitize:
+        link[2:2] = ["-Xarch_host", "-fsanitize=address",
+                     "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"]
+    logs.append(_run(link))
+    os.replace(tmp, out)
     if verbose:
         for l in logs:
             if l:
                 print(l)
-    return OUT
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv,
+                lds_poison="--lds-poison" in sys.argv))

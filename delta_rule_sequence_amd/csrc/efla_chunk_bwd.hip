@@ -129,6 +129,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_kernel(
   constexpr int KC = Mma<E>::KC, KSV = DV / KC;
   constexpr int CK = DK / 64, CV = DV / 64;  // column blocks per wave of [64][d] outputs
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_poison(smem);
   E* sK = (E*)(smem + L::oK);
   E* sQ = (E*)(smem + L::oQ);
   E* sW = (E*)(smem + L::oW);

@@ -29,6 +29,27 @@ constexpr int kThreads = 256;
 
 #define EFLA_DEV __device__ __forceinline__
 
+// Debug build (-DEFLA_LDS_POISON): a kernel with dynamic LDS first fills its whole dynamic LDS
+// allocation with all-ones bytes, which read as NaN in fp32 and bf16, and then waits at a
+// barrier. A location the kernel reads before writing it in this launch then turns its results
+// into NaN instead of silently reusing whatever an earlier workgroup left there. The size comes
+// from the dispatch packet (group_segment_size: static + dynamic LDS of this launch). In the
+// normal build this is empty. No kernel keeps integers in dynamic LDS, so the poison cannot
+// become an address.
+EFLA_DEV void lds_poison(unsigned char* smem) {
+#ifdef EFLA_LDS_POISON
+  const char* pkt = (const char*)__builtin_amdgcn_dispatch_ptr();
+  const uint32_t total = *(const uint32_t*)(pkt + 28);
+  uint32_t n = (total - __builtin_amdgcn_groupstaticsize()) / 16;
+  if (n > 160u * 1024u / 16u) n = 160u * 1024u / 16u;
+  const uint32_t nt = blockDim.x;
+  for (uint32_t i = threadIdx.x; i < n; i += nt) ((u32x4*)smem)[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+  __syncthreads();
+#else
+  (void)smem;
+#endif
+}
+
 template <typename E> EFLA_DEV E to_e(float x);
 template <> EFLA_DEV float to_e<float>(float x) { return x; }
 template <> EFLA_DEV __bf16 to_e<__bf16>(float x) { return (__bf16)x; }

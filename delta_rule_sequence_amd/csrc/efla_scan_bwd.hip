@@ -70,6 +70,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
   static_assert(TPW >= 1 && ((DK / 16) * NB) % 4 == 0, "state tiles must split over 4 waves");
   static_assert(VQ >= 1 && VM >= 1 && (64 * DK / VE) % kThreads == 0, "tile split");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_poison(smem);
   E* sG = (E*)(smem + L::oG);
   E* sDt = (E*)(smem + L::oDt);
   E* sDu = (E*)(smem + L::oDu);
@@ -328,6 +329,7 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   static_assert(TPW >= 1 && ((DK / 16) * NB) % 4 == 0, "state tiles must split over 4 waves");
   static_assert(L::bytes <= 160 * 1024, "LDS budget");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_poison(smem);
   E* sG = (E*)(smem + L::oG);
   E* sDt = (E*)(smem + L::oDt);
   E* sDu = (E*)(smem + L::oDu);

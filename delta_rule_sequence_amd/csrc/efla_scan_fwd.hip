@@ -70,6 +70,7 @@ __device__ __forceinline__ void scan_fwd_body(
   constexpr int VE = 16 / (int)sizeof(E);
   static_assert(DV % TV == 0, "column tiles");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_poison(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void seg_combine_kernel(
   constexpr int NW = DV / 16, NT = 64 * NW, NBK = DK / 16, KSK = DK / Mma<E>::KC;
   constexpr int VE = 16 / (int)sizeof(E);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_poison(smem);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x / H, h = blockIdx.x % H;

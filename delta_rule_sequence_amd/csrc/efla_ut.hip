@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   constexpr int VIT = 64 * DV / VE / kThreads;  // V vectors per thread
   static_assert(VPR <= 64 && (64 % VPR) == 0 && KIT >= 1 && VIT >= 1, "row split");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_poison(smem);
   E* sK = (E*)(smem + L::oK);
   E* sV = (E*)(smem + L::oV);
   float* sA = (float*)(smem + L::oA);

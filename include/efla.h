@@ -116,7 +116,8 @@ const char* efla_status_str(efla_status s);
 efla_status efla_check_problem(const efla_problem* p);
 
 /* Device workspace that efla_fwd (for_backward = 0) or efla_bwd (for_backward = 1)
- * needs, in bytes; 0 if the problem is invalid. For efla_bwd the figure assumes
+ * needs, in bytes; 0 if the problem is invalid. (Sizing queries of this library; no passage of
+ * the pages defines them.) For efla_bwd the figure assumes
  * saved == NULL (recompute); with a saved buffer less is used, never more. */
 size_t efla_workspace_bytes(const efla_problem* p, int for_backward);
 
@@ -202,7 +203,11 @@ efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, 
                            void* stream);
 
 /* Backward of sum(o * d_o): dq, dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T], all in
- * the problem dtype (every output fully overwritten). `saved` is the buffer a forward
+ * the problem dtype (every output fully overwritten). The pages print no backward; this is
+ * reverse-mode differentiation of the chunk form (summary page, section 3.3: chunk-level
+ * recurrence and UT transform) and of the exact-flow step (section 3.2: alpha_t replaces beta_t,
+ * so dbeta = dalpha e^{-beta lambda} and the key energy adds 2 k dalpha beta^2 phi'(beta lambda),
+ * phi(x) = (1 - e^{-x}) / x). `saved` is the buffer a forward
  * call on the same inputs filled, or NULL to recompute it inside ws.
  * ws: efla_workspace_bytes(p, 1). */
 efla_status efla_bwd(const efla_problem* p, const void* q, const void* k, const void* v,
