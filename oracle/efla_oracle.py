@@ -393,9 +393,9 @@ def gated_coefficient_derivatives(k, beta, gate, mode="exact"):
 
 
 def gated_backward(q, k, v, beta, gate, do, scale=1.0, initial_state=None, d_final_state=None,
-                   mode="exact"):
+                   mode="exact", cu_seqlens=None):
     """Reverse-mode gradients of sum(o * do) (+ <final_state, d_final_state>) for gated_forward
-    (dense batches), written out by hand per token:
+    (dense or packed batches; states per sequence), written out by hand per token:
       S_t = g (S_{t-1} - alpha k y^T) + b k v^T,  y = S_{t-1}^T k,  o_t = scale S_t^T q_t;
       dq = scale S_t do;  dv = b dS^T k;  db = k^T dS v;  dg = <dS, S_{t-1}> - alpha k^T dS y;
       dalpha = -g k^T dS y;  dk = -g alpha (dS y + S_{t-1} dS^T k) + b dS v + 2 k dlambda;
@@ -408,38 +408,42 @@ def gated_backward(q, k, v, beta, gate, do, scale=1.0, initial_state=None, d_fin
     de = gated_coefficient_derivatives(k, beta, gate, mode)
     S0 = _f64(initial_state)
     dSF = _f64(d_final_state)
+    seqs = sequences(B, T, cu_seqlens)
     out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), dbeta=np.zeros_like(beta),
-               dgate=np.zeros_like(gate), d_initial_state=np.zeros((B, H, dk, dv)))
-    for b_ in range(B):
+               dgate=np.zeros_like(gate), d_initial_state=np.zeros((len(seqs), H, dk, dv)))
+    for i, (b_, s0, s1) in enumerate(seqs):
+        Ti = s1 - s0
         for h in range(H):
-            al, bb, gg = co["alpha"][b_, h], co["b"][b_, h], co["g"][b_, h]
-            K, V, Q, dO = k[b_, h], v[b_, h], q[b_, h], do[b_, h]
-            states = [np.zeros((dk, dv)) if S0 is None else S0[b_, h].copy()]
-            for t in range(T):  # all states (tests use short sequences)
+            tok = (b_, h, slice(s0, s1))
+            al, bb, gg = co["alpha"][tok], co["b"][tok], co["g"][tok]
+            K, V, Q, dO = k[tok], v[tok], q[tok], do[tok]
+            states = [np.zeros((dk, dv)) if S0 is None else S0[i, h].copy()]
+            for t in range(Ti):  # all states (tests use short sequences)
                 S = states[-1]
                 y = S.T @ K[t]
                 states.append(gg[t] * (S - al[t] * np.outer(K[t], y)) + bb[t] * np.outer(K[t], V[t]))
-            dS = np.zeros((dk, dv)) if dSF is None else dSF[b_, h].copy()
-            dalpha, dbc, dlg = np.zeros(T), np.zeros(T), np.zeros(T)
-            for t in range(T - 1, -1, -1):
+            dS = np.zeros((dk, dv)) if dSF is None else dSF[i, h].copy()
+            dalpha, dbc, dlg = np.zeros(Ti), np.zeros(Ti), np.zeros(Ti)
+            dq_, dk_, dv_ = out["dq"][tok], out["dk"][tok], out["dv"][tok]  # views
+            for t in range(Ti - 1, -1, -1):
                 Sp, St = states[t], states[t + 1]
                 kt = K[t]
                 dS = dS + scale * np.outer(Q[t], dO[t])
-                out["dq"][b_, h, t] = scale * St @ dO[t]
+                dq_[t] = scale * St @ dO[t]
                 y = Sp.T @ kt
                 dStk = dS.T @ kt
-                out["dv"][b_, h, t] = bb[t] * dStk
+                dv_[t] = bb[t] * dStk
                 dbc[t] = kt @ dS @ V[t]
                 dg = np.sum(dS * Sp) - al[t] * (kt @ dS @ y)
                 dalpha[t] = -gg[t] * (kt @ dS @ y)
-                out["dk"][b_, h, t] = -gg[t] * al[t] * (dS @ y + Sp @ dStk) + bb[t] * (dS @ V[t])
+                dk_[t] = -gg[t] * al[t] * (dS @ y + Sp @ dStk) + bb[t] * (dS @ V[t])
                 dlg[t] = gg[t] * dg
                 dS = gg[t] * (dS - al[t] * np.outer(kt, dStk))
-            out["d_initial_state"][b_, h] = dS
-            out["dbeta"][b_, h] = dalpha * de["da_dbeta"][b_, h] + dbc * de["db_dbeta"][b_, h]
-            dlam = dalpha * de["da_dlam"][b_, h] + dbc * de["db_dlam"][b_, h]
-            out["dk"][b_, h] += 2.0 * K * dlam[:, None]
-            out["dgate"][b_, h] = dlg + dbc * de["db_da"][b_, h]
+            out["d_initial_state"][i, h] = dS
+            out["dbeta"][tok] = dalpha * de["da_dbeta"][tok] + dbc * de["db_dbeta"][tok]
+            dlam = dalpha * de["da_dlam"][tok] + dbc * de["db_dlam"][tok]
+            dk_ += 2.0 * K * dlam[:, None]
+            out["dgate"][tok] = dlg + dbc * de["db_da"][tok]
     return out
 
 

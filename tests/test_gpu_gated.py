@@ -204,8 +204,8 @@ def test_gated_autograd(E):
 
 def test_gated_packed_sequences(E):
     """Packed batch (cu_seqlens): the state, and the running log-decay sums, restart at every
-    sequence; each sequence against the oracle on its own, forward and backward, with initial
-    and final states per sequence."""
+    sequence; forward and backward against the oracle's packed gated forms, with initial and
+    final states per sequence."""
     lens = [70, 200, 1, 64, 133]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
@@ -223,23 +223,10 @@ def test_gated_packed_sequences(E):
     grads = E.efla_bwd_gated(q, k, v, beta, g, do, saved, 0.8, cu_d, initial_state=h0_d,
                              d_final_state=dht_d, d_initial_state=True)
     torch.cuda.synchronize()
-    ref_o, ref_ht = np.zeros(inp["v"].shape), np.zeros(h0.shape)
-    ref = {nm: np.zeros(inp[src].shape) for nm, src in (("dq", "q"), ("dk", "k"), ("dv", "v"),
-                                                         ("dbeta", "beta"), ("dgate", "beta"))}
-    ref["d_initial_state"] = np.zeros(h0.shape)
-    for i in range(len(lens)):
-        s0, s1 = cu[i], cu[i + 1]
-        sl = lambda x: x[:, :, s0:s1]
-        oo, hh = O.gated_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
-                                 scale=0.8, initial_state=h0[i:i + 1])
-        ref_o[:, :, s0:s1] = oo
-        ref_ht[i] = hh[0]
-        gr = O.gated_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(a),
-                              sl(inp["do"]), scale=0.8, initial_state=h0[i:i + 1],
-                              d_final_state=dht[i:i + 1])
-        for nm in ("dq", "dk", "dv", "dbeta", "dgate"):
-            ref[nm][:, :, s0:s1] = gr[nm]
-        ref["d_initial_state"][i] = gr["d_initial_state"][0]
+    ref_o, ref_ht = O.gated_forward(inp["q"], inp["k"], inp["v"], inp["beta"], a, scale=0.8,
+                                    cu_seqlens=cu, initial_state=h0)
+    ref = O.gated_backward(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["do"], scale=0.8,
+                           initial_state=h0, d_final_state=dht, cu_seqlens=cu)
     _check("o", _np(o), ref_o)
     _check("ht", _np(ht), ref_ht)
     for nm, t in zip(GRAD_NAMES, grads):

@@ -609,6 +609,61 @@ def test_gated_backward_against_central_differences(mode):
 
 
 @pytest.mark.parametrize("mode", ["exact", "euler"])
+def test_gated_packed_backward_against_central_differences(mode):
+    """Packed batch (cu_seqlens with an empty and a one-token sequence): every coordinate of
+    every input by central differences of the packed gated forward's loss, states per sequence."""
+    r = _rng(151)
+    cu = np.array([0, 3, 3, 4, 9])
+    H, T, dk, dv, n = 2, 9, 3, 2, 4
+    q, k, v = r.standard_normal((1, H, T, dk)), r.standard_normal((1, H, T, dk)) * 0.8, r.standard_normal((1, H, T, dv))
+    beta, gate = r.uniform(0.1, 1.0, (1, H, T)), -r.uniform(0.05, 1.5, (1, H, T))
+    S0, do, dF = r.standard_normal((n, H, dk, dv)), r.standard_normal((1, H, T, dv)), r.standard_normal((n, H, dk, dv))
+
+    def loss(q_, k_, v_, b_, g_, s_):
+        o, f = O.gated_forward(q_, k_, v_, b_, g_, scale=0.7, cu_seqlens=cu, initial_state=s_, mode=mode)
+        return np.sum(o * do) + np.sum(f * dF)
+
+    g = O.gated_backward(q, k, v, beta, gate, do, scale=0.7, initial_state=S0, d_final_state=dF,
+                         mode=mode, cu_seqlens=cu)
+    args = [q, k, v, beta, gate, S0]
+    names = ["dq", "dk", "dv", "dbeta", "dgate", "d_initial_state"]
+    eps = 1e-6
+    for i, (x, nm) in enumerate(zip(args, names)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = [a.copy() for a in args], [a.copy() for a in args]
+            xp[i][idx] += eps
+            xm[i][idx] -= eps
+            num[idx] = (loss(*xp) - loss(*xm)) / (2 * eps)
+        assert np.max(np.abs(num - g[nm])) < 1e-7 * max(1.0, np.max(np.abs(num))), (nm, np.max(np.abs(num - g[nm])))
+    # the empty sequence passes its final-state gradient straight through
+    assert np.array_equal(g["d_initial_state"][1], dF[1])
+
+
+def test_gated_packed_equals_separate_sequences():
+    """Packed forward and backward equal the same sequences run one by one as dense batches."""
+    r = _rng(152)
+    lens = [5, 0, 1, 70, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    H, T, dk, dv, n = 2, int(cu[-1]), 4, 3, len(lens)
+    q, k, v = r.standard_normal((1, H, T, dk)), r.standard_normal((1, H, T, dk)) * 0.7, r.standard_normal((1, H, T, dv))
+    beta, gate = r.uniform(0.1, 1.0, (1, H, T)), -r.uniform(0.0, 1.0, (1, H, T))
+    S0, do, dF = r.standard_normal((n, H, dk, dv)), r.standard_normal((1, H, T, dv)), r.standard_normal((n, H, dk, dv))
+    o, f = O.gated_forward(q, k, v, beta, gate, 0.9, cu_seqlens=cu, initial_state=S0)
+    g = O.gated_backward(q, k, v, beta, gate, do, 0.9, S0, dF, cu_seqlens=cu)
+    for i in range(n):
+        sl = lambda x: x[:, :, cu[i]:cu[i + 1]]
+        o1, f1 = O.gated_forward(sl(q), sl(k), sl(v), sl(beta), sl(gate), 0.9, initial_state=S0[i:i + 1])
+        g1 = O.gated_backward(sl(q), sl(k), sl(v), sl(beta), sl(gate), sl(do), 0.9, S0[i:i + 1], dF[i:i + 1])
+        assert np.array_equal(sl(o), o1) and np.array_equal(f[i], f1[0])
+        for nm in ("dq", "dk", "dv", "dbeta", "dgate"):
+            assert np.array_equal(sl(g[nm]), g1[nm]), nm
+        assert np.array_equal(g["d_initial_state"][i], g1["d_initial_state"][0])
+
+
+@pytest.mark.parametrize("mode", ["exact", "euler"])
 def test_gated_chunk_backward_equals_token_backward(mode):
     """The chunkwise gated backward (decayed UT factors, running log-decay sums) equals the
     hand-written token backward (itself pinned by central differences), ragged tail included."""
