@@ -53,16 +53,31 @@ def kernel_model(name, dk, dv, e, C=CHUNK):
 
     Bytes are the tensors the kernel must read and write at its interface (each once);
     flops count the tile contractions the method needs, triangular factors at half size
-    (2 per multiply-add)."""
-    if name == "ut_fwd":      # Q, K, V, beta -> W, U, M = tril(QK^T), X = (I + A)^-1
-        b = e * (2 * C * dk + C * dv + C) + e * (C * dk + C * dv + 2 * C * C)
-        f = 3 * C * C * dk + C * C * dv + C ** 3 / 3
-    elif name == "scan_fwd":  # Q, K, W, U, M -> O, U~, S_c
-        b = e * (3 * C * dk + C * dv + C * C) + e * (2 * C * dv + dk * dv)
-        f = 6 * C * dk * dv + C * C * dv
-    elif name == "scan_bwd":  # Q, K, W, M, dO -> dU~, dS_c
-        b = e * (3 * C * dk + C * C + C * dv) + e * (C * dv + dk * dv)
-        f = 6 * C * dk * dv + C * C * dv
+    (2 per multiply-add). bf16 problems (e = 2) keep X and the column scales alpha~ (fp32, one
+    per token) in place of W and U: the scans form U~ = X (diag(alpha~) (V - K S)) and
+    W^T dU~ = K^T diag(alpha~) X^T dU~ themselves; fp32 problems (e = 4) read W and U."""
+    xf = e == 2
+    if name == "ut_fwd":
+        if xf:                # Q, K, beta -> M = tril(QK^T), X = (I + A)^-1, alpha~
+            b = e * (2 * C * dk + C) + e * 2 * C * C + 4 * C
+            f = 2 * C * C * dk + C ** 3 / 3
+        else:                 # Q, K, V, beta -> W, U, M, X
+            b = e * (2 * C * dk + C * dv + C) + e * (C * dk + C * dv + 2 * C * C)
+            f = 3 * C * C * dk + C * C * dv + C ** 3 / 3
+    elif name == "scan_fwd":
+        if xf:                # Q, K, X, V, M, alpha~ -> O, U~, S_c
+            b = e * (2 * C * dk + C * dv + 2 * C * C) + 4 * C + e * (2 * C * dv + dk * dv)
+            f = 6 * C * dk * dv + 2 * C * C * dv
+        else:                 # Q, K, W, U, M -> O, U~, S_c
+            b = e * (3 * C * dk + C * dv + C * C) + e * (2 * C * dv + dk * dv)
+            f = 6 * C * dk * dv + C * C * dv
+    elif name == "scan_bwd":
+        if xf:                # Q, K, X, M, dO, alpha~ -> dU~, dS_c
+            b = e * (2 * C * dk + 2 * C * C + C * dv) + 4 * C + e * (C * dv + dk * dv)
+            f = 6 * C * dk * dv + 2 * C * C * dv
+        else:                 # Q, K, W, M, dO -> dU~, dS_c
+            b = e * (3 * C * dk + C * C + C * dv) + e * (C * dv + dk * dv)
+            f = 6 * C * dk * dv + C * C * dv
     elif name == "chunk_bwd":  # Q, K, V, dO, U~, dU~, beta, S_c, dS_c, X -> dQ, dK, dV, dbeta
         b = e * (2 * C * dk + 4 * C * dv + C + 2 * dk * dv + C * C) + e * (2 * C * dk + C * dv + C)
         f = 6 * C * dk * dv + 7 * C * C * dk + 3 * C * C * dv + 2 * C ** 3 / 3

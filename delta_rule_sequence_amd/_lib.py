@@ -47,8 +47,8 @@ class EflaProblem(ctypes.Structure):
 class EflaSavedLayout(ctypes.Structure):
     _fields_ = [("w", ctypes.c_size_t), ("ut", ctypes.c_size_t), ("states", ctypes.c_size_t),
                 ("table", ctypes.c_size_t), ("m", ctypes.c_size_t), ("x", ctypes.c_size_t),
-                ("cum", ctypes.c_size_t), ("segp", ctypes.c_size_t), ("total", ctypes.c_size_t),
-                ("n_chunk_slots", ctypes.c_int64)]
+                ("coef", ctypes.c_size_t), ("cum", ctypes.c_size_t), ("segp", ctypes.c_size_t),
+                ("total", ctypes.c_size_t), ("n_chunk_slots", ctypes.c_int64)]
 
 
 class EflaError(RuntimeError):

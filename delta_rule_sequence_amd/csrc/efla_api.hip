@@ -184,16 +184,23 @@ size_t bytes_seg(const Shape& s) {
 }
 // Gated forward: running log-decay sums per chunk, fp32 [slots][H][64].
 size_t bytes_cum(const Shape& s) { return (size_t)s.slots * s.H * kChunk * 4; }
+// The chunk factors the scans read. bf16 (xf): X and the per-token column scales alpha~ and b,
+// fp32 [2][slots][H][64] (b only when gated); fp32: W and U, whose tiles leave the fp32 scans no
+// LDS room for the X form.
+bool xform(const Shape& s) { return s.dt == Dt::BF16; }
+size_t coef_stride(const Shape& s) { return (size_t)s.slots * s.H * kChunk; }
+size_t bytes_coef(const Shape& s) { return xform(s) ? 2 * coef_stride(s) * 4 : 0; }
+size_t bytes_w(const Shape& s) { return xform(s) ? 0 : bytes_k(s); }
 
 // Layout of the forward->backward buffer.
 struct Saved {
-  size_t w, ut, states, table, m, x, cum, segp, total;
+  size_t w, ut, states, table, m, x, coef, cum, segp, total;
 };
 Saved saved_layout(const Shape& s) {
   Saved L;
   size_t o = 0;
   L.w = o;
-  o += align_up(bytes_k(s));
+  o += align_up(bytes_w(s));
   L.ut = o;
   o += align_up(bytes_v(s));
   L.states = o;
@@ -204,6 +211,8 @@ Saved saved_layout(const Shape& s) {
   o += align_up(bytes_m(s));
   L.x = o;
   o += align_up(bytes_x(s));
+  L.coef = o;
+  o += align_up(bytes_coef(s));
   L.cum = o;
   o += align_up(bytes_cum(s));
   L.segp = o;
@@ -212,11 +221,44 @@ Saved saved_layout(const Shape& s) {
   return L;
 }
 
-// Forward workspace: U, plus W, M and the chunk table when no saved buffer is given, plus
-// the segment-parallel scan's buffers.
+// Forward workspace: U and W (fp32) or X and the column scales (bf16), the chunk table and M
+// (all of them used only when no saved buffer is given, except U), the segment-parallel scan's
+// buffers, and the gated forward's decay sums.
+size_t bytes_ws_a(const Shape& s) { return xform(s) ? bytes_x(s) : bytes_v(s); }
+size_t bytes_ws_b(const Shape& s) { return xform(s) ? bytes_coef(s) : bytes_k(s); }
 size_t ws_fwd(const Shape& s) {
-  return align_up(bytes_v(s)) + align_up(bytes_k(s)) + align_up(bytes_table(s)) +
+  return align_up(bytes_ws_a(s)) + align_up(bytes_ws_b(s)) + align_up(bytes_table(s)) +
          align_up(bytes_m(s)) + bytes_seg(s) + align_up(bytes_cum(s));
+}
+// Buffers of one forward: saved-buffer regions when a saved buffer is given, workspace otherwise.
+struct FwdBufs {
+  unsigned char *w, *u, *x;  // W, U (fp32; U always in the workspace); X (bf16; fp32: saved only)
+  float* coef;               // alpha~, then b (bf16)
+  unsigned char *ut, *states;  // U~ and the chunk states (saved buffer only)
+  int* table;
+  unsigned char *m, *seg;
+  float *cum, *segp;
+};
+FwdBufs fwd_bufs(const Shape& s, unsigned char* ws, unsigned char* sv) {
+  const Saved L = saved_layout(s);
+  FwdBufs b;
+  unsigned char* a = ws;
+  unsigned char* bb = a + align_up(bytes_ws_a(s));
+  unsigned char* tb = bb + align_up(bytes_ws_b(s));
+  unsigned char* mw = tb + align_up(bytes_table(s));
+  b.seg = mw + align_up(bytes_m(s));
+  float* cum_ws = (float*)(b.seg + bytes_seg(s));
+  b.u = xform(s) ? nullptr : a;
+  b.w = xform(s) ? nullptr : (sv ? sv + L.w : bb);
+  b.x = sv ? sv + L.x : (xform(s) ? a : nullptr);
+  b.coef = xform(s) ? (float*)(sv ? sv + L.coef : bb) : nullptr;
+  b.ut = sv ? sv + L.ut : nullptr;
+  b.states = sv ? sv + L.states : nullptr;
+  b.table = sv ? (int*)(sv + L.table) : (int*)tb;
+  b.m = sv ? sv + L.m : mw;
+  b.cum = sv ? (float*)(sv + L.cum) : cum_ws;
+  b.segp = sv ? (float*)(sv + L.segp) : nullptr;
+  return b;
 }
 // Backward workspace: dU~ and the per-chunk state gradients, plus a full saved buffer and U for
 // the recompute path, plus two segment state buffers (R and the states entering the segments of
@@ -225,7 +267,7 @@ size_t ws_fwd(const Shape& s) {
 size_t bytes_seg_bwd(const Shape& s) { return 2 * align_up(bytes_seg_state(s)); }
 size_t ws_bwd(const Shape& s) {
   return align_up(bytes_v(s)) + align_up(bytes_states(s)) + saved_layout(s).total +
-         align_up(bytes_v(s)) + bytes_seg_bwd(s);
+         (xform(s) ? 0 : align_up(bytes_v(s))) + bytes_seg_bwd(s);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -234,35 +276,39 @@ efla_status hip_status(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_E
 
 bool empty(const Shape& s) { return s.T == 0; }
 
-// Forward stages shared by efla_fwd and the recompute path of efla_bwd. seg: bytes_seg(s)
-// of workspace for the segment-parallel scan (unused when the plan has one segment).
-// gate (null, or log-decays) selects gated EFLA, which then needs cum (bytes_cum(s)).
-// segp (null, or the saved buffer's region) receives the segments' transitions P for the
-// backward; without it they stay in the workspace.
+// Forward stages shared by efla_fwd and the recompute path of efla_bwd. b.seg: bytes_seg(s)
+// of workspace for the segment-parallel scan (unused when the plan has one segment). gate (null,
+// or log-decays) selects gated EFLA, which then needs b.cum. b.segp (null, or the saved buffer's
+// region) receives the segments' transitions P for the backward; without it they stay in the
+// workspace.
 efla_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
-                        const void* beta, void* o, unsigned char* w, unsigned char* ut,
-                        unsigned char* states, int* table, unsigned char* m, unsigned char* x,
-                        unsigned char* u, const float* h0, float* ht, unsigned char* seg,
-                        hipStream_t st, const void* gate = nullptr, float* cum = nullptr,
-                        float* segp = nullptr) {
+                        const void* beta, void* o, const FwdBufs& b, const float* h0, float* ht,
+                        hipStream_t st, const void* gate = nullptr) {
   if (s.cu) {
-    if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
+    if (efla_status r = hip_status(launch_chunk_table(s, b.table, st))) return r;
   }
-  if (efla_status r = hip_status(launch_ut_fwd(s, table, q, k, v, beta, gate, w, u, m, x,
-                                               gate ? cum : nullptr, st)))
+  const bool xf = xform(s);
+  float* ca = b.coef;
+  float* cb = xf && gate ? b.coef + coef_stride(s) : nullptr;
+  if (efla_status r = hip_status(launch_ut_fwd(s, b.table, q, k, v, beta, gate, b.w, b.u, b.m, b.x,
+                                               gate ? b.cum : nullptr, ca, cb, st)))
     return r;
-  const float* cm = gate ? cum : nullptr;
+  const float* cm = gate ? b.cum : nullptr;
+  const void* fa = xf ? (const void*)b.x : (const void*)b.w;  // X or W
+  const void* fb = xf ? v : (const void*)b.u;                 // V or U
   if (s.seg_plan <= 1)
-    return hip_status(launch_scan_fwd(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cm));
+    return hip_status(launch_scan_fwd(s, b.table, q, k, fa, fb, b.m, o, b.ut, b.states, h0, ht, st,
+                                      cm, ca, cb));
   // Segment-parallel: zero-start states R and transitions P of all segments, the sequential
   // chain S_in, then the output scan over all segments from S_in.
   const Shape sv = segment_view(s);
-  float* R = (float*)seg;
-  float* S_in = (float*)(seg + align_up(bytes_seg_state(s)));
-  float* P = segp ? segp : (float*)(seg + 2 * align_up(bytes_seg_state(s)));
-  if (efla_status r = hip_status(launch_scan_fwd_pair(sv, k, w, u, R, P, st, cm))) return r;
+  float* R = (float*)b.seg;
+  float* S_in = (float*)(b.seg + align_up(bytes_seg_state(s)));
+  float* P = b.segp ? b.segp : (float*)(b.seg + 2 * align_up(bytes_seg_state(s)));
+  if (efla_status r = hip_status(launch_scan_fwd_pair(sv, k, fa, fb, R, P, st, cm, ca, cb))) return r;
   if (efla_status r = hip_status(launch_seg_combine(s, P, R, h0, S_in, ht, st))) return r;
-  return hip_status(launch_scan_fwd(sv, table, q, k, w, u, m, o, ut, states, S_in, nullptr, st, cm));
+  return hip_status(launch_scan_fwd(sv, b.table, q, k, fa, fb, b.m, o, b.ut, b.states, S_in, nullptr,
+                                    st, cm, ca, cb));
 }
 
 }  // namespace
@@ -344,6 +390,7 @@ efla_status efla_get_saved_layout(const efla_problem* p, efla_saved_layout* out)
   out->table = L.table;
   out->m = L.m;
   out->x = L.x;
+  out->coef = L.coef;
   out->cum = L.cum;
   out->segp = L.segp;
   out->total = L.total;
@@ -377,7 +424,8 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
   if (s.cu) {
     if (efla_status r = hip_status(launch_chunk_table(s, table, st))) return r;
   }
-  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, nullptr, w, u, nullptr, nullptr, nullptr, st));
+  return hip_status(launch_ut_fwd(s, table, nullptr, k, v, beta, nullptr, w, u, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, st));
 }
 
 efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -391,23 +439,9 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
       !aligned16(saved) || !aligned16(h0) || !aligned16(ht))
     return EFLA_ERR_ALIGN;
   if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
-  const Saved L = saved_layout(s);
-  if (saved && saved_bytes < L.total) return EFLA_ERR_WORKSPACE;
-  unsigned char* wsb = (unsigned char*)ws;
-  unsigned char* u = wsb;
-  unsigned char* w_ws = wsb + align_up(bytes_v(s));
-  int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
-  unsigned char* m_ws = (unsigned char*)table_ws + align_up(bytes_table(s));
-  unsigned char* seg_ws = m_ws + align_up(bytes_m(s));
-  unsigned char* sv = (unsigned char*)saved;
-  unsigned char* w = sv ? sv + L.w : w_ws;
-  unsigned char* ut = sv ? sv + L.ut : nullptr;
-  unsigned char* states = sv ? sv + L.states : nullptr;
-  int* table = sv ? (int*)(sv + L.table) : table_ws;
-  unsigned char* m = sv ? sv + L.m : m_ws;
-  unsigned char* x = sv ? sv + L.x : nullptr;
-  return run_forward(s, q, k, v, beta, o, w, ut, states, table, m, x, u, h0, ht, seg_ws,
-                     (hipStream_t)stream, nullptr, nullptr, sv ? (float*)(sv + L.segp) : nullptr);
+  if (saved && saved_bytes < saved_layout(s).total) return EFLA_ERR_WORKSPACE;
+  return run_forward(s, q, k, v, beta, o, fwd_bufs(s, (unsigned char*)ws, (unsigned char*)saved),
+                     h0, ht, (hipStream_t)stream);
 }
 
 efla_status efla_fwd(const efla_problem* p, const void* q, const void* k, const void* v,
@@ -431,13 +465,7 @@ efla_status efla_fwd_noalloc(const efla_problem* p, const void* q, const void* k
   if (!ws) return EFLA_ERR_HIP;
   // the workspace layout of efla_fwd_state without a saved buffer; nothing in it has to start
   // at zero (every kernel writes what a later one reads)
-  unsigned char* wsb = (unsigned char*)ws;
-  unsigned char* u = wsb;
-  unsigned char* w = wsb + align_up(bytes_v(s));
-  int* table = (int*)(w + align_up(bytes_k(s)));
-  unsigned char* m = (unsigned char*)table + align_up(bytes_table(s));
-  unsigned char* seg = m + align_up(bytes_m(s));
-  return run_forward(s, q, k, v, beta, o, w, nullptr, nullptr, table, m, nullptr, u, h0, ht, seg,
+  return run_forward(s, q, k, v, beta, o, fwd_bufs(s, (unsigned char*)ws, nullptr), h0, ht,
                      (hipStream_t)stream);
 }
 
@@ -454,21 +482,9 @@ efla_status efla_fwd_gated(const efla_problem* p, const void* q, const void* k, 
       !aligned16(saved) || !aligned16(h0) || !aligned16(ht))
     return EFLA_ERR_ALIGN;
   if (ws_bytes < ws_fwd(s)) return EFLA_ERR_WORKSPACE;
-  const Saved L = saved_layout(s);
-  if (saved && saved_bytes < L.total) return EFLA_ERR_WORKSPACE;
-  unsigned char* wsb = (unsigned char*)ws;
-  unsigned char* u = wsb;
-  unsigned char* w_ws = wsb + align_up(bytes_v(s));
-  int* table_ws = (int*)(w_ws + align_up(bytes_k(s)));
-  unsigned char* m_ws = (unsigned char*)table_ws + align_up(bytes_table(s));
-  unsigned char* seg_ws = m_ws + align_up(bytes_m(s));
-  float* cum_ws = (float*)(seg_ws + bytes_seg(s));
-  unsigned char* sv = (unsigned char*)saved;
-  return run_forward(s, q, k, v, beta, o, sv ? sv + L.w : w_ws, sv ? sv + L.ut : nullptr,
-                     sv ? sv + L.states : nullptr, sv ? (int*)(sv + L.table) : table_ws,
-                     sv ? sv + L.m : m_ws, sv ? sv + L.x : nullptr, u, h0, ht, seg_ws,
-                     (hipStream_t)stream, gate, sv ? (float*)(sv + L.cum) : cum_ws,
-                     sv ? (float*)(sv + L.segp) : nullptr);
+  if (saved && saved_bytes < saved_layout(s).total) return EFLA_ERR_WORKSPACE;
+  return run_forward(s, q, k, v, beta, o, fwd_bufs(s, (unsigned char*)ws, (unsigned char*)saved),
+                     h0, ht, (hipStream_t)stream, gate);
 }
 
 }  // extern "C"
@@ -505,18 +521,21 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
   unsigned char* seg = dstates + align_up(bytes_states(s));
   const unsigned char* sv = (const unsigned char*)saved;
   if (!sv) {
+    // recompute: the forward into a saved buffer carved from the workspace; its own workspace
+    // (U for fp32, and the segment buffers) after it
     unsigned char* rec = dstates + align_up(bytes_states(s));
-    unsigned char* u = rec + L.total;
-    seg = u + align_up(bytes_v(s));
-    if (efla_status r = run_forward(s, q, k, v, beta, nullptr, rec + L.w, rec + L.ut,
-                                    rec + L.states, (int*)(rec + L.table), rec + L.m, rec + L.x,
-                                    u, h0, nullptr, seg, st, gate, (float*)(rec + L.cum),
-                                    (float*)(rec + L.segp)))
-      return r;
+    FwdBufs b = fwd_bufs(s, rec + L.total, rec);
+    b.u = xform(s) ? nullptr : rec + L.total;
+    b.seg = rec + L.total + (xform(s) ? 0 : align_up(bytes_v(s)));
+    seg = b.seg;
+    if (efla_status r = run_forward(s, q, k, v, beta, nullptr, b, h0, nullptr, st, gate)) return r;
     sv = rec;
   }
   const int* table = (const int*)(sv + L.table);
   const float* cum = gate ? (const float*)(sv + L.cum) : nullptr;
+  // the factors of the backward scan: X and alpha~ (bf16) or W (fp32)
+  const unsigned char* fa = xform(s) ? sv + L.x : sv + L.w;
+  const float* ca = xform(s) ? (const float*)(sv + L.coef) : nullptr;
   if (s.seg_plan > 1) {
     // Segment-parallel reverse scan: zero-start gradients R of all segments, the chain over
     // segments from the last (dht) to the first (dh0) with the transposed forward transitions
@@ -526,16 +545,16 @@ efla_status run_backward(const efla_problem* p, const void* q, const void* k, co
     float* R = (float*)seg;
     float* G_in = (float*)(seg + align_up(bytes_seg_state(s)));
     const float* A = (const float*)(sv + L.segp);
-    if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, sv + L.w, sv + L.m, d_o,
-                                                   nullptr, nullptr, nullptr, R, st, cum, true)))
+    if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, fa, sv + L.m, d_o, nullptr,
+                                                   nullptr, nullptr, R, st, cum, ca, true)))
       return r;
     if (efla_status r = hip_status(launch_seg_combine(s, A, R, dht, G_in, dh0, st, true, true)))
       return r;
-    if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, sv + L.w, sv + L.m, d_o, dut,
-                                                   dstates, G_in, nullptr, st, cum)))
+    if (efla_status r = hip_status(launch_scan_bwd(svw, table, q, k, fa, sv + L.m, d_o, dut,
+                                                   dstates, G_in, nullptr, st, cum, ca, false)))
       return r;
-  } else if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, sv + L.w, sv + L.m, d_o,
-                                                        dut, dstates, dht, dh0, st, cum))) {
+  } else if (efla_status r = hip_status(launch_scan_bwd(s, table, q, k, fa, sv + L.m, d_o, dut,
+                                                        dstates, dht, dh0, st, cum, ca, false))) {
     return r;
   }
   return hip_status(launch_chunk_bwd(s, table, q, k, v, beta, d_o, sv + L.ut, dut, sv + L.states,

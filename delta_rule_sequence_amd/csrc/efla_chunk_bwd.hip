@@ -40,7 +40,6 @@
 namespace efla {
 
 constexpr int kBwdThreads = 512;
-constexpr int kBwdWaves = kBwdThreads / 64;
 
 template <typename E, int DK, int DV, bool GT = false>
 struct ChunkBwdLds {

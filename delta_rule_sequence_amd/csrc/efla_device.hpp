@@ -458,6 +458,14 @@ EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld,
   }
 }
 
+// Request 64 consecutive floats (one per lane) into LDS at dst by LDS DMA: lane l's word lands
+// at dst + 4 l. No register takes the value, so nothing but the counted wait for the DMA has
+// to precede its use (a plain load followed by an LDS store makes the compiler wait for every
+// load in flight, the L2 warm-up loads included).
+EFLA_DEV void dma_vec64(unsigned char* dst, const float* __restrict__ g, int lane) {
+  __builtin_amdgcn_global_load_lds((const void*)(g + lane), (lds_void*)dst, 4, 0, 0);
+}
+
 // Wait until this wave's outstanding vector memory operations (loads, stores, LDS DMA) are
 // done: s_waitcnt vmcnt(0).
 EFLA_DEV void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -558,6 +566,21 @@ EFLA_DEV typename Mma<E>::vec aop_kc(const unsigned char* t, int b, int ks, int 
     const int r = 16 * ks + 4 * g, c = 16 * b + i;
     return f32x4{*(const float*)(t + S::off(r, c)), *(const float*)(t + S::off(r + 1, c)),
                  *(const float*)(t + S::off(r + 2, c)), *(const float*)(t + S::off(r + 3, c))};
+  }
+}
+
+// aop_kc for a plain row-major tile with leading dimension ld (no swizzle).
+template <typename E>
+EFLA_DEV typename Mma<E>::vec aop_kc_ld(const E* t, int ld, int b, int ks, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  if constexpr (sizeof(E) == 2) {
+    const int r = 32 * ks + 8 * g + (i >> 2), c = prow<E>(b, 4 * (i & 3));
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + r * ld + c));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + (r + 4) * ld + c));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const int r = 16 * ks + 4 * g, c = 16 * b + i;
+    return f32x4{t[r * ld + c], t[(r + 1) * ld + c], t[(r + 2) * ld + c], t[(r + 3) * ld + c]};
   }
 }
 

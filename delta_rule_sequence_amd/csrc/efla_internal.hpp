@@ -37,23 +37,29 @@ hipError_t launch_chunk_table(const Shape& s, int* table, hipStream_t st);
 hipError_t launch_prep(const Shape& s, const void* k, const void* beta, float* lam, float* alpha,
                        float* ex, float* dlam, hipStream_t st);
 // gate (log-decays, problem dtype, or null) selects gated EFLA; cum then receives the running
-// sums of the log-decays inside each chunk, fp32 [slots][H][64].
+// sums of the log-decays inside each chunk, fp32 [slots][H][64]. Every output may be null: W
+// and U (w, u), M, X, and the factors' per-token column scales ca = alpha~ (alpha, gated
+// alpha e^{c}) and cb = b (gated), fp32 [slots][H][64].
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
                          const void* v, const void* beta, const void* gate, void* w, void* u,
-                         void* m, void* x, float* cum, hipStream_t st);
+                         void* m, void* x, float* cum, float* ca, float* cb, hipStream_t st);
+// The chunk factors the scans read: bf16 problems X ([slots][H][64][64]) with ca, cb as
+// written by launch_ut_fwd, fp32 problems W and U. w / u below stand for X / V (the input
+// values) in the first case and W / U in the second; ca, cb are unused for fp32.
 // h0 / ht (scan_fwd) and dht / dh0 (scan_bwd): fp32 [n_seqs][H][dk][dv] per-sequence
 // states entering / leaving the sequence, or null (zero in, not written out).
 // cum (null, or the running log-decay sums of launch_ut_fwd) selects gated EFLA.
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
                            void* states, const float* h0, float* ht, hipStream_t st,
-                           const float* cum = nullptr);
+                           const float* cum, const float* ca, const float* cb);
 // For a segment view, in one launch: the zero-start state scan (final states into r, fp32
 // [n_seqs][H][dk][dv]) and the transition scan, the product over each sequence's chunks of
 // (I - K^T W) (gated: with the decays) into p, fp32 [n_seqs][H][dk][dk] (the scan with U = 0 from
 // S = I).
 hipError_t launch_scan_fwd_pair(const Shape& s, const void* k, const void* w, const void* u,
-                                float* r, float* p, hipStream_t st, const float* cum = nullptr);
+                                float* r, float* p, hipStream_t st, const float* cum,
+                                const float* ca, const float* cb);
 // Chain the segments of every sequence: S_0 = h0 (zero if null), S_{j+1} = P_j S_j + R_j;
 // writes S_j of every segment to sin ([B * seg_plan][H][dk][dv]) and the final state to ht
 // (if not null). P, R as produced by the transition and state-only scans of segment_view(s).
@@ -65,10 +71,11 @@ hipError_t launch_seg_combine(const Shape& s, const float* p, const float* r, co
                               bool transpose = false);
 // cum (null, or the saved running log-decay sums) selects gated EFLA. state_only: neither dU~
 // nor the per-chunk gradients are written, only dh0 (first pass of the segment-parallel scan).
+// w: X with ca = alpha~ (bf16) or W (fp32), as for launch_scan_fwd.
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
                            void* dstates, const float* dht, float* dh0, hipStream_t st,
-                           const float* cum = nullptr, bool state_only = false);
+                           const float* cum, const float* ca, bool state_only);
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
                          const void* beta, float* state, void* o, hipStream_t st,
                          const void* gate = nullptr);

@@ -32,16 +32,21 @@
 
 namespace efla {
 
+// XF (bf16): the stage holds K in W's place, and X and alpha~ (dU~^T W = Z^T K with
+// Z = diag(alpha~) X^T dU~, formed in registers); fp32: W, read as it is.
 template <typename E, int DK, int DV, int TV, bool GT = false>
 struct ScanBwdLds {
+  static constexpr bool XF = sizeof(E) == 2;
   static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64), LS = pitch<E>(TV);
-  // one stage: Q [64][LK], W [64][LK], M [64][LT], dO [64][LS]
+  // one stage: Q [64][LK], W or K [64][LK], M [64][LT], X [64][LT] (XF), dO [64][LS]
   static constexpr size_t oQ = 0;
   static constexpr size_t oW = oQ + 64 * LK * sizeof(E);
   static constexpr size_t oM = oW + 64 * LK * sizeof(E);
-  static constexpr size_t oO = oM + 64 * LT * sizeof(E);
+  static constexpr size_t oX = oM + 64 * LT * sizeof(E);
+  static constexpr size_t oO = oX + (XF ? 64 * LT * sizeof(E) : 0);
   static constexpr size_t oCs = oO + 64 * LS * sizeof(E);     // running log-decay sums [64] (GT)
-  static constexpr size_t stage = oCs + (GT ? 64 * 4 : 0);
+  static constexpr size_t oAl = oCs + (GT ? 64 * 4 : 0);       // alpha~ [64] (XF)
+  static constexpr size_t stage = oAl + (XF ? 64 * 4 : 0);
   // bf16 with 16-column tiles: one stage, so that two workgroups share a compute unit
   static constexpr int NSTG = (sizeof(E) == 2 && TV == 16) ? 1 : 2;
   static constexpr size_t oG = NSTG * stage;                    // G slice [DK][LS]
@@ -55,8 +60,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
     E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0,
-    const float* __restrict__ cum) {
+    const float* __restrict__ cum, const float* __restrict__ ca) {
   typedef ScanBwdLds<E, DK, DV, TV, GT> L;
+  constexpr bool XF = L::XF;
   typedef typename Mma<E>::vec V;
   constexpr int KC = Mma<E>::KC, KS = DK / KC, KT = kChunk / KC;
   constexpr int NTILE = DV / TV;
@@ -87,8 +93,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 
   constexpr bool OUT = MODE == 0;  // write dU~ and dS_c
   V kA[KS], kN[KS];
-  u32x4 qR[VQ], wR[VQ], mR[VM], oR[VO];
-  float cQ[VQ], cR = 0.f;  // gated: running log-decay sums of the Q rows / of token lane
+  u32x4 qR[VQ], wR[VQ], mR[VM], xR[VM], oR[VO];
+  float cQ[VQ], cR = 0.f, aR = 0.f;  // gated: running log-decay sums of the Q rows / of token
+                                     // lane; XF: alpha~ of token lane
 
   auto load_chunk = [&](int c) {
     const int n = min(kChunk, si.len - c * kChunk);
@@ -96,15 +103,22 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     const int ra = min(rA + (lane & 15), n - 1) - (lane & 15);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kN[ks] = frag_rm<E>(k + (r0 + ra) * DK + ks * KC, DK, lane);
+    const int64_t unit = (int64_t)(si.slot0 + c) * g.H + h;
 #pragma unroll
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / (DK / VE), n - 1), cc = (i % (DK / VE)) * VE;
       qR[it] = *(const u32x4*)(q + (r0 + r) * DK + cc);
-      wR[it] = *(const u32x4*)(w + (r0 + r) * DK + cc);
-      if constexpr (GT) cQ[it] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + r];
+      if constexpr (!XF) wR[it] = *(const u32x4*)(w + (r0 + r) * DK + cc);
+      if constexpr (GT) cQ[it] = cum[unit * kChunk + r];
     }
-    if constexpr (GT) cR = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
+    if constexpr (GT) cR = cum[unit * kChunk + lane];
+    if constexpr (XF) {  // X [64][64] of the chunk and alpha~
+      const E* xc = w + unit * kChunk * kChunk;
+#pragma unroll
+      for (int it = 0; it < VM; ++it) xR[it] = *(const u32x4*)(xc + (it * kThreads + tid) * VE);
+      aR = ca[unit * kChunk + lane];
+    }
     {  // M and dO (the dO term)
       const E* mc = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
 #pragma unroll
@@ -126,11 +140,23 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     const bool rowok = rA + (lane & 15) < n;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kA[ks] = keep_if_vec(kN[ks], rowok);
+    if constexpr (XF) {  // this wave's K rows into the K tile (W's place), rows >= n zero
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        *(V*)(sW + (rA + (lane & 15)) * L::LK + ks * KC + (lane >> 4) * (KC / 4)) = kA[ks];
+      E* sX = (E*)(st + L::oX);
+#pragma unroll
+      for (int it = 0; it < VM; ++it) {
+        const int i = (it * kThreads + tid) * VE;
+        *(u32x4*)(sX + (i / 64) * L::LT + i % 64) = xR[it];
+      }
+      if (tid < 64) ((float*)(st + L::oAl))[tid] = aR;
+    }
 #pragma unroll
     for (int it = 0; it < VQ; ++it) {
       const int i = it * kThreads + tid;
       const int r = i / (DK / VE), cc = (i % (DK / VE)) * VE;
-      *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
+      if constexpr (!XF) *(u32x4*)(sW + r * L::LK + cc) = keep_if(wR[it], r < n);
       u32x4 qv = qR[it];
       if constexpr (GT) {  // Q rows scaled by Gamma = e^c
         const float gm = exp_decay(cQ[it]);
@@ -191,7 +217,11 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
     const int n = min(kChunk, si.len - c * kChunk);
     const int64_t r0 = base + (int64_t)c * kChunk;
     const int bk = n * DK * (int)sizeof(E);
-    l2_touch<NL, kThreads>(pw, w + r0 * DK, bk, tile, NTILE, tid);
+    if constexpr (XF)
+      l2_touch<NL, kThreads>(pw, w + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                             kChunk * kChunk * (int)sizeof(E), tile, NTILE, tid);
+    else
+      l2_touch<NL, kThreads>(pw, w + r0 * DK, bk, tile, NTILE, tid);
     l2_touch<NL, kThreads>(pw + NL, k + r0 * DK, bk, tile, NTILE, tid);
     {
       l2_touch<NL, kThreads>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, tid);
@@ -245,7 +275,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kg = Mma<E>::step(kA[ks], frag_km<E>(sG + ks * KC * L::LS + 16 * nb, L::LS, lane), kg);
-        md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
+      md = mma<E, true, true>(sM + rA, L::LT, sO + 16 * nb, L::LS, round_down_kc<E>(rA), kChunk, md, lane);
       if constexpr (GT) {  // rows t of K G decay by e^{c_last - c_t}
         const float cl = sCs[n - 1];
 #pragma unroll
@@ -255,17 +285,56 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
       st_frag_t<E>(sDt + 16 * nb * L::LT + rA, L::LT, du, lane);
       if constexpr (OUT) st_frag_lds<E>(sDu + rA * L::LS + 16 * nb, L::LS, du, lane);
     }
+    // scale dO^T Q for every G^T tile of the wave: independent of dU~, so it runs before the
+    // barrier that waits for every wave's dU~
+    f32x4 ga[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wv + 4 * i, vb = t % NB, db = t / NB;
+      ga[i] = g.scale * mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
+    }
+    f32x4 al4[4];  // XF: alpha~ of the rows of Z below (four consecutive rows per tile)
+    if constexpr (XF) {
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        al4[sb] = *(const f32x4*)((const float*)(stc + L::oAl) + prow<E>(sb, 4 * (lane >> 4)));
+    }
     __syncthreads();
 
     if constexpr (OUT) s2g<E, TV>(dut + r0 * DV + v0, DV, sDu, L::LS, n, tid);
+    // XF: dU~^T W = Z^T K with Z = diag(alpha~) X^T dU~, formed by every wave for its columns
+    // (vb = wv % NB for all of its G^T tiles) with rows in prow order, packed straight into the
+    // A operand of Z^T K; row pair j of Z needs t >= 32 j (X is lower triangular).
+    V zA[KT];
+    if constexpr (XF) {
+      const int vb = wv % NB;
+      const E* sX = (const E*)(stc + L::oX);
+      f32x4 z[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        z[sb] = zero4();
+#pragma unroll
+        for (int kt = sb >> 1; kt < KT; ++kt)
+          z[sb] = Mma<E>::step(aop_kc_ld<E>(sX, L::LT, sb, kt, lane),
+                               frag_rm<E>(sDt + 16 * vb * L::LT + KC * kt, L::LT, lane), z[sb]);
+        z[sb] *= al4[sb];
+      }
+#pragma unroll
+      for (int j = 0; j < KT; ++j) zA[j] = bop_acc<E>(z, j);
+    }
     // G^T += scale dO^T Q - dU~^T W (gated: G^T <- e^{c_last} G^T + ..., Q pre-scaled)
     const float gC = GT ? exp_decay(sCs[n - 1]) : 1.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
-      const f32x4 a = mma<E, true, true>(sO + 16 * vb, L::LS, sQ + 16 * db, L::LK, 0, kChunk, zero4(), lane);
-      const f32x4 b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
-      Gt[i] = gC * Gt[i] + (g.scale * a - b);
+      f32x4 b = zero4();
+      if constexpr (XF) {
+#pragma unroll
+        for (int j = 0; j < KT; ++j) b = Mma<E>::step(zA[j], frag_km<E>(sW + KC * j * L::LK + 16 * db, L::LK, lane), b);
+      } else {
+        b = mma<E, false, true>(sDt + 16 * vb * L::LT, L::LT, sW + 16 * db, L::LK, 0, kChunk, zero4(), lane);
+      }
+      Gt[i] = gC * Gt[i] + (ga[i] - b);
     }
     if constexpr (L::NSTG == 1) __syncthreads();  // every wave is done with the stage
     if (more) commit_chunk(c - 1, smem + (L::NSTG == 2 ? ((c - 1) & 1) : 0) * L::stage);
@@ -294,15 +363,16 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && TV == 16) ? 2 : 1) voi
 template <typename E, int DK, int DV, bool GT = false>
 struct ScanBwdDmaLds {
   static constexpr int TV = 32;
-  typedef Swz<E, DK> SK;  // K, Q, W [64][DK]
-  typedef Swz<E, 64> SM;  // M [64][64]
+  typedef Swz<E, DK> SK;  // K, Q [64][DK]
+  typedef Swz<E, 64> SM;  // X, M [64][64]
   typedef Swz<E, TV> SO;  // dO [64][TV] (this tile's columns)
   static constexpr int LS = pitch<E>(TV), LT = pitch<E>(64);
-  static constexpr size_t oK = 0, oQ = oK + SK::BYTES, oW = oQ + SK::BYTES, oM = oW + SK::BYTES;
+  static constexpr size_t oK = 0, oQ = oK + SK::BYTES, oX = oQ + SK::BYTES, oM = oX + SM::BYTES;
   static constexpr size_t oO = oM + SM::BYTES;
   static constexpr size_t oCs = oO + SO::BYTES;  // running log-decay sums c [64] (GT)
   static constexpr size_t oGm = oCs + 64 * 4;     // Gamma = e^c [64] (GT)
-  static constexpr size_t stage = oCs + (GT ? 2 * 64 * 4 : 0);
+  static constexpr size_t oAl = oCs + (GT ? 2 * 64 * 4 : 0);  // alpha~ [64]
+  static constexpr size_t stage = oAl + 64 * 4;
   static constexpr size_t oG = 2 * stage;                   // G slice [DK][LS]
   static constexpr size_t oDt = oG + DK * LS * sizeof(E);   // dU~^T [TV][LT]
   static constexpr size_t oDu = oDt + TV * LT * sizeof(E);  // dU~ staging [64][LS]
@@ -313,10 +383,10 @@ constexpr int kScanBwdDmaThreads = 6 * 64;  // four compute waves, the loader an
 
 template <typename E, int DK, int DV, bool GT, int MODE>
 __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
-    Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
+    Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ x,
     const E* __restrict__ m, const E* __restrict__ d_o, E* __restrict__ dut,
     E* __restrict__ dstates, const float* __restrict__ dht, float* __restrict__ dh0,
-    const float* __restrict__ cum) {
+    const float* __restrict__ cum, const float* __restrict__ ca) {
   typedef ScanBwdDmaLds<E, DK, DV, GT> L;
   typedef typename Mma<E>::vec V;
   constexpr int TV = L::TV, LS = L::LS, LT = L::LT;
@@ -347,10 +417,10 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   auto tiles = [&](int c) { return smem + (c & 1) * L::stage; };
 
   constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + NTILE * 64 - 1) / (NTILE * 64);
-  constexpr int NWARM = NL * 5;  // warm-up loads issued after each DMA: W, K, Q, M, dO
+  constexpr int NWARM = NL * 5;  // warm-up loads issued after each DMA: X, K, Q, M, dO
   static_assert(NWARM <= 15, "vmcnt field");
+  static_assert(sizeof(E) == 2, "bf16 tiles (the transposed products use 32-wide steps)");
   if (wv == 4) {  // ---- loader wave
-    float cumv = 0.f;  // gated: the chunk's running log-decay sum of token lane, on its way to LDS
     int pw[5 * NL];
 #pragma unroll
     for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
@@ -358,7 +428,8 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       const int n = rows_of(c);
       const int64_t r0 = base + (int64_t)c * kChunk;
       const int bk = n * DK * (int)sizeof(E);
-      l2_touch<NL>(pw, w + r0 * DK, bk, tile, NTILE, lane);
+      l2_touch<NL>(pw, x + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                   kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
       l2_touch<NL>(pw + NL, k + r0 * DK, bk, tile, NTILE, lane);
       {
         l2_touch<NL>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, lane);
@@ -373,30 +444,32 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       unsigned char* st = tiles(c);
       const int n = rows_of(c);
       const int64_t r0 = base + (int64_t)c * kChunk;
+      const int64_t unit = (int64_t)(si.slot0 + c) * g.H + h;
       dma_tile<E, DK, 1>(st + L::oK, k + r0 * DK, DK, n, 0, lane);
-      dma_tile<E, DK, 1>(st + L::oW, w + r0 * DK, DK, n, 0, lane);
+      dma_tile<E, 64, 1>(st + L::oX, x + unit * kChunk * kChunk, kChunk, kChunk, 0, lane);
       {  // Q, M and dO (the dO term)
         dma_tile<E, DK, 1>(st + L::oQ, q + r0 * DK, DK, n, 0, lane);
         dma_tile<E, 64, 1>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
                            kChunk, kChunk, 0, lane);
         dma_tile<E, TV, 1>(st + L::oO, d_o + r0 * DV + v0, DV, n, 0, lane);
       }
-      // 64 floats, one plain load per lane; stored to LDS only after the wait for the DMA, since
-      // using the value earlier would wait for every DMA issued before it
-      if constexpr (GT) cumv = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
+      // the per-token vectors (64 floats each) by LDS DMA as well: alpha~, and the running
+      // log-decay sums (gated)
+      dma_vec64(st + L::oAl, ca + unit * kChunk, lane);
+      if constexpr (GT) dma_vec64(st + L::oCs, cum + unit * kChunk, lane);
+      // the counted waits assume every request above is issued before the warm-up loads that
+      // follow: keep the scheduler from moving any of them past this point
+      __builtin_amdgcn_sched_barrier(0);
     };
-    auto finish = [&](int c) {  // after the wait: the decay sums, and rows >= n cleared
+    auto finish = [&](int c) {  // after the wait: Gamma = e^c (gated), rows >= n cleared
       unsigned char* st = tiles(c);
-      if constexpr (GT) {
-        ((float*)(st + L::oCs))[lane] = cumv;
-        ((float*)(st + L::oGm))[lane] = exp_decay(cumv);
-      }
+      if constexpr (GT)
+        ((float*)(st + L::oGm))[lane] = exp_decay(((const float*)(st + L::oCs))[lane]);
       const int n = rows_of(c);
       if (n >= kChunk) return;  // whole rows are cleared: the swizzle stays inside a row
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int b = n * L::SK::RB + 16 * lane; b < kChunk * L::SK::RB; b += 16 * 64) {
         *(u32x4*)(st + L::oK + b) = z;
-        *(u32x4*)(st + L::oW + b) = z;
         *(u32x4*)(st + L::oQ + b) = z;
       }
         for (int b = n * L::SO::RB + 16 * lane; b < kChunk * L::SO::RB; b += 16 * 64)
@@ -474,6 +547,10 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
     V kA[KS];  // this wave's K rows (A operand of K G)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kA[ks] = frag_rm_sw<E, DK>(st + L::oK, rA, ks * KC, lane);
+    // alpha~ of the rows of Z below (four consecutive rows per tile: one 16-byte read each)
+    f32x4 al4[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) al4[sb] = *(const f32x4*)((const float*)(st + L::oAl) + prow<E>(sb, 4 * (lane >> 4)));
     // dU~ = scale M^T dO + K G for this wave's rows (tokens).
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -495,29 +572,57 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       st_frag_t<E>(sDt + 16 * nb * LT + rA, LT, du, lane);
       if constexpr (OUT) st_frag_lds<E>(sDu + rA * LS + 16 * nb, LS, du, lane);
     }
-    __syncthreads();
-
-    // G^T += scale dO^T Q - dU~^T W (gated: G^T <- e^{c_last} G^T + ..., Q scaled by Gamma)
-    const float gC = GT ? exp_decay(sCs[n - 1]) : 1.f;
+    // scale dO^T Q for every G^T tile of the wave (gated: Q scaled by Gamma): independent of
+    // dU~, so it runs before the barrier that waits for every wave's dU~
+    f32x4 ga[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int t = wv + 4 * i, vb = t % NB, db = t / NB;
-      f32x4 a = zero4(), b = zero4();
+      f32x4 a = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < kChunk; k0 += KC) {
-        {
-          V qf = frag_km_sw<E, DK>(st + L::oQ, k0, 16 * db, lane);
-          if constexpr (GT) {  // element e is token k0 + KC/4 (lane >> 4) + e
-            const int t0 = k0 + (KC / 4) * (lane >> 4);
+        V qf = frag_km_sw<E, DK>(st + L::oQ, k0, 16 * db, lane);
+        if constexpr (GT) {  // element e is token k0 + KC/4 (lane >> 4) + e
+          const int t0 = k0 + (KC / 4) * (lane >> 4);
 #pragma unroll
-            for (int e = 0; e < KC / 4; ++e) qf[e] = to_e<E>(to_f(qf[e]) * sGm[t0 + e]);
-          }
-          a = Mma<E>::step(frag_km_sw<E, TV>(st + L::oO, k0, 16 * vb, lane), qf, a);
+          for (int e = 0; e < KC / 4; ++e) qf[e] = to_e<E>(to_f(qf[e]) * sGm[t0 + e]);
         }
-        b = Mma<E>::step(frag_rm<E>(sDt + 16 * vb * LT + k0, LT, lane),
-                         frag_km_sw<E, DK>(st + L::oW, k0, 16 * db, lane), b);
+        a = Mma<E>::step(frag_km_sw<E, TV>(st + L::oO, k0, 16 * vb, lane), qf, a);
       }
-      Gt[i] = gC * Gt[i] + (g.scale * a - b);
+      ga[i] = g.scale * a;
+    }
+    __syncthreads();
+
+    // dU~^T W with W = X diag(alpha~) K is Z^T K, Z = diag(alpha~) X^T dU~: the wave forms Z for
+    // its 16 columns (every G^T tile of the wave has vb = wv % NB), rows in prow order, so that
+    // it packs straight into the A operand of Z^T K. Row pair j of Z needs t >= 32 j (X is
+    // lower triangular): 6 products.
+    V zA[kChunk / KC];
+    {
+      const int vb = wv % NB;
+      f32x4 z[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        z[sb] = zero4();
+#pragma unroll
+        for (int kt = sb >> 1; kt < kChunk / KC; ++kt)
+          z[sb] = Mma<E>::step(aop_kc<E, 64>(st + L::oX, sb, kt, lane),
+                               frag_rm<E>(sDt + 16 * vb * LT + KC * kt, LT, lane), z[sb]);
+        z[sb] *= al4[sb];
+      }
+#pragma unroll
+      for (int j = 0; j < kChunk / KC; ++j) zA[j] = bop_acc<E>(z, j);
+    }
+    // G^T <- gC G^T + scale dO^T Q - Z^T K (gated: gC = e^{c_last})
+    const float gC = GT ? exp_decay(sCs[n - 1]) : 1.f;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wv + 4 * i, db = t / NB;
+      f32x4 b = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < kChunk; k0 += KC)
+        b = Mma<E>::step(zA[k0 / KC], frag_km_sw<E, DK>(st + L::oK, k0, 16 * db, lane), b);
+      Gt[i] = gC * Gt[i] + (ga[i] - b);
     }
   }
   if (dh0) {  // gradient at the state entering the sequence
@@ -532,7 +637,7 @@ template <typename E, int DK, int DV, bool GT, int MODE>
 static hipError_t scan_bwd_dma_run(const Shape& s, const int* table, const void* q, const void* k,
                                    const void* w, const void* m, const void* d_o, void* dut,
                                    void* dstates, const float* dht, float* dh0, hipStream_t st,
-                                   const float* cum) {
+                                   const float* cum, const float* ca) {
   typedef ScanBwdDmaLds<E, DK, DV, GT> L;
   static bool attr = false;
   if (!attr) {
@@ -546,7 +651,7 @@ static hipError_t scan_bwd_dma_run(const Shape& s, const int* table, const void*
   prof_begin(st);
   hipLaunchKernelGGL((scan_bwd_dma_kernel<E, DK, DV, GT, MODE>), dim3((unsigned)blocks), dim3(kScanBwdDmaThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum, ca);
   hipError_t e = hipGetLastError();
   static const char* const names[2][2] = {{"scan_bwd", "scan_bwd_state"},
                                            {"scan_bwd_gated", "scan_bwd_state_gated"}};
@@ -558,7 +663,7 @@ template <typename E, int DK, int DV, int TV, bool GT, int MODE>
 static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* m, const void* d_o, void* dut,
                                void* dstates, const float* dht, float* dh0, hipStream_t st,
-                               const float* cum) {
+                               const float* cum, const float* ca) {
   typedef ScanBwdLds<E, DK, DV, TV, GT> L;
   static bool attr = false;
   if (!attr) {
@@ -572,7 +677,7 @@ static hipError_t scan_bwd_run(const Shape& s, const int* table, const void* q, 
   prof_begin(st);
   hipLaunchKernelGGL((scan_bwd_kernel<E, DK, DV, TV, GT, MODE>), dim3((unsigned)blocks), dim3(kThreads),
                      L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)w,
-                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum);
+                     (const E*)m, (const E*)d_o, (E*)dut, (E*)dstates, dht, dh0, cum, ca);
   hipError_t e = hipGetLastError();
   static const char* const names[2][2] = {{"scan_bwd", "scan_bwd_state"},
                                            {"scan_bwd_gated", "scan_bwd_state_gated"}};
@@ -584,29 +689,29 @@ template <typename E, int DK, int DV, int TV, int MODE>
 static hipError_t scan_bwd_mode(const Shape& s, const int* table, const void* q, const void* k,
                                 const void* w, const void* m, const void* d_o, void* dut,
                                 void* dstates, const float* dht, float* dh0, hipStream_t st,
-                                const float* cum) {
+                                const float* cum, const float* ca) {
   if (cum) {
     if constexpr (sizeof(E) == 2 && TV == 32)
-      return scan_bwd_dma_run<E, DK, DV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+      return scan_bwd_dma_run<E, DK, DV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca);
     else if constexpr (sizeof(E) == 2)
-      return scan_bwd_run<E, DK, DV, TV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+      return scan_bwd_run<E, DK, DV, TV, true, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca);
     else
       return hipErrorInvalidValue;
   }
   if constexpr (sizeof(E) == 2 && TV == 32)
-    return scan_bwd_dma_run<E, DK, DV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+    return scan_bwd_dma_run<E, DK, DV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca);
   else
-    return scan_bwd_run<E, DK, DV, TV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+    return scan_bwd_run<E, DK, DV, TV, false, MODE>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca);
 }
 
 template <typename E, int DK, int DV, int TV>
 static hipError_t scan_bwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* m, const void* d_o, void* dut,
                               void* dstates, const float* dht, float* dh0, hipStream_t st,
-                              const float* cum, int mode) {
+                              const float* cum, const float* ca, int mode) {
   if (mode == 1)
-    return scan_bwd_mode<E, DK, DV, TV, 1>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
-  return scan_bwd_mode<E, DK, DV, TV, 0>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum);
+    return scan_bwd_mode<E, DK, DV, TV, 1>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca);
+  return scan_bwd_mode<E, DK, DV, TV, 0>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca);
 }
 
 size_t lds_scan_bwd(Dt dt, int dk, int dv) {
@@ -624,10 +729,10 @@ size_t lds_scan_bwd(Dt dt, int dk, int dv) {
 hipError_t launch_scan_bwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* m, const void* d_o, void* dut,
                            void* dstates, const float* dht, float* dh0, hipStream_t st,
-                           const float* cum, bool state_only) {
+                           const float* cum, const float* ca, bool state_only) {
   const int mode = state_only ? 1 : 0;
 #define EFLA_SB(E_, DK_, DV_, TV_) \
-  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, mode)
+  return scan_bwd_go<E_, DK_, DV_, TV_>(s, table, q, k, w, m, d_o, dut, dstates, dht, dh0, st, cum, ca, mode)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SB(__bf16, 64, 64, 16);
     if (s.dk == 128 && s.dv == 64) EFLA_SB(__bf16, 128, 64, 16);

@@ -5,12 +5,15 @@
 // d_k x TV slice of the state (TV = 16 columns per wave):
 //   U~ = U - W S,   O = scale (Q S + M U~),   S <- S + K^T U~,
 // with M = tril(Q K^T) from the UT kernel. The diagonal of tril is kept because token t
-// reads the state after its own update.
+// reads the state after its own update. bf16 problems read the UT factor X = (I + A)^{-1}, V
+// and the per-token scales alpha~ (gated alpha e^{c}) and b instead of W = X diag(alpha~) K
+// and U = X diag(b) V, and form U~ = X Y with Y = diag(b) V - diag(alpha~) K S: one more short
+// product per chunk (X is lower triangular) for a quarter of W's bytes and no U at all.
 //
 // Each compute wave owns 16 columns of S for the whole sequence and keeps them in fp32 MFMA
 // accumulators. Products whose contraction runs over the rows of an accumulator take that
-// accumulator directly as their B operand, so the recurrence S -> W S -> U~ -> K^T U~ -> S
-// runs inside one wave's registers with no LDS round trip. Accumulator rows (of S, and the
+// accumulator directly as their B operand, so the recurrence S -> W S (or K S -> Y -> X Y) ->
+// U~ -> K^T U~ -> S runs inside one wave's registers with no LDS round trip. Accumulator rows (of S, and the
 // token rows of U~ and O) are numbered in the contiguous-contraction order (prow), so every
 // A operand from LDS is a single 16-byte read. Two further waves move the data, each in a loop
 // of its own with the same barrier sequence: the loader wave fills swizzled LDS tiles of W, Q,
@@ -23,21 +26,25 @@ namespace efla {
 
 // WO: O is written (Q and M are staged); WSV: U~ and the chunk states are written. The
 // output-free modes (the zero-start and transition scans of the segment-parallel forward) stage
-// only W, K and U, so two of their workgroups fit on a compute unit.
+// only the factor, K and U (or V), so two of their workgroups fit on a compute unit.
+// XF (bf16): the factor tile is X [64][64] and the per-token scales alpha~ (and b, gated) are
+// staged; fp32: the factor tile is W [64][DK] (the fp32 tiles leave no room for the X form).
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool GT = false>
 struct ScanFwdLds {
+  static constexpr bool XF = sizeof(E) == 2;
   static constexpr int TV = 16 * NWC;
   static constexpr int NWL = 1;  // loader waves (one; a second wave stores the outputs)
   typedef Swz<E, DK> SK;
   typedef Swz<E, 64> SM;
   typedef Swz<E, TV, 2> SU;  // read in accumulator layout
-  static constexpr size_t oW = 0;                              // W  [64][DK]
-  static constexpr size_t oK = oW + SK::BYTES;                 // K  [64][DK]
-  static constexpr size_t oU = oK + SK::BYTES;                 // U  [64][TV] (this tile's columns)
+  static constexpr size_t oW = 0;                              // X [64][64] (XF) or W [64][DK]
+  static constexpr size_t oK = oW + (XF ? SM::BYTES : SK::BYTES);  // K  [64][DK]
+  static constexpr size_t oU = oK + SK::BYTES;                 // V (XF) or U [64][TV] (this tile's columns)
   static constexpr size_t oQ = oU + SU::BYTES;                 // Q  [64][DK] (WO)
   static constexpr size_t oM = oQ + (WO ? SK::BYTES : 0);      // M  [64][64] (WO)
   static constexpr size_t oC = oM + (WO ? SM::BYTES : 0);      // running log-decay sums [64] (gated)
-  static constexpr size_t stage = oC + (GT ? 64 * 4 : 0);
+  static constexpr size_t oA = oC + (GT ? 64 * 4 : 0);         // alpha~ [64], then b [64] (XF, gated)
+  static constexpr size_t stage = oA + (XF ? (GT ? 2 : 1) * 64 * 4 : 0);
   // output staging (layout SU): O [64][TV] (WO), U~ [64][TV] and S [DK][TV] (WSV); two buffers
   static constexpr size_t gO = 0, gUt = WO ? SU::BYTES : 0, gS = gUt + (WSV ? SU::BYTES : 0);
   static constexpr size_t sstage = gS + (WSV ? (size_t)DK * SU::RB : 0);
@@ -52,17 +59,20 @@ struct ScanFwdLds {
 // S <- e^{c_last} S + K^T diag(e^{c_last - c}) U~; the decays are applied to accumulators.
 // PM: transition mode for the segment-parallel scan. The chunk step is affine in the state,
 // S <- (I - K^T W) S + K^T U, so running it with U = 0 from S = I (DV = DK) leaves in ht the
-// product of the (I - K^T W) over the sequence; U is neither read nor needed.
+// product of the (I - K^T W) over the sequence; U (V) is neither read nor needed.
+// Factors: bf16 (XF) w = X [slots][H][64][64], u = V [B][H][T][DV], ca = alpha~ and cb = b
+// (gated) [slots][H][64]; fp32 w = W [B][H][T][DK], u = U [B][H][T][DV].
 // The scan of one workgroup; bid plays the role of the block index.
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
 __device__ __forceinline__ void scan_fwd_body(
     int bid, Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
     E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
-    const float* __restrict__ cum) {
+    const float* __restrict__ cum, const float* __restrict__ ca, const float* __restrict__ cb) {
   typedef ScanFwdLds<E, DK, DV, NWC, WO, WSV, GT> L;
   typedef typename L::SU SU;
   typedef typename Mma<E>::vec V;
+  constexpr bool XF = L::XF;
   constexpr int TV = L::TV, NWL = L::NWL, NTILE = DV / TV, KC = Mma<E>::KC;
   constexpr int NBK = DK / 16;                 // accumulator tiles of the state slice
   constexpr int KSK = DK / KC, KST = kChunk / KC;
@@ -107,17 +117,24 @@ __device__ __forceinline__ void scan_fwd_body(
     unsigned char* st = smem + slot * L::stage;
     const int n = rows_of(c);
     const int64_t r0 = base + (int64_t)c * kChunk;
-    dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
+    const int64_t unit = (int64_t)(si.slot0 + c) * g.H + h;
+    if constexpr (XF) dma_tile<E, 64, NWL>(st + L::oW, w + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
+    else dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
     if constexpr (!PM) dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
     dma_tile<E, DK, NWL>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
     if constexpr (WO) {
       dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
-      dma_tile<E, 64, NWL>(st + L::oM, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                           kChunk, kChunk, wl, lane);
+      dma_tile<E, 64, NWL>(st + L::oM, m + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
     }
-    if constexpr (GT) {  // 64 floats: one plain load per lane of the loader wave
-      if (wl == 0) ((float*)(st + L::oC))[lane] = cum[((int64_t)(si.slot0 + c) * g.H + h) * kChunk + lane];
+    // the per-token vectors (64 floats each) by LDS DMA as well
+    if constexpr (GT) dma_vec64(st + L::oC, cum + unit * kChunk, lane);
+    if constexpr (XF) {
+      dma_vec64(st + L::oA, ca + unit * kChunk, lane);
+      if constexpr (GT) dma_vec64(st + L::oA + 64 * 4, cb + unit * kChunk, lane);
     }
+    // the counted wait assumes every request above is issued before the warm-up loads that
+    // follow: keep the scheduler from moving any of them past this point
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto copy_out = [&](int c) {  // staged outputs of chunk c -> global memory, 16-byte rows
     const unsigned char* stg = smem + L::oStg + (c & 1) * L::sstage;
@@ -172,13 +189,14 @@ __device__ __forceinline__ void scan_fwd_body(
     const int n = rows_of(c);
     // Operands that do not depend on this chunk's results, requested before any product so
     // that their LDS latency overlaps.
-    V aw[4][KSK], aq[4][KSK];
+    // aw: rows of W (fp32), or of K for the product K S (XF); ax: X for U~ = X Y (XF)
+    V aw[4][KSK], aq[4][KSK], ax[4][KST];
     E uv[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
-        aw[rb][ks] = aop_rc<E, DK>(st + L::oW, rb, ks, lane);
+        aw[rb][ks] = aop_rc<E, DK>(st + (XF ? L::oK : L::oW), rb, ks, lane);
         if constexpr (WO) aq[rb][ks] = aop_rc<E, DK>(st + L::oQ, rb, ks, lane);
       }
 #pragma unroll
@@ -212,7 +230,7 @@ __device__ __forceinline__ void scan_fwd_body(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // W S and P = Q S
+    // W S (XF: K S) and P = Q S
     f32x4 ws[4], oa[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -231,6 +249,13 @@ __device__ __forceinline__ void scan_fwd_body(
         for (int i = 0; i < 4; ++i) oa[rb][i] *= gam[rb][i];
     }
     V ak[NBK][KST], am[4][KST];
+    if constexpr (XF) {  // requested while K S runs (with aw and aq issued, registers are free)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks)
+          if (KC * ks <= 16 * rb + 15) ax[rb][ks] = aop_rc<E, 64>(st + L::oW, rb, ks, lane);
+    }
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -244,13 +269,38 @@ __device__ __forceinline__ void scan_fwd_body(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // U~ = U - W S (rows past the end of the sequence zeroed)
+    // U~ = U - W S (rows past the end of the sequence zeroed); XF: U~ = X Y with
+    // Y = diag(b) V - diag(alpha~) K S (X is lower triangular: row blocks 0-1 need one step)
     f32x4 uta[4];
+    if constexpr (XF) {
+      // the four rows prow(rb, g4 + i), i < 4, are consecutive: one 16-byte read of each scale
+      const float* av = (const float*)(st + L::oA);
+      f32x4 y[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 al = *(const f32x4*)(av + prow<E>(rb, g4));
+        const f32x4 bl = GT ? *(const f32x4*)(av + 64 + prow<E>(rb, g4)) : al;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        uta[rb][i] = prow<E>(rb, g4 + i) < n ? to_f(uv[rb][i]) - ws[rb][i] : 0.f;
+        for (int i = 0; i < 4; ++i)
+          y[rb][i] = prow<E>(rb, g4 + i) < n ? bl[i] * to_f(uv[rb][i]) - al[i] * ws[rb][i] : 0.f;
+      }
+      V yb[KST];
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) yb[ks] = bop_acc<E>(y, ks);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        uta[rb] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks)
+          if (KC * ks <= 16 * rb + 15) uta[rb] = Mma<E>::step(ax[rb][ks], yb[ks], uta[rb]);
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          uta[rb][i] = prow<E>(rb, g4 + i) < n ? to_f(uv[rb][i]) - ws[rb][i] : 0.f;
+    }
     V ub[KST], ubd[KST];
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) ub[ks] = bop_acc<E>(uta, ks);
@@ -309,7 +359,11 @@ __device__ __forceinline__ void scan_fwd_body(
     auto warm = [&](int c) {
       const int n = rows_of(c);
       const int64_t r0 = base + (int64_t)c * kChunk;
-      l2_touch<NL>(pw, w + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
+      if constexpr (XF)
+        l2_touch<NL>(pw, w + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+      else
+        l2_touch<NL>(pw, w + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
       l2_touch<NL>(pw + NL, k + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
       if constexpr (WO) {
         l2_touch<NL>(pw + 2 * NL, q + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
@@ -318,14 +372,15 @@ __device__ __forceinline__ void scan_fwd_body(
       }
       if constexpr (!PM) l2_touch<NL>(pw + 4 * NL, u + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
     };
-    // warm-up loads issued after each DMA: W and K, Q and M with the output, U unless PM
+    // warm-up loads issued after each DMA: the factor (W or X) and K, Q and M with the output,
+    // U (or V) unless PM
     constexpr int NWARM = NL * (2 + (WO ? 2 : 0) + (PM ? 0 : 1));
     static_assert(NWARM <= 15, "vmcnt field");
     issue(0, 0);
     warm(min(1, nchunks - 1));
     for (int c = 0; c < nchunks; ++c) {
-      // vmcnt(NWARM), lgkmcnt(0): chunk c's DMA has landed (only the younger warm-up loads may
-      // still be in flight), and so has the gated loader's LDS store
+      // vmcnt(NWARM): chunk c's DMA has landed (only the younger warm-up loads may still be in
+      // flight)
       __builtin_amdgcn_s_waitcnt(0x0070 | NWARM);
       __builtin_amdgcn_s_barrier();
       // after the last chunk the request repeats it into the stage that chunk c + 1 would use,
@@ -365,8 +420,9 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
     const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
     E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
-    const float* __restrict__ cum) {
-  scan_fwd_body<E, DK, DV, NWC, WO, WSV, PM, GT>(blockIdx.x, g, q, k, w, u, m, o, ut, states, h0, ht, cum);
+    const float* __restrict__ cum, const float* __restrict__ ca, const float* __restrict__ cb) {
+  scan_fwd_body<E, DK, DV, NWC, WO, WSV, PM, GT>(blockIdx.x, g, q, k, w, u, m, o, ut, states, h0, ht,
+                                                 cum, ca, cb);
 }
 
 // The two independent first passes of the segment-parallel forward in one launch: blocks
@@ -376,18 +432,20 @@ __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
 template <typename E, int DK, int DV, int NWC, bool GT>
 __global__ __launch_bounds__(64 * NWC + 128, 2) void scan_fwd_pair_kernel(
     Geom g, int nr, const E* __restrict__ k, const E* __restrict__ w, const E* __restrict__ u,
-    float* __restrict__ R, float* __restrict__ P, const float* __restrict__ cum) {
+    float* __restrict__ R, float* __restrict__ P, const float* __restrict__ cum,
+    const float* __restrict__ ca, const float* __restrict__ cb) {
   if ((int)blockIdx.x < nr)
     scan_fwd_body<E, DK, DV, NWC, false, false, false, GT>(blockIdx.x, g, nullptr, k, w, u, nullptr, nullptr,
-                                                          nullptr, nullptr, nullptr, R, cum);
+                                                          nullptr, nullptr, nullptr, R, cum, ca, cb);
   else
     scan_fwd_body<E, DK, DK, NWC, false, false, true, GT>(blockIdx.x - nr, g, nullptr, k, w, nullptr, nullptr,
-                                                         nullptr, nullptr, nullptr, nullptr, P, cum);
+                                                         nullptr, nullptr, nullptr, nullptr, P, cum, ca, cb);
 }
 
 template <typename E, int DK, int DV, int NWC, bool GT>
 static hipError_t scan_fwd_pair_run(const Shape& s, const void* k, const void* w, const void* u,
-                                    float* R, float* P, hipStream_t st, const float* cum) {
+                                    float* R, float* P, hipStream_t st, const float* cum,
+                                    const float* ca, const float* cb) {
   typedef ScanFwdLds<E, DK, DV, NWC, false, false, GT> LR;
   typedef ScanFwdLds<E, DK, DK, NWC, false, false, GT> LP;
   constexpr size_t bytes = LR::bytes > LP::bytes ? LR::bytes : LP::bytes;
@@ -404,7 +462,7 @@ static hipError_t scan_fwd_pair_run(const Shape& s, const void* k, const void* w
   prof_begin(st);
   hipLaunchKernelGGL((scan_fwd_pair_kernel<E, DK, DV, NWC, GT>), dim3((unsigned)(nr + np)),
                      dim3(64 * NWC + 128), bytes, st, make_geom(s, nullptr), (int)nr, (const E*)k,
-                     (const E*)w, (const E*)u, R, P, cum);
+                     (const E*)w, (const E*)u, R, P, cum, ca, cb);
   hipError_t e = hipGetLastError();
   prof_end(GT ? "scan_fwd_state_transition_gated" : "scan_fwd_state_transition", st);
   return e;
@@ -414,7 +472,7 @@ template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM = fals
 static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
                                const void* w, const void* u, const void* m, void* o, void* ut,
                                void* states, const float* h0, float* ht, hipStream_t st,
-                               const float* cum = nullptr) {
+                               const float* cum, const float* ca, const float* cb) {
   typedef ScanFwdLds<E, DK, DV, NWC, WO, WSV, GT> L;
   static_assert(L::bytes <= 160 * 1024, "LDS budget");
   static bool attr = false;
@@ -429,7 +487,7 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
   prof_begin(st);
   hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM, GT>), dim3((unsigned)blocks),
                      dim3(64 * NWC + 128), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
-                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht, cum);
+                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht, cum, ca, cb);
   hipError_t e = hipGetLastError();
   prof_end(PM ? (GT ? "scan_fwd_transition_gated" : "scan_fwd_transition")
              : WO || WSV ? (GT ? "scan_fwd_gated" : "scan_fwd") : (GT ? "scan_fwd_state_gated" : "scan_fwd_state"),
@@ -443,30 +501,26 @@ template <typename E, int DK, int DV, int NWC>
 static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
                               const void* w, const void* u, const void* m, void* o, void* ut,
                               void* states, const float* h0, float* ht, hipStream_t st,
-                              const float* cum) {
+                              const float* cum, const float* ca, const float* cb) {
   const bool wsv = ut && states;
+#define EFLA_SFR(WO_, WSV_, GT_) \
+  return scan_fwd_run<E, DK, DV, NWC, WO_, WSV_, false, GT_>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum, ca, cb)
   if (cum) {  // gated
     if constexpr (sizeof(E) == 2) {
-      if (o && wsv)
-        return scan_fwd_run<E, DK, DV, NWC, true, true, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
-      if (wsv)
-        return scan_fwd_run<E, DK, DV, NWC, false, true, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
-      if (o)
-        return scan_fwd_run<E, DK, DV, NWC, true, false, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
-      if (ht)
-        return scan_fwd_run<E, DK, DV, NWC, false, false, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum);
+      if (o && wsv) EFLA_SFR(true, true, true);
+      if (wsv) EFLA_SFR(false, true, true);
+      if (o) EFLA_SFR(true, false, true);
+      if (ht) EFLA_SFR(false, false, true);
       return hipSuccess;
     } else {
       return hipErrorInvalidValue;  // the fp32 tiles leave no LDS room for the decays
     }
   }
-  if (o && wsv)
-    return scan_fwd_run<E, DK, DV, NWC, true, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
-  if (o) return scan_fwd_run<E, DK, DV, NWC, true, false>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
-  if (wsv)
-    return scan_fwd_run<E, DK, DV, NWC, false, true>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
-  if (ht)
-    return scan_fwd_run<E, DK, DV, NWC, false, false>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st);
+  if (o && wsv) EFLA_SFR(true, true, false);
+  if (o) EFLA_SFR(true, false, false);
+  if (wsv) EFLA_SFR(false, true, false);
+  if (ht) EFLA_SFR(false, false, false);
+#undef EFLA_SFR
   return hipSuccess;
 }
 
@@ -487,9 +541,9 @@ size_t lds_scan_fwd(Dt dt, int dk, int dv) {
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
                            const void* w, const void* u, const void* m, void* o, void* ut,
                            void* states, const float* h0, float* ht, hipStream_t st,
-                           const float* cum) {
+                           const float* cum, const float* ca, const float* cb) {
 #define EFLA_SF(E_, DK_, DV_, NWC_) \
-  return scan_fwd_go<E_, DK_, DV_, NWC_>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum)
+  return scan_fwd_go<E_, DK_, DV_, NWC_>(s, table, q, k, w, u, m, o, ut, states, h0, ht, st, cum, ca, cb)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_SF(__bf16, 64, 64, 2);
     if (s.dk == 64 && s.dv == 128) EFLA_SF(__bf16, 64, 128, 2);
@@ -501,9 +555,10 @@ hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, cons
 }
 
 hipError_t launch_scan_fwd_pair(const Shape& s, const void* k, const void* w, const void* u,
-                                float* r, float* p, hipStream_t st, const float* cum) {
+                                float* r, float* p, hipStream_t st, const float* cum,
+                                const float* ca, const float* cb) {
 #define EFLA_SP(E_, DK_, DV_, NWC_, GT_) \
-  return scan_fwd_pair_run<E_, DK_, DV_, NWC_, GT_>(s, k, w, u, r, p, st, cum)
+  return scan_fwd_pair_run<E_, DK_, DV_, NWC_, GT_>(s, k, w, u, r, p, st, cum, ca, cb)
   if (s.dt == Dt::BF16) {
     if (cum) {
       if (s.dk == 64 && s.dv == 64) EFLA_SP(__bf16, 64, 64, 2, true);

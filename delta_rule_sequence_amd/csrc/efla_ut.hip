@@ -7,8 +7,12 @@
 // K K^T, Q K^T, T K and T V are MFMA contractions (products over the token index read the
 // row-major K and V tiles k-major); the unit lower triangular inverse is a blocked forward
 // substitution in fp32 in LDS. Padded rows of a tail chunk read as zero (their beta is zero,
-// so alpha = 0 and they do not touch the valid rows). M (q may be null) and X (kept for the
-// backward pass, which then needs no inverse of its own) are optional outputs.
+// so alpha = 0 and they do not touch the valid rows). Every output is optional: W and U (w, u;
+// V is read only for them), M (q may be null), X, and the per-token column scales of the two
+// factors, alpha~ = alpha (gated: alpha e^{c}) and b (gated). The bf16 forward keeps only X and
+// the scales: its scans form U~ = U - W S = X (diag(b) V - diag(alpha~) K S) themselves, which
+// moves less data than W and U (X is a quarter of W's size at d = 128); X also serves the
+// backward pass, which then needs no inverse of its own.
 //
 // Gated EFLA (GT): with c_t the running sum of the log-decays inside the chunk,
 //   A_ts = alpha_t e^{c_t - c_s} k_t . k_s (s < t),  X = (I + A)^{-1},
@@ -39,7 +43,8 @@ template <typename E, int DK, int DV, bool GT>
 __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ beta, const E* __restrict__ gate, E* __restrict__ w, E* __restrict__ u,
-    E* __restrict__ mout, E* __restrict__ xout, float* __restrict__ cum) {
+    E* __restrict__ mout, E* __restrict__ xout, float* __restrict__ cum, float* __restrict__ ca,
+    float* __restrict__ cb) {
   typedef UtFwdLds<E, DK, DV, GT> L;
   typedef typename Mma<E>::vec Vv;
   constexpr int KC = Mma<E>::KC, KS = DK / KC;
@@ -88,6 +93,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     if constexpr (GT) aN = to_f(aL[c.row0 + min(lane, c.n - 1)]);  // token = lane
   };
   auto issue_v = [&](const ChunkUnit& c) {
+    if (!w) return;  // V feeds U = T V only
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int i = it * kThreads + tid;
@@ -124,11 +130,13 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
         if constexpr (GT) sBl[r] = r < n ? gated_input_coef(bR[it], acc, aR[it], g.euler) : 0.f;
       }
     }
+    if (w) {
 #pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int i = it * kThreads + tid;
-      const int r = i / (DV / VE), c = (i % (DV / VE)) * VE;
-      *(u32x4*)(sV + r * L::LV + c) = keep_if(vR[it], r < n);
+      for (int it = 0; it < VIT; ++it) {
+        const int i = it * kThreads + tid;
+        const int r = i / (DV / VE), c = (i % (DV / VE)) * VE;
+        *(u32x4*)(sV + r * L::LV + c) = keep_if(vR[it], r < n);
+      }
     }
     if (mout) {
 #pragma unroll
@@ -231,6 +239,11 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     invert_unit_lower64(sA, sX, tid);
     issue_q(nxt);
 
+    // Column scales of the factors for the scans: alpha~ = alpha (gated alpha e^{c}), b.
+    if (ca && tid < 64) {
+      ca[cur.sh * 64 + tid] = GT ? sAl[tid] * exp_decay(sCm[tid]) : sAl[tid];
+      if constexpr (GT) cb[cur.sh * 64 + tid] = sBl[tid];
+    }
     // T = X diag(alpha), written over A (A is no longer needed); X to global memory.
     {
       E* gx = xout ? xout + cur.sh * 64 * 64 : nullptr;
@@ -266,15 +279,19 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
             tu[e] = (__bf16)(x0[e] * b0[e]);
             tu[e + 4] = (__bf16)(x1[e] * b1[e]);
           }
-          *(bf16x8*)(sT + r * L::LT + c) = te;
-          if constexpr (GT) *(bf16x8*)(sT2 + r * L::LT + c) = tu;
+          if (w) {
+            *(bf16x8*)(sT + r * L::LT + c) = te;
+            if constexpr (GT) *(bf16x8*)(sT2 + r * L::LT + c) = tu;
+          }
           if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
         } else {
-          *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
-          *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
-          if constexpr (GT) {
-            *(f32x4*)(sT2 + r * L::LT + c) = x0 * b0;
-            *(f32x4*)(sT2 + r * L::LT + c + 4) = x1 * b1;
+          if (w) {
+            *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
+            *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
+            if constexpr (GT) {
+              *(f32x4*)(sT2 + r * L::LT + c) = x0 * b0;
+              *(f32x4*)(sT2 + r * L::LT + c + 4) = x1 * b1;
+            }
           }
           if (gx) {
             *(f32x4*)(gx + r * 64 + c) = x0;
@@ -285,41 +302,43 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     }
     __syncthreads();
 
-    // W = T K, U = T V. Wave wv owns a quarter of the columns of each over all four row
-    // blocks (equal work per wave); T is lower triangular, so row blocks 0-1 need columns
-    // < 32 and row blocks 2-3 all 64. Formed transposed for row-layout stores.
-    constexpr int CW = DK / 64, CU = DV / 64;  // 16-column tiles per wave
-    f32x4 Wf[4][CW], Uf[4][CU];
-    {
-      f32x4 (&w01)[2][CW] = *reinterpret_cast<f32x4(*)[2][CW]>(&Wf[0]);
-      f32x4 (&w23)[2][CW] = *reinterpret_cast<f32x4(*)[2][CW]>(&Wf[2]);
-      f32x4 (&u01)[2][CU] = *reinterpret_cast<f32x4(*)[2][CU]>(&Uf[0]);
-      f32x4 (&u23)[2][CU] = *reinterpret_cast<f32x4(*)[2][CU]>(&Uf[2]);
+    if (w) {  // uniform: every thread takes the same branch, so the barriers inside match
+      // W = T K, U = T V. Wave wv owns a quarter of the columns of each over all four row
+      // blocks (equal work per wave); T is lower triangular, so row blocks 0-1 need columns
+      // < 32 and row blocks 2-3 all 64. Formed transposed for row-layout stores.
+      constexpr int CW = DK / 64, CU = DV / 64;  // 16-column tiles per wave
+      f32x4 Wf[4][CW], Uf[4][CU];
+      {
+        f32x4 (&w01)[2][CW] = *reinterpret_cast<f32x4(*)[2][CW]>(&Wf[0]);
+        f32x4 (&w23)[2][CW] = *reinterpret_cast<f32x4(*)[2][CW]>(&Wf[2]);
+        f32x4 (&u01)[2][CU] = *reinterpret_cast<f32x4(*)[2][CU]>(&Uf[0]);
+        f32x4 (&u23)[2][CU] = *reinterpret_cast<f32x4(*)[2][CU]>(&Uf[2]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < CW; ++j) Wf[i][j] = zero4();
+#pragma unroll
+          for (int j = 0; j < CU; ++j) Uf[i][j] = zero4();
+        }
+        const int k01 = round_up_kc<E>(32);
+        mma_blk<E, false, true, 2, CW, kChunk, true>(sT, L::LT, sK + 16 * CW * wv, L::LK, 0, k01, w01, lane);
+        mma_blk<E, false, true, 2, CW, kChunk, true>(sT + 32 * L::LT, L::LT, sK + 16 * CW * wv, L::LK, 0, kChunk, w23, lane);
+        const E* tU = GT ? sT2 : sT;
+        mma_blk<E, false, true, 2, CU, kChunk, true>(tU, L::LT, sV + 16 * CU * wv, L::LV, 0, k01, u01, lane);
+        mma_blk<E, false, true, 2, CU, kChunk, true>(tU + 32 * L::LT, L::LT, sV + 16 * CU * wv, L::LV, 0, kChunk, u23, lane);
+      }
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < CW; ++j) Wf[i][j] = zero4();
+        for (int j = 0; j < CW; ++j) st_frag_t<E>(sK + 16 * i * L::LK + 16 * (CW * wv + j), L::LK, Wf[i][j], lane);
 #pragma unroll
-        for (int j = 0; j < CU; ++j) Uf[i][j] = zero4();
+        for (int j = 0; j < CU; ++j) st_frag_t<E>(sV + 16 * i * L::LV + 16 * (CU * wv + j), L::LV, Uf[i][j], lane);
       }
-      const int k01 = round_up_kc<E>(32);
-      mma_blk<E, false, true, 2, CW, kChunk, true>(sT, L::LT, sK + 16 * CW * wv, L::LK, 0, k01, w01, lane);
-      mma_blk<E, false, true, 2, CW, kChunk, true>(sT + 32 * L::LT, L::LT, sK + 16 * CW * wv, L::LK, 0, kChunk, w23, lane);
-      const E* tU = GT ? sT2 : sT;
-      mma_blk<E, false, true, 2, CU, kChunk, true>(tU, L::LT, sV + 16 * CU * wv, L::LV, 0, k01, u01, lane);
-      mma_blk<E, false, true, 2, CU, kChunk, true>(tU + 32 * L::LT, L::LT, sV + 16 * CU * wv, L::LV, 0, kChunk, u23, lane);
+      __syncthreads();
+      s2g<E, DK>(w + row0 * DK, DK, sK, L::LK, n, tid);
+      s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < CW; ++j) st_frag_t<E>(sK + 16 * i * L::LK + 16 * (CW * wv + j), L::LK, Wf[i][j], lane);
-#pragma unroll
-      for (int j = 0; j < CU; ++j) st_frag_t<E>(sV + 16 * i * L::LV + 16 * (CU * wv + j), L::LV, Uf[i][j], lane);
-    }
-    __syncthreads();
-    s2g<E, DK>(w + row0 * DK, DK, sK, L::LK, n, tid);
-    s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
     if (!more) break;
     __syncthreads();  // the copies out of sK and sV are done before the next chunk lands
     land(nxt);
@@ -331,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
 template <typename E, int DK, int DV, bool GT>
 static hipError_t ut_go(const Shape& s, const int* table, const void* q, const void* k,
                         const void* v, const void* beta, const void* gate, void* w, void* u,
-                        void* m, void* x, float* cum, hipStream_t st) {
+                        void* m, void* x, float* cum, float* ca, float* cb, hipStream_t st) {
   typedef UtFwdLds<E, DK, DV, GT> L;
   static bool attr = false;
   if (!attr) {
@@ -347,7 +366,7 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
   prof_begin(st);
   hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV, GT>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
                      st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)beta, (const E*)gate, (E*)w, (E*)u, (E*)m, (E*)x, cum);
+                     (const E*)beta, (const E*)gate, (E*)w, (E*)u, (E*)m, (E*)x, cum, ca, cb);
   hipError_t e = hipGetLastError();
   prof_end(GT ? "ut_fwd_gated" : "ut_fwd", st);
   return e;
@@ -356,9 +375,10 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
 template <typename E, int DK, int DV>
 static hipError_t ut_dispatch(const Shape& s, const int* table, const void* q, const void* k,
                               const void* v, const void* beta, const void* gate, void* w,
-                              void* u, void* m, void* x, float* cum, hipStream_t st) {
-  if (gate) return ut_go<E, DK, DV, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, st);
-  return ut_go<E, DK, DV, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, st);
+                              void* u, void* m, void* x, float* cum, float* ca, float* cb,
+                              hipStream_t st) {
+  if (gate) return ut_go<E, DK, DV, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  return ut_go<E, DK, DV, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
 }
 
 size_t lds_ut_fwd(Dt dt, int dk, int dv) {
@@ -375,8 +395,9 @@ size_t lds_ut_fwd(Dt dt, int dk, int dv) {
 
 hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const void* k,
                          const void* v, const void* beta, const void* gate, void* w, void* u,
-                         void* m, void* x, float* cum, hipStream_t st) {
-#define EFLA_UT(E_, DK_, DV_) return ut_dispatch<E_, DK_, DV_>(s, table, q, k, v, beta, gate, w, u, m, x, cum, st)
+                         void* m, void* x, float* cum, float* ca, float* cb, hipStream_t st) {
+#define EFLA_UT(E_, DK_, DV_) \
+  return ut_dispatch<E_, DK_, DV_>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st)
   if (s.dt == Dt::BF16) {
     if (s.dk == 64 && s.dv == 64) EFLA_UT(__bf16, 64, 64);
     if (s.dk == 64 && s.dv == 128) EFLA_UT(__bf16, 64, 128);

@@ -79,7 +79,8 @@ def efla_get_saved_layout(p) -> dict:
     out = _lib.EflaSavedLayout()
     _lib.check("efla_get_saved_layout", _lib.lib().efla_get_saved_layout(ctypes.byref(p), ctypes.byref(out)))
     return dict(w=out.w, ut=out.ut, states=out.states, table=out.table, m=out.m, x=out.x,
-                cum=out.cum, segp=out.segp, total=out.total, n_chunk_slots=out.n_chunk_slots)
+                coef=out.coef, cum=out.cum, segp=out.segp, total=out.total,
+                n_chunk_slots=out.n_chunk_slots)
 
 
 def _bytes(n, device):
@@ -291,8 +292,9 @@ def efla_decode_gated(q, k, v, beta, gate, state, scale=1.0, mode="exact", o=Non
 
 
 def saved_views(saved, q, k, v, beta, scale=1.0, cu_seqlens=None):
-    """Tensor views of a saved buffer: W [B,H,T,dk], U~ [B,H,T,dv], states [slots,H,dk,dv],
-    M = tril(Q K^T) and X = (I + A)^{-1} per chunk [slots,H,64,64]."""
+    """Tensor views of a saved buffer: U~ [B,H,T,dv], states [slots,H,dk,dv], M = tril(Q K^T)
+    and X = (I + A)^{-1} per chunk [slots,H,64,64], and W [B,H,T,dk] (fp32 problems) or the
+    column scales alpha~, b [2,slots,H,64] fp32 (bf16 problems; W = X diag(alpha~) K)."""
     p = make_problem(q, k, v, beta, scale, cu_seqlens)
     L = efla_get_saved_layout(p)
     B, H, T, dk = k.shape
@@ -304,10 +306,16 @@ def saved_views(saved, q, k, v, beta, scale=1.0, cu_seqlens=None):
         for s in shape:
             n *= s
         return saved[off:off + n * es].view(k.dtype).view(*shape)
-    return dict(w=view(L["w"], (B, H, T, dk)), ut=view(L["ut"], (B, H, T, dv)),
-                states=view(L["states"], (L["n_chunk_slots"], H, dk, dv)),
-                m=view(L["m"], (L["n_chunk_slots"], H, 64, 64)),
-                x=view(L["x"], (L["n_chunk_slots"], H, 64, 64)))
+    out = dict(ut=view(L["ut"], (B, H, T, dv)),
+               states=view(L["states"], (L["n_chunk_slots"], H, dk, dv)),
+               m=view(L["m"], (L["n_chunk_slots"], H, 64, 64)),
+               x=view(L["x"], (L["n_chunk_slots"], H, 64, 64)))
+    if k.dtype == torch.float32:
+        out["w"] = view(L["w"], (B, H, T, dk))
+    else:
+        n = 2 * L["n_chunk_slots"] * H * 64
+        out["coef"] = saved[L["coef"]:L["coef"] + 4 * n].view(torch.float32).view(2, L["n_chunk_slots"], H, 64)
+    return out
 
 
 class EflaFunction(torch.autograd.Function):

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EFLA_ABI_VERSION 9
+#define EFLA_ABI_VERSION 10
 
 /* Size of the static device workspace of efla_fwd_noalloc (per GPU): 64 MiB. */
 #define EFLA_NOALLOC_WS_BYTES (64ull << 20)
@@ -85,7 +85,9 @@ typedef struct {
 } efla_problem;
 
 /* Byte offsets of the tensors inside the buffer that efla_fwd saves for efla_bwd.
- *   w      : W = T K per chunk, [B,H,T,dk], problem dtype
+ *   w      : fp32 problems: W = T K per chunk, [B,H,T,dk], fp32; bf16 problems: empty (the
+ *            scans form U~ = X (diag(b) V - diag(alpha~) K S) and W^T dU~ = K^T diag(alpha~)
+ *            X^T dU~ from X and coef instead)
  *   ut     : U~ = U - W S per chunk, [B,H,T,dv], problem dtype
  *   states : state entering each chunk, [n_chunk_slots][H][dk][dv], problem dtype;
  *            slot = b * ceil(T/64) + c (dense batch) or chunk_start[s] + c (packed),
@@ -94,6 +96,10 @@ typedef struct {
  *   m      : tril(Q K^T) of each chunk, [n_chunk_slots][H][64][64], problem dtype
  *   x      : X = (I + strictly_lower(diag(alpha) K K^T))^{-1} of each chunk (so that
  *            T = X diag(alpha)), [n_chunk_slots][H][64][64], problem dtype
+ *   coef   : bf16 problems only (empty for fp32): the per-token column scales of the chunk
+ *            factors, fp32 [2][n_chunk_slots][H][64]: alpha~ = alpha (gated: alpha e^{c}),
+ *            then b, the gated input coefficient (written by the gated forward only), so that
+ *            W = X diag(alpha~) K and U = X diag(b) V (ungated b = alpha)
  *   cum    : gated forward only: running sums of the log-decays inside each chunk,
  *            fp32 [n_chunk_slots][H][64] (then w, m and x hold the decayed factors of
  *            efla_fwd_gated)
@@ -102,7 +108,7 @@ typedef struct {
  *            [B * G][H][dk][dk]; the backward chains the state gradients with its transpose
  *   total  : size of the whole buffer = efla_saved_bytes()                               */
 typedef struct {
-  size_t w, ut, states, table, m, x, cum, segp, total;
+  size_t w, ut, states, table, m, x, coef, cum, segp, total;
   int64_t n_chunk_slots;
 } efla_saved_layout;
 
@@ -144,7 +150,8 @@ efla_status efla_chunk_ut(const efla_problem* p, const void* k, const void* v, c
                           void* w, void* u, void* ws, size_t ws_bytes, void* stream);
 
 /* Forward: o [B,H,T,dv] (problem dtype). `saved` (NULL, or efla_saved_bytes(p) bytes)
- * receives W, U~, the chunk states, M and X for efla_bwd. ws: efla_workspace_bytes(p, 0).
+ * receives U~, the chunk states, M, X and W (fp32) or the column scales (bf16) for efla_bwd.
+ * ws: efla_workspace_bytes(p, 0).
  * Segment-parallel scan (summary page, section 3.3: from chunk to chunk the state follows an
  * affine map, S <- (I - K^T W) S + K^T U, so the maps of consecutive chunks compose): when
  * the plan splits sequences into G > 1 segments, every segment's composed transition P and
@@ -174,7 +181,7 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
  * static device array of EFLA_NOALLOC_WS_BYTES inside the library, one per GPU, which each GPU
  * holds until the process ends. Problems whose efla_workspace_bytes(p, 0) exceeds that size
  * return EFLA_ERR_WORKSPACE before anything is enqueued (64 MiB holds, for example, 16 heads of
- * 4,096 bf16 tokens at d_k = d_v = 128, with the library's segment plan). It allocates nothing,
+ * 8,192 bf16 tokens at d_k = d_v = 128, with the library's segment plan). It allocates nothing,
  * ever. Every call on a GPU uses that GPU's array and leaves its contents behind: calls that
  * overlap on one GPU (different streams or host threads) race; calls on one stream are ordered.
  * No part of the array has to start at zero. On the first call on a device the array's address is looked up

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.efla_abi_version() == 9
+    assert L.efla_abi_version() == 10
 
 
 def test_status_strings(L):
@@ -95,21 +95,38 @@ def test_null_problem(L):
 
 
 def test_workspace_and_saved_sizes(L):
+    # bf16: the scans read X and the per-token column scales (fp32 [2][slots][H][64]) in place of
+    # W and U, so neither is saved nor kept in the workspace
     p = _p()
     e = 2
     tok = 4 * 16 * 2048
     slots = 4 * 32
-    w = tok * 128 * e
+    v = tok * 128 * e           # a [B,H,T,128] tensor (U~, dU~)
     states = slots * 16 * 128 * 128 * e
-    m = slots * 16 * 64 * 64 * e
-    cum = slots * 16 * 64 * 4  # running log-decay sums of the gated forward
-    assert L.efla_saved_bytes(ctypes.byref(p)) == 2 * w + states + 2 * m + cum
-    assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * w + m + cum
-    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (w + states) + (2 * w + states + 2 * m + cum) + w
+    m = slots * 16 * 64 * 64 * e  # M or X
+    cum = slots * 16 * 64 * 4   # running log-decay sums of the gated forward
+    coef = 2 * cum
+    saved = v + states + 2 * m + coef + cum
+    assert L.efla_saved_bytes(ctypes.byref(p)) == saved
+    assert L.efla_workspace_bytes(ctypes.byref(p), 0) == 2 * m + coef + cum
+    assert L.efla_workspace_bytes(ctypes.byref(p), 1) == (v + states) + saved
     lay = _lib.EflaSavedLayout()
     assert L.efla_get_saved_layout(ctypes.byref(p), ctypes.byref(lay)) == 0
-    assert (lay.w, lay.ut, lay.states, lay.m, lay.x, lay.n_chunk_slots) == \
-        (0, w, 2 * w, 2 * w + states, 2 * w + states + m, slots)
+    assert (lay.w, lay.ut, lay.states, lay.m, lay.x, lay.coef, lay.cum, lay.n_chunk_slots) == \
+        (0, 0, v, v + states, v + states + m, v + states + 2 * m, v + states + 2 * m + coef, slots)
+    # fp32: W saved, U and W in the forward workspace, U again for the recompute path
+    p32 = _p(dtype=_lib.EFLA_F32, dk=64, dv=64)
+    e = 4
+    w = tok * 64 * e
+    states = slots * 16 * 64 * 64 * e
+    m = slots * 16 * 64 * 64 * e
+    saved = 2 * w + states + 2 * m + cum
+    assert L.efla_saved_bytes(ctypes.byref(p32)) == saved
+    assert L.efla_workspace_bytes(ctypes.byref(p32), 0) == 2 * w + m + cum
+    assert L.efla_workspace_bytes(ctypes.byref(p32), 1) == (w + states) + saved + w
+    assert L.efla_get_saved_layout(ctypes.byref(p32), ctypes.byref(lay)) == 0
+    assert (lay.w, lay.ut, lay.states, lay.m, lay.x, lay.coef, lay.cum) == \
+        (0, w, 2 * w, 2 * w + states, 2 * w + states + m, 2 * w + states + 2 * m, 2 * w + states + 2 * m)
     # packed batch: chunk slots are bounded by T/64 + n_seqs
     pp = _p(B=1, T=1000, cu=0x1000, n_seqs=7)
     assert L.efla_get_saved_layout(ctypes.byref(pp), ctypes.byref(lay)) == 0
@@ -243,15 +260,15 @@ def test_noalloc_entry_point_rejects_without_touching_hip(L):
 
     def call(prob, q=fake, h0=None, o=fake, ht=None):
         return L.efla_fwd_noalloc(ctypes.byref(prob), q, fake, fake, fake, h0, o, ht, None)
-    big = _p(B=1, H=16, T=8192)
+    big = _p(B=1, H=16, T=16384)
     assert L.efla_workspace_bytes(ctypes.byref(big), 0) > cap
     assert call(big) == 5
-    fits = _p(B=1, H=16, T=4096)      # the header's example: 16 heads of 4,096 bf16 tokens
+    fits = _p(B=1, H=16, T=8192)      # the header's example: 16 heads of 8,192 bf16 tokens
     assert L.efla_workspace_bytes(ctypes.byref(fits), 0) <= cap
     assert call(fits, q=None) == 1
     assert call(fits, o=None) == 1
     assert call(fits, q=odd) == 7
     assert call(fits, h0=odd) == 7
     assert call(fits, ht=odd) == 7
-    assert call(_p(B=1, H=16, T=4096, dk=96)) == 4
+    assert call(_p(B=1, H=16, T=8192, dk=96)) == 4
     assert L.efla_fwd_noalloc(ctypes.byref(_p(T=0)), None, None, None, None, None, None, None, None) == 0

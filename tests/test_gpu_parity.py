@@ -61,7 +61,11 @@ def _run(E, inp, dtype, scale=1.0, backward=True):
     used = sum((e - s + O.CHUNK - 1) // O.CHUNK for (_, s, e) in O.sequences(B, T, inp["cu_seqlens"]))
     out["states"] = _np(views["states"][:used])
     out["ut"] = _np(views["ut"])
-    out["w"] = _np(views["w"])
+    if "w" in views:  # fp32 saves W; bf16 saves X and the column scales alpha~ instead
+        out["w"] = _np(views["w"])
+    else:
+        out["x"] = _np(views["x"][:used])
+        out["alpha"] = _np(views["coef"][0, :used])
     if backward:
         do = _dev(inp["do"], dt)
         dq, dk, dv, db = E.efla_bwd(q, k, v, beta, do, saved, scale, cu)
@@ -126,14 +130,37 @@ def test_parity_reduced(E, name, idx, over, bwd, scale):
     _compare(gpu, ref, w.dtype, bwd, token_rows=rows)
 
 
-def test_stage_values_match_chunk_oracle(E):
-    """Per-stage values: W, U~ and the state entering every chunk (kernels b and c)."""
-    w = workload(2, B=2, H=2, T=150)
+@pytest.mark.parametrize("widx", [2, 4])
+def test_stage_values_match_chunk_oracle(E, widx):
+    """Per-stage values: W, U~ and the state entering every chunk (kernels b and c). fp32
+    saves W itself; bf16 saves X and the column scales alpha~ (checked against the oracle's
+    alpha token by token), and W = X diag(alpha~) K is formed from them here."""
+    w = workload(widx, B=2, H=2, T=150)
     inp = make_inputs(w, with_grad=False)
     gpu = _run(E, inp, w.dtype, 1.0, backward=False)
     ref = O.chunk_forward(inp["q"], inp["k"], inp["v"], inp["beta"])
     tol = TOL[w.dtype]
-    _check("W", gpu["w"], ref["W"], tol)
+    if "w" in gpu:
+        _check("W", gpu["w"], ref["W"], tol)
+    else:
+        B, H, T = inp["k"].shape[:3]
+        ntc = (T + O.CHUNK - 1) // O.CHUNK
+        k64 = inp["k"].astype(np.float64)
+        alpha_ref = O.coefficients(inp["k"], inp["beta"])["alpha"]
+        alpha_gpu = np.zeros_like(alpha_ref)
+        w_gpu = np.zeros_like(k64)
+        for b in range(B):
+            for c in range(ntc):
+                t0, n = c * O.CHUNK, min(O.CHUNK, T - c * O.CHUNK)
+                for h in range(H):
+                    a = gpu["alpha"][b * ntc + c, h, :n].astype(np.float64)
+                    alpha_gpu[b, h, t0:t0 + n] = a
+                    X = gpu["x"][b * ntc + c, h, :n, :n].astype(np.float64)
+                    w_gpu[b, h, t0:t0 + n] = X @ (a[:, None] * k64[b, h, t0:t0 + n])
+        err = np.max(np.abs(alpha_gpu - alpha_ref) / np.maximum(np.abs(alpha_ref), 1e-30))
+        print("  alpha~ elementwise rel err %.3e" % err, flush=True)
+        assert err <= 1e-5, err  # fp32 coefficients: the exact-flow step to fp32 rounding
+        _check("W", w_gpu, ref["W"], tol)
     _check("U~", gpu["ut"], ref["Ut"], tol)
     states = np.stack(ref["states"])             # [slots, H, dk, dv]
     _check("S_c", gpu["states"][: len(states)], states, tol, per_head=False)
@@ -166,8 +193,11 @@ def test_saved_chunk_factors_match_oracle(E, widx, over):
             slot += 1
 
 
-def test_chunk_ut_entry_point(E):
-    w = workload(4, B=1, H=2, T=170)
+@pytest.mark.parametrize("widx", [4, 2])
+def test_chunk_ut_entry_point(E, widx):
+    """efla_chunk_ut forms W and U explicitly for fp32 and bf16 (the forward of bf16 problems
+    keeps X and the column scales instead)."""
+    w = workload(widx, B=1, H=2, T=170)
     inp = make_inputs(w, with_grad=False)
     dt = TDT[w.dtype]
     W, U = E.efla_chunk_ut(_dev(inp["k"], dt), _dev(inp["v"], dt), _dev(inp["beta"], dt))
