@@ -663,11 +663,12 @@ def main():
     prewarm(torch, step)  # untimed; the measurements below then see the GPU at its steady clocks
     aux = aux_measurements(E, args, torch, np, make_inputs, workload, step, q, k, v, beta, do, o,
                            saved, ws, grads) if not args.headline_only else {}
-    # The headline: W untimed warmup steps, then exactly K steps between two synchronizations.
-    # It runs after the measurements above, which keep the GPU busy: after a few seconds idle
-    # (input generation, allocations) a step takes 0.30 ms and needs some 60-80 steps to settle
-    # at its steady-state time (clock and power ramp), so the timed steps see the GPU as a
+    # The headline: W untimed warmup steps, then exactly K steps between two synchronizations,
+    # after half a second of untimed steps: after idle time (input generation, allocations) or
+    # other work (the measurements above) a step needs some 60-80 repetitions to settle at its
+    # steady-state time (clock and power ramp, caches), so the timed steps see the GPU as a
     # training loop keeps it.
+    prewarm(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
