@@ -55,19 +55,21 @@ def kernel_model(name, dk, dv, e, C=CHUNK):
     flops count the tile contractions the method needs, triangular factors at half size
     (2 per multiply-add). bf16 problems (e = 2) keep X and the column scales alpha~ (fp32, one
     per token) in place of W and U: the scans form U~ = X (diag(alpha~) (V - K S)) and
-    W^T dU~ = K^T diag(alpha~) X^T dU~ themselves; fp32 problems (e = 4) read W and U."""
+    W^T dU~ = K^T diag(alpha~) X^T dU~ themselves, and the forward scan forms M = tril(Q K^T)
+    from its Q and K tiles (writing it out for the backward); fp32 problems (e = 4) read W and
+    U, and M from the UT kernel."""
     xf = e == 2
     if name == "ut_fwd":
-        if xf:                # Q, K, beta -> M = tril(QK^T), X = (I + A)^-1, alpha~
-            b = e * (2 * C * dk + C) + e * 2 * C * C + 4 * C
-            f = 2 * C * C * dk + C ** 3 / 3
+        if xf:                # K, beta -> X = (I + A)^-1, alpha~
+            b = e * (C * dk + C) + e * C * C + 4 * C
+            f = C * C * dk + C ** 3 / 3
         else:                 # Q, K, V, beta -> W, U, M, X
             b = e * (2 * C * dk + C * dv + C) + e * (C * dk + C * dv + 2 * C * C)
             f = 3 * C * C * dk + C * C * dv + C ** 3 / 3
     elif name == "scan_fwd":
-        if xf:                # Q, K, X, V, M, alpha~ -> O, U~, S_c
-            b = e * (2 * C * dk + C * dv + 2 * C * C) + 4 * C + e * (2 * C * dv + dk * dv)
-            f = 6 * C * dk * dv + 2 * C * C * dv
+        if xf:                # Q, K, X, V, alpha~ -> O, U~, S_c, M = tril(QK^T)
+            b = e * (2 * C * dk + C * dv + C * C) + 4 * C + e * (2 * C * dv + dk * dv + C * C)
+            f = 6 * C * dk * dv + 2 * C * C * dv + C * C * dk
         else:                 # Q, K, W, U, M -> O, U~, S_c
             b = e * (3 * C * dk + C * dv + C * C) + e * (2 * C * dv + dk * dv)
             f = 6 * C * dk * dv + C * C * dv

@@ -222,13 +222,14 @@ Saved saved_layout(const Shape& s) {
 }
 
 // Forward workspace: U and W (fp32) or X and the column scales (bf16), the chunk table and M
-// (all of them used only when no saved buffer is given, except U), the segment-parallel scan's
-// buffers, and the gated forward's decay sums.
+// (fp32; all of them used only when no saved buffer is given, except U), the segment-parallel
+// scan's buffers, and the gated forward's decay sums.
 size_t bytes_ws_a(const Shape& s) { return xform(s) ? bytes_x(s) : bytes_v(s); }
 size_t bytes_ws_b(const Shape& s) { return xform(s) ? bytes_coef(s) : bytes_k(s); }
+size_t bytes_ws_m(const Shape& s) { return xform(s) ? 0 : bytes_m(s); }
 size_t ws_fwd(const Shape& s) {
   return align_up(bytes_ws_a(s)) + align_up(bytes_ws_b(s)) + align_up(bytes_table(s)) +
-         align_up(bytes_m(s)) + bytes_seg(s) + align_up(bytes_cum(s));
+         align_up(bytes_ws_m(s)) + bytes_seg(s) + align_up(bytes_cum(s));
 }
 // Buffers of one forward: saved-buffer regions when a saved buffer is given, workspace otherwise.
 struct FwdBufs {
@@ -246,7 +247,7 @@ FwdBufs fwd_bufs(const Shape& s, unsigned char* ws, unsigned char* sv) {
   unsigned char* bb = a + align_up(bytes_ws_a(s));
   unsigned char* tb = bb + align_up(bytes_ws_b(s));
   unsigned char* mw = tb + align_up(bytes_table(s));
-  b.seg = mw + align_up(bytes_m(s));
+  b.seg = mw + align_up(bytes_ws_m(s));
   float* cum_ws = (float*)(b.seg + bytes_seg(s));
   b.u = xform(s) ? nullptr : a;
   b.w = xform(s) ? nullptr : (sv ? sv + L.w : bb);
@@ -255,7 +256,9 @@ FwdBufs fwd_bufs(const Shape& s, unsigned char* ws, unsigned char* sv) {
   b.ut = sv ? sv + L.ut : nullptr;
   b.states = sv ? sv + L.states : nullptr;
   b.table = sv ? (int*)(sv + L.table) : (int*)tb;
-  b.m = sv ? sv + L.m : mw;
+  // M: fp32, written by the UT kernel and read by the forward scan; bf16, formed by the forward
+  // scan itself where it writes O, and written out (for the backward) only into a saved buffer
+  b.m = sv ? sv + L.m : (xform(s) ? nullptr : mw);
   b.cum = sv ? (float*)(sv + L.cum) : cum_ws;
   b.segp = sv ? (float*)(sv + L.segp) : nullptr;
   return b;
@@ -290,7 +293,7 @@ efla_status run_forward(const Shape& s, const void* q, const void* k, const void
   const bool xf = xform(s);
   float* ca = b.coef;
   float* cb = xf && gate ? b.coef + coef_stride(s) : nullptr;
-  if (efla_status r = hip_status(launch_ut_fwd(s, b.table, q, k, v, beta, gate, b.w, b.u, b.m, b.x,
+  if (efla_status r = hip_status(launch_ut_fwd(s, b.table, q, k, v, beta, gate, b.w, b.u, xf && o ? nullptr : b.m, b.x,
                                                gate ? b.cum : nullptr, ca, cb, st)))
     return r;
   const float* cm = gate ? b.cum : nullptr;

@@ -491,6 +491,21 @@ EFLA_DEV void l2_sink(const int* w) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" ::"v"(w[i]));
 }
+// The same warm-up by LDS DMA into `dummy` (256 bytes of LDS that nothing reads; each request
+// writes one word per lane there): no register receives the data, so the compiler places no
+// wait for these loads anywhere (a register load consumed in the next loop iteration gets a
+// wait for every vector memory operation in flight). The caller's counted vmcnt waits see them
+// as ordinary loads, N per call, issued in order.
+template <int N, int NT = 64>
+EFLA_DEV void l2_touch_lds(unsigned char* dummy, const void* p, int nbytes, int part, int nparts,
+                           int lane) {
+  const int last = (nbytes - 1) >> 7;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int j = min(part + nparts * (lane + NT * i), last);
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)p + (j << 7)), (lds_void*)dummy, 4, 0, 0);
+  }
+}
 
 // MFMA operands in the accumulator-compatible contraction order. A 16x16 accumulator tile
 // holds rows 4 (lane >> 4) + i of column lane & 15, so for a product whose contraction index
@@ -644,6 +659,55 @@ struct FlowCoef {
 // The product's rounding gives a relative error of about |x| 2^-24 on top of the instruction's
 // ~1 ulp, far below the resolution of bf16 data; results below the normal range may flush to 0.
 EFLA_DEV float exp_decay(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// M = tril(Q K^T) of one chunk (gated: M_ts = e^{c_t - c_s} q_t . k_s for s <= t) from the
+// swizzled [64][DK] Q and K tiles into the swizzled [64][64] M tile, by one wave: the ten blocks
+// on and below the diagonal, and zeros in blocks (0,1) and (2,3), which readers that step over
+// the columns 32 at a time also read. Formed transposed (K Q^T), so that a lane holds four
+// consecutive columns of one row and stores them at once; every K and Q fragment is read from
+// LDS once (K's for the whole tile, Q's per row block). c: the chunk's running log-decay sums in
+// LDS (gated). The scans' loader waves call it once a chunk's tiles have landed.
+template <typename E, int DK, bool GT>
+EFLA_DEV void m_tile(unsigned char* sm, const unsigned char* sq, const unsigned char* sk,
+                     const float* c, int lane) {
+  typedef Swz<E, 64> SM;
+  typedef typename Mma<E>::vec V;
+  constexpr int KC = Mma<E>::KC, KS = DK / KC;
+  const int g4 = 4 * (lane >> 4), cl = lane & 15;
+  V kf[4][KS];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+    for (int kd = 0; kd < KS; ++kd) kf[sb][kd] = frag_rm_sw<E, DK>(sk, 16 * sb, kd * KC, lane);
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = 16 * tb + cl;
+    const float ct = GT ? c[t] : 0.f;
+    V qf[KS];
+#pragma unroll
+    for (int kd = 0; kd < KS; ++kd) qf[kd] = frag_rm_sw<E, DK>(sq, 16 * tb, kd * KC, lane);
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const bool zero_blk = (tb == 0 && sb == 1) || (tb == 2 && sb == 3);
+      if (sb > tb && !zero_blk) continue;
+      f32x4 m = zero4();
+      if (sb <= tb) {
+#pragma unroll
+        for (int kd = 0; kd < KS; ++kd) m = Mma<E>::step(kf[sb][kd], qf[kd], m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // element i: row t, column s = 16 sb + g4 + i
+          const int s = 16 * sb + g4 + i;
+          if constexpr (GT) m[i] = s <= t ? m[i] * exp_decay(ct - c[s]) : 0.f;
+          else m[i] = s <= t ? m[i] : 0.f;
+        }
+      }
+      if constexpr (sizeof(E) == 2)
+        *(bf16x4*)(sm + SM::off(t, 16 * sb + g4)) = bf16x4{(__bf16)m[0], (__bf16)m[1], (__bf16)m[2], (__bf16)m[3]};
+      else
+        *(f32x4*)(sm + SM::off(t, 16 * sb + g4)) = m;
+    }
+  }
+}
 
 // phi(x) = (1 - e^{-x}) / x (phi(0) = 1): Taylor polynomial for |x| < 1 (degree 11), else the
 // closed form with expm1.

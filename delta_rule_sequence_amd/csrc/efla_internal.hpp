@@ -49,8 +49,10 @@ hipError_t launch_ut_fwd(const Shape& s, const int* table, const void* q, const 
 // h0 / ht (scan_fwd) and dht / dh0 (scan_bwd): fp32 [n_seqs][H][dk][dv] per-sequence
 // states entering / leaving the sequence, or null (zero in, not written out).
 // cum (null, or the running log-decay sums of launch_ut_fwd) selects gated EFLA.
+// m ([slots][H][64][64]): fp32, the M of launch_ut_fwd, read when O is written; bf16, null or
+// where the scan writes the M it forms from Q and K (only when O is written).
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                           const void* w, const void* u, const void* m, void* o, void* ut,
+                           const void* w, const void* u, void* m, void* o, void* ut,
                            void* states, const float* h0, float* ht, hipStream_t st,
                            const float* cum, const float* ca, const float* cb);
 // For a segment view, in one launch: the zero-start state scan (final states into r, fp32

@@ -376,7 +376,8 @@ struct ScanBwdDmaLds {
   static constexpr size_t oG = 2 * stage;                   // G slice [DK][LS]
   static constexpr size_t oDt = oG + DK * LS * sizeof(E);   // dU~^T [TV][LT]
   static constexpr size_t oDu = oDt + TV * LT * sizeof(E);  // dU~ staging [64][LS]
-  static constexpr size_t bytes = oDu + 64 * LS * sizeof(E);
+  static constexpr size_t oDummy = oDu + 64 * LS * sizeof(E);  // 256 bytes: L2 warm-up landing
+  static constexpr size_t bytes = oDummy + 256;
 };
 
 constexpr int kScanBwdDmaThreads = 6 * 64;  // four compute waves, the loader and the storer
@@ -421,22 +422,21 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
   static_assert(NWARM <= 15, "vmcnt field");
   static_assert(sizeof(E) == 2, "bf16 tiles (the transposed products use 32-wide steps)");
   if (wv == 4) {  // ---- loader wave
-    int pw[5 * NL];
-#pragma unroll
-    for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
-    auto warm = [&](int c) {  // one word per 128-byte line; the head's workgroups split the lines
+    // one word per 128-byte line (the head's workgroups split the lines), by LDS DMA into a row
+    // that nothing reads: no register waits for these loads, only the counted waits see them
+    unsigned char* dummy = smem + L::oDummy;
+    auto warm = [&](int c) {
       const int n = rows_of(c);
       const int64_t r0 = base + (int64_t)c * kChunk;
       const int bk = n * DK * (int)sizeof(E);
-      l2_touch<NL>(pw, x + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                   kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
-      l2_touch<NL>(pw + NL, k + r0 * DK, bk, tile, NTILE, lane);
-      {
-        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, bk, tile, NTILE, lane);
-        l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
-        l2_touch<NL>(pw + 4 * NL, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
-      }
+      l2_touch_lds<NL>(dummy, x + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                       kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+      l2_touch_lds<NL>(dummy, k + r0 * DK, bk, tile, NTILE, lane);
+      l2_touch_lds<NL>(dummy, q + r0 * DK, bk, tile, NTILE, lane);
+      l2_touch_lds<NL>(dummy, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
+                       kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+      l2_touch_lds<NL>(dummy, d_o + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
+      __builtin_amdgcn_sched_barrier(0);  // every request ahead of what follows (counted waits)
     };
     // the DMA has landed: vmcnt(NWARM) leaves only the younger warm-up loads in flight
     auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | NWARM); };
@@ -486,7 +486,6 @@ __global__ __launch_bounds__(kScanBwdDmaThreads, 1) void scan_bwd_dma_kernel(
       __builtin_amdgcn_s_barrier();  // chunk c is in LDS; every wave is done with chunk c + 1's stage
       if (c > 0) issue(c - 1);
       __builtin_amdgcn_s_barrier();  // the step's second barrier
-      l2_sink<5 * NL>(pw);           // the previous step's warm-up (and, at worst, this DMA)
       warm(max(c - 2, 0));
       if (c > 0) {
         wait_dma();

@@ -49,7 +49,11 @@ struct ScanFwdLds {
   static constexpr size_t gO = 0, gUt = WO ? SU::BYTES : 0, gS = gUt + (WSV ? SU::BYTES : 0);
   static constexpr size_t sstage = gS + (WSV ? (size_t)DK * SU::RB : 0);
   static constexpr size_t oStg = 2 * stage;
-  static constexpr size_t bytes = oStg + 2 * sstage;
+  // WDMA: 256 bytes that the loader's L2 warm-up requests land in (never read; where LDS has no
+  // room, the fp32 tiles at d = 64 with every output, the warm-up loads go to registers)
+  static constexpr size_t oDummy = oStg + 2 * sstage;
+  static constexpr bool WDMA = oDummy + 256 <= 160 * 1024;
+  static constexpr size_t bytes = oDummy + (WDMA ? 256 : 0);
 };
 
 // WO: write O (also needs Q and M); WSV: write U~ and the chunk states (saved for the
@@ -66,7 +70,7 @@ struct ScanFwdLds {
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
 __device__ __forceinline__ void scan_fwd_body(
     int bid, Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
-    const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
+    const E* __restrict__ u, E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
     E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
     const float* __restrict__ cum, const float* __restrict__ ca, const float* __restrict__ cb) {
   typedef ScanFwdLds<E, DK, DV, NWC, WO, WSV, GT> L;
@@ -124,7 +128,8 @@ __device__ __forceinline__ void scan_fwd_body(
     dma_tile<E, DK, NWL>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
     if constexpr (WO) {
       dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
-      dma_tile<E, 64, NWL>(st + L::oM, m + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
+      // XF: M is formed from the Q and K tiles by this wave once they have landed (mtile below)
+      if constexpr (!XF) dma_tile<E, 64, NWL>(st + L::oM, m + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
     }
     // the per-token vectors (64 floats each) by LDS DMA as well
     if constexpr (GT) dma_vec64(st + L::oC, cum + unit * kChunk, lane);
@@ -135,6 +140,31 @@ __device__ __forceinline__ void scan_fwd_body(
     // the counted wait assumes every request above is issued before the warm-up loads that
     // follow: keep the scheduler from moving any of them past this point
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // XF with the output, given m: M of chunk c (formed by the loader wave in stage c & 1, which
+  // stays put until the next barrier) goes to global memory for the backward. The NTILE
+  // workgroups of a (sequence, head) form the same M; each writes 64 / NTILE of its rows. The
+  // stage holds only the blocks on and below the diagonal: the others, and rows past the end of
+  // the sequence, are written as zeros.
+  auto copy_m = [&](int c) {
+    if constexpr (XF && WO) {
+      if (!m) return;
+      typedef Swz<E, 64> SM;
+      constexpr int RPT = kChunk / NTILE, CPM = SM::NCH;  // rows per workgroup, 16-byte chunks per row
+      static_assert(kChunk % NTILE == 0, "M rows per workgroup");
+      const unsigned char* sm = smem + (c & 1) * L::stage + L::oM;
+      E* gm = m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk;
+      const int n = rows_of(c);
+#pragma unroll
+      for (int it = 0; it < (RPT * CPM + NTL - 1) / NTL; ++it) {
+        const int i = it * NTL + tl, r = tile * RPT + i / CPM, lc = i % CPM;
+        if (i < RPT * CPM) {
+          u32x4 val = u32x4{0u, 0u, 0u, 0u};
+          if (r < n && lc * VE < 16 * (r / 16 + 1)) val = *(const u32x4*)(sm + SM::off(r, lc * VE));
+          *(u32x4*)(gm + r * kChunk + lc * VE) = val;
+        }
+      }
+    }
   };
   auto copy_out = [&](int c) {  // staged outputs of chunk c -> global memory, 16-byte rows
     const unsigned char* stg = smem + L::oStg + (c & 1) * L::sstage;
@@ -348,46 +378,65 @@ __device__ __forceinline__ void scan_fwd_body(
   // (sequence, head) split the shared tiles), so its DMA of chunk c + 1 reads lines requested a
   // step earlier and HBM keeps a request stream across the barriers. Before the barrier that
   // publishes a chunk it waits for the DMA only (a counted vmcnt: the younger warm-up loads stay
-  // in flight) and the barrier is a bare s_barrier, whose fence would wait for everything; each
-  // warm-up is consumed a step later. Every request is unconditional (clamped chunk index), so
-  // the compiler's counts stay exact. The storer then never waits for anything but the barriers.
+  // in flight) and the barrier is a bare s_barrier, whose fence would wait for everything. The
+  // warm-up requests are LDS DMA into a row that nothing reads (WDMA), so no register waits for
+  // them and the next chunk's warm-up leaves while this chunk's DMA is in flight. Every request
+  // is unconditional (clamped chunk index), so the counts stay exact; the last wait before the
+  // wave leaves covers them all. The storer never waits for anything but the barriers.
   if (loader) {
     constexpr int NL = (64 * (DK > DV ? DK : DV) * (int)sizeof(E) / 128 + 64 * NTILE - 1) / (64 * NTILE);
-    int pw[5 * NL];
+    unsigned char* dummy = smem + L::oDummy;
+    int pw[L::WDMA ? 1 : 5 * NL];  // register warm-up only
 #pragma unroll
-    for (int i = 0; i < 5 * NL; ++i) pw[i] = 0;
+    for (int i = 0; i < (L::WDMA ? 1 : 5 * NL); ++i) pw[i] = 0;
+    auto touch = [&](int slot, const void* p, int nbytes) {
+      if constexpr (L::WDMA) l2_touch_lds<NL>(dummy, p, nbytes, tile, NTILE, lane);
+      else l2_touch<NL>(pw + slot * NL, p, nbytes, tile, NTILE, lane);
+    };
     auto warm = [&](int c) {
       const int n = rows_of(c);
       const int64_t r0 = base + (int64_t)c * kChunk;
       if constexpr (XF)
-        l2_touch<NL>(pw, w + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+        touch(0, w + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk, kChunk * kChunk * (int)sizeof(E));
       else
-        l2_touch<NL>(pw, w + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
-      l2_touch<NL>(pw + NL, k + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
+        touch(0, w + r0 * DK, n * DK * (int)sizeof(E));
+      touch(1, k + r0 * DK, n * DK * (int)sizeof(E));
       if constexpr (WO) {
-        l2_touch<NL>(pw + 2 * NL, q + r0 * DK, n * DK * (int)sizeof(E), tile, NTILE, lane);
-        l2_touch<NL>(pw + 3 * NL, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk,
-                     kChunk * kChunk * (int)sizeof(E), tile, NTILE, lane);
+        touch(2, q + r0 * DK, n * DK * (int)sizeof(E));
+        if constexpr (!XF)
+          touch(3, m + ((int64_t)(si.slot0 + c) * g.H + h) * kChunk * kChunk, kChunk * kChunk * (int)sizeof(E));
       }
-      if constexpr (!PM) l2_touch<NL>(pw + 4 * NL, u + r0 * DV, n * DV * (int)sizeof(E), tile, NTILE, lane);
+      if constexpr (!PM) touch(4, u + r0 * DV, n * DV * (int)sizeof(E));
+      // keep every warm-up request ahead of the work that follows (the counted waits rely on it)
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // warm-up loads issued after each DMA: the factor (W or X) and K, Q and M with the output,
-    // U (or V) unless PM
-    constexpr int NWARM = NL * (2 + (WO ? 2 : 0) + (PM ? 0 : 1));
+    // warm-up loads issued after each DMA: the factor (W or X) and K, Q and M (XF: Q only)
+    // with the output, U (or V) unless PM
+    constexpr int NWARM = NL * (2 + (WO ? (XF ? 1 : 2) : 0) + (PM ? 0 : 1));
     static_assert(NWARM <= 15, "vmcnt field");
+    // XF with the output: once a chunk's tiles have landed, this wave forms its M into the
+    // chunk's stage (the compute waves work on the other stage meanwhile)
+    auto mtile = [&](int slot) {
+      if constexpr (XF && WO) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | NWARM);  // vmcnt(NWARM): the chunk's DMA has landed
+        unsigned char* st = smem + slot * L::stage;
+        m_tile<E, DK, GT>(st + L::oM, st + L::oQ, st + L::oK, (const float*)(st + L::oC), lane);
+      }
+    };
     issue(0, 0);
     warm(min(1, nchunks - 1));
+    mtile(0);
     for (int c = 0; c < nchunks; ++c) {
-      // vmcnt(NWARM): chunk c's DMA has landed (only the younger warm-up loads may still be in
-      // flight)
+      // vmcnt(NWARM), lgkmcnt(0): chunk c's DMA has landed (only the younger warm-up loads may
+      // still be in flight), and so have this wave's LDS writes
       __builtin_amdgcn_s_waitcnt(0x0070 | NWARM);
       __builtin_amdgcn_s_barrier();
       // after the last chunk the request repeats it into the stage that chunk c + 1 would use,
       // which no wave reads any more (every request is unconditional)
       issue(min(c + 1, nchunks - 1), (c + 1) & 1);
-      l2_sink<5 * NL>(pw);
+      if constexpr (!L::WDMA) l2_sink<5 * NL>(pw);  // the previous step's register warm-up
       warm(min(c + 2, nchunks - 1));
+      mtile((c + 1) & 1);
     }
     wait_vm_all();
     __syncthreads();
@@ -395,8 +444,9 @@ __device__ __forceinline__ void scan_fwd_body(
   }
   if (storer) {
     for (int c = 0; c < nchunks; ++c) {
-      __syncthreads();  // staging of chunk c - 1 is complete
+      __syncthreads();  // staging of chunk c - 1 is complete, and M of chunk c is in its stage
       if (c > 0) copy_out(c - 1);
+      copy_m(c);
     }
     __syncthreads();
     copy_out(nchunks - 1);
@@ -418,7 +468,7 @@ __device__ __forceinline__ void scan_fwd_body(
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM, bool GT>
 __global__ __launch_bounds__(64 * NWC + 128, 1) void scan_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ w,
-    const E* __restrict__ u, const E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
+    const E* __restrict__ u, E* __restrict__ m, E* __restrict__ o, E* __restrict__ ut,
     E* __restrict__ states, const float* __restrict__ h0, float* __restrict__ ht,
     const float* __restrict__ cum, const float* __restrict__ ca, const float* __restrict__ cb) {
   scan_fwd_body<E, DK, DV, NWC, WO, WSV, PM, GT>(blockIdx.x, g, q, k, w, u, m, o, ut, states, h0, ht,
@@ -470,7 +520,7 @@ static hipError_t scan_fwd_pair_run(const Shape& s, const void* k, const void* w
 
 template <typename E, int DK, int DV, int NWC, bool WO, bool WSV, bool PM = false, bool GT = false>
 static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, const void* k,
-                               const void* w, const void* u, const void* m, void* o, void* ut,
+                               const void* w, const void* u, void* m, void* o, void* ut,
                                void* states, const float* h0, float* ht, hipStream_t st,
                                const float* cum, const float* ca, const float* cb) {
   typedef ScanFwdLds<E, DK, DV, NWC, WO, WSV, GT> L;
@@ -487,7 +537,7 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
   prof_begin(st);
   hipLaunchKernelGGL((scan_fwd_kernel<E, DK, DV, NWC, WO, WSV, PM, GT>), dim3((unsigned)blocks),
                      dim3(64 * NWC + 128), L::bytes, st, make_geom(s, table), (const E*)q, (const E*)k,
-                     (const E*)w, (const E*)u, (const E*)m, (E*)o, (E*)ut, (E*)states, h0, ht, cum, ca, cb);
+                     (const E*)w, (const E*)u, (E*)m, (E*)o, (E*)ut, (E*)states, h0, ht, cum, ca, cb);
   hipError_t e = hipGetLastError();
   prof_end(PM ? (GT ? "scan_fwd_transition_gated" : "scan_fwd_transition")
              : WO || WSV ? (GT ? "scan_fwd_gated" : "scan_fwd") : (GT ? "scan_fwd_state_gated" : "scan_fwd_state"),
@@ -499,7 +549,7 @@ static hipError_t scan_fwd_run(const Shape& s, const int* table, const void* q, 
 // only the final states (first pass of the segment-parallel scan).
 template <typename E, int DK, int DV, int NWC>
 static hipError_t scan_fwd_go(const Shape& s, const int* table, const void* q, const void* k,
-                              const void* w, const void* u, const void* m, void* o, void* ut,
+                              const void* w, const void* u, void* m, void* o, void* ut,
                               void* states, const float* h0, float* ht, hipStream_t st,
                               const float* cum, const float* ca, const float* cb) {
   const bool wsv = ut && states;
@@ -539,7 +589,7 @@ size_t lds_scan_fwd(Dt dt, int dk, int dv) {
 }
 
 hipError_t launch_scan_fwd(const Shape& s, const int* table, const void* q, const void* k,
-                           const void* w, const void* u, const void* m, void* o, void* ut,
+                           const void* w, const void* u, void* m, void* o, void* ut,
                            void* states, const float* h0, float* ht, hipStream_t st,
                            const float* cum, const float* ca, const float* cb) {
 #define EFLA_SF(E_, DK_, DV_, NWC_) \

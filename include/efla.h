@@ -93,7 +93,8 @@ typedef struct {
  *            slot = b * ceil(T/64) + c (dense batch) or chunk_start[s] + c (packed),
  *            where chunk_start[s] = sum over earlier sequences of ceil(len/64)
  *   table  : chunk_start, int32 [n_seqs+1] (packed batches only, else unused)
- *   m      : tril(Q K^T) of each chunk, [n_chunk_slots][H][64][64], problem dtype
+ *   m      : tril(Q K^T) of each chunk, [n_chunk_slots][H][64][64], problem dtype (zero above
+ *            the diagonal and in rows past the end of a sequence)
  *   x      : X = (I + strictly_lower(diag(alpha) K K^T))^{-1} of each chunk (so that
  *            T = X diag(alpha)), [n_chunk_slots][H][64][64], problem dtype
  *   coef   : bf16 problems only (empty for fp32): the per-token column scales of the chunk
@@ -181,7 +182,7 @@ efla_status efla_fwd_state(const efla_problem* p, const void* q, const void* k, 
  * static device array of EFLA_NOALLOC_WS_BYTES inside the library, one per GPU, which each GPU
  * holds until the process ends. Problems whose efla_workspace_bytes(p, 0) exceeds that size
  * return EFLA_ERR_WORKSPACE before anything is enqueued (64 MiB holds, for example, 16 heads of
- * 8,192 bf16 tokens at d_k = d_v = 128, with the library's segment plan). It allocates nothing,
+ * 16,384 bf16 tokens at d_k = d_v = 128, with the library's segment plan). It allocates nothing,
  * ever. Every call on a GPU uses that GPU's array and leaves its contents behind: calls that
  * overlap on one GPU (different streams or host threads) race; calls on one stream are ordered.
  * No part of the array has to start at zero. On the first call on a device the array's address is looked up

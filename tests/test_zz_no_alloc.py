@@ -97,7 +97,7 @@ def test_noalloc_matches_efla_fwd_state(L):
 
 def test_noalloc_rejects_problems_beyond_its_workspace(L):
     """A problem whose forward workspace exceeds the static array is refused, nothing launched."""
-    p = _lib.problem(1, 16, 16384, 128, 128, _lib.EFLA_BF16)
+    p = _lib.problem(1, 16, 32768, 128, 128, _lib.EFLA_BF16)
     assert L.efla_workspace_bytes(ctypes.byref(p), 0) > _lib.NOALLOC_WS_BYTES
     t = torch.empty(16, dtype=torch.uint8, device="cuda")
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
