@@ -122,17 +122,17 @@ __device__ __forceinline__ void scan_fwd_body(
     const int n = rows_of(c);
     const int64_t r0 = base + (int64_t)c * kChunk;
     const int64_t unit = (int64_t)(si.slot0 + c) * g.H + h;
-    if constexpr (XF) dma_tile<E, 64, NWL>(st + L::oW, w + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
-    else dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
-    if constexpr (!PM) dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
+    // K, Q and (gated) the running log-decay sums first: with the output, XF forms M from them
+    // (mtile below) while the rest lands. The per-token vectors (64 floats each) by LDS DMA too.
     dma_tile<E, DK, NWL>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
     if constexpr (WO) {
       dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
-      // XF: M is formed from the Q and K tiles by this wave once they have landed (mtile below)
       if constexpr (!XF) dma_tile<E, 64, NWL>(st + L::oM, m + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
     }
-    // the per-token vectors (64 floats each) by LDS DMA as well
     if constexpr (GT) dma_vec64(st + L::oC, cum + unit * kChunk, lane);
+    if constexpr (XF) dma_tile<E, 64, NWL>(st + L::oW, w + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
+    else dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
+    if constexpr (!PM) dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
     if constexpr (XF) {
       dma_vec64(st + L::oA, ca + unit * kChunk, lane);
       if constexpr (GT) dma_vec64(st + L::oA + 64 * 4, cb + unit * kChunk, lane);
@@ -414,11 +414,16 @@ __device__ __forceinline__ void scan_fwd_body(
     // with the output, U (or V) unless PM
     constexpr int NWARM = NL * (2 + (WO ? (XF ? 1 : 2) : 0) + (PM ? 0 : 1));
     static_assert(NWARM <= 15, "vmcnt field");
-    // XF with the output: once a chunk's tiles have landed, this wave forms its M into the
-    // chunk's stage (the compute waves work on the other stage meanwhile)
+    // XF with the output: once a chunk's K and Q tiles (and gated, its decay sums) have landed,
+    // this wave forms its M into the chunk's stage (the compute waves work on the other stage
+    // meanwhile); the requests issued after them (X, V, alpha~, b) and the warm-up may still be
+    // in flight
     auto mtile = [&](int slot) {
       if constexpr (XF && WO) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | NWARM);  // vmcnt(NWARM): the chunk's DMA has landed
+        constexpr int NAFT = NWARM + Swz<E, 64>::BYTES / 1024 / NWL +
+                             (PM ? 0 : Swz<E, TV, 2>::BYTES / 1024 / NWL) + 1 + (GT ? 1 : 0);  // warm-up; X, V; alpha~, b
+        static_assert(NAFT < 64, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt((NAFT & 15) | ((NAFT >> 4) << 14) | 0x0F70);
         unsigned char* st = smem + slot * L::stage;
         m_tile<E, DK, GT>(st + L::oM, st + L::oQ, st + L::oK, (const float*)(st + L::oC), lane);
       }
