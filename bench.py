@@ -115,9 +115,12 @@ def ingest_counters(fetch_csv, write_csv, probe_mib):
     import csv
     import collections
 
+    import gzip
+
     def per_kernel(path, counter):  # kernel symbol -> (mean per dispatch, dispatches)
         vals = collections.defaultdict(list)
-        for r in csv.DictReader(open(path)):
+        opener = gzip.open if path.endswith(".gz") else open
+        for r in csv.DictReader(opener(path, "rt")):
             if r["Counter_Name"] == counter:
                 vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}

@@ -679,10 +679,23 @@ EFLA_DEV void m_tile(unsigned char* sm, const unsigned char* sq, const unsigned 
   for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
     for (int kd = 0; kd < KS; ++kd) kf[sb][kd] = frag_rm_sw<E, DK>(sk, 16 * sb, kd * KC, lane);
+  // gated: every decay sum this lane needs, read up front (rows t = 16 tb + cl, columns
+  // s = 16 sb + g4 + i), so the decay factors below wait for no LDS read
+  // (scaled by log2 e once, so that each factor e^{c_t - c_s} is one subtraction and one exp2)
+  float crow[4];
+  f32x4 ccol[4];
+  if constexpr (GT) {
+    constexpr float kLog2e = 1.44269504088896341f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      crow[b] = c[16 * b + cl] * kLog2e;
+      ccol[b] = *(const f32x4*)(c + 16 * b + g4) * kLog2e;
+    }
+  }
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const int t = 16 * tb + cl;
-    const float ct = GT ? c[t] : 0.f;
+    const float ct = GT ? crow[tb] : 0.f;
     V qf[KS];
 #pragma unroll
     for (int kd = 0; kd < KS; ++kd) qf[kd] = frag_rm_sw<E, DK>(sq, 16 * tb, kd * KC, lane);
@@ -697,8 +710,8 @@ EFLA_DEV void m_tile(unsigned char* sm, const unsigned char* sq, const unsigned 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {  // element i: row t, column s = 16 sb + g4 + i
           const int s = 16 * sb + g4 + i;
-          if constexpr (GT) m[i] = s <= t ? m[i] * exp_decay(ct - c[s]) : 0.f;
-          else m[i] = s <= t ? m[i] : 0.f;
+          if constexpr (GT) m[i] *= __builtin_amdgcn_exp2f(ct - ccol[sb][i]);
+          if (sb == tb) m[i] = s <= t ? m[i] : 0.f;  // below the diagonal blocks, s < t always
         }
       }
       if constexpr (sizeof(E) == 2)
