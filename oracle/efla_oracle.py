@@ -486,6 +486,22 @@ def gated_chunk_forward(q, k, v, beta, gate, scale=1.0, chunk=CHUNK, initial_sta
     return dict(o=o, final=final, W=Wf, U=Uf, Ut=Ut, cum=cum)
 
 
+def gated_chunk_factors(q, k, beta, gate, mode="exact"):
+    """Per-chunk factors of gated EFLA that the forward keeps for the backward pass (section 3.4
+    reading above, in the chunk form of gated_chunk_forward). q, k: [C, dk]; beta, gate: [C].
+    With c the running sum of the chunk's log-decays and D_ts = e^{c_t - c_s} (s <= t):
+    M = tril(Q K^T) * D, the decayed causal scores of the intra-chunk read-out, and
+    X = (I + strictly_lower(diag(alpha) K K^T * D))^{-1}."""
+    q, k, beta, gate = _f64(q), _f64(k), _f64(beta), _f64(gate)
+    C = k.shape[0]
+    co = gated_coefficients(k, beta, gate, mode)
+    cc = np.cumsum(gate)
+    D = np.exp(np.tril(cc[:, None] - cc[None, :]))
+    A = np.tril(co["alpha"][:, None] * D * (k @ k.T), -1)
+    X = scipy.linalg.solve_triangular(np.eye(C) + A, np.eye(C), lower=True, unit_diagonal=True)
+    return dict(X=X, M=np.tril(q @ k.T) * D)
+
+
 def gated_chunk_backward(q, k, v, beta, gate, do, scale=1.0, chunk=CHUNK, initial_state=None,
                          d_final_state=None, mode="exact"):
     """Chunkwise gated backward (dense batches): the reverse-mode form of gated_chunk_forward,

@@ -233,6 +233,48 @@ def test_gated_packed_sequences(E):
         _check(nm, _np(t), ref[nm])
 
 
+FACTOR_CASES = [  # name, workload overrides, gate mean, packed sequence lengths
+    ("dense_mild", dict(B=2, H=3, T=64 * 3 + 21), 3.0, None),
+    ("dense_strong_d64", dict(B=1, H=2, T=64 * 2 + 40, dk=64, dv=64), 0.0, None),
+    ("packed", dict(B=1, H=2), 1.0, [70, 200, 1, 64, 133]),
+]
+
+
+@pytest.mark.parametrize("name,wl,mu,lens", FACTOR_CASES, ids=[c[0] for c in FACTOR_CASES])
+def test_gated_saved_chunk_factors(E, name, wl, mu, lens):
+    """The decayed M = tril(Q K^T) * e^{c_t - c_s} (formed by the forward scan) and X that the gated
+    forward saves for the backward, per (chunk slot, head), against oracle.gated_chunk_factors
+    (pinned in test_oracle_pins against the token recurrence). X's rows past the end of a sequence
+    are padding; M is zero above the diagonal and in those rows."""
+    cu = None
+    if lens:
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        wl = dict(wl, T=int(cu[-1]))
+    w = workload(2, **wl)
+    inp = make_inputs(w, with_grad=False)
+    B, H, T, dk = inp["k"].shape
+    a = _gates((B, H, T), mu, 23)
+    print("%s: B=%d H=%d T=%d dk=%d" % (name, B, H, T, dk), flush=True)
+    q, k, v, beta, g = (_dev(x) for x in (inp["q"], inp["k"], inp["v"], inp["beta"], a))
+    cu_d = None if cu is None else torch.from_numpy(cu).cuda()
+    _, saved = E.efla_fwd_gated(q, k, v, beta, g, 0.8, cu_d, save=True)
+    views = E.saved_views(saved, q, k, v, beta, 0.8, cu_d)
+    gm, gx = _np(views["m"]), _np(views["x"])
+    slot, worst = 0, 0.0
+    for (b, s0, e0) in O.sequences(B, T, cu):
+        for c0 in range(s0, e0, O.CHUNK):
+            n = min(e0, c0 + O.CHUNK) - c0
+            for h in range(H):
+                sl = slice(c0, c0 + n)
+                ref = O.gated_chunk_factors(inp["q"][b, h, sl], inp["k"][b, h, sl], inp["beta"][b, h, sl], a[b, h, sl])
+                em, ex = O.rel_err(gm[slot, h, :n, :n], ref["M"]), O.rel_err(gx[slot, h, :n, :n], ref["X"])
+                worst = max(worst, em, ex)
+                assert em <= TOL and ex <= TOL, (slot, h, em, ex)
+                assert not np.any(np.triu(gm[slot, h], 1)) and not np.any(gm[slot, h, n:]), ("M zeros", slot, h)
+            slot += 1
+    print("  M, X worst normwise rel err per (chunk, head) %.3e (tol %.0e)" % (worst, TOL), flush=True)
+
+
 @pytest.mark.parametrize("segments", [1, 3])
 def test_positive_gate_follows_formula(E, segments):
     """Log-decays of either sign, a ~ N(0.01, 0.03): a > 0 is growth, outside the decay reading,

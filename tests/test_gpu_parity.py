@@ -166,11 +166,13 @@ def test_stage_values_match_chunk_oracle(E, widx):
     _check("S_c", gpu["states"][: len(states)], states, tol, per_head=False)
 
 
-@pytest.mark.parametrize("widx,over", [(2, dict(B=2, H=2, T=150)), (5, dict(H=2))])
+@pytest.mark.parametrize("widx,over", [(2, dict(B=2, H=2, T=150)), (5, dict(H=2)),
+                                       (4, dict(B=1, H=2, T=150))])
 def test_saved_chunk_factors_match_oracle(E, widx, over):
     """M = tril(Q K^T) and X = (I + A)^{-1} that the forward saves for the backward, per
-    (chunk slot, head), on a ragged dense batch and on a packed batch. Rows past the end of
-    a sequence are padding and are not compared."""
+    (chunk slot, head), on a ragged dense batch and on a packed batch (bf16: M formed by the
+    forward scan), and fp32 (M formed by the UT kernel). X's rows past the end of a sequence are
+    padding and are not compared; M is zero above the diagonal and in those rows."""
     w = workload(widx, **over)
     inp = make_inputs(w, with_grad=False)
     dt = TDT[w.dtype]
@@ -190,6 +192,7 @@ def test_saved_chunk_factors_match_oracle(E, widx, over):
                                       inp["beta"][b, h, c0:c0 + n])
                 assert O.rel_err(gm[slot, h, :n, :n], ref["M"]) <= tol, ("M", slot, h)
                 assert O.rel_err(gx[slot, h, :n, :n], ref["X"]) <= tol, ("X", slot, h)
+                assert not np.any(np.triu(gm[slot, h], 1)) and not np.any(gm[slot, h, n:]), ("M zeros", slot, h)
             slot += 1
 
 

@@ -578,6 +578,28 @@ def test_gated_chunk_form_equals_token_recurrence():
     assert O.rel_err(ob["o"], o) > 1e-3
 
 
+@pytest.mark.parametrize("C", [64, 37])
+def test_gated_chunk_factors_reproduce_token_recurrence(C):
+    """From a zero state one chunk's read-out is o = scale M (X diag(b) V): the decayed M and X of
+    gated_chunk_factors against the token recurrence (strong decays; a full and a ragged chunk).
+    A zero gate gives chunk_factors' M and X."""
+    r = _rng(150 + C)
+    dk, dv = 8, 5
+    q, k, v = r.standard_normal((C, dk)), r.standard_normal((C, dk)) * 0.7, r.standard_normal((C, dv))
+    beta, a = r.uniform(0, 1, C), -r.uniform(0, 1.5, C)
+    f = O.gated_chunk_factors(q, k, beta, a)
+    b = O.gated_coefficients(k, beta, a)["b"]
+    o = 0.7 * f["M"] @ (f["X"] @ (b[:, None] * v))
+    ref, _ = O.gated_forward(q[None, None], k[None, None], v[None, None], beta[None, None], a[None, None], scale=0.7)
+    assert O.rel_err(o, ref[0, 0]) < 1e-12
+    # the decay taken the wrong way round (e^{c_s - c_t}) is caught
+    bad = np.tril(q @ k.T) * np.exp(np.tril(np.cumsum(a)[None, :] - np.cumsum(a)[:, None]))
+    assert O.rel_err(0.7 * bad @ (f["X"] @ (b[:, None] * v)), ref[0, 0]) > 1e-3
+    z = O.gated_chunk_factors(q, k, beta, np.zeros(C))
+    u = O.chunk_factors(q, k, beta)
+    assert O.rel_err(z["M"], u["M"]) < 1e-14 and O.rel_err(z["X"], u["X"]) < 1e-14
+
+
 @pytest.mark.parametrize("mode", ["exact", "euler"])
 def test_gated_backward_against_central_differences(mode):
     """Every coordinate of every input of gated EFLA (q, k, v, beta, gate, initial state) by
