@@ -88,11 +88,36 @@ def kernel_model(name, dk, dv, e, C=CHUNK):
     return float(b), float(f)
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines (string and character literals kept), so
+    that edits to comments leave a kernel's hash unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def _source_sha(name):
+    """Hash of the code (comments excluded) of the sources a kernel is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(name, []):
-        with open(os.path.join(ROOT, "delta_rule_sequence_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "delta_rule_sequence_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -2,7 +2,7 @@
 //
 // Reverse-mode differentiation of the chunk recurrence of section 3.3 (Exact Flow Linear
 // Attention summary page): with G the gradient of the state leaving chunk c,
-//   dU~_c = scale M_c^T dO_c + K_c G,          M_c = tril(Q_c K_c^T) from the UT kernel,
+//   dU~_c = scale M_c^T dO_c + K_c G,          M_c = tril(Q_c K_c^T) saved by the forward,
 //   G    <- G + scale Q_c^T dO_c - W_c^T dU~_c (gradient of the state entering c).
 // One workgroup walks the chunks of one (sequence, head) backwards and owns a d_k x TV
 // slice of G, kept transposed (G^T, TV x d_k) in fp32 MFMA accumulators. It writes dU~ and,

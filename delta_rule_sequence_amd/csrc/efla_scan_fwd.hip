@@ -4,8 +4,10 @@
 // outputs). One workgroup walks the chunks of one (sequence, head) in order and owns a
 // d_k x TV slice of the state (TV = 16 columns per wave):
 //   U~ = U - W S,   O = scale (Q S + M U~),   S <- S + K^T U~,
-// with M = tril(Q K^T) from the UT kernel. The diagonal of tril is kept because token t
-// reads the state after its own update. bf16 problems read the UT factor X = (I + A)^{-1}, V
+// with M = tril(Q K^T) (fp32: from the UT kernel; bf16: formed here from the staged Q and K
+// tiles, and written out for the backward when a saved buffer is given). The diagonal of tril is
+// kept because token t reads the state after its own update. bf16 problems read the UT factor
+// X = (I + A)^{-1}, V
 // and the per-token scales alpha~ (gated alpha e^{c}) and b instead of W = X diag(alpha~) K
 // and U = X diag(b) V, and form U~ = X Y with Y = diag(b) V - diag(alpha~) K S: one more short
 // product per chunk (X is lower triangular) for a quarter of W's bytes and no U at all.
@@ -16,10 +18,11 @@
 // U~ -> K^T U~ -> S runs inside one wave's registers with no LDS round trip. Accumulator rows (of S, and the
 // token rows of U~ and O) are numbered in the contiguous-contraction order (prow), so every
 // A operand from LDS is a single 16-byte read. Two further waves move the data, each in a loop
-// of its own with the same barrier sequence: the loader wave fills swizzled LDS tiles of W, Q,
-// K, M and U one chunk ahead by LDS DMA (double-buffered) and warms L2 for the chunk after; the
-// storer wave copies the staged O, U~ and chunk states out as 16-byte rows. Kept apart from the
-// loads, the output stores are never waited for. One barrier per chunk hands the buffers over.
+// of its own with the same barrier sequence: the loader wave fills swizzled LDS tiles of K, Q,
+// the factor and U (or V), and M (fp32), one chunk ahead by LDS DMA (double-buffered), forms M
+// (bf16) once K and Q have landed, and warms L2 for the chunk after; the storer wave copies the
+// staged O, U~ and chunk states (and M's rows) out as 16-byte rows. Kept apart from the loads,
+// the output stores are never waited for. One barrier per chunk hands the buffers over.
 #include "efla_internal.hpp"
 
 namespace efla {

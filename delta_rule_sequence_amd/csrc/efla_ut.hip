@@ -11,7 +11,9 @@
 // V is read only for them), M (q may be null), X, and the per-token column scales of the two
 // factors, alpha~ = alpha (gated: alpha e^{c}) and b (gated). The bf16 forward keeps only X and
 // the scales: its scans form U~ = U - W S = X (diag(b) V - diag(alpha~) K S) themselves, which
-// moves less data than W and U (X is a quarter of W's size at d = 128); X also serves the
+// moves less data than W and U (X is a quarter of W's size at d = 128), and its forward scan
+// forms M from the Q and K tiles it stages anyway, so this kernel reads no Q there (it still
+// forms M where no output scan follows: the backward's recomputed forward); X also serves the
 // backward pass, which then needs no inverse of its own.
 //
 // Gated EFLA (GT): with c_t the running sum of the log-decays inside the chunk,
