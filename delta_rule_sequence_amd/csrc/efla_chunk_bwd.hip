@@ -43,7 +43,10 @@ constexpr int kBwdThreads = 512;
 
 template <typename E, int DK, int DV, bool GT = false>
 struct ChunkBwdLds {
-  static constexpr int LK = pitch<E>(DK), LV = pitch<E>(DV), LT = pitch<E>(64);
+  // bf16: d-wide rows padded by 32 bytes rather than 16 (fewer LDS bank conflicts in this
+  // kernel's mix of row-major and transposed reads; measured 2% faster at d = 128)
+  static constexpr int PADE = sizeof(E) == 2 ? 16 / (int)sizeof(E) : 0;
+  static constexpr int LK = pitch<E>(DK) + PADE, LV = pitch<E>(DV) + PADE, LT = pitch<E>(64);
   static constexpr size_t TK = 64 * LK * sizeof(E), TV = 64 * LV * sizeof(E),
                           TT = 64 * LT * sizeof(E);
   static constexpr size_t oK = 0;                // K   [64][LK]
