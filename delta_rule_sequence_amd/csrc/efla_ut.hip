@@ -26,7 +26,10 @@ namespace efla {
 
 template <typename E, int DK, int DV, bool GT = false>
 struct UtFwdLds {
-  static constexpr int LK = pitch<E>(DK), LT = pitch<E>(64), LV = pitch<E>(DV), LF = kPitchF;
+  // bf16: K and V rows padded by 32 bytes rather than 16 (fewer LDS bank conflicts; measured
+  // slightly faster)
+  static constexpr int PADE = sizeof(E) == 2 ? 16 / (int)sizeof(E) : 0;
+  static constexpr int LK = pitch<E>(DK) + PADE, LT = pitch<E>(64), LV = pitch<E>(DV) + PADE, LF = kPitchF;
   static constexpr size_t oK = 0;                                   // K        [64][LK]
   static constexpr size_t oV = oK + 64 * LK * sizeof(E);            // V        [64][LV]
   static constexpr size_t oA = oV + 64 * LV * sizeof(E);            // A (fp32) [64][LF]; later T
@@ -37,6 +40,7 @@ struct UtFwdLds {
   static constexpr size_t oT2 = oCm + 64 * 4;                       // X diag(b) [64][LT] (GT)
   static constexpr size_t bytes = GT ? oT2 + 64 * LT * sizeof(E) : oAl + 64 * 4;
   static_assert(64 * LT * sizeof(E) <= 64 * LF * 4, "T and M must fit in an fp32 work matrix");
+  static_assert(sizeof(E) == 4 || 2 * bytes <= 160 * 1024, "bf16: two workgroups per compute unit");
 };
 
 // Persistent: the workgroup walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...; the
