@@ -424,27 +424,40 @@ EFLA_DEV void s2g(E* __restrict__ g, int64_t gld, const E* s, int ld, int nvalid
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename E, int COLS, int SH = 0>
+template <typename E, int COLS, int SH = 0, int MX = 0>
 struct Swz {
   static constexpr int RB = COLS * (int)sizeof(E);  // bytes per row
   static constexpr int NCH = RB / 16;
   static constexpr int BYTES = 64 * RB;
   static_assert((NCH & (NCH - 1)) == 0 && BYTES % 1024 == 0, "swizzled tile shape");
-  // byte offset of element (r, c); the chunk index is XORed with bits SH.. of the row
-  // (SH = 2 for tiles read in accumulator layout, whose lanes hold rows 4 (lane >> 4) + i)
+  // The 16-byte chunk index of row r is XORed with mask(r): bits SH.. of the row (SH = 2 for
+  // tiles read in accumulator layout, whose lanes hold rows 4 (lane >> 4) + i). MX = 1 selects,
+  // for bf16 rows of 128 elements, a mask built so that none of the tile's readers meets a bank
+  // conflict it can avoid: with row bits r0..r4 the mask bits are (r2 ^ r3, r0, r1, r3 ^ r4). It
+  // is one-to-one on any 16 consecutive rows (16-byte row-major reads), on the rows
+  // prow(b, 0..15) of an A operand, and, in bits 1..3, on the rows {0..3, 8..11} + const of a
+  // transposed read of two adjacent chunks. (It costs a few more instructions per address than
+  // the plain mask, which some kernels cannot spare.)
+  EFLA_DEV static int mask(int r) {
+    if constexpr (MX == 1 && sizeof(E) == 2 && COLS == 128 && SH == 0)
+      return (((r >> 2) ^ (r >> 3)) & 1) | ((r & 3) << 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 3);
+    else
+      return (r >> SH) & (NCH - 1);
+  }
+  // byte offset of element (r, c)
   EFLA_DEV static int off(int r, int c) {
     const int b = c * (int)sizeof(E);
-    return r * RB + (((b >> 4) ^ ((r >> SH) & (NCH - 1))) << 4) + (b & 15);
+    return r * RB + (((b >> 4) ^ mask(r)) << 4) + (b & 15);
   }
 };
 
 // Request rows [0, 64) of a [64][COLS] tile (row r at g + r * gld; rows >= n repeat row n - 1,
 // so every address stays inside the chunk) into the swizzled LDS tile at dst. The NW waves
 // that call it share the instructions: wave wi issues numbers wi, wi + NW, ...
-template <typename E, int COLS, int NW, int SH = 0>
+template <typename E, int COLS, int NW, int SH = 0, int MX = 0>
 EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld, int n, int wi,
                        int lane) {
-  typedef Swz<E, COLS, SH> S;
+  typedef Swz<E, COLS, SH, MX> S;
   constexpr int NI = S::BYTES / 1024;
   static_assert(NI % NW == 0, "DMA split");
 #pragma unroll
@@ -452,7 +465,7 @@ EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld,
     const int j = jj * NW + wi;
     const int byte = j * 1024 + lane * 16;
     const int r = byte / S::RB, pc = (byte % S::RB) >> 4;
-    const int lc = pc ^ ((r >> SH) & (S::NCH - 1));
+    const int lc = pc ^ S::mask(r);
     const E* src = g + (int64_t)min(r, n - 1) * gld + lc * (16 / (int)sizeof(E));
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
   }
@@ -555,9 +568,9 @@ template <typename E> EFLA_DEV constexpr int prow(int b, int r) {
 // A operand, row-major in a swizzled tile, for a product whose B operand is bop_acc of
 // prow-ordered accumulators and whose result is prow-ordered: output tile rb takes rows
 // prow(rb, lane & 15), contraction slots ks.
-template <typename E, int COLS>
+template <typename E, int COLS, int MX = 0>
 EFLA_DEV typename Mma<E>::vec aop_rc(const unsigned char* t, int rb, int ks, int lane) {
-  typedef Swz<E, COLS> S;
+  typedef Swz<E, COLS, 0, MX> S;
   const int r = prow<E>(rb, lane & 15), g = lane >> 4;
   if constexpr (sizeof(E) == 2) return *(const bf16x8*)(t + S::off(r, 32 * ks + 8 * g));
   else return *(const f32x4*)(t + S::off(r, 16 * ks + 4 * g));
@@ -565,9 +578,9 @@ EFLA_DEV typename Mma<E>::vec aop_rc(const unsigned char* t, int rb, int ks, int
 
 // The same with the contraction index along the tile's rows (k-major, LDS transpose reads
 // for bf16): output tile b takes columns prow(b, lane & 15).
-template <typename E, int COLS>
+template <typename E, int COLS, int MX = 0>
 EFLA_DEV typename Mma<E>::vec aop_kc(const unsigned char* t, int b, int ks, int lane) {
-  typedef Swz<E, COLS> S;
+  typedef Swz<E, COLS, 0, MX> S;
   const int i = lane & 15, g = lane >> 4;
   if constexpr (sizeof(E) == 2) {
     // transpose read: output lane j, slot s gets element j % 4 of the 8-byte row that lane
@@ -603,14 +616,14 @@ EFLA_DEV typename Mma<E>::vec aop_kc_ld(const E* t, int ld, int b, int ks, int l
 // swizzled LDS tile (swizzle keyed on row >> SH): frag_rm_sw reads A[m0 + (lane & 15)][k0..] with
 // A[m][k] at (m, k); frag_km_sw reads X[k0..][m0 + (lane & 15)] with X stored at (k, m), by
 // transpose reads.
-template <typename E, int COLS, int SH = 0>
+template <typename E, int COLS, int SH = 0, int MX = 0>
 EFLA_DEV typename Mma<E>::vec frag_rm_sw(const unsigned char* t, int m0, int k0, int lane) {
-  typedef Swz<E, COLS, SH> S;
+  typedef Swz<E, COLS, SH, MX> S;
   return *(const typename Mma<E>::vec*)(t + S::off(m0 + (lane & 15), k0 + (lane >> 4) * (Mma<E>::KC / 4)));
 }
-template <typename E, int COLS, int SH = 0>
+template <typename E, int COLS, int SH = 0, int MX = 0>
 EFLA_DEV typename Mma<E>::vec frag_km_sw(const unsigned char* t, int k0, int m0, int lane) {
-  typedef Swz<E, COLS, SH> S;
+  typedef Swz<E, COLS, SH, MX> S;
   const int gq = lane >> 4, i = lane & 15;
   if constexpr (sizeof(E) == 2) {
     const int r = k0 + 8 * gq + (i >> 2), c = m0 + 4 * (i & 3);
@@ -661,13 +674,13 @@ struct FlowCoef {
 EFLA_DEV float exp_decay(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
 // M = tril(Q K^T) of one chunk (gated: M_ts = e^{c_t - c_s} q_t . k_s for s <= t) from the
-// swizzled [64][DK] Q and K tiles into the swizzled [64][64] M tile, by one wave: the ten blocks
+// swizzled [64][DK] Q and K tiles (mask MX) into the swizzled [64][64] M tile, by one wave: the ten blocks
 // on and below the diagonal, and zeros in blocks (0,1) and (2,3), which readers that step over
 // the columns 32 at a time also read. Formed transposed (K Q^T), so that a lane holds four
 // consecutive columns of one row and stores them at once; every K and Q fragment is read from
 // LDS once (K's for the whole tile, Q's per row block). c: the chunk's running log-decay sums in
 // LDS (gated). The scans' loader waves call it once a chunk's tiles have landed.
-template <typename E, int DK, bool GT>
+template <typename E, int DK, bool GT, int MX = 0>
 EFLA_DEV void m_tile(unsigned char* sm, const unsigned char* sq, const unsigned char* sk,
                      const float* c, int lane) {
   typedef Swz<E, 64> SM;
@@ -678,7 +691,7 @@ EFLA_DEV void m_tile(unsigned char* sm, const unsigned char* sq, const unsigned 
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-    for (int kd = 0; kd < KS; ++kd) kf[sb][kd] = frag_rm_sw<E, DK>(sk, 16 * sb, kd * KC, lane);
+    for (int kd = 0; kd < KS; ++kd) kf[sb][kd] = frag_rm_sw<E, DK, 0, MX>(sk, 16 * sb, kd * KC, lane);
   // gated: every decay sum this lane needs, read up front (rows t = 16 tb + cl, columns
   // s = 16 sb + g4 + i), so the decay factors below wait for no LDS read
   // (scaled by log2 e once, so that each factor e^{c_t - c_s} is one subtraction and one exp2)
@@ -698,7 +711,7 @@ EFLA_DEV void m_tile(unsigned char* sm, const unsigned char* sq, const unsigned 
     const float ct = GT ? crow[tb] : 0.f;
     V qf[KS];
 #pragma unroll
-    for (int kd = 0; kd < KS; ++kd) qf[kd] = frag_rm_sw<E, DK>(sq, 16 * tb, kd * KC, lane);
+    for (int kd = 0; kd < KS; ++kd) qf[kd] = frag_rm_sw<E, DK, 0, MX>(sq, 16 * tb, kd * KC, lane);
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       const bool zero_blk = (tb == 0 && sb == 1) || (tb == 2 && sb == 3);

@@ -37,7 +37,9 @@ struct ScanFwdLds {
   static constexpr bool XF = sizeof(E) == 2;
   static constexpr int TV = 16 * NWC;
   static constexpr int NWL = 1;  // loader waves (one; a second wave stores the outputs)
-  typedef Swz<E, DK> SK;
+  // the [64][DK] tiles (K, Q, and W for fp32) take the conflict-free row mask (MXK, in Swz)
+  static constexpr int MXK = 1;
+  typedef Swz<E, DK, 0, MXK> SK;
   typedef Swz<E, 64> SM;
   typedef Swz<E, TV, 2> SU;  // read in accumulator layout
   static constexpr size_t oW = 0;                              // X [64][64] (XF) or W [64][DK]
@@ -127,14 +129,14 @@ __device__ __forceinline__ void scan_fwd_body(
     const int64_t unit = (int64_t)(si.slot0 + c) * g.H + h;
     // K, Q and (gated) the running log-decay sums first: with the output, XF forms M from them
     // (mtile below) while the rest lands. The per-token vectors (64 floats each) by LDS DMA too.
-    dma_tile<E, DK, NWL>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
+    dma_tile<E, DK, NWL, 0, L::MXK>(st + L::oK, k + r0 * DK, DK, n, wl, lane);
     if constexpr (WO) {
-      dma_tile<E, DK, NWL>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
+      dma_tile<E, DK, NWL, 0, L::MXK>(st + L::oQ, q + r0 * DK, DK, n, wl, lane);
       if constexpr (!XF) dma_tile<E, 64, NWL>(st + L::oM, m + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
     }
     if constexpr (GT) dma_vec64(st + L::oC, cum + unit * kChunk, lane);
     if constexpr (XF) dma_tile<E, 64, NWL>(st + L::oW, w + unit * kChunk * kChunk, kChunk, kChunk, wl, lane);
-    else dma_tile<E, DK, NWL>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
+    else dma_tile<E, DK, NWL, 0, L::MXK>(st + L::oW, w + r0 * DK, DK, n, wl, lane);
     if constexpr (!PM) dma_tile<E, TV, NWL, 2>(st + L::oU, u + r0 * DV + v0, DV, n, wl, lane);
     if constexpr (XF) {
       dma_vec64(st + L::oA, ca + unit * kChunk, lane);
@@ -229,8 +231,8 @@ __device__ __forceinline__ void scan_fwd_body(
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
-        aw[rb][ks] = aop_rc<E, DK>(st + (XF ? L::oK : L::oW), rb, ks, lane);
-        if constexpr (WO) aq[rb][ks] = aop_rc<E, DK>(st + L::oQ, rb, ks, lane);
+        aw[rb][ks] = aop_rc<E, DK, L::MXK>(st + (XF ? L::oK : L::oW), rb, ks, lane);
+        if constexpr (WO) aq[rb][ks] = aop_rc<E, DK, L::MXK>(st + L::oQ, rb, ks, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -292,7 +294,7 @@ __device__ __forceinline__ void scan_fwd_body(
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) ak[b][ks] = aop_kc<E, DK>(st + L::oK, b, ks, lane);
+      for (int ks = 0; ks < KST; ++ks) ak[b][ks] = aop_kc<E, DK, L::MXK>(st + L::oK, b, ks, lane);
     if constexpr (WO) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
@@ -428,7 +430,7 @@ __device__ __forceinline__ void scan_fwd_body(
         static_assert(NAFT < 64, "vmcnt field");
         __builtin_amdgcn_s_waitcnt((NAFT & 15) | ((NAFT >> 4) << 14) | 0x0F70);
         unsigned char* st = smem + slot * L::stage;
-        m_tile<E, DK, GT>(st + L::oM, st + L::oQ, st + L::oK, (const float*)(st + L::oC), lane);
+        m_tile<E, DK, GT, L::MXK>(st + L::oM, st + L::oQ, st + L::oK, (const float*)(st + L::oC), lane);
       }
     };
     issue(0, 0);
