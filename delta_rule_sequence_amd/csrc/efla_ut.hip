@@ -24,34 +24,38 @@
 
 namespace efla {
 
-template <typename E, int DK, int DV, bool GT = false>
+// WU: the launch writes W and U (V is read for U). Without them (the bf16 factor form) there is
+// no V tile, and a bf16 workgroup's LDS is small enough for three per compute unit.
+template <typename E, int DK, int DV, bool GT = false, bool WU = true>
 struct UtFwdLds {
   // bf16: K and V rows padded by 32 bytes rather than 16 (fewer LDS bank conflicts; measured
   // slightly faster)
   static constexpr int PADE = sizeof(E) == 2 ? 16 / (int)sizeof(E) : 0;
   static constexpr int LK = pitch<E>(DK) + PADE, LT = pitch<E>(64), LV = pitch<E>(DV) + PADE, LF = kPitchF;
   static constexpr size_t oK = 0;                                   // K        [64][LK]
-  static constexpr size_t oV = oK + 64 * LK * sizeof(E);            // V        [64][LV]
-  static constexpr size_t oA = oV + 64 * LV * sizeof(E);            // A (fp32) [64][LF]; later T
+  static constexpr size_t oV = oK + 64 * LK * sizeof(E);            // V        [64][LV] (WU)
+  static constexpr size_t oA = oV + (WU ? 64 * LV * sizeof(E) : 0); // A (fp32) [64][LF]; later T
   static constexpr size_t oX = oA + 64 * LF * 4;                    // X (fp32) [64][LF]; M staging first
   static constexpr size_t oAl = oX + 64 * LF * 4;                   // alpha    [64]
   static constexpr size_t oBl = oAl + 64 * 4;                       // b, c     [64] each (GT)
   static constexpr size_t oCm = oBl + 64 * 4;
-  static constexpr size_t oT2 = oCm + 64 * 4;                       // X diag(b) [64][LT] (GT)
-  static constexpr size_t bytes = GT ? oT2 + 64 * LT * sizeof(E) : oAl + 64 * 4;
+  static constexpr size_t oT2 = oCm + 64 * 4;                       // X diag(b) [64][LT] (GT, WU)
+  static constexpr size_t bytes = GT ? (WU ? oT2 + 64 * LT * sizeof(E) : oCm + 64 * 4) : oAl + 64 * 4;
+  // workgroups per compute unit that the LDS admits (bf16); the kernel's launch bounds match
+  static constexpr int PER_CU = sizeof(E) == 2 && !WU ? 3 : 2;
   static_assert(64 * LT * sizeof(E) <= 64 * LF * 4, "T and M must fit in an fp32 work matrix");
-  static_assert(sizeof(E) == 4 || 2 * bytes <= 160 * 1024, "bf16: two workgroups per compute unit");
+  static_assert(sizeof(E) == 4 || PER_CU * bytes <= 160 * 1024, "bf16: workgroups per compute unit");
 };
 
 // Persistent: the workgroup walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...; the
 // next unit's K, V and Q rows are requested into registers while the current one computes.
-template <typename E, int DK, int DV, bool GT>
-__global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
+template <typename E, int DK, int DV, bool GT, bool WU>
+__global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && !WU) ? 3 : 2) void ut_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ beta, const E* __restrict__ gate, E* __restrict__ w, E* __restrict__ u,
     E* __restrict__ mout, E* __restrict__ xout, float* __restrict__ cum, float* __restrict__ ca,
     float* __restrict__ cb) {
-  typedef UtFwdLds<E, DK, DV, GT> L;
+  typedef UtFwdLds<E, DK, DV, GT, WU> L;
   typedef typename Mma<E>::vec Vv;
   constexpr int KC = Mma<E>::KC, KS = DK / KC;
   constexpr int VE = 16 / (int)sizeof(E);
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     if constexpr (GT) aN = to_f(aL[c.row0 + min(lane, c.n - 1)]);  // token = lane
   };
   auto issue_v = [&](const ChunkUnit& c) {
-    if (!w) return;  // V feeds U = T V only
+    if (!WU) return;  // V feeds U = T V only
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int i = it * kThreads + tid;
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
         if constexpr (GT) sBl[r] = r < n ? gated_input_coef(bR[it], acc, aR[it], g.euler) : 0.f;
       }
     }
-    if (w) {
+    if constexpr (WU) {
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
         const int i = it * kThreads + tid;
@@ -285,13 +289,13 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
             tu[e] = (__bf16)(x0[e] * b0[e]);
             tu[e + 4] = (__bf16)(x1[e] * b1[e]);
           }
-          if (w) {
+          if (WU) {
             *(bf16x8*)(sT + r * L::LT + c) = te;
             if constexpr (GT) *(bf16x8*)(sT2 + r * L::LT + c) = tu;
           }
           if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
         } else {
-          if (w) {
+          if (WU) {
             *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
             *(f32x4*)(sT + r * L::LT + c + 4) = x1 * a1;
             if constexpr (GT) {
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
     }
     __syncthreads();
 
-    if (w) {  // uniform: every thread takes the same branch, so the barriers inside match
+    if constexpr (WU) {  // W and U: every thread takes this branch, so the barriers inside match
       // W = T K, U = T V. Wave wv owns a quarter of the columns of each over all four row
       // blocks (equal work per wave); T is lower triangular, so row blocks 0-1 need columns
       // < 32 and row blocks 2-3 all 64. Formed transposed for row-layout stores.
@@ -353,24 +357,25 @@ __global__ __launch_bounds__(kThreads, 2) void ut_fwd_kernel(
   }
 }
 
-template <typename E, int DK, int DV, bool GT>
+template <typename E, int DK, int DV, bool GT, bool WU>
 static hipError_t ut_go(const Shape& s, const int* table, const void* q, const void* k,
                         const void* v, const void* beta, const void* gate, void* w, void* u,
                         void* m, void* x, float* cum, float* ca, float* cb, hipStream_t st) {
-  typedef UtFwdLds<E, DK, DV, GT> L;
+  typedef UtFwdLds<E, DK, DV, GT, WU> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)ut_fwd_kernel<E, DK, DV, GT>,
+    hipError_t e = hipFuncSetAttribute((const void*)ut_fwd_kernel<E, DK, DV, GT, WU>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  // Persistent: two workgroups per compute unit walk the chunks.
+  // Persistent: L::PER_CU workgroups per compute unit walk the chunks.
   const int64_t units = s.slots * s.H;
   if (units < 1) return hipSuccess;
-  const int64_t blocks = units < 2 * cu_count() ? units : 2 * cu_count();
+  const int64_t slots = (int64_t)L::PER_CU * cu_count();
+  const int64_t blocks = units < slots ? units : slots;
   prof_begin(st);
-  hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV, GT>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
+  hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV, GT, WU>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
                      st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
                      (const E*)beta, (const E*)gate, (E*)w, (E*)u, (E*)m, (E*)x, cum, ca, cb);
   hipError_t e = hipGetLastError();
@@ -378,13 +383,22 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
   return e;
 }
 
+// W and U are written together (both or neither); without them the kernel reads no V.
 template <typename E, int DK, int DV>
 static hipError_t ut_dispatch(const Shape& s, const int* table, const void* q, const void* k,
                               const void* v, const void* beta, const void* gate, void* w,
                               void* u, void* m, void* x, float* cum, float* ca, float* cb,
                               hipStream_t st) {
-  if (gate) return ut_go<E, DK, DV, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
-  return ut_go<E, DK, DV, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  if (!w != !u) return hipErrorInvalidValue;
+  if (w) {
+    if (gate) return ut_go<E, DK, DV, true, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+    return ut_go<E, DK, DV, false, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  }
+  if constexpr (sizeof(E) == 2) {  // the factor form (bf16) is the only caller without W and U
+    if (gate) return ut_go<E, DK, DV, true, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+    return ut_go<E, DK, DV, false, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 size_t lds_ut_fwd(Dt dt, int dk, int dv) {
