@@ -24,39 +24,50 @@
 
 namespace efla {
 
-// WU: the launch writes W and U (V is read for U). Without them (the bf16 factor form) there is
-// no V tile, and a bf16 workgroup's LDS is small enough for three per compute unit.
-template <typename E, int DK, int DV, bool GT = false, bool WU = true>
+// WU: the launch writes W and U (V is read for U). MO: it may form M (q, mout). Without W and U
+// (the bf16 factor form) there is no V tile; without M as well, nothing reads K once A is formed,
+// so X takes K's place (KX). A bf16 workgroup's LDS then admits three (four with KX) workgroups
+// per compute unit.
+// Workgroups per compute unit that the LDS admits (the kernel's launch bounds match).
+template <typename E> constexpr int ut_per_cu(bool wu, bool mo) {
+  return sizeof(E) == 2 && !wu ? (mo ? 3 : 4) : 2;
+}
+
+template <typename E, int DK, int DV, bool GT = false, bool WU = true, bool MO = true>
 struct UtFwdLds {
+  static constexpr bool KX = !WU && !MO;
   // bf16: K and V rows padded by 32 bytes rather than 16 (fewer LDS bank conflicts; measured
   // slightly faster)
   static constexpr int PADE = sizeof(E) == 2 ? 16 / (int)sizeof(E) : 0;
   static constexpr int LK = pitch<E>(DK) + PADE, LT = pitch<E>(64), LV = pitch<E>(DV) + PADE, LF = kPitchF;
+  static constexpr size_t TKB = 64 * LK * sizeof(E), TFB = 64 * LF * 4;
   static constexpr size_t oK = 0;                                   // K        [64][LK]
-  static constexpr size_t oV = oK + 64 * LK * sizeof(E);            // V        [64][LV] (WU)
+  static constexpr size_t oV = KX && TFB > TKB ? TFB : TKB;         // V        [64][LV] (WU)
   static constexpr size_t oA = oV + (WU ? 64 * LV * sizeof(E) : 0); // A (fp32) [64][LF]; later T
-  static constexpr size_t oX = oA + 64 * LF * 4;                    // X (fp32) [64][LF]; M staging first
-  static constexpr size_t oAl = oX + 64 * LF * 4;                   // alpha    [64]
+  static constexpr size_t oX = KX ? oK : oA + TFB;                  // X (fp32) [64][LF]; M staging first
+  static constexpr size_t oAl = (KX ? oA : oX) + TFB;               // alpha    [64]
   static constexpr size_t oBl = oAl + 64 * 4;                       // b, c     [64] each (GT)
   static constexpr size_t oCm = oBl + 64 * 4;
   static constexpr size_t oT2 = oCm + 64 * 4;                       // X diag(b) [64][LT] (GT, WU)
   static constexpr size_t bytes = GT ? (WU ? oT2 + 64 * LT * sizeof(E) : oCm + 64 * 4) : oAl + 64 * 4;
-  // workgroups per compute unit that the LDS admits (bf16); the kernel's launch bounds match
-  static constexpr int PER_CU = sizeof(E) == 2 && !WU ? 3 : 2;
+  static constexpr int PER_CU = ut_per_cu<E>(WU, MO);
+  static_assert(WU || sizeof(E) == 2, "only the bf16 factor form runs without W and U");
+  static_assert(MO || !WU, "W/U launches may form M");
   static_assert(64 * LT * sizeof(E) <= 64 * LF * 4, "T and M must fit in an fp32 work matrix");
   static_assert(sizeof(E) == 4 || PER_CU * bytes <= 160 * 1024, "bf16: workgroups per compute unit");
 };
 
 // Persistent: the workgroup walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...; the
 // next unit's K, V and Q rows are requested into registers while the current one computes.
-template <typename E, int DK, int DV, bool GT, bool WU>
-__global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && !WU) ? 3 : 2) void ut_fwd_kernel(
+template <typename E, int DK, int DV, bool GT, bool WU, bool MO>
+__global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kernel(
     Geom g, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ beta, const E* __restrict__ gate, E* __restrict__ w, E* __restrict__ u,
     E* __restrict__ mout, E* __restrict__ xout, float* __restrict__ cum, float* __restrict__ ca,
     float* __restrict__ cb) {
-  typedef UtFwdLds<E, DK, DV, GT, WU> L;
+  typedef UtFwdLds<E, DK, DV, GT, WU, MO> L;
   typedef typename Mma<E>::vec Vv;
+  if constexpr (!MO) mout = nullptr;  // launched with M only where MO
   constexpr int KC = Mma<E>::KC, KS = DK / KC;
   constexpr int VE = 16 / (int)sizeof(E);
   constexpr int VPR = DK / VE;                  // 16-byte vectors per K row
@@ -357,14 +368,14 @@ __global__ __launch_bounds__(kThreads, (sizeof(E) == 2 && !WU) ? 3 : 2) void ut_
   }
 }
 
-template <typename E, int DK, int DV, bool GT, bool WU>
+template <typename E, int DK, int DV, bool GT, bool WU, bool MO>
 static hipError_t ut_go(const Shape& s, const int* table, const void* q, const void* k,
                         const void* v, const void* beta, const void* gate, void* w, void* u,
                         void* m, void* x, float* cum, float* ca, float* cb, hipStream_t st) {
-  typedef UtFwdLds<E, DK, DV, GT, WU> L;
+  typedef UtFwdLds<E, DK, DV, GT, WU, MO> L;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)ut_fwd_kernel<E, DK, DV, GT, WU>,
+    hipError_t e = hipFuncSetAttribute((const void*)ut_fwd_kernel<E, DK, DV, GT, WU, MO>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -375,7 +386,7 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
   const int64_t slots = (int64_t)L::PER_CU * cu_count();
   const int64_t blocks = units < slots ? units : slots;
   prof_begin(st);
-  hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV, GT, WU>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
+  hipLaunchKernelGGL((ut_fwd_kernel<E, DK, DV, GT, WU, MO>), dim3((unsigned)blocks), dim3(kThreads), L::bytes,
                      st, make_geom(s, table), (const E*)q, (const E*)k, (const E*)v,
                      (const E*)beta, (const E*)gate, (E*)w, (E*)u, (E*)m, (E*)x, cum, ca, cb);
   hipError_t e = hipGetLastError();
@@ -383,22 +394,28 @@ static hipError_t ut_go(const Shape& s, const int* table, const void* q, const v
   return e;
 }
 
-// W and U are written together (both or neither); without them the kernel reads no V.
+// W and U are written together (both or neither); without them the kernel reads no V, and
+// without M either it keeps X in K's place.
+template <typename E, int DK, int DV, bool GT>
+static hipError_t ut_gate(const Shape& s, const int* table, const void* q, const void* k,
+                          const void* v, const void* beta, const void* gate, void* w, void* u,
+                          void* m, void* x, float* cum, float* ca, float* cb, hipStream_t st) {
+  if (!w != !u) return hipErrorInvalidValue;
+  if (w) return ut_go<E, DK, DV, GT, true, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  if constexpr (sizeof(E) == 2) {  // the factor form (bf16) is the only caller without W and U
+    if (m) return ut_go<E, DK, DV, GT, false, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+    return ut_go<E, DK, DV, GT, false, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename E, int DK, int DV>
 static hipError_t ut_dispatch(const Shape& s, const int* table, const void* q, const void* k,
                               const void* v, const void* beta, const void* gate, void* w,
                               void* u, void* m, void* x, float* cum, float* ca, float* cb,
                               hipStream_t st) {
-  if (!w != !u) return hipErrorInvalidValue;
-  if (w) {
-    if (gate) return ut_go<E, DK, DV, true, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
-    return ut_go<E, DK, DV, false, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
-  }
-  if constexpr (sizeof(E) == 2) {  // the factor form (bf16) is the only caller without W and U
-    if (gate) return ut_go<E, DK, DV, true, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
-    return ut_go<E, DK, DV, false, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
-  }
-  return hipErrorInvalidValue;
+  if (gate) return ut_gate<E, DK, DV, true>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
+  return ut_gate<E, DK, DV, false>(s, table, q, k, v, beta, gate, w, u, m, x, cum, ca, cb, st);
 }
 
 size_t lds_ut_fwd(Dt dt, int dk, int dv) {
