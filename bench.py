@@ -508,14 +508,24 @@ def aux_measurements(E, args, torch, np, make_inputs, workload, step, q, k, v, b
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # replays and eager steps alternate in blocks after a pre-warm, both timed on the host clock
+    # around a synchronize, so neither sees the clock ramp that follows the capture
+    prewarm(torch, graph.replay)
+    graph_t = eager_t = 0.0
+    n_blk = max(1, args.steps // 10)
+    for blk in range(2 * n_blk):
+        f = graph.replay if blk % 2 == 0 else step
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        if blk % 2 == 0:
+            graph_t += time.perf_counter() - t0
+        else:
+            eager_t += time.perf_counter() - t0
+    graph_ms = graph_t * 1e3 / (10 * n_blk)
+    graph_eager_ms = eager_t * 1e3 / (10 * n_blk)
     del graph
 
     # Cold last-level cache: before each step a 512 MiB buffer is overwritten (evicting the
@@ -601,6 +611,30 @@ def aux_measurements(E, args, torch, np, make_inputs, workload, step, q, k, v, b
     decode_us = (time.perf_counter() - t0) * 1e6 / args.steps
     dec_k = kernel_avgs(E, dec, args.steps)[0]
     dec_kernel_us = 1e3 * sum(dec_k.values())
+    # A serving loop without host launch cost: 16 decode calls (one token each) captured into one
+    # HIP graph and replayed; time per call.
+    decode_graph_us = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            dec()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        dg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dg):
+            for _ in range(16):
+                dec()
+        prewarm(torch, dg.replay, 0.2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dg.replay()
+        torch.cuda.synchronize()
+        decode_graph_us = (time.perf_counter() - t0) * 1e6 / (16 * args.steps)
+        del dg
+    except RuntimeError as e:  # reported as null; the rest of the line stands
+        print("decode graph not measured: %s" % e, file=sys.stderr)
     state_bytes = 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv + 1) * 2  # state in + out, tokens
 
     # Long context (the pages' long-sequence setting, forward only): B=1, H=16, T=32768. The
@@ -608,8 +642,9 @@ def aux_measurements(E, args, torch, np, make_inputs, workload, step, q, k, v, b
     long_ctx = None if args.no_long_context else long_context(E, make_inputs, workload, args.warmup,
                                                                 max(5, args.steps // 5))
 
-    return {"graph_ms": graph_ms, "cold_ms": cold_ms, "euler": euler, "gated": gated,
+    return {"graph_ms": graph_ms, "graph_eager_ms": graph_eager_ms, "cold_ms": cold_ms, "euler": euler, "gated": gated,
             "decode_us": decode_us, "dec_k": dec_k, "dec_kernel_us": dec_kernel_us,
+            "decode_graph_us": decode_graph_us,
             "state_bytes": state_bytes, "long_ctx": long_ctx}
 
 
@@ -780,12 +815,14 @@ def main():
         graph_ms, cold_ms = aux["graph_ms"], aux["cold_ms"]
         out.update({
             "hip_graph": {"ms_per_step": round(graph_ms, 4),
-                          "tokens_per_s": round(B * T / (graph_ms * 1e-3), 1)},
+                          "tokens_per_s": round(B * T / (graph_ms * 1e-3), 1),
+                          "eager_ms_per_step_interleaved": round(aux["graph_eager_ms"], 4)},
             "cold_cache": {"median_ms_per_step": round(cold_ms[len(cold_ms) // 2], 4),
                            "tokens_per_s": round(B * T / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),
                            "steps": len(cold_ms)},
             "euler_mode": aux["euler"],
             "decode": {"us_per_call": round(aux["decode_us"], 2),
+                       "graph_us_per_call": None if aux["decode_graph_us"] is None else round(aux["decode_graph_us"], 2),
                        "kernel_us": round(aux["dec_kernel_us"], 2),
                        "kernels_avg_ms": aux["dec_k"], "tokens_per_call": B, "token_heads_per_call": B * H,
                        "hbm_bytes_per_call": aux["state_bytes"],

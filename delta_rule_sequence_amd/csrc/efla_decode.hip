@@ -11,22 +11,22 @@
 //
 // The state is [B][H][d_k][d_v] fp32; decoding is bound by reading and writing it once per
 // call, which for one token is a single round trip to memory and back. Each (batch row, head) is
-// split over d_v / 8 workgroups of one wave each (1,024 waves at 4 x 16 heads of width 128), so a
-// call fills the chip and every reduction stays inside a wave: no barrier, no LDS. Lane l holds
-// the 16-byte column group l & 1 of the rows l / 2 + 32 i (i < d_k / 32) in registers for all T
-// tokens and loads the k and q entries of its own rows itself. Per token the partial sums of
-// S^T k, S^T q, ||k||^2 and k . q over a lane's rows are reduced over the 32 lanes that share its
-// column group (five xor shuffles). The four workgroups that cover one 128-byte line of every
-// state row (32 columns) are placed on the same XCD (workgroups are dealt to the 8 XCDs round
-// robin), so each line is fetched into one L2 only.
+// split over d_v / COLS workgroups of one wave each, so a call fills the chip and every reduction
+// stays inside a wave: no barrier, no LDS. A wave's COLS columns form COLS / 4 groups of four;
+// lane l holds the 16-byte column group l % (COLS / 4) of the rows l / (COLS / 4) + R i
+// (R = 256 / COLS lanes share a group) in registers for all T tokens and loads the k and q
+// entries of its own rows itself. Per token the partial sums of S^T k, S^T q, ||k||^2 and k . q
+// over a lane's rows are reduced over the R lanes that share its column group (xor shuffles).
+// The workgroups that cover one 128-byte line of every state row (32 columns) are placed on the
+// same XCD (workgroups are dealt to the 8 XCDs round robin), so each line is fetched into one
+// L2 only.
 #include "efla_internal.hpp"
 
 namespace efla {
 
-constexpr int kDecCols = 8;    // state columns per workgroup (one wave)
-constexpr int kDecRows = 32;   // rows covered by one pass of the wave (two column groups)
+constexpr int kDecCols = 16;  // state columns per workgroup (one wave): 16 measured fastest of 8, 16, 32
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int COLS>
 __global__ __launch_bounds__(64) void decode_kernel(Geom g, const E* __restrict__ q,
                                                     const E* __restrict__ k,
                                                     const E* __restrict__ v,
@@ -34,29 +34,33 @@ __global__ __launch_bounds__(64) void decode_kernel(Geom g, const E* __restrict_
                                                     const E* __restrict__ gate,
                                                     float* __restrict__ state,
                                                     E* __restrict__ o, int xcd_map) {
-  constexpr int RPT = DK / kDecRows;            // rows per lane (4 or 2)
-  constexpr int NT = DV / kDecCols;             // workgroups per (batch row, head)
+  constexpr int NG = COLS / 4;                  // column groups per wave
+  constexpr int R = 64 / NG;                    // lanes sharing a column group (row stride)
+  constexpr int RPT = DK / R;                   // rows per lane
+  constexpr int NT = DV / COLS;                 // workgroups per (batch row, head)
+  constexpr int NPL = 32 / COLS;                // workgroups per 128-byte line of a row
+  static_assert(RPT >= 1 && DK % R == 0 && DV % 32 == 0 && NPL >= 1, "decode tiling");
   const int lane = threadIdx.x;
-  const int cg = lane & 1, rg = lane >> 1;      // column group, first row
+  const int cg = lane % NG, rg = lane / NG;     // column group, first row
   int u = blockIdx.x;
-  if (xcd_map) {  // the 4 consecutive units of one 32-column group share blockIdx % 8
+  if (xcd_map && NPL > 1) {  // the NPL consecutive units of one 32-column group share blockIdx % 8
     const int L = u >> 3, x = u & 7;
-    u = ((L >> 2) << 5) + (x << 2) + (L & 3);
+    u = (L / NPL) * (8 * NPL) + x * NPL + L % NPL;
   }
   const int64_t bh = u / NT;                    // b * H + h
-  const int c0 = (u % NT) * kDecCols + 4 * cg;  // this lane's first column
+  const int c0 = (u % NT) * COLS + 4 * cg;      // this lane's first column
   float* S = state + bh * DK * DV + c0;
-  f32x4 col[RPT];                               // S[rg + 32 i][c0 .. c0 + 3]
+  f32x4 col[RPT];                               // S[rg + R i][c0 .. c0 + 3]
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) col[i] = *(const f32x4*)(S + (int64_t)(rg + kDecRows * i) * DV);
+  for (int i = 0; i < RPT; ++i) col[i] = *(const f32x4*)(S + (int64_t)(rg + R * i) * DV);
   const int64_t row0 = bh * g.T;
   for (int t = 0; t < g.T; ++t) {
     const int64_t r = row0 + t;
     float kd[RPT], qd[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      kd[i] = to_f(k[r * DK + rg + kDecRows * i]);
-      qd[i] = to_f(q[r * DK + rg + kDecRows * i]);
+      kd[i] = to_f(k[r * DK + rg + R * i]);
+      qd[i] = to_f(q[r * DK + rg + R * i]);
     }
     const f32x4 vv = ld4f<E>(v + r * DV + c0);
     const float bt = to_f(beta[r]);
@@ -70,9 +74,9 @@ __global__ __launch_bounds__(64) void decode_kernel(Geom g, const E* __restrict_
       lam = fmaf(kd[i], kd[i], lam);
       kq = fmaf(kd[i], qd[i], kq);
     }
-    // sum over the 32 lanes of this column group (every lane ends with the full sums)
+    // sum over the R lanes of this column group (every lane ends with the full sums)
 #pragma unroll
-    for (int off = 2; off < 64; off <<= 1) {
+    for (int off = NG; off < 64; off <<= 1) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         y[e] += __shfl_xor(y[e], off);
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(64) void decode_kernel(Geom g, const E* __restrict_
     const f32x4 rr = bin * vv - (gd * alpha) * y;   // r_j (ungated: alpha (v_j - y_j))
 #pragma unroll
     for (int i = 0; i < RPT; ++i) col[i] = gd * col[i] + kd[i] * rr;
-    if (rg == 0) {  // o_j = scale (g (S^T q)_j + r_j k . q): lanes 0 and 1
+    if (rg == 0) {  // o_j = scale (g (S^T q)_j + r_j k . q): the lanes of row 0
       const f32x4 oj = g.scale * (gd * z + kq * rr);
       if constexpr (sizeof(E) == 4) {
         *(f32x4*)(o + r * DV + c0) = oj;
@@ -100,19 +104,19 @@ __global__ __launch_bounds__(64) void decode_kernel(Geom g, const E* __restrict_
     }
   }
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) *(f32x4*)(S + (int64_t)(rg + kDecRows * i) * DV) = col[i];
+  for (int i = 0; i < RPT; ++i) *(f32x4*)(S + (int64_t)(rg + R * i) * DV) = col[i];
 }
 
 template <typename E, int DK, int DV>
 static hipError_t decode_go(const Shape& s, const void* q, const void* k, const void* v,
                             const void* beta, const void* gate, float* state, void* o,
                             hipStream_t st) {
-  static_assert(DK % kDecRows == 0 && DV % (4 * kDecCols) == 0, "decode tiling");
-  const int64_t blocks = (int64_t)s.B * s.H * (DV / kDecCols);
+  constexpr int COLS = kDecCols, NPL = 32 / COLS;
+  const int64_t blocks = (int64_t)s.B * s.H * (DV / COLS);
   if (blocks < 1) return hipSuccess;
-  const int xcd_map = blocks % 32 == 0 ? 1 : 0;  // the unit mapping is a bijection then
+  const int xcd_map = blocks % (8 * NPL) == 0 ? 1 : 0;  // the unit mapping is a bijection then
   prof_begin(st);
-  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3((unsigned)blocks), dim3(64), 0, st,
+  hipLaunchKernelGGL((decode_kernel<E, DK, DV, COLS>), dim3((unsigned)blocks), dim3(64), 0, st,
                      make_geom(s, nullptr), (const E*)q, (const E*)k, (const E*)v,
                      (const E*)beta, (const E*)gate, state, (E*)o, xcd_map);
   hipError_t e = hipGetLastError();
