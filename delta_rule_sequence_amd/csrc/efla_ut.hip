@@ -46,10 +46,11 @@ struct UtFwdLds {
   static constexpr size_t oA = oV + (WU ? 64 * LV * sizeof(E) : 0); // A (fp32) [64][LF]; later T
   static constexpr size_t oX = KX ? oK : oA + TFB;                  // X (fp32) [64][LF]; M staging first
   static constexpr size_t oAl = (KX ? oA : oX) + TFB;               // alpha    [64]
-  static constexpr size_t oBl = oAl + 64 * 4;                       // b, c     [64] each (GT)
+  static constexpr size_t oLm = oAl + 64 * 4;                       // lambda   [64]
+  static constexpr size_t oBl = oLm + 64 * 4;                       // b, c     [64] each (GT)
   static constexpr size_t oCm = oBl + 64 * 4;
   static constexpr size_t oT2 = oCm + 64 * 4;                       // X diag(b) [64][LT] (GT, WU)
-  static constexpr size_t bytes = GT ? (WU ? oT2 + 64 * LT * sizeof(E) : oCm + 64 * 4) : oAl + 64 * 4;
+  static constexpr size_t bytes = GT ? (WU ? oT2 + 64 * LT * sizeof(E) : oCm + 64 * 4) : oLm + 64 * 4;
   static constexpr int PER_CU = ut_per_cu<E>(WU, MO);
   static_assert(WU || sizeof(E) == 2, "only the bf16 factor form runs without W and U");
   static_assert(MO || !WU, "W/U launches may form M");
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
   float* sX = (float*)(smem + L::oX);
   E* sM = (E*)(smem + L::oX);
   float* sAl = (float*)(smem + L::oAl);
+  float* sLm = (float*)(smem + L::oLm);
   float* sBl = (float*)(smem + L::oBl);
   float* sCm = (float*)(smem + L::oCm);
   E* sT2 = (E*)(smem + L::oT2);
@@ -95,7 +97,8 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
   if (un >= nu) return;
 
   u32x4 kR[KIT], vR[VIT];
-  float bR[KIT], aR[KIT], aN = 0.f;
+  float bN = 0.f, aN = 0.f;  // beta and (gated) log-decay of token `lane` of the requested chunk
+  float bC = 0.f, aC = 0.f;  // the same for the chunk in LDS
   Vv qN[KS], qA[KS];
   // Requests for the next chunk's inputs, spread over the current one. Every request is
   // unconditional (row indices are clamped; after the last chunk, one row of the first), and inside
@@ -108,10 +111,9 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
       const int i = it * kThreads + tid;
       const int r = min(i / VPR, c.n - 1), cc = (i % VPR) * VE;
       kR[it] = *(const u32x4*)(kL + (c.row0 + r) * DK + cc);
-      bR[it] = to_f(bL[c.row0 + r]);
-      if constexpr (GT) aR[it] = to_f(aL[c.row0 + r]);
     }
-    if constexpr (GT) aN = to_f(aL[c.row0 + min(lane, c.n - 1)]);  // token = lane
+    bN = to_f(bL[c.row0 + min(lane, c.n - 1)]);  // token = lane
+    if constexpr (GT) aN = to_f(aL[c.row0 + min(lane, c.n - 1)]);
   };
   auto issue_v = [&](const ChunkUnit& c) {
     if (!WU) return;  // V feeds U = T V only
@@ -130,9 +132,9 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
   };
 
   // K and V land in LDS; ||k||^2 is reduced from the K vectors (VPR consecutive threads per
-  // row), giving alpha. Done before the loop for the first chunk and at the end of each
-  // iteration for the next one, after that iteration's stores, so the compiler waits for the
-  // loads alone there.
+  // row) into LDS (the coefficients follow after the next barrier, one token per lane). Done
+  // before the loop for the first chunk and at the end of each iteration for the next one, after
+  // that iteration's stores, so the compiler waits for the loads alone there.
   auto land = [&](const ChunkUnit& cu) {
     const int n = cu.n;
 #pragma unroll
@@ -146,11 +148,10 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc = fmaf(to_f(x[e]), to_f(x[e]), acc);
       acc = group_sum<VPR>(acc);
-      if (i % VPR == 0) {
-        sAl[r] = flow_coef(r < n ? bR[it] : 0.f, acc, g.euler).alpha;
-        if constexpr (GT) sBl[r] = r < n ? gated_input_coef(bR[it], acc, aR[it], g.euler) : 0.f;
-      }
+      if (i % VPR == 0) sLm[r] = r < n ? acc : 0.f;
     }
+    bC = bN;
+    if constexpr (GT) aC = aN;
     if constexpr (WU) {
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
@@ -201,6 +202,18 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
     // row of the first chunk, which all workgroups then share in L2.
     ChunkUnit nxt = chunk_unit(g, more ? unx : 0);
     if (!more) nxt.n = 1;
+    // Flow coefficients, one token per lane, computed by every wave (each needs alpha of the rows
+    // it scales; one pass of the coefficient code instead of one per K vector group). Wave 0
+    // keeps them in LDS for the later steps. Padded tokens have beta = 0, so alpha = b = 0.
+    float al_l;
+    {
+      const float lam = sLm[lane];
+      al_l = flow_coef(lane < n ? bC : 0.f, lam, g.euler).alpha;
+      if (wv == 0) {
+        sAl[lane] = al_l;
+        if constexpr (GT) sBl[lane] = lane < n ? gated_input_coef(bC, lam, aC, g.euler) : 0.f;
+      }
+    }
     issue_k(nxt);
 
     // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T), lower blocks only (the
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
     // so a lane holds four consecutive columns of one row and stores them at once.
     {
       const int ra = 3 - wv, rowa = 16 * ra + (lane & 15), c4 = 4 * (lane >> 4);
-      const float ala = sAl[rowa];
+      const float ala = __shfl(al_l, rowa);
       const float cra = GT ? sCm[rowa] : 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
