@@ -466,8 +466,11 @@ EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld,
     const int byte = j * 1024 + lane * 16;
     const int r = byte / S::RB, pc = (byte % S::RB) >> 4;
     const int lc = pc ^ S::mask(r);
-    const E* src = g + (int64_t)min(r, n - 1) * gld + lc * (16 / (int)sizeof(E));
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + j * 1024), 16, 0, 0);
+    // a 32-bit byte offset from the wave-uniform base: scalar-base addressing, no per-lane
+    // 64-bit address arithmetic (the tile spans under 64 rows of gld elements)
+    const unsigned off = (unsigned)(min(r, n - 1) * (int)gld * (int)sizeof(E) + 16 * lc);
+    __builtin_amdgcn_global_load_lds((const void*)at_byte<unsigned char>(g, off),
+                                     (lds_void*)(dst + j * 1024), 16, 0, 0);
   }
 }
 
@@ -476,7 +479,8 @@ EFLA_DEV void dma_tile(unsigned char* dst, const E* __restrict__ g, int64_t gld,
 // to precede its use (a plain load followed by an LDS store makes the compiler wait for every
 // load in flight, the L2 warm-up loads included).
 EFLA_DEV void dma_vec64(unsigned char* dst, const float* __restrict__ g, int lane) {
-  __builtin_amdgcn_global_load_lds((const void*)(g + lane), (lds_void*)dst, 4, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void*)at_byte<unsigned char>(g, 4u * (unsigned)lane),
+                                   (lds_void*)dst, 4, 0, 0);
 }
 
 // Wait until this wave's outstanding vector memory operations (loads, stores, LDS DMA) are
@@ -516,7 +520,8 @@ EFLA_DEV void l2_touch_lds(unsigned char* dummy, const void* p, int nbytes, int 
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int j = min(part + nparts * (lane + NT * i), last);
-    __builtin_amdgcn_global_load_lds((const void*)((const char*)p + (j << 7)), (lds_void*)dummy, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)at_byte<unsigned char>((const unsigned char*)p, (unsigned)j << 7),
+                                     (lds_void*)dummy, 4, 0, 0);
   }
 }
 

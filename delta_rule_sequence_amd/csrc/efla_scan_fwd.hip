@@ -166,11 +166,13 @@ __device__ __forceinline__ void scan_fwd_body(
         if (i < RPT * CPM) {
           u32x4 val = u32x4{0u, 0u, 0u, 0u};
           if (r < n && lc * VE < 16 * (r / 16 + 1)) val = *(const u32x4*)(sm + SM::off(r, lc * VE));
-          *(u32x4*)(gm + r * kChunk + lc * VE) = val;
+          *at_byte<u32x4>(gm, (unsigned)((r * kChunk + lc * VE) * (int)sizeof(E))) = val;
         }
       }
     }
   };
+  // Stores address 32-bit byte offsets from wave-uniform tile bases (scalar-base addressing; no
+  // 64-bit address arithmetic per lane).
   auto copy_out = [&](int c) {  // staged outputs of chunk c -> global memory, 16-byte rows
     const unsigned char* stg = smem + L::oStg + (c & 1) * L::sstage;
     const int n = rows_of(c);
@@ -181,7 +183,8 @@ __device__ __forceinline__ void scan_fwd_body(
       for (int it = 0; it < (64 * CPR + NTL - 1) / NTL; ++it) {
         const int i = it * NTL + tl, r = i / CPR, lc = i % CPR;
         if (i < 64 * CPR && r < n)
-          *(u32x4*)(o + (r0 + r) * DV + v0 + lc * VE) = *(const u32x4*)(stg + L::gO + SU::off(r, lc * VE));
+          *at_byte<u32x4>(o + r0 * DV + v0, (unsigned)((r * DV + lc * VE) * (int)sizeof(E))) =
+              *(const u32x4*)(stg + L::gO + SU::off(r, lc * VE));
       }
     }
     if constexpr (WSV) {
@@ -189,7 +192,8 @@ __device__ __forceinline__ void scan_fwd_body(
       for (int it = 0; it < (64 * CPR + NTL - 1) / NTL; ++it) {
         const int i = it * NTL + tl, r = i / CPR, lc = i % CPR;
         if (i < 64 * CPR && r < n)
-          *(u32x4*)(ut + (r0 + r) * DV + v0 + lc * VE) = *(const u32x4*)(stg + L::gUt + SU::off(r, lc * VE));
+          *at_byte<u32x4>(ut + r0 * DV + v0, (unsigned)((r * DV + lc * VE) * (int)sizeof(E))) =
+              *(const u32x4*)(stg + L::gUt + SU::off(r, lc * VE));
       }
     }
     if constexpr (WSV) {
@@ -198,7 +202,8 @@ __device__ __forceinline__ void scan_fwd_body(
       for (int it = 0; it < (DK * CPR + NTL - 1) / NTL; ++it) {
         const int i = it * NTL + tl, d = i / CPR, lc = i % CPR;
         if (i < DK * CPR)
-          *(u32x4*)(gS + (int64_t)d * DV + lc * VE) = *(const u32x4*)(stg + L::gS + SU::off(d, lc * VE));
+          *at_byte<u32x4>(gS, (unsigned)((d * DV + lc * VE) * (int)sizeof(E))) =
+              *(const u32x4*)(stg + L::gS + SU::off(d, lc * VE));
       }
     }
   };
