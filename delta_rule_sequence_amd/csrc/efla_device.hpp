@@ -943,8 +943,10 @@ EFLA_DEV void scan_block(int bid, int nsh, int ntile, int& sh, int& tile) {
 // ---------------------------------------------------------------------------
 // X = (I + A)^{-1} for a strictly lower triangular 64x64 fp32 A (LDS, pitch kPitchF).
 // Blocked forward substitution over 16x16 blocks:
-//   diagonal blocks X_ii = (I + A_ii)^{-1} by column substitution (16 lanes of wave i; each
-//   solved row at once updates every later row, so the FMAs form short independent chains),
+//   diagonal blocks X_ii = (I + A_ii)^{-1} by column substitution, all four in wave 3 (lane
+//   16 i + c solves column c of block i; each solved row at once updates every later row, so
+//   the FMAs form short independent chains; the other waves leave their issue slots to the
+//   other workgroups on the compute unit, and wave 3 has no block column below),
 //   then wave j fills block column j downwards, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj,
 //   with fp32 MFMA: an accumulator tile has exactly the layout of a B operand, so the
 //   X_kj already computed stay in registers and feed the next products.
@@ -956,17 +958,17 @@ EFLA_DEV void invert_unit_lower64(const float* sA, float* sX, int tid) {
   constexpr int ld = kPitchF;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (lane < 16) {
-    const int o = wv * 16;
+  if (wv == 3) {
+    const int o = 16 * (lane >> 4), c = lane & 15;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
     for (int m = 0; m < 15; ++m)
 #pragma unroll
       for (int r = m + 1; r < 16; ++r) x[r] = fmaf(-sA[(o + r) * ld + o + m], x[m], x[r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sX[(o + r) * ld + o + lane] = x[r];
+    for (int r = 0; r < 16; ++r) sX[(o + r) * ld + o + c] = x[r];
   }
   __syncthreads();
   const int j = wv;
