@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
     for (int it = 0; it < KIT; ++it) {
       const int i = it * kThreads + tid;
       const int r = min(i / VPR, c.n - 1), cc = (i % VPR) * VE;
-      kR[it] = *(const u32x4*)(kL + (c.row0 + r) * DK + cc);
+      kR[it] = *at_byte<u32x4>(kL + c.row0 * DK, (unsigned)((r * DK + cc) * (int)sizeof(E)));
     }
     bN = to_f(bL[c.row0 + min(lane, c.n - 1)]);  // token = lane
     if constexpr (GT) aN = to_f(aL[c.row0 + min(lane, c.n - 1)]);
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
             *(bf16x8*)(sT + r * L::LT + c) = te;
             if constexpr (GT) *(bf16x8*)(sT2 + r * L::LT + c) = tu;
           }
-          if (gx) *(bf16x8*)(gx + r * 64 + c) = xe;
+          if (gx) *at_byte<bf16x8>(gx, (unsigned)((r * 64 + c) * (int)sizeof(E))) = xe;
         } else {
           if (WU) {
             *(f32x4*)(sT + r * L::LT + c) = x0 * a0;
