@@ -217,16 +217,16 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
     issue_k(nxt);
 
     // A = strictly_lower(diag(alpha) K K^T) and M = tril(Q K^T), lower blocks only (the
-    // inverse never reads A above the diagonal). Wave wv takes A's row block 3 - wv and M's
-    // row block wv: five block products each. Both are formed transposed (operands swapped),
-    // so a lane holds four consecutive columns of one row and stores them at once.
+    // inverse never reads A above the diagonal). With M, wave wv takes A's row block 3 - wv and
+    // M's row block wv: five block products each; without M the ten blocks of A are dealt 3, 3,
+    // 2, 2. Both are formed transposed (operands swapped), so a lane holds four consecutive
+    // columns of one row and stores them at once.
     {
-      const int ra = 3 - wv, rowa = 16 * ra + (lane & 15), c4 = 4 * (lane >> 4);
-      const float ala = __shfl(al_l, rowa);
-      const float cra = GT ? sCm[rowa] : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        if (nb > ra) continue;
+      const int c4 = 4 * (lane >> 4);
+      auto ablk = [&](int ra, int nb) {
+        const int rowa = 16 * ra + (lane & 15);
+        const float ala = __shfl(al_l, rowa);
+        const float cra = GT ? sCm[rowa] : 0.f;
         f32x4 acc = mma<E, false, false>(sK + 16 * nb * L::LK, L::LK, sK + 16 * ra * L::LK, L::LK, 0, DK, zero4(), lane);
         f32x4 av;
 #pragma unroll
@@ -236,6 +236,19 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
           av[i] = rowa > col ? ala * dec * acc[i] : 0.f;
         }
         *(f32x4*)(sA + rowa * L::LF + 16 * nb + c4) = av;
+      };
+      if constexpr (MO) {
+        const int ra = 3 - wv;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          if (nb <= ra) ablk(ra, nb);
+      } else {
+        switch (wv) {
+          case 0: ablk(3, 0); ablk(3, 1); ablk(3, 2); break;
+          case 1: ablk(3, 3); ablk(2, 0); ablk(2, 1); break;
+          case 2: ablk(2, 2); ablk(1, 0); break;
+          default: ablk(1, 1); ablk(0, 0); break;
+        }
       }
     }
     if (mout) {
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
       s2g<E, 64>(gm, 64, sM, L::LT, kChunk, tid);
     }
     issue_v(nxt);
-    __syncthreads();
+    if constexpr (!L::KX) __syncthreads();  // M's staging (X's region) is copied out first
     invert_unit_lower64(sA, sX, tid);
     issue_q(nxt);
 
@@ -374,7 +387,7 @@ __global__ __launch_bounds__(kThreads, (ut_per_cu<E>(WU, MO))) void ut_fwd_kerne
       s2g<E, DV>(u + row0 * DV, DV, sV, L::LV, n, tid);
     }
     if (!more) break;
-    __syncthreads();  // the copies out of sK and sV are done before the next chunk lands
+    if constexpr (WU) __syncthreads();  // the copies out of sK and sV are done before the next chunk lands
     land(nxt);
     un = unx;
     cur = nxt;
